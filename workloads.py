@@ -1,0 +1,132 @@
+"""Seeded synthetic inputs for the RMSNorm forward/backward workloads.
+
+This module holds no RMSNorm arithmetic: it only names the workloads (shape, dtype, convention,
+epsilon, value distributions) and draws their inputs. Both the GPU library's tests/benchmark and
+the CPU oracle's tests take their inputs from here; it imports neither of them.
+
+Recipe (the same for every workload): ``numpy.random.default_rng(seed)`` draws x, then w, then dy
+(in that order; an all-ones tensor draws nothing) as float64, which are cast to float32 and then
+rounded to the I/O dtype with an independent library conversion (torch's CPU bfloat16 cast, NumPy's
+float16 cast). Both sides therefore receive the same already-rounded values, as the blog post
+"Den dolda avrundningen i RMSNorm" (section "Ge testet samma precision som modellen") recommends
+for comparing implementations.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "f32" | "f16" | "bf16": dtype of x, w, y, dy, dx
+    M: int              # rows
+    N: int              # row width (hidden size)
+    rounding: str       # "once" | "twice"
+    offset: float       # gain = offset + w
+    eps: float
+    x_dist: tuple       # ("normal", mean, std) | ("uniform", lo, hi) | ("ones",)
+    w_dist: tuple
+    dy_dist: tuple
+    seed: int = 0
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def itemsize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def fwd_bytes(self) -> int:
+        """Algorithmic bytes of one forward: read x, write y, read w once, write the fp32 rstd."""
+        s = self.itemsize
+        return 2 * self.M * self.N * s + self.N * s + 4 * self.M
+
+    def bwd_bytes(self) -> int:
+        """Algorithmic bytes of one backward: read dy and x, write dx, read w and rstd, write dw."""
+        s = self.itemsize
+        return 3 * self.M * self.N * s + self.N * s + 4 * self.M + 4 * self.N
+
+
+_STD = ("normal", 0.0, 1.0)
+_GAIN = ("uniform", 0.9, 1.1)
+
+WORKLOADS = {
+    # fp32 I/O, tiny: the two conventions coincide; checked against the oracle in full.
+    "fp32_64x1024": Workload("fp32_64x1024", "f32", 64, 1024, "twice", 0.0, 1e-6,
+                             _STD, _GAIN, _STD, 0),
+    # bf16 I/O, Llama-style (round twice), the headline measurement.
+    "bf16_4096x4096": Workload("bf16_4096x4096", "bf16", 4096, 4096, "twice", 0.0, 1e-6,
+                               _STD, _GAIN, _STD, 0),
+    # fp16 I/O with x ~ N(0, 8^2): the sum of squares of a row overflows binary16.
+    "fp16_8192x8192": Workload("fp16_8192x8192", "f16", 8192, 8192, "twice", 0.0, 1e-5,
+                               ("normal", 0.0, 8.0), _GAIN, ("ones",), 0),
+    # bf16 Gemma-style: round once with gain 1 + w, w ~ N(0, 0.1) read as variance 0.1.
+    "bf16_16384x3072_gemma": Workload("bf16_16384x3072_gemma", "bf16", 16384, 3072, "once", 1.0,
+                                      1e-6, _STD, ("normal", 0.0, math.sqrt(0.1)), _STD, 0),
+}
+# Hidden-size sweep at M = 4096, bf16, round twice.
+for _n in (1024, 2048, 4096, 8192, 16384, 32768):
+    WORKLOADS[f"bf16_sweep_4096x{_n}"] = Workload(f"bf16_sweep_4096x{_n}", "bf16", 4096, _n, "twice",
+                                                  0.0, 1e-6, _STD, _GAIN, _STD, 0)
+HEADLINE = "bf16_4096x4096"
+
+
+def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
+    kind = dist[0]
+    if kind == "normal":
+        return rng.normal(dist[1], dist[2], size=shape)
+    if kind == "uniform":
+        return rng.uniform(dist[1], dist[2], size=shape)
+    if kind == "ones":
+        return np.ones(shape, dtype=np.float64)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def to_dtype_values(a, dtype: str) -> np.ndarray:
+    """float32 array holding the values of ``a`` converted to ``dtype`` by a library cast."""
+    a32 = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    if dtype == "f32":
+        return a32
+    if dtype == "f16":
+        return a32.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        import torch
+        return torch.from_numpy(a32).to(torch.bfloat16).to(torch.float32).numpy()
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(wl: Workload, M: int | None = None, N: int | None = None,
+                seed: int | None = None) -> dict:
+    """Draw ``x`` [M, N], ``w`` [N], ``dy`` [M, N] for a workload (float32 arrays of T values).
+
+    ``M``, ``N`` and ``seed`` override the workload's own, for smaller parity cases that keep the
+    workload's distributions.
+    """
+    M = wl.M if M is None else M
+    N = wl.N if N is None else N
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = _draw(rng, wl.x_dist, (M, N))
+    w = _draw(rng, wl.w_dist, (N,))
+    dy = _draw(rng, wl.dy_dist, (M, N))
+    return {
+        "x": to_dtype_values(x, wl.dtype),
+        "w": to_dtype_values(w, wl.dtype),
+        "dy": to_dtype_values(dy, wl.dtype),
+    }
+
+
+def torch_dtype(dtype: str):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+
+
+def to_device(a: np.ndarray, dtype: str, device: str):
+    """Copy a float32 array of T values to a ``device`` tensor of dtype T (exact conversion)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch_dtype(dtype)).to(device)
