@@ -1,0 +1,291 @@
+"""RMSNorm forward/backward on AMD Instinct MI355X (gfx950): Python binding of ``librmsnorm``.
+
+The binding only marshals arguments: it checks tensor shapes, dtypes, devices and strides, allocates
+outputs with torch (device memory and streams are all torch provides here) and calls the C
+interface in ``librmsnorm.so`` on torch's current stream. Every step of the computation runs in the
+library's HIP kernels; there is no fallback. If the library has not been built the first call
+raises ``LibraryMissing`` (build it with ``python -m bwd_precision_numerics_amd.build``).
+
+    y, rstd = fwd(x, w, eps=1e-6, offset=0.0, rounding="twice")
+    dx, dw  = bwd(dy, x, w, rstd, offset=0.0)
+    y       = rms_norm(x, w, eps, offset, rounding)        # autograd-aware
+
+``rounding="twice"`` is the Llama convention T(float(T(xhat)) * g); ``"once"`` is the Gemma
+convention T(xhat * g); the gain is ``g = offset + w`` (offset 1 for Gemma).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librmsnorm.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "librmsnorm.h")
+
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+ROUNDING_CODES = {"once": 0, "twice": 1}
+VARIANT_CODES = {"auto": 0, "registers": 1, "lds": 2, "streaming": 3}
+STATUS_NAMES = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_MISALIGNED",
+                4: "ERR_WORKSPACE", 5: "ERR_HIP"}
+
+
+class LibraryMissing(RuntimeError):
+    """librmsnorm.so is not built (or cannot be loaded)."""
+
+
+class RMSNormError(RuntimeError):
+    """A librmsnorm call returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} ({message})")
+        self.status = status
+
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_f = ctypes.c_float
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+SIGNATURES = {
+    "rmsnorm_fwd": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i, _f, _f, _i, _p]),
+    "rmsnorm_fwd_variant": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i, _f, _f, _i, _i, _p]),
+    "rmsnorm_bwd_workspace_bytes": (_sz, [_i64, _i64, _i]),
+    "rmsnorm_bwd": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p, _sz, _i64, _i64, _i, _f,
+                         _f, _i, _p]),
+    "rmsnorm_bwd_variant": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p, _sz, _i64, _i64,
+                                 _i, _f, _f, _i, _i, _p]),
+    "rmsnorm_bwd_rows": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _sz, _i64, _i64, _i, _f,
+                              _i, _p]),
+    "rmsnorm_bwd_dw_reduce": (_i, [_p, _sz, _p, _i64, _i64, _i, _p]),
+    "rmsnorm_status_string": (ctypes.c_char_p, [_i]),
+    "rmsnorm_abi_version": (_i, []),
+}
+
+
+def header_functions(path: str = HEADER_PATH) -> list:
+    """Names of the functions the C header declares."""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmsnorm_[a-z_0-9]+)\s*\(", text)))
+
+
+def library(path: str | None = None) -> ctypes.CDLL:
+    """Load librmsnorm.so once and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise LibraryMissing(f"{p} is not built; run `python -m bwd_precision_numerics_amd.build`")
+    try:
+        lib = ctypes.CDLL(p)
+    except OSError as e:
+        raise LibraryMissing(f"cannot load {p}: {e}") from e
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = library().rmsnorm_status_string(status).decode()
+        raise RMSNormError(fn, status, msg)
+
+
+# ---- tensor plumbing --------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_name(t) -> str:
+    torch = _torch()
+    m = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return m[t.dtype]
+
+
+def _rows(t, name: str):
+    """Check a 2-D device tensor with unit column stride; return (ptr, row stride)."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [M, N], got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along the last dimension")
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    return t.data_ptr(), max(ld, t.shape[1])
+
+
+def _vec(t, name: str, n: int):
+    if t.dim() != 1 or t.shape[0] != n:
+        raise ValueError(f"{name} must be 1-D of length {n}, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if n > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+
+
+def _stream(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(M: int, N: int, dtype: str) -> int:
+    return int(library().rmsnorm_bwd_workspace_bytes(M, N, DTYPE_CODES[dtype]))
+
+
+def fwd(x, w, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twice",
+        variant: str = "auto", y=None, rstd=None, want_rstd: bool = True):
+    """RMSNorm forward. Returns ``(y, rstd)`` (``rstd`` is None when ``want_rstd`` is False)."""
+    torch = _torch()
+    dt = dtype_name(x)
+    if w.dtype != x.dtype:
+        raise TypeError("w must have the dtype of x")
+    M, N = x.shape
+    px, ldx = _rows(x, "x")
+    pw = _vec(w, "w", N)
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if y.dtype != x.dtype or tuple(y.shape) != (M, N):
+        raise ValueError("y must match x in shape and dtype")
+    py, ldy = _rows(y, "y")
+    if want_rstd and rstd is None:
+        rstd = torch.empty((M,), dtype=torch.float32, device=x.device)
+    prs = None
+    if rstd is not None:
+        if rstd.dtype != torch.float32:
+            raise TypeError("rstd must be float32")
+        prs = _vec(rstd, "rstd", M)
+        _same_device(x, rstd)
+    _same_device(x, w, y)
+    st = library().rmsnorm_fwd_variant(px, ldx, pw, py, ldy, prs, M, N, DTYPE_CODES[dt], eps,
+                                       offset, ROUNDING_CODES[rounding], VARIANT_CODES[variant],
+                                       _stream(x.device))
+    _check("rmsnorm_fwd", st)
+    return y, rstd
+
+
+def _bwd_common(dy, x, w, rstd, dx):
+    torch = _torch()
+    dt = dtype_name(x)
+    if dy.dtype != x.dtype or w.dtype != x.dtype:
+        raise TypeError("dy and w must have the dtype of x")
+    if tuple(dy.shape) != tuple(x.shape):
+        raise ValueError("dy must have the shape of x")
+    if rstd is None or rstd.dtype != torch.float32:
+        raise TypeError("rstd (float32, from fwd) is required")
+    M, N = x.shape
+    if dx is None:
+        dx = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if dx.dtype != x.dtype or tuple(dx.shape) != (M, N):
+        raise ValueError("dx must match x in shape and dtype")
+    _same_device(dy, x, w, rstd, dx)
+    return dt, M, N, dx
+
+
+def _workspace(M, N, dt, device, workspace):
+    torch = _torch()
+    need = workspace_bytes(M, N, dt)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def bwd(dy, x, w, rstd, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twice",
+        variant: str = "auto", dx=None, dw=None, workspace=None):
+    """RMSNorm backward. Returns ``(dx, dw)``; ``dw`` is float32."""
+    torch = _torch()
+    dt, M, N, dx = _bwd_common(dy, x, w, rstd, dx)
+    if dw is None:
+        dw = torch.empty((N,), dtype=torch.float32, device=x.device)
+    if dw.dtype != torch.float32:
+        raise TypeError("dw must be float32")
+    pdy, lddy = _rows(dy, "dy")
+    px, ldx = _rows(x, "x")
+    pdx, lddx = _rows(dx, "dx")
+    workspace, wsb = _workspace(M, N, dt, x.device, workspace)
+    st = library().rmsnorm_bwd_variant(pdy, lddy, px, ldx, _vec(w, "w", N), _vec(rstd, "rstd", M),
+                                       pdx, lddx, _vec(dw, "dw", N), workspace.data_ptr(), wsb, M,
+                                       N, DTYPE_CODES[dt], eps, offset, ROUNDING_CODES[rounding],
+                                       VARIANT_CODES[variant], _stream(x.device))
+    _check("rmsnorm_bwd", st)
+    return dx, dw
+
+
+def bwd_rows(dy, x, w, rstd, workspace, offset: float = 0.0, variant: str = "auto", dx=None):
+    """First backward stage: dx and the per-block dw partials (in ``workspace``)."""
+    dt, M, N, dx = _bwd_common(dy, x, w, rstd, dx)
+    pdy, lddy = _rows(dy, "dy")
+    px, ldx = _rows(x, "x")
+    pdx, lddx = _rows(dx, "dx")
+    wsb = workspace.numel() * workspace.element_size()
+    st = library().rmsnorm_bwd_rows(pdy, lddy, px, ldx, _vec(w, "w", N), _vec(rstd, "rstd", M),
+                                    pdx, lddx, workspace.data_ptr(), wsb, M, N, DTYPE_CODES[dt],
+                                    offset, VARIANT_CODES[variant], _stream(x.device))
+    _check("rmsnorm_bwd_rows", st)
+    return dx
+
+
+def dw_reduce(workspace, dw, M: int, N: int, dtype: str):
+    """Second backward stage: dw = fixed-order sum of the partials in ``workspace``."""
+    wsb = workspace.numel() * workspace.element_size()
+    st = library().rmsnorm_bwd_dw_reduce(workspace.data_ptr(), wsb, _vec(dw, "dw", N), M, N,
+                                         DTYPE_CODES[dtype], _stream(dw.device))
+    _check("rmsnorm_bwd_dw_reduce", st)
+    return dw
+
+
+def _make_autograd():
+    torch = _torch()
+
+    class RMSNormFunction(torch.autograd.Function):
+        """y = RMSNorm(x) * (offset + w) over the last dimension; backward through librmsnorm."""
+
+        @staticmethod
+        def forward(ctx, x, w, eps, offset, rounding):
+            shape = x.shape
+            x2 = x.reshape(-1, shape[-1])
+            y, rstd = fwd(x2, w, eps=eps, offset=offset, rounding=rounding)
+            ctx.save_for_backward(x2, w, rstd)
+            ctx.cfg = (eps, offset, rounding, shape)
+            return y.reshape(shape)
+
+        @staticmethod
+        def backward(ctx, gy):
+            x2, w, rstd = ctx.saved_tensors
+            eps, offset, rounding, shape = ctx.cfg
+            gy2 = gy.reshape(-1, shape[-1])
+            if gy2.stride(-1) != 1:
+                gy2 = gy2.contiguous()
+            dx, dw = bwd(gy2, x2, w, rstd, eps=eps, offset=offset, rounding=rounding)
+            return dx.reshape(shape), dw.to(w.dtype), None, None, None
+
+    return RMSNormFunction
+
+
+_autograd_fn = None
+
+
+def rms_norm(x, w, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twice"):
+    """Autograd-aware RMSNorm over the last dimension of ``x``."""
+    global _autograd_fn
+    if _autograd_fn is None:
+        _autograd_fn = _make_autograd()
+    return _autograd_fn.apply(x, w, eps, offset, rounding)

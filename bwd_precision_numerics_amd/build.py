@@ -1,0 +1,76 @@
+"""Compile the HIP library ``librmsnorm.so`` for gfx950, in place next to this file.
+
+Usage: ``python -m bwd_precision_numerics_amd.build [--resource-usage FILE]``.
+
+Flags:
+* ``--offload-arch=gfx950``: MI355X only.
+* ``-ffp-contract=off``: no implicit multiply-add fusion, so every product and difference in the
+  elementwise formulas is one IEEE float32 operation as the contract states; the kernels request
+  fused multiply-adds explicitly where a reduction may use them.
+* ``-Xclang -target-feature -Xclang -packed-fp32-ops``: no packed float32 VALU instructions.
+* ``-fvisibility=hidden``: only the ``extern "C"`` entry points are exported.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "librmsnorm.hip")
+OUT = os.path.join(HERE, "librmsnorm.so")
+HEADERS = [os.path.join(HERE, "csrc", f) for f in
+           ("rmsnorm_common.hpp", "rmsnorm_fwd.hpp", "rmsnorm_bwd.hpp")]
+HEADERS.append(os.path.join(ROOT, "include", "librmsnorm.h"))
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    return path if os.path.exists(path) else (shutil.which("hipcc") or "hipcc")
+
+
+def flags() -> list:
+    return [
+        "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-ffp-contract=off",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-fvisibility=hidden",
+        "-I", os.path.join(ROOT, "include"),
+    ]
+
+
+def build(resource_usage: str | None = None, verbose: bool = False) -> str:
+    """Compile librmsnorm.so (always recompiles). Returns the path of the library."""
+    tmp = OUT + ".tmp"
+    cmd = [hipcc()] + flags() + [SRC, "-o", tmp]
+    if resource_usage:
+        cmd += ["-Rpass-analysis=kernel-resource-usage"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    diag = proc.stdout + proc.stderr
+    if resource_usage:
+        with open(resource_usage, "w") as f:
+            f.write(diag)
+    if proc.returncode != 0:
+        sys.stderr.write(diag)
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+    os.replace(tmp, OUT)
+    return OUT
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--resource-usage", help="write the compiler's per-kernel resource report here")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args()
+    print(build(args.resource_usage, args.verbose))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

@@ -1,0 +1,461 @@
+// librmsnorm: C interface, argument validation, kernel selection and launches.
+//
+// Every argument check runs before the first HIP call, so a rejected call launches nothing and
+// touches no device state. The library keeps no state apart from a per-device cache of the LDS
+// limit, filled on first use (a relaxed atomic per device: racing threads store the same value).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/librmsnorm.h"
+#include "rmsnorm_bwd.hpp"
+#include "rmsnorm_fwd.hpp"
+
+using namespace rmsn;
+
+namespace {
+
+constexpr int kFwdBlockThreads = 256;   // forward rows per block = 256 / threads-per-row
+constexpr int kBwdBlockThreads = 1024;  // backward: 16 wavefronts per persistent block
+constexpr int kFwdMaxIters = 8;         // 16-byte vectors per thread, forward register kernel
+constexpr int kBwdRegMaxIters = 2;      // backward register kernel (rows + prefetch in registers)
+constexpr int kBwdLdsMaxIters = 4;      // backward LDS-staged kernel
+
+int elem_bytes(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F32 ? 4 : 2; }
+int vec_elems(rmsnorm_dtype d) { return 16 / elem_bytes(d); }
+bool dtype_ok(int d) { return d == RMSNORM_DTYPE_F32 || d == RMSNORM_DTYPE_F16 || d == RMSNORM_DTYPE_BF16; }
+bool rounding_ok(int r) { return r == RMSNORM_ROUND_ONCE || r == RMSNORM_ROUND_TWICE; }
+bool variant_ok(int v) { return v >= RMSNORM_VARIANT_AUTO && v <= RMSNORM_VARIANT_STREAMING; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t pow2_ceil(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// The largest element offset a row-strided [M, N] access touches must fit in int64.
+bool extent_ok(int64_t M, int64_t N, int64_t ld) {
+  if (M <= 1) return true;
+  return (M - 1) <= (INT64_MAX - N) / ld;
+}
+
+// ---- device LDS limit (queried once per device) ---------------------------------------------------
+std::atomic<int> g_lds_limit[64];
+
+rmsnorm_status lds_limit(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RMSNORM_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    const int cached = g_lds_limit[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *out = cached;
+      return RMSNORM_OK;
+    }
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return RMSNORM_ERR_HIP;
+  if (dev >= 0 && dev < 64) g_lds_limit[dev].store(v, std::memory_order_relaxed);
+  *out = v;
+  return RMSNORM_OK;
+}
+
+// ---- kernel plans ---------------------------------------------------------------------------------
+struct Plan {
+  rmsnorm_variant variant;  // resolved (never AUTO)
+  bool wide;                // 16-byte vectors
+  int tpr, iters, groups;
+  size_t lds;               // dynamic LDS bytes
+  int64_t grid;
+};
+
+size_t round16(size_t b) { return (b + 15) & ~size_t(15); }
+
+// Forward: a wavefront per row up to 512 vectors (4096 16-bit elements), wider rows spread over
+// more wavefronts with at most 8 vectors per thread.
+void fwd_shape(int64_t nv, int* tpr, int* iters) {
+  if (nv <= 64 * kFwdMaxIters) {
+    *tpr = 64;
+  } else {
+    *tpr = (int)clamp64(pow2_ceil(ceil_div(nv, kFwdMaxIters)), 64, 1024);
+  }
+  *iters = (int)ceil_div(nv, *tpr);
+}
+
+rmsnorm_status plan_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
+                        rmsnorm_variant req, Plan* p) {
+  const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
+  int tpr, iters;
+  fwd_shape(nv_wide, &tpr, &iters);
+  const bool reg_ok = wide_ok && iters <= kFwdMaxIters;
+  rmsnorm_variant v = req;
+  if (v == RMSNORM_VARIANT_AUTO) v = reg_ok ? RMSNORM_VARIANT_REGISTERS : RMSNORM_VARIANT_STREAMING;
+  if ((v == RMSNORM_VARIANT_REGISTERS || v == RMSNORM_VARIANT_LDS) && !reg_ok)
+    return RMSNORM_ERR_UNSUPPORTED;
+  p->variant = v;
+  if (v == RMSNORM_VARIANT_STREAMING) {
+    p->wide = wide_ok;
+    const int64_t nv = wide_ok ? nv_wide : N;
+    fwd_shape(nv, &tpr, &iters);
+    iters = 0;
+  } else {
+    p->wide = true;
+  }
+  p->tpr = tpr;
+  p->iters = iters;
+  p->groups = tpr >= kFwdBlockThreads ? 1 : kFwdBlockThreads / tpr;
+  const int wpr = tpr / 64;
+  size_t lds = round16(sizeof(float) * (size_t)p->groups * wpr);
+  if (v == RMSNORM_VARIANT_LDS) lds += (size_t)p->groups * iters * tpr * 16;
+  p->lds = lds;
+  p->grid = ceil_div(M, p->groups);
+  if (p->grid > INT32_MAX) return RMSNORM_ERR_UNSUPPORTED;
+  return RMSNORM_OK;
+}
+
+// Backward: each thread owns at most 2 (register kernel) or 4 (LDS kernel) vectors of a row.
+void bwd_shape(int64_t nv, int* tpr, int* iters) {
+  *tpr = (int)clamp64(pow2_ceil(ceil_div(nv, 2)), 64, 1024);
+  *iters = (int)ceil_div(nv, *tpr);
+}
+
+rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
+                        rmsnorm_variant req, Plan* p) {
+  const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
+  int tpr, iters;
+  bwd_shape(nv_wide, &tpr, &iters);
+  const bool reg_ok = wide_ok && iters <= kBwdRegMaxIters;
+  const bool lds_ok = wide_ok && iters <= kBwdLdsMaxIters;
+  rmsnorm_variant v = req;
+  if (v == RMSNORM_VARIANT_AUTO) {
+    v = reg_ok ? RMSNORM_VARIANT_REGISTERS
+               : (lds_ok ? RMSNORM_VARIANT_LDS : RMSNORM_VARIANT_STREAMING);
+  }
+  if (v == RMSNORM_VARIANT_REGISTERS && !reg_ok) return RMSNORM_ERR_UNSUPPORTED;
+  if (v == RMSNORM_VARIANT_LDS && !lds_ok) return RMSNORM_ERR_UNSUPPORTED;
+  p->variant = v;
+  p->grid = num_partials(M);
+  if (v == RMSNORM_VARIANT_STREAMING) {
+    p->wide = wide_ok;
+    const int64_t nv = wide_ok ? nv_wide : N;
+    bwd_shape(nv, &tpr, &iters);
+    p->tpr = tpr;
+    p->iters = 0;
+    p->groups = 1;
+    p->lds = round16(sizeof(float) * 2 * (tpr / 64));
+    return RMSNORM_OK;
+  }
+  p->wide = true;
+  p->tpr = tpr;
+  p->iters = iters;
+  p->groups = kBwdBlockThreads / tpr;
+  const int wpr = tpr / 64;
+  const int V = vec_elems(dtype);
+  size_t main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr);
+  if (v == RMSNORM_VARIANT_LDS) main_bytes += (size_t)p->groups * 2 * iters * tpr * 16;
+  const size_t combine_bytes = sizeof(float) * (size_t)(p->groups / 2) * tpr * iters * V;
+  p->lds = main_bytes > combine_bytes ? main_bytes : combine_bytes;
+  return RMSNORM_OK;
+}
+
+// ---- launch helpers -------------------------------------------------------------------------------
+template <typename Kernel, typename Args>
+rmsnorm_status launch(Kernel k, int64_t grid, int block, size_t lds, hipStream_t stream,
+                      const Args& args) {
+  if (lds > 65536) {
+    int limit = 0;
+    const rmsnorm_status st = lds_limit(&limit);
+    if (st != RMSNORM_OK) return st;
+    if (lds > (size_t)limit) return RMSNORM_ERR_UNSUPPORTED;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return RMSNORM_ERR_HIP;
+  }
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3((unsigned)block), lds, stream, args);
+  return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+}
+
+template <DT D, bool TWICE>
+rmsnorm_status fwd_dispatch(const Plan& p, const FwdArgs& a, hipStream_t s) {
+  const int block = p.groups * p.tpr;
+  if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    return p.wide ? launch(fwd_stream_kernel<D, true, TWICE>, p.grid, block, p.lds, s, a)
+                  : launch(fwd_stream_kernel<D, false, TWICE>, p.grid, block, p.lds, s, a);
+  }
+  const bool lds = p.variant == RMSNORM_VARIANT_LDS;
+#define RMSN_FWD_CASE(IT)                                                                  \
+  case IT:                                                                                 \
+    return lds ? launch(fwd_rows_kernel<D, IT, TWICE, true>, p.grid, block, p.lds, s, a)   \
+               : launch(fwd_rows_kernel<D, IT, TWICE, false>, p.grid, block, p.lds, s, a);
+  switch (p.iters) {
+    RMSN_FWD_CASE(1)
+    RMSN_FWD_CASE(2)
+    RMSN_FWD_CASE(3)
+    RMSN_FWD_CASE(4)
+    RMSN_FWD_CASE(5)
+    RMSN_FWD_CASE(6)
+    RMSN_FWD_CASE(7)
+    RMSN_FWD_CASE(8)
+    default:
+      return RMSNORM_ERR_UNSUPPORTED;
+  }
+#undef RMSN_FWD_CASE
+}
+
+template <DT D>
+rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
+  const int block = p.groups * p.tpr;
+  if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    return p.wide ? launch(bwd_stream_kernel<D, true>, p.grid, block, p.lds, s, a)
+                  : launch(bwd_stream_kernel<D, false>, p.grid, block, p.lds, s, a);
+  }
+  if (p.variant == RMSNORM_VARIANT_LDS) {
+    switch (p.iters) {
+      case 1: return launch(bwd_lds_kernel<D, 1>, p.grid, block, p.lds, s, a);
+      case 2: return launch(bwd_lds_kernel<D, 2>, p.grid, block, p.lds, s, a);
+      case 3: return launch(bwd_lds_kernel<D, 3>, p.grid, block, p.lds, s, a);
+      case 4: return launch(bwd_lds_kernel<D, 4>, p.grid, block, p.lds, s, a);
+      default: return RMSNORM_ERR_UNSUPPORTED;
+    }
+  }
+  switch (p.iters) {
+    case 1: return launch(bwd_rows_kernel<D, 1>, p.grid, block, p.lds, s, a);
+    case 2: return launch(bwd_rows_kernel<D, 2>, p.grid, block, p.lds, s, a);
+    default: return RMSNORM_ERR_UNSUPPORTED;
+  }
+}
+
+// ---- validation -----------------------------------------------------------------------------------
+rmsnorm_status check_common(int64_t M, int64_t N, int dtype, float eps, float offset) {
+  if (!dtype_ok(dtype)) return RMSNORM_ERR_INVALID_ARG;
+  if (M < 0 || N < 1) return RMSNORM_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(offset)) return RMSNORM_ERR_INVALID_ARG;
+  if (N > RMSNORM_MAX_N) return RMSNORM_ERR_UNSUPPORTED;
+  return RMSNORM_OK;
+}
+
+rmsnorm_status check_matrix(const void* p, int64_t ld, int64_t M, int64_t N, int eb) {
+  if (ld < N) return RMSNORM_ERR_INVALID_ARG;
+  if (!extent_ok(M, N, ld)) return RMSNORM_ERR_INVALID_ARG;
+  if (M > 0 && p == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(p, (uintptr_t)eb)) return RMSNORM_ERR_MISALIGNED;
+  return RMSNORM_OK;
+}
+
+bool wide_fits(const void* p, int64_t ld, int eb) {
+  return aligned(p, 16) && ((ld * eb) % 16 == 0);
+}
+
+rmsnorm_status fwd_impl(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
+                        float* rstd, int64_t M, int64_t N, rmsnorm_dtype dtype, float eps,
+                        float offset, rmsnorm_rounding rounding, rmsnorm_variant variant,
+                        void* stream) {
+  rmsnorm_status st = check_common(M, N, dtype, eps, offset);
+  if (st != RMSNORM_OK) return st;
+  if (!rounding_ok(rounding) || !variant_ok(variant)) return RMSNORM_ERR_INVALID_ARG;
+  const int eb = elem_bytes(dtype);
+  if ((st = check_matrix(x, ldx, M, N, eb)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(y, ldy, M, N, eb)) != RMSNORM_OK) return st;
+  if (M > 0 && w == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(w, (uintptr_t)eb) || !aligned(rstd, 4)) return RMSNORM_ERR_MISALIGNED;
+  const bool wide = wide_fits(x, ldx, eb) && wide_fits(y, ldy, eb) && aligned(w, 16);
+  Plan p;
+  if ((st = plan_fwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  if (M == 0) return RMSNORM_OK;
+
+  FwdArgs a;
+  a.x = x; a.w = w; a.y = y; a.rstd = rstd;
+  a.ldx = ldx; a.ldy = ldy; a.M = M; a.N = (int)N;
+  a.tpr = p.tpr; a.groups = p.groups; a.eps = eps; a.offset = offset;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool twice = rounding == RMSNORM_ROUND_TWICE;
+  switch (dtype) {
+    case RMSNORM_DTYPE_F32:  // the two conventions coincide for float32 I/O
+      return fwd_dispatch<DT::F32, false>(p, a, s);
+    case RMSNORM_DTYPE_F16:
+      return twice ? fwd_dispatch<DT::F16, true>(p, a, s) : fwd_dispatch<DT::F16, false>(p, a, s);
+    case RMSNORM_DTYPE_BF16:
+      return twice ? fwd_dispatch<DT::BF16, true>(p, a, s) : fwd_dispatch<DT::BF16, false>(p, a, s);
+  }
+  return RMSNORM_ERR_INVALID_ARG;
+}
+
+size_t workspace_bytes(int64_t M, int64_t N) {
+  return (size_t)num_partials(M) * (size_t)partial_ld(N) * sizeof(float);
+}
+
+rmsnorm_status check_bwd_rows(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                              const void* w, const float* rstd, void* dx, int64_t lddx,
+                              void* workspace, size_t workspace_bytes_given, int64_t M, int64_t N,
+                              int dtype, float offset, int variant) {
+  rmsnorm_status st = check_common(M, N, dtype, 0.f, offset);
+  if (st != RMSNORM_OK) return st;
+  if (!variant_ok(variant)) return RMSNORM_ERR_INVALID_ARG;
+  const int eb = elem_bytes((rmsnorm_dtype)dtype);
+  if ((st = check_matrix(dy, lddy, M, N, eb)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(x, ldx, M, N, eb)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(dx, lddx, M, N, eb)) != RMSNORM_OK) return st;
+  if (M > 0 && (w == nullptr || rstd == nullptr || workspace == nullptr))
+    return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(w, (uintptr_t)eb) || !aligned(rstd, 4) || !aligned(workspace, 16))
+    return RMSNORM_ERR_MISALIGNED;
+  if (workspace_bytes_given < workspace_bytes(M, N)) return RMSNORM_ERR_WORKSPACE;
+  return RMSNORM_OK;
+}
+
+rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                             const void* w, const float* rstd, void* dx, int64_t lddx,
+                             void* workspace, size_t workspace_bytes_given, int64_t M, int64_t N,
+                             rmsnorm_dtype dtype, float offset, rmsnorm_variant variant,
+                             void* stream) {
+  rmsnorm_status st = check_bwd_rows(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace,
+                                     workspace_bytes_given, M, N, dtype, offset, variant);
+  if (st != RMSNORM_OK) return st;
+  const int eb = elem_bytes(dtype);
+  const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) && wide_fits(dx, lddx, eb) &&
+                    aligned(w, 16);
+  Plan p;
+  if ((st = plan_bwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  if (M == 0) return RMSNORM_OK;
+
+  BwdArgs a;
+  a.dy = dy; a.x = x; a.w = w; a.rstd = rstd; a.dx = dx;
+  a.part = static_cast<float*>(workspace);
+  a.lddy = lddy; a.ldx = ldx; a.lddx = lddx; a.M = M;
+  a.N = (int)N; a.ldp = (int)partial_ld(N); a.P = (int)num_partials(M);
+  a.tpr = p.tpr; a.groups = p.groups; a.offset = offset;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case RMSNORM_DTYPE_F32: return bwd_dispatch<DT::F32>(p, a, s);
+    case RMSNORM_DTYPE_F16: return bwd_dispatch<DT::F16>(p, a, s);
+    case RMSNORM_DTYPE_BF16: return bwd_dispatch<DT::BF16>(p, a, s);
+  }
+  return RMSNORM_ERR_INVALID_ARG;
+}
+
+rmsnorm_status dw_reduce_impl(const void* workspace, size_t workspace_bytes_given, float* dw,
+                              int64_t M, int64_t N, rmsnorm_dtype dtype, void* stream) {
+  rmsnorm_status st = check_common(M, N, dtype, 0.f, 0.f);
+  if (st != RMSNORM_OK) return st;
+  if (dw == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (M > 0 && workspace == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(dw, 4) || !aligned(workspace, 16)) return RMSNORM_ERR_MISALIGNED;
+  if (workspace_bytes_given < workspace_bytes(M, N)) return RMSNORM_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s, dw,
+                       (int)N);
+    return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+  }
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)ceil_div(N, 64)), dim3(1024), 0, s,
+                     static_cast<const float*>(workspace), partial_ld(N), (int)num_partials(M),
+                     (int)N, dw);
+  return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+}
+
+rmsnorm_status bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w,
+                        const float* rstd, void* dx, int64_t lddx, float* dw, void* workspace,
+                        size_t workspace_bytes_given, int64_t M, int64_t N, rmsnorm_dtype dtype,
+                        float eps, float offset, rmsnorm_rounding rounding,
+                        rmsnorm_variant variant, void* stream) {
+  // Validate everything (both stages) before enqueuing anything.
+  rmsnorm_status st = check_common(M, N, dtype, eps, offset);
+  if (st != RMSNORM_OK) return st;
+  if (!rounding_ok(rounding)) return RMSNORM_ERR_INVALID_ARG;
+  if ((st = check_bwd_rows(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace, workspace_bytes_given,
+                           M, N, dtype, offset, variant)) != RMSNORM_OK)
+    return st;
+  if (dw == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(dw, 4)) return RMSNORM_ERR_MISALIGNED;
+  {
+    const int eb = elem_bytes(dtype);
+    const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) &&
+                      wide_fits(dx, lddx, eb) && aligned(w, 16);
+    Plan p;
+    if ((st = plan_bwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  }
+  st = bwd_rows_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace, workspace_bytes_given, M, N,
+                     dtype, offset, variant, stream);
+  if (st != RMSNORM_OK) return st;
+  return dw_reduce_impl(workspace, workspace_bytes_given, dw, M, N, dtype, stream);
+}
+
+}  // namespace
+
+// ---- exported C interface -------------------------------------------------------------------------
+extern "C" {
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_fwd(
+    const void* x, int64_t ldx, const void* w, void* y, int64_t ldy, float* rstd, int64_t M,
+    int64_t N, rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
+    void* stream) {
+  return fwd_impl(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, rounding,
+                  RMSNORM_VARIANT_AUTO, stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_fwd_variant(
+    const void* x, int64_t ldx, const void* w, void* y, int64_t ldy, float* rstd, int64_t M,
+    int64_t N, rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
+    rmsnorm_variant variant, void* stream) {
+  return fwd_impl(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, rounding, variant, stream);
+}
+
+__attribute__((visibility("default"))) size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N,
+                                                                          rmsnorm_dtype dtype) {
+  if (!dtype_ok(dtype) || M <= 0 || N < 1 || N > RMSNORM_MAX_N) return 0;
+  return workspace_bytes(M, N);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd(
+    const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, const float* rstd,
+    void* dx, int64_t lddx, float* dw, void* workspace, size_t workspace_bytes_given, int64_t M,
+    int64_t N, rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
+    void* stream) {
+  return bwd_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, workspace, workspace_bytes_given, M, N,
+                  dtype, eps, offset, rounding, RMSNORM_VARIANT_AUTO, stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_variant(
+    const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, const float* rstd,
+    void* dx, int64_t lddx, float* dw, void* workspace, size_t workspace_bytes_given, int64_t M,
+    int64_t N, rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
+    rmsnorm_variant variant, void* stream) {
+  return bwd_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, workspace, workspace_bytes_given, M, N,
+                  dtype, eps, offset, rounding, variant, stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_rows(
+    const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, const float* rstd,
+    void* dx, int64_t lddx, void* workspace, size_t workspace_bytes_given, int64_t M, int64_t N,
+    rmsnorm_dtype dtype, float offset, rmsnorm_variant variant, void* stream) {
+  return bwd_rows_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace, workspace_bytes_given, M, N,
+                       dtype, offset, variant, stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_dw_reduce(
+    const void* workspace, size_t workspace_bytes_given, float* dw, int64_t M, int64_t N,
+    rmsnorm_dtype dtype, void* stream) {
+  return dw_reduce_impl(workspace, workspace_bytes_given, dw, M, N, dtype, stream);
+}
+
+__attribute__((visibility("default"))) const char* rmsnorm_status_string(rmsnorm_status s) {
+  switch (s) {
+    case RMSNORM_OK: return "ok";
+    case RMSNORM_ERR_INVALID_ARG: return "invalid argument";
+    case RMSNORM_ERR_UNSUPPORTED: return "unsupported size or variant";
+    case RMSNORM_ERR_MISALIGNED: return "misaligned pointer";
+    case RMSNORM_ERR_WORKSPACE: return "workspace too small";
+    case RMSNORM_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+__attribute__((visibility("default"))) int rmsnorm_abi_version(void) {
+  return LIBRMSNORM_ABI_VERSION;
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+// Shared device helpers for the RMSNorm kernels (gfx950, wave64).
+//
+// Element I/O: 16-bit types travel as 16-byte vectors of 8 elements and fp32 as 16-byte vectors
+// of 4; the element-wise ("narrow") path moves one element at a time and serves any alignment.
+// Upcasts are exact; downcasts are round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32 under the default round mode).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsn {
+
+enum class DT : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <DT D> struct Elem;
+template <> struct Elem<DT::F32> { using S = float; static constexpr int VEC = 4; };
+template <> struct Elem<DT::F16> { using S = uint16_t; static constexpr int VEC = 8; };
+template <> struct Elem<DT::BF16> { using S = uint16_t; static constexpr int VEC = 8; };
+
+// The narrowing conversions below take their float32 operand through `materialize`: an empty asm
+// with a register constraint (no instruction is emitted). It stops the backend from folding a
+// float32 multiply into the conversion (gfx950 v_fma_mixlo_f16 rounds the exact product once to
+// binary16), so every product is rounded to float32 first and then to the 16-bit type, as the
+// contract states: y = T(fl(a * b)).
+__device__ __forceinline__ float materialize(float v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// ---- scalar conversions ------------------------------------------------------------------------
+template <DT D> __device__ __forceinline__ float to_f32(typename Elem<D>::S s);
+template <> __device__ __forceinline__ float to_f32<DT::F32>(float s) { return s; }
+template <> __device__ __forceinline__ float to_f32<DT::F16>(uint16_t s) {
+  return (float)__builtin_bit_cast(_Float16, s);
+}
+template <> __device__ __forceinline__ float to_f32<DT::BF16>(uint16_t s) {
+  return __uint_as_float((uint32_t)s << 16);
+}
+
+template <DT D> __device__ __forceinline__ typename Elem<D>::S from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<DT::F32>(float f) { return f; }
+template <> __device__ __forceinline__ uint16_t from_f32<DT::F16>(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)materialize(f));
+}
+template <> __device__ __forceinline__ uint16_t from_f32<DT::BF16>(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)materialize(f));
+}
+
+// ---- packed pairs (one 32-bit word holds two 16-bit elements) -----------------------------------
+template <DT D> __device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi);
+template <> __device__ __forceinline__ void unpack2<DT::BF16>(uint32_t w, float& lo, float& hi) {
+  lo = __uint_as_float(w << 16);
+  hi = __uint_as_float(w & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void unpack2<DT::F16>(uint32_t w, float& lo, float& hi) {
+  f32x2_t f = __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+  lo = f.x;
+  hi = f.y;
+}
+template <DT D> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<DT::BF16>(float lo, float hi) {
+  f32x2_t f = {materialize(lo), materialize(hi)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+template <> __device__ __forceinline__ uint32_t pack2<DT::F16>(float lo, float hi) {
+  f32x2_t f = {materialize(lo), materialize(hi)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+}
+
+// ---- vector I/O --------------------------------------------------------------------------------
+// VecIO<D, true>: 16-byte vectors (requires 16-byte aligned addresses).
+// VecIO<D, false>: single elements.
+template <DT D, bool WIDE> struct VecIO;
+
+template <DT D> struct VecIO<D, true> {
+  using S = typename Elem<D>::S;
+  static constexpr int V = Elem<D>::VEC;
+  using Raw = uint4;
+  static __device__ __forceinline__ Raw zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  static __device__ __forceinline__ Raw load(const S* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+  static __device__ __forceinline__ Raw load_part(const S* p, int n) {
+    S tmp[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) tmp[i] = (i < n) ? p[i] : S(0);
+    return __builtin_bit_cast(uint4, tmp);
+  }
+  static __device__ __forceinline__ void store(S* p, Raw r) { *reinterpret_cast<uint4*>(p) = r; }
+  static __device__ __forceinline__ void store_part(S* p, Raw r, int n) {
+    S tmp[V];
+    __builtin_memcpy(tmp, &r, sizeof(r));
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (i < n) p[i] = tmp[i];
+  }
+  static __device__ __forceinline__ void unpack(const Raw& r, float (&f)[V]) {
+    if constexpr (D == DT::F32) {
+      f[0] = __uint_as_float(r.x);
+      f[1] = __uint_as_float(r.y);
+      f[2] = __uint_as_float(r.z);
+      f[3] = __uint_as_float(r.w);
+    } else {
+      unpack2<D>(r.x, f[0], f[1]);
+      unpack2<D>(r.y, f[2], f[3]);
+      unpack2<D>(r.z, f[4], f[5]);
+      unpack2<D>(r.w, f[6], f[7]);
+    }
+  }
+  static __device__ __forceinline__ Raw pack(const float (&f)[V]) {
+    if constexpr (D == DT::F32) {
+      return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                        __float_as_uint(f[3]));
+    } else {
+      return make_uint4(pack2<D>(f[0], f[1]), pack2<D>(f[2], f[3]), pack2<D>(f[4], f[5]),
+                        pack2<D>(f[6], f[7]));
+    }
+  }
+};
+
+template <DT D> struct VecIO<D, false> {
+  using S = typename Elem<D>::S;
+  static constexpr int V = 1;
+  using Raw = S;
+  static __device__ __forceinline__ Raw zero() { return S(0); }
+  static __device__ __forceinline__ Raw load(const S* p) { return *p; }
+  static __device__ __forceinline__ Raw load_part(const S* p, int) { return *p; }
+  static __device__ __forceinline__ void store(S* p, Raw r) { *p = r; }
+  static __device__ __forceinline__ void store_part(S* p, Raw r, int) { *p = r; }
+  static __device__ __forceinline__ void unpack(const Raw& r, float (&f)[1]) { f[0] = to_f32<D>(r); }
+  static __device__ __forceinline__ Raw pack(const float (&f)[1]) { return from_f32<D>(f[0]); }
+};
+
+// float -> T -> float (the inner cast of the round-twice convention); identity for fp32.
+template <DT D> __device__ __forceinline__ float round_trip(float f) {
+  if constexpr (D == DT::F32) {
+    return f;
+  } else {
+    return to_f32<D>(from_f32<D>(f));
+  }
+}
+
+// ---- reductions ----------------------------------------------------------------------------------
+// Butterfly sum over the 64 lanes of a wave. Every lane ends with the same bits: at each level the
+// two partners add the same two values, and IEEE addition is commutative.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Workgroup barrier that orders LDS only: outstanding global loads stay in flight across it, so a
+// row prefetched before the barrier keeps streaming while the current row is reduced.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Sum of a value over the TPR threads of one row group (TPR = 64 * wpr). Waves publish their wave
+// sums in red[slot * wpr + wave] and every thread adds them in wave order, so all threads of the
+// group end with the same bits. Must be reached by every thread of the block when wpr > 1.
+__device__ __forceinline__ float group_sum(float v, float* red, int wpr, int tl) {
+  v = wave_sum(v);
+  if (wpr > 1) {
+    if ((tl & 63) == 0) red[tl >> 6] = v;
+    lds_barrier();
+    v = red[0];
+    for (int k = 1; k < wpr; ++k) v += red[k];
+  }
+  return v;
+}
+
+}  // namespace rmsn

@@ -1,0 +1,167 @@
+// RMSNorm forward kernels.
+//
+// Per row (blog post "Den dolda avrundningen i RMSNorm", sections "En välbekant operation" and
+// "Två ställen att avrunda"):
+//   rstd = 1 / sqrt(sum(x^2) / N + eps)           float32; epsilon under the root
+//   xhat = x * rstd                                 formed first
+//   y    = T(float(T(xhat)) * g)   (round twice)    or   T(xhat * g)   (round once),  g = offset + w
+//
+// Work decomposition: a row is owned by a group of TPR threads (TPR = 64 * wpr, one or more
+// wavefronts); a block holds `groups` such rows. Thread tl of a group owns the 16-byte vectors
+// it * TPR + tl (it = 0 .. ITERS-1) of its row, so every wavefront load is one contiguous
+// 64 x 16 B = 1 KiB segment. Summation order of the squares is fixed by this mapping: per thread,
+// two accumulators (even / odd element of each vector) over it = 0, 1, ...; then the wave
+// butterfly; then the waves of the row in order. All three kernel families below use the same
+// mapping for the same TPR, so their rstd and y are bit-identical.
+#pragma once
+
+#include "rmsnorm_common.hpp"
+
+namespace rmsn {
+
+struct FwdArgs {
+  const void* x;
+  const void* w;
+  void* y;
+  float* rstd;  // may be null
+  int64_t ldx, ldy, M;
+  int N;
+  int tpr;     // threads per row, multiple of 64
+  int groups;  // rows per block
+  float eps, offset;
+};
+
+template <DT D, bool TWICE, int V>
+__device__ __forceinline__ void apply_gain(const float (&xf)[V], const float (&wf)[V], float rs,
+                                           float offset, float (&yf)[V]) {
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const float xh = xf[e] * rs;
+    const float g = offset + wf[e];
+    yf[e] = TWICE ? round_trip<D>(xh) * g : xh * g;
+  }
+}
+
+// Row held in registers (STAGE_LDS = false) or staged in LDS (true) between the two passes.
+template <DT D, int ITERS, bool TWICE, bool STAGE_LDS>
+__global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
+  using IO = VecIO<D, true>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+
+  float* red = reinterpret_cast<float*>(smem) + grp * wpr;
+  Raw* stage = smem + ((a.groups * wpr + 3) >> 2) + (size_t)grp * ITERS * TPR;
+
+  const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+  Raw raw[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    Raw r = IO::zero();
+    if (valid) {
+      if (col + V <= N) r = IO::load(xr + col);
+      else if (col < N) r = IO::load_part(xr + col, N - col);
+    }
+    raw[it] = r;
+  }
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    float f[V];
+    IO::unpack(raw[it], f);
+#pragma unroll
+    for (int e = 0; e < V; e += 2) {
+      acc0 = __builtin_fmaf(f[e], f[e], acc0);
+      acc1 = __builtin_fmaf(f[e + 1], f[e + 1], acc1);
+    }
+    if constexpr (STAGE_LDS) stage[it * TPR + tl] = raw[it];
+  }
+  const float ss = group_sum(acc0 + acc1, red, wpr, tl);
+  const float rs = 1.0f / __builtin_sqrtf(ss / (float)N + a.eps);
+  if (!valid) return;
+  if (tl == 0 && a.rstd) a.rstd[row] = rs;
+
+  const S* wr = static_cast<const S*>(a.w);
+  S* yr = static_cast<S*>(a.y) + row * a.ldy;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    if (col >= N) continue;
+    const bool full = col + V <= N;
+    const Raw r = STAGE_LDS ? stage[it * TPR + tl] : raw[it];
+    const Raw wv = full ? IO::load(wr + col) : IO::load_part(wr + col, N - col);
+    float xf[V], wf[V], yf[V];
+    IO::unpack(r, xf);
+    IO::unpack(wv, wf);
+    apply_gain<D, TWICE, V>(xf, wf, rs, a.offset, yf);
+    const Raw out = IO::pack(yf);
+    if (full) IO::store(yr + col, out);
+    else IO::store_part(yr + col, out, N - col);
+  }
+}
+
+// Any N and any alignment: the elementwise pass reads x again (from cache) instead of keeping it.
+// WIDE selects 16-byte vectors or single elements.
+template <DT D, bool WIDE, bool TWICE>
+__global__ void __launch_bounds__(1024) fwd_stream_kernel(FwdArgs a) {
+  using IO = VecIO<D, WIDE>;
+  using S = typename IO::S;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int nv = (N + V - 1) / V;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+  float* red = reinterpret_cast<float*>(smem) + grp * wpr;
+
+  const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+  float acc0 = 0.f, acc1 = 0.f;
+  if (valid) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      const auto r = (col + V <= N) ? IO::load(xr + col) : IO::load_part(xr + col, N - col);
+      float f[V];
+      IO::unpack(r, f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (e & 1) acc1 = __builtin_fmaf(f[e], f[e], acc1);
+        else acc0 = __builtin_fmaf(f[e], f[e], acc0);
+      }
+    }
+  }
+  const float ss = group_sum(acc0 + acc1, red, wpr, tl);
+  const float rs = 1.0f / __builtin_sqrtf(ss / (float)N + a.eps);
+  if (!valid) return;
+  if (tl == 0 && a.rstd) a.rstd[row] = rs;
+
+  const S* wr = static_cast<const S*>(a.w);
+  S* yr = static_cast<S*>(a.y) + row * a.ldy;
+  for (int v = tl; v < nv; v += TPR) {
+    const int col = v * V;
+    const bool full = col + V <= N;
+    const auto r = full ? IO::load(xr + col) : IO::load_part(xr + col, N - col);
+    const auto wv = full ? IO::load(wr + col) : IO::load_part(wr + col, N - col);
+    float xf[V], wf[V], yf[V];
+    IO::unpack(r, xf);
+    IO::unpack(wv, wf);
+    apply_gain<D, TWICE, V>(xf, wf, rs, a.offset, yf);
+    const auto out = IO::pack(yf);
+    if (full) IO::store(yr + col, out);
+    else IO::store_part(yr + col, out, N - col);
+  }
+}
+
+}  // namespace rmsn

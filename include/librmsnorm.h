@@ -1,0 +1,174 @@
+/*
+ * librmsnorm — row-wise RMSNorm forward and backward for AMD Instinct MI355X (gfx950).
+ *
+ * C interface. Every pointer argument is a device pointer owned by the caller; the library
+ * allocates nothing, keeps no state between calls and never synchronizes: work is enqueued on the
+ * caller's HIP stream and its results are valid once that stream reaches this point. No C++
+ * exception crosses this interface and nothing aborts; failures come back as rmsnorm_status.
+ *
+ * The operation (blog post "Den dolda avrundningen i RMSNorm", precisit.com, section
+ * "En välbekant operation"): for each row r of an [M, N] matrix x,
+ *
+ *     rstd_r = 1 / sqrt( (1/N) * sum_j x_rj^2 + eps )      epsilon under the root
+ *     xhat   = x * rstd                                     formed first, in float32
+ *     g_j    = offset + w_j                                 offset 0: Llama gain, 1: Gemma gain
+ *
+ * and the output y is rounded to the I/O type T in one of two ways (same post, section
+ * "Två ställen att avrunda"; section "Vilken konvention hör till modellen?" ties the first to
+ * Llama and the second to Gemma):
+ *
+ *     RMSNORM_ROUND_TWICE:  y = T( float(T(xhat)) * g )     the normalized value is cast first
+ *     RMSNORM_ROUND_ONCE:   y = T( xhat * g )               one cast, at the store
+ *
+ * where every product is one float32 multiply and T(.) is round-to-nearest-even. For T = float32
+ * the two conventions coincide. Statistics are float32 (sums of float32 values in an order of the
+ * library's choosing); the per-row rstd is cached in float32 for the backward, which reads it back
+ * instead of recomputing it (Liger-Kernel pull request 92, "feat: correct casts in RMSNorm to match
+ * references": the inverse RMS cache and the weight gradient are kept in float32).
+ *
+ * Backward (the derivative of the composed formula, as in candle pull request 4059, "Add backward
+ * passes to the fused rms_norm, layer_norm and softmax_last_dim ops"; inputs upcast to float32 on
+ * load and every reduction in float32, as in Liger-Kernel pull request 1608, "fix(group_norm): keep
+ * the backward statistics and reductions in fp32"):
+ *
+ *     xhat = x * rstd,  gdy = g * dy,  c = (1/N) * sum_j gdy_j * xhat_j
+ *     dx   = T( rstd * (gdy - xhat * c) )          each operation one float32 operation
+ *     dw_j = sum_r dy_rj * xhat_rj                  float32, summed in a fixed order
+ *
+ * The backward is the same for both rounding conventions. dw is produced as per-block float32
+ * partial column sums in a caller-provided workspace followed by a second pass that adds the
+ * partials in a fixed order: no floating-point atomics, so results are bit-reproducible run to run
+ * and independent of the device's compute-unit count.
+ *
+ * Layout: x, y, dy and dx are row-major [M, N] with unit column stride and a row stride ld* (in
+ * elements, ld* >= N; non-contiguous gradients are handled through the row stride). w is [N].
+ * x, w, y, dy and dx share one dtype (the comparison in the blog post's footnote 6 assumes weights
+ * stored in the input dtype). rstd is float32 [M]; dw is float32 [N]. Outputs must not overlap
+ * inputs. The fast paths use 16-byte accesses; when a base pointer or a row stride does not allow
+ * them the call still succeeds through an element-wise path.
+ */
+#ifndef LIBRMSNORM_H
+#define LIBRMSNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LIBRMSNORM_ABI_VERSION 1
+/* Largest supported row width N. */
+#define RMSNORM_MAX_N (1 << 24)
+
+typedef enum rmsnorm_dtype {
+  RMSNORM_DTYPE_F32 = 0,
+  RMSNORM_DTYPE_F16 = 1,  /* IEEE binary16 */
+  RMSNORM_DTYPE_BF16 = 2  /* bfloat16 */
+} rmsnorm_dtype;
+
+typedef enum rmsnorm_rounding {
+  RMSNORM_ROUND_ONCE = 0,  /* y = T(xhat * g)                (Gemma convention) */
+  RMSNORM_ROUND_TWICE = 1  /* y = T(float(T(xhat)) * g)      (Llama convention) */
+} rmsnorm_rounding;
+
+/* Kernel family. AUTO picks by dtype and N. The others force one family, for consistency tests
+ * and measurements; a forced family that cannot serve the arguments returns
+ * RMSNORM_ERR_UNSUPPORTED with nothing launched.
+ *   REGISTERS  a row lives in registers between the reduction and the elementwise pass
+ *   LDS        a row is staged in LDS between the two passes (same thread-to-element mapping and
+ *              summation order as REGISTERS, so results are bit-identical to it)
+ *   STREAMING  the elementwise pass reads the row again from memory; serves any N and any
+ *              alignment (element-wise accesses when 16-byte accesses are not possible)   */
+typedef enum rmsnorm_variant {
+  RMSNORM_VARIANT_AUTO = 0,
+  RMSNORM_VARIANT_REGISTERS = 1,
+  RMSNORM_VARIANT_LDS = 2,
+  RMSNORM_VARIANT_STREAMING = 3
+} rmsnorm_variant;
+
+typedef enum rmsnorm_status {
+  RMSNORM_OK = 0,
+  RMSNORM_ERR_INVALID_ARG = 1,  /* null pointer, negative size, ld < N, unknown enum, bad eps */
+  RMSNORM_ERR_UNSUPPORTED = 2,  /* N > RMSNORM_MAX_N, or a forced variant that cannot serve */
+  RMSNORM_ERR_MISALIGNED = 3,   /* a pointer not aligned to its element size (4 B for float32
+                                   buffers, 2 B for 16-bit ones; 16 B for the workspace) */
+  RMSNORM_ERR_WORKSPACE = 4,    /* workspace smaller than rmsnorm_bwd_workspace_bytes() */
+  RMSNORM_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} rmsnorm_status;
+
+/* Forward. Computes y [M, N] (dtype) and, when rstd is not NULL, the per-row float32 rstd [M].
+ *   x, ldx     input rows, row stride in elements (>= N)
+ *   w          gain weights [N], same dtype as x
+ *   y, ldy     output rows, row stride in elements (>= N)
+ *   rstd       float32 [M] cache for the backward, or NULL to skip writing it
+ *   eps        >= 0 and finite; added to the mean of squares under the root
+ *   offset     finite; the gain is offset + w (0: Llama, 1: Gemma)
+ *   rounding   RMSNORM_ROUND_ONCE or RMSNORM_ROUND_TWICE (no effect for float32)
+ *   stream     hipStream_t to enqueue on (NULL = the null stream)
+ * M = 0 is a no-op. All argument checks run before any HIP call; on an error nothing is launched. */
+rmsnorm_status rmsnorm_fwd(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
+                           float* rstd, int64_t M, int64_t N, rmsnorm_dtype dtype, float eps,
+                           float offset, rmsnorm_rounding rounding, void* stream);
+
+/* rmsnorm_fwd with an explicit kernel family (see rmsnorm_variant). */
+rmsnorm_status rmsnorm_fwd_variant(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
+                                   float* rstd, int64_t M, int64_t N, rmsnorm_dtype dtype,
+                                   float eps, float offset, rmsnorm_rounding rounding,
+                                   rmsnorm_variant variant, void* stream);
+
+/* Bytes of device workspace rmsnorm_bwd needs for an [M, N] problem: the float32 partial column
+ * sums of dw, one row per block of rows. A pure function of (M, N, dtype): it makes no HIP call
+ * and does not depend on the device. Returns 0 for M = 0 and for invalid sizes. */
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype dtype);
+
+/* Backward. Computes dx [M, N] (dtype) and dw [N] (float32, fully overwritten).
+ *   dy, lddy      upstream gradient rows
+ *   x, ldx        the forward's input rows
+ *   w             gain weights [N]
+ *   rstd          float32 [M] written by rmsnorm_fwd for the same x and eps (required, not NULL)
+ *   dx, lddx      input-gradient rows
+ *   dw            float32 [N] weight gradient (d(offset + w)/dw = 1, so it does not depend on
+ *                 offset)
+ *   workspace     device buffer of at least rmsnorm_bwd_workspace_bytes(M, N, dtype) bytes,
+ *                 16-byte aligned; its contents on entry do not matter and are clobbered
+ *   eps, rounding validated for symmetry with the forward; the backward reads rstd instead of
+ *                 recomputing it and is the same for both rounding conventions
+ * M = 0 writes dw = 0. All argument checks run before any HIP call. */
+rmsnorm_status rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                           const void* w, const float* rstd, void* dx, int64_t lddx, float* dw,
+                           void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                           rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
+                           void* stream);
+
+/* rmsnorm_bwd with an explicit kernel family. */
+rmsnorm_status rmsnorm_bwd_variant(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                                   const void* w, const float* rstd, void* dx, int64_t lddx,
+                                   float* dw, void* workspace, size_t workspace_bytes, int64_t M,
+                                   int64_t N, rmsnorm_dtype dtype, float eps, float offset,
+                                   rmsnorm_rounding rounding, rmsnorm_variant variant,
+                                   void* stream);
+
+/* The two stages of rmsnorm_bwd, exported so each kernel can be enqueued (and timed) on its own.
+ * rmsnorm_bwd_rows writes dx and the per-block dw partials into the workspace;
+ * rmsnorm_bwd_dw_reduce adds the partials of the same (M, N, dtype) into dw in a fixed order.
+ * rmsnorm_bwd(...) == rmsnorm_bwd_rows(...) followed by rmsnorm_bwd_dw_reduce(...). */
+rmsnorm_status rmsnorm_bwd_rows(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                                const void* w, const float* rstd, void* dx, int64_t lddx,
+                                void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                                rmsnorm_dtype dtype, float offset, rmsnorm_variant variant,
+                                void* stream);
+rmsnorm_status rmsnorm_bwd_dw_reduce(const void* workspace, size_t workspace_bytes, float* dw,
+                                     int64_t M, int64_t N, rmsnorm_dtype dtype, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* rmsnorm_status_string(rmsnorm_status status);
+
+/* LIBRMSNORM_ABI_VERSION of the built library. */
+int rmsnorm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRMSNORM_H */

@@ -148,3 +148,14 @@ def rmsnorm_bwd(dy, x, w, rstd, *, offset: float = 0.0, dtype: str = "bf16", exa
     if exact:
         return dx, dw
     return rne_to(dx, dtype), rne_f32(dw)
+
+
+def rmsnorm_dw(dy, x, rstd) -> np.ndarray:
+    """Only the weight gradient of ``rmsnorm_bwd``: dw_j = RNE_f32(sum_r dy_rj * fl(x_rj * rstd_r)).
+
+    The same formula as the backward's dw (the tests hold the two equal bit for bit); it skips the
+    input gradient so that full-size matrices stay cheap to check.
+    """
+    xhat = np.asarray(x, np.float32) * np.asarray(rstd, np.float32)[..., None]
+    dw = np.sum(np.asarray(dy, np.float32).astype(np.float64) * xhat.astype(np.float64), axis=0)
+    return rne_f32(dw)

@@ -1,0 +1,126 @@
+"""Comparison of GPU results with the oracle, to the stated tolerances.
+
+Tolerances (the comparison contract):
+
+* rstd (float32 statistic): |gpu - oracle| <= 8 float32 ulps of the oracle value. The GPU sums in
+  its own float32 order and takes a float32 square root; the oracle sums in float64.
+* y, 16-bit I/O:
+  - conditioned: the oracle's elementwise steps re-run from the GPU's own rstd must reproduce y
+    bit for bit (the elementwise arithmetic is fully specified);
+  - unconditioned: >= 99.9 % of elements bit-identical to the oracle's y, every element within
+    2 ulps of T (a 1-ulp change of rstd can move the inner rounding of round twice by one step and
+    the outer one by one more).
+* y, float32 I/O: conditioned bit-exact; unconditioned elementwise relative error <= 2^-20.
+* dx, 16-bit I/O (oracle run from the GPU's rstd): >= 99.9 % bit-identical and every element within
+  1 ulp of T, the ulp taken at max(|dx_oracle|, 2^-12 * rms of the oracle's dx row) so that
+  elements produced by cancellation are judged at the scale of their row.
+* dx, float32 I/O: normwise relative error <= 1e-5.
+* dw (float32): normwise relative error <= 1e-4.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+RSTD_ULPS = 8
+Y_BITEXACT_FRAC = 0.999
+Y_MAX_ULPS = 2
+DX_BITEXACT_FRAC = 0.999
+DX_MAX_ULPS = 1
+DX_FLOOR = 2.0**-12
+F32_Y_REL = 2.0**-20
+F32_DX_NORMWISE = 1e-5
+DW_NORMWISE = 1e-4
+
+
+def to_np(t) -> np.ndarray:
+    """Device tensor -> float32 NumPy array (exact for 16-bit values)."""
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def same_bits(a, b) -> np.ndarray:
+    """Elementwise: equal values (signed zeros distinguished) or NaN in both."""
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    return (np.isnan(a) & np.isnan(b)) | ((a.view(np.uint32) == b.view(np.uint32)))
+
+
+def ulps(a, b, dtype: str, floor=None) -> np.ndarray:
+    """|a - b| in units of the dtype's spacing at |b| (or at ``floor`` where larger)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    ref = np.abs(b)
+    if floor is not None:
+        ref = np.maximum(ref, floor)
+    fmt = "f32" if dtype == "f32" else dtype
+    d = np.abs(a - b) / oracle.ulp_of(ref, fmt)
+    both_nan = np.isnan(a) & np.isnan(b)
+    return np.where(both_nan, 0.0, d)
+
+
+def check_rstd(rstd_gpu, rstd_oracle) -> dict:
+    d = ulps(rstd_gpu, rstd_oracle, "f32")
+    stats = {"rstd_max_ulp": float(np.nanmax(d)) if d.size else 0.0}
+    assert np.all(d <= RSTD_ULPS), stats
+    return stats
+
+
+def check_fwd(y_gpu, rstd_gpu, x, w, *, eps, offset, rounding, dtype, rows=None) -> dict:
+    """Check a forward result (``rows``: the row indices of x that y_gpu/rstd_gpu hold)."""
+    x = np.asarray(x, np.float32)
+    y_o, r_o = oracle.rmsnorm_fwd(x, w, eps=eps, offset=offset, rounding=rounding, dtype=dtype)
+    stats = check_rstd(rstd_gpu, r_o)
+    # conditioned on the GPU's rstd: bit-exact
+    xhat = x * np.asarray(rstd_gpu, np.float32)[:, None]
+    y_c = oracle.apply_gain(xhat, oracle.gain(w, offset), rounding=rounding, dtype=dtype)
+    cond = same_bits(y_gpu, y_c)
+    stats["y_conditioned_bitexact"] = float(cond.mean()) if cond.size else 1.0
+    assert cond.all(), (stats, np.argwhere(~cond)[:5])
+    eq = same_bits(y_gpu, y_o)
+    stats["y_bitexact"] = float(eq.mean()) if eq.size else 1.0
+    if dtype == "f32":
+        rel = np.abs(y_gpu.astype(np.float64) - y_o) / np.maximum(np.abs(y_o), 1e-30)
+        stats["y_max_rel"] = float(rel.max()) if rel.size else 0.0
+        assert np.all((rel <= F32_Y_REL) | eq), stats
+    else:
+        d = ulps(y_gpu, y_o, dtype)
+        stats["y_max_ulp"] = float(d.max()) if d.size else 0.0
+        stats["y_over_1ulp"] = int((d > 1).sum())
+        assert stats["y_bitexact"] >= Y_BITEXACT_FRAC, stats
+        assert np.all(d <= Y_MAX_ULPS), stats
+    return stats
+
+
+def check_dx(dx_gpu, dy, x, w, rstd_gpu, *, offset, dtype) -> dict:
+    dx_o, _ = oracle.rmsnorm_bwd(dy, x, w, rstd_gpu, offset=offset, dtype=dtype)
+    stats = {}
+    if dtype == "f32":
+        num = np.linalg.norm(dx_gpu.astype(np.float64) - dx_o)
+        den = np.linalg.norm(dx_o.astype(np.float64))
+        stats["dx_normwise"] = float(num / den) if den > 0 else float(num)
+        assert stats["dx_normwise"] <= F32_DX_NORMWISE, stats
+        return stats
+    eq = same_bits(dx_gpu, dx_o)
+    stats["dx_bitexact"] = float(eq.mean()) if eq.size else 1.0
+    rms = np.sqrt(np.mean(dx_o.astype(np.float64) ** 2, axis=1, keepdims=True))
+    d = ulps(dx_gpu, dx_o, dtype, floor=DX_FLOOR * rms)
+    stats["dx_max_ulp_floored"] = float(d.max()) if d.size else 0.0
+    stats["dx_max_ulp_raw"] = float(ulps(dx_gpu, dx_o, dtype).max()) if d.size else 0.0
+    assert stats["dx_bitexact"] >= DX_BITEXACT_FRAC, stats
+    assert np.all(d <= DX_MAX_ULPS), stats
+    return stats
+
+
+def check_dw(dw_gpu, dw_oracle) -> dict:
+    num = np.linalg.norm(np.asarray(dw_gpu, np.float64) - dw_oracle)
+    den = np.linalg.norm(np.asarray(dw_oracle, np.float64))
+    stats = {"dw_normwise": float(num / den) if den > 0 else float(num)}
+    assert stats["dw_normwise"] <= DW_NORMWISE, stats
+    return stats
+
+
+def oracle_dw(dy, x, w, rstd_gpu, *, offset, dtype) -> np.ndarray:
+    _, dw = oracle.rmsnorm_bwd(dy, x, w, rstd_gpu, offset=offset, dtype=dtype)
+    return dw

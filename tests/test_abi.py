@@ -1,0 +1,132 @@
+"""The C interface on the CPU: the library loads, exports every declared symbol, and rejects bad
+arguments with the documented status before making any HIP call (no GPU is touched here)."""
+import ctypes
+import os
+
+import pytest
+
+import bwd_precision_numerics_amd as rn
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rn.LIB_PATH),
+                                reason="librmsnorm.so not built (run __graft_entry__.build())")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, 1, 2, 3, 4
+F32, F16, BF16 = 0, 1, 2
+ONCE, TWICE = 0, 1
+FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rn.library()
+
+
+def test_exports_every_declared_function(lib):
+    declared = rn.header_functions()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(rn.SIGNATURES)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.rmsnorm_abi_version() == 1
+    for s in range(6):
+        assert lib.rmsnorm_status_string(s)
+    assert lib.rmsnorm_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes_is_a_pure_function(lib):
+    f = lib.rmsnorm_bwd_workspace_bytes
+    assert f(4096, 4096, BF16) == 256 * 4096 * 4
+    assert f(64, 1024, F32) == 64 * 1024 * 4            # one partial row per row when M < 256
+    assert f(300, 1027, F16) == 256 * 1028 * 4           # rows padded to 16 bytes
+    assert f(0, 4096, BF16) == 0
+    assert f(10, 0, BF16) == 0
+    assert f(10, 10, 7) == 0
+    assert f(10, (1 << 24) + 1, BF16) == 0
+
+
+def fwd(lib, x=FAKE, ldx=8, w=FAKE, y=FAKE + 0x1000, ldy=8, rstd=None, M=4, N=8, dtype=BF16,
+        eps=1e-6, offset=0.0, rounding=TWICE, variant=0):
+    return lib.rmsnorm_fwd_variant(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, rounding,
+                                   variant, None)
+
+
+def bwd(lib, dy=FAKE, lddy=8, x=FAKE + 0x1000, ldx=8, w=FAKE + 0x2000, rstd=FAKE + 0x3000,
+        dx=FAKE + 0x4000, lddx=8, dw=FAKE + 0x5000, ws=FAKE + 0x6000, wsb=1 << 20, M=4, N=8,
+        dtype=BF16, eps=1e-6, offset=0.0, rounding=TWICE, variant=0):
+    return lib.rmsnorm_bwd_variant(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, ws, wsb, M, N, dtype,
+                                   eps, offset, rounding, variant, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
+    (dict(M=-1), INVALID), (dict(N=0), INVALID), (dict(ldx=7), INVALID), (dict(ldy=4), INVALID),
+    (dict(dtype=3), INVALID), (dict(rounding=2), INVALID), (dict(variant=9), INVALID),
+    (dict(eps=-1e-6), INVALID), (dict(eps=float("nan")), INVALID),
+    (dict(eps=float("inf")), INVALID), (dict(offset=float("nan")), INVALID),
+    (dict(N=(1 << 24) + 1, ldx=(1 << 24) + 1, ldy=(1 << 24) + 1), UNSUPPORTED),
+    (dict(x=FAKE + 1), MISALIGNED), (dict(w=FAKE + 1), MISALIGNED), (dict(y=FAKE + 1), MISALIGNED),
+    (dict(rstd=FAKE + 2), MISALIGNED), (dict(dtype=F32, x=FAKE + 2), MISALIGNED),
+    (dict(M=2**62, ldx=8), INVALID),                        # row extent overflows int64
+    (dict(N=70000, ldx=70000, ldy=70000, variant=1), UNSUPPORTED),  # register kernel too narrow
+])
+def test_fwd_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def test_fwd_with_no_rows_is_a_noop(lib):
+    # M = 0: nothing to do, no pointers needed, no HIP call made
+    assert fwd(lib, x=None, w=None, y=None, M=0) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), INVALID), (dict(x=None), INVALID), (dict(w=None), INVALID),
+    (dict(rstd=None), INVALID), (dict(dx=None), INVALID), (dict(dw=None), INVALID),
+    (dict(ws=None), INVALID), (dict(lddy=7), INVALID), (dict(ldx=7), INVALID),
+    (dict(lddx=7), INVALID), (dict(M=-3), INVALID), (dict(N=0), INVALID),
+    (dict(dtype=-1), INVALID), (dict(rounding=5), INVALID), (dict(variant=4), INVALID),
+    (dict(eps=float("-inf")), INVALID), (dict(offset=float("inf")), INVALID),
+    (dict(wsb=4 * 8 * 4 - 1), WORKSPACE), (dict(wsb=0), WORKSPACE),
+    (dict(ws=FAKE + 8), MISALIGNED), (dict(dw=FAKE + 2), MISALIGNED),
+    (dict(rstd=FAKE + 1), MISALIGNED), (dict(dx=FAKE + 1), MISALIGNED),
+    (dict(N=(1 << 24) + 1, lddy=(1 << 24) + 1, ldx=(1 << 24) + 1, lddx=(1 << 24) + 1),
+     UNSUPPORTED),
+    (dict(N=40000, lddy=40000, ldx=40000, lddx=40000, wsb=1 << 30, variant=1), UNSUPPORTED),
+    (dict(N=70000, lddy=70000, ldx=70000, lddx=70000, wsb=1 << 30, variant=2), UNSUPPORTED),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_stages_reject(lib):
+    assert lib.rmsnorm_bwd_rows(FAKE, 8, FAKE, 8, FAKE, FAKE, FAKE, 8, FAKE, 16, 4, 8, BF16, 0.0,
+                                0, None) == WORKSPACE
+    assert lib.rmsnorm_bwd_rows(FAKE, 8, None, 8, FAKE, FAKE, FAKE, 8, FAKE, 1 << 20, 4, 8, BF16,
+                                0.0, 0, None) == INVALID
+    assert lib.rmsnorm_bwd_dw_reduce(FAKE, 1 << 20, None, 4, 8, BF16, None) == INVALID
+    assert lib.rmsnorm_bwd_dw_reduce(FAKE + 4, 1 << 20, FAKE, 4, 8, BF16, None) == MISALIGNED
+    assert lib.rmsnorm_bwd_dw_reduce(FAKE, 4, FAKE, 4, 8, BF16, None) == WORKSPACE
+
+
+def test_binding_rejects_host_tensors_before_calling():
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    w = torch.ones(8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rn.fwd(x, w)
+    with pytest.raises(TypeError):
+        rn.fwd(x.double(), w.double())
+
+
+def test_binding_signatures_match_the_header():
+    """Each ctypes signature has as many arguments as the header's prototype."""
+    import re
+    text = open(rn.HEADER_PATH, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    for name, (_, args) in rn.SIGNATURES.items():
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), (name, params)

@@ -1,0 +1,263 @@
+"""GPU parity: librmsnorm (through its C interface) against the CPU oracle on seeded inputs.
+
+Shapes span several row groups and blocks, ragged row counts (not multiples of the 256 backward
+blocks), ragged widths (a partial last 16-byte vector through a padded row stride; widths whose
+rows are not 16-byte aligned, which take the element-wise path), single-column rows, and the
+widest rows (streaming kernels). Each case also checks that a forward feeding the backward gives
+the documented dw, and that repeated runs are bit-identical.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parity import (check_dw, check_dx, check_fwd, same_bits, to_np)
+from workloads import WORKLOADS, make_inputs, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bwd_precision_numerics_amd as rn  # noqa: E402
+
+DEV = "cuda:0"
+WL = {"f32": WORKLOADS["fp32_64x1024"], "bf16": WORKLOADS["bf16_4096x4096"],
+      "f16": WORKLOADS["fp16_8192x8192"]}
+
+
+def padded(a: np.ndarray, dtype: str, ld: int):
+    """Device [M, N] view with row stride ld >= N."""
+    M, N = a.shape
+    buf = np.zeros((M, ld), np.float32)
+    buf[:, :N] = a
+    return to_device(buf, dtype, DEV)[:, :N]
+
+
+def run_case(dtype, M, N, rounding="twice", offset=0.0, eps=1e-6, ld=None, variant="auto",
+             seed=1, x_scale=None):
+    wl = WL[dtype].with_(rounding=rounding, offset=offset, eps=eps)
+    inp = make_inputs(wl, M=M, N=N, seed=seed)
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    if ld is None:
+        xt, dyt = to_device(x, dtype, DEV), to_device(dy, dtype, DEV)
+    else:
+        xt, dyt = padded(x, dtype, ld), padded(dy, dtype, ld)
+    wt = to_device(w, dtype, DEV)
+    print(f"case dtype={dtype} M={M} N={N} ld={ld} rounding={rounding} offset={offset} "
+          f"variant={variant} seed={seed}", flush=True)
+    y, rstd = rn.fwd(xt, wt, eps=eps, offset=offset, rounding=rounding, variant=variant)
+    dx, dw = rn.bwd(dyt, xt, wt, rstd, eps=eps, offset=offset, rounding=rounding,
+                    variant=variant)
+    torch.cuda.synchronize()
+    yg, rg, dxg, dwg = to_np(y), to_np(rstd), to_np(dx), to_np(dw)
+    st = check_fwd(yg, rg, x, w, eps=eps, offset=offset, rounding=rounding, dtype=dtype)
+    st.update(check_dx(dxg, dy, x, w, rg, offset=offset, dtype=dtype))
+    st.update(check_dw(dwg, oracle.rmsnorm_dw(dy, x, rg)))
+    return st, (yg, rg, dxg, dwg)
+
+
+SHAPES = [
+    # (M, N, ld)
+    (1, 8, None),
+    (5, 1, None),          # single column: element-wise path
+    (7, 3, None),          # tiny ragged width: element-wise path
+    (33, 64, None),
+    (300, 1000, None),     # 125 vectors per row; 300 rows over 256 backward blocks
+    (300, 1027, 1032),     # partial last vector through a padded row stride
+    (129, 1027, None),     # rows not 16-byte aligned: element-wise path
+    (257, 3072, None),
+    (64, 4096, None),
+    (40, 8192, None),
+    (24, 16384, None),
+    (12, 32768, None),     # LDS-staged backward
+    (6, 40000, None),      # streaming backward (beyond the LDS kernel's width)
+    (3, 70000, None),      # streaming forward and backward
+]
+
+
+@pytest.mark.parametrize("M,N,ld", SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_parity_shapes_round_twice(dtype, M, N, ld):
+    run_case(dtype, M, N, rounding="twice", ld=ld)
+
+
+@pytest.mark.parametrize("M,N,ld", [(300, 1000, None), (257, 3072, None), (129, 1027, None),
+                                    (12, 32768, None), (3, 70000, None), (300, 1027, 1032)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("offset", [0.0, 1.0])
+def test_parity_round_once(dtype, M, N, ld, offset):
+    run_case(dtype, M, N, rounding="once", offset=offset, ld=ld)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-5, 0.25])
+def test_parity_eps(eps):
+    run_case("bf16", 200, 2048, eps=eps)
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 1000), ("bf16", 3072), ("f16", 4096),
+                                     ("f32", 1024), ("bf16", 8192), ("bf16", 16384),
+                                     ("f16", 2040)])
+def test_kernel_families_agree_bit_for_bit(dtype, N):
+    """Register, LDS-staged and streaming kernels share the thread-to-element mapping and the
+    summation order, so rstd, y and dx agree bit for bit; dw is bit-identical between the register
+    and LDS kernels and within float32 rounding of the streaming one (another row grouping)."""
+    results = {}
+    for variant in ("registers", "lds", "streaming"):
+        try:
+            _, res = run_case(dtype, 70, N, variant=variant, seed=3)
+        except rn.RMSNormError as e:
+            assert e.status == 2, e  # a family that cannot serve this width says so
+            continue
+        results[variant] = res
+    assert "streaming" in results and len(results) >= 2
+    base = results["streaming"]
+    for v, res in results.items():
+        for k in range(3):
+            assert same_bits(res[k], base[k]).all(), (v, k)
+        assert np.allclose(res[3], base[3], rtol=1e-5, atol=1e-6)
+    if "registers" in results and "lds" in results:
+        assert same_bits(results["registers"][3], results["lds"][3]).all()
+
+
+def test_forward_register_and_lds_staging_at_wide_rows():
+    for variant in ("registers", "lds", "streaming"):
+        wl = WL["bf16"]
+        inp = make_inputs(wl, M=9, N=32768, seed=4)
+        xt, wt = to_device(inp["x"], "bf16", DEV), to_device(inp["w"], "bf16", DEV)
+        print(f"case fwd variant={variant} N=32768", flush=True)
+        y, r = rn.fwd(xt, wt, variant=variant)
+        torch.cuda.synchronize()
+        check_fwd(to_np(y), to_np(r), inp["x"], inp["w"], eps=1e-6, offset=0.0,
+                  rounding="twice", dtype="bf16")
+
+
+def test_repeated_runs_are_bit_identical():
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=1024, N=4096, seed=5)
+    xt, wt, dyt = (to_device(inp[k], "bf16", DEV) for k in ("x", "w", "dy"))
+    outs = []
+    for _ in range(3):
+        y, r = rn.fwd(xt, wt)
+        dx, dw = rn.bwd(dyt, xt, wt, r)
+        torch.cuda.synchronize()
+        outs.append([to_np(t) for t in (y, r, dx, dw)])
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert same_bits(a, b).all()
+
+
+def test_backward_does_not_depend_on_rounding_or_eps_arguments():
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=100, N=2048, seed=6)
+    xt, wt, dyt = (to_device(inp[k], "bf16", DEV) for k in ("x", "w", "dy"))
+    _, r = rn.fwd(xt, wt)
+    a = rn.bwd(dyt, xt, wt, r, rounding="twice", eps=1e-6)
+    b = rn.bwd(dyt, xt, wt, r, rounding="once", eps=0.5)
+    torch.cuda.synchronize()
+    for p, q in zip(a, b):
+        assert same_bits(to_np(p), to_np(q)).all()
+
+
+def test_noncontiguous_gradient_rows():
+    """dy given as a row-strided view (a non-contiguous upstream gradient)."""
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=96, N=1024, seed=7)
+    xt, wt = to_device(inp["x"], "bf16", DEV), to_device(inp["w"], "bf16", DEV)
+    big = np.zeros((96, 3072), np.float32)
+    big[:, 1024:2048] = inp["dy"]
+    dyt = to_device(big, "bf16", DEV)[:, 1024:2048]
+    assert dyt.stride(0) == 3072 and not dyt.is_contiguous()
+    _, r = rn.fwd(xt, wt)
+    dx, dw = rn.bwd(dyt, xt, wt, r)
+    torch.cuda.synchronize()
+    rg = to_np(r)
+    check_dx(to_np(dx), inp["dy"], inp["x"], inp["w"], rg, offset=0.0, dtype="bf16")
+    check_dw(to_np(dw), oracle.rmsnorm_dw(inp["dy"], inp["x"], rg))
+
+
+def test_no_rows():
+    xt = torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
+    wt = torch.ones(512, dtype=torch.bfloat16, device=DEV)
+    y, r = rn.fwd(xt, wt)
+    dw = torch.full((512,), 7.0, device=DEV)
+    dx, dw = rn.bwd(xt, xt, wt, r, dw=dw)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 512) and dx.shape == (0, 512)
+    assert (to_np(dw) == 0).all()
+
+
+def test_rstd_may_be_omitted():
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=64, N=4096, seed=8)
+    xt, wt = to_device(inp["x"], "bf16", DEV), to_device(inp["w"], "bf16", DEV)
+    y1, r = rn.fwd(xt, wt)
+    y2, none = rn.fwd(xt, wt, want_rstd=False)
+    torch.cuda.synchronize()
+    assert none is None and same_bits(to_np(y1), to_np(y2)).all()
+
+
+def test_nan_and_zero_rows():
+    """A NaN poisons its own row only; a zero row with eps = 0 gives rstd = inf and NaN outputs,
+    as IEEE arithmetic does on both sides."""
+    x = np.ones((4, 256), np.float32)
+    x[1, 17] = np.nan
+    x[2] = 0.0
+    w = np.ones(256, np.float32)
+    xt, wt = to_device(x, "bf16", DEV), to_device(w, "bf16", DEV)
+    y, r = rn.fwd(xt, wt, eps=0.0)
+    torch.cuda.synchronize()
+    yg, rg = to_np(y), to_np(r)
+    yo, ro = oracle.rmsnorm_fwd(x, w, eps=0.0, dtype="bf16")
+    assert same_bits(rg, ro).all()
+    assert same_bits(yg, yo).all()
+    assert np.isnan(yg[1]).all() and np.isnan(yg[2]).all() and (yg[[0, 3]] == 1.0).all()
+
+
+def test_conventions_coincide_on_gpu_for_f32_and_unit_gain():
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=64, N=2048, seed=9)
+    for dtype, w in (("f32", inp["w"]), ("bf16", np.ones(2048, np.float32))):
+        xt, wt = to_device(inp["x"], dtype, DEV), to_device(w, dtype, DEV)
+        a, _ = rn.fwd(xt, wt, rounding="once")
+        b, _ = rn.fwd(xt, wt, rounding="twice")
+        torch.cuda.synchronize()
+        assert same_bits(to_np(a), to_np(b)).all()
+
+
+def test_conventions_differ_on_gpu_as_the_oracle_says():
+    """Round once and round twice disagree on about a quarter of bf16 outputs, always by one step,
+    and on exactly the elements where the oracle's two conventions disagree (given the same rstd)."""
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=256, N=4096, seed=10)
+    xt, wt = to_device(inp["x"], "bf16", DEV), to_device(inp["w"], "bf16", DEV)
+    a, ra = rn.fwd(xt, wt, rounding="once")
+    b, rb = rn.fwd(xt, wt, rounding="twice")
+    torch.cuda.synchronize()
+    a, b, ra = to_np(a), to_np(b), to_np(ra)
+    assert same_bits(ra, to_np(rb)).all()
+    differ = a != b
+    assert 0.15 < differ.mean() < 0.35
+    xh = inp["x"] * ra[:, None]
+    g = oracle.gain(inp["w"], 0.0)
+    oa = oracle.apply_gain(xh, g, rounding="once", dtype="bf16")
+    ob = oracle.apply_gain(xh, g, rounding="twice", dtype="bf16")
+    assert np.array_equal(differ, oa != ob)
+
+
+def test_autograd_function_matches_direct_calls():
+    wl = WORKLOADS["bf16_16384x3072_gemma"]
+    inp = make_inputs(wl, M=96, N=3072, seed=11)
+    x = to_device(inp["x"], "bf16", DEV).reshape(4, 24, 3072).requires_grad_(True)
+    w = to_device(inp["w"], "bf16", DEV).requires_grad_(True)
+    dy = to_device(inp["dy"], "bf16", DEV).reshape(4, 24, 3072)
+    y = rn.rms_norm(x, w, 1e-6, 1.0, "once")
+    y.backward(dy)
+    y2, r = rn.fwd(x.detach().reshape(96, 3072), w.detach(), offset=1.0, rounding="once")
+    dx2, dw2 = rn.bwd(dy.reshape(96, 3072), x.detach().reshape(96, 3072), w.detach(), r,
+                      offset=1.0)
+    torch.cuda.synchronize()
+    assert same_bits(to_np(y.reshape(96, 3072)), to_np(y2)).all()
+    assert same_bits(to_np(x.grad.reshape(96, 3072)), to_np(dx2)).all()
+    assert w.grad.dtype == torch.bfloat16
+    assert same_bits(to_np(w.grad), to_np(dw2.to(torch.bfloat16))).all()

@@ -289,6 +289,15 @@ def test_dw_is_additive_over_rows():
     assert np.allclose(dw, dwa.astype(np.float64) + dwb, rtol=1e-6, atol=1e-6)
 
 
+def test_dw_only_function_equals_backward_dw():
+    for name in ("fp32_64x1024", "bf16_16384x3072_gemma", "fp16_8192x8192"):
+        wl = WORKLOADS[name]
+        inp = make_inputs(wl, M=48, N=200)
+        _, r = rmsnorm_fwd(inp["x"], inp["w"], eps=wl.eps, offset=wl.offset, dtype=wl.dtype)
+        _, dw = rmsnorm_bwd(inp["dy"], inp["x"], inp["w"], r, offset=wl.offset, dtype=wl.dtype)
+        assert np.array_equal(oracle.rmsnorm_dw(inp["dy"], inp["x"], r), dw)
+
+
 def test_backward_independent_of_forward_convention_and_offset_derivative():
     """dw does not depend on the offset (d(offset + w)/dw = 1); dx does through the gain."""
     inp = make_inputs(WORKLOADS["bf16_16384x3072_gemma"], M=16, N=192)
