@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""RMSNorm forward + backward on one MI355X: achieved HBM bandwidth of the whole step.
+
+A step is one pass of the whole path over one [M, N] batch: the forward (y and the float32 rstd
+cache), then the backward (dx and the per-block dw partials, then the fixed-order dw reduction).
+Default workload: bf16, M = N = 4096, round twice (Llama convention), eps = 1e-6, seeded synthetic
+inputs x ~ N(0,1), w ~ U(0.9,1.1), dy ~ N(0,1).
+
+Measurement:
+* Inputs are resident in HBM before timing. The step's buffers rotate over independent buffer
+  sets, enough that the x matrices alone span --rotate-mib (default 1 GiB, four times the 256 MiB
+  Infinity Cache; 32 sets at 4096 x 4096), and the forward and the backward of one step use sets
+  half a rotation apart, so no kernel reads data a recent kernel left in the caches (the outputs are
+  written with non-temporal stores and do not displace them either).
+* The K timed steps are replayed from a HIP graph captured once (no host launch overhead), with a
+  device synchronize before and after; value = K * algorithmic bytes of a step / wall time.
+* Algorithmic bytes: forward 2*M*N*s + N*s + 4*M (read x, write y, read w, write rstd); backward
+  3*M*N*s + N*s + 4*M + 4*N (read dy and x, write dx, read w and rstd, write dw). The dw partials are
+  implementation traffic and are not credited.
+* roofline: the dominant kernel is the backward rows kernel. Its average duration comes from HIP
+  events recorded on the launch stream around the replay of a graph of K back-to-back launches of
+  that kernel alone (over the same rotating sets), divided by K; achieved = its algorithmic bytes
+  per launch (3*M*N*s + N*s + 4*M) / that duration. traffic is the HBM bytes per
+  launch measured with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by the same counters'
+  reading for a plain copy of known size), read from the committed summary under profiles/, and
+  null when the kernel sources have changed since that summary was taken.
+* copy_ceiling: a device-to-device copy with the forward's traffic, timed the same way; value is
+  also reported as a fraction of it.
+* cpu_baseline: the CPU oracle (NumPy, one thread) on a bounded sample of the same rows.
+
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload NAME] [--rounding once]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_bwd_rows_bf16_4096x4096.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "bwd_precision_numerics_amd", "csrc", f) for f in
+                  ("librmsnorm.hip", "rmsnorm_common.hpp", "rmsnorm_fwd.hpp", "rmsnorm_bwd.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """Measured HBM bytes per backward-rows launch, if the committed counters match the sources."""
+    if workload != "bf16_4096x4096" or not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    vals = {}
+    with open(TRAFFIC_SUMMARY, encoding="utf-8") as f:
+        for line in f:
+            if line.startswith("traffic:"):
+                for kv in line[len("traffic:"):].split():
+                    k, _, v = kv.partition("=")
+                    vals[k] = v
+    if vals.get("sources") != kernel_source_hash() or "bytes_per_launch" not in vals:
+        return None
+    return float(vals["bytes_per_launch"])
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description="RMSNorm fwd+bwd HBM bandwidth on one MI355X")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: bf16_4096x4096)")
+    ap.add_argument("--rounding", choices=["once", "twice"], default=None)
+    ap.add_argument("--rotate-mib", type=int, default=1024,
+                    help="rotate over enough buffer sets that the x matrices span this many MiB")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps eagerly instead of replaying a graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget for the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--kernel-only", choices=["fwd", "bwd_rows", "dw_reduce"], default=None,
+                    help="launch only this kernel --steps times (for counter collection)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, copy a buffer of this many MiB --steps times "
+                         "(calibrates the HBM byte counters)")
+    return ap.parse_args(argv)
+
+
+class Sets:
+    """Rotating device buffer sets and the raw C-interface calls on them."""
+
+    def __init__(self, rn, torch, wl, rounding, inp, nsets, device):
+        from workloads import to_device
+        self.rn, self.torch, self.wl, self.rounding = rn, torch, wl, rounding
+        self.lib = rn.library()
+        M, N = wl.M, wl.N
+        x0 = to_device(inp["x"], wl.dtype, device)
+        dy0 = to_device(inp["dy"], wl.dtype, device)
+        self.w = to_device(inp["w"], wl.dtype, device)
+        self.sets = []
+        for _ in range(nsets):
+            s = {"x": x0.clone(), "dy": dy0.clone(),
+                 "y": torch.empty_like(x0), "dx": torch.empty_like(x0),
+                 "rstd": torch.empty(M, dtype=torch.float32, device=device),
+                 "dw": torch.empty(N, dtype=torch.float32, device=device)}
+            self.sets.append(s)
+        del x0, dy0
+        self.wsb = rn.workspace_bytes(M, N, wl.dtype)
+        self.ws = torch.empty(max(self.wsb, 16) // 4, dtype=torch.float32, device=device)
+        self.dt = rn.DTYPE_CODES[wl.dtype]
+        self.rc = rn.ROUNDING_CODES[rounding]
+
+    def stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def fwd(self, i):
+        s, wl = self.sets[i], self.wl
+        st = self.lib.rmsnorm_fwd(s["x"].data_ptr(), wl.N, self.w.data_ptr(), s["y"].data_ptr(),
+                                  wl.N, s["rstd"].data_ptr(), wl.M, wl.N, self.dt, wl.eps,
+                                  wl.offset, self.rc, self.stream())
+        if st:
+            raise RuntimeError(f"rmsnorm_fwd status {st}")
+
+    def bwd_rows(self, i):
+        s, wl = self.sets[i], self.wl
+        st = self.lib.rmsnorm_bwd_rows(s["dy"].data_ptr(), wl.N, s["x"].data_ptr(), wl.N,
+                                       self.w.data_ptr(), s["rstd"].data_ptr(), s["dx"].data_ptr(),
+                                       wl.N, self.ws.data_ptr(), self.wsb, wl.M, wl.N, self.dt,
+                                       wl.offset, 0, self.stream())
+        if st:
+            raise RuntimeError(f"rmsnorm_bwd_rows status {st}")
+
+    def dw_reduce(self, i):
+        s, wl = self.sets[i], self.wl
+        st = self.lib.rmsnorm_bwd_dw_reduce(self.ws.data_ptr(), self.wsb, s["dw"].data_ptr(), wl.M,
+                                            wl.N, self.dt, self.stream())
+        if st:
+            raise RuntimeError(f"rmsnorm_bwd_dw_reduce status {st}")
+
+    def step(self, k):
+        """Forward on one set, backward on the set half a rotation away."""
+        n = len(self.sets)
+        a, b = k % n, (k + n // 2) % n
+        self.fwd(a)
+        self.bwd_rows(b)
+        self.dw_reduce(b)
+
+
+def copy_probe(torch, mib, steps):
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t
+    print(json.dumps({"copy_probe_bytes_per_launch": 2 * n * 4, "launches": steps,
+                      "GBps": 2 * n * 4 * steps / dt / 1e9}), flush=True)
+
+
+def capture(torch, fn, count):
+    """A graph of `count` back-to-back calls fn(0), fn(1), ... on the capture stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(count):
+            fn(k)
+    g.replay()  # first replay is untimed
+    torch.cuda.synchronize()
+    return g
+
+
+def kernel_durations(torch, sets, launches):
+    """Average duration (s) of each kernel: events on the launch stream around one replay of a
+    graph of `launches` back-to-back launches of that kernel over the rotating sets."""
+    out = {}
+    n = len(sets.sets)
+    for name, fn in (("fwd", sets.fwd), ("bwd_rows", sets.bwd_rows),
+                     ("dw_reduce", sets.dw_reduce)):
+        g = capture(torch, lambda k: fn(k % n), launches)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / 1e3 / launches
+        del g
+    return out
+
+
+def copy_ceiling(torch, sets, launches):
+    """Device-to-device copies with the forward's traffic (read x, write y of the same rotating
+    sets), timed like the kernels: the bandwidth a plain copy reaches under the same protocol."""
+    n = len(sets.sets)
+
+    def cp(k):
+        s = sets.sets[k % n]
+        s["y"].copy_(s["x"])
+
+    g = capture(torch, cp, launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / launches
+    nbytes = 2 * sets.sets[0]["x"].numel() * sets.sets[0]["x"].element_size()
+    return {"GBps": round(nbytes / sec / 1e9, 1), "us": round(sec * 1e6, 3),
+            "bytes_per_launch": nbytes, "what": "hipMemcpy device-to-device, read x write y"}
+
+
+def cpu_baseline(wl, rounding, inp, budget_s):
+    """The CPU oracle, single-threaded, over row chunks of the same inputs (cycling through the
+    rows again if one pass takes less than the budget) until the time budget is used."""
+    import oracle
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    rows, start, chunk, t0 = 0, 0, 64, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        sl = slice(start, min(start + chunk, wl.M))
+        y, r = oracle.rmsnorm_fwd(x[sl], w, eps=wl.eps, offset=wl.offset, rounding=rounding,
+                                  dtype=wl.dtype)
+        oracle.rmsnorm_bwd(dy[sl], x[sl], w, r, offset=wl.offset, dtype=wl.dtype)
+        rows += sl.stop - sl.start
+        start = 0 if sl.stop >= wl.M else sl.stop
+    dt = time.perf_counter() - t0
+    sub = wl.with_(M=rows)
+    nbytes = sub.fwd_bytes() + sub.bwd_bytes()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} rows ({rows / wl.M:.2f} passes over the {wl.M} x {wl.N} inputs in "
+                      f"chunks of {chunk} rows), forward + backward, {dt:.1f} s, NumPy single "
+                      f"thread (host has {cores} usable cores)"}
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import bwd_precision_numerics_amd as rn
+    from workloads import HEADLINE, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    rn.library()  # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib, args.steps)
+        return 0
+
+    name = args.workload or HEADLINE
+    wl = WORKLOADS[name]
+    rounding = args.rounding or wl.rounding
+    inp = make_inputs(wl)
+    nsets = max(4, -(-args.rotate_mib * 2**20 // (wl.M * wl.N * wl.itemsize)))
+    sets = Sets(rn, torch, wl, rounding, inp, nsets, "cuda:0")
+    for i in range(len(sets.sets)):  # every set gets a valid rstd cache
+        sets.fwd(i)
+    torch.cuda.synchronize()
+
+    if args.kernel_only:
+        fn = {"fwd": sets.fwd, "bwd_rows": sets.bwd_rows, "dw_reduce": sets.dw_reduce}[
+            args.kernel_only]
+        for k in range(args.warmup + args.steps):
+            fn(k % len(sets.sets))
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_only": args.kernel_only, "launches": args.warmup + args.steps,
+                          "workload": name}), flush=True)
+        return 0
+
+    for k in range(args.warmup):
+        sets.step(k)
+    torch.cuda.synchronize()
+
+    graph = None if args.no_graph else capture(torch, sets.step, args.steps)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for k in range(args.steps):
+            sets.step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_bytes = wl.fwd_bytes() + wl.bwd_bytes()
+    value = step_bytes * args.steps / elapsed / 1e9
+
+    dur = kernel_durations(torch, sets, max(args.steps, 20))
+    copy = copy_ceiling(torch, sets, max(args.steps, 20))
+    del graph
+    s = wl.itemsize
+    rows_bytes = 3 * wl.M * wl.N * s + wl.N * s + 4 * wl.M
+    achieved = rows_bytes / dur["bwd_rows"] / 1e9
+    traffic = read_traffic(name)
+
+    line = {
+        "metric": f"RMSNorm fwd+bwd achieved HBM GB/s and % of peak, {wl.dtype} M={wl.M} N={wl.N}",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "M": wl.M, "N": wl.N, "rounding": rounding,
+                   "offset": wl.offset, "eps": wl.eps, "buffer_sets": len(sets.sets),
+                   "graph": not args.no_graph},
+        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "step_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": "bwd_rows_kernel",
+                     "bytes_per_launch": rows_bytes,
+                     "avg_us": round(dur["bwd_rows"] * 1e6, 3)},
+        "kernels_us": {k: round(v * 1e6, 3) for k, v in dur.items()},
+        "phase_GBps": {"fwd": round(wl.fwd_bytes() / dur["fwd"] / 1e9, 1),
+                       "bwd": round(wl.bwd_bytes() / (dur["bwd_rows"] + dur["dw_reduce"]) / 1e9,
+                                    1)},
+        "copy_ceiling": copy,
+        "frac_of_copy_ceiling": round(value / copy["GBps"], 4),
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(wl, rounding, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -22,6 +22,11 @@ constexpr int kBwdBlockThreads = 1024;  // backward: 16 wavefronts per persisten
 constexpr int kFwdMaxIters = 8;         // 16-byte vectors per thread, forward register kernel
 constexpr int kBwdRegMaxIters = 2;      // backward register kernel (rows + prefetch in registers)
 constexpr int kBwdLdsMaxIters = 4;      // backward LDS-staged kernel
+// Register backward pipeline per vectors-per-thread: rows per barrier (batch) and batches in flight
+// ahead of the current one. Ring registers: (DEPTH + 1) * RB * ITERS * 2 sixteen-byte vectors.
+template <int ITERS> struct BwdPipe;
+template <> struct BwdPipe<1> { static constexpr int RB = 1, DEPTH = 3; };
+template <> struct BwdPipe<2> { static constexpr int RB = 1, DEPTH = 1; };
 
 int elem_bytes(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F32 ? 4 : 2; }
 int vec_elems(rmsnorm_dtype d) { return 16 / elem_bytes(d); }
@@ -117,11 +122,13 @@ rmsnorm_status plan_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   return RMSNORM_OK;
 }
 
-// Backward: each thread owns at most 2 (register kernel) or 4 (LDS kernel) vectors of a row.
+// Backward: one 16-byte vector per thread up to 1024 vectors a row (8192 16-bit elements); wider
+// rows give each thread 2 (register kernel) or up to 4 (LDS kernel) vectors.
 void bwd_shape(int64_t nv, int* tpr, int* iters) {
-  *tpr = (int)clamp64(pow2_ceil(ceil_div(nv, 2)), 64, 1024);
+  *tpr = (int)clamp64(pow2_ceil(nv), 64, 1024);
   *iters = (int)ceil_div(nv, *tpr);
 }
+int bwd_batch(int iters) { return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB; }
 
 rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
                         rmsnorm_variant req, Plan* p) {
@@ -155,8 +162,13 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   p->groups = kBwdBlockThreads / tpr;
   const int wpr = tpr / 64;
   const int V = vec_elems(dtype);
-  size_t main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr);
-  if (v == RMSNORM_VARIANT_LDS) main_bytes += (size_t)p->groups * 2 * iters * tpr * 16;
+  size_t main_bytes;
+  if (v == RMSNORM_VARIANT_LDS) {
+    main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr) +
+                 (size_t)p->groups * 2 * iters * tpr * 16;
+  } else {
+    main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr * bwd_batch(iters));
+  }
   const size_t combine_bytes = sizeof(float) * (size_t)(p->groups / 2) * tpr * iters * V;
   p->lds = main_bytes > combine_bytes ? main_bytes : combine_bytes;
   return RMSNORM_OK;
@@ -223,8 +235,12 @@ rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
     }
   }
   switch (p.iters) {
-    case 1: return launch(bwd_rows_kernel<D, 1>, p.grid, block, p.lds, s, a);
-    case 2: return launch(bwd_rows_kernel<D, 2>, p.grid, block, p.lds, s, a);
+    case 1:
+      return launch(bwd_rows_kernel<D, 1, BwdPipe<1>::DEPTH, BwdPipe<1>::RB>, p.grid, block, p.lds,
+                    s, a);
+    case 2:
+      return launch(bwd_rows_kernel<D, 2, BwdPipe<2>::DEPTH, BwdPipe<2>::RB>, p.grid, block, p.lds,
+                    s, a);
     default: return RMSNORM_ERR_UNSUPPORTED;
   }
 }
@@ -351,7 +367,7 @@ rmsnorm_status dw_reduce_impl(const void* workspace, size_t workspace_bytes_give
                        (int)N);
     return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
   }
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)ceil_div(N, 64)), dim3(1024), 0, s,
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)ceil_div(N, 16)), dim3(256), 0, s,
                      static_cast<const float*>(workspace), partial_ld(N), (int)num_partials(M),
                      (int)N, dw);
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;

@@ -9,11 +9,13 @@
 //   dw_j = sum over rows of dy_j * xhat_j         (float32; Liger-Kernel pull request 92 keeps the
 //                                                   weight gradient in float32)
 //
-// dw without atomics: the rows are split into P contiguous, balanced chunks, one per block of a
-// persistent grid (P depends only on M, so the result does not depend on the device). A block's
-// threads keep float32 column accumulators in registers while they walk the chunk, combine them
-// across the block's row groups in a fixed tree order, and write one partial row of a
-// [P, ldp] float32 workspace. A second kernel adds the P partial rows in a fixed order.
+// dw without atomics: block b of a persistent grid of P blocks owns rows b, b + P, b + 2P, ... (P
+// depends only on M, so the result does not depend on the device). Interleaving keeps the whole
+// grid on one contiguous stretch of rows at a time, which spreads DRAM traffic evenly; a block
+// owning one contiguous chunk instead makes 256 far-apart streams and leaves some compute units
+// starved. A block's threads keep float32 column accumulators in registers while they walk their
+// rows, combine them across the block's row groups in a fixed tree order, and write one partial
+// row of a [P, ldp] float32 workspace. A second kernel adds the P partial rows in a fixed order.
 #pragma once
 
 #include "rmsnorm_common.hpp"
@@ -23,6 +25,8 @@ namespace rmsn {
 // Partial rows of the dw workspace: one per block; a function of M only.
 constexpr int kMaxPartials = 256;
 inline int64_t num_partials(int64_t M) { return M < kMaxPartials ? M : kMaxPartials; }
+// Rows owned by block b of P: b, b + P, ... below M.
+__device__ __forceinline__ int64_t block_rows(int64_t M, int P, int b) { return (M - b + P - 1) / P; }
 // Row stride of the workspace in floats (16-byte aligned rows).
 inline int64_t partial_ld(int64_t N) { return (N + 3) & ~int64_t(3); }
 
@@ -85,26 +89,51 @@ __device__ __forceinline__ void store_partial(const float (&acc)[ITERS * V], flo
   }
 }
 
-// Register kernel: a row group keeps its row's xhat and g*dy in registers between the reduction
-// and the elementwise pass, and prefetches the next row of its chunk into registers while the
-// current one is reduced. The gain g = offset + w stays in registers for the whole chunk.
-template <DT D, int ITERS>
+// Sums of RB values over the TPR threads of one row group, with the order of group_sum for each:
+// one LDS round trip and one barrier serve the whole batch. Every thread of the block must call it.
+template <int RB>
+__device__ __forceinline__ void group_sum_batch(float (&v)[RB], float* red, int wpr, int tl) {
+#pragma unroll
+  for (int k = 0; k < RB; ++k) v[k] = wave_sum(v[k]);
+  if (wpr > 1) {
+    if ((tl & 63) == 0) {
+#pragma unroll
+      for (int k = 0; k < RB; ++k) red[(tl >> 6) * RB + k] = v[k];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      float t = red[k];
+      for (int w = 1; w < wpr; ++w) t += red[w * RB + k];
+      v[k] = t;
+    }
+  }
+}
+
+// Register kernel. A row group takes its block's rows in batches of RB rows (local index
+// (s * RB + k) * groups + grp for step s and batch index k; row = b + local * P) and keeps a ring of
+// DEPTH + 1 batches of raw (x, dy) in registers: while batch s is reduced and written, batches
+// s + 1 .. s + DEPTH are in flight, and one barrier serves all RB rows of a batch. Pass 1 upcasts
+// a raw row to form its dot product and its dw contributions; pass 2 upcasts it again for dx
+// (cheaper in registers than keeping xhat and g*dy). The gain g = offset + w stays in registers.
+template <DT D, int ITERS, int DEPTH, int RB>
 __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
   using Raw = typename IO::Raw;
   constexpr int V = IO::V;
+  constexpr int RING = DEPTH + 1;
   extern __shared__ uint4 smem[];
 
   const int TPR = a.tpr, wpr = TPR >> 6, G = a.groups, N = a.N;
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
-  const int b = blockIdx.x;
-  const int64_t r0 = (int64_t)b * a.M / a.P;
-  const int64_t r1 = (int64_t)(b + 1) * a.M / a.P;
-  const int nsteps = (int)((r1 - r0 + G - 1) / G);
-  float* red = reinterpret_cast<float*>(smem);  // [2][G * wpr]
+  const int b = blockIdx.x, P = a.P;
+  const int64_t nloc = block_rows(a.M, P, b);
+  const int64_t span = (int64_t)G * RB;
+  const int nsteps = (int)((nloc + span - 1) / span);
+  float* red = reinterpret_cast<float*>(smem);  // [2][G][wpr][RB]
 
   const S* dyb = static_cast<const S*>(a.dy);
   const S* xb = static_cast<const S*>(a.x);
@@ -129,71 +158,90 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < ITERS * V; ++k) acc[k] = 0.f;
 
-  Raw nx[ITERS], nd[ITERS];
+  Raw rx[RING][RB][ITERS], rd[RING][RB][ITERS];
+  // Rows past the chunk load as zeros: they add nothing to the dot products or to dw.
+  auto load_batch = [&](int slot, int s) {
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) nx[it] = nd[it] = IO::zero();
-  auto load_row = [&](int64_t row) {
-    const S* xr = xb + row * a.ldx;
-    const S* dr = dyb + row * a.lddy;
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int col = (it * TPR + tl) * V;
-      if (col + V <= N) {
-        nx[it] = IO::load(xr + col);
-        nd[it] = IO::load(dr + col);
-      } else if (col < N) {
-        nx[it] = IO::load_part(xr + col, N - col);
-        nd[it] = IO::load_part(dr + col, N - col);
-      }
-    }
-  };
-  if (r0 + grp < r1) load_row(r0 + grp);
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int64_t row = r0 + (int64_t)s * G + grp;
-    const bool valid = row < r1;
-    Raw cx[ITERS], cd[ITERS];
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      cx[it] = nx[it];
-      cd[it] = nd[it];
-    }
-    if (row + G < r1) load_row(row + G);  // prefetch; consumed next step
-    const float rs = valid ? a.rstd[row] : 0.f;
-
-    float xh[ITERS][V], gdy[ITERS][V];
-    float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      float xf[V], df[V];
-      IO::unpack(cx[it], xf);
-      IO::unpack(cd[it], df);
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        xh[it][e] = xf[e] * rs;
-        gdy[it][e] = g[it][e] * df[e];
-        acc[it * V + e] = __builtin_fmaf(df[e], xh[it][e], acc[it * V + e]);
-      }
-#pragma unroll
-      for (int e = 0; e < V; e += 2) {
-        d0 = __builtin_fmaf(gdy[it][e], xh[it][e], d0);
-        d1 = __builtin_fmaf(gdy[it][e + 1], xh[it][e + 1], d1);
-      }
-    }
-    const float dot = group_sum(d0 + d1, red + (s & 1) * G * wpr + grp * wpr, wpr, tl);
-    const float c = dot / (float)N;
-    if (valid) {
-      S* dxr = dxb + row * a.lddx;
+    for (int k = 0; k < RB; ++k) {
+      const int64_t li = ((int64_t)s * RB + k) * G + grp;
+      const int64_t row = b + (li < nloc ? li : 0) * P;
+      const S* xr = xb + row * a.ldx;
+      const S* dr = dyb + row * a.lddy;
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
         const int col = (it * TPR + tl) * V;
-        if (col >= N) continue;
-        float o[V];
+        rx[slot][k][it] = IO::zero();
+        rd[slot][k][it] = IO::zero();
+        if (li < nloc) {
+          if (col + V <= N) {
+            rx[slot][k][it] = IO::load(xr + col);
+            rd[slot][k][it] = IO::load(dr + col);
+          } else if (col < N) {
+            rx[slot][k][it] = IO::load_part(xr + col, N - col);
+            rd[slot][k][it] = IO::load_part(dr + col, N - col);
+          }
+        }
+      }
+    }
+  };
 #pragma unroll
-        for (int e = 0; e < V; ++e) o[e] = rs * (gdy[it][e] - xh[it][e] * c);
-        const Raw out = IO::pack(o);
-        if (col + V <= N) IO::store(dxr + col, out);
-        else IO::store_part(dxr + col, out, N - col);
+  for (int j = 0; j < DEPTH; ++j) load_batch(j, j);
+
+  for (int s0 = 0; s0 < nsteps; s0 += RING) {
+#pragma unroll
+    for (int j = 0; j < RING; ++j) {
+      const int s = s0 + j;
+      if (s < nsteps) {  // block-uniform
+        if (s + DEPTH < nsteps) load_batch((j + DEPTH) % RING, s + DEPTH);
+        float rs[RB], dot[RB];
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+          const int64_t li = ((int64_t)s * RB + k) * G + grp;
+          rs[k] = li < nloc ? a.rstd[b + li * P] : 0.f;
+          float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+          for (int it = 0; it < ITERS; ++it) {
+            float xf[V], df[V];
+            IO::unpack(rx[j][k][it], xf);
+            IO::unpack(rd[j][k][it], df);
+#pragma unroll
+            for (int e = 0; e < V; e += 2) {
+              const float xh0 = xf[e] * rs[k], xh1 = xf[e + 1] * rs[k];
+              const float gd0 = g[it][e] * df[e], gd1 = g[it][e + 1] * df[e + 1];
+              acc[it * V + e] = __builtin_fmaf(df[e], xh0, acc[it * V + e]);
+              acc[it * V + e + 1] = __builtin_fmaf(df[e + 1], xh1, acc[it * V + e + 1]);
+              d0 = __builtin_fmaf(gd0, xh0, d0);
+              d1 = __builtin_fmaf(gd1, xh1, d1);
+            }
+          }
+          dot[k] = d0 + d1;
+        }
+        group_sum_batch<RB>(dot, red + ((s & 1) * G + grp) * wpr * RB, wpr, tl);
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+          const int64_t li = ((int64_t)s * RB + k) * G + grp;
+          if (li >= nloc) continue;
+          const int64_t row = b + li * P;
+          const float c = dot[k] / (float)N;
+          S* dxr = dxb + row * a.lddx;
+#pragma unroll
+          for (int it = 0; it < ITERS; ++it) {
+            const int col = (it * TPR + tl) * V;
+            if (col >= N) continue;
+            float xf[V], df[V], o[V];
+            IO::unpack(rx[j][k][it], xf);
+            IO::unpack(rd[j][k][it], df);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+              const float xh = xf[e] * rs[k];
+              const float gd = g[it][e] * df[e];
+              o[e] = rs[k] * (gd - xh * c);
+            }
+            const Raw out = IO::pack(o);
+            if (col + V <= N) IO::store(dxr + col, out);
+            else IO::store_part(dxr + col, out, N - col);
+          }
+        }
       }
     }
   }
@@ -219,10 +267,9 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
-  const int b = blockIdx.x;
-  const int64_t r0 = (int64_t)b * a.M / a.P;
-  const int64_t r1 = (int64_t)(b + 1) * a.M / a.P;
-  const int nsteps = (int)((r1 - r0 + G - 1) / G);
+  const int b = blockIdx.x, P = a.P;
+  const int64_t nloc = block_rows(a.M, P, b);
+  const int nsteps = (int)((nloc + G - 1) / G);
   float* red = reinterpret_cast<float*>(smem);                                    // [2][G * wpr]
   Raw* stage = smem + ((2 * G * wpr + 3) >> 2) + (size_t)grp * 2 * ITERS * TPR;  // [G][2][ITERS*TPR]
 
@@ -232,9 +279,10 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
   for (int k = 0; k < ITERS * V; ++k) acc[k] = 0.f;
 
   for (int s = 0; s < nsteps; ++s) {
-    const int64_t row = r0 + (int64_t)s * G + grp;
-    const bool valid = row < r1;
-    const int64_t lrow = valid ? row : r0;
+    const int64_t li = (int64_t)s * G + grp;
+    const bool valid = li < nloc;
+    const int64_t row = b + (valid ? li : 0) * P;
+    const int64_t lrow = row;
     const S* xr = static_cast<const S*>(a.x) + lrow * a.ldx;
     const S* dr = static_cast<const S*>(a.dy) + lrow * a.lddy;
     Raw rx[ITERS], rd[ITERS];
@@ -318,9 +366,7 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
   const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
   const int nv = (N + V - 1) / V;
   const int tl = threadIdx.x;
-  const int b = blockIdx.x;
-  const int64_t r0 = (int64_t)b * a.M / a.P;
-  const int64_t r1 = (int64_t)(b + 1) * a.M / a.P;
+  const int b = blockIdx.x, P = a.P;
   float* red = reinterpret_cast<float*>(smem);  // [2][wpr]
   const S* wr = static_cast<const S*>(a.w);
   float* pr = a.part + (int64_t)b * a.ldp;
@@ -333,7 +379,7 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
   }
 
   int s = 0;
-  for (int64_t row = r0; row < r1; ++row, ++s) {
+  for (int64_t row = b; row < a.M; row += P, ++s) {
     const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
     const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
     const float rs = a.rstd[row];
@@ -377,25 +423,34 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
   }
 }
 
-// dw_j = sum over p of part[p, j], p in a fixed order: wave k of the block adds partial rows
-// k, k + 16, ... ; then the 16 wave sums are added in wave order. One column per lane.
-__global__ void __launch_bounds__(1024) dw_reduce_kernel(const float* part, int64_t ldp, int P,
-                                                         int N, float* dw) {
-  __shared__ float buf[16][64];
+// dw_j = sum over p of part[p, j] in a fixed order, spread over many compute units: a block of
+// 4 wavefronts owns 16 columns. Lane l of wave k reads column l % 16 of partial rows
+// p = 16 * i + 4 * k + l / 16 (i = 0 .. kMaxPartials / 16 - 1, all loads in flight together) and
+// adds them in order of i; the four lanes of a column (l / 16 = 0..3) are then added in order, and
+// finally the four waves in order.
+static_assert(kMaxPartials % 16 == 0, "dw_reduce_kernel reads partial rows in groups of 16");
+__global__ void __launch_bounds__(256) dw_reduce_kernel(const float* part, int64_t ldp, int P,
+                                                        int N, float* dw) {
+  constexpr int L = kMaxPartials / 16;
+  __shared__ float buf[4][16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int col = blockIdx.x * 64 + lane;
-  float s = 0.f;
-  if (col < N) {
-    for (int p = wv; p < P; p += 16) s += part[(int64_t)p * ldp + col];
-  }
-  buf[wv][lane] = s;
-  __syncthreads();
-  if (wv == 0 && col < N) {
-    float t = buf[0][lane];
+  const int c = lane & 15, q = lane >> 4;
+  const int col = blockIdx.x * 16 + c;
+  float v[L];
 #pragma unroll
-    for (int k = 1; k < 16; ++k) t += buf[k][lane];
-    dw[col] = t;
+  for (int i = 0; i < L; ++i) {
+    const int p = 16 * i + 4 * wv + q;
+    v[i] = (col < N && p < P) ? part[(int64_t)p * ldp + col] : 0.f;
   }
+  float s = v[0];
+#pragma unroll
+  for (int i = 1; i < L; ++i) s += v[i];
+  // lanes c, c+16, c+32, c+48 hold the four row phases of column c: add them in order q = 0..3
+  const float s1 = __shfl(s, c + 16, 64), s2 = __shfl(s, c + 32, 64), s3 = __shfl(s, c + 48, 64);
+  const float t = ((s + s1) + s2) + s3;
+  if (q == 0) buf[wv][c] = t;
+  __syncthreads();
+  if (wv == 0 && q == 0 && col < N) dw[col] = ((buf[0][c] + buf[1][c]) + buf[2][c]) + buf[3][c];
 }
 
 __global__ void fill_zero_kernel(float* p, int n) {

@@ -91,7 +91,12 @@ template <DT D> struct VecIO<D, true> {
     for (int i = 0; i < V; ++i) tmp[i] = (i < n) ? p[i] : S(0);
     return __builtin_bit_cast(uint4, tmp);
   }
-  static __device__ __forceinline__ void store(S* p, Raw r) { *reinterpret_cast<uint4*>(p) = r; }
+  // Outputs are written once and not re-read by the kernel: non-temporal 16-byte stores keep
+  // them from displacing the input stream in the caches.
+  static __device__ __forceinline__ void store(S* p, Raw r) {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, r), reinterpret_cast<u32x4_t*>(p));
+  }
   static __device__ __forceinline__ void store_part(S* p, Raw r, int n) {
     S tmp[V];
     __builtin_memcpy(tmp, &r, sizeof(r));
@@ -146,12 +151,23 @@ template <DT D> __device__ __forceinline__ float round_trip(float f) {
 }
 
 // ---- reductions ----------------------------------------------------------------------------------
-// Butterfly sum over the 64 lanes of a wave. Every lane ends with the same bits: at each level the
-// two partners add the same two values, and IEEE addition is commutative.
+// Sum over the 64 lanes of a wave with DPP lane moves (register-to-register, no LDS round trip):
+// pairs and quads (quad_perm), then rows of 16 (row_shr 4 and 8), then rows 0+1 and 2+3
+// (row_bcast 15) and all four rows (row_bcast 31); lane 63 ends with the total, which is read into
+// a scalar register, so every lane gets the same bits. The order of additions is fixed.
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, BOUND_ZERO));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += dpp_move<0xb1, 0xf, true>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4e, 0xf, true>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x114, 0xf, true>(v);  // row_shr:4 (lanes 0-3 of a row add 0)
+  v += dpp_move<0x118, 0xf, true>(v);  // row_shr:8: lane 15 of each row holds the row sum
+  v += dpp_move<0x142, 0xa, false>(v); // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc, false>(v); // row_bcast:31 into rows 2 and 3: lane 63 holds the total
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Workgroup barrier that orders LDS only: outstanding global loads stay in flight across it, so a

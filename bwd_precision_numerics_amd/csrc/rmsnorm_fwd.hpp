@@ -11,7 +11,7 @@
 // it * TPR + tl (it = 0 .. ITERS-1) of its row, so every wavefront load is one contiguous
 // 64 x 16 B = 1 KiB segment. Summation order of the squares is fixed by this mapping: per thread,
 // two accumulators (even / odd element of each vector) over it = 0, 1, ...; then the wave
-// butterfly; then the waves of the row in order. All three kernel families below use the same
+// reduction; then the waves of the row in order. All three kernel families below use the same
 // mapping for the same TPR, so their rstd and y are bit-identical.
 #pragma once
 
@@ -62,16 +62,23 @@ __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
   Raw* stage = smem + ((a.groups * wpr + 3) >> 2) + (size_t)grp * ITERS * TPR;
 
   const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
-  Raw raw[ITERS];
+  const S* wr = static_cast<const S*>(a.w);
+  Raw raw[ITERS], wraw[ITERS];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
-    Raw r = IO::zero();
+    Raw r = IO::zero(), rw = IO::zero();
     if (valid) {
-      if (col + V <= N) r = IO::load(xr + col);
-      else if (col < N) r = IO::load_part(xr + col, N - col);
+      if (col + V <= N) {
+        r = IO::load(xr + col);
+        rw = IO::load(wr + col);
+      } else if (col < N) {
+        r = IO::load_part(xr + col, N - col);
+        rw = IO::load_part(wr + col, N - col);
+      }
     }
     raw[it] = r;
+    wraw[it] = rw;
   }
   float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
@@ -90,7 +97,6 @@ __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
   if (!valid) return;
   if (tl == 0 && a.rstd) a.rstd[row] = rs;
 
-  const S* wr = static_cast<const S*>(a.w);
   S* yr = static_cast<S*>(a.y) + row * a.ldy;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
@@ -98,10 +104,9 @@ __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
     if (col >= N) continue;
     const bool full = col + V <= N;
     const Raw r = STAGE_LDS ? stage[it * TPR + tl] : raw[it];
-    const Raw wv = full ? IO::load(wr + col) : IO::load_part(wr + col, N - col);
     float xf[V], wf[V], yf[V];
     IO::unpack(r, xf);
-    IO::unpack(wv, wf);
+    IO::unpack(wraw[it], wf);
     apply_gain<D, TWICE, V>(xf, wf, rs, a.offset, yf);
     const Raw out = IO::pack(yf);
     if (full) IO::store(yr + col, out);

@@ -261,3 +261,44 @@ def test_autograd_function_matches_direct_calls():
     assert same_bits(to_np(x.grad.reshape(96, 3072)), to_np(dx2)).all()
     assert w.grad.dtype == torch.bfloat16
     assert same_bits(to_np(w.grad), to_np(dw2.to(torch.bfloat16))).all()
+
+
+def test_graph_replays_match_eager():
+    """The benchmark replays the step from a captured graph: every replay (with eager work and
+    synchronizations in between) must reproduce the eager results bit for bit."""
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=512, N=4096, seed=12)
+    xt, wt, dyt = (to_device(inp[k], "bf16", DEV) for k in ("x", "w", "dy"))
+    M, N = 512, 4096
+    y = torch.empty_like(xt)
+    dx = torch.empty_like(xt)
+    r = torch.empty(M, dtype=torch.float32, device=DEV)
+    dw = torch.empty(N, dtype=torch.float32, device=DEV)
+    ws = torch.empty(rn.workspace_bytes(M, N, "bf16") // 4, dtype=torch.float32, device=DEV)
+
+    def step():
+        rn.fwd(xt, wt, y=y, rstd=r)
+        rn.bwd_rows(dyt, xt, wt, r, ws, dx=dx)
+        rn.dw_reduce(ws, dw, M, N, "bf16")
+
+    step()
+    torch.cuda.synchronize()
+    ref = [to_np(t) for t in (y, r, dx, dw)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (y, r, dx, dw):
+            t.fill_(float("nan"))
+        _, _ = rn.fwd(xt[:7], wt)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (y, r, dx, dw)):
+            assert same_bits(a, to_np(b)).all(), rep
