@@ -25,7 +25,7 @@ constexpr int kBwdLdsMaxIters = 4;      // backward LDS-staged kernel
 // Register backward pipeline per vectors-per-thread: rows per barrier (batch) and batches in flight
 // ahead of the current one. Ring registers: (DEPTH + 1) * RB * ITERS * 2 sixteen-byte vectors.
 template <int ITERS> struct BwdPipe;
-template <> struct BwdPipe<1> { static constexpr int RB = 1, DEPTH = 3; };
+template <> struct BwdPipe<1> { static constexpr int RB = 1, DEPTH = 5; };
 template <> struct BwdPipe<2> { static constexpr int RB = 1, DEPTH = 1; };
 
 int elem_bytes(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F32 ? 4 : 2; }

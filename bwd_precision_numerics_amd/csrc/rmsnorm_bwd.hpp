@@ -159,7 +159,8 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   for (int k = 0; k < ITERS * V; ++k) acc[k] = 0.f;
 
   Raw rx[RING][RB][ITERS], rd[RING][RB][ITERS];
-  // Rows past the chunk load as zeros: they add nothing to the dot products or to dw.
+  float rr[RING][RB];  // the rows' rstd travels with their data: no dependent load per step
+  // Rows past the block's share load as zeros: they add nothing to the dot products or to dw.
   auto load_batch = [&](int slot, int s) {
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
@@ -167,6 +168,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
       const int64_t row = b + (li < nloc ? li : 0) * P;
       const S* xr = xb + row * a.ldx;
       const S* dr = dyb + row * a.lddy;
+      rr[slot][k] = li < nloc ? a.rstd[row] : 0.f;
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
         const int col = (it * TPR + tl) * V;
@@ -196,8 +198,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
         float rs[RB], dot[RB];
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
-          const int64_t li = ((int64_t)s * RB + k) * G + grp;
-          rs[k] = li < nloc ? a.rstd[b + li * P] : 0.f;
+          rs[k] = rr[j][k];
           float d0 = 0.f, d1 = 0.f;
 #pragma unroll
           for (int it = 0; it < ITERS; ++it) {
@@ -285,6 +286,7 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
     const int64_t lrow = row;
     const S* xr = static_cast<const S*>(a.x) + lrow * a.ldx;
     const S* dr = static_cast<const S*>(a.dy) + lrow * a.lddy;
+    const float rs = valid ? a.rstd[row] : 0.f;  // issued with the row's loads
     Raw rx[ITERS], rd[ITERS];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -300,7 +302,6 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
         }
       }
     }
-    const float rs = valid ? a.rstd[row] : 0.f;
     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
