@@ -10,11 +10,11 @@ them: the two share no code. Every function is pinned by CPU tests to values the
 closed forms, invariants, library conversions and float64 finite differences.
 """
 from .rounding import round_to_format, rne_bf16, rne_f16, rne_f32, rne_to, ulp_of
-from .rmsnorm import (DTYPES, ROUNDINGS, apply_gain, gain, rmsnorm_bwd, rmsnorm_dw, rmsnorm_fwd,
+from .rmsnorm import (CASTS, DTYPES, ROUNDINGS, apply_gain, gain, rmsnorm_bwd, rmsnorm_dw, rmsnorm_fwd,
                       rstd_of)
 
 __all__ = [
     "round_to_format", "rne_bf16", "rne_f16", "rne_f32", "rne_to", "ulp_of",
-    "DTYPES", "ROUNDINGS", "apply_gain", "gain", "rmsnorm_bwd", "rmsnorm_dw", "rmsnorm_fwd",
+    "CASTS", "DTYPES", "ROUNDINGS", "apply_gain", "gain", "rmsnorm_bwd", "rmsnorm_dw", "rmsnorm_fwd",
     "rstd_of",
 ]

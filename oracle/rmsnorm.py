@@ -50,6 +50,16 @@ per-convention casts of a backward):
 This is the exact derivative of y = x * r(x) * g with r = (mean(x^2) + eps)^(-1/2):
 dL/dx_i = r * (g_i dy_i - xhat_i * mean_j(g_j dy_j xhat_j)) and dL/dw_j = sum_rows dy_j xhat_j.
 
+Second backward (``casts="autograd"``; only differs for round twice with a 16-bit T): the casts an
+autograd engine makes when it differentiates the round-twice forward computed in T, as the Liger
+pull request describes for matching the references. The forward multiplies the gain by the
+T-rounded xhat in T, so the gradient reaching xhat is the T product of the upstream gradient and the
+gain, and the gain's gradient multiplies the upstream gradient by the T-rounded xhat:
+
+    gdy  = RNE_T( fl(g * dy) )
+    dw_j = RNE_f32( sum_r dy_rj * RNE_T(xhat_rj) )
+    c and dx as above (the normalization itself runs in float32).
+
 ``exact=True`` evaluates the same formulas entirely in float64 with no rounding to T or float32; it
 is the real-number function, used for finite-difference and closed-form checks.
 """
@@ -61,6 +71,7 @@ from .rounding import rne_f32, rne_to
 
 DTYPES = ("f32", "f16", "bf16")
 ROUNDINGS = ("once", "twice")
+CASTS = ("float32", "autograd")
 
 
 def _check(dtype: str, rounding: str) -> None:
@@ -125,14 +136,23 @@ def rmsnorm_fwd(x, w, *, eps: float, offset: float = 0.0, rounding: str = "twice
     return y, rstd
 
 
-def rmsnorm_bwd(dy, x, w, rstd, *, offset: float = 0.0, dtype: str = "bf16", exact: bool = False):
+def _autograd_casts(casts: str, rounding: str, dtype: str, exact: bool) -> bool:
+    if casts not in CASTS:
+        raise ValueError(f"casts must be one of {CASTS}, got {casts!r}")
+    _check(dtype, rounding)
+    return casts == "autograd" and rounding == "twice" and dtype != "f32" and not exact
+
+
+def rmsnorm_bwd(dy, x, w, rstd, *, offset: float = 0.0, dtype: str = "bf16", exact: bool = False,
+                rounding: str = "twice", casts: str = "float32"):
     """Backward of RMSNorm given the forward's per-row ``rstd`` cache.
 
     Returns ``(dx, dw)``: ``dx`` [M, N] (float32 holding T values, or float64 if exact) and
-    ``dw`` [N] (float32, or float64 if exact). Independent of the forward's rounding convention.
+    ``dw`` [N] (float32, or float64 if exact). With ``casts="float32"`` it does not depend on the
+    forward's rounding convention; ``casts="autograd"`` reproduces the casts of differentiating the
+    round-twice forward in T (see the module docstring).
     """
-    if dtype not in DTYPES:
-        raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
+    ag = _autograd_casts(casts, rounding, dtype, exact)
     F = np.float64 if exact else np.float32
     x = np.asarray(x, F)
     dy = np.asarray(dy, F)
@@ -141,21 +161,29 @@ def rmsnorm_bwd(dy, x, w, rstd, *, offset: float = 0.0, dtype: str = "bf16", exa
     with np.errstate(invalid="ignore", over="ignore"):
         xhat = x * r
         gdy = gain(w, offset, exact).astype(F) * dy
+        if ag:
+            gdy = rne_to(gdy, dtype)
         c = np.sum(gdy.astype(np.float64) * xhat.astype(np.float64), axis=-1) / n
         c = (c if exact else rne_f32(c))[..., None]
         dx = r * (gdy - xhat * c)
-        dw = np.sum(dy.astype(np.float64) * xhat.astype(np.float64), axis=0)
+        xw = rne_to(xhat, dtype) if ag else xhat
+        dw = np.sum(dy.astype(np.float64) * xw.astype(np.float64), axis=0)
     if exact:
         return dx, dw
     return rne_to(dx, dtype), rne_f32(dw)
 
 
-def rmsnorm_dw(dy, x, rstd) -> np.ndarray:
-    """Only the weight gradient of ``rmsnorm_bwd``: dw_j = RNE_f32(sum_r dy_rj * fl(x_rj * rstd_r)).
+def rmsnorm_dw(dy, x, rstd, *, dtype: str = "bf16", rounding: str = "twice",
+               casts: str = "float32") -> np.ndarray:
+    """Only the weight gradient of ``rmsnorm_bwd``: dw_j = RNE_f32(sum_r dy_rj * fl(x_rj * rstd_r))
+    (with RNE_T applied to the normalized value for the autograd casts).
 
     The same formula as the backward's dw (the tests hold the two equal bit for bit); it skips the
     input gradient so that full-size matrices stay cheap to check.
     """
+    ag = _autograd_casts(casts, rounding, dtype, False)
     xhat = np.asarray(x, np.float32) * np.asarray(rstd, np.float32)[..., None]
+    if ag:
+        xhat = rne_to(xhat, dtype)
     dw = np.sum(np.asarray(dy, np.float32).astype(np.float64) * xhat.astype(np.float64), axis=0)
     return rne_f32(dw)
