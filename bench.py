@@ -80,6 +80,8 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: bf16_4096x4096)")
     ap.add_argument("--rounding", choices=["once", "twice"], default=None)
+    ap.add_argument("--bwd-casts", choices=["float32", "autograd"], default="float32",
+                    help="backward reading: float32 (default) or the autograd casts")
     ap.add_argument("--rotate-mib", type=int, default=1024,
                     help="rotate over enough buffer sets that the x matrices span this many MiB")
     ap.add_argument("--no-graph", action="store_true",
@@ -97,7 +99,7 @@ def parse_args(argv=None):
 class Sets:
     """Rotating device buffer sets and the raw C-interface calls on them."""
 
-    def __init__(self, rn, torch, wl, rounding, inp, nsets, device):
+    def __init__(self, rn, torch, wl, rounding, inp, nsets, device, casts="float32"):
         from workloads import to_device
         self.rn, self.torch, self.wl, self.rounding = rn, torch, wl, rounding
         self.lib = rn.library()
@@ -117,6 +119,7 @@ class Sets:
         self.ws = torch.empty(max(self.wsb, 16) // 4, dtype=torch.float32, device=device)
         self.dt = rn.DTYPE_CODES[wl.dtype]
         self.rc = rn.ROUNDING_CODES[rounding]
+        self.bwd_rc = rn.bwd_rounding_code(rounding, casts)
 
     def stream(self):
         return self.torch.cuda.current_stream().cuda_stream
@@ -134,7 +137,7 @@ class Sets:
         st = self.lib.rmsnorm_bwd_rows(s["dy"].data_ptr(), wl.N, s["x"].data_ptr(), wl.N,
                                        self.w.data_ptr(), s["rstd"].data_ptr(), s["dx"].data_ptr(),
                                        wl.N, self.ws.data_ptr(), self.wsb, wl.M, wl.N, self.dt,
-                                       wl.offset, 0, self.stream())
+                                       wl.offset, self.bwd_rc, 0, self.stream())
         if st:
             raise RuntimeError(f"rmsnorm_bwd_rows status {st}")
 
@@ -277,7 +280,7 @@ def main(argv=None) -> int:
     rounding = args.rounding or wl.rounding
     inp = make_inputs(wl)
     nsets = max(4, -(-args.rotate_mib * 2**20 // (wl.M * wl.N * wl.itemsize)))
-    sets = Sets(rn, torch, wl, rounding, inp, nsets, "cuda:0")
+    sets = Sets(rn, torch, wl, rounding, inp, nsets, "cuda:0", casts=args.bwd_casts)
     for i in range(len(sets.sets)):  # every set gets a valid rstd cache
         sets.fwd(i)
     torch.cuda.synchronize()
@@ -333,6 +336,7 @@ def main(argv=None) -> int:
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": name, "M": wl.M, "N": wl.N, "rounding": rounding,
+                   "bwd_casts": args.bwd_casts,
                    "offset": wl.offset, "eps": wl.eps, "buffer_sets": len(sets.sets),
                    "graph": not args.no_graph},
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),

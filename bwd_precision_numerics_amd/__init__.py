@@ -25,6 +25,8 @@ HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "librmsnorm.h")
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 ROUNDING_CODES = {"once": 0, "twice": 1}
+BWD_AUTOGRAD_CASTS = 0x10  # flag OR-ed into the backward's rounding argument
+CASTS = ("float32", "autograd")
 VARIANT_CODES = {"auto": 0, "registers": 1, "lds": 2, "streaming": 3}
 STATUS_NAMES = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_MISALIGNED",
                 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
@@ -58,7 +60,7 @@ SIGNATURES = {
     "rmsnorm_bwd_variant": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p, _sz, _i64, _i64,
                                  _i, _f, _f, _i, _i, _p]),
     "rmsnorm_bwd_rows": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _sz, _i64, _i64, _i, _f,
-                              _i, _p]),
+                              _i, _i, _p]),
     "rmsnorm_bwd_dw_reduce": (_i, [_p, _sz, _p, _i64, _i64, _i, _p]),
     "rmsnorm_status_string": (ctypes.c_char_p, [_i]),
     "rmsnorm_abi_version": (_i, []),
@@ -208,9 +210,19 @@ def _workspace(M, N, dt, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+def bwd_rounding_code(rounding: str, casts: str) -> int:
+    """The backward's rounding argument: the convention, plus the autograd-casts flag."""
+    if casts not in CASTS:
+        raise ValueError(f"casts must be one of {CASTS}, got {casts!r}")
+    return ROUNDING_CODES[rounding] | (BWD_AUTOGRAD_CASTS if casts == "autograd" else 0)
+
+
 def bwd(dy, x, w, rstd, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twice",
-        variant: str = "auto", dx=None, dw=None, workspace=None):
-    """RMSNorm backward. Returns ``(dx, dw)``; ``dw`` is float32."""
+        variant: str = "auto", dx=None, dw=None, workspace=None, casts: str = "float32"):
+    """RMSNorm backward. Returns ``(dx, dw)``; ``dw`` is float32.
+
+    ``casts="autograd"`` reproduces the casts of differentiating the round-twice forward in T
+    (no effect for round once or float32); the default is the float32 backward."""
     torch = _torch()
     dt, M, N, dx = _bwd_common(dy, x, w, rstd, dx)
     if dw is None:
@@ -223,13 +235,15 @@ def bwd(dy, x, w, rstd, eps: float = 1e-6, offset: float = 0.0, rounding: str = 
     workspace, wsb = _workspace(M, N, dt, x.device, workspace)
     st = library().rmsnorm_bwd_variant(pdy, lddy, px, ldx, _vec(w, "w", N), _vec(rstd, "rstd", M),
                                        pdx, lddx, _vec(dw, "dw", N), workspace.data_ptr(), wsb, M,
-                                       N, DTYPE_CODES[dt], eps, offset, ROUNDING_CODES[rounding],
+                                       N, DTYPE_CODES[dt], eps, offset,
+                                       bwd_rounding_code(rounding, casts),
                                        VARIANT_CODES[variant], _stream(x.device))
     _check("rmsnorm_bwd", st)
     return dx, dw
 
 
-def bwd_rows(dy, x, w, rstd, workspace, offset: float = 0.0, variant: str = "auto", dx=None):
+def bwd_rows(dy, x, w, rstd, workspace, offset: float = 0.0, variant: str = "auto", dx=None,
+             rounding: str = "twice", casts: str = "float32"):
     """First backward stage: dx and the per-block dw partials (in ``workspace``)."""
     dt, M, N, dx = _bwd_common(dy, x, w, rstd, dx)
     pdy, lddy = _rows(dy, "dy")
@@ -238,7 +252,8 @@ def bwd_rows(dy, x, w, rstd, workspace, offset: float = 0.0, variant: str = "aut
     wsb = workspace.numel() * workspace.element_size()
     st = library().rmsnorm_bwd_rows(pdy, lddy, px, ldx, _vec(w, "w", N), _vec(rstd, "rstd", M),
                                     pdx, lddx, workspace.data_ptr(), wsb, M, N, DTYPE_CODES[dt],
-                                    offset, VARIANT_CODES[variant], _stream(x.device))
+                                    offset, bwd_rounding_code(rounding, casts),
+                                    VARIANT_CODES[variant], _stream(x.device))
     _check("rmsnorm_bwd_rows", st)
     return dx
 
@@ -259,23 +274,23 @@ def _make_autograd():
         """y = RMSNorm(x) * (offset + w) over the last dimension; backward through librmsnorm."""
 
         @staticmethod
-        def forward(ctx, x, w, eps, offset, rounding):
+        def forward(ctx, x, w, eps, offset, rounding, casts):
             shape = x.shape
             x2 = x.reshape(-1, shape[-1])
             y, rstd = fwd(x2, w, eps=eps, offset=offset, rounding=rounding)
             ctx.save_for_backward(x2, w, rstd)
-            ctx.cfg = (eps, offset, rounding, shape)
+            ctx.cfg = (eps, offset, rounding, shape, casts)
             return y.reshape(shape)
 
         @staticmethod
         def backward(ctx, gy):
             x2, w, rstd = ctx.saved_tensors
-            eps, offset, rounding, shape = ctx.cfg
+            eps, offset, rounding, shape, casts = ctx.cfg
             gy2 = gy.reshape(-1, shape[-1])
             if gy2.stride(-1) != 1:
                 gy2 = gy2.contiguous()
-            dx, dw = bwd(gy2, x2, w, rstd, eps=eps, offset=offset, rounding=rounding)
-            return dx.reshape(shape), dw.to(w.dtype), None, None, None
+            dx, dw = bwd(gy2, x2, w, rstd, eps=eps, offset=offset, rounding=rounding, casts=casts)
+            return dx.reshape(shape), dw.to(w.dtype), None, None, None, None
 
     return RMSNormFunction
 
@@ -283,9 +298,10 @@ def _make_autograd():
 _autograd_fn = None
 
 
-def rms_norm(x, w, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twice"):
+def rms_norm(x, w, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twice",
+             casts: str = "float32"):
     """Autograd-aware RMSNorm over the last dimension of ``x``."""
     global _autograd_fn
     if _autograd_fn is None:
         _autograd_fn = _make_autograd()
-    return _autograd_fn.apply(x, w, eps, offset, rounding)
+    return _autograd_fn.apply(x, w, eps, offset, rounding, casts)

@@ -32,6 +32,13 @@ int elem_bytes(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F32 ? 4 : 2; }
 int vec_elems(rmsnorm_dtype d) { return 16 / elem_bytes(d); }
 bool dtype_ok(int d) { return d == RMSNORM_DTYPE_F32 || d == RMSNORM_DTYPE_F16 || d == RMSNORM_DTYPE_BF16; }
 bool rounding_ok(int r) { return r == RMSNORM_ROUND_ONCE || r == RMSNORM_ROUND_TWICE; }
+// The backward's rounding argument may carry RMSNORM_BWD_AUTOGRAD_CASTS.
+bool bwd_rounding_ok(int r) { return rounding_ok(r & ~RMSNORM_BWD_AUTOGRAD_CASTS); }
+// The autograd casts only differ from the float32 backward for round twice in a 16-bit type.
+bool autograd_casts(int r, int dtype) {
+  return (r & RMSNORM_BWD_AUTOGRAD_CASTS) != 0 &&
+         (r & ~RMSNORM_BWD_AUTOGRAD_CASTS) == RMSNORM_ROUND_TWICE && dtype != RMSNORM_DTYPE_F32;
+}
 bool variant_ok(int v) { return v >= RMSNORM_VARIANT_AUTO && v <= RMSNORM_VARIANT_STREAMING; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -218,30 +225,31 @@ rmsnorm_status fwd_dispatch(const Plan& p, const FwdArgs& a, hipStream_t s) {
 #undef RMSN_FWD_CASE
 }
 
-template <DT D>
+template <DT D, bool AG>
 rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if (p.variant == RMSNORM_VARIANT_STREAMING) {
-    return p.wide ? launch(bwd_stream_kernel<D, true>, p.grid, block, p.lds, s, a)
-                  : launch(bwd_stream_kernel<D, false>, p.grid, block, p.lds, s, a);
+    return p.wide ? launch(bwd_stream_kernel<D, true, AG>, p.grid, block, p.lds, s, a)
+                  : launch(bwd_stream_kernel<D, false, AG>, p.grid, block, p.lds, s, a);
   }
   if (p.variant == RMSNORM_VARIANT_LDS) {
     switch (p.iters) {
-      case 1: return launch(bwd_lds_kernel<D, 1>, p.grid, block, p.lds, s, a);
-      case 2: return launch(bwd_lds_kernel<D, 2>, p.grid, block, p.lds, s, a);
-      case 3: return launch(bwd_lds_kernel<D, 3>, p.grid, block, p.lds, s, a);
-      case 4: return launch(bwd_lds_kernel<D, 4>, p.grid, block, p.lds, s, a);
+      case 1: return launch(bwd_lds_kernel<D, 1, AG>, p.grid, block, p.lds, s, a);
+      case 2: return launch(bwd_lds_kernel<D, 2, AG>, p.grid, block, p.lds, s, a);
+      case 3: return launch(bwd_lds_kernel<D, 3, AG>, p.grid, block, p.lds, s, a);
+      case 4: return launch(bwd_lds_kernel<D, 4, AG>, p.grid, block, p.lds, s, a);
       default: return RMSNORM_ERR_UNSUPPORTED;
     }
   }
   switch (p.iters) {
     case 1:
-      return launch(bwd_rows_kernel<D, 1, BwdPipe<1>::DEPTH, BwdPipe<1>::RB>, p.grid, block, p.lds,
-                    s, a);
+      return launch(bwd_rows_kernel<D, 1, BwdPipe<1>::DEPTH, BwdPipe<1>::RB, AG>, p.grid, block,
+                    p.lds, s, a);
     case 2:
-      return launch(bwd_rows_kernel<D, 2, BwdPipe<2>::DEPTH, BwdPipe<2>::RB>, p.grid, block, p.lds,
-                    s, a);
-    default: return RMSNORM_ERR_UNSUPPORTED;
+      return launch(bwd_rows_kernel<D, 2, BwdPipe<2>::DEPTH, BwdPipe<2>::RB, AG>, p.grid, block,
+                    p.lds, s, a);
+    default:
+      return RMSNORM_ERR_UNSUPPORTED;
   }
 }
 
@@ -307,10 +315,10 @@ size_t workspace_bytes(int64_t M, int64_t N) {
 rmsnorm_status check_bwd_rows(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                               const void* w, const float* rstd, void* dx, int64_t lddx,
                               void* workspace, size_t workspace_bytes_given, int64_t M, int64_t N,
-                              int dtype, float offset, int variant) {
+                              int dtype, float offset, int rounding, int variant) {
   rmsnorm_status st = check_common(M, N, dtype, 0.f, offset);
   if (st != RMSNORM_OK) return st;
-  if (!variant_ok(variant)) return RMSNORM_ERR_INVALID_ARG;
+  if (!variant_ok(variant) || !bwd_rounding_ok(rounding)) return RMSNORM_ERR_INVALID_ARG;
   const int eb = elem_bytes((rmsnorm_dtype)dtype);
   if ((st = check_matrix(dy, lddy, M, N, eb)) != RMSNORM_OK) return st;
   if ((st = check_matrix(x, ldx, M, N, eb)) != RMSNORM_OK) return st;
@@ -326,10 +334,10 @@ rmsnorm_status check_bwd_rows(const void* dy, int64_t lddy, const void* x, int64
 rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                              const void* w, const float* rstd, void* dx, int64_t lddx,
                              void* workspace, size_t workspace_bytes_given, int64_t M, int64_t N,
-                             rmsnorm_dtype dtype, float offset, rmsnorm_variant variant,
-                             void* stream) {
+                             rmsnorm_dtype dtype, float offset, int rounding,
+                             rmsnorm_variant variant, void* stream) {
   rmsnorm_status st = check_bwd_rows(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace,
-                                     workspace_bytes_given, M, N, dtype, offset, variant);
+                                     workspace_bytes_given, M, N, dtype, offset, rounding, variant);
   if (st != RMSNORM_OK) return st;
   const int eb = elem_bytes(dtype);
   const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) && wide_fits(dx, lddx, eb) &&
@@ -345,10 +353,14 @@ rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_
   a.N = (int)N; a.ldp = (int)partial_ld(N); a.P = (int)num_partials(M);
   a.tpr = p.tpr; a.groups = p.groups; a.offset = offset;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool ag = autograd_casts(rounding, dtype);
   switch (dtype) {
-    case RMSNORM_DTYPE_F32: return bwd_dispatch<DT::F32>(p, a, s);
-    case RMSNORM_DTYPE_F16: return bwd_dispatch<DT::F16>(p, a, s);
-    case RMSNORM_DTYPE_BF16: return bwd_dispatch<DT::BF16>(p, a, s);
+    case RMSNORM_DTYPE_F32:
+      return bwd_dispatch<DT::F32, false>(p, a, s);
+    case RMSNORM_DTYPE_F16:
+      return ag ? bwd_dispatch<DT::F16, true>(p, a, s) : bwd_dispatch<DT::F16, false>(p, a, s);
+    case RMSNORM_DTYPE_BF16:
+      return ag ? bwd_dispatch<DT::BF16, true>(p, a, s) : bwd_dispatch<DT::BF16, false>(p, a, s);
   }
   return RMSNORM_ERR_INVALID_ARG;
 }
@@ -376,14 +388,13 @@ rmsnorm_status dw_reduce_impl(const void* workspace, size_t workspace_bytes_give
 rmsnorm_status bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w,
                         const float* rstd, void* dx, int64_t lddx, float* dw, void* workspace,
                         size_t workspace_bytes_given, int64_t M, int64_t N, rmsnorm_dtype dtype,
-                        float eps, float offset, rmsnorm_rounding rounding,
-                        rmsnorm_variant variant, void* stream) {
+                        float eps, float offset, int rounding, rmsnorm_variant variant,
+                        void* stream) {
   // Validate everything (both stages) before enqueuing anything.
   rmsnorm_status st = check_common(M, N, dtype, eps, offset);
   if (st != RMSNORM_OK) return st;
-  if (!rounding_ok(rounding)) return RMSNORM_ERR_INVALID_ARG;
   if ((st = check_bwd_rows(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace, workspace_bytes_given,
-                           M, N, dtype, offset, variant)) != RMSNORM_OK)
+                           M, N, dtype, offset, rounding, variant)) != RMSNORM_OK)
     return st;
   if (dw == nullptr) return RMSNORM_ERR_INVALID_ARG;
   if (!aligned(dw, 4)) return RMSNORM_ERR_MISALIGNED;
@@ -395,7 +406,7 @@ rmsnorm_status bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx
     if ((st = plan_bwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
   }
   st = bwd_rows_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace, workspace_bytes_given, M, N,
-                     dtype, offset, variant, stream);
+                     dtype, offset, rounding, variant, stream);
   if (st != RMSNORM_OK) return st;
   return dw_reduce_impl(workspace, workspace_bytes_given, dw, M, N, dtype, stream);
 }
@@ -429,8 +440,7 @@ __attribute__((visibility("default"))) size_t rmsnorm_bwd_workspace_bytes(int64_
 __attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd(
     const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, const float* rstd,
     void* dx, int64_t lddx, float* dw, void* workspace, size_t workspace_bytes_given, int64_t M,
-    int64_t N, rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
-    void* stream) {
+    int64_t N, rmsnorm_dtype dtype, float eps, float offset, int rounding, void* stream) {
   return bwd_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, workspace, workspace_bytes_given, M, N,
                   dtype, eps, offset, rounding, RMSNORM_VARIANT_AUTO, stream);
 }
@@ -438,8 +448,8 @@ __attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd(
 __attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_variant(
     const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, const float* rstd,
     void* dx, int64_t lddx, float* dw, void* workspace, size_t workspace_bytes_given, int64_t M,
-    int64_t N, rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
-    rmsnorm_variant variant, void* stream) {
+    int64_t N, rmsnorm_dtype dtype, float eps, float offset, int rounding, rmsnorm_variant variant,
+    void* stream) {
   return bwd_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, workspace, workspace_bytes_given, M, N,
                   dtype, eps, offset, rounding, variant, stream);
 }
@@ -447,9 +457,9 @@ __attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_variant(
 __attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_rows(
     const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, const float* rstd,
     void* dx, int64_t lddx, void* workspace, size_t workspace_bytes_given, int64_t M, int64_t N,
-    rmsnorm_dtype dtype, float offset, rmsnorm_variant variant, void* stream) {
+    rmsnorm_dtype dtype, float offset, int rounding, rmsnorm_variant variant, void* stream) {
   return bwd_rows_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace, workspace_bytes_given, M, N,
-                       dtype, offset, variant, stream);
+                       dtype, offset, rounding, variant, stream);
 }
 
 __attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_dw_reduce(

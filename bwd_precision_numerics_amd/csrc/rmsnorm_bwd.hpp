@@ -9,6 +9,11 @@
 //   dw_j = sum over rows of dy_j * xhat_j         (float32; Liger-Kernel pull request 92 keeps the
 //                                                   weight gradient in float32)
 //
+// With AG (autograd casts; 16-bit T, round twice): g*dy is rounded to T before it enters the row
+// reduction and dx, and dw sums dy * T(xhat): the casts of differentiating the round-twice forward
+// computed in T (the Liger RMSNorm pull request, "feat: correct casts in RMSNorm to match
+// references", reproduces the references' casts in its backward).
+//
 // dw without atomics: block b of a persistent grid of P blocks owns rows b, b + P, b + 2P, ... (P
 // depends only on M, so the result does not depend on the device). Interleaving keeps the whole
 // grid on one contiguous stretch of rows at a time, which spreads DRAM traffic evenly; a block
@@ -116,7 +121,17 @@ __device__ __forceinline__ void group_sum_batch(float (&v)[RB], float* red, int 
 // s + 1 .. s + DEPTH are in flight, and one barrier serves all RB rows of a batch. Pass 1 upcasts
 // a raw row to form its dot product and its dw contributions; pass 2 upcasts it again for dx
 // (cheaper in registers than keeping xhat and g*dy). The gain g = offset + w stays in registers.
-template <DT D, int ITERS, int DEPTH, int RB>
+// g * dy and the value dw multiplies dy by, under the two backward readings.
+template <DT D, bool AG>
+__device__ __forceinline__ float gain_dy(float g, float dy) {
+  return AG ? round_trip<D>(g * dy) : g * dy;
+}
+template <DT D, bool AG>
+__device__ __forceinline__ float dw_factor(float xh) {
+  return AG ? round_trip<D>(xh) : xh;
+}
+
+template <DT D, int ITERS, int DEPTH, int RB, bool AG>
 __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -208,9 +223,11 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < V; e += 2) {
               const float xh0 = xf[e] * rs[k], xh1 = xf[e + 1] * rs[k];
-              const float gd0 = g[it][e] * df[e], gd1 = g[it][e + 1] * df[e + 1];
-              acc[it * V + e] = __builtin_fmaf(df[e], xh0, acc[it * V + e]);
-              acc[it * V + e + 1] = __builtin_fmaf(df[e + 1], xh1, acc[it * V + e + 1]);
+              const float gd0 = gain_dy<D, AG>(g[it][e], df[e]);
+              const float gd1 = gain_dy<D, AG>(g[it][e + 1], df[e + 1]);
+              acc[it * V + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh0), acc[it * V + e]);
+              acc[it * V + e + 1] =
+                  __builtin_fmaf(df[e + 1], dw_factor<D, AG>(xh1), acc[it * V + e + 1]);
               d0 = __builtin_fmaf(gd0, xh0, d0);
               d1 = __builtin_fmaf(gd1, xh1, d1);
             }
@@ -235,7 +252,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
               const float xh = xf[e] * rs[k];
-              const float gd = g[it][e] * df[e];
+              const float gd = gain_dy<D, AG>(g[it][e], df[e]);
               o[e] = rs[k] * (gd - xh * c);
             }
             const Raw out = IO::pack(o);
@@ -256,7 +273,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 // elementwise pass, so registers hold only the column accumulators and one row's loads in flight.
 // The gain is re-read from w (cache-resident) in each pass. Same thread-to-element mapping and
 // summation order as the register kernel, so dx is bit-identical to it for the same shape.
-template <DT D, int ITERS>
+template <DT D, int ITERS, bool AG>
 __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -318,8 +335,8 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const float xh = xf[e] * rs;
-        const float gd = (a.offset + wf[e]) * df[e];
-        acc[it * V + e] = __builtin_fmaf(df[e], xh, acc[it * V + e]);
+        const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
+        acc[it * V + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), acc[it * V + e]);
         if (e & 1) d1 = __builtin_fmaf(gd, xh, d1);
         else d0 = __builtin_fmaf(gd, xh, d0);
       }
@@ -340,7 +357,7 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const float xh = xf[e] * rs;
-          const float gd = (a.offset + wf[e]) * df[e];
+          const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
           o[e] = rs * (gd - xh * c);
         }
         const Raw out = IO::pack(o);
@@ -357,7 +374,7 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
 // Any N and any alignment. One row at a time per block (groups = 1); the elementwise pass reads
 // x and dy again, and the block's dw partial row accumulates in the workspace itself (each column
 // is owned by one thread, rows are added in order).
-template <DT D, bool WIDE>
+template <DT D, bool WIDE, bool AG>
 __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
   using IO = VecIO<D, WIDE>;
   using S = typename IO::S;
@@ -395,7 +412,7 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const float xh = xf[e] * rs;
-        const float gd = (a.offset + wf[e]) * df[e];
+        const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
         if (e & 1) d1 = __builtin_fmaf(gd, xh, d1);
         else d0 = __builtin_fmaf(gd, xh, d0);
       }
@@ -413,9 +430,9 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const float xh = xf[e] * rs;
-        const float gd = (a.offset + wf[e]) * df[e];
+        const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
         o[e] = rs * (gd - xh * c);
-        if (col + e < N) pr[col + e] = __builtin_fmaf(df[e], xh, pr[col + e]);
+        if (col + e < N) pr[col + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), pr[col + e]);
       }
       const auto out = IO::pack(o);
       if (full) IO::store(dxr + col, out);

@@ -35,7 +35,15 @@
  *     dx   = T( rstd * (gdy - xhat * c) )          each operation one float32 operation
  *     dw_j = sum_r dy_rj * xhat_rj                  float32, summed in a fixed order
  *
- * The backward is the same for both rounding conventions. dw is produced as per-block float32
+ * By default the backward is the same for both rounding conventions. With the flag
+ * RMSNORM_BWD_AUTOGRAD_CASTS it instead makes the casts of differentiating the round-twice forward
+ * computed in T (the Liger pull request says its backward reproduces the references' casts):
+ *
+ *     gdy  = T(g * dy)                              rounded to T before the reduction and dx
+ *     dw_j = sum_r dy_rj * T(xhat_rj)
+ *
+ * (no effect with RMSNORM_ROUND_ONCE, whose forward works in float32 until the store, or with
+ * float32 I/O). dw is produced as per-block float32
  * partial column sums in a caller-provided workspace followed by a second pass that adds the
  * partials in a fixed order: no floating-point atomics, so results are bit-reproducible run to run
  * and independent of the device's compute-unit count.
@@ -57,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBRMSNORM_ABI_VERSION 1
+#define LIBRMSNORM_ABI_VERSION 2
 /* Largest supported row width N. */
 #define RMSNORM_MAX_N (1 << 24)
 
@@ -71,6 +79,11 @@ typedef enum rmsnorm_rounding {
   RMSNORM_ROUND_ONCE = 0,  /* y = T(xhat * g)                (Gemma convention) */
   RMSNORM_ROUND_TWICE = 1  /* y = T(float(T(xhat)) * g)      (Llama convention) */
 } rmsnorm_rounding;
+
+/* Flag bit OR-ed into the backward's `rounding` argument (rmsnorm_bwd, rmsnorm_bwd_variant,
+ * rmsnorm_bwd_rows): reproduce the casts of the autograd backward of the round-twice forward (see
+ * above). The forward rejects it. */
+#define RMSNORM_BWD_AUTOGRAD_CASTS 0x10
 
 /* Kernel family. AUTO picks by dtype and N. The others force one family, for consistency tests
  * and measurements; a forced family that cannot serve the arguments returns
@@ -132,13 +145,15 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype dtype);
  *                 offset)
  *   workspace     device buffer of at least rmsnorm_bwd_workspace_bytes(M, N, dtype) bytes,
  *                 16-byte aligned; its contents on entry do not matter and are clobbered
- *   eps, rounding validated for symmetry with the forward; the backward reads rstd instead of
- *                 recomputing it and is the same for both rounding conventions
+ *   eps           validated for symmetry with the forward; the backward reads rstd instead of
+ *                 recomputing it
+ *   rounding      RMSNORM_ROUND_ONCE or RMSNORM_ROUND_TWICE, optionally OR-ed with
+ *                 RMSNORM_BWD_AUTOGRAD_CASTS; without the flag the result is the same for both
  * M = 0 writes dw = 0. All argument checks run before any HIP call. */
 rmsnorm_status rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                            const void* w, const float* rstd, void* dx, int64_t lddx, float* dw,
                            void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
-                           rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
+                           rmsnorm_dtype dtype, float eps, float offset, int rounding,
                            void* stream);
 
 /* rmsnorm_bwd with an explicit kernel family. */
@@ -146,8 +161,7 @@ rmsnorm_status rmsnorm_bwd_variant(const void* dy, int64_t lddy, const void* x, 
                                    const void* w, const float* rstd, void* dx, int64_t lddx,
                                    float* dw, void* workspace, size_t workspace_bytes, int64_t M,
                                    int64_t N, rmsnorm_dtype dtype, float eps, float offset,
-                                   rmsnorm_rounding rounding, rmsnorm_variant variant,
-                                   void* stream);
+                                   int rounding, rmsnorm_variant variant, void* stream);
 
 /* The two stages of rmsnorm_bwd, exported so each kernel can be enqueued (and timed) on its own.
  * rmsnorm_bwd_rows writes dx and the per-block dw partials into the workspace;
@@ -156,8 +170,8 @@ rmsnorm_status rmsnorm_bwd_variant(const void* dy, int64_t lddy, const void* x, 
 rmsnorm_status rmsnorm_bwd_rows(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                                 const void* w, const float* rstd, void* dx, int64_t lddx,
                                 void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
-                                rmsnorm_dtype dtype, float offset, rmsnorm_variant variant,
-                                void* stream);
+                                rmsnorm_dtype dtype, float offset, int rounding,
+                                rmsnorm_variant variant, void* stream);
 rmsnorm_status rmsnorm_bwd_dw_reduce(const void* workspace, size_t workspace_bytes, float* dw,
                                      int64_t M, int64_t N, rmsnorm_dtype dtype, void* stream);
 

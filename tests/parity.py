@@ -93,8 +93,10 @@ def check_fwd(y_gpu, rstd_gpu, x, w, *, eps, offset, rounding, dtype, rows=None)
     return stats
 
 
-def check_dx(dx_gpu, dy, x, w, rstd_gpu, *, offset, dtype) -> dict:
-    dx_o, _ = oracle.rmsnorm_bwd(dy, x, w, rstd_gpu, offset=offset, dtype=dtype)
+def check_dx(dx_gpu, dy, x, w, rstd_gpu, *, offset, dtype, rounding="twice",
+             casts="float32") -> dict:
+    dx_o, _ = oracle.rmsnorm_bwd(dy, x, w, rstd_gpu, offset=offset, dtype=dtype,
+                                 rounding=rounding, casts=casts)
     stats = {}
     if dtype == "f32":
         num = np.linalg.norm(dx_gpu.astype(np.float64) - dx_o)
@@ -121,6 +123,8 @@ def check_dw(dw_gpu, dw_oracle) -> dict:
     return stats
 
 
-def oracle_dw(dy, x, w, rstd_gpu, *, offset, dtype) -> np.ndarray:
-    _, dw = oracle.rmsnorm_bwd(dy, x, w, rstd_gpu, offset=offset, dtype=dtype)
+def oracle_dw(dy, x, w, rstd_gpu, *, offset, dtype, rounding="twice",
+              casts="float32") -> np.ndarray:
+    _, dw = oracle.rmsnorm_bwd(dy, x, w, rstd_gpu, offset=offset, dtype=dtype,
+                               rounding=rounding, casts=casts)
     return dw

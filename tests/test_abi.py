@@ -30,7 +30,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.rmsnorm_abi_version() == 1
+    assert lib.rmsnorm_abi_version() == 2
     for s in range(6):
         assert lib.rmsnorm_status_string(s)
     assert lib.rmsnorm_status_string(99) == b"unknown status"
@@ -69,11 +69,18 @@ def bwd(lib, dy=FAKE, lddy=8, x=FAKE + 0x1000, ldx=8, w=FAKE + 0x2000, rstd=FAKE
     (dict(N=(1 << 24) + 1, ldx=(1 << 24) + 1, ldy=(1 << 24) + 1), UNSUPPORTED),
     (dict(x=FAKE + 1), MISALIGNED), (dict(w=FAKE + 1), MISALIGNED), (dict(y=FAKE + 1), MISALIGNED),
     (dict(rstd=FAKE + 2), MISALIGNED), (dict(dtype=F32, x=FAKE + 2), MISALIGNED),
+    (dict(rounding=TWICE | 0x10), INVALID),                  # the autograd flag is backward-only
     (dict(M=2**62, ldx=8), INVALID),                        # row extent overflows int64
     (dict(N=70000, ldx=70000, ldy=70000, variant=1), UNSUPPORTED),  # register kernel too narrow
 ])
 def test_fwd_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+def test_bwd_accepts_the_autograd_flag_before_any_hip_call(lib):
+    # an otherwise invalid call still fails on the invalid argument, not on the flag
+    assert bwd(lib, rounding=TWICE | 0x10, wsb=0) == WORKSPACE
+    assert bwd(lib, rounding=ONCE | 0x10, wsb=0) == WORKSPACE
 
 
 def test_fwd_with_no_rows_is_a_noop(lib):
@@ -87,6 +94,7 @@ def test_fwd_with_no_rows_is_a_noop(lib):
     (dict(ws=None), INVALID), (dict(lddy=7), INVALID), (dict(ldx=7), INVALID),
     (dict(lddx=7), INVALID), (dict(M=-3), INVALID), (dict(N=0), INVALID),
     (dict(dtype=-1), INVALID), (dict(rounding=5), INVALID), (dict(variant=4), INVALID),
+    (dict(rounding=0x12), INVALID), (dict(rounding=0x20 | TWICE), INVALID),
     (dict(eps=float("-inf")), INVALID), (dict(offset=float("inf")), INVALID),
     (dict(wsb=4 * 8 * 4 - 1), WORKSPACE), (dict(wsb=0), WORKSPACE),
     (dict(ws=FAKE + 8), MISALIGNED), (dict(dw=FAKE + 2), MISALIGNED),
@@ -102,9 +110,11 @@ def test_bwd_rejects(lib, kw, status):
 
 def test_bwd_stages_reject(lib):
     assert lib.rmsnorm_bwd_rows(FAKE, 8, FAKE, 8, FAKE, FAKE, FAKE, 8, FAKE, 16, 4, 8, BF16, 0.0,
-                                0, None) == WORKSPACE
+                                TWICE, 0, None) == WORKSPACE
     assert lib.rmsnorm_bwd_rows(FAKE, 8, None, 8, FAKE, FAKE, FAKE, 8, FAKE, 1 << 20, 4, 8, BF16,
-                                0.0, 0, None) == INVALID
+                                0.0, TWICE, 0, None) == INVALID
+    assert lib.rmsnorm_bwd_rows(FAKE, 8, FAKE, 8, FAKE, FAKE, FAKE, 8, FAKE, 1 << 20, 4, 8, BF16,
+                                0.0, 0x12, 0, None) == INVALID
     assert lib.rmsnorm_bwd_dw_reduce(FAKE, 1 << 20, None, 4, 8, BF16, None) == INVALID
     assert lib.rmsnorm_bwd_dw_reduce(FAKE + 4, 1 << 20, FAKE, 4, 8, BF16, None) == MISALIGNED
     assert lib.rmsnorm_bwd_dw_reduce(FAKE, 4, FAKE, 4, 8, BF16, None) == WORKSPACE

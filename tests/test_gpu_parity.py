@@ -35,7 +35,7 @@ def padded(a: np.ndarray, dtype: str, ld: int):
 
 
 def run_case(dtype, M, N, rounding="twice", offset=0.0, eps=1e-6, ld=None, variant="auto",
-             seed=1, x_scale=None):
+             seed=1, casts="float32"):
     wl = WL[dtype].with_(rounding=rounding, offset=offset, eps=eps)
     inp = make_inputs(wl, M=M, N=N, seed=seed)
     x, w, dy = inp["x"], inp["w"], inp["dy"]
@@ -45,15 +45,17 @@ def run_case(dtype, M, N, rounding="twice", offset=0.0, eps=1e-6, ld=None, varia
         xt, dyt = padded(x, dtype, ld), padded(dy, dtype, ld)
     wt = to_device(w, dtype, DEV)
     print(f"case dtype={dtype} M={M} N={N} ld={ld} rounding={rounding} offset={offset} "
-          f"variant={variant} seed={seed}", flush=True)
+          f"variant={variant} seed={seed} casts={casts}", flush=True)
     y, rstd = rn.fwd(xt, wt, eps=eps, offset=offset, rounding=rounding, variant=variant)
     dx, dw = rn.bwd(dyt, xt, wt, rstd, eps=eps, offset=offset, rounding=rounding,
-                    variant=variant)
+                    variant=variant, casts=casts)
     torch.cuda.synchronize()
     yg, rg, dxg, dwg = to_np(y), to_np(rstd), to_np(dx), to_np(dw)
     st = check_fwd(yg, rg, x, w, eps=eps, offset=offset, rounding=rounding, dtype=dtype)
-    st.update(check_dx(dxg, dy, x, w, rg, offset=offset, dtype=dtype))
-    st.update(check_dw(dwg, oracle.rmsnorm_dw(dy, x, rg)))
+    st.update(check_dx(dxg, dy, x, w, rg, offset=offset, dtype=dtype, rounding=rounding,
+                       casts=casts))
+    st.update(check_dw(dwg, oracle.rmsnorm_dw(dy, x, rg, dtype=dtype, rounding=rounding,
+                                              casts=casts)))
     return st, (yg, rg, dxg, dwg)
 
 
@@ -88,6 +90,43 @@ def test_parity_shapes_round_twice(dtype, M, N, ld):
 @pytest.mark.parametrize("offset", [0.0, 1.0])
 def test_parity_round_once(dtype, M, N, ld, offset):
     run_case(dtype, M, N, rounding="once", offset=offset, ld=ld)
+
+
+@pytest.mark.parametrize("M,N,ld", [(300, 1000, None), (257, 3072, None), (129, 1027, None),
+                                    (40, 8192, None), (24, 16384, None), (12, 32768, None),
+                                    (3, 70000, None), (300, 1027, 1032)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_parity_autograd_casts(dtype, M, N, ld):
+    run_case(dtype, M, N, rounding="twice", ld=ld, casts="autograd")
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 1000), ("f16", 4096), ("bf16", 16384)])
+def test_autograd_casts_kernel_families_agree(dtype, N):
+    results = {}
+    for variant in ("registers", "lds", "streaming"):
+        try:
+            _, res = run_case(dtype, 70, N, variant=variant, seed=13, casts="autograd")
+        except rn.RMSNormError as e:
+            assert e.status == 2, e
+            continue
+        results[variant] = res
+    base = results["streaming"]
+    for v, res in results.items():
+        assert same_bits(res[2], base[2]).all(), v
+        assert np.allclose(res[3], base[3], rtol=1e-5, atol=1e-6)
+
+
+def test_autograd_flag_is_a_noop_for_round_once_and_f32():
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=128, N=2048, seed=14)
+    for dtype, rounding in (("bf16", "once"), ("f32", "twice")):
+        xt, wt, dyt = (to_device(inp[k], dtype, DEV) for k in ("x", "w", "dy"))
+        _, r = rn.fwd(xt, wt, rounding=rounding)
+        a = rn.bwd(dyt, xt, wt, r, rounding=rounding, casts="float32")
+        b = rn.bwd(dyt, xt, wt, r, rounding=rounding, casts="autograd")
+        torch.cuda.synchronize()
+        for p, q in zip(a, b):
+            assert same_bits(to_np(p), to_np(q)).all(), (dtype, rounding)
 
 
 @pytest.mark.parametrize("eps", [0.0, 1e-5, 0.25])

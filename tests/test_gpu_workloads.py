@@ -63,3 +63,17 @@ def test_full_size_workload(name):
             assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(dx).all())
             assert bool(torch.isfinite(dw).all())
         print(f"workload {name} {rounding}: {st}", flush=True)
+    if wl.dtype != "f32":
+        # the autograd-cast backward at full size, round twice
+        y, rstd = rn.fwd(xt, wt, eps=wl.eps, offset=wl.offset, rounding="twice")
+        dx, dw = rn.bwd(dyt, xt, wt, rstd, eps=wl.eps, offset=wl.offset, rounding="twice",
+                        casts="autograd")
+        torch.cuda.synchronize()
+        rows = sample_rows(wl.M, seed=1)
+        rt = torch.from_numpy(rows).to(DEV)
+        rg_all = to_np(rstd)
+        st = check_dx(to_np(dx.index_select(0, rt)), dy[rows], x[rows], w, rg_all[rows],
+                      offset=wl.offset, dtype=wl.dtype, rounding="twice", casts="autograd")
+        st.update(check_dw(to_np(dw), oracle.rmsnorm_dw(dy, x, rg_all, dtype=wl.dtype,
+                                                        rounding="twice", casts="autograd")))
+        print(f"workload {name} autograd casts: {st}", flush=True)
