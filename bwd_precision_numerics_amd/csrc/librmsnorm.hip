@@ -25,8 +25,14 @@ constexpr int kBwdLdsMaxIters = 4;      // backward LDS-staged kernel
 // Register backward pipeline per vectors-per-thread: rows per barrier (batch) and batches in flight
 // ahead of the current one. Ring registers: (DEPTH + 1) * RB * ITERS * 2 sixteen-byte vectors.
 template <int ITERS> struct BwdPipe;
-template <> struct BwdPipe<1> { static constexpr int RB = 1, DEPTH = 5; };
-template <> struct BwdPipe<2> { static constexpr int RB = 1, DEPTH = 1; };
+template <> struct BwdPipe<1> {
+  static constexpr int RB = 1, DEPTH = 5;
+  static constexpr bool KEEP = true;
+};
+template <> struct BwdPipe<2> {
+  static constexpr int RB = 1, DEPTH = 1;
+  static constexpr bool KEEP = false;
+};
 
 int elem_bytes(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F32 ? 4 : 2; }
 int vec_elems(rmsnorm_dtype d) { return 16 / elem_bytes(d); }
@@ -243,11 +249,11 @@ rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
   }
   switch (p.iters) {
     case 1:
-      return launch(bwd_rows_kernel<D, 1, BwdPipe<1>::DEPTH, BwdPipe<1>::RB, AG>, p.grid, block,
-                    p.lds, s, a);
+      return launch(bwd_rows_kernel<D, 1, BwdPipe<1>::DEPTH, BwdPipe<1>::RB, AG, BwdPipe<1>::KEEP>,
+                    p.grid, block, p.lds, s, a);
     case 2:
-      return launch(bwd_rows_kernel<D, 2, BwdPipe<2>::DEPTH, BwdPipe<2>::RB, AG>, p.grid, block,
-                    p.lds, s, a);
+      return launch(bwd_rows_kernel<D, 2, BwdPipe<2>::DEPTH, BwdPipe<2>::RB, AG, BwdPipe<2>::KEEP>,
+                    p.grid, block, p.lds, s, a);
     default:
       return RMSNORM_ERR_UNSUPPORTED;
   }

@@ -115,12 +115,6 @@ __device__ __forceinline__ void group_sum_batch(float (&v)[RB], float* red, int 
   }
 }
 
-// Register kernel. A row group takes its block's rows in batches of RB rows (local index
-// (s * RB + k) * groups + grp for step s and batch index k; row = b + local * P) and keeps a ring of
-// DEPTH + 1 batches of raw (x, dy) in registers: while batch s is reduced and written, batches
-// s + 1 .. s + DEPTH are in flight, and one barrier serves all RB rows of a batch. Pass 1 upcasts
-// a raw row to form its dot product and its dw contributions; pass 2 upcasts it again for dx
-// (cheaper in registers than keeping xhat and g*dy). The gain g = offset + w stays in registers.
 // g * dy and the value dw multiplies dy by, under the two backward readings.
 template <DT D, bool AG>
 __device__ __forceinline__ float gain_dy(float g, float dy) {
@@ -131,7 +125,14 @@ __device__ __forceinline__ float dw_factor(float xh) {
   return AG ? round_trip<D>(xh) : xh;
 }
 
-template <DT D, int ITERS, int DEPTH, int RB, bool AG>
+// Register kernel. A row group takes its block's rows in batches of RB rows (local index
+// (s * RB + k) * groups + grp for step s and batch index k; row = b + local * P) and keeps a ring of
+// DEPTH + 1 batches of raw (x, dy) in registers: while batch s is reduced and written, batches
+// s + 1 .. s + DEPTH are in flight, and one barrier serves all RB rows of a batch. Pass 1 upcasts
+// a raw row to form its dot product and its dw contributions; pass 2 either reuses xhat and g*dy
+// kept from pass 1 (KEEP: fewer VALU operations, more registers) or upcasts the raw row again.
+// The gain g = offset + w stays in registers.
+template <DT D, int ITERS, int DEPTH, int RB, bool AG, bool KEEP>
 __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -211,6 +212,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
       if (s < nsteps) {  // block-uniform
         if (s + DEPTH < nsteps) load_batch((j + DEPTH) % RING, s + DEPTH);
         float rs[RB], dot[RB];
+        float kx[KEEP ? RB : 1][KEEP ? ITERS * V : 1], kg[KEEP ? RB : 1][KEEP ? ITERS * V : 1];
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
           rs[k] = rr[j][k];
@@ -228,6 +230,12 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
               acc[it * V + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh0), acc[it * V + e]);
               acc[it * V + e + 1] =
                   __builtin_fmaf(df[e + 1], dw_factor<D, AG>(xh1), acc[it * V + e + 1]);
+              if constexpr (KEEP) {
+                kx[k][it * V + e] = xh0;
+                kx[k][it * V + e + 1] = xh1;
+                kg[k][it * V + e] = gd0;
+                kg[k][it * V + e + 1] = gd1;
+              }
               d0 = __builtin_fmaf(gd0, xh0, d0);
               d1 = __builtin_fmaf(gd1, xh1, d1);
             }
@@ -246,14 +254,21 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
           for (int it = 0; it < ITERS; ++it) {
             const int col = (it * TPR + tl) * V;
             if (col >= N) continue;
-            float xf[V], df[V], o[V];
-            IO::unpack(rx[j][k][it], xf);
-            IO::unpack(rd[j][k][it], df);
+            float o[V];
+            if constexpr (KEEP) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-              const float xh = xf[e] * rs[k];
-              const float gd = gain_dy<D, AG>(g[it][e], df[e]);
-              o[e] = rs[k] * (gd - xh * c);
+              for (int e = 0; e < V; ++e)
+                o[e] = rs[k] * (kg[k][it * V + e] - kx[k][it * V + e] * c);
+            } else {
+              float xf[V], df[V];
+              IO::unpack(rx[j][k][it], xf);
+              IO::unpack(rd[j][k][it], df);
+#pragma unroll
+              for (int e = 0; e < V; ++e) {
+                const float xh = xf[e] * rs[k];
+                const float gd = gain_dy<D, AG>(g[it][e], df[e]);
+                o[e] = rs[k] * (gd - xh * c);
+              }
             }
             const Raw out = IO::pack(o);
             if (col + V <= N) IO::store(dxr + col, out);
