@@ -9,12 +9,12 @@ this package. The GPU library and its Python binding never import it, and it imp
 them: the two share no code. Every function is pinned by CPU tests to values the pages print,
 closed forms, invariants, library conversions and float64 finite differences.
 """
-from .rounding import round_to_format, rne_bf16, rne_f16, rne_f32, rne_to, ulp_of
+from .rounding import round_to_format, rne_bf16, rne_f16, rne_f32, rne_fp8, rne_to, ulp_of
 from .rmsnorm import (CASTS, DTYPES, ROUNDINGS, apply_gain, gain, rmsnorm_bwd, rmsnorm_dw, rmsnorm_fwd,
-                      rstd_of)
+                      rmsnorm_fwd_fp8, rstd_of)
 
 __all__ = [
-    "round_to_format", "rne_bf16", "rne_f16", "rne_f32", "rne_to", "ulp_of",
+    "round_to_format", "rne_bf16", "rne_f16", "rne_f32", "rne_fp8", "rne_to", "ulp_of",
     "CASTS", "DTYPES", "ROUNDINGS", "apply_gain", "gain", "rmsnorm_bwd", "rmsnorm_dw", "rmsnorm_fwd",
-    "rstd_of",
+    "rmsnorm_fwd_fp8", "rstd_of",
 ]

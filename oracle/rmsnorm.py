@@ -67,7 +67,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .rounding import rne_f32, rne_to
+from .rounding import rne_f32, rne_fp8, rne_to
 
 DTYPES = ("f32", "f16", "bf16")
 ROUNDINGS = ("once", "twice")
@@ -141,6 +141,29 @@ def _autograd_casts(casts: str, rounding: str, dtype: str, exact: bool) -> bool:
         raise ValueError(f"casts must be one of {CASTS}, got {casts!r}")
     _check(dtype, rounding)
     return casts == "autograd" and rounding == "twice" and dtype != "f32" and not exact
+
+
+def rmsnorm_fwd_fp8(x, w, *, eps: float, scale: float, fmt: str = "e4m3", offset: float = 0.0,
+                    dtype: str = "bf16"):
+    """Forward with an 8-bit float output: normalization, gain and the per-tensor output scale all
+    in float32, then one cast to the OCP 8-bit format (the blog post "Den dolda avrundningen i
+    RMSNorm", section "Var implementationerna skiljer sig" and its footnote 3, on Transformer
+    Engine's FP8 output path):
+
+        y8 = RNE_fmt( fl( fl(xhat * g) * scale ) )
+
+    Returns ``(y8, rstd)`` with ``y8`` a float32 array holding 8-bit values (NaN where e4m3
+    overflows, +-inf where e5m2 does).
+    """
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
+    x = np.asarray(x)
+    rstd = rstd_of(x, eps)
+    with np.errstate(invalid="ignore", over="ignore"):
+        xhat = np.asarray(x, np.float32) * rstd[..., None]
+        yg = xhat * gain(w, offset)
+        y8 = rne_fp8(yg * np.float32(scale), fmt)
+    return y8, rstd
 
 
 def rmsnorm_bwd(dy, x, w, rstd, *, offset: float = 0.0, dtype: str = "bf16", exact: bool = False,

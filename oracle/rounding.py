@@ -1,8 +1,9 @@
-"""Round-to-nearest-even onto the bfloat16 and binary16 grids, written from the IEEE 754 definition.
+"""Round-to-nearest-even onto the bfloat16, binary16 and OCP 8-bit grids, written from the IEEE 754
+definition.
 
 TEST INFRASTRUCTURE ONLY: part of the CPU oracle (see ``oracle/__init__.py``).
 
-Both 16-bit formats of the path are binary floating-point formats described by three numbers:
+Each format of the path is a binary floating-point format described by three numbers:
 the significand precision ``p`` (hidden bit included), the smallest normal exponent ``emin`` and the
 largest exponent ``emax``. Rounding a real value ``v`` to such a format with ties-to-even means:
 
@@ -30,14 +31,23 @@ FORMATS = {
     "bf16": (8, -126, 127),
     "f16": (11, -14, 15),
     "f32": (24, -126, 127),
+    # OCP 8-bit formats. e5m2 follows the IEEE pattern (infinities at the top exponent). e4m3 has no
+    # infinities: its top exponent holds normal values except the all-ones code, which is NaN, so
+    # the largest finite value is 1.75 * 2^8 = 448 and anything that rounds beyond it is NaN.
+    "e4m3": (4, -6, 8),
+    "e5m2": (3, -14, 15),
 }
+# Largest finite value and what overflow becomes, where they differ from the IEEE pattern.
+_MAX_FINITE = {"e4m3": 448.0}
+_OVERFLOW_NAN = {"e4m3"}
 
 
 def round_to_format(v, fmt: str) -> np.ndarray:
     """Round each element of ``v`` (float32 or float64 input) to the nearest value of ``fmt``.
 
     Ties go to the even neighbour. Returns a float32 array whose values are exactly representable
-    in ``fmt`` (NaN, +-Inf and +-0 included). ``fmt`` is one of "bf16", "f16", "f32".
+    in ``fmt`` (NaN, +-Inf and +-0 included). ``fmt`` is one of "bf16", "f16", "f32", "e4m3",
+    "e5m2".
     For "f32" the input is expected in float64 and the result is the correctly rounded float32.
     """
     p, emin, emax = FORMATS[fmt]
@@ -52,9 +62,12 @@ def round_to_format(v, fmt: str) -> np.ndarray:
         spacing = np.ldexp(1.0, lead - (p - 1))
         # af / spacing is exact (power-of-two scaling in float64); rint rounds half to even.
         q = np.rint(af / spacing) * spacing
-        big = (2.0 - 2.0 ** (1 - p)) * 2.0 ** emax
-        q = np.where(np.abs(q) > big, np.copysign(np.inf, af), q)
+        big = _MAX_FINITE.get(fmt, (2.0 - 2.0 ** (1 - p)) * 2.0 ** emax)
+        over = np.nan if fmt in _OVERFLOW_NAN else np.inf
+        q = np.where(np.abs(q) > big, np.copysign(over, af), q)
         out[finite] = q
+    if fmt in _OVERFLOW_NAN:
+        out[np.isinf(a)] = np.nan
     return out.astype(np.float32)
 
 
@@ -71,6 +84,14 @@ def rne_f16(v) -> np.ndarray:
 def rne_f32(v) -> np.ndarray:
     """Round float64 values to float32 (nearest, ties to even)."""
     return round_to_format(v, "f32")
+
+
+def rne_fp8(v, fmt: str) -> np.ndarray:
+    """Round to an OCP 8-bit float format ("e4m3" or "e5m2"): nearest, ties to even; beyond the
+    largest finite value e5m2 gives an infinity and e4m3 (which has none) gives NaN."""
+    if fmt not in ("e4m3", "e5m2"):
+        raise ValueError(f"unknown 8-bit format {fmt!r}")
+    return round_to_format(v, fmt)
 
 
 def rne_to(v, dtype: str) -> np.ndarray:
