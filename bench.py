@@ -88,7 +88,8 @@ def parse_args(argv=None):
                     help="launch the timed steps eagerly instead of replaying a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget for the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--kernel-only", choices=["fwd", "bwd_rows", "dw_reduce"], default=None,
+    ap.add_argument("--kernel-only", choices=["fwd", "bwd_rows", "dw_reduce", "fwd_fp8"],
+                    default=None,
                     help="launch only this kernel --steps times (for counter collection)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, copy a buffer of this many MiB --steps times "
@@ -112,6 +113,7 @@ class Sets:
             s = {"x": x0.clone(), "dy": dy0.clone(),
                  "y": torch.empty_like(x0), "dx": torch.empty_like(x0),
                  "rstd": torch.empty(M, dtype=torch.float32, device=device),
+                 "y8": torch.empty((M, N), dtype=torch.uint8, device=device),
                  "dw": torch.empty(N, dtype=torch.float32, device=device)}
             self.sets.append(s)
         del x0, dy0
@@ -131,6 +133,16 @@ class Sets:
                                   wl.offset, self.rc, self.stream())
         if st:
             raise RuntimeError(f"rmsnorm_fwd status {st}")
+
+    def fwd_fp8(self, i):
+        """The forward with an e4m3 output (scale 1), same input and rstd cache."""
+        s, wl = self.sets[i], self.wl
+        st = self.lib.rmsnorm_fwd_fp8(s["x"].data_ptr(), wl.N, self.w.data_ptr(),
+                                      s["y8"].data_ptr(), wl.N, s["rstd"].data_ptr(), wl.M, wl.N,
+                                      self.dt, wl.eps, wl.offset, 1.0,
+                                      self.rn.FP8_CODES["e4m3"], 0, self.stream())
+        if st:
+            raise RuntimeError(f"rmsnorm_fwd_fp8 status {st}")
 
     def bwd_rows(self, i):
         s, wl = self.sets[i], self.wl
@@ -194,7 +206,7 @@ def kernel_durations(torch, sets, launches):
     out = {}
     n = len(sets.sets)
     for name, fn in (("fwd", sets.fwd), ("bwd_rows", sets.bwd_rows),
-                     ("dw_reduce", sets.dw_reduce)):
+                     ("dw_reduce", sets.dw_reduce), ("fwd_fp8", sets.fwd_fp8)):
         g = capture(torch, lambda k: fn(k % n), launches)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -286,8 +298,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     if args.kernel_only:
-        fn = {"fwd": sets.fwd, "bwd_rows": sets.bwd_rows, "dw_reduce": sets.dw_reduce}[
-            args.kernel_only]
+        fn = {"fwd": sets.fwd, "bwd_rows": sets.bwd_rows, "dw_reduce": sets.dw_reduce,
+              "fwd_fp8": sets.fwd_fp8}[args.kernel_only]
         for k in range(args.warmup + args.steps):
             fn(k % len(sets.sets))
         torch.cuda.synchronize()
@@ -319,6 +331,7 @@ def main(argv=None) -> int:
     del graph
     s = wl.itemsize
     rows_bytes = 3 * wl.M * wl.N * s + wl.N * s + 4 * wl.M
+    fp8_bytes = wl.M * wl.N * (s + 1) + wl.N * s + 4 * wl.M  # x, w in; y8, rstd out
     achieved = rows_bytes / dur["bwd_rows"] / 1e9
     traffic = read_traffic(name)
 
@@ -348,6 +361,7 @@ def main(argv=None) -> int:
                      "avg_us": round(dur["bwd_rows"] * 1e6, 3)},
         "kernels_us": {k: round(v * 1e6, 3) for k, v in dur.items()},
         "phase_GBps": {"fwd": round(wl.fwd_bytes() / dur["fwd"] / 1e9, 1),
+                       "fwd_fp8": round(fp8_bytes / dur["fwd_fp8"] / 1e9, 1),
                        "bwd": round(wl.bwd_bytes() / (dur["bwd_rows"] + dur["dw_reduce"]) / 1e9,
                                     1)},
         "copy_ceiling": copy,

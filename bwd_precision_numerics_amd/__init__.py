@@ -9,6 +9,7 @@ raises ``LibraryMissing`` (build it with ``python -m bwd_precision_numerics_amd.
     y, rstd = fwd(x, w, eps=1e-6, offset=0.0, rounding="twice")
     dx, dw  = bwd(dy, x, w, rstd, offset=0.0)
     y       = rms_norm(x, w, eps, offset, rounding)        # autograd-aware
+    y8, rstd = fwd_fp8(x, w, scale=1.0, fmt="e4m3")        # OCP 8-bit output
 
 ``rounding="twice"`` is the Llama convention T(float(T(xhat)) * g); ``"once"`` is the Gemma
 convention T(xhat * g); the gain is ``g = offset + w`` (offset 1 for Gemma).
@@ -28,6 +29,7 @@ ROUNDING_CODES = {"once": 0, "twice": 1}
 BWD_AUTOGRAD_CASTS = 0x10  # flag OR-ed into the backward's rounding argument
 CASTS = ("float32", "autograd")
 VARIANT_CODES = {"auto": 0, "registers": 1, "lds": 2, "streaming": 3}
+FP8_CODES = {"e4m3": 0, "e5m2": 1}
 STATUS_NAMES = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_MISALIGNED",
                 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
@@ -54,6 +56,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "rmsnorm_fwd": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i, _f, _f, _i, _p]),
     "rmsnorm_fwd_variant": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i, _f, _f, _i, _i, _p]),
+    "rmsnorm_fwd_fp8": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i, _f, _f, _f, _i, _i,
+                             _p]),
     "rmsnorm_bwd_workspace_bytes": (_sz, [_i64, _i64, _i]),
     "rmsnorm_bwd": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p, _sz, _i64, _i64, _i, _f,
                          _f, _i, _p]),
@@ -181,6 +185,48 @@ def fwd(x, w, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twice",
                                        offset, ROUNDING_CODES[rounding], VARIANT_CODES[variant],
                                        _stream(x.device))
     _check("rmsnorm_fwd", st)
+    return y, rstd
+
+
+def fp8_torch_dtype(fmt: str):
+    torch = _torch()
+    return {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+
+
+def fwd_fp8(x, w, eps: float = 1e-6, offset: float = 0.0, scale: float = 1.0,
+            fmt: str = "e4m3", variant: str = "auto", y=None, rstd=None, want_rstd: bool = True):
+    """RMSNorm forward with an 8-bit output ``FP8(fl(xhat * g) * scale)``.
+
+    Returns ``(y8, rstd)``; y8 is ``torch.float8_e4m3fn`` or ``torch.float8_e5m2`` (or the
+    caller's ``y``, which may also be uint8). ``rstd`` equals the one ``fwd`` writes.
+    """
+    torch = _torch()
+    dt = dtype_name(x)
+    if fmt not in FP8_CODES:
+        raise ValueError(f"fmt must be one of {sorted(FP8_CODES)}")
+    if w.dtype != x.dtype:
+        raise TypeError("w must have the dtype of x")
+    M, N = x.shape
+    px, ldx = _rows(x, "x")
+    pw = _vec(w, "w", N)
+    if y is None:
+        y = torch.empty((M, N), dtype=fp8_torch_dtype(fmt), device=x.device)
+    if y.dtype not in (fp8_torch_dtype(fmt), torch.uint8) or tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be [M, N] of {fp8_torch_dtype(fmt)} or uint8")
+    py, ldy = _rows(y, "y")
+    if want_rstd and rstd is None:
+        rstd = torch.empty((M,), dtype=torch.float32, device=x.device)
+    prs = None
+    if rstd is not None:
+        if rstd.dtype != torch.float32:
+            raise TypeError("rstd must be float32")
+        prs = _vec(rstd, "rstd", M)
+        _same_device(x, rstd)
+    _same_device(x, w, y)
+    st = library().rmsnorm_fwd_fp8(px, ldx, pw, py, ldy, prs, M, N, DTYPE_CODES[dt], eps, offset,
+                                   scale, FP8_CODES[fmt], VARIANT_CODES[variant],
+                                   _stream(x.device))
+    _check("rmsnorm_fwd_fp8", st)
     return y, rstd
 
 

@@ -204,18 +204,18 @@ rmsnorm_status launch(Kernel k, int64_t grid, int block, size_t lds, hipStream_t
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
 }
 
-template <DT D, bool TWICE>
+template <DT D, Out O>
 rmsnorm_status fwd_dispatch(const Plan& p, const FwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if (p.variant == RMSNORM_VARIANT_STREAMING) {
-    return p.wide ? launch(fwd_stream_kernel<D, true, TWICE>, p.grid, block, p.lds, s, a)
-                  : launch(fwd_stream_kernel<D, false, TWICE>, p.grid, block, p.lds, s, a);
+    return p.wide ? launch(fwd_stream_kernel<D, true, O>, p.grid, block, p.lds, s, a)
+                  : launch(fwd_stream_kernel<D, false, O>, p.grid, block, p.lds, s, a);
   }
   const bool lds = p.variant == RMSNORM_VARIANT_LDS;
-#define RMSN_FWD_CASE(IT)                                                                  \
-  case IT:                                                                                 \
-    return lds ? launch(fwd_rows_kernel<D, IT, TWICE, true>, p.grid, block, p.lds, s, a)   \
-               : launch(fwd_rows_kernel<D, IT, TWICE, false>, p.grid, block, p.lds, s, a);
+#define RMSN_FWD_CASE(IT)                                                              \
+  case IT:                                                                             \
+    return lds ? launch(fwd_rows_kernel<D, IT, O, true>, p.grid, block, p.lds, s, a)   \
+               : launch(fwd_rows_kernel<D, IT, O, false>, p.grid, block, p.lds, s, a);
   switch (p.iters) {
     RMSN_FWD_CASE(1)
     RMSN_FWD_CASE(2)
@@ -280,19 +280,38 @@ bool wide_fits(const void* p, int64_t ld, int eb) {
   return aligned(p, 16) && ((ld * eb) % 16 == 0);
 }
 
+template <Out O>
+rmsnorm_status fwd_by_dtype(rmsnorm_dtype dtype, const Plan& p, const FwdArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case RMSNORM_DTYPE_F32:  // the two conventions coincide for float32 I/O
+      return fwd_dispatch<DT::F32, O == Out::TWICE ? Out::ONCE : O>(p, a, s);
+    case RMSNORM_DTYPE_F16:
+      return fwd_dispatch<DT::F16, O>(p, a, s);
+    case RMSNORM_DTYPE_BF16:
+      return fwd_dispatch<DT::BF16, O>(p, a, s);
+  }
+  return RMSNORM_ERR_INVALID_ARG;
+}
+
+// Shared by the T-output and 8-bit-output forwards: y holds `yb` bytes per element; its 16-byte
+// input vectors map to V * yb output bytes, which the vector store needs aligned. The kernel and
+// its summation order depend on x and w alone: a y that does not allow vector stores is written
+// one element at a time by the same kernel, so rstd does not depend on where y lives.
 rmsnorm_status fwd_impl(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
                         float* rstd, int64_t M, int64_t N, rmsnorm_dtype dtype, float eps,
-                        float offset, rmsnorm_rounding rounding, rmsnorm_variant variant,
+                        float offset, float scale, Out out, rmsnorm_variant variant,
                         void* stream) {
   rmsnorm_status st = check_common(M, N, dtype, eps, offset);
   if (st != RMSNORM_OK) return st;
-  if (!rounding_ok(rounding) || !variant_ok(variant)) return RMSNORM_ERR_INVALID_ARG;
+  if (!variant_ok(variant) || !std::isfinite(scale)) return RMSNORM_ERR_INVALID_ARG;
   const int eb = elem_bytes(dtype);
+  const int yb = is_f8(out) ? 1 : eb;
   if ((st = check_matrix(x, ldx, M, N, eb)) != RMSNORM_OK) return st;
-  if ((st = check_matrix(y, ldy, M, N, eb)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(y, ldy, M, N, yb)) != RMSNORM_OK) return st;
   if (M > 0 && w == nullptr) return RMSNORM_ERR_INVALID_ARG;
   if (!aligned(w, (uintptr_t)eb) || !aligned(rstd, 4)) return RMSNORM_ERR_MISALIGNED;
-  const bool wide = wide_fits(x, ldx, eb) && wide_fits(y, ldy, eb) && aligned(w, 16);
+  const int yvec = vec_elems(dtype) * yb;  // output bytes per 16-byte input vector
+  const bool wide = wide_fits(x, ldx, eb) && aligned(w, 16);
   Plan p;
   if ((st = plan_fwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
   if (M == 0) return RMSNORM_OK;
@@ -300,18 +319,24 @@ rmsnorm_status fwd_impl(const void* x, int64_t ldx, const void* w, void* y, int6
   FwdArgs a;
   a.x = x; a.w = w; a.y = y; a.rstd = rstd;
   a.ldx = ldx; a.ldy = ldy; a.M = M; a.N = (int)N;
-  a.tpr = p.tpr; a.groups = p.groups; a.eps = eps; a.offset = offset;
+  a.tpr = p.tpr; a.groups = p.groups; a.eps = eps; a.offset = offset; a.scale = scale;
+  a.yvec = aligned(y, (uintptr_t)yvec) && (ldy * yb) % yvec == 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool twice = rounding == RMSNORM_ROUND_TWICE;
-  switch (dtype) {
-    case RMSNORM_DTYPE_F32:  // the two conventions coincide for float32 I/O
-      return fwd_dispatch<DT::F32, false>(p, a, s);
-    case RMSNORM_DTYPE_F16:
-      return twice ? fwd_dispatch<DT::F16, true>(p, a, s) : fwd_dispatch<DT::F16, false>(p, a, s);
-    case RMSNORM_DTYPE_BF16:
-      return twice ? fwd_dispatch<DT::BF16, true>(p, a, s) : fwd_dispatch<DT::BF16, false>(p, a, s);
+  switch (out) {
+    case Out::ONCE: return fwd_by_dtype<Out::ONCE>(dtype, p, a, s);
+    case Out::TWICE: return fwd_by_dtype<Out::TWICE>(dtype, p, a, s);
+    case Out::E4M3: return fwd_by_dtype<Out::E4M3>(dtype, p, a, s);
+    case Out::E5M2: return fwd_by_dtype<Out::E5M2>(dtype, p, a, s);
   }
   return RMSNORM_ERR_INVALID_ARG;
+}
+
+rmsnorm_status fwd_t(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy, float* rstd,
+                     int64_t M, int64_t N, rmsnorm_dtype dtype, float eps, float offset,
+                     rmsnorm_rounding rounding, rmsnorm_variant variant, void* stream) {
+  if (!rounding_ok(rounding)) return RMSNORM_ERR_INVALID_ARG;
+  const Out out = rounding == RMSNORM_ROUND_TWICE ? Out::TWICE : Out::ONCE;
+  return fwd_impl(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, 1.0f, out, variant, stream);
 }
 
 size_t workspace_bytes(int64_t M, int64_t N) {
@@ -426,15 +451,24 @@ __attribute__((visibility("default"))) rmsnorm_status rmsnorm_fwd(
     const void* x, int64_t ldx, const void* w, void* y, int64_t ldy, float* rstd, int64_t M,
     int64_t N, rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
     void* stream) {
-  return fwd_impl(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, rounding,
-                  RMSNORM_VARIANT_AUTO, stream);
+  return fwd_t(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, rounding, RMSNORM_VARIANT_AUTO,
+               stream);
 }
 
 __attribute__((visibility("default"))) rmsnorm_status rmsnorm_fwd_variant(
     const void* x, int64_t ldx, const void* w, void* y, int64_t ldy, float* rstd, int64_t M,
     int64_t N, rmsnorm_dtype dtype, float eps, float offset, rmsnorm_rounding rounding,
     rmsnorm_variant variant, void* stream) {
-  return fwd_impl(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, rounding, variant, stream);
+  return fwd_t(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, rounding, variant, stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_fwd_fp8(
+    const void* x, int64_t ldx, const void* w, void* y, int64_t ldy, float* rstd, int64_t M,
+    int64_t N, rmsnorm_dtype dtype, float eps, float offset, float scale,
+    rmsnorm_fp8_format format, rmsnorm_variant variant, void* stream) {
+  if (format != RMSNORM_FP8_E4M3 && format != RMSNORM_FP8_E5M2) return RMSNORM_ERR_INVALID_ARG;
+  const Out out = format == RMSNORM_FP8_E4M3 ? Out::E4M3 : Out::E5M2;
+  return fwd_impl(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, scale, out, variant, stream);
 }
 
 __attribute__((visibility("default"))) size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N,

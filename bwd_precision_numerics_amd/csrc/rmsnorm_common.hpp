@@ -141,6 +141,32 @@ template <DT D> struct VecIO<D, false> {
   static __device__ __forceinline__ Raw pack(const float (&f)[1]) { return from_f32<D>(f[0]); }
 };
 
+// ---- OCP 8-bit outputs ----------------------------------------------------------------------------
+// gfx950 converts packed float32 pairs to e4m3 (fp8) or e5m2 (bf8) with round-to-nearest-even;
+// overflow gives NaN in e4m3 (no infinities) and an infinity in e5m2.
+enum class F8 : int { E4M3 = 0, E5M2 = 1 };
+
+template <F8 F>
+__device__ __forceinline__ uint32_t cvt_pair_f8(float a, float b, uint32_t old, bool hi) {
+  a = materialize(a);
+  b = materialize(b);
+  if constexpr (F == F8::E4M3) {
+    return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true)
+              : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+  } else {
+    return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, true)
+              : (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, false);
+  }
+}
+template <F8 F>
+__device__ __forceinline__ uint32_t cvt4_f8(float a, float b, float c, float d) {
+  return cvt_pair_f8<F>(c, d, cvt_pair_f8<F>(a, b, 0u, false), true);
+}
+template <F8 F>
+__device__ __forceinline__ uint8_t cvt1_f8(float a) {
+  return (uint8_t)(cvt_pair_f8<F>(a, 0.f, 0u, false) & 0xffu);
+}
+
 // float -> T -> float (the inner cast of the round-twice convention); identity for fp32.
 template <DT D> __device__ __forceinline__ float round_trip(float f) {
   if constexpr (D == DT::F32) {

@@ -5,6 +5,10 @@
 //   rstd = 1 / sqrt(sum(x^2) / N + eps)           float32; epsilon under the root
 //   xhat = x * rstd                                 formed first
 //   y    = T(float(T(xhat)) * g)   (round twice)    or   T(xhat * g)   (round once),  g = offset + w
+//   y8   = FP8(fl(xhat * g) * scale)                  (8-bit output; the blog post's section "Var
+//                                                      implementationerna skiljer sig" and footnote
+//                                                      3: normalization, gain and the per-tensor
+//                                                      scale in float32, then one cast)
 //
 // Work decomposition: a row is owned by a group of TPR threads (TPR = 64 * wpr, one or more
 // wavefronts); a block holds `groups` such rows. Thread tl of a group owns the 16-byte vectors
@@ -22,28 +26,82 @@ namespace rmsn {
 struct FwdArgs {
   const void* x;
   const void* w;
-  void* y;
+  void* y;      // T elements, or bytes for the 8-bit outputs
   float* rstd;  // may be null
   int64_t ldx, ldy, M;
   int N;
   int tpr;     // threads per row, multiple of 64
   int groups;  // rows per block
-  float eps, offset;
+  int yvec;    // y and ldy allow one vector store per 16-byte input vector
+  float eps, offset, scale;
 };
 
-template <DT D, bool TWICE, int V>
+// Output of the forward: the two rounding conventions in T, or an OCP 8-bit format.
+enum class Out : int { ONCE = 0, TWICE = 1, E4M3 = 2, E5M2 = 3 };
+constexpr bool is_f8(Out o) { return o == Out::E4M3 || o == Out::E5M2; }
+constexpr F8 f8_of(Out o) { return o == Out::E4M3 ? F8::E4M3 : F8::E5M2; }
+
+template <DT D, Out O, int V>
 __device__ __forceinline__ void apply_gain(const float (&xf)[V], const float (&wf)[V], float rs,
-                                           float offset, float (&yf)[V]) {
+                                           float offset, float scale, float (&yf)[V]) {
 #pragma unroll
   for (int e = 0; e < V; ++e) {
     const float xh = xf[e] * rs;
     const float g = offset + wf[e];
-    yf[e] = TWICE ? round_trip<D>(xh) * g : xh * g;
+    if constexpr (O == Out::TWICE) yf[e] = round_trip<D>(xh) * g;
+    else if constexpr (O == Out::ONCE) yf[e] = xh * g;
+    else yf[e] = materialize(xh * g) * scale;
   }
 }
 
+// Writes V output values at element column `col` of row yr (n valid values): T elements through
+// VecIO, or one byte per value for the 8-bit outputs (a 16-byte input vector of 8 16-bit values
+// gives 8 bytes, of 4 float32 values 4 bytes). `vec` (uniform) allows the single vector store;
+// without it the values go out one element at a time, so the alignment of y never changes the
+// kernel's loads or its summation order.
+template <DT D, Out O, bool WIDE, int V>
+__device__ __forceinline__ void store_out(void* yrow, int col, int n, bool vec,
+                                          const float (&yf)[V]) {
+  if constexpr (!is_f8(O)) {
+    using IO = VecIO<D, WIDE>;
+    using S = typename IO::S;
+    S* yr = static_cast<S*>(yrow);
+    const auto out = IO::pack(yf);
+    if (vec && n >= V) IO::store(yr + col, out);
+    else IO::store_part(yr + col, out, n);
+  } else {
+    constexpr F8 F = f8_of(O);
+    uint8_t* yr = static_cast<uint8_t*>(yrow) + col;
+    if constexpr (V == 8) {
+      if (vec && n >= 8) {
+        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t v = {cvt4_f8<F>(yf[0], yf[1], yf[2], yf[3]),
+                           cvt4_f8<F>(yf[4], yf[5], yf[6], yf[7])};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(yr));
+        return;
+      }
+    } else if constexpr (V == 4) {
+      if (vec && n >= 4) {
+        __builtin_nontemporal_store(cvt4_f8<F>(yf[0], yf[1], yf[2], yf[3]),
+                                    reinterpret_cast<uint32_t*>(yr));
+        return;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+      if (e < n) yr[e] = cvt1_f8<F>(yf[e]);
+  }
+}
+
+// Row pointer of the output (element stride ldy; bytes for the 8-bit outputs).
+template <DT D, Out O>
+__device__ __forceinline__ void* out_row(void* y, int64_t row, int64_t ldy) {
+  if constexpr (is_f8(O)) return static_cast<uint8_t*>(y) + row * ldy;
+  else return static_cast<typename Elem<D>::S*>(y) + row * ldy;
+}
+
 // Row held in registers (STAGE_LDS = false) or staged in LDS (true) between the two passes.
-template <DT D, int ITERS, bool TWICE, bool STAGE_LDS>
+template <DT D, int ITERS, Out O, bool STAGE_LDS>
 __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -97,26 +155,23 @@ __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
   if (!valid) return;
   if (tl == 0 && a.rstd) a.rstd[row] = rs;
 
-  S* yr = static_cast<S*>(a.y) + row * a.ldy;
+  void* yr = out_row<D, O>(a.y, row, a.ldy);
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
     if (col >= N) continue;
-    const bool full = col + V <= N;
     const Raw r = STAGE_LDS ? stage[it * TPR + tl] : raw[it];
     float xf[V], wf[V], yf[V];
     IO::unpack(r, xf);
     IO::unpack(wraw[it], wf);
-    apply_gain<D, TWICE, V>(xf, wf, rs, a.offset, yf);
-    const Raw out = IO::pack(yf);
-    if (full) IO::store(yr + col, out);
-    else IO::store_part(yr + col, out, N - col);
+    apply_gain<D, O, V>(xf, wf, rs, a.offset, a.scale, yf);
+    store_out<D, O, true, V>(yr, col, N - col, a.yvec != 0, yf);
   }
 }
 
 // Any N and any alignment: the elementwise pass reads x again (from cache) instead of keeping it.
 // WIDE selects 16-byte vectors or single elements.
-template <DT D, bool WIDE, bool TWICE>
+template <DT D, bool WIDE, Out O>
 __global__ void __launch_bounds__(1024) fwd_stream_kernel(FwdArgs a) {
   using IO = VecIO<D, WIDE>;
   using S = typename IO::S;
@@ -153,7 +208,7 @@ __global__ void __launch_bounds__(1024) fwd_stream_kernel(FwdArgs a) {
   if (tl == 0 && a.rstd) a.rstd[row] = rs;
 
   const S* wr = static_cast<const S*>(a.w);
-  S* yr = static_cast<S*>(a.y) + row * a.ldy;
+  void* yr = out_row<D, O>(a.y, row, a.ldy);
   for (int v = tl; v < nv; v += TPR) {
     const int col = v * V;
     const bool full = col + V <= N;
@@ -162,10 +217,8 @@ __global__ void __launch_bounds__(1024) fwd_stream_kernel(FwdArgs a) {
     float xf[V], wf[V], yf[V];
     IO::unpack(r, xf);
     IO::unpack(wv, wf);
-    apply_gain<D, TWICE, V>(xf, wf, rs, a.offset, yf);
-    const auto out = IO::pack(yf);
-    if (full) IO::store(yr + col, out);
-    else IO::store_part(yr + col, out, N - col);
+    apply_gain<D, O, V>(xf, wf, rs, a.offset, a.scale, yf);
+    store_out<D, O, WIDE, V>(yr, col, N - col, a.yvec != 0, yf);
   }
 }
 

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBRMSNORM_ABI_VERSION 2
+#define LIBRMSNORM_ABI_VERSION 3
 /* Largest supported row width N. */
 #define RMSNORM_MAX_N (1 << 24)
 
@@ -84,6 +84,12 @@ typedef enum rmsnorm_rounding {
  * rmsnorm_bwd_rows): reproduce the casts of the autograd backward of the round-twice forward (see
  * above). The forward rejects it. */
 #define RMSNORM_BWD_AUTOGRAD_CASTS 0x10
+
+/* OCP 8-bit output formats of rmsnorm_fwd_fp8 (1 sign bit, then exponent and significand bits). */
+typedef enum rmsnorm_fp8_format {
+  RMSNORM_FP8_E4M3 = 0,  /* bias 7, largest finite 448, no infinities: overflow gives NaN */
+  RMSNORM_FP8_E5M2 = 1   /* bias 15, largest finite 57344, IEEE-style: overflow gives +-inf */
+} rmsnorm_fp8_format;
 
 /* Kernel family. AUTO picks by dtype and N. The others force one family, for consistency tests
  * and measurements; a forced family that cannot serve the arguments returns
@@ -129,6 +135,28 @@ rmsnorm_status rmsnorm_fwd_variant(const void* x, int64_t ldx, const void* w, vo
                                    float* rstd, int64_t M, int64_t N, rmsnorm_dtype dtype,
                                    float eps, float offset, rmsnorm_rounding rounding,
                                    rmsnorm_variant variant, void* stream);
+
+/* Forward with an OCP 8-bit output (blog post "Den dolda avrundningen i RMSNorm", section
+ * "Var implementationerna skiljer sig" and its footnote 3: a fused kernel that emits FP8 keeps the
+ * normalization, the gain and the per-tensor scale in float32 and casts once at the store):
+ *
+ *     y8 = FP8( fl(xhat * g) * scale )      one float32 multiply each, then one cast
+ *
+ * FP8(.) rounds to nearest, ties to even, and does not saturate: a value beyond the format's
+ * largest finite one becomes NaN (e4m3) or +-inf (e5m2), the behaviour of a plain conversion.
+ * rstd is computed exactly as by rmsnorm_fwd (same summation order: bit-identical values) and is
+ * written when not NULL.
+ *   x, ldx, w, rstd, M, N, dtype, eps, offset, variant   as for rmsnorm_fwd_variant
+ *   y, ldy     output rows, one byte per element; row stride in bytes (= elements), >= N
+ *   scale      finite float32 per-tensor scale applied after the gain (1 for none)
+ *   format     RMSNORM_FP8_E4M3 or RMSNORM_FP8_E5M2
+ * The vector path needs y and ldy aligned to the bytes one 16-byte input vector maps to (8 for
+ * 16-bit input, 4 for float32); otherwise the element-wise path serves the call. All argument
+ * checks run before any HIP call. */
+rmsnorm_status rmsnorm_fwd_fp8(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
+                               float* rstd, int64_t M, int64_t N, rmsnorm_dtype dtype, float eps,
+                               float offset, float scale, rmsnorm_fp8_format format,
+                               rmsnorm_variant variant, void* stream);
 
 /* Bytes of device workspace rmsnorm_bwd needs for an [M, N] problem: the float32 partial column
  * sums of dw, one row per block of rows. A pure function of (M, N, dtype): it makes no HIP call

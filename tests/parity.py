@@ -128,3 +128,38 @@ def oracle_dw(dy, x, w, rstd_gpu, *, offset, dtype, rounding="twice",
     _, dw = oracle.rmsnorm_bwd(dy, x, w, rstd_gpu, offset=offset, dtype=dtype,
                                rounding=rounding, casts=casts)
     return dw
+
+
+FP8_BITEXACT_FRAC = 0.999
+FP8_MAX_ULPS = 1
+
+
+def check_fwd_fp8(y8_gpu, rstd_gpu, x, w, *, eps, offset, scale, fmt, dtype) -> dict:
+    """Check an 8-bit forward result (y8_gpu: float32 values of the 8-bit outputs).
+
+    * rstd: as for the T-output forward.
+    * conditioned on the GPU's rstd: the oracle's elementwise steps reproduce y8 bit for bit
+      (NaN where e4m3 overflows, +-inf where e5m2 does, signed zeros distinguished).
+    * unconditioned: >= 99.9 % bit-identical to the oracle, every finite element within one step
+      of the 8-bit grid (a 1-ulp change of rstd moves fl(xhat * g) by about one float32 ulp, which
+      can cross one rounding boundary of the 8-bit format), non-finite elements identical.
+    """
+    x = np.asarray(x, np.float32)
+    y_o, r_o = oracle.rmsnorm_fwd_fp8(x, w, eps=eps, scale=scale, fmt=fmt, offset=offset,
+                                      dtype=dtype)
+    stats = check_rstd(rstd_gpu, r_o)
+    with np.errstate(invalid="ignore", over="ignore"):
+        xhat = x * np.asarray(rstd_gpu, np.float32)[:, None]
+        y_c = oracle.rne_fp8((xhat * oracle.gain(w, offset)) * np.float32(scale), fmt)
+    cond = same_bits(y8_gpu, y_c)
+    stats["y8_conditioned_bitexact"] = float(cond.mean()) if cond.size else 1.0
+    assert cond.all(), (stats, np.argwhere(~cond)[:5])
+    eq = same_bits(y8_gpu, y_o)
+    stats["y8_bitexact"] = float(eq.mean()) if eq.size else 1.0
+    assert stats["y8_bitexact"] >= FP8_BITEXACT_FRAC, stats
+    fin = np.isfinite(y_o) & np.isfinite(y8_gpu)
+    assert np.all(eq | fin), stats  # NaN / inf only where the oracle has the same
+    d = ulps(y8_gpu[fin], y_o[fin], fmt)
+    stats["y8_max_ulp"] = float(d.max()) if d.size else 0.0
+    assert np.all(d <= FP8_MAX_ULPS), stats
+    return stats

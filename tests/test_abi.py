@@ -30,7 +30,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.rmsnorm_abi_version() == 2
+    assert lib.rmsnorm_abi_version() == 3
     for s in range(6):
         assert lib.rmsnorm_status_string(s)
     assert lib.rmsnorm_status_string(99) == b"unknown status"
@@ -75,6 +75,33 @@ def bwd(lib, dy=FAKE, lddy=8, x=FAKE + 0x1000, ldx=8, w=FAKE + 0x2000, rstd=FAKE
 ])
 def test_fwd_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+def fwd8(lib, x=FAKE, ldx=8, w=FAKE, y=FAKE + 0x1000, ldy=8, rstd=None, M=4, N=8, dtype=BF16,
+         eps=1e-6, offset=0.0, scale=1.0, fmt=0, variant=0):
+    return lib.rmsnorm_fwd_fp8(x, ldx, w, y, ldy, rstd, M, N, dtype, eps, offset, scale, fmt,
+                               variant, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(w=None), INVALID),
+    (dict(fmt=2), INVALID), (dict(fmt=-1), INVALID), (dict(variant=4), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(dtype=5), INVALID), (dict(ldy=7), INVALID),
+    (dict(x=FAKE + 1), MISALIGNED), (dict(rstd=FAKE + 2), MISALIGNED),
+    (dict(N=(1 << 24) + 1, ldx=(1 << 24) + 1, ldy=(1 << 24) + 1), UNSUPPORTED),
+    # a forced register or LDS kernel needs 16-byte loads of x and w (y's alignment only picks
+    # the store width)
+    (dict(x=FAKE + 2, variant=1), UNSUPPORTED), (dict(ldx=9, variant=2), UNSUPPORTED),
+    (dict(dtype=F32, w=FAKE + 4, variant=1), UNSUPPORTED),
+])
+def test_fwd_fp8_rejects(lib, kw, status):
+    assert fwd8(lib, **kw) == status
+
+
+def test_fwd_fp8_with_no_rows_is_a_noop(lib):
+    assert fwd8(lib, x=None, w=None, y=None, M=0) == OK
+    assert fwd8(lib, x=None, w=None, y=None, M=0, fmt=1, scale=-3.0) == OK
 
 
 def test_bwd_accepts_the_autograd_flag_before_any_hip_call(lib):

@@ -341,3 +341,24 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for a, b in zip(ref, (y, r, dx, dw)):
             assert same_bits(a, to_np(b)).all(), rep
+
+
+@pytest.mark.parametrize("dtype,off", [("bf16", 1), ("f16", 3), ("f32", 1)])
+def test_fwd_output_alignment_only_changes_the_stores(dtype, off):
+    """A y that does not allow 16-byte stores (base off by `off` elements) is written element by
+    element by the same kernel: y and rstd equal those of an aligned y, bit for bit."""
+    wl = WL[dtype]
+    M, N = 130, 2048
+    inp = make_inputs(wl, M=M, N=N, seed=21)
+    xt, wt = to_device(inp["x"], dtype, DEV), to_device(inp["w"], dtype, DEV)
+    print(f"case dtype={dtype} M={M} N={N} y offset={off}", flush=True)
+    y_a, r_a = rn.fwd(xt, wt)
+    buf = torch.zeros(M * N + off + 8, dtype=xt.dtype, device=DEV)
+    y_u = buf[off:off + M * N].view(M, N)
+    _, r_u = rn.fwd(xt, wt, y=y_u)
+    torch.cuda.synchronize()
+    assert same_bits(to_np(y_u), to_np(y_a)).all()
+    assert same_bits(to_np(r_u), to_np(r_a)).all()
+    st = check_fwd(to_np(y_u), to_np(r_u), inp["x"], inp["w"], eps=wl.eps, offset=0.0,
+                   rounding="twice", dtype=dtype)
+    print(st)
