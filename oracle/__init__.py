@@ -1,4 +1,4 @@
-"""CPU oracle for the RMSNorm forward/backward path — TEST INFRASTRUCTURE, NOT PRODUCT CODE.
+"""CPU oracle for the RMSNorm forward/backward path (and LayerNorm / GroupNorm) — TEST INFRASTRUCTURE, NOT PRODUCT CODE.
 
 A plain, slow, directly checkable NumPy implementation of what the GPU library computes: float64
 reductions, float32 elementwise arithmetic emulated with NumPy float32 operations, and
@@ -12,9 +12,11 @@ closed forms, invariants, library conversions and float64 finite differences.
 from .rounding import round_to_format, rne_bf16, rne_f16, rne_f32, rne_fp8, rne_to, ulp_of
 from .rmsnorm import (CASTS, DTYPES, ROUNDINGS, apply_gain, gain, rmsnorm_bwd, rmsnorm_dw, rmsnorm_fwd,
                       rmsnorm_fwd_fp8, rstd_of)
+from .layernorm import groupnorm_bwd, groupnorm_fwd, layernorm_bwd, layernorm_fwd, row_stats
 
 __all__ = [
     "round_to_format", "rne_bf16", "rne_f16", "rne_f32", "rne_fp8", "rne_to", "ulp_of",
     "CASTS", "DTYPES", "ROUNDINGS", "apply_gain", "gain", "rmsnorm_bwd", "rmsnorm_dw", "rmsnorm_fwd",
     "rmsnorm_fwd_fp8", "rstd_of",
+    "groupnorm_bwd", "groupnorm_fwd", "layernorm_bwd", "layernorm_fwd", "row_stats",
 ]
