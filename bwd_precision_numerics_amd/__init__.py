@@ -10,6 +10,8 @@ raises ``LibraryMissing`` (build it with ``python -m bwd_precision_numerics_amd.
     dx, dw  = bwd(dy, x, w, rstd, offset=0.0)
     y       = rms_norm(x, w, eps, offset, rounding)        # autograd-aware
     y8, rstd = fwd_fp8(x, w, scale=1.0, fmt="e4m3")        # OCP 8-bit output
+    y, mean, rstd = layernorm_fwd(x, w, b, eps=1e-5)       # LayerNorm (b may be None)
+    dx, dw, db    = layernorm_bwd(dy, x, w, mean, rstd, bias=True)
 
 ``rounding="twice"`` is the Llama convention T(float(T(xhat)) * g); ``"once"`` is the Gemma
 convention T(xhat * g); the gain is ``g = offset + w`` (offset 1 for Gemma).
@@ -23,6 +25,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librmsnorm.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "librmsnorm.h")
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(HERE), "include", "libnorms.h")]
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 ROUNDING_CODES = {"once": 0, "twice": 1}
@@ -66,16 +69,25 @@ SIGNATURES = {
     "rmsnorm_bwd_rows": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _sz, _i64, _i64, _i, _f,
                               _i, _i, _p]),
     "rmsnorm_bwd_dw_reduce": (_i, [_p, _sz, _p, _i64, _i64, _i, _p]),
+    "layernorm_fwd": (_i, [_p, _i64, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i, _f, _i, _p]),
+    "layernorm_bwd_workspace_bytes": (_sz, [_i64, _i64, _i]),
+    "layernorm_bwd": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _i64, _i64,
+                           _i, _i, _p]),
     "rmsnorm_status_string": (ctypes.c_char_p, [_i]),
     "rmsnorm_abi_version": (_i, []),
 }
 
 
-def header_functions(path: str = HEADER_PATH) -> list:
-    """Names of the functions the C header declares."""
-    text = open(path, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rmsnorm_[a-z_0-9]+)\s*\(", text)))
+def header_text(paths=None) -> str:
+    """The C headers' text without comments."""
+    text = "\n".join(open(p, encoding="utf-8").read() for p in (paths or HEADER_PATHS))
+    return re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+
+
+def header_functions(paths=None) -> list:
+    """Names of the functions the C headers declare."""
+    return sorted(set(re.findall(r"\b((?:rmsnorm|layernorm|groupnorm)_[a-z_0-9]+)\s*\(",
+                                 header_text(paths))))
 
 
 def library(path: str | None = None) -> ctypes.CDLL:
@@ -311,6 +323,84 @@ def dw_reduce(workspace, dw, M: int, N: int, dtype: str):
                                          DTYPE_CODES[dtype], _stream(dw.device))
     _check("rmsnorm_bwd_dw_reduce", st)
     return dw
+
+
+# ---- LayerNorm --------------------------------------------------------------------------------------
+
+def layernorm_workspace_bytes(M: int, N: int, dtype: str) -> int:
+    return int(library().layernorm_bwd_workspace_bytes(M, N, DTYPE_CODES[dtype]))
+
+
+def _opt_vec(t, name, n, dtype):
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}")
+    return _vec(t, name, n)
+
+
+def layernorm_fwd(x, w, b=None, eps: float = 1e-5, variant: str = "auto", y=None, mean=None,
+                  rstd=None, want_stats: bool = True):
+    """LayerNorm over the last dimension of a 2-D ``x``. Returns ``(y, mean, rstd)`` (the float32
+    caches are None when ``want_stats`` is False)."""
+    torch = _torch()
+    dt = dtype_name(x)
+    M, N = x.shape
+    px, ldx = _rows(x, "x")
+    pw = _opt_vec(w, "w", N, x.dtype)
+    pb = _opt_vec(b, "b", N, x.dtype)
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if y.dtype != x.dtype or tuple(y.shape) != (M, N):
+        raise ValueError("y must match x in shape and dtype")
+    py, ldy = _rows(y, "y")
+    if want_stats:
+        mean = torch.empty((M,), dtype=torch.float32, device=x.device) if mean is None else mean
+        rstd = torch.empty((M,), dtype=torch.float32, device=x.device) if rstd is None else rstd
+    pm = _opt_vec(mean, "mean", M, torch.float32)
+    pr = _opt_vec(rstd, "rstd", M, torch.float32)
+    _same_device(*[t for t in (x, w, b, y, mean, rstd) if t is not None])
+    st = library().layernorm_fwd(px, ldx, pw, pb, py, ldy, pm, pr, M, N, DTYPE_CODES[dt], eps,
+                                 VARIANT_CODES[variant], _stream(x.device))
+    _check("layernorm_fwd", st)
+    return y, mean, rstd
+
+
+def layernorm_bwd(dy, x, w, mean, rstd, bias: bool = True, variant: str = "auto", dx=None,
+                  dw=None, db=None, workspace=None):
+    """LayerNorm backward. Returns ``(dx, dw, db)``; dw, db float32 (db None if not ``bias``)."""
+    torch = _torch()
+    dt = dtype_name(x)
+    if dy.dtype != x.dtype or w.dtype != x.dtype:
+        raise TypeError("dy and w must have the dtype of x")
+    if tuple(dy.shape) != tuple(x.shape):
+        raise ValueError("dy must have the shape of x")
+    M, N = x.shape
+    if dx is None:
+        dx = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if dx.dtype != x.dtype or tuple(dx.shape) != (M, N):
+        raise ValueError("dx must match x in shape and dtype")
+    if dw is None:
+        dw = torch.empty((N,), dtype=torch.float32, device=x.device)
+    if bias and db is None:
+        db = torch.empty((N,), dtype=torch.float32, device=x.device)
+    pdy, lddy = _rows(dy, "dy")
+    px, ldx = _rows(x, "x")
+    pdx, lddx = _rows(dx, "dx")
+    need = layernorm_workspace_bytes(M, N, dt)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _same_device(*[t for t in (dy, x, w, mean, rstd, dx, dw, db, workspace) if t is not None])
+    st = library().layernorm_bwd(pdy, lddy, px, ldx, _vec(w, "w", N),
+                                 _opt_vec(mean, "mean", M, torch.float32),
+                                 _opt_vec(rstd, "rstd", M, torch.float32), pdx, lddx,
+                                 _opt_vec(dw, "dw", N, torch.float32),
+                                 _opt_vec(db, "db", N, torch.float32) if bias else None,
+                                 workspace.data_ptr(), wsb, M, N, DTYPE_CODES[dt],
+                                 VARIANT_CODES[variant], _stream(x.device))
+    _check("layernorm_bwd", st)
+    return dx, dw, (db if bias else None)
 
 
 def _make_autograd():

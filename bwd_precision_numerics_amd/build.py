@@ -1,5 +1,8 @@
 """Compile the HIP library ``librmsnorm.so`` for gfx950, in place next to this file.
 
+The library is built from two translation units: ``librmsnorm.hip`` (the RMSNorm entry points of
+``include/librmsnorm.h``) and ``libnorms.hip`` (LayerNorm and GroupNorm, ``include/libnorms.h``).
+
 Usage: ``python -m bwd_precision_numerics_amd.build [--resource-usage FILE]``.
 
 Flags:
@@ -20,11 +23,12 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "librmsnorm.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("librmsnorm.hip", "libnorms.hip")]
 OUT = os.path.join(HERE, "librmsnorm.so")
 HEADERS = [os.path.join(HERE, "csrc", f) for f in
-           ("rmsnorm_common.hpp", "rmsnorm_fwd.hpp", "rmsnorm_bwd.hpp")]
-HEADERS.append(os.path.join(ROOT, "include", "librmsnorm.h"))
+           ("host_common.hpp", "rmsnorm_common.hpp", "rmsnorm_fwd.hpp", "rmsnorm_bwd.hpp",
+            "layernorm.hpp")]
+HEADERS += [os.path.join(ROOT, "include", f) for f in ("librmsnorm.h", "libnorms.h")]
 
 
 def hipcc() -> str:
@@ -46,7 +50,7 @@ def flags() -> list:
 def build(resource_usage: str | None = None, verbose: bool = False) -> str:
     """Compile librmsnorm.so (always recompiles). Returns the path of the library."""
     tmp = OUT + ".tmp"
-    cmd = [hipcc()] + flags() + [SRC, "-o", tmp]
+    cmd = [hipcc()] + flags() + SRCS + ["-o", tmp]
     if resource_usage:
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
     if verbose:

@@ -1,0 +1,462 @@
+// LayerNorm forward and backward kernels (row-wise over the last dimension).
+//
+// Forward, per row (candle pull request 4059, "Add backward passes to the fused rms_norm,
+// layer_norm and softmax_last_dim ops": float32 statistics for the 16-bit types, one cast at the
+// store; Liger-Kernel pull request 1608, "fix(group_norm): keep the backward statistics and
+// reductions in fp32": mean and rstd kept in float32 for the backward):
+//   mean = (sum_j x_j) / N,   var = (sum_j (x_j - mean)^2) / N,   rstd = 1 / sqrt(var + eps)
+//   y    = T( (x - mean) * rstd * w + b )          each step one float32 operation, left to right
+// The row stays in registers, so the variance is taken about the mean in a second pass over the
+// registers rather than as E[x^2] - mean^2 (which cancels when the mean is large against the
+// spread).
+//
+// Backward, from the float32 mean and rstd caches, inputs upcast on load:
+//   xhat = (x - mean) * rstd,  gdy = w * dy,  c1 = (sum_j gdy_j) / N,  c2 = (sum_j gdy_j xhat_j) / N
+//   dx   = T( rstd * ((gdy - c1) - xhat * c2) )
+//   dw_j = sum over rows of dy_j * xhat_j,  db_j = sum over rows of dy_j      (float32)
+// dw and db come from the same persistent-grid partials as the RMSNorm backward (no atomics): the
+// workspace holds [2][P][ldp] floats, the dw partial rows then the db partial rows, each reduced in
+// a fixed order by dw_reduce_kernel.
+#pragma once
+
+#include "rmsnorm_bwd.hpp"
+#include "rmsnorm_fwd.hpp"
+
+namespace rmsn {
+
+struct LnFwdArgs {
+  const void* x;
+  const void* w;
+  const void* b;  // may be null (no bias)
+  void* y;
+  float* mean;    // may be null
+  float* rstd;    // may be null
+  int64_t ldx, ldy, M;
+  int N;
+  int tpr;     // threads per row, multiple of 64
+  int groups;  // rows per block
+  int yvec;    // y and ldy allow 16-byte stores
+  float eps;
+};
+
+// y for V elements of one vector: ((x - mean) * rstd) * w (+ b), one float32 operation each.
+template <int V, bool HAS_B>
+__device__ __forceinline__ void ln_affine(const float (&xf)[V], const float (&wf)[V],
+                                          const float (&bf)[V], float mean, float rs,
+                                          float (&yf)[V]) {
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const float xh = (xf[e] - mean) * rs;
+    yf[e] = HAS_B ? xh * wf[e] + bf[e] : xh * wf[e];
+  }
+}
+
+// Centred squares of the valid elements of one vector (elements at or past N excluded).
+template <int V>
+__device__ __forceinline__ void add_centred_squares(const float (&f)[V], float mean, int n,
+                                                    float& q0, float& q1) {
+  if (n >= V) {
+#pragma unroll
+    for (int e = 0; e < V; e += 2) {
+      const float d0 = f[e] - mean, d1 = f[e + 1] - mean;
+      q0 = __builtin_fmaf(d0, d0, q0);
+      q1 = __builtin_fmaf(d1, d1, q1);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float d = e < n ? f[e] - mean : 0.f;
+      if (e & 1) q1 = __builtin_fmaf(d, d, q1);
+      else q0 = __builtin_fmaf(d, d, q0);
+    }
+  }
+}
+
+// Register kernel: the row (and w, b) stays in registers through the two reductions and the store.
+// LDS: two reduction slots of wpr floats per row group.
+template <DT D, int ITERS, bool HAS_B>
+__global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
+  using IO = VecIO<D, true>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+  float* red = reinterpret_cast<float*>(smem) + grp * 2 * wpr;
+
+  const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+  const S* wr = static_cast<const S*>(a.w);
+  const S* br = static_cast<const S*>(a.b);
+  Raw raw[ITERS], wraw[ITERS], braw[HAS_B ? ITERS : 1];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    Raw r = IO::zero(), rw = IO::zero(), rb = IO::zero();
+    if (valid) {
+      if (col + V <= N) {
+        r = IO::load(xr + col);
+        rw = IO::load(wr + col);
+        if constexpr (HAS_B) rb = IO::load(br + col);
+      } else if (col < N) {
+        r = IO::load_part(xr + col, N - col);
+        rw = IO::load_part(wr + col, N - col);
+        if constexpr (HAS_B) rb = IO::load_part(br + col, N - col);
+      }
+    }
+    raw[it] = r;
+    wraw[it] = rw;
+    if constexpr (HAS_B) braw[it] = rb;
+  }
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    float f[V];
+    IO::unpack(raw[it], f);
+#pragma unroll
+    for (int e = 0; e < V; e += 2) {
+      s0 += f[e];
+      s1 += f[e + 1];
+    }
+  }
+  const float mean = group_sum(s0 + s1, red, wpr, tl) / (float)N;
+  float q0 = 0.f, q1 = 0.f;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    float f[V];
+    IO::unpack(raw[it], f);
+    add_centred_squares<V>(f, mean, N - col, q0, q1);
+  }
+  const float var = group_sum(q0 + q1, red + wpr, wpr, tl) / (float)N;
+  const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
+  if (!valid) return;
+  if (tl == 0) {
+    if (a.mean) a.mean[row] = mean;
+    if (a.rstd) a.rstd[row] = rs;
+  }
+  void* yr = out_row<D, Out::ONCE>(a.y, row, a.ldy);
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    if (col >= N) continue;
+    float xf[V], wf[V], bf[V], yf[V];
+    IO::unpack(raw[it], xf);
+    IO::unpack(wraw[it], wf);
+    if constexpr (HAS_B) IO::unpack(braw[it], bf);
+    ln_affine<V, HAS_B>(xf, wf, bf, mean, rs, yf);
+    store_out<D, Out::ONCE, true, V>(yr, col, N - col, a.yvec != 0, yf);
+  }
+}
+
+// Any N and any alignment: three passes over the row (sum, centred squares, store), reading x again
+// from the caches. Same thread-to-element mapping and summation order as the register kernel.
+template <DT D, bool WIDE, bool HAS_B>
+__global__ void __launch_bounds__(1024) ln_fwd_stream_kernel(LnFwdArgs a) {
+  using IO = VecIO<D, WIDE>;
+  using S = typename IO::S;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int nv = (N + V - 1) / V;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+  float* red = reinterpret_cast<float*>(smem) + grp * 2 * wpr;
+  const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+
+  float s0 = 0.f, s1 = 0.f;
+  if (valid) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      float f[V];
+      IO::unpack(col + V <= N ? IO::load(xr + col) : IO::load_part(xr + col, N - col), f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (e & 1) s1 += f[e];
+        else s0 += f[e];
+      }
+    }
+  }
+  const float mean = group_sum(s0 + s1, red, wpr, tl) / (float)N;
+  float q0 = 0.f, q1 = 0.f;
+  if (valid) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      float f[V];
+      IO::unpack(col + V <= N ? IO::load(xr + col) : IO::load_part(xr + col, N - col), f);
+      add_centred_squares<V>(f, mean, N - col, q0, q1);
+    }
+  }
+  const float var = group_sum(q0 + q1, red + wpr, wpr, tl) / (float)N;
+  const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
+  if (!valid) return;
+  if (tl == 0) {
+    if (a.mean) a.mean[row] = mean;
+    if (a.rstd) a.rstd[row] = rs;
+  }
+  const S* wr = static_cast<const S*>(a.w);
+  const S* br = static_cast<const S*>(a.b);
+  void* yr = out_row<D, Out::ONCE>(a.y, row, a.ldy);
+  for (int v = tl; v < nv; v += TPR) {
+    const int col = v * V;
+    const bool full = col + V <= N;
+    float xf[V], wf[V], bf[V], yf[V];
+    IO::unpack(full ? IO::load(xr + col) : IO::load_part(xr + col, N - col), xf);
+    IO::unpack(full ? IO::load(wr + col) : IO::load_part(wr + col, N - col), wf);
+    if constexpr (HAS_B)
+      IO::unpack(full ? IO::load(br + col) : IO::load_part(br + col, N - col), bf);
+    ln_affine<V, HAS_B>(xf, wf, bf, mean, rs, yf);
+    store_out<D, Out::ONCE, WIDE, V>(yr, col, N - col, a.yvec != 0, yf);
+  }
+}
+
+struct LnBwdArgs {
+  const void* dy;
+  const void* x;
+  const void* w;
+  const float* mean;
+  const float* rstd;
+  void* dx;
+  float* part;  // [2][P][ldp]: dw partial rows, then db partial rows
+  int64_t lddy, ldx, lddx, M;
+  int N, ldp, P;
+  int tpr;     // threads per row, multiple of 64
+  int groups;  // rows processed concurrently per block
+};
+
+// Register kernel on the persistent grid of the RMSNorm backward (block b owns rows b, b + P, ...).
+// A ring of DEPTH + 1 rows of raw (x, dy) and their (mean, rstd) per row group keeps DEPTH rows in
+// flight while one is reduced and written. HAS_DB adds the bias-gradient accumulators.
+template <DT D, int ITERS, int DEPTH, bool HAS_DB>
+__global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
+  using IO = VecIO<D, true>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  constexpr int V = IO::V;
+  constexpr int RING = DEPTH + 1;
+  constexpr int K = ITERS * V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, G = a.groups, N = a.N;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int b = blockIdx.x, P = a.P;
+  const int64_t nloc = block_rows(a.M, P, b);
+  const int nsteps = (int)((nloc + G - 1) / G);
+  float* red = reinterpret_cast<float*>(smem);  // [2][G][wpr][2]
+
+  const S* dyb = static_cast<const S*>(a.dy);
+  const S* xb = static_cast<const S*>(a.x);
+  S* dxb = static_cast<S*>(a.dx);
+
+  float g[ITERS][V];
+  {
+    const S* wr = static_cast<const S*>(a.w);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      Raw r = IO::zero();
+      if (col + V <= N) r = IO::load(wr + col);
+      else if (col < N) r = IO::load_part(wr + col, N - col);
+      IO::unpack(r, g[it]);
+    }
+  }
+  float accw[K], accb[HAS_DB ? K : 1];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    accw[k] = 0.f;
+    if constexpr (HAS_DB) accb[k] = 0.f;
+  }
+
+  Raw rx[RING][ITERS], rd[RING][ITERS];
+  float rm[RING], rr[RING];
+  // Rows past the block's share load as zeros (mean 0, rstd 0: xhat = 0): they add nothing.
+  auto load_row = [&](int slot, int s) {
+    const int64_t li = (int64_t)s * G + grp;
+    const bool ok = li < nloc;
+    const int64_t row = b + (ok ? li : 0) * P;
+    const S* xr = xb + row * a.ldx;
+    const S* dr = dyb + row * a.lddy;
+    rm[slot] = ok ? a.mean[row] : 0.f;
+    rr[slot] = ok ? a.rstd[row] : 0.f;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      rx[slot][it] = IO::zero();
+      rd[slot][it] = IO::zero();
+      if (ok) {
+        if (col + V <= N) {
+          rx[slot][it] = IO::load(xr + col);
+          rd[slot][it] = IO::load(dr + col);
+        } else if (col < N) {
+          rx[slot][it] = IO::load_part(xr + col, N - col);
+          rd[slot][it] = IO::load_part(dr + col, N - col);
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) load_row(j, j);
+
+  for (int s0 = 0; s0 < nsteps; s0 += RING) {
+#pragma unroll
+    for (int j = 0; j < RING; ++j) {
+      const int s = s0 + j;
+      if (s < nsteps) {  // block-uniform
+        if (s + DEPTH < nsteps) load_row((j + DEPTH) % RING, s + DEPTH);
+        const float mu = rm[j], rs = rr[j];
+        float d1a = 0.f, d1b = 0.f, d2a = 0.f, d2b = 0.f;
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+          float xf[V], df[V];
+          IO::unpack(rx[j][it], xf);
+          IO::unpack(rd[j][it], df);
+#pragma unroll
+          for (int e = 0; e < V; e += 2) {
+            const float xh0 = (xf[e] - mu) * rs, xh1 = (xf[e + 1] - mu) * rs;
+            const float gd0 = g[it][e] * df[e], gd1 = g[it][e + 1] * df[e + 1];
+            accw[it * V + e] = __builtin_fmaf(df[e], xh0, accw[it * V + e]);
+            accw[it * V + e + 1] = __builtin_fmaf(df[e + 1], xh1, accw[it * V + e + 1]);
+            if constexpr (HAS_DB) {
+              accb[it * V + e] += df[e];
+              accb[it * V + e + 1] += df[e + 1];
+            }
+            d1a += gd0;
+            d1b += gd1;
+            d2a = __builtin_fmaf(gd0, xh0, d2a);
+            d2b = __builtin_fmaf(gd1, xh1, d2b);
+          }
+        }
+        float dots[2] = {d1a + d1b, d2a + d2b};
+        group_sum_batch<2>(dots, red + ((s & 1) * G + grp) * wpr * 2, wpr, tl);
+        const int64_t li = (int64_t)s * G + grp;
+        if (li < nloc) {
+          const int64_t row = b + li * P;
+          const float c1 = dots[0] / (float)N, c2 = dots[1] / (float)N;
+          S* dxr = dxb + row * a.lddx;
+#pragma unroll
+          for (int it = 0; it < ITERS; ++it) {
+            const int col = (it * TPR + tl) * V;
+            if (col >= N) continue;
+            float xf[V], df[V], o[V];
+            IO::unpack(rx[j][it], xf);
+            IO::unpack(rd[j][it], df);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+              const float xh = (xf[e] - mu) * rs;
+              const float gd = g[it][e] * df[e];
+              o[e] = rs * ((gd - c1) - xh * c2);
+            }
+            const Raw out = IO::pack(o);
+            if (col + V <= N) IO::store(dxr + col, out);
+            else IO::store_part(dxr + col, out, N - col);
+          }
+        }
+      }
+    }
+  }
+
+  float* cbuf = reinterpret_cast<float*>(smem);
+  combine_groups<K>(accw, cbuf, G, grp, tl, TPR);
+  if (grp == 0) store_partial<ITERS, V>(accw, a.part + (int64_t)b * a.ldp, TPR, tl, N);
+  if constexpr (HAS_DB) {
+    combine_groups<K>(accb, cbuf, G, grp, tl, TPR);
+    if (grp == 0) store_partial<ITERS, V>(accb, a.part + (int64_t)(P + b) * a.ldp, TPR, tl, N);
+  }
+}
+
+// Any N and any alignment. One row at a time per block; the elementwise pass reads x and dy again,
+// and the block's dw (and db) partial rows accumulate in the workspace itself (each column owned by
+// one thread, rows added in order).
+template <DT D, bool WIDE, bool HAS_DB>
+__global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
+  using IO = VecIO<D, WIDE>;
+  using S = typename IO::S;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int nv = (N + V - 1) / V;
+  const int tl = threadIdx.x;
+  const int b = blockIdx.x, P = a.P;
+  float* red = reinterpret_cast<float*>(smem);  // [2][wpr][2]
+  const S* wr = static_cast<const S*>(a.w);
+  float* pw = a.part + (int64_t)b * a.ldp;
+  float* pb = a.part + (int64_t)(P + b) * a.ldp;
+
+  for (int v = tl; v < nv; v += TPR) {
+    const int col = v * V;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      if (col + e < N) {
+        pw[col + e] = 0.f;
+        if constexpr (HAS_DB) pb[col + e] = 0.f;
+      }
+    }
+  }
+
+  int s = 0;
+  for (int64_t row = b; row < a.M; row += P, ++s) {
+    const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
+    const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
+    const float mu = a.mean[row], rs = a.rstd[row];
+    float d1a = 0.f, d1b = 0.f, d2a = 0.f, d2b = 0.f;
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      const bool full = col + V <= N;
+      float xf[V], df[V], wf[V];
+      IO::unpack(full ? IO::load(xr + col) : IO::load_part(xr + col, N - col), xf);
+      IO::unpack(full ? IO::load(dr + col) : IO::load_part(dr + col, N - col), df);
+      IO::unpack(full ? IO::load(wr + col) : IO::load_part(wr + col, N - col), wf);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float xh = (xf[e] - mu) * rs;
+        const float gd = wf[e] * df[e];
+        if (e & 1) {
+          d1b += gd;
+          d2b = __builtin_fmaf(gd, xh, d2b);
+        } else {
+          d1a += gd;
+          d2a = __builtin_fmaf(gd, xh, d2a);
+        }
+      }
+    }
+    float dots[2] = {d1a + d1b, d2a + d2b};
+    group_sum_batch<2>(dots, red + (s & 1) * wpr * 2, wpr, tl);
+    const float c1 = dots[0] / (float)N, c2 = dots[1] / (float)N;
+    S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      const bool full = col + V <= N;
+      float xf[V], df[V], wf[V], o[V];
+      IO::unpack(full ? IO::load(xr + col) : IO::load_part(xr + col, N - col), xf);
+      IO::unpack(full ? IO::load(dr + col) : IO::load_part(dr + col, N - col), df);
+      IO::unpack(full ? IO::load(wr + col) : IO::load_part(wr + col, N - col), wf);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float xh = (xf[e] - mu) * rs;
+        const float gd = wf[e] * df[e];
+        o[e] = rs * ((gd - c1) - xh * c2);
+        if (col + e < N) {
+          pw[col + e] = __builtin_fmaf(df[e], xh, pw[col + e]);
+          if constexpr (HAS_DB) pb[col + e] += df[e];
+        }
+      }
+      const auto out = IO::pack(o);
+      if (full) IO::store(dxr + col, out);
+      else IO::store_part(dxr + col, out, N - col);
+    }
+  }
+}
+
+}  // namespace rmsn

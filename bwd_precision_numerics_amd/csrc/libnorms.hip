@@ -1,0 +1,227 @@
+// LayerNorm (and GroupNorm) C interface: argument validation, kernel selection and launches.
+//
+// Same conventions as the RMSNorm entry points: every argument check runs before the first HIP
+// call, nothing is allocated, work is enqueued on the caller's stream.
+#include "host_common.hpp"
+#include "layernorm.hpp"
+
+using namespace rmsn;
+
+namespace {
+
+constexpr int kLnBwdBlockThreads = 1024;
+constexpr int kLnBwdRegMaxIters = 2;
+// Rows in flight ahead of the current one, per vectors-per-thread of the register backward.
+template <int ITERS> struct LnBwdPipe;
+template <> struct LnBwdPipe<1> { static constexpr int DEPTH = 3; };
+template <> struct LnBwdPipe<2> { static constexpr int DEPTH = 1; };
+
+size_t ln_workspace_bytes(int64_t M, int64_t N) {
+  return 2 * (size_t)num_partials(M) * (size_t)partial_ld(N) * sizeof(float);
+}
+
+// ---- LayerNorm forward ----------------------------------------------------------------------------
+template <DT D, bool HAS_B>
+rmsnorm_status ln_fwd_dispatch(const Plan& p, const LnFwdArgs& a, hipStream_t s) {
+  const int block = p.groups * p.tpr;
+  if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    return p.wide ? launch(ln_fwd_stream_kernel<D, true, HAS_B>, p.grid, block, p.lds, s, a)
+                  : launch(ln_fwd_stream_kernel<D, false, HAS_B>, p.grid, block, p.lds, s, a);
+  }
+  switch (p.iters) {
+    case 1: return launch(ln_fwd_rows_kernel<D, 1, HAS_B>, p.grid, block, p.lds, s, a);
+    case 2: return launch(ln_fwd_rows_kernel<D, 2, HAS_B>, p.grid, block, p.lds, s, a);
+    case 3: return launch(ln_fwd_rows_kernel<D, 3, HAS_B>, p.grid, block, p.lds, s, a);
+    case 4: return launch(ln_fwd_rows_kernel<D, 4, HAS_B>, p.grid, block, p.lds, s, a);
+    case 5: return launch(ln_fwd_rows_kernel<D, 5, HAS_B>, p.grid, block, p.lds, s, a);
+    case 6: return launch(ln_fwd_rows_kernel<D, 6, HAS_B>, p.grid, block, p.lds, s, a);
+    case 7: return launch(ln_fwd_rows_kernel<D, 7, HAS_B>, p.grid, block, p.lds, s, a);
+    case 8: return launch(ln_fwd_rows_kernel<D, 8, HAS_B>, p.grid, block, p.lds, s, a);
+    default: return RMSNORM_ERR_UNSUPPORTED;
+  }
+}
+
+template <bool HAS_B>
+rmsnorm_status ln_fwd_by_dtype(rmsnorm_dtype dtype, const Plan& p, const LnFwdArgs& a,
+                               hipStream_t s) {
+  switch (dtype) {
+    case RMSNORM_DTYPE_F32: return ln_fwd_dispatch<DT::F32, HAS_B>(p, a, s);
+    case RMSNORM_DTYPE_F16: return ln_fwd_dispatch<DT::F16, HAS_B>(p, a, s);
+    case RMSNORM_DTYPE_BF16: return ln_fwd_dispatch<DT::BF16, HAS_B>(p, a, s);
+  }
+  return RMSNORM_ERR_INVALID_ARG;
+}
+
+rmsnorm_status ln_fwd_impl(const void* x, int64_t ldx, const void* w, const void* b, void* y,
+                           int64_t ldy, float* mean, float* rstd, int64_t M, int64_t N,
+                           rmsnorm_dtype dtype, float eps, rmsnorm_variant variant, void* stream) {
+  rmsnorm_status st = check_common(M, N, dtype, eps, 0.f);
+  if (st != RMSNORM_OK) return st;
+  if (!variant_ok(variant)) return RMSNORM_ERR_INVALID_ARG;
+  if (variant == RMSNORM_VARIANT_LDS) return RMSNORM_ERR_UNSUPPORTED;  // no LDS-staged family
+  const int eb = elem_bytes(dtype);
+  if ((st = check_matrix(x, ldx, M, N, eb)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(y, ldy, M, N, eb)) != RMSNORM_OK) return st;
+  if (M > 0 && w == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(w, (uintptr_t)eb) || !aligned(b, (uintptr_t)eb) || !aligned(mean, 4) ||
+      !aligned(rstd, 4))
+    return RMSNORM_ERR_MISALIGNED;
+  const bool wide = wide_fits(x, ldx, eb) && aligned(w, 16) && aligned(b, 16);
+  Plan p;
+  if ((st = plan_fwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  p.lds = round16(sizeof(float) * 2 * (size_t)p.groups * (p.tpr / 64));
+  if (M == 0) return RMSNORM_OK;
+
+  LnFwdArgs a;
+  a.x = x; a.w = w; a.b = b; a.y = y; a.mean = mean; a.rstd = rstd;
+  a.ldx = ldx; a.ldy = ldy; a.M = M; a.N = (int)N;
+  a.tpr = p.tpr; a.groups = p.groups; a.eps = eps;
+  a.yvec = wide_fits(y, ldy, eb);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return b ? ln_fwd_by_dtype<true>(dtype, p, a, s) : ln_fwd_by_dtype<false>(dtype, p, a, s);
+}
+
+// ---- LayerNorm backward ---------------------------------------------------------------------------
+rmsnorm_status plan_ln_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
+                           rmsnorm_variant req, Plan* p) {
+  const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
+  int tpr, iters;
+  bwd_shape(nv_wide, &tpr, &iters);
+  const bool reg_ok = wide_ok && iters <= kLnBwdRegMaxIters;
+  rmsnorm_variant v = req;
+  if (v == RMSNORM_VARIANT_AUTO) v = reg_ok ? RMSNORM_VARIANT_REGISTERS : RMSNORM_VARIANT_STREAMING;
+  if (v == RMSNORM_VARIANT_LDS) return RMSNORM_ERR_UNSUPPORTED;
+  if (v == RMSNORM_VARIANT_REGISTERS && !reg_ok) return RMSNORM_ERR_UNSUPPORTED;
+  p->variant = v;
+  p->grid = num_partials(M);
+  if (v == RMSNORM_VARIANT_STREAMING) {
+    p->wide = wide_ok;
+    bwd_shape(wide_ok ? nv_wide : N, &tpr, &iters);
+    p->tpr = tpr;
+    p->iters = 0;
+    p->groups = 1;
+    p->lds = round16(sizeof(float) * 2 * 2 * (tpr / 64));
+    return RMSNORM_OK;
+  }
+  p->wide = true;
+  p->tpr = tpr;
+  p->iters = iters;
+  p->groups = kLnBwdBlockThreads / tpr;
+  const size_t red_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * (tpr / 64) * 2);
+  const size_t combine_bytes =
+      sizeof(float) * (size_t)(p->groups / 2) * tpr * iters * vec_elems(dtype);
+  p->lds = red_bytes > combine_bytes ? red_bytes : combine_bytes;
+  return RMSNORM_OK;
+}
+
+template <DT D, bool HAS_DB>
+rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s) {
+  const int block = p.groups * p.tpr;
+  if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    return p.wide ? launch(ln_bwd_stream_kernel<D, true, HAS_DB>, p.grid, block, p.lds, s, a)
+                  : launch(ln_bwd_stream_kernel<D, false, HAS_DB>, p.grid, block, p.lds, s, a);
+  }
+  switch (p.iters) {
+    case 1:
+      return launch(ln_bwd_rows_kernel<D, 1, LnBwdPipe<1>::DEPTH, HAS_DB>, p.grid, block, p.lds,
+                    s, a);
+    case 2:
+      return launch(ln_bwd_rows_kernel<D, 2, LnBwdPipe<2>::DEPTH, HAS_DB>, p.grid, block, p.lds,
+                    s, a);
+    default:
+      return RMSNORM_ERR_UNSUPPORTED;
+  }
+}
+
+template <bool HAS_DB>
+rmsnorm_status ln_bwd_by_dtype(rmsnorm_dtype dtype, const Plan& p, const LnBwdArgs& a,
+                               hipStream_t s) {
+  switch (dtype) {
+    case RMSNORM_DTYPE_F32: return ln_bwd_dispatch<DT::F32, HAS_DB>(p, a, s);
+    case RMSNORM_DTYPE_F16: return ln_bwd_dispatch<DT::F16, HAS_DB>(p, a, s);
+    case RMSNORM_DTYPE_BF16: return ln_bwd_dispatch<DT::BF16, HAS_DB>(p, a, s);
+  }
+  return RMSNORM_ERR_INVALID_ARG;
+}
+
+// Fixed-order column sums of P partial rows (stride ldp) into out[N]; zeros when there are none.
+rmsnorm_status reduce_partials(const float* part, int64_t P, int64_t N, float* out,
+                               hipStream_t s) {
+  if (P == 0) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s, out,
+                       (int)N);
+  } else {
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)ceil_div(N, 16)), dim3(256), 0, s, part,
+                       partial_ld(N), (int)P, (int)N, out);
+  }
+  return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+}
+
+rmsnorm_status ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                           const void* w, const float* mean, const float* rstd, void* dx,
+                           int64_t lddx, float* dw, float* db, void* workspace,
+                           size_t workspace_bytes_given, int64_t M, int64_t N,
+                           rmsnorm_dtype dtype, rmsnorm_variant variant, void* stream) {
+  rmsnorm_status st = check_common(M, N, dtype, 0.f, 0.f);
+  if (st != RMSNORM_OK) return st;
+  if (!variant_ok(variant)) return RMSNORM_ERR_INVALID_ARG;
+  const int eb = elem_bytes(dtype);
+  if ((st = check_matrix(dy, lddy, M, N, eb)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(x, ldx, M, N, eb)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(dx, lddx, M, N, eb)) != RMSNORM_OK) return st;
+  if (dw == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (M > 0 && (w == nullptr || mean == nullptr || rstd == nullptr || workspace == nullptr))
+    return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(w, (uintptr_t)eb) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dw, 4) ||
+      !aligned(db, 4) || !aligned(workspace, 16))
+    return RMSNORM_ERR_MISALIGNED;
+  if (workspace_bytes_given < ln_workspace_bytes(M, N)) return RMSNORM_ERR_WORKSPACE;
+  const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) && wide_fits(dx, lddx, eb) &&
+                    aligned(w, 16);
+  Plan p;
+  if ((st = plan_ln_bwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t P = num_partials(M);
+  float* part = static_cast<float*>(workspace);
+  if (M > 0) {
+    LnBwdArgs a;
+    a.dy = dy; a.x = x; a.w = w; a.mean = mean; a.rstd = rstd; a.dx = dx; a.part = part;
+    a.lddy = lddy; a.ldx = ldx; a.lddx = lddx; a.M = M;
+    a.N = (int)N; a.ldp = (int)partial_ld(N); a.P = (int)P;
+    a.tpr = p.tpr; a.groups = p.groups;
+    st = db ? ln_bwd_by_dtype<true>(dtype, p, a, s) : ln_bwd_by_dtype<false>(dtype, p, a, s);
+    if (st != RMSNORM_OK) return st;
+  }
+  if ((st = reduce_partials(part, P, N, dw, s)) != RMSNORM_OK) return st;
+  if (db) st = reduce_partials(part + P * partial_ld(N), P, N, db, s);
+  return st;
+}
+
+}  // namespace
+
+// ---- exported C interface -------------------------------------------------------------------------
+extern "C" {
+
+__attribute__((visibility("default"))) rmsnorm_status layernorm_fwd(
+    const void* x, int64_t ldx, const void* w, const void* b, void* y, int64_t ldy, float* mean,
+    float* rstd, int64_t M, int64_t N, rmsnorm_dtype dtype, float eps, rmsnorm_variant variant,
+    void* stream) {
+  return ln_fwd_impl(x, ldx, w, b, y, ldy, mean, rstd, M, N, dtype, eps, variant, stream);
+}
+
+__attribute__((visibility("default"))) size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N,
+                                                                            rmsnorm_dtype dtype) {
+  if (!dtype_ok(dtype) || M <= 0 || N < 1 || N > RMSNORM_MAX_N) return 0;
+  return ln_workspace_bytes(M, N);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status layernorm_bwd(
+    const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, const float* mean,
+    const float* rstd, void* dx, int64_t lddx, float* dw, float* db, void* workspace,
+    size_t workspace_bytes, int64_t M, int64_t N, rmsnorm_dtype dtype, rmsnorm_variant variant,
+    void* stream) {
+  return ln_bwd_impl(dy, lddy, x, ldx, w, mean, rstd, dx, lddx, dw, db, workspace,
+                     workspace_bytes, M, N, dtype, variant, stream);
+}
+
+}  // extern "C"

@@ -462,7 +462,7 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
 // adds them in order of i; the four lanes of a column (l / 16 = 0..3) are then added in order, and
 // finally the four waves in order.
 static_assert(kMaxPartials % 16 == 0, "dw_reduce_kernel reads partial rows in groups of 16");
-__global__ void __launch_bounds__(256) dw_reduce_kernel(const float* part, int64_t ldp, int P,
+inline __global__ void __launch_bounds__(256) dw_reduce_kernel(const float* part, int64_t ldp, int P,
                                                         int N, float* dw) {
   constexpr int L = kMaxPartials / 16;
   __shared__ float buf[4][16];
@@ -486,7 +486,7 @@ __global__ void __launch_bounds__(256) dw_reduce_kernel(const float* part, int64
   if (wv == 0 && q == 0 && col < N) dw[col] = ((buf[0][c] + buf[1][c]) + buf[2][c]) + buf[3][c];
 }
 
-__global__ void fill_zero_kernel(float* p, int n) {
+inline __global__ void fill_zero_kernel(float* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;
 }

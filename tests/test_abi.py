@@ -160,10 +160,52 @@ def test_binding_rejects_host_tensors_before_calling():
 def test_binding_signatures_match_the_header():
     """Each ctypes signature has as many arguments as the header's prototype."""
     import re
-    text = open(rn.HEADER_PATH, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = rn.header_text()
     for name, (_, args) in rn.SIGNATURES.items():
         m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
         assert m, name
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(params) == len(args), (name, params)
+
+
+def lnf(lib, x=FAKE, ldx=8, w=FAKE, b=None, y=FAKE + 0x1000, ldy=8, mean=None, rstd=None, M=4,
+        N=8, dtype=BF16, eps=1e-5, variant=0):
+    return lib.layernorm_fwd(x, ldx, w, b, y, ldy, mean, rstd, M, N, dtype, eps, variant, None)
+
+
+def lnb(lib, dy=FAKE, lddy=8, x=FAKE + 0x1000, ldx=8, w=FAKE + 0x2000, mean=FAKE + 0x3000,
+        rstd=FAKE + 0x3800, dx=FAKE + 0x4000, lddx=8, dw=FAKE + 0x5000, db=None, ws=FAKE + 0x6000,
+        wsb=1 << 20, M=4, N=8, dtype=BF16, variant=0):
+    return lib.layernorm_bwd(dy, lddy, x, ldx, w, mean, rstd, dx, lddx, dw, db, ws, wsb, M, N,
+                             dtype, variant, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
+    (dict(M=-1), INVALID), (dict(N=0), INVALID), (dict(ldx=7), INVALID), (dict(dtype=3), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(variant=7), INVALID),
+    (dict(variant=2), UNSUPPORTED), (dict(b=FAKE + 1), MISALIGNED), (dict(mean=FAKE + 2), MISALIGNED),
+    (dict(x=FAKE + 2, variant=1), UNSUPPORTED),
+    (dict(N=(1 << 24) + 1, ldx=(1 << 24) + 1, ldy=(1 << 24) + 1), UNSUPPORTED),
+])
+def test_layernorm_fwd_rejects(lib, kw, status):
+    assert lnf(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), INVALID), (dict(x=None), INVALID), (dict(w=None), INVALID),
+    (dict(mean=None), INVALID), (dict(rstd=None), INVALID), (dict(dx=None), INVALID),
+    (dict(dw=None), INVALID), (dict(ws=None), INVALID), (dict(lddx=7), INVALID),
+    (dict(variant=2), UNSUPPORTED), (dict(wsb=2 * 4 * 8 * 4 - 1), WORKSPACE),
+    (dict(db=FAKE + 2), MISALIGNED), (dict(ws=FAKE + 8), MISALIGNED),
+    (dict(N=40000, lddy=40000, ldx=40000, lddx=40000, wsb=1 << 30, variant=1), UNSUPPORTED),
+])
+def test_layernorm_bwd_rejects(lib, kw, status):
+    assert lnb(lib, **kw) == status
+
+
+def test_layernorm_workspace_bytes(lib):
+    f = lib.layernorm_bwd_workspace_bytes
+    assert f(4096, 4096, BF16) == 2 * 256 * 4096 * 4
+    assert f(3, 10, F32) == 2 * 3 * 12 * 4
+    assert f(0, 10, F32) == 0 and f(5, 0, F32) == 0 and f(5, 5, 9) == 0

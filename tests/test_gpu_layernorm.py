@@ -1,0 +1,133 @@
+"""GPU parity of LayerNorm (through the C interface) against the CPU oracle.
+
+Shapes span several row groups and persistent blocks, ragged row counts, ragged widths (partial
+last vector through a padded row stride; rows that are not 16-byte aligned, which take the
+element-wise kernels), single-column rows, rows whose mean is large against their spread, and
+widths past the register kernels (streaming kernels). Each case checks y, mean, rstd, dx, dw and db;
+families must agree bit for bit, repeated runs must be bit-identical, and a bias-free call must give
+the same dx and dw.
+"""
+import numpy as np
+import pytest
+
+from parity import check_ln_bwd, check_ln_fwd, same_bits, to_np
+from workloads import LN_WORKLOADS, make_norm_inputs, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bwd_precision_numerics_amd as rn  # noqa: E402
+
+DEV = "cuda:0"
+WL = {"f32": LN_WORKLOADS["ln_fp32_64x1024"], "bf16": LN_WORKLOADS["ln_bf16_4096x4096"],
+      "f16": LN_WORKLOADS["ln_fp16_8192x8192"]}
+
+
+def padded(a, dtype, ld):
+    M, N = a.shape
+    buf = np.zeros((M, ld), np.float32)
+    buf[:, :N] = a
+    return to_device(buf, dtype, DEV)[:, :N]
+
+
+def run_ln(dtype, M, N, *, ld=None, variant="auto", seed=1, bias=True, x_dist=None, eps=None):
+    wl = WL[dtype]
+    eps = wl.eps if eps is None else eps
+    inp = make_norm_inputs(wl, M=M, N=N, seed=seed, x_dist=x_dist)
+    x, w, b, dy = inp["x"], inp["w"], (inp["b"] if bias else None), inp["dy"]
+    if ld is None:
+        xt, dyt = to_device(x, dtype, DEV), to_device(dy, dtype, DEV)
+    else:
+        xt, dyt = padded(x, dtype, ld), padded(dy, dtype, ld)
+    wt = to_device(w, dtype, DEV)
+    bt = to_device(b, dtype, DEV) if bias else None
+    print(f"ln case dtype={dtype} M={M} N={N} ld={ld} variant={variant} seed={seed} bias={bias} "
+          f"x_dist={x_dist}", flush=True)
+    y, mean, rstd = rn.layernorm_fwd(xt, wt, bt, eps=eps, variant=variant)
+    dx, dw, db = rn.layernorm_bwd(dyt, xt, wt, mean, rstd, bias=bias, variant=variant)
+    torch.cuda.synchronize()
+    yg, mg, rg, dxg, dwg = (to_np(t) for t in (y, mean, rstd, dx, dw))
+    dbg = to_np(db) if bias else None
+    st = check_ln_fwd(yg, mg, rg, x, w, b, eps=eps, dtype=dtype)
+    st.update(check_ln_bwd(dxg, dwg, dbg, dy, x, w, mg, rg, dtype=dtype))
+    return st, (yg, mg, rg, dxg, dwg, dbg)
+
+
+SHAPES = [
+    (1, 8, None), (5, 1, None), (7, 3, None), (33, 64, None), (300, 1000, None),
+    (300, 1027, 1032), (129, 1027, None), (257, 3072, None), (64, 4096, None), (40, 8192, None),
+    (24, 16384, None), (12, 32768, None), (3, 70000, None),
+]
+
+
+@pytest.mark.parametrize("M,N,ld", SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_ln_parity(dtype, M, N, ld):
+    run_ln(dtype, M, N, ld=ld)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", [1000, 4096, 16384])
+def test_ln_large_mean_rows(dtype, N):
+    """x ~ 16 + N(0, 1): the variance about the mean must survive (no E[x^2] - mean^2)."""
+    run_ln(dtype, 96, N, x_dist=("normal", 16.0, 1.0))
+
+
+@pytest.mark.parametrize("N", [1000, 4096, 8192])
+def test_ln_without_bias(N):
+    st, res_nb = run_ln("bf16", 130, N, bias=False, seed=5)
+    _, res_b = run_ln("bf16", 130, N, bias=True, seed=5)
+    # dx and dw do not depend on the bias
+    assert same_bits(res_nb[3], res_b[3]).all() and same_bits(res_nb[4], res_b[4]).all()
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 1000), ("bf16", 4096), ("f16", 8192),
+                                     ("f32", 1024), ("bf16", 16384)])
+def test_ln_families_agree(dtype, N):
+    """Register and streaming kernels share the mapping and summation order: y, mean, rstd and dx
+    agree bit for bit; dw and db within float32 rounding (another row grouping)."""
+    _, reg = run_ln(dtype, 70, N, variant="registers", seed=3)
+    _, stream = run_ln(dtype, 70, N, variant="streaming", seed=3)
+    for k in range(4):
+        assert same_bits(reg[k], stream[k]).all(), k
+    for k in (4, 5):
+        assert np.allclose(reg[k], stream[k], rtol=1e-5, atol=1e-5)
+
+
+def test_ln_repeatable():
+    _, a = run_ln("bf16", 1000, 4096, seed=9)
+    _, b = run_ln("bf16", 1000, 4096, seed=9)
+    for u, v in zip(a, b):
+        assert same_bits(u, v).all()
+
+
+def test_ln_eps_zero_and_large():
+    run_ln("bf16", 200, 2048, eps=0.0)
+    run_ln("bf16", 200, 2048, eps=0.25)
+
+
+def test_ln_lds_family_is_unsupported():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(rn.RMSNormError) as e:
+        rn.layernorm_fwd(x, w, variant="lds")
+    assert e.value.status == 2
+
+
+def test_ln_zero_rows():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    y, m, r = rn.layernorm_fwd(x, w)
+    dx, dw, db = rn.layernorm_bwd(x, x, w, m, r)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64) and dx.shape == (0, 64)
+    assert float(dw.abs().sum()) == 0.0 and float(db.abs().sum()) == 0.0
+
+
+def test_ln_full_size_bf16():
+    wl = LN_WORKLOADS["ln_bf16_4096x4096"]
+    st, _ = run_ln("bf16", wl.M, wl.N, seed=wl.seed)
+    print(st)

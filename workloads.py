@@ -130,3 +130,40 @@ def to_device(a: np.ndarray, dtype: str, device: str):
     """Copy a float32 array of T values to a ``device`` tensor of dtype T (exact conversion)."""
     import torch
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch_dtype(dtype)).to(device)
+
+
+# ---- LayerNorm / GroupNorm inputs -----------------------------------------------------------------
+# Same recipe; the bias is drawn after x, w and dy (so x, w and dy equal the RMSNorm workload's),
+# as b ~ N(0, 0.1^2). ``x_dist`` overrides the workload's, e.g. ("normal", 16.0, 1.0) for rows whose
+# mean is large against their spread (the group_norm page's test cases with an input offset).
+_BIAS = ("normal", 0.0, 0.1)
+
+
+def make_norm_inputs(wl: Workload, M: int | None = None, N: int | None = None,
+                     seed: int | None = None, x_dist: tuple | None = None,
+                     b_dist: tuple = _BIAS) -> dict:
+    """Draw ``x`` [M, N], ``w`` [N], ``dy`` [M, N], then ``b`` [N] (float32 arrays of T values)."""
+    M = wl.M if M is None else M
+    N = wl.N if N is None else N
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = _draw(rng, x_dist or wl.x_dist, (M, N))
+    w = _draw(rng, wl.w_dist, (N,))
+    dy = _draw(rng, wl.dy_dist, (M, N))
+    b = _draw(rng, b_dist, (N,))
+    return {
+        "x": to_dtype_values(x, wl.dtype),
+        "w": to_dtype_values(w, wl.dtype),
+        "dy": to_dtype_values(dy, wl.dtype),
+        "b": to_dtype_values(b, wl.dtype),
+    }
+
+
+# LayerNorm at the RMSNorm headline shape: bf16 4096 x 4096, eps 1e-5 (the usual LayerNorm eps).
+LN_WORKLOADS = {
+    "ln_bf16_4096x4096": Workload("ln_bf16_4096x4096", "bf16", 4096, 4096, "once", 0.0, 1e-5,
+                                  _STD, _GAIN, _STD, 0),
+    "ln_fp32_64x1024": Workload("ln_fp32_64x1024", "f32", 64, 1024, "once", 0.0, 1e-5,
+                                _STD, _GAIN, _STD, 0),
+    "ln_fp16_8192x8192": Workload("ln_fp16_8192x8192", "f16", 8192, 8192, "once", 0.0, 1e-5,
+                                  ("normal", 0.0, 8.0), _GAIN, ("ones",), 0),
+}
