@@ -12,6 +12,8 @@ raises ``LibraryMissing`` (build it with ``python -m bwd_precision_numerics_amd.
     y8, rstd = fwd_fp8(x, w, scale=1.0, fmt="e4m3")        # OCP 8-bit output
     y, mean, rstd = layernorm_fwd(x, w, b, eps=1e-5)       # LayerNorm (b may be None)
     dx, dw, db    = layernorm_bwd(dy, x, w, mean, rstd, bias=True)
+    y, mean, rstd = groupnorm_fwd(x, G, w, b, eps=1e-5)    # GroupNorm of [B, C, *spatial]
+    dx, dw, db    = groupnorm_bwd(dy, x, G, w, mean, rstd)
 
 ``rounding="twice"`` is the Llama convention T(float(T(xhat)) * g); ``"once"`` is the Gemma
 convention T(xhat * g); the gain is ``g = offset + w`` (offset 1 for Gemma).
@@ -73,6 +75,10 @@ SIGNATURES = {
     "layernorm_bwd_workspace_bytes": (_sz, [_i64, _i64, _i]),
     "layernorm_bwd": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _i64, _i64,
                            _i, _i, _p]),
+    "groupnorm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),
+    "groupnorm_fwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _sz, _i64, _i64, _i64, _i64, _i, _f, _p]),
+    "groupnorm_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _i64, _i64, _i64, _i64, _i,
+                           _p]),
     "rmsnorm_status_string": (ctypes.c_char_p, [_i]),
     "rmsnorm_abi_version": (_i, []),
 }
@@ -400,6 +406,94 @@ def layernorm_bwd(dy, x, w, mean, rstd, bias: bool = True, variant: str = "auto"
                                  workspace.data_ptr(), wsb, M, N, DTYPE_CODES[dt],
                                  VARIANT_CODES[variant], _stream(x.device))
     _check("layernorm_bwd", st)
+    return dx, dw, (db if bias else None)
+
+
+# ---- GroupNorm --------------------------------------------------------------------------------------
+
+def groupnorm_workspace_bytes(B: int, C: int, S: int, G: int, dtype: str) -> int:
+    return int(library().groupnorm_workspace_bytes(B, C, S, G, DTYPE_CODES[dtype]))
+
+
+def _contig(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _gn_shape(x):
+    if x.dim() < 2:
+        raise ValueError("x must be [B, C, *spatial]")
+    B, C = x.shape[0], x.shape[1]
+    S = 1
+    for d in x.shape[2:]:
+        S *= d
+    return B, C, S
+
+
+def _gn_workspace(B, C, S, G, dt, device, workspace):
+    torch = _torch()
+    need = groupnorm_workspace_bytes(B, C, S, G, dt)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def groupnorm_fwd(x, G: int, w, b=None, eps: float = 1e-5, y=None, mean=None, rstd=None,
+                  workspace=None):
+    """GroupNorm of a contiguous ``x`` [B, C, *spatial] with G groups. Returns ``(y, mean, rstd)``
+    (mean and rstd float32 [B, G])."""
+    torch = _torch()
+    dt = dtype_name(x)
+    B, C, S = _gn_shape(x)
+    px = _contig(x, "x")
+    pw = _opt_vec(w, "w", C, x.dtype)
+    pb = _opt_vec(b, "b", C, x.dtype)
+    if y is None:
+        y = torch.empty_like(x)
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("y must match x in shape and dtype")
+    mean = torch.empty((B, G), dtype=torch.float32, device=x.device) if mean is None else mean
+    rstd = torch.empty((B, G), dtype=torch.float32, device=x.device) if rstd is None else rstd
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        if t.dtype != torch.float32 or t.numel() != B * G:
+            raise ValueError(f"{n} must be float32 with B * G elements")
+    workspace, wsb = _gn_workspace(B, C, S, G, dt, x.device, workspace)
+    _same_device(*[t for t in (x, w, b, y, mean, rstd, workspace) if t is not None])
+    st = library().groupnorm_fwd(px, pw, pb, _contig(y, "y"), _contig(mean, "mean"),
+                                 _contig(rstd, "rstd"), workspace.data_ptr(), wsb, B, C, S, G,
+                                 DTYPE_CODES[dt], eps, _stream(x.device))
+    _check("groupnorm_fwd", st)
+    return y, mean, rstd
+
+
+def groupnorm_bwd(dy, x, G: int, w, mean, rstd, bias: bool = True, dx=None, dw=None, db=None,
+                  workspace=None):
+    """GroupNorm backward. Returns ``(dx, dw, db)``; dw, db float32 [C] (db None if not ``bias``)."""
+    torch = _torch()
+    dt = dtype_name(x)
+    if dy.dtype != x.dtype or w.dtype != x.dtype:
+        raise TypeError("dy and w must have the dtype of x")
+    if dy.shape != x.shape:
+        raise ValueError("dy must have the shape of x")
+    B, C, S = _gn_shape(x)
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dw is None:
+        dw = torch.empty((C,), dtype=torch.float32, device=x.device)
+    if bias and db is None:
+        db = torch.empty((C,), dtype=torch.float32, device=x.device)
+    workspace, wsb = _gn_workspace(B, C, S, G, dt, x.device, workspace)
+    _same_device(*[t for t in (dy, x, w, mean, rstd, dx, dw, db, workspace) if t is not None])
+    st = library().groupnorm_bwd(_contig(dy, "dy"), _contig(x, "x"), _vec(w, "w", C),
+                                 _contig(mean, "mean"), _contig(rstd, "rstd"), _contig(dx, "dx"),
+                                 _opt_vec(dw, "dw", C, torch.float32),
+                                 _opt_vec(db, "db", C, torch.float32) if bias else None,
+                                 workspace.data_ptr(), wsb, B, C, S, G, DTYPE_CODES[dt],
+                                 _stream(x.device))
+    _check("groupnorm_bwd", st)
     return dx, dw, (db if bias else None)
 
 

@@ -27,7 +27,7 @@ SRCS = [os.path.join(HERE, "csrc", f) for f in ("librmsnorm.hip", "libnorms.hip"
 OUT = os.path.join(HERE, "librmsnorm.so")
 HEADERS = [os.path.join(HERE, "csrc", f) for f in
            ("host_common.hpp", "rmsnorm_common.hpp", "rmsnorm_fwd.hpp", "rmsnorm_bwd.hpp",
-            "layernorm.hpp")]
+            "layernorm.hpp", "groupnorm.hpp")]
 HEADERS += [os.path.join(ROOT, "include", f) for f in ("librmsnorm.h", "libnorms.h")]
 
 

@@ -1,0 +1,350 @@
+// GroupNorm forward and backward kernels for x of shape [B, C, S] (S the flattened spatial size),
+// C split into G groups of Cg = C / G adjacent channels; a (batch, group) row is the Cg * S
+// contiguous elements of its channels.
+//
+// Statistics and reductions in float32, mean and rstd cached in float32, inputs upcast on load
+// (Liger-Kernel pull request 1608, "fix(group_norm): keep the backward statistics and reductions
+// in fp32"); the backward is the derivative of the formula (the layer_norm rule of candle pull
+// request 4059 with per-channel weights):
+//   y    = T( ((x - mean) * rstd) * w_c + b_c )                 c the element's channel
+//   dx   = T( rstd * ((w_c * dy - c1) - xhat * c2) ),  c1 = sum(w_c dy) / n,  c2 = sum(w_c dy xhat) / n
+//   dW_c = sum over batch and space of dy * xhat,      dB_c = sum over batch and space of dy
+//
+// Work is split into chunks of at most CH elements of one (batch, channel) segment, one 256-thread
+// block per chunk, so the affine weight and bias are one scalar per block and rows of any length
+// spread over the whole GPU. Every cross-chunk combination runs in a fixed order:
+//   forward   gn_stats_kernel writes each chunk's (mean, M2 = sum of squared deviations from the
+//             chunk mean, taken in a second pass over registers); gn_fwd_kernel merges the row's
+//             chunk statistics with Chan's pairwise update (lane-strided sequential merges, then a
+//             fixed shuffle tree) — every block of a row derives the same bits — and normalizes its
+//             chunk, reading x a second time.
+//   backward  gn_bwd_sums_kernel writes each chunk's (sum dy, sum dy * xhat); gn_bwd_dx_kernel
+//             merges c1 = sum_c w_c * (sum dy) and c2 = sum_c w_c * (sum dy * xhat) over the row and
+//             writes dx; gn_param_kernel adds the same per-chunk sums over batch and chunks into
+//             dW_c and dB_c. Since w_c is constant over a chunk, w_c * sum(dy) is the row sum of
+//             w_c * dy up to float32 rounding order, and one pair of sums per chunk serves both the
+//             row constants and the parameter gradients.
+#pragma once
+
+#include "rmsnorm_common.hpp"
+
+namespace rmsn {
+
+constexpr int kGnThreads = 256;  // threads per chunk block (4 wavefronts)
+
+// Elements per chunk: two 16-byte vectors per thread.
+template <DT D> constexpr int gn_chunk() { return kGnThreads * 2 * Elem<D>::VEC; }
+
+struct GnArgs {
+  const void* x;
+  const void* dy;   // backward only
+  const void* w;    // [C]
+  const void* b;    // [C] or null (forward)
+  void* out;        // y (forward) or dx (backward), [B, C, S]
+  float* mean;      // [B * G]
+  float* rstd;      // [B * G]
+  float2* ws;       // [B * C * K] per-chunk pairs
+  float* dw;        // [C] (parameter kernel)
+  float* db;        // [C] or null
+  int64_t B, C, S;
+  int G, Cg, K;     // groups, channels per group, chunks per (batch, channel) segment
+  float eps;
+};
+
+// (count, mean, M2) of a set of values; merge() is Chan et al.'s pairwise update (float32).
+struct Moments {
+  float n, m, m2;
+};
+__device__ __forceinline__ Moments merge(Moments a, Moments b) {
+  if (b.n == 0.f) return a;
+  if (a.n == 0.f) return b;
+  const float n = a.n + b.n;
+  const float d = b.m - a.m;
+  const float fb = b.n / n;
+  return {n, a.m + d * fb, (a.m2 + b.m2) + (d * d) * (a.n * fb)};
+}
+__device__ __forceinline__ Moments shfl_down(Moments v, int off) {
+  return {__shfl_down(v.n, off, 64), __shfl_down(v.m, off, 64), __shfl_down(v.m2, off, 64)};
+}
+
+// Block-level sums over the 4 wavefronts in wave order (group_sum with one group of 256 threads).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  return group_sum(v, red, kGnThreads / 64, threadIdx.x);
+}
+
+// The chunk of block u: segment bc = u / K (= batch * C + channel), chunk k = u % K.
+struct Chunk {
+  int64_t bc, base;  // segment index; element offset of the chunk in x
+  int64_t bidx, c;   // batch, channel
+  int k, cnt;        // chunk index within the segment, valid elements
+};
+template <DT D>
+__device__ __forceinline__ Chunk chunk_of(const GnArgs& a, int64_t u) {
+  constexpr int CH = gn_chunk<D>();
+  Chunk ch;
+  ch.bc = u / a.K;
+  ch.k = (int)(u - ch.bc * a.K);
+  ch.bidx = ch.bc / a.C;
+  ch.c = ch.bc - ch.bidx * a.C;
+  ch.base = ch.bc * a.S + (int64_t)ch.k * CH;
+  const int64_t left = a.S - (int64_t)ch.k * CH;
+  ch.cnt = (int)(left < CH ? left : CH);
+  return ch;
+}
+
+// Loads of one chunk: thread t holds vectors t and t + 256 (WIDE) or elements t + 256 i.
+template <DT D, bool WIDE>
+struct ChunkIO {
+  using IO = VecIO<D, WIDE>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  static constexpr int V = IO::V;
+  static constexpr int IT = gn_chunk<D>() / (kGnThreads * V);
+  static __device__ __forceinline__ void load(const S* p, int cnt, Raw (&r)[IT]) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int col = (it * kGnThreads + (int)threadIdx.x) * V;
+      r[it] = IO::zero();
+      if (col + V <= cnt) r[it] = IO::load(p + col);
+      else if (col < cnt) r[it] = IO::load_part(p + col, cnt - col);
+    }
+  }
+};
+
+// Forward pass 1: per-chunk (mean, M2).
+template <DT D, bool WIDE>
+__global__ void __launch_bounds__(kGnThreads) gn_stats_kernel(GnArgs a) {
+  using CI = ChunkIO<D, WIDE>;
+  using IO = typename CI::IO;
+  constexpr int V = CI::V, IT = CI::IT;
+  __shared__ float red[8];
+  const Chunk ch = chunk_of<D>(a, blockIdx.x);
+  typename CI::Raw r[IT];
+  CI::load(static_cast<const typename CI::S*>(a.x) + ch.base, ch.cnt, r);
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    float f[V];
+    IO::unpack(r[it], f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      if (e & 1) s1 += f[e];
+      else s0 += f[e];
+    }
+  }
+  const float m = block_sum(s0 + s1, red) / (float)ch.cnt;
+  float q0 = 0.f, q1 = 0.f;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int col = (it * kGnThreads + (int)threadIdx.x) * V;
+    float f[V];
+    IO::unpack(r[it], f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float d = col + e < ch.cnt ? f[e] - m : 0.f;
+      if (e & 1) q1 = __builtin_fmaf(d, d, q1);
+      else q0 = __builtin_fmaf(d, d, q0);
+    }
+  }
+  const float m2 = block_sum(q0 + q1, red + 4);
+  if (threadIdx.x == 0) a.ws[blockIdx.x] = make_float2(m, m2);
+}
+
+// Chunk statistics of the row (batch, group) merged in a fixed order by wave 0; lane 0 returns it.
+template <DT D>
+__device__ __forceinline__ Moments row_moments(const GnArgs& a, int64_t bidx, int g) {
+  constexpr int CH = gn_chunk<D>();
+  const int lane = threadIdx.x & 63;
+  const int nent = a.Cg * a.K;
+  const int64_t first = (bidx * a.C + (int64_t)g * a.Cg) * a.K;  // the row's entries are adjacent
+  Moments acc = {0.f, 0.f, 0.f};
+  for (int e = lane; e < nent; e += 64) {
+    const int k = e % a.K;
+    const int64_t left = a.S - (int64_t)k * CH;
+    const float2 v = a.ws[first + e];
+    acc = merge(acc, {(float)(left < CH ? left : CH), v.x, v.y});
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const Moments o = shfl_down(acc, off);
+    if (lane < off) acc = merge(acc, o);
+  }
+  return acc;
+}
+
+// Forward pass 2: merge the row's statistics, write the caches (first chunk of the row), normalize.
+template <DT D, bool WIDE, bool HAS_B>
+__global__ void __launch_bounds__(kGnThreads) gn_fwd_kernel(GnArgs a) {
+  using CI = ChunkIO<D, WIDE>;
+  using IO = typename CI::IO;
+  using S = typename CI::S;
+  constexpr int V = CI::V, IT = CI::IT;
+  __shared__ float stat[2];
+  const Chunk ch = chunk_of<D>(a, blockIdx.x);
+  const int g = (int)(ch.c / a.Cg);
+  typename CI::Raw r[IT];
+  CI::load(static_cast<const S*>(a.x) + ch.base, ch.cnt, r);  // in flight during the merge
+  if (threadIdx.x < 64) {
+    const Moments mo = row_moments<D>(a, ch.bidx, g);
+    if (threadIdx.x == 0) {
+      const float rs = 1.0f / __builtin_sqrtf(mo.m2 / mo.n + a.eps);
+      stat[0] = mo.m;
+      stat[1] = rs;
+      if (ch.k == 0 && ch.c == (int64_t)g * a.Cg) {
+        const int64_t row = ch.bidx * a.G + g;
+        if (a.mean) a.mean[row] = mo.m;
+        if (a.rstd) a.rstd[row] = rs;
+      }
+    }
+  }
+  __syncthreads();
+  const float mean = stat[0], rs = stat[1];
+  const float wc = to_f32<D>(static_cast<const S*>(a.w)[ch.c]);
+  const float bc = HAS_B ? to_f32<D>(static_cast<const S*>(a.b)[ch.c]) : 0.f;
+  S* yp = static_cast<S*>(a.out) + ch.base;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int col = (it * kGnThreads + (int)threadIdx.x) * V;
+    if (col >= ch.cnt) continue;
+    float f[V], o[V];
+    IO::unpack(r[it], f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float xh = (f[e] - mean) * rs;
+      o[e] = HAS_B ? xh * wc + bc : xh * wc;
+    }
+    const auto out = IO::pack(o);
+    if (col + V <= ch.cnt) IO::store(yp + col, out);
+    else IO::store_part(yp + col, out, ch.cnt - col);
+  }
+}
+
+// Backward pass 1: per-chunk (sum dy, sum dy * xhat).
+template <DT D, bool WIDE>
+__global__ void __launch_bounds__(kGnThreads) gn_bwd_sums_kernel(GnArgs a) {
+  using CI = ChunkIO<D, WIDE>;
+  using IO = typename CI::IO;
+  using S = typename CI::S;
+  constexpr int V = CI::V, IT = CI::IT;
+  __shared__ float red[8];
+  const Chunk ch = chunk_of<D>(a, blockIdx.x);
+  const int64_t row = ch.bidx * a.G + ch.c / a.Cg;
+  const float mean = a.mean[row], rs = a.rstd[row];
+  typename CI::Raw rx[IT], rd[IT];
+  CI::load(static_cast<const S*>(a.x) + ch.base, ch.cnt, rx);
+  CI::load(static_cast<const S*>(a.dy) + ch.base, ch.cnt, rd);
+  float s0 = 0.f, s1 = 0.f, t0 = 0.f, t1 = 0.f;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    float xf[V], df[V];
+    IO::unpack(rx[it], xf);
+    IO::unpack(rd[it], df);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float xh = (xf[e] - mean) * rs;  // padding: dy = 0 adds nothing
+      if (e & 1) {
+        s1 += df[e];
+        t1 = __builtin_fmaf(df[e], xh, t1);
+      } else {
+        s0 += df[e];
+        t0 = __builtin_fmaf(df[e], xh, t0);
+      }
+    }
+  }
+  const float sdy = block_sum(s0 + s1, red);
+  const float sdx = block_sum(t0 + t1, red + 4);
+  if (threadIdx.x == 0) a.ws[blockIdx.x] = make_float2(sdy, sdx);
+}
+
+// Backward pass 2: row constants from the chunk sums (fixed order), then dx for the chunk.
+template <DT D, bool WIDE>
+__global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
+  using CI = ChunkIO<D, WIDE>;
+  using IO = typename CI::IO;
+  using S = typename CI::S;
+  constexpr int V = CI::V, IT = CI::IT;
+  __shared__ float cst[2];
+  const Chunk ch = chunk_of<D>(a, blockIdx.x);
+  const int g = (int)(ch.c / a.Cg);
+  const int64_t row = ch.bidx * a.G + g;
+  const float mean = a.mean[row], rs = a.rstd[row];
+  const S* wp = static_cast<const S*>(a.w);
+  typename CI::Raw rx[IT], rd[IT];
+  CI::load(static_cast<const S*>(a.x) + ch.base, ch.cnt, rx);
+  CI::load(static_cast<const S*>(a.dy) + ch.base, ch.cnt, rd);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int nent = a.Cg * a.K;
+    const int64_t first = (ch.bidx * a.C + (int64_t)g * a.Cg) * a.K;
+    float u1 = 0.f, u2 = 0.f;
+    for (int e = lane; e < nent; e += 64) {
+      const float wc = to_f32<D>(wp[(int64_t)g * a.Cg + e / a.K]);
+      const float2 v = a.ws[first + e];
+      u1 += wc * v.x;
+      u2 += wc * v.y;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float o1 = __shfl_down(u1, off, 64), o2 = __shfl_down(u2, off, 64);
+      if (lane < off) {
+        u1 += o1;
+        u2 += o2;
+      }
+    }
+    if (lane == 0) {
+      const float n = (float)(a.Cg * a.S);
+      cst[0] = u1 / n;
+      cst[1] = u2 / n;
+    }
+  }
+  __syncthreads();
+  const float c1 = cst[0], c2 = cst[1];
+  const float wc = to_f32<D>(wp[ch.c]);
+  S* dxp = static_cast<S*>(a.out) + ch.base;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int col = (it * kGnThreads + (int)threadIdx.x) * V;
+    if (col >= ch.cnt) continue;
+    float xf[V], df[V], o[V];
+    IO::unpack(rx[it], xf);
+    IO::unpack(rd[it], df);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float xh = (xf[e] - mean) * rs;
+      o[e] = rs * ((wc * df[e] - c1) - xh * c2);
+    }
+    const auto out = IO::pack(o);
+    if (col + V <= ch.cnt) IO::store(dxp + col, out);
+    else IO::store_part(dxp + col, out, ch.cnt - col);
+  }
+}
+
+// dW_c = sum over (batch, chunk) of sum(dy * xhat), dB_c of sum(dy): one wavefront per channel,
+// lane-strided sequential sums then a fixed shuffle tree.
+__global__ void __launch_bounds__(256) gn_param_kernel(GnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= a.C) return;  // whole wavefronts leave together
+  const int64_t nent = a.B * a.K;
+  float u1 = 0.f, u2 = 0.f;
+  for (int64_t e = lane; e < nent; e += 64) {
+    const int64_t bidx = e / a.K, k = e - bidx * a.K;
+    const float2 v = a.ws[(bidx * a.C + c) * a.K + k];
+    u1 += v.x;
+    u2 += v.y;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o1 = __shfl_down(u1, off, 64), o2 = __shfl_down(u2, off, 64);
+    if (lane < off) {
+      u1 += o1;
+      u2 += o2;
+    }
+  }
+  if (lane == 0) {
+    a.dw[c] = u2;
+    if (a.db) a.db[c] = u1;
+  }
+}
+
+}  // namespace rmsn

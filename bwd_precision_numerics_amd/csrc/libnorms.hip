@@ -2,6 +2,7 @@
 //
 // Same conventions as the RMSNorm entry points: every argument check runs before the first HIP
 // call, nothing is allocated, work is enqueued on the caller's stream.
+#include "groupnorm.hpp"
 #include "host_common.hpp"
 #include "layernorm.hpp"
 
@@ -197,6 +198,136 @@ rmsnorm_status ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t 
   return st;
 }
 
+// ---- GroupNorm -----------------------------------------------------------------------------------
+int gn_chunk_elems(rmsnorm_dtype d) {
+  return d == RMSNORM_DTYPE_F32 ? gn_chunk<DT::F32>() : gn_chunk<DT::BF16>();
+}
+
+// Validates the shape; on success *chunks = B * C * K (one block per chunk) and *K.
+rmsnorm_status gn_shape(int64_t B, int64_t C, int64_t S, int64_t G, int dtype, int64_t* K,
+                        int64_t* chunks) {
+  if (!dtype_ok(dtype)) return RMSNORM_ERR_INVALID_ARG;
+  if (B < 0 || C < 1 || S < 1 || G < 1 || C % G != 0) return RMSNORM_ERR_INVALID_ARG;
+  if (C > INT32_MAX) return RMSNORM_ERR_UNSUPPORTED;
+  const int64_t Cg = C / G;
+  if (S > RMSNORM_MAX_N || Cg > RMSNORM_MAX_N / S) return RMSNORM_ERR_UNSUPPORTED;  // group size
+  *K = ceil_div(S, gn_chunk_elems((rmsnorm_dtype)dtype));
+  if (B > 0 && C > (INT64_MAX / B) / S) return RMSNORM_ERR_INVALID_ARG;  // element count
+  if (B > 0 && (C > INT32_MAX / *K || B > INT32_MAX / (C * *K))) return RMSNORM_ERR_UNSUPPORTED;
+  *chunks = B * C * *K;
+  return RMSNORM_OK;
+}
+
+rmsnorm_status gn_common(const void* x, const void* w, const void* out, const float* mean,
+                         const float* rstd, void* workspace, size_t wsb, int64_t B, int64_t C,
+                         int64_t S, int64_t G, rmsnorm_dtype dtype, int64_t* K, int64_t* chunks) {
+  rmsnorm_status st = gn_shape(B, C, S, G, dtype, K, chunks);
+  if (st != RMSNORM_OK) return st;
+  if (B > 0 && (x == nullptr || w == nullptr || out == nullptr || workspace == nullptr))
+    return RMSNORM_ERR_INVALID_ARG;
+  const int eb = elem_bytes(dtype);
+  if (!aligned(x, (uintptr_t)eb) || !aligned(w, (uintptr_t)eb) || !aligned(out, (uintptr_t)eb) ||
+      !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(workspace, 16))
+    return RMSNORM_ERR_MISALIGNED;
+  if (wsb < (size_t)*chunks * sizeof(float2)) return RMSNORM_ERR_WORKSPACE;
+  return RMSNORM_OK;
+}
+
+GnArgs gn_args(int64_t B, int64_t C, int64_t S, int64_t G, int64_t K, void* workspace) {
+  GnArgs a = {};
+  a.B = B; a.C = C; a.S = S; a.G = (int)G; a.Cg = (int)(C / G); a.K = (int)K;
+  a.ws = static_cast<float2*>(workspace);
+  return a;
+}
+
+template <DT D, bool WIDE>
+rmsnorm_status gn_fwd_launch(const GnArgs& a, int64_t chunks, hipStream_t s) {
+  hipLaunchKernelGGL((gn_stats_kernel<D, WIDE>), dim3((unsigned)chunks), dim3(kGnThreads), 0, s,
+                     a);
+  if (a.b)
+    hipLaunchKernelGGL((gn_fwd_kernel<D, WIDE, true>), dim3((unsigned)chunks), dim3(kGnThreads),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL((gn_fwd_kernel<D, WIDE, false>), dim3((unsigned)chunks), dim3(kGnThreads),
+                       0, s, a);
+  return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+}
+
+template <DT D, bool WIDE>
+rmsnorm_status gn_bwd_launch(const GnArgs& a, int64_t chunks, hipStream_t s) {
+  hipLaunchKernelGGL((gn_bwd_sums_kernel<D, WIDE>), dim3((unsigned)chunks), dim3(kGnThreads), 0,
+                     s, a);
+  hipLaunchKernelGGL((gn_bwd_dx_kernel<D, WIDE>), dim3((unsigned)chunks), dim3(kGnThreads), 0, s,
+                     a);
+  hipLaunchKernelGGL(gn_param_kernel, dim3((unsigned)ceil_div(a.C, 4)), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+}
+
+template <bool FWD, bool WIDE>
+rmsnorm_status gn_by_dtype(rmsnorm_dtype dtype, const GnArgs& a, int64_t chunks, hipStream_t s) {
+  switch (dtype) {
+    case RMSNORM_DTYPE_F32:
+      return FWD ? gn_fwd_launch<DT::F32, WIDE>(a, chunks, s) : gn_bwd_launch<DT::F32, WIDE>(a, chunks, s);
+    case RMSNORM_DTYPE_F16:
+      return FWD ? gn_fwd_launch<DT::F16, WIDE>(a, chunks, s) : gn_bwd_launch<DT::F16, WIDE>(a, chunks, s);
+    case RMSNORM_DTYPE_BF16:
+      return FWD ? gn_fwd_launch<DT::BF16, WIDE>(a, chunks, s) : gn_bwd_launch<DT::BF16, WIDE>(a, chunks, s);
+  }
+  return RMSNORM_ERR_INVALID_ARG;
+}
+
+// 16-byte accesses: every chunk starts 16-byte aligned when the bases are and S * sizeof(T) is a
+// multiple of 16 (chunks are whole numbers of vectors).
+bool gn_wide(const void* p, int64_t S, int eb) { return aligned(p, 16) && (S * eb) % 16 == 0; }
+
+rmsnorm_status gn_fwd_impl(const void* x, const void* w, const void* b, void* y, float* mean,
+                           float* rstd, void* workspace, size_t wsb, int64_t B, int64_t C,
+                           int64_t S, int64_t G, rmsnorm_dtype dtype, float eps, void* stream) {
+  if (!std::isfinite(eps) || eps < 0.f) return RMSNORM_ERR_INVALID_ARG;
+  int64_t K = 0, chunks = 0;
+  rmsnorm_status st = gn_common(x, w, y, mean, rstd, workspace, wsb, B, C, S, G, dtype, &K, &chunks);
+  if (st != RMSNORM_OK) return st;
+  const int eb = elem_bytes(dtype);
+  if (!aligned(b, (uintptr_t)eb)) return RMSNORM_ERR_MISALIGNED;
+  if (B == 0) return RMSNORM_OK;
+  GnArgs a = gn_args(B, C, S, G, K, workspace);
+  a.x = x; a.w = w; a.b = b; a.out = y; a.mean = mean; a.rstd = rstd; a.eps = eps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool wide = gn_wide(x, S, eb) && gn_wide(y, S, eb);
+  return wide ? gn_by_dtype<true, true>(dtype, a, chunks, s)
+              : gn_by_dtype<true, false>(dtype, a, chunks, s);
+}
+
+rmsnorm_status gn_bwd_impl(const void* dy, const void* x, const void* w, const float* mean,
+                           const float* rstd, void* dx, float* dw, float* db, void* workspace,
+                           size_t wsb, int64_t B, int64_t C, int64_t S, int64_t G,
+                           rmsnorm_dtype dtype, void* stream) {
+  int64_t K = 0, chunks = 0;
+  rmsnorm_status st = gn_common(x, w, dx, mean, rstd, workspace, wsb, B, C, S, G, dtype, &K,
+                                &chunks);
+  if (st != RMSNORM_OK) return st;
+  if (dw == nullptr || (B > 0 && (dy == nullptr || mean == nullptr || rstd == nullptr)))
+    return RMSNORM_ERR_INVALID_ARG;
+  const int eb = elem_bytes(dtype);
+  if (!aligned(dy, (uintptr_t)eb) || !aligned(dw, 4) || !aligned(db, 4))
+    return RMSNORM_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 0) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(C, 256)), dim3(256), 0, s, dw,
+                       (int)C);
+    if (db)
+      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(C, 256)), dim3(256), 0, s, db,
+                         (int)C);
+    return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+  }
+  GnArgs a = gn_args(B, C, S, G, K, workspace);
+  a.x = x; a.dy = dy; a.w = w; a.out = dx; a.dw = dw; a.db = db;
+  a.mean = const_cast<float*>(mean); a.rstd = const_cast<float*>(rstd);
+  const bool wide = gn_wide(x, S, eb) && gn_wide(dy, S, eb) && gn_wide(dx, S, eb);
+  return wide ? gn_by_dtype<false, true>(dtype, a, chunks, s)
+              : gn_by_dtype<false, false>(dtype, a, chunks, s);
+}
+
 }  // namespace
 
 // ---- exported C interface -------------------------------------------------------------------------
@@ -222,6 +353,30 @@ __attribute__((visibility("default"))) rmsnorm_status layernorm_bwd(
     void* stream) {
   return ln_bwd_impl(dy, lddy, x, ldx, w, mean, rstd, dx, lddx, dw, db, workspace,
                      workspace_bytes, M, N, dtype, variant, stream);
+}
+
+__attribute__((visibility("default"))) size_t groupnorm_workspace_bytes(int64_t B, int64_t C,
+                                                                        int64_t S, int64_t G,
+                                                                        rmsnorm_dtype dtype) {
+  int64_t K = 0, chunks = 0;
+  if (gn_shape(B, C, S, G, dtype, &K, &chunks) != RMSNORM_OK) return 0;
+  return (size_t)chunks * sizeof(float2);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status groupnorm_fwd(
+    const void* x, const void* w, const void* b, void* y, float* mean, float* rstd,
+    void* workspace, size_t workspace_bytes, int64_t B, int64_t C, int64_t S, int64_t G,
+    rmsnorm_dtype dtype, float eps, void* stream) {
+  return gn_fwd_impl(x, w, b, y, mean, rstd, workspace, workspace_bytes, B, C, S, G, dtype, eps,
+                     stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status groupnorm_bwd(
+    const void* dy, const void* x, const void* w, const float* mean, const float* rstd, void* dx,
+    float* dw, float* db, void* workspace, size_t workspace_bytes, int64_t B, int64_t C, int64_t S,
+    int64_t G, rmsnorm_dtype dtype, void* stream) {
+  return gn_bwd_impl(dy, x, w, mean, rstd, dx, dw, db, workspace, workspace_bytes, B, C, S, G,
+                     dtype, stream);
 }
 
 }  // extern "C"

@@ -79,6 +79,44 @@ rmsnorm_status layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_
                              size_t workspace_bytes, int64_t M, int64_t N, rmsnorm_dtype dtype,
                              rmsnorm_variant variant, void* stream);
 
+/* ---- GroupNorm ----------------------------------------------------------------------------------
+ * x is [B, C, S] contiguous (S the flattened spatial size, row-major: element (b, c, s) at
+ * (b * C + c) * S + s); C is split into G groups of Cg = C / G adjacent channels, and each
+ * (batch, group) row of Cg * S elements is normalized with its own float32 mean and rstd; the
+ * weight w [C] and bias b [C] (I/O dtype) are per channel:
+ *
+ *     y    = T( ((x - mean) * rstd) * w_c + b_c )
+ *     dx   = T( rstd * ((w_c * dy - c1) - xhat * c2) ),  c1 = sum(w_c dy) / n, c2 = sum(w_c dy xhat) / n
+ *     dW_c = sum over batch and space of dy * xhat,      dB_c = sum over batch and space of dy
+ *
+ * sums over the n = Cg * S elements of a row, in float32 (Liger-Kernel pull request 1608). The
+ * work is split into chunks of one (batch, channel) segment (at most 4096 elements for 16-bit types,
+ * 2048 for float32); per-chunk statistics and sums go to a caller-provided float32 workspace and are
+ * combined in a fixed order, so results are bit-reproducible and no atomics are used. Group sizes
+ * up to RMSNORM_MAX_N elements are supported. S * sizeof(T) a multiple of 16 with 16-byte-aligned
+ * tensors gives 16-byte accesses; anything else takes element-wise kernels. mean and rstd are
+ * float32 [B, G]. */
+
+/* Bytes of workspace groupnorm_fwd and groupnorm_bwd need (the same for both): 8 bytes per chunk.
+ * A pure function of the shape and dtype; 0 for invalid shapes. */
+size_t groupnorm_workspace_bytes(int64_t B, int64_t C, int64_t S, int64_t G, rmsnorm_dtype dtype);
+
+/* GroupNorm forward. y [B, C, S]; mean, rstd [B, G] written when not NULL (the backward needs
+ * them). w [C] required, b [C] or NULL for no bias. eps >= 0 and finite. B = 0 is a no-op.
+ * C % G != 0, or a non-positive C, S or G, returns RMSNORM_ERR_INVALID_ARG. */
+rmsnorm_status groupnorm_fwd(const void* x, const void* w, const void* b, void* y, float* mean,
+                             float* rstd, void* workspace, size_t workspace_bytes, int64_t B,
+                             int64_t C, int64_t S, int64_t G, rmsnorm_dtype dtype, float eps,
+                             void* stream);
+
+/* GroupNorm backward from the forward's mean and rstd. dx [B, C, S] (dtype); dw [C] float32
+ * (required), db [C] float32 or NULL; both fully overwritten (zeros for B = 0). The workspace
+ * contents on entry do not matter and are clobbered. */
+rmsnorm_status groupnorm_bwd(const void* dy, const void* x, const void* w, const float* mean,
+                             const float* rstd, void* dx, float* dw, float* db, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t C, int64_t S, int64_t G,
+                             rmsnorm_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -245,3 +245,39 @@ def check_ln_bwd(dx_gpu, dw_gpu, db_gpu, dy, x, w, mean_gpu, rstd_gpu, *, dtype)
         s = check_dw(db_gpu, db_o)
         stats["db_normwise"] = s["dw_normwise"]
     return stats
+
+
+def check_gn(y_gpu, mean_gpu, rstd_gpu, dx_gpu, dw_gpu, db_gpu, x, w, b, dy, *, G, eps,
+             dtype) -> dict:
+    """GroupNorm: the LayerNorm contract applied to the (batch, group) rows, the oracle's backward
+    run from the GPU's mean and rstd."""
+    x = np.asarray(x, np.float32)
+    B, C, S = x.shape
+    y_o, m_o, r_o = oracle.groupnorm_fwd(x, w, b, G=G, eps=eps, dtype=dtype)
+    rows = x.reshape(B, G, -1)
+    stats = check_stats(mean_gpu, rstd_gpu, m_o, r_o, rows.reshape(B * G, -1))
+    mg = np.asarray(mean_gpu, np.float32).reshape(B, G)
+    rg = np.asarray(rstd_gpu, np.float32).reshape(B, G)
+    xhat = oracle.layernorm.normalize(rows, mg, rg)
+    wr = np.repeat(np.asarray(w, np.float32).reshape(G, C // G), S, axis=1)
+    br = None if b is None else np.repeat(np.asarray(b, np.float32).reshape(G, C // G), S, axis=1)
+    y_c = oracle.layernorm.affine(xhat, wr, br, dtype=dtype).reshape(B, C, S)
+    cond = same_bits(y_gpu, y_c)
+    stats["y_conditioned_bitexact"] = float(cond.mean()) if cond.size else 1.0
+    assert cond.all(), (stats, np.argwhere(~cond)[:5])
+    cnd = 1.0 + np.abs(np.asarray(m_o, np.float64)) * np.asarray(r_o, np.float64)
+    stats.update(check_floored(np.asarray(y_gpu).reshape(B * G, -1), y_o.reshape(B * G, -1), dtype,
+                               "y", cond=cnd.reshape(-1)))
+    dx_o, dw_o, db_o = oracle.groupnorm_bwd(dy, x, w, mg, rg, G=G, dtype=dtype)
+    if dtype == "f32":
+        num = np.linalg.norm(dx_gpu.astype(np.float64) - dx_o)
+        den = np.linalg.norm(dx_o.astype(np.float64))
+        stats["dx_normwise"] = float(num / den) if den > 0 else float(num)
+        assert stats["dx_normwise"] <= F32_DX_NORMWISE, stats
+    else:
+        stats.update(check_floored(np.asarray(dx_gpu).reshape(B * G, -1), dx_o.reshape(B * G, -1),
+                                   dtype, "dx", frac=LN_DX_BITEXACT_FRAC))
+    stats.update(check_dw(dw_gpu, dw_o))
+    if db_gpu is not None:
+        stats["db_normwise"] = check_dw(db_gpu, db_o)["dw_normwise"]
+    return stats

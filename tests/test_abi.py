@@ -209,3 +209,49 @@ def test_layernorm_workspace_bytes(lib):
     assert f(4096, 4096, BF16) == 2 * 256 * 4096 * 4
     assert f(3, 10, F32) == 2 * 3 * 12 * 4
     assert f(0, 10, F32) == 0 and f(5, 0, F32) == 0 and f(5, 5, 9) == 0
+
+
+def gnf(lib, x=FAKE, w=FAKE + 0x1000, b=None, y=FAKE + 0x2000, mean=None, rstd=None,
+        ws=FAKE + 0x3000, wsb=1 << 20, B=2, C=4, S=8, G=2, dtype=BF16, eps=1e-5):
+    return lib.groupnorm_fwd(x, w, b, y, mean, rstd, ws, wsb, B, C, S, G, dtype, eps, None)
+
+
+def gnb(lib, dy=FAKE, x=FAKE + 0x1000, w=FAKE + 0x2000, mean=FAKE + 0x3000, rstd=FAKE + 0x3800,
+        dx=FAKE + 0x4000, dw=FAKE + 0x5000, db=None, ws=FAKE + 0x6000, wsb=1 << 20, B=2, C=4, S=8,
+        G=2, dtype=BF16):
+    return lib.groupnorm_bwd(dy, x, w, mean, rstd, dx, dw, db, ws, wsb, B, C, S, G, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
+    (dict(ws=None), INVALID), (dict(B=-1), INVALID), (dict(C=0), INVALID), (dict(S=0), INVALID),
+    (dict(G=0), INVALID), (dict(G=3), INVALID), (dict(dtype=4), INVALID), (dict(eps=-1.0), INVALID),
+    (dict(eps=float("inf")), INVALID), (dict(x=FAKE + 1), MISALIGNED), (dict(b=FAKE + 1), MISALIGNED),
+    (dict(mean=FAKE + 2), MISALIGNED), (dict(ws=FAKE + 8), MISALIGNED), (dict(wsb=2 * 4 * 8 - 1), WORKSPACE),
+    (dict(C=2, G=1, S=(1 << 23) + 1), UNSUPPORTED),
+])
+def test_groupnorm_fwd_rejects(lib, kw, status):
+    assert gnf(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), INVALID), (dict(x=None), INVALID), (dict(w=None), INVALID),
+    (dict(mean=None), INVALID), (dict(rstd=None), INVALID), (dict(dx=None), INVALID),
+    (dict(dw=None), INVALID), (dict(G=3), INVALID), (dict(db=FAKE + 2), MISALIGNED),
+    (dict(dy=FAKE + 1), MISALIGNED), (dict(wsb=0), WORKSPACE),
+])
+def test_groupnorm_bwd_rejects(lib, kw, status):
+    assert gnb(lib, **kw) == status
+
+
+def test_groupnorm_workspace_bytes(lib):
+    f = lib.groupnorm_workspace_bytes
+    assert f(2, 4, 8, 2, BF16) == 2 * 4 * 1 * 8
+    assert f(1, 16, 65536, 4, BF16) == 16 * 16 * 8          # 4096-element chunks
+    assert f(1, 16, 65536, 4, F32) == 16 * 32 * 8           # 2048-element chunks
+    assert f(0, 4, 8, 2, BF16) == 0
+    assert f(2, 4, 8, 3, BF16) == 0 and f(2, 0, 8, 1, BF16) == 0 and f(2, 4, 8, 2, 9) == 0
+
+
+def test_groupnorm_no_batch_is_a_noop(lib):
+    assert gnf(lib, x=None, w=None, y=None, ws=None, B=0) == OK

@@ -1,0 +1,105 @@
+"""GPU parity of GroupNorm (through the C interface) against the CPU oracle.
+
+Cases: the group_norm page's shapes that the oracle finishes in seconds ((1, 16, 256, 256) with 4
+groups in bf16 and in float16 with an upstream gradient and weight of ones; (2, 64, 32, 32) with 8
+groups and an input offset of 16; (2, 8, 16) with 4 groups in float32), segments that split into
+several chunks with a ragged last chunk, spatial sizes that break 16-byte alignment (element-wise
+kernels), one channel per group and one group, tiny spatial sizes, and no bias.
+"""
+import numpy as np
+import pytest
+
+from parity import check_gn, same_bits, to_np
+from workloads import GN_WORKLOADS, make_gn_inputs, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bwd_precision_numerics_amd as rn  # noqa: E402
+
+DEV = "cuda:0"
+BASE = {"bf16": GN_WORKLOADS["gn_bf16_1x16x256x256_g4"],
+        "f16": GN_WORKLOADS["gn_bf16_1x16x256x256_g4"].with_(dtype="f16"),
+        "f32": GN_WORKLOADS["gn_f32_2x8x16_g4"]}
+
+
+def run_gn(wl, B=None, C=None, S=None, G=None, seed=None, bias=True):
+    inp = make_gn_inputs(wl, B=B, C=C, S=S, seed=seed)
+    G = wl.G if G is None else G
+    x, w, b, dy = inp["x"], inp["w"], (inp["b"] if bias else None), inp["dy"]
+    Bv, Cv, Sv = x.shape
+    print(f"gn case {wl.name} dtype={wl.dtype} B={Bv} C={Cv} S={Sv} G={G} seed={seed} "
+          f"bias={bias}", flush=True)
+    xt, dyt = to_device(x, wl.dtype, DEV), to_device(dy, wl.dtype, DEV)
+    wt = to_device(w, wl.dtype, DEV)
+    bt = to_device(b, wl.dtype, DEV) if bias else None
+    y, mean, rstd = rn.groupnorm_fwd(xt, G, wt, bt, eps=wl.eps)
+    dx, dw, db = rn.groupnorm_bwd(dyt, xt, G, wt, mean, rstd, bias=bias)
+    torch.cuda.synchronize()
+    out = [to_np(t) for t in (y, mean, rstd, dx, dw)] + [to_np(db) if bias else None]
+    st = check_gn(out[0], out[1], out[2], out[3], out[4], out[5], x, w, b, dy, G=G, eps=wl.eps,
+                  dtype=wl.dtype)
+    return st, out
+
+
+@pytest.mark.parametrize("name", ["gn_bf16_1x16x256x256_g4", "gn_f16_1x16x256x256_g4_ones",
+                                  "gn_bf16_2x64x32x32_g8_offset16", "gn_f32_2x8x16_g4"])
+def test_gn_page_shapes(name):
+    st, out = run_gn(GN_WORKLOADS[name])
+    print(st)
+    if name == "gn_f16_1x16x256x256_g4_ones":
+        dx, db = out[3], out[5]
+        assert np.isfinite(dx).all() and float(np.abs(dx).max()) <= 2.0**-24
+        assert np.all(db == 65536.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("B,C,S,G", [
+    (2, 8, 4096, 2),      # one full chunk per segment (16-bit)
+    (3, 6, 9000, 3),      # several chunks, ragged last chunk
+    (2, 4, 1000, 4),      # one channel per group; S * 2 bytes not a multiple of 16 for 16-bit
+    (2, 6, 333, 1),       # one group, odd S: element-wise kernels
+    (5, 12, 1, 3),        # one element per channel
+    (1, 3, 7, 3),         # one channel per group, tiny S
+    (4, 64, 64, 16),
+])
+def test_gn_shapes(dtype, B, C, S, G):
+    run_gn(BASE[dtype], B=B, C=C, S=S, G=G, seed=B * 1000 + C + S)
+
+
+def test_gn_without_bias():
+    _, a = run_gn(BASE["bf16"], B=2, C=8, S=2048, G=4, seed=5, bias=False)
+    _, b = run_gn(BASE["bf16"], B=2, C=8, S=2048, G=4, seed=5, bias=True)
+    assert same_bits(a[3], b[3]).all() and same_bits(a[4], b[4]).all()
+
+
+def test_gn_repeatable():
+    _, a = run_gn(BASE["bf16"], B=4, C=32, S=4096, G=8, seed=7)
+    _, b = run_gn(BASE["bf16"], B=4, C=32, S=4096, G=8, seed=7)
+    for u, v in zip(a, b):
+        assert same_bits(u, v).all()
+
+
+def test_gn_four_dim_input():
+    """[B, C, H, W] input flattens its spatial dimensions."""
+    wl = BASE["bf16"]
+    inp = make_gn_inputs(wl, B=2, C=8, S=64 * 32, seed=11)
+    x4 = to_device(inp["x"], "bf16", DEV).reshape(2, 8, 64, 32)
+    w = to_device(inp["w"], "bf16", DEV)
+    y4, m4, r4 = rn.groupnorm_fwd(x4, 4, w)
+    y3, m3, r3 = rn.groupnorm_fwd(x4.reshape(2, 8, -1), 4, w)
+    torch.cuda.synchronize()
+    assert y4.shape == (2, 8, 64, 32)
+    assert same_bits(to_np(y4).reshape(2, 8, -1), to_np(y3)).all()
+
+
+def test_gn_zero_batch():
+    x = torch.empty((0, 8, 16), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(8, dtype=torch.bfloat16, device=DEV)
+    y, m, r = rn.groupnorm_fwd(x, 4, w)
+    dx, dw, db = rn.groupnorm_bwd(x, x, 4, w, m, r)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 8, 16) and float(dw.abs().sum()) == 0.0 and float(db.abs().sum()) == 0.0

@@ -167,3 +167,75 @@ LN_WORKLOADS = {
     "ln_fp16_8192x8192": Workload("ln_fp16_8192x8192", "f16", 8192, 8192, "once", 0.0, 1e-5,
                                   ("normal", 0.0, 8.0), _GAIN, ("ones",), 0),
 }
+
+
+# GroupNorm: x [B, C, S] (S the flattened spatial size), G groups. Shapes from the group_norm
+# page's Details table (Liger-Kernel pull request 1608, its backward timings and accuracy cases).
+@dataclasses.dataclass(frozen=True)
+class GnWorkload:
+    name: str
+    dtype: str
+    B: int
+    C: int
+    S: int
+    G: int
+    eps: float
+    x_dist: tuple
+    w_dist: tuple
+    dy_dist: tuple
+    b_dist: tuple = _BIAS
+    seed: int = 0
+
+    def with_(self, **kw) -> "GnWorkload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def itemsize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def numel(self) -> int:
+        return self.B * self.C * self.S
+
+    def fwd_bytes(self) -> int:
+        """Read x, write y, read w and b, write the float32 mean and rstd."""
+        s = self.itemsize
+        return 2 * self.numel * s + 2 * self.C * s + 8 * self.B * self.G
+
+    def bwd_bytes(self) -> int:
+        """Read dy and x, write dx, read w, mean and rstd, write the float32 dw and db."""
+        s = self.itemsize
+        return 3 * self.numel * s + self.C * s + 8 * self.B * self.G + 8 * self.C
+
+
+GN_WORKLOADS = {
+    w.name: w for w in [
+        GnWorkload("gn_bf16_1x16x256x256_g4", "bf16", 1, 16, 256 * 256, 4, 1e-5, _STD, _GAIN,
+                   _STD),
+        GnWorkload("gn_bf16_16x32x256x256_g8", "bf16", 16, 32, 256 * 256, 8, 1e-5, _STD, _GAIN,
+                   _STD),
+        GnWorkload("gn_bf16_16x512x64x64_g32", "bf16", 16, 512, 64 * 64, 32, 1e-5, _STD, _GAIN,
+                   _STD),
+        GnWorkload("gn_bf16_64x64x8192_g8", "bf16", 64, 64, 8192, 8, 1e-5, _STD, _GAIN, _STD),
+        GnWorkload("gn_f16_1x16x256x256_g4_ones", "f16", 1, 16, 256 * 256, 4, 1e-5, _STD,
+                   ("ones",), ("ones",), ("normal", 0.0, 0.0)),
+        GnWorkload("gn_bf16_2x64x32x32_g8_offset16", "bf16", 2, 64, 32 * 32, 8, 1e-5,
+                   ("normal", 16.0, 1.0), _GAIN, _STD),
+        GnWorkload("gn_f32_2x8x16_g4", "f32", 2, 8, 16, 4, 1e-5, _STD, _GAIN, _STD),
+    ]
+}
+GN_HEADLINE = "gn_bf16_16x32x256x256_g8"
+
+
+def make_gn_inputs(wl: GnWorkload, B: int | None = None, C: int | None = None,
+                   S: int | None = None, seed: int | None = None) -> dict:
+    """Draw ``x`` [B, C, S], ``w`` [C], ``dy`` [B, C, S], then ``b`` [C] (T values in float32)."""
+    B = wl.B if B is None else B
+    C = wl.C if C is None else C
+    S = wl.S if S is None else S
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = _draw(rng, wl.x_dist, (B, C, S))
+    w = _draw(rng, wl.w_dist, (C,))
+    dy = _draw(rng, wl.dy_dist, (B, C, S))
+    b = _draw(rng, wl.b_dist, (C,))
+    return {k: to_dtype_values(v, wl.dtype) for k, v in (("x", x), ("w", w), ("dy", dy), ("b", b))}
