@@ -1,4 +1,4 @@
-"""CPU oracle for the RMSNorm forward/backward path (and LayerNorm / GroupNorm) — TEST INFRASTRUCTURE, NOT PRODUCT CODE.
+"""CPU oracle for the RMSNorm forward/backward path (and LayerNorm / GroupNorm / softmax) — TEST INFRASTRUCTURE, NOT PRODUCT CODE.
 
 A plain, slow, directly checkable NumPy implementation of what the GPU library computes: float64
 reductions, float32 elementwise arithmetic emulated with NumPy float32 operations, and
@@ -13,10 +13,12 @@ from .rounding import round_to_format, rne_bf16, rne_f16, rne_f32, rne_fp8, rne_
 from .rmsnorm import (CASTS, DTYPES, ROUNDINGS, apply_gain, gain, rmsnorm_bwd, rmsnorm_dw, rmsnorm_fwd,
                       rmsnorm_fwd_fp8, rstd_of)
 from .layernorm import groupnorm_bwd, groupnorm_fwd, layernorm_bwd, layernorm_fwd, row_stats
+from .softmax import rmsnorm_bwd_f64, rmsnorm_fwd_f64, softmax_bwd, softmax_fwd
 
 __all__ = [
     "round_to_format", "rne_bf16", "rne_f16", "rne_f32", "rne_fp8", "rne_to", "ulp_of",
     "CASTS", "DTYPES", "ROUNDINGS", "apply_gain", "gain", "rmsnorm_bwd", "rmsnorm_dw", "rmsnorm_fwd",
     "rmsnorm_fwd_fp8", "rstd_of",
     "groupnorm_bwd", "groupnorm_fwd", "layernorm_bwd", "layernorm_fwd", "row_stats",
+    "rmsnorm_bwd_f64", "rmsnorm_fwd_f64", "softmax_bwd", "softmax_fwd",
 ]
