@@ -91,6 +91,8 @@ def parse_args(argv=None):
     ap.add_argument("--kernel-only", choices=["fwd", "bwd_rows", "dw_reduce", "fwd_fp8"],
                     default=None,
                     help="launch only this kernel --steps times (for counter collection)")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the LayerNorm / GroupNorm measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, copy a buffer of this many MiB --steps times "
                          "(calibrates the HBM byte counters)")
@@ -239,6 +241,114 @@ def copy_ceiling(torch, sets, launches):
             "bytes_per_launch": nbytes, "what": "hipMemcpy device-to-device, read x write y"}
 
 
+def graph_time(torch, fn, launches):
+    """Average seconds per call of fn(k): events around one replay of a graph of `launches` calls."""
+    g = capture(torch, fn, launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / launches
+    del g
+    return sec
+
+
+def layernorm_row(torch, rn, sets, launches):
+    """LayerNorm forward and backward at the headline shape, on the same rotating x / dy buffers
+    (their values are the LayerNorm workload's: x, w and dy are drawn first, then the bias)."""
+    from workloads import LN_WORKLOADS, make_norm_inputs, to_device
+    wl = LN_WORKLOADS["ln_bf16_4096x4096"]
+    assert (wl.M, wl.N, wl.dtype) == (sets.wl.M, sets.wl.N, sets.wl.dtype)
+    lib, M, N = sets.lib, wl.M, wl.N
+    dt = rn.DTYPE_CODES[wl.dtype]
+    b = to_device(make_norm_inputs(wl)["b"], wl.dtype, "cuda:0")
+    n = len(sets.sets)
+    mean = [torch.empty(M, dtype=torch.float32, device="cuda:0") for _ in range(n)]
+    db = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    wsb = rn.layernorm_workspace_bytes(M, N, wl.dtype)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device="cuda:0")
+
+    def fwd(k):
+        s = sets.sets[k % n]
+        st = lib.layernorm_fwd(s["x"].data_ptr(), N, sets.w.data_ptr(), b.data_ptr(),
+                               s["y"].data_ptr(), N, mean[k % n].data_ptr(), s["rstd"].data_ptr(),
+                               M, N, dt, wl.eps, 0, sets.stream())
+        if st:
+            raise RuntimeError(f"layernorm_fwd status {st}")
+
+    def bwd(k):
+        s = sets.sets[(k + n // 2) % n]
+        st = lib.layernorm_bwd(s["dy"].data_ptr(), N, s["x"].data_ptr(), N, sets.w.data_ptr(),
+                               mean[(k + n // 2) % n].data_ptr(), s["rstd"].data_ptr(),
+                               s["dx"].data_ptr(), N, s["dw"].data_ptr(), db.data_ptr(),
+                               ws.data_ptr(), wsb, M, N, dt, 0, sets.stream())
+        if st:
+            raise RuntimeError(f"layernorm_bwd status {st}")
+
+    for k in range(n):
+        fwd(k)
+    torch.cuda.synchronize()
+    tf, tb = graph_time(torch, fwd, launches), graph_time(torch, bwd, launches)
+    s = wl.itemsize
+    fb = 2 * M * N * s + 2 * N * s + 8 * M
+    bb = 3 * M * N * s + N * s + 8 * M + 8 * N
+    return {"workload": wl.name, "fwd_us": round(tf * 1e6, 3), "bwd_us": round(tb * 1e6, 3),
+            "fwd_GBps": round(fb / tf / 1e9, 1), "bwd_GBps": round(bb / tb / 1e9, 1),
+            "fwd_bytes": fb, "bwd_bytes": bb,
+            "bwd_includes": "rows kernel + dw and db reductions"}
+
+
+def groupnorm_row(torch, rn, launches, rotate_mib):
+    """GroupNorm forward and backward at the group_norm page's (16, 32, 256, 256), 8 groups."""
+    from workloads import GN_HEADLINE, GN_WORKLOADS, make_gn_inputs, to_device
+    wl = GN_WORKLOADS[GN_HEADLINE]
+    lib, dev = rn.library(), "cuda:0"
+    dt = rn.DTYPE_CODES[wl.dtype]
+    inp = make_gn_inputs(wl)
+    x0, dy0 = to_device(inp["x"], wl.dtype, dev), to_device(inp["dy"], wl.dtype, dev)
+    w, b = to_device(inp["w"], wl.dtype, dev), to_device(inp["b"], wl.dtype, dev)
+    del inp
+    n = max(4, -(-rotate_mib * 2**20 // (wl.numel * wl.itemsize)))
+    sets = [{"x": x0.clone(), "dy": dy0.clone(), "y": torch.empty_like(x0),
+             "dx": torch.empty_like(x0),
+             "mean": torch.empty(wl.B * wl.G, dtype=torch.float32, device=dev),
+             "rstd": torch.empty(wl.B * wl.G, dtype=torch.float32, device=dev)} for _ in range(n)]
+    del x0, dy0
+    dw = torch.empty(wl.C, dtype=torch.float32, device=dev)
+    db = torch.empty(wl.C, dtype=torch.float32, device=dev)
+    wsb = rn.groupnorm_workspace_bytes(wl.B, wl.C, wl.S, wl.G, wl.dtype)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+
+    def fwd(k):
+        s = sets[k % n]
+        st = lib.groupnorm_fwd(s["x"].data_ptr(), w.data_ptr(), b.data_ptr(), s["y"].data_ptr(),
+                               s["mean"].data_ptr(), s["rstd"].data_ptr(), ws.data_ptr(), wsb,
+                               wl.B, wl.C, wl.S, wl.G, dt, wl.eps, stream())
+        if st:
+            raise RuntimeError(f"groupnorm_fwd status {st}")
+
+    def bwd(k):
+        s = sets[(k + n // 2) % n]
+        st = lib.groupnorm_bwd(s["dy"].data_ptr(), s["x"].data_ptr(), w.data_ptr(),
+                               s["mean"].data_ptr(), s["rstd"].data_ptr(), s["dx"].data_ptr(),
+                               dw.data_ptr(), db.data_ptr(), ws.data_ptr(), wsb, wl.B, wl.C,
+                               wl.S, wl.G, dt, stream())
+        if st:
+            raise RuntimeError(f"groupnorm_bwd status {st}")
+
+    for k in range(n):
+        fwd(k)
+    torch.cuda.synchronize()
+    tf, tb = graph_time(torch, fwd, launches), graph_time(torch, bwd, launches)
+    return {"workload": wl.name, "fwd_us": round(tf * 1e6, 3), "bwd_us": round(tb * 1e6, 3),
+            "fwd_GBps": round(wl.fwd_bytes() / tf / 1e9, 1),
+            "bwd_GBps": round(wl.bwd_bytes() / tb / 1e9, 1),
+            "fwd_bytes": wl.fwd_bytes(), "bwd_bytes": wl.bwd_bytes(), "buffer_sets": n,
+            "passes": "fwd reads x twice (statistics, then normalize); bwd reads x and dy twice"}
+
+
 def cpu_baseline(wl, rounding, inp, budget_s):
     """The CPU oracle, single-threaded, over row chunks of the same inputs (cycling through the
     rows again if one pass takes less than the budget) until the time budget is used."""
@@ -367,6 +477,12 @@ def main(argv=None) -> int:
         "copy_ceiling": copy,
         "frac_of_copy_ceiling": round(value / copy["GBps"], 4),
     }
+    if not args.no_rows and name == HEADLINE:
+        launches = max(min(args.steps, 100), 20)
+        line["rows"] = {"layernorm": layernorm_row(torch, rn, sets, launches)}
+        del sets
+        torch.cuda.empty_cache()
+        line["rows"]["groupnorm"] = groupnorm_row(torch, rn, launches, args.rotate_mib)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(wl, rounding, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -14,6 +14,8 @@ raises ``LibraryMissing`` (build it with ``python -m bwd_precision_numerics_amd.
     dx, dw, db    = layernorm_bwd(dy, x, w, mean, rstd, bias=True)
     y, mean, rstd = groupnorm_fwd(x, G, w, b, eps=1e-5)    # GroupNorm of [B, C, *spatial]
     dx, dw, db    = groupnorm_bwd(dy, x, G, w, mean, rstd)
+    y = softmax_fwd(x); dx = softmax_bwd(dy, y)             # softmax over the last dimension
+    y, rstd = fwd_f64(x64, w64); dx, dw = bwd_f64(dy64, x64, w64, rstd)   # float64 RMSNorm
 
 ``rounding="twice"`` is the Llama convention T(float(T(xhat)) * g); ``"once"`` is the Gemma
 convention T(xhat * g); the gain is ``g = offset + w`` (offset 1 for Gemma).
@@ -27,9 +29,10 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librmsnorm.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "librmsnorm.h")
-HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(HERE), "include", "libnorms.h")]
+HEADER_PATHS = [HEADER_PATH] + [os.path.join(os.path.dirname(HERE), "include", f)
+                               for f in ("libnorms.h", "libsoftmax.h")]
 
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 ROUNDING_CODES = {"once": 0, "twice": 1}
 BWD_AUTOGRAD_CASTS = 0x10  # flag OR-ed into the backward's rounding argument
 CASTS = ("float32", "autograd")
@@ -58,6 +61,7 @@ _p = ctypes.c_void_p
 _f = ctypes.c_float
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
+_d = ctypes.c_double
 SIGNATURES = {
     "rmsnorm_fwd": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i, _f, _f, _i, _p]),
     "rmsnorm_fwd_variant": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i, _f, _f, _i, _i, _p]),
@@ -79,6 +83,12 @@ SIGNATURES = {
     "groupnorm_fwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _sz, _i64, _i64, _i64, _i64, _i, _f, _p]),
     "groupnorm_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _i64, _i64, _i64, _i64, _i,
                            _p]),
+    "softmax_fwd": (_i, [_p, _i64, _p, _i64, _i64, _i64, _i, _i, _p]),
+    "softmax_bwd": (_i, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i, _i, _p]),
+    "rmsnorm_fwd_f64": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _d, _d, _p]),
+    "rmsnorm_bwd_f64_workspace_bytes": (_sz, [_i64, _i64]),
+    "rmsnorm_bwd_f64": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p, _sz, _i64, _i64, _d,
+                             _p]),
     "rmsnorm_status_string": (ctypes.c_char_p, [_i]),
     "rmsnorm_abi_version": (_i, []),
 }
@@ -92,7 +102,7 @@ def header_text(paths=None) -> str:
 
 def header_functions(paths=None) -> list:
     """Names of the functions the C headers declare."""
-    return sorted(set(re.findall(r"\b((?:rmsnorm|layernorm|groupnorm)_[a-z_0-9]+)\s*\(",
+    return sorted(set(re.findall(r"\b((?:rmsnorm|layernorm|groupnorm|softmax)_[a-z_0-9]+)\s*\(",
                                  header_text(paths))))
 
 
@@ -495,6 +505,89 @@ def groupnorm_bwd(dy, x, G: int, w, mean, rstd, bias: bool = True, dx=None, dw=N
                                  _stream(x.device))
     _check("groupnorm_bwd", st)
     return dx, dw, (db if bias else None)
+
+
+# ---- softmax and float64 RMSNorm -------------------------------------------------------------------
+
+def _any_dtype_name(t) -> str:
+    """dtype name for the entry points that also take float64."""
+    torch = _torch()
+    return "f64" if t.dtype == torch.float64 else dtype_name(t)
+
+
+def softmax_fwd(x, variant: str = "auto", y=None):
+    """Softmax over the last dimension of a 2-D ``x`` (float32 / float16 / bfloat16 / float64)."""
+    torch = _torch()
+    dt = _any_dtype_name(x)
+    M, N = x.shape
+    px, ldx = _rows(x, "x")
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if y.dtype != x.dtype or tuple(y.shape) != (M, N):
+        raise ValueError("y must match x in shape and dtype")
+    py, ldy = _rows(y, "y")
+    _same_device(x, y)
+    st = library().softmax_fwd(px, ldx, py, ldy, M, N, DTYPE_CODES[dt], VARIANT_CODES[variant],
+                               _stream(x.device))
+    _check("softmax_fwd", st)
+    return y
+
+
+def softmax_bwd(dy, y, variant: str = "auto", dx=None):
+    """dx = y * (dy - sum(dy * y)) over the last dimension, from the forward's output ``y``."""
+    torch = _torch()
+    dt = _any_dtype_name(y)
+    if dy.dtype != y.dtype or dy.shape != y.shape:
+        raise ValueError("dy must match y in shape and dtype")
+    M, N = y.shape
+    if dx is None:
+        dx = torch.empty((M, N), dtype=y.dtype, device=y.device)
+    pdy, lddy = _rows(dy, "dy")
+    py, ldy = _rows(y, "y")
+    pdx, lddx = _rows(dx, "dx")
+    _same_device(dy, y, dx)
+    st = library().softmax_bwd(pdy, lddy, py, ldy, pdx, lddx, M, N, DTYPE_CODES[dt],
+                               VARIANT_CODES[variant], _stream(y.device))
+    _check("softmax_bwd", st)
+    return dx
+
+
+def fwd_f64(x, w, eps: float = 1e-6, offset: float = 0.0, y=None, rstd=None):
+    """RMSNorm with float64 I/O and float64 statistics. Returns ``(y, rstd)`` (rstd float64)."""
+    torch = _torch()
+    if x.dtype != torch.float64 or w.dtype != torch.float64:
+        raise TypeError("x and w must be float64")
+    M, N = x.shape
+    px, ldx = _rows(x, "x")
+    y = torch.empty_like(x) if y is None else y
+    rstd = torch.empty((M,), dtype=torch.float64, device=x.device) if rstd is None else rstd
+    py, ldy = _rows(y, "y")
+    _same_device(x, w, y, rstd)
+    st = library().rmsnorm_fwd_f64(px, ldx, _vec(w, "w", N), py, ldy, _vec(rstd, "rstd", M), M,
+                                   N, eps, offset, _stream(x.device))
+    _check("rmsnorm_fwd_f64", st)
+    return y, rstd
+
+
+def bwd_f64(dy, x, w, rstd, offset: float = 0.0, dx=None, dw=None, workspace=None):
+    """Backward of ``fwd_f64``. Returns ``(dx, dw)``, both float64."""
+    torch = _torch()
+    M, N = x.shape
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty((N,), dtype=torch.float64, device=x.device) if dw is None else dw
+    need = int(library().rmsnorm_bwd_f64_workspace_bytes(M, N))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 7) // 8, dtype=torch.float64, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    pdy, lddy = _rows(dy, "dy")
+    px, ldx = _rows(x, "x")
+    pdx, lddx = _rows(dx, "dx")
+    _same_device(dy, x, w, rstd, dx, dw, workspace)
+    st = library().rmsnorm_bwd_f64(pdy, lddy, px, ldx, _vec(w, "w", N), _vec(rstd, "rstd", M), pdx,
+                                   lddx, _vec(dw, "dw", N), workspace.data_ptr(), wsb, M, N, offset,
+                                   _stream(x.device))
+    _check("rmsnorm_bwd_f64", st)
+    return dx, dw
 
 
 def _make_autograd():

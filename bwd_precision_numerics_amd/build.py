@@ -1,7 +1,8 @@
 """Compile the HIP library ``librmsnorm.so`` for gfx950, in place next to this file.
 
-The library is built from two translation units: ``librmsnorm.hip`` (the RMSNorm entry points of
-``include/librmsnorm.h``) and ``libnorms.hip`` (LayerNorm and GroupNorm, ``include/libnorms.h``).
+The library is built from three translation units: ``librmsnorm.hip`` (the RMSNorm entry points of
+``include/librmsnorm.h``), ``libnorms.hip`` (LayerNorm and GroupNorm, ``include/libnorms.h``) and
+``libsoftmax.hip`` (softmax, ``include/libsoftmax.h``, and the float64 RMSNorm).
 
 Usage: ``python -m bwd_precision_numerics_amd.build [--resource-usage FILE]``.
 
@@ -16,6 +17,7 @@ Flags:
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -23,12 +25,12 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", f) for f in ("librmsnorm.hip", "libnorms.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("librmsnorm.hip", "libnorms.hip", "libsoftmax.hip")]
 OUT = os.path.join(HERE, "librmsnorm.so")
 HEADERS = [os.path.join(HERE, "csrc", f) for f in
            ("host_common.hpp", "rmsnorm_common.hpp", "rmsnorm_fwd.hpp", "rmsnorm_bwd.hpp",
-            "layernorm.hpp", "groupnorm.hpp")]
-HEADERS += [os.path.join(ROOT, "include", f) for f in ("librmsnorm.h", "libnorms.h")]
+            "layernorm.hpp", "groupnorm.hpp", "softmax.hpp")]
+HEADERS += [os.path.join(ROOT, "include", f) for f in ("librmsnorm.h", "libnorms.h", "libsoftmax.h")]
 
 
 def hipcc() -> str:
@@ -38,8 +40,9 @@ def hipcc() -> str:
 
 
 def flags() -> list:
+    """Compile flags of every translation unit."""
     return [
-        "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
         "-ffp-contract=off",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-fvisibility=hidden",
@@ -47,22 +50,37 @@ def flags() -> list:
     ]
 
 
-def build(resource_usage: str | None = None, verbose: bool = False) -> str:
-    """Compile librmsnorm.so (always recompiles). Returns the path of the library."""
-    tmp = OUT + ".tmp"
-    cmd = [hipcc()] + flags() + SRCS + ["-o", tmp]
-    if resource_usage:
-        cmd += ["-Rpass-analysis=kernel-resource-usage"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
-    diag = proc.stdout + proc.stderr
+    return proc.returncode, proc.stdout + proc.stderr
+
+
+def build(resource_usage: str | None = None, verbose: bool = False) -> str:
+    """Compile librmsnorm.so (always recompiles; the translation units in parallel, into objects
+    under ``_build/``, then one link). Returns the path of the library."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    objs = [os.path.join(objdir, os.path.splitext(os.path.basename(s))[0] + ".o") for s in SRCS]
+    cmds = [[hipcc()] + flags() + extra + ["-c", src, "-o", obj] for src, obj in zip(SRCS, objs)]
+    with concurrent.futures.ThreadPoolExecutor(len(cmds)) as ex:
+        results = list(ex.map(lambda c: _run(c, verbose), cmds))
+    diag = "".join(d for _, d in results)
     if resource_usage:
         with open(resource_usage, "w") as f:
             f.write(diag)
-    if proc.returncode != 0:
+    if any(rc for rc, _ in results):
         sys.stderr.write(diag)
-        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+        raise RuntimeError("hipcc failed compiling " +
+                           ", ".join(os.path.basename(s) for s, (rc, _) in zip(SRCS, results) if rc))
+    tmp = OUT + ".tmp"
+    rc, d = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
+                 verbose)
+    if rc:
+        sys.stderr.write(d)
+        raise RuntimeError(f"hipcc link failed with exit code {rc}")
     os.replace(tmp, OUT)
     return OUT
 

@@ -15,7 +15,9 @@ namespace {
 constexpr int kFwdBlockThreads = 256;   // forward rows per block = 256 / threads-per-row
 constexpr int kFwdMaxIters = 8;         // 16-byte vectors per thread, forward register kernels
 
-int elem_bytes(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F32 ? 4 : 2; }
+int elem_bytes(rmsnorm_dtype d) {
+  return d == RMSNORM_DTYPE_F32 ? 4 : (d == RMSNORM_DTYPE_F64 ? 8 : 2);
+}
 int vec_elems(rmsnorm_dtype d) { return 16 / elem_bytes(d); }
 bool dtype_ok(int d) { return d == RMSNORM_DTYPE_F32 || d == RMSNORM_DTYPE_F16 || d == RMSNORM_DTYPE_BF16; }
 bool rounding_ok(int r) { return r == RMSNORM_ROUND_ONCE || r == RMSNORM_ROUND_TWICE; }

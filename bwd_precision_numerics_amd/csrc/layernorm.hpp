@@ -235,8 +235,10 @@ struct LnBwdArgs {
 
 // Register kernel on the persistent grid of the RMSNorm backward (block b owns rows b, b + P, ...).
 // A ring of DEPTH + 1 rows of raw (x, dy) and their (mean, rstd) per row group keeps DEPTH rows in
-// flight while one is reduced and written. HAS_DB adds the bias-gradient accumulators.
-template <DT D, int ITERS, int DEPTH, bool HAS_DB>
+// flight while one is reduced and written. HAS_DB adds the bias-gradient accumulators. KEEP holds
+// xhat and w * dy from the first pass for the second (fewer vector ALU operations, more registers)
+// instead of recomputing them from the raw row.
+template <DT D, int ITERS, int DEPTH, bool HAS_DB, bool KEEP>
 __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -316,6 +318,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
         if (s + DEPTH < nsteps) load_row((j + DEPTH) % RING, s + DEPTH);
         const float mu = rm[j], rs = rr[j];
         float d1a = 0.f, d1b = 0.f, d2a = 0.f, d2b = 0.f;
+        float kx[KEEP ? K : 1], kg[KEEP ? K : 1];
 #pragma unroll
         for (int it = 0; it < ITERS; ++it) {
           float xf[V], df[V];
@@ -325,6 +328,12 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
           for (int e = 0; e < V; e += 2) {
             const float xh0 = (xf[e] - mu) * rs, xh1 = (xf[e + 1] - mu) * rs;
             const float gd0 = g[it][e] * df[e], gd1 = g[it][e + 1] * df[e + 1];
+            if constexpr (KEEP) {
+              kx[it * V + e] = xh0;
+              kx[it * V + e + 1] = xh1;
+              kg[it * V + e] = gd0;
+              kg[it * V + e + 1] = gd1;
+            }
             accw[it * V + e] = __builtin_fmaf(df[e], xh0, accw[it * V + e]);
             accw[it * V + e + 1] = __builtin_fmaf(df[e + 1], xh1, accw[it * V + e + 1]);
             if constexpr (HAS_DB) {
@@ -348,14 +357,21 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
           for (int it = 0; it < ITERS; ++it) {
             const int col = (it * TPR + tl) * V;
             if (col >= N) continue;
-            float xf[V], df[V], o[V];
-            IO::unpack(rx[j][it], xf);
-            IO::unpack(rd[j][it], df);
+            float o[V];
+            if constexpr (KEEP) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-              const float xh = (xf[e] - mu) * rs;
-              const float gd = g[it][e] * df[e];
-              o[e] = rs * ((gd - c1) - xh * c2);
+              for (int e = 0; e < V; ++e)
+                o[e] = rs * ((kg[it * V + e] - c1) - kx[it * V + e] * c2);
+            } else {
+              float xf[V], df[V];
+              IO::unpack(rx[j][it], xf);
+              IO::unpack(rd[j][it], df);
+#pragma unroll
+              for (int e = 0; e < V; ++e) {
+                const float xh = (xf[e] - mu) * rs;
+                const float gd = g[it][e] * df[e];
+                o[e] = rs * ((gd - c1) - xh * c2);
+              }
             }
             const Raw out = IO::pack(o);
             if (col + V <= N) IO::store(dxr + col, out);

@@ -10,18 +10,59 @@ using namespace rmsn;
 
 namespace {
 
+constexpr int kLnFwdMaxIters = 4;  // x, w and b of a row stay in registers through two reductions
 constexpr int kLnBwdBlockThreads = 1024;
 constexpr int kLnBwdRegMaxIters = 2;
-// Rows in flight ahead of the current one, per vectors-per-thread of the register backward.
+// Rows in flight ahead of the current one, and whether xhat and w * dy are kept between the
+// passes, per vectors-per-thread of the register backward.
 template <int ITERS> struct LnBwdPipe;
-template <> struct LnBwdPipe<1> { static constexpr int DEPTH = 3; };
-template <> struct LnBwdPipe<2> { static constexpr int DEPTH = 1; };
+template <> struct LnBwdPipe<1> {
+  static constexpr int DEPTH = 1;
+  static constexpr bool KEEP = true;
+};
+template <> struct LnBwdPipe<2> {
+  static constexpr int DEPTH = 1;
+  static constexpr bool KEEP = false;
+};
 
 size_t ln_workspace_bytes(int64_t M, int64_t N) {
   return 2 * (size_t)num_partials(M) * (size_t)partial_ld(N) * sizeof(float);
 }
 
 // ---- LayerNorm forward ----------------------------------------------------------------------------
+// A wavefront per row up to 4 vectors a thread; wider rows get more wavefronts (x, w and b stay in
+// registers through the two reductions). Both families use the same threads per row for 16-byte
+// rows, so they sum in the same order.
+void ln_fwd_shape(int64_t nv, int* tpr, int* iters) {
+  *tpr = (int)clamp64(pow2_ceil(ceil_div(nv, kLnFwdMaxIters)), 64, 1024);
+  *iters = (int)ceil_div(nv, *tpr);
+}
+
+rmsnorm_status plan_ln_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
+                           rmsnorm_variant req, Plan* p) {
+  const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
+  int tpr, iters;
+  ln_fwd_shape(nv_wide, &tpr, &iters);
+  const bool reg_ok = wide_ok && iters <= kLnFwdMaxIters;
+  rmsnorm_variant v = req;
+  if (v == RMSNORM_VARIANT_AUTO) v = reg_ok ? RMSNORM_VARIANT_REGISTERS : RMSNORM_VARIANT_STREAMING;
+  if (v == RMSNORM_VARIANT_LDS || (v == RMSNORM_VARIANT_REGISTERS && !reg_ok))
+    return RMSNORM_ERR_UNSUPPORTED;
+  p->variant = v;
+  p->wide = v == RMSNORM_VARIANT_REGISTERS || wide_ok;
+  if (v == RMSNORM_VARIANT_STREAMING) {
+    ln_fwd_shape(wide_ok ? nv_wide : N, &tpr, &iters);
+    iters = 0;
+  }
+  p->tpr = tpr;
+  p->iters = iters;
+  p->groups = tpr >= kFwdBlockThreads ? 1 : kFwdBlockThreads / tpr;
+  p->lds = round16(sizeof(float) * 2 * (size_t)p->groups * (tpr / 64));
+  p->grid = ceil_div(M, p->groups);
+  if (p->grid > INT32_MAX) return RMSNORM_ERR_UNSUPPORTED;
+  return RMSNORM_OK;
+}
+
 template <DT D, bool HAS_B>
 rmsnorm_status ln_fwd_dispatch(const Plan& p, const LnFwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
@@ -34,10 +75,6 @@ rmsnorm_status ln_fwd_dispatch(const Plan& p, const LnFwdArgs& a, hipStream_t s)
     case 2: return launch(ln_fwd_rows_kernel<D, 2, HAS_B>, p.grid, block, p.lds, s, a);
     case 3: return launch(ln_fwd_rows_kernel<D, 3, HAS_B>, p.grid, block, p.lds, s, a);
     case 4: return launch(ln_fwd_rows_kernel<D, 4, HAS_B>, p.grid, block, p.lds, s, a);
-    case 5: return launch(ln_fwd_rows_kernel<D, 5, HAS_B>, p.grid, block, p.lds, s, a);
-    case 6: return launch(ln_fwd_rows_kernel<D, 6, HAS_B>, p.grid, block, p.lds, s, a);
-    case 7: return launch(ln_fwd_rows_kernel<D, 7, HAS_B>, p.grid, block, p.lds, s, a);
-    case 8: return launch(ln_fwd_rows_kernel<D, 8, HAS_B>, p.grid, block, p.lds, s, a);
     default: return RMSNORM_ERR_UNSUPPORTED;
   }
 }
@@ -69,8 +106,7 @@ rmsnorm_status ln_fwd_impl(const void* x, int64_t ldx, const void* w, const void
     return RMSNORM_ERR_MISALIGNED;
   const bool wide = wide_fits(x, ldx, eb) && aligned(w, 16) && aligned(b, 16);
   Plan p;
-  if ((st = plan_fwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
-  p.lds = round16(sizeof(float) * 2 * (size_t)p.groups * (p.tpr / 64));
+  if ((st = plan_ln_fwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
   if (M == 0) return RMSNORM_OK;
 
   LnFwdArgs a;
@@ -124,11 +160,11 @@ rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s)
   }
   switch (p.iters) {
     case 1:
-      return launch(ln_bwd_rows_kernel<D, 1, LnBwdPipe<1>::DEPTH, HAS_DB>, p.grid, block, p.lds,
-                    s, a);
+      return launch(ln_bwd_rows_kernel<D, 1, LnBwdPipe<1>::DEPTH, HAS_DB, LnBwdPipe<1>::KEEP>,
+                    p.grid, block, p.lds, s, a);
     case 2:
-      return launch(ln_bwd_rows_kernel<D, 2, LnBwdPipe<2>::DEPTH, HAS_DB>, p.grid, block, p.lds,
-                    s, a);
+      return launch(ln_bwd_rows_kernel<D, 2, LnBwdPipe<2>::DEPTH, HAS_DB, LnBwdPipe<2>::KEEP>,
+                    p.grid, block, p.lds, s, a);
     default:
       return RMSNORM_ERR_UNSUPPORTED;
   }
@@ -145,15 +181,20 @@ rmsnorm_status ln_bwd_by_dtype(rmsnorm_dtype dtype, const Plan& p, const LnBwdAr
   return RMSNORM_ERR_INVALID_ARG;
 }
 
-// Fixed-order column sums of P partial rows (stride ldp) into out[N]; zeros when there are none.
-rmsnorm_status reduce_partials(const float* part, int64_t P, int64_t N, float* out,
+// Fixed-order column sums of P partial rows (stride ldp) into out[N], and of the next P rows into
+// out2[N] when out2 is not null, in one launch; zeros when there are no rows.
+rmsnorm_status reduce_partials(const float* part, int64_t P, int64_t N, float* out, float* out2,
                                hipStream_t s) {
   if (P == 0) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s, out,
                        (int)N);
+    if (out2)
+      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s,
+                         out2, (int)N);
   } else {
-    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)ceil_div(N, 16)), dim3(256), 0, s, part,
-                       partial_ld(N), (int)P, (int)N, out);
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)ceil_div(N, 16), out2 ? 2u : 1u),
+                       dim3(256), 0, s, part, partial_ld(N), (int)P, (int)N, out, out2,
+                       P * partial_ld(N));
   }
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
 }
@@ -193,9 +234,7 @@ rmsnorm_status ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t 
     st = db ? ln_bwd_by_dtype<true>(dtype, p, a, s) : ln_bwd_by_dtype<false>(dtype, p, a, s);
     if (st != RMSNORM_OK) return st;
   }
-  if ((st = reduce_partials(part, P, N, dw, s)) != RMSNORM_OK) return st;
-  if (db) st = reduce_partials(part + P * partial_ld(N), P, N, db, s);
-  return st;
+  return reduce_partials(part, P, N, dw, db, s);
 }
 
 // ---- GroupNorm -----------------------------------------------------------------------------------

@@ -1,0 +1,204 @@
+// Softmax (include/libsoftmax.h) and float64 RMSNorm (the _f64 entry points of
+// include/librmsnorm.h): argument validation, kernel selection and launches. Every argument check
+// runs before the first HIP call; nothing is allocated.
+#include "../../include/libsoftmax.h"
+#include "host_common.hpp"
+#include "rmsnorm_bwd.hpp"
+#include "softmax.hpp"
+
+using namespace rmsn;
+
+namespace {
+
+constexpr int kSmMaxIters = 4;  // 16-byte vectors per thread in the register kernels
+
+bool sm_dtype_ok(int d) { return dtype_ok(d) || d == RMSNORM_DTYPE_F64; }
+
+// Threads per row for a row of nv vectors (or elements): at most kSmMaxIters per thread.
+void sm_shape(int64_t nv, int* tpr, int* iters) {
+  *tpr = (int)clamp64(pow2_ceil(ceil_div(nv, kSmMaxIters)), 64, 1024);
+  *iters = (int)ceil_div(nv, *tpr);
+}
+
+rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
+                       rmsnorm_variant req, size_t acc_bytes, int slots, Plan* p) {
+  const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
+  int tpr, iters;
+  sm_shape(nv_wide, &tpr, &iters);
+  const bool reg_ok = wide_ok && iters <= kSmMaxIters;
+  rmsnorm_variant v = req;
+  if (v == RMSNORM_VARIANT_AUTO) v = reg_ok ? RMSNORM_VARIANT_REGISTERS : RMSNORM_VARIANT_STREAMING;
+  if (v == RMSNORM_VARIANT_LDS || (v == RMSNORM_VARIANT_REGISTERS && !reg_ok))
+    return RMSNORM_ERR_UNSUPPORTED;
+  p->variant = v;
+  p->wide = v == RMSNORM_VARIANT_REGISTERS || wide_ok;
+  if (v == RMSNORM_VARIANT_STREAMING) {
+    sm_shape(wide_ok ? nv_wide : N, &tpr, &iters);
+    iters = 0;
+  }
+  p->tpr = tpr;
+  p->iters = iters;
+  p->groups = tpr >= kFwdBlockThreads ? 1 : kFwdBlockThreads / tpr;
+  p->lds = round16(acc_bytes * slots * (size_t)p->groups * (tpr / 64));
+  p->grid = ceil_div(M, p->groups);
+  if (p->grid > INT32_MAX) return RMSNORM_ERR_UNSUPPORTED;
+  return RMSNORM_OK;
+}
+
+template <DT D, bool FWD>
+rmsnorm_status sm_dispatch(const Plan& p, const SmArgs& a, hipStream_t s) {
+  const int block = p.groups * p.tpr;
+#define RMSN_SM(W, IT)                                                                          \
+  (FWD ? launch(softmax_fwd_kernel<D, W, IT>, p.grid, block, p.lds, s, a)                       \
+       : launch(softmax_bwd_kernel<D, W, IT>, p.grid, block, p.lds, s, a))
+  if (p.variant == RMSNORM_VARIANT_STREAMING) return p.wide ? RMSN_SM(true, 0) : RMSN_SM(false, 0);
+  switch (p.iters) {
+    case 1: return RMSN_SM(true, 1);
+    case 2: return RMSN_SM(true, 2);
+    case 3: return RMSN_SM(true, 3);
+    case 4: return RMSN_SM(true, 4);
+    default: return RMSNORM_ERR_UNSUPPORTED;
+  }
+#undef RMSN_SM
+}
+
+template <bool FWD>
+rmsnorm_status sm_impl(const void* a_in, int64_t lda, const void* dy, int64_t lddy, void* out,
+                       int64_t ldo, int64_t M, int64_t N, rmsnorm_dtype dtype,
+                       rmsnorm_variant variant, void* stream) {
+  if (!sm_dtype_ok(dtype) || !variant_ok(variant)) return RMSNORM_ERR_INVALID_ARG;
+  if (M < 0 || N < 1) return RMSNORM_ERR_INVALID_ARG;
+  if (N > RMSNORM_MAX_N) return RMSNORM_ERR_UNSUPPORTED;
+  const int eb = elem_bytes(dtype);
+  rmsnorm_status st;
+  if ((st = check_matrix(a_in, lda, M, N, eb)) != RMSNORM_OK) return st;
+  if (!FWD && (st = check_matrix(dy, lddy, M, N, eb)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(out, ldo, M, N, eb)) != RMSNORM_OK) return st;
+  const bool wide = wide_fits(a_in, lda, eb) && wide_fits(out, ldo, eb) &&
+                    (FWD || wide_fits(dy, lddy, eb));
+  const size_t acc = dtype == RMSNORM_DTYPE_F64 ? 8 : 4;
+  Plan p;
+  if ((st = plan_sm(M, N, dtype, wide, variant, acc, FWD ? 3 : 1, &p)) != RMSNORM_OK) return st;
+  if (M == 0) return RMSNORM_OK;
+  SmArgs a;
+  a.x = a_in; a.dy = dy; a.out = out;
+  a.ldx = lda; a.lddy = lddy; a.ldo = ldo; a.M = M; a.N = (int)N;
+  a.tpr = p.tpr; a.groups = p.groups;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case RMSNORM_DTYPE_F32: return sm_dispatch<DT::F32, FWD>(p, a, s);
+    case RMSNORM_DTYPE_F16: return sm_dispatch<DT::F16, FWD>(p, a, s);
+    case RMSNORM_DTYPE_BF16: return sm_dispatch<DT::BF16, FWD>(p, a, s);
+    case RMSNORM_DTYPE_F64: return sm_dispatch<DT::F64, FWD>(p, a, s);
+  }
+  return RMSNORM_ERR_INVALID_ARG;
+}
+
+// ---- float64 RMSNorm ------------------------------------------------------------------------------
+size_t f64_workspace_bytes(int64_t M, int64_t N) {
+  return (size_t)num_partials(M) * (size_t)N * sizeof(double);
+}
+
+rmsnorm_status f64_fwd_impl(const double* x, int64_t ldx, const double* w, double* y, int64_t ldy,
+                            double* rstd, int64_t M, int64_t N, double eps, double offset,
+                            void* stream) {
+  if (M < 0 || N < 1 || !std::isfinite(eps) || eps < 0.0 || !std::isfinite(offset))
+    return RMSNORM_ERR_INVALID_ARG;
+  if (N > RMSNORM_MAX_N) return RMSNORM_ERR_UNSUPPORTED;
+  rmsnorm_status st;
+  if ((st = check_matrix(x, ldx, M, N, 8)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(y, ldy, M, N, 8)) != RMSNORM_OK) return st;
+  if (M > 0 && w == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(w, 8) || !aligned(rstd, 8)) return RMSNORM_ERR_MISALIGNED;
+  const bool wide = wide_fits(x, ldx, 8) && wide_fits(y, ldy, 8) && aligned(w, 16);
+  int tpr, iters;
+  sm_shape(wide ? ceil_div(N, 2) : N, &tpr, &iters);
+  const int groups = tpr >= kFwdBlockThreads ? 1 : kFwdBlockThreads / tpr;
+  const int64_t grid = ceil_div(M, groups);
+  if (grid > INT32_MAX) return RMSNORM_ERR_UNSUPPORTED;
+  if (M == 0) return RMSNORM_OK;
+  F64Args a = {};
+  a.x = x; a.w = w; a.out = y; a.rstd = rstd;
+  a.ldx = ldx; a.ldo = ldy; a.M = M; a.N = (int)N; a.tpr = tpr; a.groups = groups;
+  a.eps = eps; a.offset = offset;
+  const size_t lds = round16(sizeof(double) * (size_t)groups * (tpr / 64));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return wide ? launch(rms_f64_fwd_kernel<true>, grid, groups * tpr, lds, s, a)
+              : launch(rms_f64_fwd_kernel<false>, grid, groups * tpr, lds, s, a);
+}
+
+rmsnorm_status f64_bwd_impl(const double* dy, int64_t lddy, const double* x, int64_t ldx,
+                            const double* w, const double* rstd, double* dx, int64_t lddx,
+                            double* dw, void* workspace, size_t wsb, int64_t M, int64_t N,
+                            double offset, void* stream) {
+  if (M < 0 || N < 1 || !std::isfinite(offset)) return RMSNORM_ERR_INVALID_ARG;
+  if (N > RMSNORM_MAX_N) return RMSNORM_ERR_UNSUPPORTED;
+  rmsnorm_status st;
+  if ((st = check_matrix(dy, lddy, M, N, 8)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(x, ldx, M, N, 8)) != RMSNORM_OK) return st;
+  if ((st = check_matrix(dx, lddx, M, N, 8)) != RMSNORM_OK) return st;
+  if (dw == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (M > 0 && (w == nullptr || rstd == nullptr || workspace == nullptr))
+    return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(w, 8) || !aligned(rstd, 8) || !aligned(dw, 8) || !aligned(workspace, 16))
+    return RMSNORM_ERR_MISALIGNED;
+  if (wsb < f64_workspace_bytes(M, N)) return RMSNORM_ERR_WORKSPACE;
+  const bool wide = wide_fits(dy, lddy, 8) && wide_fits(x, ldx, 8) && wide_fits(dx, lddx, 8) &&
+                    aligned(w, 16);
+  F64Args a = {};
+  a.x = x; a.dy = dy; a.w = w; a.rstd = const_cast<double*>(rstd); a.out = dx;
+  a.part = static_cast<double*>(workspace); a.dw = dw;
+  a.ldx = ldx; a.lddy = lddy; a.ldo = lddx; a.M = M; a.N = (int)N;
+  a.P = (int)num_partials(M); a.offset = offset;
+  int iters;
+  bwd_shape(wide ? ceil_div(N, 2) : N, &a.tpr, &iters);
+  a.groups = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M > 0) {
+    const size_t lds = round16(sizeof(double) * 2 * (a.tpr / 64));
+    st = wide ? launch(rms_f64_bwd_kernel<true>, a.P, a.tpr, lds, s, a)
+              : launch(rms_f64_bwd_kernel<false>, a.P, a.tpr, lds, s, a);
+    if (st != RMSNORM_OK) return st;
+  }
+  hipLaunchKernelGGL(rms_f64_dw_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+}
+
+}  // namespace
+
+// ---- exported C interface -------------------------------------------------------------------------
+extern "C" {
+
+__attribute__((visibility("default"))) rmsnorm_status softmax_fwd(
+    const void* x, int64_t ldx, void* y, int64_t ldy, int64_t M, int64_t N, rmsnorm_dtype dtype,
+    rmsnorm_variant variant, void* stream) {
+  return sm_impl<true>(x, ldx, nullptr, 0, y, ldy, M, N, dtype, variant, stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status softmax_bwd(
+    const void* dy, int64_t lddy, const void* y, int64_t ldy, void* dx, int64_t lddx, int64_t M,
+    int64_t N, rmsnorm_dtype dtype, rmsnorm_variant variant, void* stream) {
+  return sm_impl<false>(y, ldy, dy, lddy, dx, lddx, M, N, dtype, variant, stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_fwd_f64(
+    const double* x, int64_t ldx, const double* w, double* y, int64_t ldy, double* rstd,
+    int64_t M, int64_t N, double eps, double offset, void* stream) {
+  return f64_fwd_impl(x, ldx, w, y, ldy, rstd, M, N, eps, offset, stream);
+}
+
+__attribute__((visibility("default"))) size_t rmsnorm_bwd_f64_workspace_bytes(int64_t M,
+                                                                              int64_t N) {
+  if (M <= 0 || N < 1 || N > RMSNORM_MAX_N) return 0;
+  return f64_workspace_bytes(M, N);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_f64(
+    const double* dy, int64_t lddy, const double* x, int64_t ldx, const double* w,
+    const double* rstd, double* dx, int64_t lddx, double* dw, void* workspace,
+    size_t workspace_bytes, int64_t M, int64_t N, double offset, void* stream) {
+  return f64_bwd_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, workspace, workspace_bytes, M, N,
+                      offset, stream);
+}
+
+}  // extern "C"

@@ -460,10 +460,16 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
 // 4 wavefronts owns 16 columns. Lane l of wave k reads column l % 16 of partial rows
 // p = 16 * i + 4 * k + l / 16 (i = 0 .. kMaxPartials / 16 - 1, all loads in flight together) and
 // adds them in order of i; the four lanes of a column (l / 16 = 0..3) are then added in order, and
-// finally the four waves in order.
+// finally the four waves in order. blockIdx.y selects one of gridDim.y sets of partial rows,
+// set_stride floats apart, and its output (dw, or dw2 for the second set).
 static_assert(kMaxPartials % 16 == 0, "dw_reduce_kernel reads partial rows in groups of 16");
 inline __global__ void __launch_bounds__(256) dw_reduce_kernel(const float* part, int64_t ldp, int P,
-                                                        int N, float* dw) {
+                                                               int N, float* dw, float* dw2,
+                                                               int64_t set_stride) {
+  if (blockIdx.y) {
+    part += set_stride;
+    dw = dw2;
+  }
   constexpr int L = kMaxPartials / 16;
   __shared__ float buf[4][16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;

@@ -11,7 +11,7 @@
 
 namespace rmsn {
 
-enum class DT : int { F32 = 0, F16 = 1, BF16 = 2 };
+enum class DT : int { F32 = 0, F16 = 1, BF16 = 2, F64 = 3 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -21,6 +21,7 @@ template <DT D> struct Elem;
 template <> struct Elem<DT::F32> { using S = float; static constexpr int VEC = 4; };
 template <> struct Elem<DT::F16> { using S = uint16_t; static constexpr int VEC = 8; };
 template <> struct Elem<DT::BF16> { using S = uint16_t; static constexpr int VEC = 8; };
+template <> struct Elem<DT::F64> { using S = double; static constexpr int VEC = 2; };
 
 // The narrowing conversions below take their float32 operand through `materialize`: an empty asm
 // with a register constraint (no instruction is emitted). It stops the backend from folding a

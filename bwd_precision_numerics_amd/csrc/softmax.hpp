@@ -1,0 +1,438 @@
+// Softmax over the last dimension (forward and backward) and the float64 RMSNorm.
+//
+// Candle pull request 4059, "Add backward passes to the fused rms_norm, layer_norm and
+// softmax_last_dim ops": the softmax forward computes in float32 for the 16-bit types and rounds
+// once at the store; the backward is dx = y * (dy - sum(dy * y)) with the sum in float32 for the
+// 16-bit types and float64 for float64; float64 kernels accumulate in float64 (a float accumulator
+// made the float64 forward's statistics differ from the backward's).
+//
+//   forward   m = max_j x_j,  e_j = exp(x_j - m),  y_j = T(e_j / sum_k e_k)
+//   backward  s = sum_j dy_j * y_j,  dx_j = T(y_j * (dy_j - s))
+//
+// A is the compute type: float for float32 / float16 / bfloat16 I/O, double for float64.
+#pragma once
+
+#include "rmsnorm_common.hpp"
+
+namespace rmsn {
+
+template <DT D> struct Acc { using A = float; };
+template <> struct Acc<DT::F64> { using A = double; };
+
+// 16-byte vector or single-element I/O in the compute type.
+template <DT D, bool WIDE> struct NumIO {
+  using IO = VecIO<D, WIDE>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  static constexpr int V = IO::V;
+  static __device__ __forceinline__ Raw load(const S* p, int n) {
+    return n >= V ? IO::load(p) : IO::load_part(p, n);
+  }
+  static __device__ __forceinline__ void unpack(const Raw& r, float (&f)[V]) { IO::unpack(r, f); }
+  static __device__ __forceinline__ void store(S* p, const float (&f)[V], int n) {
+    const Raw r = IO::pack(f);
+    if (n >= V) IO::store(p, r);
+    else IO::store_part(p, r, n);
+  }
+};
+template <> struct NumIO<DT::F64, true> {
+  using S = double;
+  using Raw = uint4;
+  static constexpr int V = 2;
+  static __device__ __forceinline__ Raw load(const S* p, int n) {
+    if (n >= 2) return *reinterpret_cast<const uint4*>(p);
+    const double t[2] = {n > 0 ? p[0] : 0.0, 0.0};
+    return __builtin_bit_cast(uint4, t);
+  }
+  static __device__ __forceinline__ void unpack(const Raw& r, double (&f)[2]) {
+    f[0] = __builtin_bit_cast(double, make_uint2(r.x, r.y));
+    f[1] = __builtin_bit_cast(double, make_uint2(r.z, r.w));
+  }
+  static __device__ __forceinline__ void store(S* p, const double (&f)[2], int n) {
+    if (n >= 2) {
+      typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+      const uint2 a = __builtin_bit_cast(uint2, f[0]), b = __builtin_bit_cast(uint2, f[1]);
+      const u32x4_t v = {a.x, a.y, b.x, b.y};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+    } else if (n > 0) {
+      p[0] = f[0];
+    }
+  }
+};
+template <> struct NumIO<DT::F64, false> {
+  using S = double;
+  using Raw = double;
+  static constexpr int V = 1;
+  static __device__ __forceinline__ Raw load(const S* p, int) { return *p; }
+  static __device__ __forceinline__ void unpack(const Raw& r, double (&f)[1]) { f[0] = r; }
+  static __device__ __forceinline__ void store(S* p, const double (&f)[1], int) { *p = f[0]; }
+};
+
+// Wave reductions by xor butterfly: at every step each lane combines the same two operands as its
+// partner (a + b == b + a in IEEE arithmetic), so all lanes end with the same bits; the order of
+// additions is fixed.
+template <typename A> __device__ __forceinline__ A shfl_xor_any(A v, int m) {
+  if constexpr (sizeof(A) == 8) {
+    const int2 i = __builtin_bit_cast(int2, v);
+    return __builtin_bit_cast(A, make_int2(__shfl_xor(i.x, m, 64), __shfl_xor(i.y, m, 64)));
+  } else {
+    return __shfl_xor(v, m, 64);
+  }
+}
+template <typename A> __device__ __forceinline__ A wave_sum_x(A v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += shfl_xor_any(v, m);
+  return v;
+}
+template <typename A> __device__ __forceinline__ A wave_max_x(A v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmax(v, shfl_xor_any(v, m));
+  return v;
+}
+
+// Sum (MAX = false) or maximum over the TPR = 64 * wpr threads of a row group: waves publish their
+// results in red[wave] and every thread combines them in wave order. Every thread of the block
+// must call it when wpr > 1.
+template <bool MAX, typename A>
+__device__ __forceinline__ A group_reduce(A v, A* red, int wpr, int tl) {
+  v = MAX ? wave_max_x(v) : wave_sum_x(v);
+  if (wpr > 1) {
+    if ((tl & 63) == 0) red[tl >> 6] = v;
+    lds_barrier();
+    v = red[0];
+    for (int k = 1; k < wpr; ++k) v = MAX ? fmax(v, red[k]) : v + red[k];
+  }
+  return v;
+}
+
+// exp in the compute type (the accurate device library functions).
+__device__ __forceinline__ float exp_a(float v) { return expf(v); }
+__device__ __forceinline__ double exp_a(double v) { return exp(v); }
+
+struct SmArgs {
+  const void* x;   // forward input, or the forward's output y (backward)
+  const void* dy;  // backward only
+  void* out;       // y (forward) or dx (backward)
+  int64_t ldx, lddy, ldo, M;
+  int N;
+  int tpr, groups;
+};
+
+// Forward. Register kernel (ITERS > 0: the row's exp values stay in registers between the
+// reductions and the store) or streaming (ITERS = 0: each pass reads x again from the caches).
+// LDS: three reduction slots of wpr compute-type values per row group.
+template <DT D, bool WIDE, int ITERS>
+__global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
+  using A = typename Acc<D>::A;
+  using IO = NumIO<D, WIDE>;
+  using S = typename IO::S;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int nv = (N + V - 1) / V;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+  A* red = reinterpret_cast<A*>(smem) + grp * 3 * wpr;
+  const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+  constexpr int R = ITERS > 0 ? ITERS : 1;
+  A ev[R][V];
+
+  A mx = -INFINITY;
+  if constexpr (ITERS > 0) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      A f[V];
+      if (valid && col < N) {
+        IO::unpack(IO::load(xr + col, N - col), f);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        ev[it][e] = (valid && col + e < N) ? f[e] : (A)-INFINITY;
+        mx = fmax(mx, ev[it][e]);
+      }
+    }
+  } else if (valid) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      A f[V];
+      IO::unpack(IO::load(xr + col, N - col), f);
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (col + e < N) mx = fmax(mx, f[e]);
+    }
+  }
+  mx = group_reduce<true>(mx, red, wpr, tl);
+
+  A s0 = 0, s1 = 0;
+  if constexpr (ITERS > 0) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const A t = exp_a(ev[it][e] - mx);  // padding: exp(-inf) = 0
+        ev[it][e] = t;
+        if (e & 1) s1 += t;
+        else s0 += t;
+      }
+    }
+  } else if (valid) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      A f[V];
+      IO::unpack(IO::load(xr + col, N - col), f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (col + e < N) {
+          const A t = exp_a(f[e] - mx);
+          if (e & 1) s1 += t;
+          else s0 += t;
+        }
+      }
+    }
+  }
+  const A sum = group_reduce<false>(s0 + s1, red + wpr, wpr, tl);
+  if (!valid) return;
+  S* yr = static_cast<S*>(a.out) + row * a.ldo;
+  if constexpr (ITERS > 0) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      if (col >= N) continue;
+      A o[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] = ev[it][e] / sum;
+      IO::store(yr + col, o, N - col);
+    }
+  } else {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      A f[V], o[V];
+      IO::unpack(IO::load(xr + col, N - col), f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] = exp_a(f[e] - mx) / sum;
+      IO::store(yr + col, o, N - col);
+    }
+  }
+}
+
+// Backward: s = sum(dy * y) over the row, dx = T(y * (dy - s)). Register kernel (ITERS > 0: y and
+// dy stay in registers) or streaming (ITERS = 0: read again for the elementwise pass).
+template <DT D, bool WIDE, int ITERS>
+__global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
+  using A = typename Acc<D>::A;
+  using IO = NumIO<D, WIDE>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int nv = (N + V - 1) / V;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+  A* red = reinterpret_cast<A*>(smem) + grp * wpr;
+  const S* yr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+  const S* dr = static_cast<const S*>(a.dy) + (valid ? row : 0) * a.lddy;
+  constexpr int R = ITERS > 0 ? ITERS : 1;
+  Raw ry[R], rd[R];
+
+  A s0 = 0, s1 = 0;
+  if constexpr (ITERS > 0) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      if (valid && col < N) {
+        ry[it] = IO::load(yr + col, N - col);
+        rd[it] = IO::load(dr + col, N - col);
+      } else {
+        ry[it] = IO::load(yr, 0);
+        rd[it] = IO::load(dr, 0);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      if (!(valid && col < N)) continue;
+      A yf[V], df[V];
+      IO::unpack(ry[it], yf);
+      IO::unpack(rd[it], df);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (e & 1) s1 = fma(df[e], yf[e], s1);
+        else s0 = fma(df[e], yf[e], s0);
+      }
+    }
+  } else if (valid) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      A yf[V], df[V];
+      IO::unpack(IO::load(yr + col, N - col), yf);
+      IO::unpack(IO::load(dr + col, N - col), df);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (e & 1) s1 = fma(df[e], yf[e], s1);
+        else s0 = fma(df[e], yf[e], s0);
+      }
+    }
+  }
+  const A s = group_reduce<false>(s0 + s1, red, wpr, tl);
+  if (!valid) return;
+  S* xr = static_cast<S*>(a.out) + row * a.ldo;
+  if constexpr (ITERS > 0) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      if (col >= N) continue;
+      A yf[V], df[V], o[V];
+      IO::unpack(ry[it], yf);
+      IO::unpack(rd[it], df);
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] = yf[e] * (df[e] - s);
+      IO::store(xr + col, o, N - col);
+    }
+  } else {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      A yf[V], df[V], o[V];
+      IO::unpack(IO::load(yr + col, N - col), yf);
+      IO::unpack(IO::load(dr + col, N - col), df);
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] = yf[e] * (df[e] - s);
+      IO::store(xr + col, o, N - col);
+    }
+  }
+}
+
+// ---- float64 RMSNorm ------------------------------------------------------------------------------
+// rstd = 1 / sqrt(sum(x^2) / N + eps), y = (x * rstd) * (offset + w); backward
+// c = sum((offset + w) * dy * xhat) / N, dx = rstd * ((offset + w) * dy - xhat * c),
+// dw = sum over rows of dy * xhat; all in float64. Two passes over each row (the second reads it
+// again from the caches); the backward runs on the persistent grid of the 16-bit backward, its
+// float64 partial rows of dw accumulated in the workspace and then summed in a fixed order.
+struct F64Args {
+  const double* x;
+  const double* dy;
+  const double* w;
+  double* rstd;  // forward: written (may be null); backward: read
+  double* out;   // y or dx
+  double* part;  // [P, N] backward partials
+  double* dw;
+  int64_t ldx, lddy, ldo, M;
+  int N, P, tpr, groups;
+  double eps, offset;
+};
+
+template <bool WIDE>
+__global__ void __launch_bounds__(1024) rms_f64_fwd_kernel(F64Args a) {
+  using IO = NumIO<DT::F64, WIDE>;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int nv = (N + V - 1) / V;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+  double* red = reinterpret_cast<double*>(smem) + grp * wpr;
+  const double* xr = a.x + (valid ? row : 0) * a.ldx;
+  double q0 = 0, q1 = 0;
+  if (valid) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      double f[V];
+      IO::unpack(IO::load(xr + col, N - col), f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (e & 1) q1 = fma(f[e], f[e], q1);
+        else q0 = fma(f[e], f[e], q0);
+      }
+    }
+  }
+  const double ss = group_reduce<false>(q0 + q1, red, wpr, tl);
+  const double rs = 1.0 / sqrt(ss / (double)N + a.eps);
+  if (!valid) return;
+  if (tl == 0 && a.rstd) a.rstd[row] = rs;
+  double* yr = a.out + row * a.ldo;
+  for (int v = tl; v < nv; v += TPR) {
+    const int col = v * V;
+    double f[V], wf[V], o[V];
+    IO::unpack(IO::load(xr + col, N - col), f);
+    IO::unpack(IO::load(a.w + col, N - col), wf);
+#pragma unroll
+    for (int e = 0; e < V; ++e) o[e] = (f[e] * rs) * (a.offset + wf[e]);
+    IO::store(yr + col, o, N - col);
+  }
+}
+
+template <bool WIDE>
+__global__ void __launch_bounds__(1024) rms_f64_bwd_kernel(F64Args a) {
+  using IO = NumIO<DT::F64, WIDE>;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int nv = (N + V - 1) / V;
+  const int tl = threadIdx.x;
+  const int b = blockIdx.x, P = a.P;
+  double* red = reinterpret_cast<double*>(smem);  // [2][wpr]
+  double* pr = a.part + (int64_t)b * N;
+  // zeroed by the thread that owns each column below (same mapping, program order)
+  for (int v = tl; v < nv; v += TPR) {
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+      if (v * V + e < N) pr[v * V + e] = 0.0;
+  }
+  int s = 0;
+  for (int64_t row = b; row < a.M; row += P, ++s) {
+    const double* xr = a.x + row * a.ldx;
+    const double* dr = a.dy + row * a.lddy;
+    const double rs = a.rstd[row];
+    double d0 = 0, d1 = 0;
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      double f[V], df[V], wf[V];
+      IO::unpack(IO::load(xr + col, N - col), f);
+      IO::unpack(IO::load(dr + col, N - col), df);
+      IO::unpack(IO::load(a.w + col, N - col), wf);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const double xh = f[e] * rs, gd = (a.offset + wf[e]) * df[e];
+        if (e & 1) d1 = fma(gd, xh, d1);
+        else d0 = fma(gd, xh, d0);
+      }
+    }
+    const double c = group_reduce<false>(d0 + d1, red + (s & 1) * wpr, wpr, tl) / (double)N;
+    double* xo = a.out + row * a.ldo;
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+      double f[V], df[V], wf[V], o[V];
+      IO::unpack(IO::load(xr + col, N - col), f);
+      IO::unpack(IO::load(dr + col, N - col), df);
+      IO::unpack(IO::load(a.w + col, N - col), wf);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const double xh = f[e] * rs, gd = (a.offset + wf[e]) * df[e];
+        o[e] = rs * (gd - xh * c);
+        if (col + e < N) pr[col + e] = fma(df[e], xh, pr[col + e]);
+      }
+      IO::store(xo + col, o, N - col);
+    }
+  }
+}
+
+// dw_j = sum over p of part[p, j], p in order; one thread per column.
+__global__ void __launch_bounds__(256) rms_f64_dw_kernel(F64Args a) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= a.N) return;
+  double s = 0.0;
+  for (int p = 0; p < a.P; ++p) s += a.part[(int64_t)p * a.N + j];
+  a.dw[j] = s;
+}
+
+}  // namespace rmsn

@@ -65,14 +65,16 @@
 extern "C" {
 #endif
 
-#define LIBRMSNORM_ABI_VERSION 3
+#define LIBRMSNORM_ABI_VERSION 4
 /* Largest supported row width N. */
 #define RMSNORM_MAX_N (1 << 24)
 
 typedef enum rmsnorm_dtype {
   RMSNORM_DTYPE_F32 = 0,
   RMSNORM_DTYPE_F16 = 1,  /* IEEE binary16 */
-  RMSNORM_DTYPE_BF16 = 2  /* bfloat16 */
+  RMSNORM_DTYPE_BF16 = 2, /* bfloat16 */
+  RMSNORM_DTYPE_F64 = 3   /* IEEE binary64: softmax_* only (the float64 RMSNorm has its own
+                             entry points below); elsewhere RMSNORM_ERR_INVALID_ARG */
 } rmsnorm_dtype;
 
 typedef enum rmsnorm_rounding {
@@ -202,6 +204,33 @@ rmsnorm_status rmsnorm_bwd_rows(const void* dy, int64_t lddy, const void* x, int
                                 rmsnorm_variant variant, void* stream);
 rmsnorm_status rmsnorm_bwd_dw_reduce(const void* workspace, size_t workspace_bytes, float* dw,
                                      int64_t M, int64_t N, rmsnorm_dtype dtype, void* stream);
+
+/* ---- float64 -------------------------------------------------------------------------------------
+ * RMSNorm with float64 I/O and float64 arithmetic throughout, statistics included (candle pull
+ * request 4059: float64 norm kernels take a float64 accumulator, so the forward's statistics equal
+ * the ones the backward works with):
+ *
+ *     rstd = 1 / sqrt(sum_j x_j^2 / N + eps),   y = (x * rstd) * (offset + w)
+ *     c = sum_j (offset + w_j) dy_j xhat_j / N,  dx = rstd * ((offset + w) * dy - xhat * c)
+ *     dw_j = sum_r dy_rj * xhat_rj
+ *
+ * Same layout, ownership and error conventions as above; rstd is double [M], dw double [N], eps
+ * and offset are doubles. dw is summed without atomics in a fixed order (float64 partial rows in
+ * the workspace, then a fixed-order column sum). Rounding conventions do not apply (T = float64).
+ * The 16-byte path needs 16-byte aligned bases and row strides; otherwise element-wise. */
+rmsnorm_status rmsnorm_fwd_f64(const double* x, int64_t ldx, const double* w, double* y,
+                               int64_t ldy, double* rstd, int64_t M, int64_t N, double eps,
+                               double offset, void* stream);
+
+/* Bytes of workspace rmsnorm_bwd_f64 needs (float64 partial rows); 0 for M = 0 or bad sizes. */
+size_t rmsnorm_bwd_f64_workspace_bytes(int64_t M, int64_t N);
+
+/* rstd (double [M], required) as written by rmsnorm_fwd_f64; dw double [N] fully overwritten
+ * (zeros for M = 0); workspace 16-byte aligned, contents clobbered. */
+rmsnorm_status rmsnorm_bwd_f64(const double* dy, int64_t lddy, const double* x, int64_t ldx,
+                               const double* w, const double* rstd, double* dx, int64_t lddx,
+                               double* dw, void* workspace, size_t workspace_bytes, int64_t M,
+                               int64_t N, double offset, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* rmsnorm_status_string(rmsnorm_status status);

@@ -281,3 +281,73 @@ def check_gn(y_gpu, mean_gpu, rstd_gpu, dx_gpu, dw_gpu, db_gpu, x, w, b, dy, *, 
     if db_gpu is not None:
         stats["db_normwise"] = check_dw(db_gpu, db_o)["dw_normwise"]
     return stats
+
+
+
+# ---- softmax and float64 ------------------------------------------------------------------------
+SM_F32_REL = 2.0**-18   # float32 softmax: expf, the x - max rounding, sums and the division
+F64_NORMWISE = 1e-10    # the candle page's bound for float64 fused kernels vs the composed formula
+
+
+def normwise(a, b) -> float:
+    num = np.linalg.norm(np.asarray(a, np.float64) - np.asarray(b, np.float64))
+    den = np.linalg.norm(np.asarray(b, np.float64))
+    return float(num / den) if den > 0 else float(num)
+
+
+def check_softmax_fwd(y_gpu, x, *, dtype) -> dict:
+    y_o = oracle.softmax_fwd(x, dtype=dtype)
+    if dtype == "f64":
+        st = {"y_normwise": normwise(y_gpu, y_o)}
+        assert st["y_normwise"] <= F64_NORMWISE, st
+        return st
+    eq = same_bits(y_gpu, y_o)
+    st = {"y_bitexact": float(eq.mean()) if eq.size else 1.0}
+    if dtype == "f32":
+        rel = np.abs(np.asarray(y_gpu, np.float64) - y_o) / np.maximum(np.abs(y_o), 1e-38)
+        st["y_max_rel"] = float(rel.max()) if rel.size else 0.0
+        assert np.all(rel <= SM_F32_REL), st
+        return st
+    d = ulps(y_gpu, y_o, dtype)
+    st["y_max_ulp"] = float(d.max()) if d.size else 0.0
+    assert st["y_bitexact"] >= Y_BITEXACT_FRAC, st
+    assert np.all(d <= 1), st
+    return st
+
+
+def check_softmax_bwd(dx_gpu, dy, y_gpu, *, dtype) -> dict:
+    dx_o = oracle.softmax_bwd(dy, y_gpu, dtype=dtype)
+    if dtype == "f64":
+        st = {"dx_normwise": normwise(dx_gpu, dx_o)}
+        assert st["dx_normwise"] <= F64_NORMWISE, st
+        return st
+    if dtype == "f32":
+        st = {"dx_normwise": normwise(dx_gpu, dx_o)}
+        assert st["dx_normwise"] <= F32_DX_NORMWISE, st
+        return st
+    # dx = y * (dy - s): the GPU's float32 s may differ from the correctly rounded one by a few
+    # float32 ulps of sum |dy * y| (its summation order), and where dy - s cancels (y near 1) that
+    # difference times y is the whole error. Allowed per element: 1 ulp of T (at the row-scaled
+    # floor) plus y * 8 * 2^-24 * sum |dy * y|.
+    y = np.asarray(y_gpu, np.float64)
+    sabs = np.sum(np.abs(np.asarray(dy, np.float64) * y), axis=-1, keepdims=True)
+    slack = y * 8.0 * 2.0**-24 * sabs
+    eq = same_bits(dx_gpu, dx_o)
+    st = {"dx_bitexact": float(eq.mean()) if eq.size else 1.0}
+    rms = np.sqrt(np.mean(np.asarray(dx_o, np.float64) ** 2, axis=-1, keepdims=True))
+    ref = np.maximum(np.abs(np.asarray(dx_o, np.float64)), DX_FLOOR * rms)
+    err = np.abs(np.asarray(dx_gpu, np.float64) - dx_o)
+    ok = eq | (err <= oracle.ulp_of(ref, dtype) + slack)
+    st["dx_outside"] = int((~ok).sum())
+    assert st["dx_bitexact"] >= DX_BITEXACT_FRAC, st
+    assert ok.all(), (st, np.argwhere(~ok)[:5])
+    return st
+
+
+def check_rms_f64(y_gpu, rstd_gpu, dx_gpu, dw_gpu, x, w, dy, *, eps, offset) -> dict:
+    y_o, r_o = oracle.rmsnorm_fwd_f64(x, w, eps=eps, offset=offset)
+    dx_o, dw_o = oracle.rmsnorm_bwd_f64(dy, x, w, r_o, offset=offset)
+    st = {"rstd_normwise": normwise(rstd_gpu, r_o), "y_normwise": normwise(y_gpu, y_o),
+          "dx_normwise": normwise(dx_gpu, dx_o), "dw_normwise": normwise(dw_gpu, dw_o)}
+    assert all(v <= F64_NORMWISE for v in st.values()), st
+    return st

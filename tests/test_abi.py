@@ -30,7 +30,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.rmsnorm_abi_version() == 3
+    assert lib.rmsnorm_abi_version() == 4
     for s in range(6):
         assert lib.rmsnorm_status_string(s)
     assert lib.rmsnorm_status_string(99) == b"unknown status"
@@ -255,3 +255,83 @@ def test_groupnorm_workspace_bytes(lib):
 
 def test_groupnorm_no_batch_is_a_noop(lib):
     assert gnf(lib, x=None, w=None, y=None, ws=None, B=0) == OK
+
+
+def smf(lib, x=FAKE, ldx=8, y=FAKE + 0x1000, ldy=8, M=4, N=8, dtype=BF16, variant=0):
+    return lib.softmax_fwd(x, ldx, y, ldy, M, N, dtype, variant, None)
+
+
+def smb(lib, dy=FAKE, lddy=8, y=FAKE + 0x1000, ldy=8, dx=FAKE + 0x2000, lddx=8, M=4, N=8,
+        dtype=BF16, variant=0):
+    return lib.softmax_bwd(dy, lddy, y, ldy, dx, lddx, M, N, dtype, variant, None)
+
+
+F64 = 3
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(M=-1), INVALID), (dict(N=0), INVALID),
+    (dict(ldx=7), INVALID), (dict(dtype=4), INVALID), (dict(variant=5), INVALID),
+    (dict(variant=2), UNSUPPORTED), (dict(x=FAKE + 1), MISALIGNED),
+    (dict(dtype=F64, y=FAKE + 4), MISALIGNED), (dict(x=FAKE + 2, variant=1), UNSUPPORTED),
+    (dict(N=(1 << 24) + 1, ldx=(1 << 24) + 1, ldy=(1 << 24) + 1), UNSUPPORTED),
+])
+def test_softmax_fwd_rejects(lib, kw, status):
+    assert smf(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), INVALID), (dict(y=None), INVALID), (dict(dx=None), INVALID),
+    (dict(lddy=3), INVALID), (dict(dtype=-2), INVALID), (dict(dy=FAKE + 1), MISALIGNED),
+    (dict(variant=2), UNSUPPORTED),
+])
+def test_softmax_bwd_rejects(lib, kw, status):
+    assert smb(lib, **kw) == status
+
+
+def test_softmax_no_rows_is_a_noop(lib):
+    assert smf(lib, x=None, y=None, M=0) == OK
+    assert smb(lib, dy=None, y=None, dx=None, M=0, dtype=F64) == OK
+
+
+def test_f64_dtype_is_rejected_by_the_16_bit_entry_points(lib):
+    assert fwd(lib, dtype=F64) == INVALID
+    assert lnf(lib, dtype=F64) == INVALID
+    assert lib.rmsnorm_bwd_workspace_bytes(4, 8, F64) == 0
+
+
+def f64f(lib, x=FAKE, ldx=8, w=FAKE + 0x1000, y=FAKE + 0x2000, ldy=8, rstd=None, M=4, N=8,
+         eps=1e-6, offset=0.0):
+    return lib.rmsnorm_fwd_f64(x, ldx, w, y, ldy, rstd, M, N, eps, offset, None)
+
+
+def f64b(lib, dy=FAKE, lddy=8, x=FAKE + 0x1000, ldx=8, w=FAKE + 0x2000, rstd=FAKE + 0x3000,
+         dx=FAKE + 0x4000, lddx=8, dw=FAKE + 0x5000, ws=FAKE + 0x6000, wsb=1 << 20, M=4, N=8,
+         offset=0.0):
+    return lib.rmsnorm_bwd_f64(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, ws, wsb, M, N, offset,
+                               None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(offset=float("inf")), INVALID),
+    (dict(ldy=7), INVALID), (dict(x=FAKE + 4), MISALIGNED), (dict(rstd=FAKE + 4), MISALIGNED),
+    (dict(N=(1 << 24) + 1, ldx=(1 << 24) + 1, ldy=(1 << 24) + 1), UNSUPPORTED),
+])
+def test_rmsnorm_fwd_f64_rejects(lib, kw, status):
+    assert f64f(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), INVALID), (dict(rstd=None), INVALID), (dict(dw=None), INVALID),
+    (dict(ws=None), INVALID), (dict(wsb=4 * 8 * 8 - 1), WORKSPACE), (dict(ws=FAKE + 8), MISALIGNED),
+    (dict(dw=FAKE + 4), MISALIGNED), (dict(offset=float("nan")), INVALID),
+])
+def test_rmsnorm_bwd_f64_rejects(lib, kw, status):
+    assert f64b(lib, **kw) == status
+
+
+def test_f64_workspace_bytes(lib):
+    f = lib.rmsnorm_bwd_f64_workspace_bytes
+    assert f(4096, 4096) == 256 * 4096 * 8 and f(3, 5) == 3 * 5 * 8
+    assert f(0, 5) == 0 and f(5, 0) == 0

@@ -1,0 +1,130 @@
+"""GPU parity of softmax over the last dimension and of the float64 RMSNorm (through the C
+interface) against the CPU oracle.
+
+Softmax: float32 / float16 / bfloat16 / float64, register and streaming kernels (bit-identical),
+ragged and misaligned widths, peaked rows (large logits), rows of -inf but one element, and the
+backward from the GPU's own forward output. Float64 RMSNorm: forward and backward to the candle
+page's 1e-10 bound against the composed float64 formula.
+"""
+import numpy as np
+import pytest
+
+from parity import check_rms_f64, check_softmax_bwd, check_softmax_fwd, same_bits, to_np
+from workloads import F64_WORKLOADS, SM_WORKLOADS, make_inputs, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bwd_precision_numerics_amd as rn  # noqa: E402
+
+DEV = "cuda:0"
+WL = {"bf16": SM_WORKLOADS["sm_bf16_4096x4096"], "f16": SM_WORKLOADS["sm_f16_4096x4096"],
+      "f32": SM_WORKLOADS["sm_f32_64x1024"], "f64": SM_WORKLOADS["sm_f64_1024x4096"]}
+
+
+def arr(t):
+    return t.detach().cpu().numpy() if t.dtype == torch.float64 else to_np(t)
+
+
+def run_sm(dtype, M, N, variant="auto", seed=1, x=None, ld=None):
+    inp = make_inputs(WL[dtype], M=M, N=N, seed=seed)
+    x = inp["x"] if x is None else x
+    dy = inp["dy"]
+    if ld is None:
+        xt, dyt = to_device(x, dtype, DEV), to_device(dy, dtype, DEV)
+    else:
+        bx = np.zeros((M, ld), x.dtype)
+        bx[:, :N] = x
+        bd = np.zeros((M, ld), dy.dtype)
+        bd[:, :N] = dy
+        xt, dyt = to_device(bx, dtype, DEV)[:, :N], to_device(bd, dtype, DEV)[:, :N]
+    print(f"softmax case dtype={dtype} M={M} N={N} ld={ld} variant={variant} seed={seed}",
+          flush=True)
+    y = rn.softmax_fwd(xt, variant=variant)
+    dx = rn.softmax_bwd(dyt, y, variant=variant)
+    torch.cuda.synchronize()
+    yg, dxg = arr(y), arr(dx)
+    st = check_softmax_fwd(yg, x, dtype=dtype)
+    st.update(check_softmax_bwd(dxg, dy, yg, dtype=dtype))
+    return st, (yg, dxg)
+
+
+SHAPES = [(1, 1), (3, 7), (33, 64), (300, 1000), (129, 1027), (257, 3072), (64, 4096),
+          (40, 8192), (12, 16384), (5, 32768), (3, 70000)]
+
+
+@pytest.mark.parametrize("M,N", SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32", "f64"])
+def test_softmax_parity(dtype, M, N):
+    run_sm(dtype, M, N)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_softmax_padded_rows(dtype):
+    run_sm(dtype, 100, 1000, ld=1032)
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 1000), ("bf16", 4096), ("f16", 8192),
+                                     ("f32", 2048), ("f64", 4096)])
+def test_softmax_families_agree(dtype, N):
+    _, a = run_sm(dtype, 70, N, variant="registers", seed=3)
+    _, b = run_sm(dtype, 70, N, variant="streaming", seed=3)
+    assert same_bits(a[0], b[0]).all() and same_bits(a[1], b[1]).all()
+
+
+def test_softmax_peaked_and_infinite_logits():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((64, 2048)) * 30.0).astype(np.float32)
+    x[3, :] = -np.inf
+    x[3, 17] = 0.0
+    xb = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    st, (yg, _) = run_sm("bf16", 64, 2048, x=xb)
+    assert yg[3, 17] == 1.0 and np.count_nonzero(yg[3]) == 1
+
+
+def test_softmax_zero_rows():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    assert rn.softmax_fwd(x).shape == (0, 64)
+    assert rn.softmax_bwd(x, x).shape == (0, 64)
+
+
+def test_softmax_full_size_bf16():
+    wl = WL["bf16"]
+    st, _ = run_sm("bf16", wl.M, wl.N, seed=wl.seed)
+    print(st)
+
+
+def run_f64(M, N, seed=2, eps=1e-6, offset=0.0, ld=None):
+    wl = F64_WORKLOADS["f64_4096x4096"]
+    inp = make_inputs(wl, M=M, N=N, seed=seed)
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    print(f"f64 rmsnorm case M={M} N={N} eps={eps} offset={offset} ld={ld}", flush=True)
+    if ld is None:
+        xt, dyt = to_device(x, "f64", DEV), to_device(dy, "f64", DEV)
+    else:
+        bx, bd = np.zeros((M, ld)), np.zeros((M, ld))
+        bx[:, :N], bd[:, :N] = x, dy
+        xt, dyt = to_device(bx, "f64", DEV)[:, :N], to_device(bd, "f64", DEV)[:, :N]
+    wt = to_device(w, "f64", DEV)
+    y, rstd = rn.fwd_f64(xt, wt, eps=eps, offset=offset)
+    dx, dw = rn.bwd_f64(dyt, xt, wt, rstd, offset=offset)
+    torch.cuda.synchronize()
+    return check_rms_f64(arr(y), arr(rstd), arr(dx), arr(dw), x, w, dy, eps=eps, offset=offset)
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (5, 3), (300, 1000), (129, 1027), (257, 4096),
+                                 (24, 16384), (3, 70000)])
+def test_rmsnorm_f64_parity(M, N):
+    print(run_f64(M, N))
+
+
+def test_rmsnorm_f64_gemma_offset_and_padding():
+    print(run_f64(200, 2048, offset=1.0, eps=1e-5, ld=2056))
+
+
+def test_rmsnorm_f64_full_size():
+    wl = F64_WORKLOADS["f64_4096x4096"]
+    print(run_f64(wl.M, wl.N, seed=wl.seed, eps=wl.eps))

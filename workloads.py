@@ -18,7 +18,7 @@ import math
 
 import numpy as np
 
-DTYPES = ("f32", "f16", "bf16")
+DTYPES = ("f32", "f16", "bf16", "f64")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -40,7 +40,7 @@ class Workload:
 
     @property
     def itemsize(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "f64": 8}.get(self.dtype, 2)
 
     def fwd_bytes(self) -> int:
         """Algorithmic bytes of one forward: read x, write y, read w once, write the fp32 rstd."""
@@ -89,7 +89,10 @@ def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
 
 
 def to_dtype_values(a, dtype: str) -> np.ndarray:
-    """float32 array holding the values of ``a`` converted to ``dtype`` by a library cast."""
+    """float32 array holding the values of ``a`` converted to ``dtype`` by a library cast
+    (float64 array, the values as drawn, for "f64")."""
+    if dtype == "f64":
+        return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
     a32 = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
     if dtype == "f32":
         return a32
@@ -123,11 +126,13 @@ def make_inputs(wl: Workload, M: int | None = None, N: int | None = None,
 
 def torch_dtype(dtype: str):
     import torch
-    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+            "f64": torch.float64}[dtype]
 
 
 def to_device(a: np.ndarray, dtype: str, device: str):
-    """Copy a float32 array of T values to a ``device`` tensor of dtype T (exact conversion)."""
+    """Copy an array of T values (float32, or float64 for "f64") to a ``device`` tensor of dtype T
+    (exact conversion)."""
     import torch
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch_dtype(dtype)).to(device)
 
@@ -239,3 +244,21 @@ def make_gn_inputs(wl: GnWorkload, B: int | None = None, C: int | None = None,
     dy = _draw(rng, wl.dy_dist, (B, C, S))
     b = _draw(rng, wl.b_dist, (C,))
     return {k: to_dtype_values(v, wl.dtype) for k, v in (("x", x), ("w", w), ("dy", dy), ("b", b))}
+
+
+# Softmax over the last dimension: logits x ~ N(0, 2^2) (a spread that gives peaked rows), dy ~
+# N(0, 1), at the RMSNorm headline shape; and the float64 RMSNorm at the same shape.
+SM_WORKLOADS = {
+    "sm_bf16_4096x4096": Workload("sm_bf16_4096x4096", "bf16", 4096, 4096, "once", 0.0, 0.0,
+                                  ("normal", 0.0, 2.0), _GAIN, _STD, 0),
+    "sm_f32_64x1024": Workload("sm_f32_64x1024", "f32", 64, 1024, "once", 0.0, 0.0,
+                               ("normal", 0.0, 2.0), _GAIN, _STD, 0),
+    "sm_f16_4096x4096": Workload("sm_f16_4096x4096", "f16", 4096, 4096, "once", 0.0, 0.0,
+                                 ("normal", 0.0, 2.0), _GAIN, _STD, 0),
+    "sm_f64_1024x4096": Workload("sm_f64_1024x4096", "f64", 1024, 4096, "once", 0.0, 0.0,
+                                 ("normal", 0.0, 2.0), _GAIN, _STD, 0),
+}
+F64_WORKLOADS = {
+    "f64_4096x4096": Workload("f64_4096x4096", "f64", 4096, 4096, "once", 0.0, 1e-6, _STD, _GAIN,
+                              _STD, 0),
+}
