@@ -299,6 +299,83 @@ def layernorm_row(torch, rn, sets, launches):
             "bwd_includes": "rows kernel + dw and db reductions"}
 
 
+def softmax_row(torch, rn, sets, launches):
+    """Softmax over the last dimension, forward and backward, at the headline shape and dtype, on
+    the rotating buffers (x as logits, y the output, then dy, y -> dx)."""
+    lib, wl = sets.lib, sets.wl
+    M, N, dt, n = wl.M, wl.N, rn.DTYPE_CODES[wl.dtype], len(sets.sets)
+
+    def fwd(k):
+        s = sets.sets[k % n]
+        st = lib.softmax_fwd(s["x"].data_ptr(), N, s["y"].data_ptr(), N, M, N, dt, 0,
+                             sets.stream())
+        if st:
+            raise RuntimeError(f"softmax_fwd status {st}")
+
+    def bwd(k):
+        s = sets.sets[(k + n // 2) % n]
+        st = lib.softmax_bwd(s["dy"].data_ptr(), N, s["y"].data_ptr(), N, s["dx"].data_ptr(), N,
+                             M, N, dt, 0, sets.stream())
+        if st:
+            raise RuntimeError(f"softmax_bwd status {st}")
+
+    for k in range(n):
+        fwd(k)
+    torch.cuda.synchronize()
+    tf, tb = graph_time(torch, fwd, launches), graph_time(torch, bwd, launches)
+    s = wl.itemsize
+    fb, bb = 2 * M * N * s, 3 * M * N * s
+    return {"workload": f"softmax_{wl.dtype}_{M}x{N}", "fwd_us": round(tf * 1e6, 3),
+            "bwd_us": round(tb * 1e6, 3), "fwd_GBps": round(fb / tf / 1e9, 1),
+            "bwd_GBps": round(bb / tb / 1e9, 1), "fwd_bytes": fb, "bwd_bytes": bb}
+
+
+def f64_row(torch, rn, launches, rotate_mib):
+    """The float64 RMSNorm, forward and backward, at 4096 x 4096."""
+    from workloads import F64_WORKLOADS, make_inputs, to_device
+    wl = F64_WORKLOADS["f64_4096x4096"]
+    lib, dev, M, N = rn.library(), "cuda:0", wl.M, wl.N
+    inp = make_inputs(wl)
+    x0, dy0 = to_device(inp["x"], "f64", dev), to_device(inp["dy"], "f64", dev)
+    w = to_device(inp["w"], "f64", dev)
+    del inp
+    n = max(4, -(-rotate_mib * 2**20 // (M * N * 8)))
+    sets = [{"x": x0.clone(), "dy": dy0.clone(), "y": torch.empty_like(x0),
+             "dx": torch.empty_like(x0),
+             "rstd": torch.empty(M, dtype=torch.float64, device=dev)} for _ in range(n)]
+    del x0, dy0
+    dw = torch.empty(N, dtype=torch.float64, device=dev)
+    wsb = int(lib.rmsnorm_bwd_f64_workspace_bytes(M, N))
+    ws = torch.empty(wsb // 8, dtype=torch.float64, device=dev)
+    stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+
+    def fwd(k):
+        s = sets[k % n]
+        st = lib.rmsnorm_fwd_f64(s["x"].data_ptr(), N, w.data_ptr(), s["y"].data_ptr(), N,
+                                 s["rstd"].data_ptr(), M, N, wl.eps, wl.offset, stream())
+        if st:
+            raise RuntimeError(f"rmsnorm_fwd_f64 status {st}")
+
+    def bwd(k):
+        s = sets[(k + n // 2) % n]
+        st = lib.rmsnorm_bwd_f64(s["dy"].data_ptr(), N, s["x"].data_ptr(), N, w.data_ptr(),
+                                 s["rstd"].data_ptr(), s["dx"].data_ptr(), N, dw.data_ptr(),
+                                 ws.data_ptr(), wsb, M, N, wl.offset, stream())
+        if st:
+            raise RuntimeError(f"rmsnorm_bwd_f64 status {st}")
+
+    for k in range(n):
+        fwd(k)
+    torch.cuda.synchronize()
+    tf, tb = graph_time(torch, fwd, launches), graph_time(torch, bwd, launches)
+    fb = 2 * M * N * 8 + N * 8 + 8 * M
+    bb = 3 * M * N * 8 + N * 8 + 8 * M + 8 * N
+    return {"workload": wl.name, "fwd_us": round(tf * 1e6, 3), "bwd_us": round(tb * 1e6, 3),
+            "fwd_GBps": round(fb / tf / 1e9, 1), "bwd_GBps": round(bb / tb / 1e9, 1),
+            "fwd_bytes": fb, "bwd_bytes": bb, "buffer_sets": n,
+            "bwd_includes": "rows kernel + float64 dw reduction"}
+
+
 def groupnorm_row(torch, rn, launches, rotate_mib):
     """GroupNorm forward and backward at the group_norm page's (16, 32, 256, 256), 8 groups."""
     from workloads import GN_HEADLINE, GN_WORKLOADS, make_gn_inputs, to_device
@@ -479,10 +556,13 @@ def main(argv=None) -> int:
     }
     if not args.no_rows and name == HEADLINE:
         launches = max(min(args.steps, 100), 20)
-        line["rows"] = {"layernorm": layernorm_row(torch, rn, sets, launches)}
+        line["rows"] = {"layernorm": layernorm_row(torch, rn, sets, launches),
+                        "softmax": softmax_row(torch, rn, sets, launches)}
         del sets
         torch.cuda.empty_cache()
         line["rows"]["groupnorm"] = groupnorm_row(torch, rn, launches, args.rotate_mib)
+        torch.cuda.empty_cache()
+        line["rows"]["rmsnorm_f64"] = f64_row(torch, rn, launches, args.rotate_mib)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(wl, rounding, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -113,6 +113,7 @@ rmsnorm_status f64_fwd_impl(const double* x, int64_t ldx, const double* w, doubl
   const bool wide = wide_fits(x, ldx, 8) && wide_fits(y, ldy, 8) && aligned(w, 16);
   int tpr, iters;
   sm_shape(wide ? ceil_div(N, 2) : N, &tpr, &iters);
+  const bool regs = wide && iters <= kSmMaxIters;
   const int groups = tpr >= kFwdBlockThreads ? 1 : kFwdBlockThreads / tpr;
   const int64_t grid = ceil_div(M, groups);
   if (grid > INT32_MAX) return RMSNORM_ERR_UNSUPPORTED;
@@ -123,8 +124,17 @@ rmsnorm_status f64_fwd_impl(const double* x, int64_t ldx, const double* w, doubl
   a.eps = eps; a.offset = offset;
   const size_t lds = round16(sizeof(double) * (size_t)groups * (tpr / 64));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return wide ? launch(rms_f64_fwd_kernel<true>, grid, groups * tpr, lds, s, a)
-              : launch(rms_f64_fwd_kernel<false>, grid, groups * tpr, lds, s, a);
+  const int block = groups * tpr;
+  if (!regs)
+    return wide ? launch(rms_f64_fwd_kernel<true>, grid, block, lds, s, a)
+                : launch(rms_f64_fwd_kernel<false>, grid, block, lds, s, a);
+  switch (iters) {
+    case 1: return launch(rms_f64_fwd_rows_kernel<1>, grid, block, lds, s, a);
+    case 2: return launch(rms_f64_fwd_rows_kernel<2>, grid, block, lds, s, a);
+    case 3: return launch(rms_f64_fwd_rows_kernel<3>, grid, block, lds, s, a);
+    case 4: return launch(rms_f64_fwd_rows_kernel<4>, grid, block, lds, s, a);
+    default: return RMSNORM_ERR_UNSUPPORTED;
+  }
 }
 
 rmsnorm_status f64_bwd_impl(const double* dy, int64_t lddy, const double* x, int64_t ldx,
@@ -154,13 +164,20 @@ rmsnorm_status f64_bwd_impl(const double* dy, int64_t lddy, const double* x, int
   bwd_shape(wide ? ceil_div(N, 2) : N, &a.tpr, &iters);
   a.groups = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M > 0) {
-    const size_t lds = round16(sizeof(double) * 2 * (a.tpr / 64));
+  if (M == 0) {
+    hipLaunchKernelGGL(fill_zero_f64_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s, dw,
+                       (int)N);
+    return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+  }
+  const size_t lds = round16(sizeof(double) * 2 * (a.tpr / 64));
+  if (wide && iters == 1) st = launch(rms_f64_bwd_rows_kernel<1>, a.P, a.tpr, lds, s, a);
+  else if (wide && iters == 2) st = launch(rms_f64_bwd_rows_kernel<2>, a.P, a.tpr, lds, s, a);
+  else
     st = wide ? launch(rms_f64_bwd_kernel<true>, a.P, a.tpr, lds, s, a)
               : launch(rms_f64_bwd_kernel<false>, a.P, a.tpr, lds, s, a);
-    if (st != RMSNORM_OK) return st;
-  }
-  hipLaunchKernelGGL(rms_f64_dw_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s, a);
+  if (st != RMSNORM_OK) return st;
+  hipLaunchKernelGGL(dw_reduce_kernel<double>, dim3((unsigned)ceil_div(N, 16)), dim3(256), 0, s,
+                     a.part, N, a.P, (int)N, dw, nullptr, (int64_t)0);
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
 }
 

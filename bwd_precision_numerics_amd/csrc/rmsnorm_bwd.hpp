@@ -462,31 +462,32 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
 // adds them in order of i; the four lanes of a column (l / 16 = 0..3) are then added in order, and
 // finally the four waves in order. blockIdx.y selects one of gridDim.y sets of partial rows,
 // set_stride floats apart, and its output (dw, or dw2 for the second set).
+// T is float, or double for the float64 RMSNorm.
 static_assert(kMaxPartials % 16 == 0, "dw_reduce_kernel reads partial rows in groups of 16");
-inline __global__ void __launch_bounds__(256) dw_reduce_kernel(const float* part, int64_t ldp, int P,
-                                                               int N, float* dw, float* dw2,
-                                                               int64_t set_stride) {
+template <typename T>
+__global__ void __launch_bounds__(256) dw_reduce_kernel(const T* part, int64_t ldp, int P, int N,
+                                                        T* dw, T* dw2, int64_t set_stride) {
   if (blockIdx.y) {
     part += set_stride;
     dw = dw2;
   }
   constexpr int L = kMaxPartials / 16;
-  __shared__ float buf[4][16];
+  __shared__ T buf[4][16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 15, q = lane >> 4;
   const int col = blockIdx.x * 16 + c;
-  float v[L];
+  T v[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     const int p = 16 * i + 4 * wv + q;
-    v[i] = (col < N && p < P) ? part[(int64_t)p * ldp + col] : 0.f;
+    v[i] = (col < N && p < P) ? part[(int64_t)p * ldp + col] : T(0);
   }
-  float s = v[0];
+  T s = v[0];
 #pragma unroll
   for (int i = 1; i < L; ++i) s += v[i];
   // lanes c, c+16, c+32, c+48 hold the four row phases of column c: add them in order q = 0..3
-  const float s1 = __shfl(s, c + 16, 64), s2 = __shfl(s, c + 32, 64), s3 = __shfl(s, c + 48, 64);
-  const float t = ((s + s1) + s2) + s3;
+  const T s1 = __shfl(s, c + 16, 64), s2 = __shfl(s, c + 32, 64), s3 = __shfl(s, c + 48, 64);
+  const T t = ((s + s1) + s2) + s3;
   if (q == 0) buf[wv][c] = t;
   __syncthreads();
   if (wv == 0 && q == 0 && col < N) dw[col] = ((buf[0][c] + buf[1][c]) + buf[2][c]) + buf[3][c];

@@ -6,13 +6,15 @@
 // 16-bit types and float64 for float64; float64 kernels accumulate in float64 (a float accumulator
 // made the float64 forward's statistics differ from the backward's).
 //
-//   forward   m = max_j x_j,  e_j = exp(x_j - m),  y_j = T(e_j / sum_k e_k)
+//   forward   m = max_j x_j,  e_j = exp(x_j - m),  y_j = T(e_j * r),  r = 1 / sum_k e_k
+// (one division per row; each y is within about three float32 ulps of the exact quotient before
+// the cast, against nine vector instructions per element for an IEEE division)
 //   backward  s = sum_j dy_j * y_j,  dx_j = T(y_j * (dy_j - s))
 //
 // A is the compute type: float for float32 / float16 / bfloat16 I/O, double for float64.
 #pragma once
 
-#include "rmsnorm_common.hpp"
+#include "rmsnorm_bwd.hpp"
 
 namespace rmsn {
 
@@ -41,8 +43,8 @@ template <> struct NumIO<DT::F64, true> {
   static constexpr int V = 2;
   static __device__ __forceinline__ Raw load(const S* p, int n) {
     if (n >= 2) return *reinterpret_cast<const uint4*>(p);
-    const double t[2] = {n > 0 ? p[0] : 0.0, 0.0};
-    return __builtin_bit_cast(uint4, t);
+    const uint2 u = __builtin_bit_cast(uint2, n > 0 ? p[0] : 0.0);
+    return make_uint4(u.x, u.y, 0u, 0u);
   }
   static __device__ __forceinline__ void unpack(const Raw& r, double (&f)[2]) {
     f[0] = __builtin_bit_cast(double, make_uint2(r.x, r.y));
@@ -196,6 +198,7 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   }
   const A sum = group_reduce<false>(s0 + s1, red + wpr, wpr, tl);
   if (!valid) return;
+  const A r = (A)1 / sum;
   S* yr = static_cast<S*>(a.out) + row * a.ldo;
   if constexpr (ITERS > 0) {
 #pragma unroll
@@ -204,7 +207,7 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
       if (col >= N) continue;
       A o[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) o[e] = ev[it][e] / sum;
+      for (int e = 0; e < V; ++e) o[e] = ev[it][e] * r;
       IO::store(yr + col, o, N - col);
     }
   } else {
@@ -213,7 +216,7 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
       A f[V], o[V];
       IO::unpack(IO::load(xr + col, N - col), f);
 #pragma unroll
-      for (int e = 0; e < V; ++e) o[e] = exp_a(f[e] - mx) / sum;
+      for (int e = 0; e < V; ++e) o[e] = exp_a(f[e] - mx) * r;
       IO::store(yr + col, o, N - col);
     }
   }
@@ -426,13 +429,146 @@ __global__ void __launch_bounds__(1024) rms_f64_bwd_kernel(F64Args a) {
   }
 }
 
-// dw_j = sum over p of part[p, j], p in order; one thread per column.
-__global__ void __launch_bounds__(256) rms_f64_dw_kernel(F64Args a) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= a.N) return;
-  double s = 0.0;
-  for (int p = 0; p < a.P; ++p) s += a.part[(int64_t)p * a.N + j];
-  a.dw[j] = s;
+__global__ void fill_zero_f64_kernel(double* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0;
+}
+
+// Register forward: a row of at most ITERS 16-byte vectors per thread stays in registers (with w)
+// between the reduction and the store; x is read once.
+template <int ITERS>
+__global__ void __launch_bounds__(1024) rms_f64_fwd_rows_kernel(F64Args a) {
+  using IO = NumIO<DT::F64, true>;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+  double* red = reinterpret_cast<double*>(smem) + grp * wpr;
+  const double* xr = a.x + (valid ? row : 0) * a.ldx;
+  uint4 rx[ITERS], rw[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    const bool ok = valid && col < N;
+    rx[it] = IO::load(xr + (ok ? col : 0), ok ? N - col : 0);
+    rw[it] = IO::load(a.w + (ok ? col : 0), ok ? N - col : 0);
+  }
+  double q0 = 0, q1 = 0;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    double f[V];
+    IO::unpack(rx[it], f);
+    q0 = fma(f[0], f[0], q0);
+    q1 = fma(f[1], f[1], q1);
+  }
+  const double ss = group_reduce<false>(q0 + q1, red, wpr, tl);
+  const double rs = 1.0 / sqrt(ss / (double)N + a.eps);
+  if (!valid) return;
+  if (tl == 0 && a.rstd) a.rstd[row] = rs;
+  double* yr = a.out + row * a.ldo;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    if (col >= N) continue;
+    double f[V], wf[V], o[V];
+    IO::unpack(rx[it], f);
+    IO::unpack(rw[it], wf);
+#pragma unroll
+    for (int e = 0; e < V; ++e) o[e] = (f[e] * rs) * (a.offset + wf[e]);
+    IO::store(yr + col, o, N - col);
+  }
+}
+
+// Register backward on the persistent grid (block b of P owns rows b, b + P, ...; one row at a
+// time per block, the next row's x, dy and rstd loaded while the current one is reduced). The dw
+// column sums stay in registers and are written once as partial row b of the [P, N] workspace.
+template <int ITERS>
+__global__ void __launch_bounds__(1024) rms_f64_bwd_rows_kernel(F64Args a) {
+  using IO = NumIO<DT::F64, true>;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int tl = threadIdx.x;
+  const int b = blockIdx.x, P = a.P;
+  double* red = reinterpret_cast<double*>(smem);  // [2][wpr]
+  double g[ITERS][V], acc[ITERS][V];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    double wf[V];
+    IO::unpack(IO::load(a.w + (col < N ? col : 0), col < N ? N - col : 0), wf);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      g[it][e] = a.offset + wf[e];
+      acc[it][e] = 0.0;
+    }
+  }
+  uint4 rx[2][ITERS], rd[2][ITERS];
+  double rr[2];
+  auto load_row = [&](int slot, int64_t row) {
+    rr[slot] = a.rstd[row];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      const bool ok = col < N;
+      rx[slot][it] = IO::load(a.x + row * a.ldx + (ok ? col : 0), ok ? N - col : 0);
+      rd[slot][it] = IO::load(a.dy + row * a.lddy + (ok ? col : 0), ok ? N - col : 0);
+    }
+  };
+  const int64_t nloc = block_rows(a.M, P, b);
+  if (nloc > 0) load_row(0, b);
+  for (int64_t s0 = 0; s0 < nloc; s0 += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t s = s0 + j;
+      if (s < nloc) {  // block-uniform
+        if (s + 1 < nloc) load_row(j ^ 1, b + (s + 1) * P);
+        const double rs = rr[j];
+        double d0 = 0, d1 = 0;
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+          double f[V], df[V];
+          IO::unpack(rx[j][it], f);
+          IO::unpack(rd[j][it], df);
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const double xh = f[e] * rs, gd = g[it][e] * df[e];
+            acc[it][e] = fma(df[e], xh, acc[it][e]);
+            if (e & 1) d1 = fma(gd, xh, d1);
+            else d0 = fma(gd, xh, d0);
+          }
+        }
+        const double c = group_reduce<false>(d0 + d1, red + (s & 1) * wpr, wpr, tl) / (double)N;
+        double* xo = a.out + (b + s * P) * a.ldo;
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+          const int col = (it * TPR + tl) * V;
+          if (col >= N) continue;
+          double f[V], df[V], o[V];
+          IO::unpack(rx[j][it], f);
+          IO::unpack(rd[j][it], df);
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const double xh = f[e] * rs;
+            o[e] = rs * (g[it][e] * df[e] - xh * c);
+          }
+          IO::store(xo + col, o, N - col);
+        }
+      }
+    }
+  }
+  double* pr = a.part + (int64_t)b * N;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+      if (col + e < N) pr[col + e] = acc[it][e];
+  }
 }
 
 }  // namespace rmsn

@@ -11,8 +11,10 @@
  *     dx = T( y * (dy - s) ),   s = sum_j dy_j * y_j
  *
  * from the forward's output y, with s in float32 for the 16-bit types and float32, float64 for
- * float64. The forward, per row: m = max_j x_j, e_j = exp(x_j - m), y_j = T(e_j / sum_k e_k)
- * (exp and every division in the compute type; sums in an order of the library's choosing).
+ * float64. The forward, per row: m = max_j x_j, e_j = exp(x_j - m), r = 1 / sum_k e_k,
+ * y_j = T(e_j * r) (exp, the one division per row and every product in the compute type; sums in
+ * an order of the library's choosing), within a few ulps of the compute type of the exact
+ * e_j / sum before the cast.
  *
  * Layout: row-major [M, N], unit column stride, row strides in elements (>= N); dtype is one of
  * RMSNORM_DTYPE_F32, _F16, _BF16, _F64 for all tensors of a call. variant: AUTO, REGISTERS (the
