@@ -46,7 +46,8 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_bwd_rows_bf16_4096x4096.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "bwd_precision_numerics_amd", "csrc", f) for f in
-                  ("librmsnorm.hip", "rmsnorm_common.hpp", "rmsnorm_fwd.hpp", "rmsnorm_bwd.hpp")]
+                  ("librmsnorm.hip", "host_common.hpp", "rmsnorm_common.hpp", "rmsnorm_fwd.hpp",
+                   "rmsnorm_bwd.hpp")]
 
 
 def kernel_source_hash() -> str:
