@@ -250,7 +250,7 @@ def check_ln_bwd(dx_gpu, dw_gpu, db_gpu, dy, x, w, mean_gpu, rstd_gpu, *, dtype)
 def check_gn(y_gpu, mean_gpu, rstd_gpu, dx_gpu, dw_gpu, db_gpu, x, w, b, dy, *, G, eps,
              dtype) -> dict:
     """GroupNorm: the LayerNorm contract applied to the (batch, group) rows, the oracle's backward
-    run from the GPU's mean and rstd."""
+    run from the GPU's mean and rstd. dw_gpu None skips the parameter gradients (a batch subset)."""
     x = np.asarray(x, np.float32)
     B, C, S = x.shape
     y_o, m_o, r_o = oracle.groupnorm_fwd(x, w, b, G=G, eps=eps, dtype=dtype)
@@ -277,7 +277,8 @@ def check_gn(y_gpu, mean_gpu, rstd_gpu, dx_gpu, dw_gpu, db_gpu, x, w, b, dy, *, 
     else:
         stats.update(check_floored(np.asarray(dx_gpu).reshape(B * G, -1), dx_o.reshape(B * G, -1),
                                    dtype, "dx", frac=LN_DX_BITEXACT_FRAC))
-    stats.update(check_dw(dw_gpu, dw_o))
+    if dw_gpu is not None:
+        stats.update(check_dw(dw_gpu, dw_o))
     if db_gpu is not None:
         stats["db_normwise"] = check_dw(db_gpu, db_o)["dw_normwise"]
     return stats

@@ -103,3 +103,32 @@ def test_gn_zero_batch():
     dx, dw, db = rn.groupnorm_bwd(x, x, 4, w, m, r)
     torch.cuda.synchronize()
     assert y.shape == (0, 8, 16) and float(dw.abs().sum()) == 0.0 and float(db.abs().sum()) == 0.0
+
+
+def test_gn_full_size_bench_shape():
+    """The shape and launch configuration the benchmark times: bf16 (16, 32, 256, 256), 8 groups,
+    with bias. mean and rstd of every row, y and dx on sampled batches (the first, a seeded one and
+    the last), dW and dB over the whole batch."""
+    import oracle
+    from parity import check_dw, check_stats
+    wl = GN_WORKLOADS["gn_bf16_16x32x256x256_g8"]
+    inp = make_gn_inputs(wl)
+    x, w, b, dy = inp["x"], inp["w"], inp["b"], inp["dy"]
+    B, C, S, G = wl.B, wl.C, wl.S, wl.G
+    print(f"gn full size {wl.name}", flush=True)
+    xt, dyt = to_device(x, "bf16", DEV), to_device(dy, "bf16", DEV)
+    wt, bt = to_device(w, "bf16", DEV), to_device(b, "bf16", DEV)
+    y, mean, rstd = rn.groupnorm_fwd(xt, G, wt, bt, eps=wl.eps)
+    dx, dw, db = rn.groupnorm_bwd(dyt, xt, G, wt, mean, rstd)
+    torch.cuda.synchronize()
+    yg, mg, rg, dxg, dwg, dbg = (to_np(t) for t in (y, mean, rstd, dx, dw, db))
+    rows = x.reshape(B * G, -1)
+    m_o, r_o = oracle.row_stats(rows, wl.eps)
+    st = check_stats(mg.reshape(-1), rg.reshape(-1), m_o, r_o, rows)
+    pick = sorted({0, int(np.random.default_rng(7).integers(1, B - 1)), B - 1})
+    st.update(check_gn(yg[pick], mg[pick], rg[pick], dxg[pick], None, None, x[pick], w, b,
+                       dy[pick], G=G, eps=wl.eps, dtype="bf16"))
+    _, dw_o, db_o = oracle.groupnorm_bwd(dy, x, w, mg, rg, G=G, dtype="bf16")
+    st.update(check_dw(dwg, dw_o))
+    st["db_normwise"] = check_dw(dbg, db_o)["dw_normwise"]
+    print(pick, st)
