@@ -15,6 +15,7 @@ raises ``LibraryMissing`` (build it with ``python -m bwd_precision_numerics_amd.
     y, mean, rstd = groupnorm_fwd(x, G, w, b, eps=1e-5)    # GroupNorm of [B, C, *spatial]
     dx, dw, db    = groupnorm_bwd(dy, x, G, w, mean, rstd)
     y = softmax_fwd(x); dx = softmax_bwd(dy, y)             # softmax over the last dimension
+    layer_norm(x, w, b), group_norm(x, G, w, b), softmax(x) # autograd-aware versions
     y, rstd = fwd_f64(x64, w64); dx, dw = bwd_f64(dy64, x64, w64, rstd)   # float64 RMSNorm
 
 ``rounding="twice"`` is the Llama convention T(float(T(xhat)) * g); ``"once"`` is the Gemma
@@ -628,3 +629,87 @@ def rms_norm(x, w, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twic
     if _autograd_fn is None:
         _autograd_fn = _make_autograd()
     return _autograd_fn.apply(x, w, eps, offset, rounding, casts)
+
+
+def _make_autograd_widened():
+    torch = _torch()
+
+    def rows(t, n):
+        t2 = t.reshape(-1, n)
+        return t2 if t2.stride(-1) == 1 else t2.contiguous()
+
+    class LayerNormFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, w, b, eps):
+            shape = x.shape
+            x2 = rows(x, shape[-1])
+            y, mean, rstd = layernorm_fwd(x2, w, b, eps=eps)
+            ctx.save_for_backward(x2, w, mean, rstd)
+            ctx.cfg = (shape, b is not None)
+            return y.reshape(shape)
+
+        @staticmethod
+        def backward(ctx, gy):
+            x2, w, mean, rstd = ctx.saved_tensors
+            shape, has_b = ctx.cfg
+            dx, dw, db = layernorm_bwd(rows(gy, shape[-1]), x2, w, mean, rstd, bias=has_b)
+            return (dx.reshape(shape), dw.to(w.dtype), db.to(w.dtype) if has_b else None,
+                    None)
+
+    class GroupNormFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, G, w, b, eps):
+            xc = x.contiguous()
+            y, mean, rstd = groupnorm_fwd(xc, G, w, b, eps=eps)
+            ctx.save_for_backward(xc, w, mean, rstd)
+            ctx.cfg = (G, b is not None)
+            return y
+
+        @staticmethod
+        def backward(ctx, gy):
+            xc, w, mean, rstd = ctx.saved_tensors
+            G, has_b = ctx.cfg
+            dx, dw, db = groupnorm_bwd(gy.contiguous(), xc, G, w, mean, rstd, bias=has_b)
+            return dx, None, dw.to(w.dtype), db.to(w.dtype) if has_b else None, None
+
+    class SoftmaxFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x):
+            shape = x.shape
+            y = softmax_fwd(rows(x, shape[-1]))
+            ctx.save_for_backward(y)
+            ctx.shape = shape
+            return y.reshape(shape)
+
+        @staticmethod
+        def backward(ctx, gy):
+            (y,) = ctx.saved_tensors
+            return softmax_bwd(rows(gy, ctx.shape[-1]), y).reshape(ctx.shape)
+
+    return LayerNormFunction, GroupNormFunction, SoftmaxFunction
+
+
+_widened = None
+
+
+def _widened_fns():
+    global _widened
+    if _widened is None:
+        _widened = _make_autograd_widened()
+    return _widened
+
+
+def layer_norm(x, w, b=None, eps: float = 1e-5):
+    """Autograd-aware LayerNorm over the last dimension of ``x`` (weight required, bias optional);
+    the gradients of w and b come back in w's dtype (computed in float32)."""
+    return _widened_fns()[0].apply(x, w, b, eps)
+
+
+def group_norm(x, G: int, w, b=None, eps: float = 1e-5):
+    """Autograd-aware GroupNorm of ``x`` [B, C, *spatial] with G groups."""
+    return _widened_fns()[1].apply(x, G, w, b, eps)
+
+
+def softmax(x):
+    """Autograd-aware softmax over the last dimension of ``x``."""
+    return _widened_fns()[2].apply(x)
