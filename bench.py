@@ -427,6 +427,61 @@ def groupnorm_row(torch, rn, launches, rotate_mib):
             "passes": "fwd reads x twice (statistics, then normalize); bwd reads x and dy twice"}
 
 
+def row_cpu_baselines(budget_s):
+    """The oracle of each widened row, one NumPy thread, on a bounded sample of the same workload
+    (whole rows; GroupNorm on batch 0), forward + backward: algorithmic GB/s of the sample."""
+    import oracle
+    from workloads import (F64_WORKLOADS, GN_HEADLINE, GN_WORKLOADS, LN_WORKLOADS, SM_WORKLOADS,
+                           make_gn_inputs, make_inputs, make_norm_inputs)
+    out = {}
+
+    def timed(fn, nbytes_per_call, what):
+        calls, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s or calls == 0:
+            fn()
+            calls += 1
+        dt = time.perf_counter() - t0
+        return {"value": round(nbytes_per_call * calls / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                "kind": "oracle", "sample": f"{what}, {calls} passes in {dt:.1f} s"}
+
+    wl = LN_WORKLOADS["ln_bf16_4096x4096"]
+    rows = 64
+    inp = make_norm_inputs(wl, M=rows)
+
+    def ln():
+        y, m, r = oracle.layernorm_fwd(inp["x"], inp["w"], inp["b"], eps=wl.eps, dtype="bf16")
+        oracle.layernorm_bwd(inp["dy"], inp["x"], inp["w"], m, r, dtype="bf16")
+    s, N = 2, wl.N
+    out["layernorm"] = timed(ln, rows * (2 * N * s + 8) + rows * (3 * N * s + 8) + 4 * N * s,
+                             f"{rows} rows of {wl.name}")
+
+    wl = SM_WORKLOADS["sm_bf16_4096x4096"]
+    inp = make_inputs(wl, M=rows)
+
+    def sm():
+        y = oracle.softmax_fwd(inp["x"], dtype="bf16")
+        oracle.softmax_bwd(inp["dy"], y, dtype="bf16")
+    out["softmax"] = timed(sm, rows * 5 * wl.N * 2, f"{rows} rows of {wl.name}")
+
+    wl = GN_WORKLOADS[GN_HEADLINE]
+    inp = make_gn_inputs(wl, B=1)
+
+    def gn():
+        y, m, r = oracle.groupnorm_fwd(inp["x"], inp["w"], inp["b"], G=wl.G, eps=wl.eps,
+                                       dtype="bf16")
+        oracle.groupnorm_bwd(inp["dy"], inp["x"], inp["w"], m, r, G=wl.G, dtype="bf16")
+    out["groupnorm"] = timed(gn, 5 * wl.C * wl.S * 2, f"batch 0 of {wl.name}")
+
+    wl = F64_WORKLOADS["f64_4096x4096"]
+    inp = make_inputs(wl, M=rows)
+
+    def f64():
+        y, r = oracle.rmsnorm_fwd_f64(inp["x"], inp["w"], eps=wl.eps)
+        oracle.rmsnorm_bwd_f64(inp["dy"], inp["x"], inp["w"], r)
+    out["rmsnorm_f64"] = timed(f64, rows * 5 * wl.N * 8, f"{rows} rows of {wl.name}")
+    return out
+
+
 def cpu_baseline(wl, rounding, inp, budget_s):
     """The CPU oracle, single-threaded, over row chunks of the same inputs (cycling through the
     rows again if one pass takes less than the budget) until the time budget is used."""
@@ -564,8 +619,15 @@ def main(argv=None) -> int:
         line["rows"]["groupnorm"] = groupnorm_row(torch, rn, launches, args.rotate_mib)
         torch.cuda.empty_cache()
         line["rows"]["rmsnorm_f64"] = f64_row(torch, rn, launches, args.rotate_mib)
+    if "rows" in line:
+        for r in line["rows"].values():
+            r["fwd_frac_of_peak"] = round(r["fwd_GBps"] / PEAK_HBM_GBPS, 4)
+            r["bwd_frac_of_peak"] = round(r["bwd_GBps"] / PEAK_HBM_GBPS, 4)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(wl, rounding, inp, args.cpu_seconds)
+        if "rows" in line:
+            for k, v in row_cpu_baselines(min(1.5, args.cpu_seconds)).items():
+                line["rows"][k]["cpu_baseline"] = v
     print(json.dumps(line), flush=True)
     return 0
 
