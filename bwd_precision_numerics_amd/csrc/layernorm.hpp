@@ -72,9 +72,11 @@ __device__ __forceinline__ void add_centred_squares(const float (&f)[V], float m
   }
 }
 
-// Register kernel: the row (and w, b) stays in registers through the two reductions and the store.
+// Register kernel: the row stays in registers through the two reductions and the store. With
+// LATE_WB, w and b (cache-resident, shared by every row) are loaded in the store loop instead of
+// with x, so wider rows fit one wavefront without holding three row slices in registers.
 // LDS: two reduction slots of wpr floats per row group.
-template <DT D, int ITERS, bool HAS_B>
+template <DT D, int ITERS, bool HAS_B, bool LATE_WB = false>
 __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -93,7 +95,8 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
   const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
   const S* wr = static_cast<const S*>(a.w);
   const S* br = static_cast<const S*>(a.b);
-  Raw raw[ITERS], wraw[ITERS], braw[HAS_B ? ITERS : 1];
+  constexpr int WB = LATE_WB ? 1 : ITERS;
+  Raw raw[ITERS], wraw[WB], braw[HAS_B ? WB : 1];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
@@ -101,17 +104,23 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
     if (valid) {
       if (col + V <= N) {
         r = IO::load(xr + col);
-        rw = IO::load(wr + col);
-        if constexpr (HAS_B) rb = IO::load(br + col);
+        if constexpr (!LATE_WB) {
+          rw = IO::load(wr + col);
+          if constexpr (HAS_B) rb = IO::load(br + col);
+        }
       } else if (col < N) {
         r = IO::load_part(xr + col, N - col);
-        rw = IO::load_part(wr + col, N - col);
-        if constexpr (HAS_B) rb = IO::load_part(br + col, N - col);
+        if constexpr (!LATE_WB) {
+          rw = IO::load_part(wr + col, N - col);
+          if constexpr (HAS_B) rb = IO::load_part(br + col, N - col);
+        }
       }
     }
     raw[it] = r;
-    wraw[it] = rw;
-    if constexpr (HAS_B) braw[it] = rb;
+    if constexpr (!LATE_WB) {
+      wraw[it] = rw;
+      if constexpr (HAS_B) braw[it] = rb;
+    }
   }
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -147,8 +156,15 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
     if (col >= N) continue;
     float xf[V], wf[V], bf[V], yf[V];
     IO::unpack(raw[it], xf);
-    IO::unpack(wraw[it], wf);
-    if constexpr (HAS_B) IO::unpack(braw[it], bf);
+    if constexpr (LATE_WB) {
+      const bool full = col + V <= N;
+      IO::unpack(full ? IO::load(wr + col) : IO::load_part(wr + col, N - col), wf);
+      if constexpr (HAS_B)
+        IO::unpack(full ? IO::load(br + col) : IO::load_part(br + col, N - col), bf);
+    } else {
+      IO::unpack(wraw[it], wf);
+      if constexpr (HAS_B) IO::unpack(braw[it], bf);
+    }
     ln_affine<V, HAS_B>(xf, wf, bf, mean, rs, yf);
     store_out<D, Out::ONCE, true, V>(yr, col, N - col, a.yvec != 0, yf);
   }

@@ -10,7 +10,10 @@ using namespace rmsn;
 
 namespace {
 
-constexpr int kLnFwdMaxIters = 4;  // x, w and b of a row stay in registers through two reductions
+// Forward register kernel: one wavefront per row up to 8 vectors a thread (w and b then loaded
+// at the store), x, w and b all held up to 4.
+constexpr int kLnFwdMaxIters = 8;
+constexpr int kLnFwdEarlyWbIters = 4;
 constexpr int kLnBwdBlockThreads = 1024;
 constexpr int kLnBwdRegMaxIters = 2;
 // Rows in flight ahead of the current one, and whether xhat and w * dy are kept between the
@@ -70,11 +73,16 @@ rmsnorm_status ln_fwd_dispatch(const Plan& p, const LnFwdArgs& a, hipStream_t s)
     return p.wide ? launch(ln_fwd_stream_kernel<D, true, HAS_B>, p.grid, block, p.lds, s, a)
                   : launch(ln_fwd_stream_kernel<D, false, HAS_B>, p.grid, block, p.lds, s, a);
   }
+  static_assert(kLnFwdEarlyWbIters == 4, "cases below");
   switch (p.iters) {
     case 1: return launch(ln_fwd_rows_kernel<D, 1, HAS_B>, p.grid, block, p.lds, s, a);
     case 2: return launch(ln_fwd_rows_kernel<D, 2, HAS_B>, p.grid, block, p.lds, s, a);
     case 3: return launch(ln_fwd_rows_kernel<D, 3, HAS_B>, p.grid, block, p.lds, s, a);
     case 4: return launch(ln_fwd_rows_kernel<D, 4, HAS_B>, p.grid, block, p.lds, s, a);
+    case 5: return launch(ln_fwd_rows_kernel<D, 5, HAS_B, true>, p.grid, block, p.lds, s, a);
+    case 6: return launch(ln_fwd_rows_kernel<D, 6, HAS_B, true>, p.grid, block, p.lds, s, a);
+    case 7: return launch(ln_fwd_rows_kernel<D, 7, HAS_B, true>, p.grid, block, p.lds, s, a);
+    case 8: return launch(ln_fwd_rows_kernel<D, 8, HAS_B, true>, p.grid, block, p.lds, s, a);
     default: return RMSNORM_ERR_UNSUPPORTED;
   }
 }
