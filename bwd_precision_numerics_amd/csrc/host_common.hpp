@@ -9,6 +9,7 @@
 #include <cstdint>
 
 #include "../../include/librmsnorm.h"
+#include "rmsnorm_common.hpp"
 
 namespace {
 
@@ -85,6 +86,13 @@ void fwd_shape(int64_t nv, int* tpr, int* iters) {
     *tpr = (int)clamp64(pow2_ceil(ceil_div(nv, kFwdMaxIters)), 64, 1024);
   }
   *iters = (int)ceil_div(nv, *tpr);
+}
+
+// Compensated row sums in a streaming kernel: when a thread adds more than kPlainChainVectors
+// vectors (or elements) of a row. `wide` says whether the kernel moves 16-byte vectors.
+bool long_chain(int64_t N, rmsnorm_dtype dtype, bool wide, int tpr) {
+  const int64_t nv = wide ? ceil_div(N, vec_elems(dtype)) : N;
+  return ceil_div(nv, tpr) > rmsn::kPlainChainVectors;
 }
 
 // Backward: one 16-byte vector per thread up to 1024 vectors a row (8192 16-bit elements); wider

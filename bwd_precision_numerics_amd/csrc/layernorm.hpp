@@ -36,6 +36,7 @@ struct LnFwdArgs {
   int tpr;     // threads per row, multiple of 64
   int groups;  // rows per block
   int yvec;    // y and ldy allow 16-byte stores
+  int comp;    // streaming kernel: compensated row sums (long per-thread chains)
   float eps;
 };
 
@@ -54,20 +55,18 @@ __device__ __forceinline__ void ln_affine(const float (&xf)[V], const float (&wf
 // Centred squares of the valid elements of one vector (elements at or past N excluded).
 template <int V>
 __device__ __forceinline__ void add_centred_squares(const float (&f)[V], float mean, int n,
-                                                    float& q0, float& q1) {
+                                                    RowAcc& q, bool comp) {
   if (n >= V) {
 #pragma unroll
-    for (int e = 0; e < V; e += 2) {
-      const float d0 = f[e] - mean, d1 = f[e + 1] - mean;
-      q0 = __builtin_fmaf(d0, d0, q0);
-      q1 = __builtin_fmaf(d1, d1, q1);
+    for (int e = 0; e < V; ++e) {
+      const float d = f[e] - mean;
+      q.fma(e, d, d, comp);
     }
   } else {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       const float d = e < n ? f[e] - mean : 0.f;
-      if (e & 1) q1 = __builtin_fmaf(d, d, q1);
-      else q0 = __builtin_fmaf(d, d, q0);
+      q.fma(e, d, d, comp);
     }
   }
 }
@@ -134,15 +133,15 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
     }
   }
   const float mean = group_sum(s0 + s1, red, wpr, tl) / (float)N;
-  float q0 = 0.f, q1 = 0.f;
+  RowAcc q;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
     float f[V];
     IO::unpack(raw[it], f);
-    add_centred_squares<V>(f, mean, N - col, q0, q1);
+    add_centred_squares<V>(f, mean, N - col, q, false);
   }
-  const float var = group_sum(q0 + q1, red + wpr, wpr, tl) / (float)N;
+  const float var = group_sum(q.total(), red + wpr, wpr, tl) / (float)N;
   const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
   if (!valid) return;
   if (tl == 0) {
@@ -189,30 +188,28 @@ __global__ void __launch_bounds__(1024) ln_fwd_stream_kernel(LnFwdArgs a) {
   float* red = reinterpret_cast<float*>(smem) + grp * 2 * wpr;
   const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
 
-  float s0 = 0.f, s1 = 0.f;
+  const bool comp = a.comp != 0;
+  RowAcc sx;
   if (valid) {
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       float f[V];
       IO::unpack(col + V <= N ? IO::load(xr + col) : IO::load_part(xr + col, N - col), f);
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        if (e & 1) s1 += f[e];
-        else s0 += f[e];
-      }
+      for (int e = 0; e < V; ++e) sx.add(e, f[e], comp);
     }
   }
-  const float mean = group_sum(s0 + s1, red, wpr, tl) / (float)N;
-  float q0 = 0.f, q1 = 0.f;
+  const float mean = group_sum(sx.total(), red, wpr, tl) / (float)N;
+  RowAcc q;
   if (valid) {
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       float f[V];
       IO::unpack(col + V <= N ? IO::load(xr + col) : IO::load_part(xr + col, N - col), f);
-      add_centred_squares<V>(f, mean, N - col, q0, q1);
+      add_centred_squares<V>(f, mean, N - col, q, comp);
     }
   }
-  const float var = group_sum(q0 + q1, red + wpr, wpr, tl) / (float)N;
+  const float var = group_sum(q.total(), red + wpr, wpr, tl) / (float)N;
   const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
   if (!valid) return;
   if (tl == 0) {
@@ -247,6 +244,7 @@ struct LnBwdArgs {
   int N, ldp, P;
   int tpr;     // threads per row, multiple of 64
   int groups;  // rows processed concurrently per block
+  int comp;    // streaming kernel: compensated row sums (long per-thread chains)
 };
 
 // Register kernel on the persistent grid of the RMSNorm backward (block b owns rows b, b + P, ...).
@@ -442,7 +440,8 @@ __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
     const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
     const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
     const float mu = a.mean[row], rs = a.rstd[row];
-    float d1a = 0.f, d1b = 0.f, d2a = 0.f, d2b = 0.f;
+    const bool comp = a.comp != 0;
+    RowAcc d1, d2;
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       const bool full = col + V <= N;
@@ -454,16 +453,11 @@ __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
       for (int e = 0; e < V; ++e) {
         const float xh = (xf[e] - mu) * rs;
         const float gd = wf[e] * df[e];
-        if (e & 1) {
-          d1b += gd;
-          d2b = __builtin_fmaf(gd, xh, d2b);
-        } else {
-          d1a += gd;
-          d2a = __builtin_fmaf(gd, xh, d2a);
-        }
+        d1.add(e, gd, comp);
+        d2.fma(e, gd, xh, comp);
       }
     }
-    float dots[2] = {d1a + d1b, d2a + d2b};
+    float dots[2] = {d1.total(), d2.total()};
     group_sum_batch<2>(dots, red + (s & 1) * wpr * 2, wpr, tl);
     const float c1 = dots[0] / (float)N, c2 = dots[1] / (float)N;
     S* dxr = static_cast<S*>(a.dx) + row * a.lddx;

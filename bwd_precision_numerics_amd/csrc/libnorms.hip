@@ -122,6 +122,7 @@ rmsnorm_status ln_fwd_impl(const void* x, int64_t ldx, const void* w, const void
   a.ldx = ldx; a.ldy = ldy; a.M = M; a.N = (int)N;
   a.tpr = p.tpr; a.groups = p.groups; a.eps = eps;
   a.yvec = wide_fits(y, ldy, eb);
+  a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return b ? ln_fwd_by_dtype<true>(dtype, p, a, s) : ln_fwd_by_dtype<false>(dtype, p, a, s);
 }
@@ -239,6 +240,7 @@ rmsnorm_status ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t 
     a.lddy = lddy; a.ldx = ldx; a.lddx = lddx; a.M = M;
     a.N = (int)N; a.ldp = (int)partial_ld(N); a.P = (int)P;
     a.tpr = p.tpr; a.groups = p.groups;
+    a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
     st = db ? ln_bwd_by_dtype<true>(dtype, p, a, s) : ln_bwd_by_dtype<false>(dtype, p, a, s);
     if (st != RMSNORM_OK) return st;
   }

@@ -170,6 +170,7 @@ rmsnorm_status fwd_impl(const void* x, int64_t ldx, const void* w, void* y, int6
   a.ldx = ldx; a.ldy = ldy; a.M = M; a.N = (int)N;
   a.tpr = p.tpr; a.groups = p.groups; a.eps = eps; a.offset = offset; a.scale = scale;
   a.yvec = aligned(y, (uintptr_t)yvec) && (ldy * yb) % yvec == 0;
+  a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (out) {
     case Out::ONCE: return fwd_by_dtype<Out::ONCE>(dtype, p, a, s);
@@ -232,6 +233,7 @@ rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_
   a.lddy = lddy; a.ldx = ldx; a.lddx = lddx; a.M = M;
   a.N = (int)N; a.ldp = (int)partial_ld(N); a.P = (int)num_partials(M);
   a.tpr = p.tpr; a.groups = p.groups; a.offset = offset;
+  a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool ag = autograd_casts(rounding, dtype);
   switch (dtype) {

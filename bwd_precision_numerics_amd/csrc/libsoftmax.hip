@@ -84,6 +84,7 @@ rmsnorm_status sm_impl(const void* a_in, int64_t lda, const void* dy, int64_t ld
   a.x = a_in; a.dy = dy; a.out = out;
   a.ldx = lda; a.lddy = lddy; a.ldo = ldo; a.M = M; a.N = (int)N;
   a.tpr = p.tpr; a.groups = p.groups;
+  a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case RMSNORM_DTYPE_F32: return sm_dispatch<DT::F32, FWD>(p, a, s);

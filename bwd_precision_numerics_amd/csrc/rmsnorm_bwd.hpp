@@ -46,6 +46,7 @@ struct BwdArgs {
   int N, ldp, P;
   int tpr;     // threads per row, multiple of 64
   int groups;  // rows processed concurrently per block
+  int comp;    // streaming kernel: compensated row sums (long per-thread chains)
   float offset;
 };
 
@@ -416,7 +417,7 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
     const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
     const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
     const float rs = a.rstd[row];
-    float d0 = 0.f, d1 = 0.f;
+    RowAcc d;
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       const bool full = col + V <= N;
@@ -428,11 +429,10 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
       for (int e = 0; e < V; ++e) {
         const float xh = xf[e] * rs;
         const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
-        if (e & 1) d1 = __builtin_fmaf(gd, xh, d1);
-        else d0 = __builtin_fmaf(gd, xh, d0);
+        d.fma(e, gd, xh, a.comp != 0);
       }
     }
-    const float dot = group_sum(d0 + d1, red + (s & 1) * wpr, wpr, tl);
+    const float dot = group_sum(d.total(), red + (s & 1) * wpr, wpr, tl);
     const float c = dot / (float)N;
     S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
     for (int v = tl; v < nv; v += TPR) {

@@ -197,6 +197,37 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// A thread's share of a row sum in two interleaved float32 accumulators (even / odd elements of a
+// vector). Chains of at most kPlainChainVectors vectors per thread add plainly, in the order the
+// register kernels use; longer chains (the streaming kernels on very wide rows) set `comp` and
+// compensate every addition (Kahan: c carries the low-order part lost so far), so that a row of
+// 2^24 elements keeps its float32 sums within a few ulps of the exact value instead of drifting by
+// about sqrt(chain length) ulps.
+constexpr int kPlainChainVectors = 8;
+struct RowAcc {
+  float s0 = 0.f, s1 = 0.f, c0 = 0.f, c1 = 0.f;
+  static __device__ __forceinline__ void kahan(float& s, float& c, float v) {
+    const float y = v - c;
+    const float t = s + y;
+    c = (t - s) - y;
+    s = t;
+  }
+  // s += v for element parity e
+  __device__ __forceinline__ void add(int e, float v, bool comp) {
+    float& s = (e & 1) ? s1 : s0;
+    if (comp) kahan(s, (e & 1) ? c1 : c0, v);
+    else s += v;
+  }
+  // s += a * b (one fused multiply-add on the plain path)
+  __device__ __forceinline__ void fma(int e, float a, float b, bool comp) {
+    float& s = (e & 1) ? s1 : s0;
+    if (comp) kahan(s, (e & 1) ? c1 : c0, a * b);
+    else s = __builtin_fmaf(a, b, s);
+  }
+  // s0 + s1 on the plain path (c0 = c1 = 0), bit for bit
+  __device__ __forceinline__ float total() const { return (s0 + s1) - (c0 + c1); }
+};
+
 // Workgroup barrier that orders LDS only: outstanding global loads stay in flight across it, so a
 // row prefetched before the barrier keeps streaming while the current row is reduced.
 __device__ __forceinline__ void lds_barrier() {

@@ -33,6 +33,7 @@ struct FwdArgs {
   int tpr;     // threads per row, multiple of 64
   int groups;  // rows per block
   int yvec;    // y and ldy allow one vector store per 16-byte input vector
+  int comp;    // streaming kernel: compensated row sums (long per-thread chains)
   float eps, offset, scale;
 };
 
@@ -188,7 +189,8 @@ __global__ void __launch_bounds__(1024) fwd_stream_kernel(FwdArgs a) {
   float* red = reinterpret_cast<float*>(smem) + grp * wpr;
 
   const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
-  float acc0 = 0.f, acc1 = 0.f;
+  const bool comp = a.comp != 0;
+  RowAcc acc;
   if (valid) {
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
@@ -196,13 +198,10 @@ __global__ void __launch_bounds__(1024) fwd_stream_kernel(FwdArgs a) {
       float f[V];
       IO::unpack(r, f);
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        if (e & 1) acc1 = __builtin_fmaf(f[e], f[e], acc1);
-        else acc0 = __builtin_fmaf(f[e], f[e], acc0);
-      }
+      for (int e = 0; e < V; ++e) acc.fma(e, f[e], f[e], comp);
     }
   }
-  const float ss = group_sum(acc0 + acc1, red, wpr, tl);
+  const float ss = group_sum(acc.total(), red, wpr, tl);
   const float rs = 1.0f / __builtin_sqrtf(ss / (float)N + a.eps);
   if (!valid) return;
   if (tl == 0 && a.rstd) a.rstd[row] = rs;

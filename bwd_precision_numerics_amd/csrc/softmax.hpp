@@ -118,7 +118,21 @@ struct SmArgs {
   int64_t ldx, lddy, ldo, M;
   int N;
   int tpr, groups;
+  int comp;  // streaming kernels: compensated float32 row sums (long per-thread chains)
 };
+
+// Two interleaved accumulators in the compute type; float sums of long chains are compensated
+// (RowAcc), float64 sums are plain (a float64 chain of 2^24 terms stays far inside the tolerance).
+template <typename A> struct SmAcc {
+  A s0 = 0, s1 = 0;
+  __device__ __forceinline__ void add(int e, A v, bool) { (e & 1 ? s1 : s0) += v; }
+  __device__ __forceinline__ void fma(int e, A x, A y, bool) {
+    A& s = e & 1 ? s1 : s0;
+    s = ::fma(x, y, s);
+  }
+  __device__ __forceinline__ A total() const { return s0 + s1; }
+};
+template <> struct SmAcc<float> : RowAcc {};
 
 // Forward. Register kernel (ITERS > 0: the row's exp values stay in registers between the
 // reductions and the store) or streaming (ITERS = 0: each pass reads x again from the caches).
@@ -182,19 +196,16 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
       }
     }
   } else if (valid) {
+    SmAcc<A> acc;
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       A f[V];
       IO::unpack(IO::load(xr + col, N - col), f);
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        if (col + e < N) {
-          const A t = exp_a(f[e] - mx);
-          if (e & 1) s1 += t;
-          else s0 += t;
-        }
-      }
+      for (int e = 0; e < V; ++e)
+        if (col + e < N) acc.add(e, exp_a(f[e] - mx), a.comp != 0);
     }
+    s0 = acc.total();
   }
   const A sum = group_reduce<false>(s0 + s1, red + wpr, wpr, tl);
   if (!valid) return;
@@ -272,17 +283,16 @@ __global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
       }
     }
   } else if (valid) {
+    SmAcc<A> acc;
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       A yf[V], df[V];
       IO::unpack(IO::load(yr + col, N - col), yf);
       IO::unpack(IO::load(dr + col, N - col), df);
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        if (e & 1) s1 = fma(df[e], yf[e], s1);
-        else s0 = fma(df[e], yf[e], s0);
-      }
+      for (int e = 0; e < V; ++e) acc.fma(e, df[e], yf[e], a.comp != 0);
     }
+    s0 = acc.total();
   }
   const A s = group_reduce<false>(s0 + s1, red, wpr, tl);
   if (!valid) return;
