@@ -20,10 +20,10 @@
 //             chunk, reading x a second time.
 //   backward  gn_bwd_sums_kernel writes each chunk's (sum dy, sum dy * xhat); gn_bwd_dx_kernel
 //             merges c1 = sum_c w_c * (sum dy) and c2 = sum_c w_c * (sum dy * xhat) over the row and
-//             writes dx; gn_param_kernel adds the same per-chunk sums over batch and chunks into
-//             dW_c and dB_c. Since w_c is constant over a chunk, w_c * sum(dy) is the row sum of
-//             w_c * dy up to float32 rounding order, and one pair of sums per chunk serves both the
-//             row constants and the parameter gradients.
+//             writes dx; one block per channel also adds the same per-chunk sums over batch and
+//             chunks into dW_c and dB_c. Since w_c is constant over a chunk, w_c * sum(dy) is the
+//             row sum of w_c * dy up to float32 rounding order, and one pair of sums per chunk
+//             serves both the row constants and the parameter gradients.
 #pragma once
 
 #include "rmsnorm_common.hpp"
@@ -44,7 +44,7 @@ struct GnArgs {
   float* mean;      // [B * G]
   float* rstd;      // [B * G]
   float2* ws;       // [B * C * K] per-chunk pairs
-  float* dw;        // [C] (parameter kernel)
+  float* dw;        // [C]
   float* db;        // [C] or null
   int64_t B, C, S;
   int G, Cg, K;     // groups, channels per group, chunks per (batch, channel) segment
@@ -256,6 +256,32 @@ __global__ void __launch_bounds__(kGnThreads) gn_bwd_sums_kernel(GnArgs a) {
   if (threadIdx.x == 0) a.ws[blockIdx.x] = make_float2(sdy, sdx);
 }
 
+// dW_c = sum over (batch, chunk) of sum(dy * xhat), dB_c of sum(dy), by one wavefront: lane-strided
+// sequential sums then a fixed shuffle tree.
+__device__ __forceinline__ void gn_param_sums(const GnArgs& a, int64_t c) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nent = a.B * a.K;
+  float u1 = 0.f, u2 = 0.f;
+  for (int64_t e = lane; e < nent; e += 64) {
+    const int64_t bidx = e / a.K, k = e - bidx * a.K;
+    const float2 v = a.ws[(bidx * a.C + c) * a.K + k];
+    u1 += v.x;
+    u2 += v.y;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o1 = __shfl_down(u1, off, 64), o2 = __shfl_down(u2, off, 64);
+    if (lane < off) {
+      u1 += o1;
+      u2 += o2;
+    }
+  }
+  if (lane == 0) {
+    a.dw[c] = u2;
+    if (a.db) a.db[c] = u1;
+  }
+}
+
 // Backward pass 2: row constants from the chunk sums (fixed order), then dx for the chunk.
 template <DT D, bool WIDE>
 __global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
@@ -297,6 +323,9 @@ __global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
       cst[1] = u2 / n;
     }
   }
+  // The first chunk of batch 0 of each channel also sums that channel's dW and dB in its second
+  // wavefront (the per-chunk sums are complete since the previous kernel).
+  if (ch.bidx == 0 && ch.k == 0 && threadIdx.x >= 64 && threadIdx.x < 128) gn_param_sums(a, ch.c);
   __syncthreads();
   const float c1 = cst[0], c2 = cst[1];
   const float wc = to_f32<D>(wp[ch.c]);
@@ -316,34 +345,6 @@ __global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
     const auto out = IO::pack(o);
     if (col + V <= ch.cnt) IO::store(dxp + col, out);
     else IO::store_part(dxp + col, out, ch.cnt - col);
-  }
-}
-
-// dW_c = sum over (batch, chunk) of sum(dy * xhat), dB_c of sum(dy): one wavefront per channel,
-// lane-strided sequential sums then a fixed shuffle tree.
-__global__ void __launch_bounds__(256) gn_param_kernel(GnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= a.C) return;  // whole wavefronts leave together
-  const int64_t nent = a.B * a.K;
-  float u1 = 0.f, u2 = 0.f;
-  for (int64_t e = lane; e < nent; e += 64) {
-    const int64_t bidx = e / a.K, k = e - bidx * a.K;
-    const float2 v = a.ws[(bidx * a.C + c) * a.K + k];
-    u1 += v.x;
-    u2 += v.y;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o1 = __shfl_down(u1, off, 64), o2 = __shfl_down(u2, off, 64);
-    if (lane < off) {
-      u1 += o1;
-      u2 += o2;
-    }
-  }
-  if (lane == 0) {
-    a.dw[c] = u2;
-    if (a.db) a.db[c] = u1;
   }
 }
 

@@ -307,8 +307,7 @@ rmsnorm_status gn_bwd_launch(const GnArgs& a, int64_t chunks, hipStream_t s) {
   hipLaunchKernelGGL((gn_bwd_sums_kernel<D, WIDE>), dim3((unsigned)chunks), dim3(kGnThreads), 0,
                      s, a);
   hipLaunchKernelGGL((gn_bwd_dx_kernel<D, WIDE>), dim3((unsigned)chunks), dim3(kGnThreads), 0, s,
-                     a);
-  hipLaunchKernelGGL(gn_param_kernel, dim3((unsigned)ceil_div(a.C, 4)), dim3(256), 0, s, a);
+                     a);  // also writes dW, dB
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
 }
 
