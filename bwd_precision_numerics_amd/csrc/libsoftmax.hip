@@ -10,22 +10,37 @@ using namespace rmsn;
 
 namespace {
 
-constexpr int kSmMaxIters = 4;  // 16-byte vectors per thread in the register kernels
+// 16-byte vectors per thread in the register kernels: at most 4 (the backward keeps y and dy,
+// the forward one float per element plus the code for partial vectors), and 8 for forward rows
+// that the threads' vectors tile exactly (N = iters * tpr * 16 / element size: a 4096-wide 16-bit
+// row is then one wavefront with no LDS round).
+constexpr int kSmMaxIters = 4;
+constexpr int kSmFwdFullMaxIters = 8;
+// Threads per block: the forward's row groups share a block's barriers, so it stays small; the
+// backward was measured faster with 1024.
+constexpr int kSmFwdBlockThreads = 256;
+constexpr int kSmBwdBlockThreads = 1024;
 
 bool sm_dtype_ok(int d) { return dtype_ok(d) || d == RMSNORM_DTYPE_F64; }
 
-// Threads per row for a row of nv vectors (or elements): at most kSmMaxIters per thread.
-void sm_shape(int64_t nv, int* tpr, int* iters) {
-  *tpr = (int)clamp64(pow2_ceil(ceil_div(nv, kSmMaxIters)), 64, 1024);
+// Threads per row for a row of nv vectors (or elements): at most max_iters per thread.
+void sm_shape(int64_t nv, int max_iters, int* tpr, int* iters) {
+  *tpr = (int)clamp64(pow2_ceil(ceil_div(nv, max_iters)), 64, 1024);
   *iters = (int)ceil_div(nv, *tpr);
 }
 
+// Shape of a forward or backward row. Both kernel families of one direction take the same shape
+// for the same N and dtype, so with 16-byte vectors they map elements to threads identically.
 rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
-                       rmsnorm_variant req, size_t acc_bytes, int slots, Plan* p) {
+                       rmsnorm_variant req, size_t acc_bytes, int slots, bool fwd, Plan* p) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
-  int tpr, iters;
-  sm_shape(nv_wide, &tpr, &iters);
-  const bool reg_ok = wide_ok && iters <= kSmMaxIters;
+  int tpr, iters, max_iters = kSmMaxIters;
+  if (fwd) {
+    sm_shape(nv_wide, kSmFwdFullMaxIters, &tpr, &iters);
+    if ((int64_t)iters * tpr * vec_elems(dtype) == N) max_iters = kSmFwdFullMaxIters;
+  }
+  sm_shape(nv_wide, max_iters, &tpr, &iters);
+  const bool reg_ok = wide_ok && iters <= max_iters;
   rmsnorm_variant v = req;
   if (v == RMSNORM_VARIANT_AUTO) v = reg_ok ? RMSNORM_VARIANT_REGISTERS : RMSNORM_VARIANT_STREAMING;
   if (v == RMSNORM_VARIANT_LDS || (v == RMSNORM_VARIANT_REGISTERS && !reg_ok))
@@ -33,12 +48,13 @@ rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   p->variant = v;
   p->wide = v == RMSNORM_VARIANT_REGISTERS || wide_ok;
   if (v == RMSNORM_VARIANT_STREAMING) {
-    sm_shape(wide_ok ? nv_wide : N, &tpr, &iters);
+    sm_shape(wide_ok ? nv_wide : N, max_iters, &tpr, &iters);
     iters = 0;
   }
   p->tpr = tpr;
   p->iters = iters;
-  p->groups = tpr >= kFwdBlockThreads ? 1 : kFwdBlockThreads / tpr;
+  const int bt = fwd ? kSmFwdBlockThreads : kSmBwdBlockThreads;
+  p->groups = tpr >= bt ? 1 : bt / tpr;
   p->lds = round16(acc_bytes * slots * (size_t)p->groups * (tpr / 64));
   p->grid = ceil_div(M, p->groups);
   if (p->grid > INT32_MAX) return RMSNORM_ERR_UNSUPPORTED;
@@ -48,6 +64,24 @@ rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
 template <DT D, bool FWD>
 rmsnorm_status sm_dispatch(const Plan& p, const SmArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
+  if constexpr (FWD) {
+    constexpr int V = 16 / (int)sizeof(typename Elem<D>::S);
+    if (p.variant != RMSNORM_VARIANT_STREAMING && (int64_t)p.iters * p.tpr * V == a.N) {
+#define RMSN_SMF(IT) launch(softmax_fwd_kernel<D, true, IT, true>, p.grid, block, p.lds, s, a)
+      switch (p.iters) {
+        case 1: return RMSN_SMF(1);
+        case 2: return RMSN_SMF(2);
+        case 3: return RMSN_SMF(3);
+        case 4: return RMSN_SMF(4);
+        case 5: return RMSN_SMF(5);
+        case 6: return RMSN_SMF(6);
+        case 7: return RMSN_SMF(7);
+        case 8: return RMSN_SMF(8);
+        default: return RMSNORM_ERR_UNSUPPORTED;
+      }
+#undef RMSN_SMF
+    }
+  }
 #define RMSN_SM(W, IT)                                                                          \
   (FWD ? launch(softmax_fwd_kernel<D, W, IT>, p.grid, block, p.lds, s, a)                       \
        : launch(softmax_bwd_kernel<D, W, IT>, p.grid, block, p.lds, s, a))
@@ -78,7 +112,8 @@ rmsnorm_status sm_impl(const void* a_in, int64_t lda, const void* dy, int64_t ld
                     (FWD || wide_fits(dy, lddy, eb));
   const size_t acc = dtype == RMSNORM_DTYPE_F64 ? 8 : 4;
   Plan p;
-  if ((st = plan_sm(M, N, dtype, wide, variant, acc, FWD ? 3 : 1, &p)) != RMSNORM_OK) return st;
+  if ((st = plan_sm(M, N, dtype, wide, variant, acc, FWD ? 3 : 1, FWD, &p)) != RMSNORM_OK)
+    return st;
   if (M == 0) return RMSNORM_OK;
   SmArgs a;
   a.x = a_in; a.dy = dy; a.out = out;
@@ -113,7 +148,7 @@ rmsnorm_status f64_fwd_impl(const double* x, int64_t ldx, const double* w, doubl
   if (!aligned(w, 8) || !aligned(rstd, 8)) return RMSNORM_ERR_MISALIGNED;
   const bool wide = wide_fits(x, ldx, 8) && wide_fits(y, ldy, 8) && aligned(w, 16);
   int tpr, iters;
-  sm_shape(wide ? ceil_div(N, 2) : N, &tpr, &iters);
+  sm_shape(wide ? ceil_div(N, 2) : N, kSmMaxIters, &tpr, &iters);
   const bool regs = wide && iters <= kSmMaxIters;
   const int groups = tpr >= kFwdBlockThreads ? 1 : kFwdBlockThreads / tpr;
   const int64_t grid = ceil_div(M, groups);

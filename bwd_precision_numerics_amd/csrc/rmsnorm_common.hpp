@@ -197,6 +197,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Maximum over the 64 lanes with the same moves; here a lane without a source keeps its own value
+// (max(v, v) = v) instead of reading 0. Every lane gets lane 63's result.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_keep(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_keep<0xb1, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x4e, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x114, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x118, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+  v = fmaxf(v, dpp_keep<0x143, 0xc>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // A thread's share of a row sum in two interleaved float32 accumulators (even / odd elements of a
 // vector). Chains of at most kPlainChainVectors vectors per thread add plainly, in the order the
 // register kernels use; longer chains (the streaming kernels on very wide rows) set `comp` and

@@ -8,7 +8,11 @@
 //
 //   forward   m = max_j x_j,  e_j = exp(x_j - m),  y_j = T(e_j * r),  r = 1 / sum_k e_k
 // (one division per row; each y is within about three float32 ulps of the exact quotient before
-// the cast, against nine vector instructions per element for an IEEE division)
+// the cast, against nine vector instructions per element for an IEEE division). The float32 exp
+// is the device library's, or on rows whose every e_j is a normal float32 a shorter evaluation of
+// the same function to about two ulps (exp_row_normal below): the library's range reduction and
+// its over- and underflow handling cost more vector instructions per element than the memory
+// traffic leaves room for.
 //   backward  s = sum_j dy_j * y_j,  dx_j = T(y_j * (dy_j - s))
 //
 // A is the compute type: float for float32 / float16 / bfloat16 I/O, double for float64.
@@ -91,13 +95,18 @@ template <typename A> __device__ __forceinline__ A wave_max_x(A v) {
   for (int m = 1; m < 64; m <<= 1) v = fmax(v, shfl_xor_any(v, m));
   return v;
 }
+// float: the DPP reductions (register moves, result broadcast from lane 63); double: butterflies.
+__device__ __forceinline__ float wave_sum_a(float v) { return wave_sum(v); }
+__device__ __forceinline__ double wave_sum_a(double v) { return wave_sum_x(v); }
+__device__ __forceinline__ float wave_max_a(float v) { return wave_max(v); }
+__device__ __forceinline__ double wave_max_a(double v) { return wave_max_x(v); }
 
 // Sum (MAX = false) or maximum over the TPR = 64 * wpr threads of a row group: waves publish their
 // results in red[wave] and every thread combines them in wave order. Every thread of the block
 // must call it when wpr > 1.
 template <bool MAX, typename A>
 __device__ __forceinline__ A group_reduce(A v, A* red, int wpr, int tl) {
-  v = MAX ? wave_max_x(v) : wave_sum_x(v);
+  v = MAX ? wave_max_a(v) : wave_sum_a(v);
   if (wpr > 1) {
     if ((tl & 63) == 0) red[tl >> 6] = v;
     lds_barrier();
@@ -110,6 +119,48 @@ __device__ __forceinline__ A group_reduce(A v, A* red, int wpr, int tl) {
 // exp in the compute type (the accurate device library functions).
 __device__ __forceinline__ float exp_a(float v) { return expf(v); }
 __device__ __forceinline__ double exp_a(double v) { return exp(v); }
+
+// exp(v) for -kSmNormalSpan < v <= 0, where the result is a normal float32. Method: a two-term
+// (Cody-Waite style) split of the exponent. v * log2(e) = hi + lo with hi = fl(v * L),
+// L = fl32(log2 e); the fma yields the rounding error of that product exactly, and v * Llo adds
+// the part of log2(e) that L leaves out. The hardware base-2 exponential (v_exp_f32, about one
+// ulp for normal results; it flushes results below 2^-126, hence the span) gives 2^hi, and
+// 2^lo = 1 + lo * ln 2 + O(lo^2) with |lo| < 2^-16 leaves a second-order term below 2^-33.
+// Emulated on the CPU with a correctly rounded 2^hi the error is at most 1.0 ulp; with the
+// hardware's, about two. No special values: callers use it only on rows known to qualify.
+constexpr float kSmNormalSpan = 87.0f;  // exp(-87) = 1.6e-38 > 2^-126
+__device__ __forceinline__ float exp_row_normal(float v) {
+  constexpr float kL = 0x1.715476p+0f;     // log2(e) rounded to float32
+  constexpr float kLlo = 0x1.4ae0cp-26f;   // log2(e) - kL, rounded to float32
+  constexpr float kLn2 = 0x1.62e43p-1f;    // ln(2) rounded to float32
+  const float hi = v * kL;
+  const float lo = __builtin_fmaf(v, kLlo, __builtin_fmaf(v, kL, -hi));
+  const float p = __builtin_amdgcn_exp2f(hi);
+  return __builtin_fmaf(p, lo * kLn2, p);
+}
+
+// Max of u and of v over the TPR threads of a row group in one LDS round: red holds 2 * wpr
+// slots. Every thread of the block must call it when wpr > 1.
+template <typename A>
+__device__ __forceinline__ void group_max2(A& u, A& v, A* red, int wpr, int tl) {
+  u = wave_max_a(u);
+  v = wave_max_a(v);
+  if (wpr > 1) {
+    if ((tl & 63) == 0) {
+      red[tl >> 6] = u;
+      red[wpr + (tl >> 6)] = v;
+    }
+    lds_barrier();
+    u = red[0];
+    v = red[wpr];
+    for (int k = 1; k < wpr; ++k) {
+      u = fmax(u, red[k]);
+      v = fmax(v, red[wpr + k]);
+    }
+  }
+}
+
+template <bool B> struct Flag { static constexpr bool value = B; };
 
 struct SmArgs {
   const void* x;   // forward input, or the forward's output y (backward)
@@ -136,13 +187,22 @@ template <> struct SmAcc<float> : RowAcc {};
 
 // Forward. Register kernel (ITERS > 0: the row's exp values stay in registers between the
 // reductions and the store) or streaming (ITERS = 0: each pass reads x again from the caches).
-// LDS: three reduction slots of wpr compute-type values per row group.
-template <DT D, bool WIDE, int ITERS>
+// FULL (register kernel): the host has checked that N = ITERS * TPR * V, so every vector of every
+// thread lies inside the row and the kernel carries no code for partial vectors or padding (that
+// code alone would push the 8-vector kernel past its register budget).
+// The max pass also finds the row's minimum: when max - min < kSmNormalSpan (false for rows with
+// infinities or only NaN), every e_j is a normal float32 and the float32 kernels use
+// exp_row_normal, else the library exp. The choice is made per row from exact values, so the two
+// kernel families take the same one. LDS: three reduction slots of wpr compute-type values per
+// row group (max and -min, then the sum).
+template <DT D, bool WIDE, int ITERS, bool FULL = false>
 __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   using A = typename Acc<D>::A;
   using IO = NumIO<D, WIDE>;
   using S = typename IO::S;
   constexpr int V = IO::V;
+  constexpr bool F32 = sizeof(A) == 4;
+  static_assert(!FULL || (ITERS > 0 && WIDE), "FULL applies to the register kernel");
   extern __shared__ uint4 smem[];
   const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
   const int nv = (N + V - 1) / V;
@@ -152,44 +212,74 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
   const bool valid = row < a.M;
   A* red = reinterpret_cast<A*>(smem) + grp * 3 * wpr;
+  // Rows past M read row 0 (in bounds) and store nothing.
   const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
   constexpr int R = ITERS > 0 ? ITERS : 1;
   A ev[R][V];
 
-  A mx = -INFINITY;
+  A mx = -INFINITY, nmn = -INFINITY;  // max and -min over the row
   if constexpr (ITERS > 0) {
+    if constexpr (FULL) {
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int col = (it * TPR + tl) * V;
-      A f[V];
-      if (valid && col < N) {
-        IO::unpack(IO::load(xr + col, N - col), f);
+      for (int it = 0; it < ITERS; ++it) {
+        const int col = (it * TPR + tl) * V;
+        IO::unpack(IO::load(xr + col, V), ev[it]);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          mx = fmax(mx, ev[it][e]);
+          if constexpr (F32) nmn = fmax(nmn, -ev[it][e]);
+        }
       }
+    } else {
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        ev[it][e] = (valid && col + e < N) ? f[e] : (A)-INFINITY;
-        mx = fmax(mx, ev[it][e]);
+      for (int it = 0; it < ITERS; ++it) {
+        const int col = (it * TPR + tl) * V;
+        A f[V];
+        if (col < N) IO::unpack(IO::load(xr + col, N - col), f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const bool in = col + e < N;
+          ev[it][e] = in ? f[e] : (A)-INFINITY;
+          mx = fmax(mx, ev[it][e]);
+          if constexpr (F32) nmn = fmax(nmn, in ? -f[e] : (A)-INFINITY);
+        }
       }
     }
-  } else if (valid) {
+  } else {
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       A f[V];
       IO::unpack(IO::load(xr + col, N - col), f);
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        if (col + e < N) mx = fmax(mx, f[e]);
+        if (col + e < N) {
+          mx = fmax(mx, f[e]);
+          if constexpr (F32) nmn = fmax(nmn, -f[e]);
+        }
     }
   }
-  mx = group_reduce<true>(mx, red, wpr, tl);
+  if constexpr (F32) group_max2(mx, nmn, red, wpr, tl);
+  else mx = group_reduce<true>(mx, red, wpr, tl);
+  const bool fast = F32 && mx + nmn < (A)kSmNormalSpan;
+  auto ex = [&](auto fast_tag, A v) -> A {
+    if constexpr (F32 && decltype(fast_tag)::value) return exp_row_normal(v);
+    else return exp_a(v);
+  };
 
+  // The register kernels keep the row only on the short-exp path. Otherwise they, like the
+  // streaming kernel, read x again for the sum and for the store (from the caches), with the same
+  // element-to-thread mapping and order, so register values are not held across the library exp.
+  const bool in_regs = ITERS > 0 && fast;
   A s0 = 0, s1 = 0;
-  if constexpr (ITERS > 0) {
+  if (in_regs) {
+    // Padding lanes (partial rows) hold -inf, which the short exp does not take: select 0.
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
+    for (int it = 0; it < R; ++it) {
+      const int col = (it * TPR + tl) * V;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const A t = exp_a(ev[it][e] - mx);  // padding: exp(-inf) = 0
+        A t = ex(Flag<true>{}, ev[it][e] - mx);
+        if constexpr (!FULL) t = col + e < N ? t : (A)0;
         ev[it][e] = t;
         if (e & 1) s1 += t;
         else s0 += t;
@@ -197,39 +287,47 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
     }
   } else if (valid) {
     SmAcc<A> acc;
-    for (int v = tl; v < nv; v += TPR) {
-      const int col = v * V;
-      A f[V];
-      IO::unpack(IO::load(xr + col, N - col), f);
+    auto sum_pass = [&](auto fast_tag) {
+      for (int v = tl; v < nv; v += TPR) {
+        const int col = v * V;
+        A f[V];
+        IO::unpack(IO::load(xr + col, N - col), f);
 #pragma unroll
-      for (int e = 0; e < V; ++e)
-        if (col + e < N) acc.add(e, exp_a(f[e] - mx), a.comp != 0);
-    }
+        for (int e = 0; e < V; ++e)
+          if (col + e < N) acc.add(e, ex(fast_tag, f[e] - mx), a.comp != 0);
+      }
+    };
+    if (fast) sum_pass(Flag<true>{});
+    else sum_pass(Flag<false>{});
     s0 = acc.total();
   }
-  const A sum = group_reduce<false>(s0 + s1, red + wpr, wpr, tl);
+  const A sum = group_reduce<false>(s0 + s1, red + 2 * wpr, wpr, tl);
   if (!valid) return;
   const A r = (A)1 / sum;
   S* yr = static_cast<S*>(a.out) + row * a.ldo;
-  if constexpr (ITERS > 0) {
+  if (in_regs) {
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
+    for (int it = 0; it < R; ++it) {
       const int col = (it * TPR + tl) * V;
-      if (col >= N) continue;
+      if (!FULL && col >= N) continue;
       A o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = ev[it][e] * r;
-      IO::store(yr + col, o, N - col);
+      IO::store(yr + col, o, FULL ? V : N - col);
     }
   } else {
-    for (int v = tl; v < nv; v += TPR) {
-      const int col = v * V;
-      A f[V], o[V];
-      IO::unpack(IO::load(xr + col, N - col), f);
+    auto store_pass = [&](auto fast_tag) {
+      for (int v = tl; v < nv; v += TPR) {
+        const int col = v * V;
+        A f[V], o[V];
+        IO::unpack(IO::load(xr + col, N - col), f);
 #pragma unroll
-      for (int e = 0; e < V; ++e) o[e] = exp_a(f[e] - mx) * r;
-      IO::store(yr + col, o, N - col);
-    }
+        for (int e = 0; e < V; ++e) o[e] = ex(fast_tag, f[e] - mx) * r;
+        IO::store(yr + col, o, N - col);
+      }
+    };
+    if (fast) store_pass(Flag<true>{});
+    else store_pass(Flag<false>{});
   }
 }
 

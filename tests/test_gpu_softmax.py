@@ -85,6 +85,39 @@ def test_softmax_peaked_and_infinite_logits():
     assert yg[3, 17] == 1.0 and np.count_nonzero(yg[3]) == 1
 
 
+@pytest.mark.parametrize("dtype,N", [("bf16", 4096), ("f32", 2048), ("bf16", 1000)])
+def test_softmax_exp_paths(dtype, N):
+    """Rows whose span max - min straddles 87 (the bound below which every exp is a normal float32
+    and the forward takes its short exp) and rows with -inf: both exp paths against the oracle, on
+    full rows (N = 4096 bf16, 2048 f32: the 8-vector register kernel) and ragged ones, with the
+    register and streaming kernels bit-identical; a NaN makes its whole row NaN."""
+    spans = [1.0, 20.0, 50.0, 86.5, 86.99, 87.0, 87.01, 88.0, 100.0, 120.0, 200.0]
+    rng = np.random.default_rng(11)
+    rows = []
+    for sp in spans:
+        for _ in range(3):
+            r = rng.uniform(-sp, 0.0, N).astype(np.float32)
+            r[rng.integers(N)] = 0.0
+            r[rng.integers(N)] = -sp
+            rows.append(r + np.float32(rng.uniform(-5, 5)))
+    inf_row = rng.standard_normal(N).astype(np.float32)
+    inf_row[::7] = -np.inf
+    rows.append(inf_row)
+    x = np.stack(rows)
+    if dtype == "bf16":
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    M = x.shape[0]
+    _, a = run_sm(dtype, M, N, variant="registers", x=x)
+    _, b = run_sm(dtype, M, N, variant="streaming", x=x)
+    assert same_bits(a[0], b[0]).all() and same_bits(a[1], b[1]).all()
+    xn = x.copy()
+    xn[1, 5] = np.nan
+    xt = to_device(xn, dtype, DEV)
+    for variant in ("registers", "streaming"):
+        y = arr(rn.softmax_fwd(xt, variant=variant)).astype(np.float64)
+        assert np.isnan(y[1]).all() and np.isfinite(y[0]).all() and np.isfinite(y[2]).all()
+
+
 def test_softmax_zero_rows():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
     assert rn.softmax_fwd(x).shape == (0, 64)
