@@ -73,6 +73,10 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
 }
 
 
+// Register kernels on rows that their threads' vectors tile exactly (N = iters * tpr * V) take the
+// FULL instantiation, which has no partial-vector code; the arithmetic is the same.
+bool tiles_row(const Plan& p, int64_t N, int V) { return (int64_t)p.iters * p.tpr * V == N; }
+
 template <DT D, Out O>
 rmsnorm_status fwd_dispatch(const Plan& p, const FwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
@@ -81,10 +85,12 @@ rmsnorm_status fwd_dispatch(const Plan& p, const FwdArgs& a, hipStream_t s) {
                   : launch(fwd_stream_kernel<D, false, O>, p.grid, block, p.lds, s, a);
   }
   const bool lds = p.variant == RMSNORM_VARIANT_LDS;
-#define RMSN_FWD_CASE(IT)                                                              \
-  case IT:                                                                             \
-    return lds ? launch(fwd_rows_kernel<D, IT, O, true>, p.grid, block, p.lds, s, a)   \
-               : launch(fwd_rows_kernel<D, IT, O, false>, p.grid, block, p.lds, s, a);
+  const bool full = tiles_row(p, a.N, Elem<D>::VEC);
+#define RMSN_FWD_CASE(IT)                                                                   \
+  case IT:                                                                                  \
+    return lds    ? launch(fwd_rows_kernel<D, IT, O, true>, p.grid, block, p.lds, s, a)     \
+           : full ? launch(fwd_rows_kernel<D, IT, O, false, true>, p.grid, block, p.lds, s, a) \
+                  : launch(fwd_rows_kernel<D, IT, O, false>, p.grid, block, p.lds, s, a);
   switch (p.iters) {
     RMSN_FWD_CASE(1)
     RMSN_FWD_CASE(2)
@@ -116,16 +122,16 @@ rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
       default: return RMSNORM_ERR_UNSUPPORTED;
     }
   }
+  const bool full = tiles_row(p, a.N, Elem<D>::VEC);
+#define RMSN_BWD_ROWS(IT, F)                                                                     \
+  launch(bwd_rows_kernel<D, IT, BwdPipe<IT>::DEPTH, BwdPipe<IT>::RB, AG, BwdPipe<IT>::KEEP, F>, \
+         p.grid, block, p.lds, s, a)
   switch (p.iters) {
-    case 1:
-      return launch(bwd_rows_kernel<D, 1, BwdPipe<1>::DEPTH, BwdPipe<1>::RB, AG, BwdPipe<1>::KEEP>,
-                    p.grid, block, p.lds, s, a);
-    case 2:
-      return launch(bwd_rows_kernel<D, 2, BwdPipe<2>::DEPTH, BwdPipe<2>::RB, AG, BwdPipe<2>::KEEP>,
-                    p.grid, block, p.lds, s, a);
-    default:
-      return RMSNORM_ERR_UNSUPPORTED;
+    case 1: return full ? RMSN_BWD_ROWS(1, true) : RMSN_BWD_ROWS(1, false);
+    case 2: return full ? RMSN_BWD_ROWS(2, true) : RMSN_BWD_ROWS(2, false);
+    default: return RMSNORM_ERR_UNSUPPORTED;
   }
+#undef RMSN_BWD_ROWS
 }
 
 

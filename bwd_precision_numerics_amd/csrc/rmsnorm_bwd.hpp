@@ -132,8 +132,9 @@ __device__ __forceinline__ float dw_factor(float xh) {
 // s + 1 .. s + DEPTH are in flight, and one barrier serves all RB rows of a batch. Pass 1 upcasts
 // a raw row to form its dot product and its dw contributions; pass 2 either reuses xhat and g*dy
 // kept from pass 1 (KEEP: fewer VALU operations, more registers) or upcasts the raw row again.
-// The gain g = offset + w stays in registers.
-template <DT D, int ITERS, int DEPTH, int RB, bool AG, bool KEEP>
+// The gain g = offset + w stays in registers. FULL: the host has checked N = ITERS * TPR * V (the
+// threads' vectors tile the row exactly), and the kernel carries no partial-vector code.
+template <DT D, int ITERS, int DEPTH, int RB, bool AG, bool KEEP, bool FULL = false>
 __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -192,7 +193,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
         rx[slot][k][it] = IO::zero();
         rd[slot][k][it] = IO::zero();
         if (li < nloc) {
-          if (col + V <= N) {
+          if (FULL || col + V <= N) {
             rx[slot][k][it] = IO::load(xr + col);
             rd[slot][k][it] = IO::load(dr + col);
           } else if (col < N) {
@@ -254,7 +255,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
           for (int it = 0; it < ITERS; ++it) {
             const int col = (it * TPR + tl) * V;
-            if (col >= N) continue;
+            if (!FULL && col >= N) continue;
             float o[V];
             if constexpr (KEEP) {
 #pragma unroll
@@ -272,7 +273,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
               }
             }
             const Raw out = IO::pack(o);
-            if (col + V <= N) IO::store(dxr + col, out);
+            if (FULL || col + V <= N) IO::store(dxr + col, out);
             else IO::store_part(dxr + col, out, N - col);
           }
         }

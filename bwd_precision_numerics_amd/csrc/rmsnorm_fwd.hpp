@@ -102,7 +102,9 @@ __device__ __forceinline__ void* out_row(void* y, int64_t row, int64_t ldy) {
 }
 
 // Row held in registers (STAGE_LDS = false) or staged in LDS (true) between the two passes.
-template <DT D, int ITERS, Out O, bool STAGE_LDS>
+// FULL: the host has checked N = ITERS * TPR * V (the threads' vectors tile the row exactly), and
+// the kernel carries no partial-vector code.
+template <DT D, int ITERS, Out O, bool STAGE_LDS, bool FULL = false>
 __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -128,7 +130,7 @@ __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
     const int col = (it * TPR + tl) * V;
     Raw r = IO::zero(), rw = IO::zero();
     if (valid) {
-      if (col + V <= N) {
+      if (FULL || col + V <= N) {
         r = IO::load(xr + col);
         rw = IO::load(wr + col);
       } else if (col < N) {
@@ -160,13 +162,13 @@ __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
-    if (col >= N) continue;
+    if (!FULL && col >= N) continue;
     const Raw r = STAGE_LDS ? stage[it * TPR + tl] : raw[it];
     float xf[V], wf[V], yf[V];
     IO::unpack(r, xf);
     IO::unpack(wraw[it], wf);
     apply_gain<D, O, V>(xf, wf, rs, a.offset, a.scale, yf);
-    store_out<D, O, true, V>(yr, col, N - col, a.yvec != 0, yf);
+    store_out<D, O, true, V>(yr, col, FULL ? V : N - col, a.yvec != 0, yf);
   }
 }
 
