@@ -74,8 +74,9 @@ __device__ __forceinline__ void add_centred_squares(const float (&f)[V], float m
 // Register kernel: the row stays in registers through the two reductions and the store. With
 // LATE_WB, w and b (cache-resident, shared by every row) are loaded in the store loop instead of
 // with x, so wider rows fit one wavefront without holding three row slices in registers.
-// LDS: two reduction slots of wpr floats per row group.
-template <DT D, int ITERS, bool HAS_B, bool LATE_WB = false>
+// LDS: two reduction slots of wpr floats per row group. FULL: the host has checked
+// N = ITERS * TPR * V (the threads' vectors tile the row), and there is no partial-vector code.
+template <DT D, int ITERS, bool HAS_B, bool LATE_WB = false, bool FULL = false>
 __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -101,7 +102,7 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
     const int col = (it * TPR + tl) * V;
     Raw r = IO::zero(), rw = IO::zero(), rb = IO::zero();
     if (valid) {
-      if (col + V <= N) {
+      if (FULL || col + V <= N) {
         r = IO::load(xr + col);
         if constexpr (!LATE_WB) {
           rw = IO::load(wr + col);
@@ -139,7 +140,7 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
     const int col = (it * TPR + tl) * V;
     float f[V];
     IO::unpack(raw[it], f);
-    add_centred_squares<V>(f, mean, N - col, q, false);
+    add_centred_squares<V>(f, mean, FULL ? V : N - col, q, false);
   }
   const float var = group_sum(q.total(), red + wpr, wpr, tl) / (float)N;
   const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
@@ -152,11 +153,11 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
-    if (col >= N) continue;
+    if (!FULL && col >= N) continue;
     float xf[V], wf[V], bf[V], yf[V];
     IO::unpack(raw[it], xf);
     if constexpr (LATE_WB) {
-      const bool full = col + V <= N;
+      const bool full = FULL || col + V <= N;
       IO::unpack(full ? IO::load(wr + col) : IO::load_part(wr + col, N - col), wf);
       if constexpr (HAS_B)
         IO::unpack(full ? IO::load(br + col) : IO::load_part(br + col, N - col), bf);
@@ -165,7 +166,7 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
       if constexpr (HAS_B) IO::unpack(braw[it], bf);
     }
     ln_affine<V, HAS_B>(xf, wf, bf, mean, rs, yf);
-    store_out<D, Out::ONCE, true, V>(yr, col, N - col, a.yvec != 0, yf);
+    store_out<D, Out::ONCE, true, V>(yr, col, FULL ? V : N - col, a.yvec != 0, yf);
   }
 }
 
@@ -251,8 +252,8 @@ struct LnBwdArgs {
 // A ring of DEPTH + 1 rows of raw (x, dy) and their (mean, rstd) per row group keeps DEPTH rows in
 // flight while one is reduced and written. HAS_DB adds the bias-gradient accumulators. KEEP holds
 // xhat and w * dy from the first pass for the second (fewer vector ALU operations, more registers)
-// instead of recomputing them from the raw row.
-template <DT D, int ITERS, int DEPTH, bool HAS_DB, bool KEEP>
+// instead of recomputing them from the raw row. FULL: as in the forward.
+template <DT D, int ITERS, int DEPTH, bool HAS_DB, bool KEEP, bool FULL = false>
 __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -311,7 +312,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
       rx[slot][it] = IO::zero();
       rd[slot][it] = IO::zero();
       if (ok) {
-        if (col + V <= N) {
+        if (FULL || col + V <= N) {
           rx[slot][it] = IO::load(xr + col);
           rd[slot][it] = IO::load(dr + col);
         } else if (col < N) {
@@ -370,7 +371,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
 #pragma unroll
           for (int it = 0; it < ITERS; ++it) {
             const int col = (it * TPR + tl) * V;
-            if (col >= N) continue;
+            if (!FULL && col >= N) continue;
             float o[V];
             if constexpr (KEEP) {
 #pragma unroll
@@ -388,7 +389,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
               }
             }
             const Raw out = IO::pack(o);
-            if (col + V <= N) IO::store(dxr + col, out);
+            if (FULL || col + V <= N) IO::store(dxr + col, out);
             else IO::store_part(dxr + col, out, N - col);
           }
         }

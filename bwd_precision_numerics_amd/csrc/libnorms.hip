@@ -74,17 +74,24 @@ rmsnorm_status ln_fwd_dispatch(const Plan& p, const LnFwdArgs& a, hipStream_t s)
                   : launch(ln_fwd_stream_kernel<D, false, HAS_B>, p.grid, block, p.lds, s, a);
   }
   static_assert(kLnFwdEarlyWbIters == 4, "cases below");
+  // Rows that the threads' vectors tile exactly take the FULL instantiation (no partial-vector
+  // code; the same arithmetic).
+  const bool full = (int64_t)p.iters * p.tpr * Elem<D>::VEC == a.N;
+#define RMSN_LNF(IT, LATE)                                                                    \
+  (full ? launch(ln_fwd_rows_kernel<D, IT, HAS_B, LATE, true>, p.grid, block, p.lds, s, a)  \
+        : launch(ln_fwd_rows_kernel<D, IT, HAS_B, LATE>, p.grid, block, p.lds, s, a))
   switch (p.iters) {
-    case 1: return launch(ln_fwd_rows_kernel<D, 1, HAS_B>, p.grid, block, p.lds, s, a);
-    case 2: return launch(ln_fwd_rows_kernel<D, 2, HAS_B>, p.grid, block, p.lds, s, a);
-    case 3: return launch(ln_fwd_rows_kernel<D, 3, HAS_B>, p.grid, block, p.lds, s, a);
-    case 4: return launch(ln_fwd_rows_kernel<D, 4, HAS_B>, p.grid, block, p.lds, s, a);
-    case 5: return launch(ln_fwd_rows_kernel<D, 5, HAS_B, true>, p.grid, block, p.lds, s, a);
-    case 6: return launch(ln_fwd_rows_kernel<D, 6, HAS_B, true>, p.grid, block, p.lds, s, a);
-    case 7: return launch(ln_fwd_rows_kernel<D, 7, HAS_B, true>, p.grid, block, p.lds, s, a);
-    case 8: return launch(ln_fwd_rows_kernel<D, 8, HAS_B, true>, p.grid, block, p.lds, s, a);
+    case 1: return RMSN_LNF(1, false);
+    case 2: return RMSN_LNF(2, false);
+    case 3: return RMSN_LNF(3, false);
+    case 4: return RMSN_LNF(4, false);
+    case 5: return RMSN_LNF(5, true);
+    case 6: return RMSN_LNF(6, true);
+    case 7: return RMSN_LNF(7, true);
+    case 8: return RMSN_LNF(8, true);
     default: return RMSNORM_ERR_UNSUPPORTED;
   }
+#undef RMSN_LNF
 }
 
 template <bool HAS_B>
@@ -167,16 +174,16 @@ rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s)
     return p.wide ? launch(ln_bwd_stream_kernel<D, true, HAS_DB>, p.grid, block, p.lds, s, a)
                   : launch(ln_bwd_stream_kernel<D, false, HAS_DB>, p.grid, block, p.lds, s, a);
   }
+  const bool full = (int64_t)p.iters * p.tpr * Elem<D>::VEC == a.N;
+#define RMSN_LNB(IT, F)                                                                          \
+  launch(ln_bwd_rows_kernel<D, IT, LnBwdPipe<IT>::DEPTH, HAS_DB, LnBwdPipe<IT>::KEEP, F>, p.grid, \
+         block, p.lds, s, a)
   switch (p.iters) {
-    case 1:
-      return launch(ln_bwd_rows_kernel<D, 1, LnBwdPipe<1>::DEPTH, HAS_DB, LnBwdPipe<1>::KEEP>,
-                    p.grid, block, p.lds, s, a);
-    case 2:
-      return launch(ln_bwd_rows_kernel<D, 2, LnBwdPipe<2>::DEPTH, HAS_DB, LnBwdPipe<2>::KEEP>,
-                    p.grid, block, p.lds, s, a);
-    default:
-      return RMSNORM_ERR_UNSUPPORTED;
+    case 1: return full ? RMSN_LNB(1, true) : RMSN_LNB(1, false);
+    case 2: return full ? RMSN_LNB(2, true) : RMSN_LNB(2, false);
+    default: return RMSNORM_ERR_UNSUPPORTED;
   }
+#undef RMSN_LNB
 }
 
 template <bool HAS_DB>
