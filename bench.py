@@ -27,6 +27,12 @@ Measurement:
 * copy_ceiling: a device-to-device copy with the forward's traffic, timed the same way; value is
   also reported as a fraction of it.
 * cpu_baseline: the CPU oracle (NumPy, one thread) on a bounded sample of the same rows.
+* rows: LayerNorm, softmax, GroupNorm and the float64 RMSNorm, forward and backward, timed the same
+  way (graph of back-to-back launches over rotating buffers), each with its own CPU oracle sample.
+* configs: every RMSNorm configuration (fp32 64 x 1024; bf16 4096 x 4096 in the other rounding
+  mode; fp16 8192 x 8192; bf16 16384 x 3072 Gemma round once; bf16 M = 4096 hidden-size sweep up to
+  N = 32768): step, forward and backward times, GB/s and fraction of peak per phase, on inputs
+  drawn on the device with the same distributions.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload NAME] [--rounding once]
 """
@@ -94,6 +100,8 @@ def parse_args(argv=None):
                     help="launch only this kernel --steps times (for counter collection)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the LayerNorm / GroupNorm measurements")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration RMSNorm sweep")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, copy a buffer of this many MiB --steps times "
                          "(calibrates the HBM byte counters)")
@@ -108,9 +116,11 @@ class Sets:
         self.rn, self.torch, self.wl, self.rounding = rn, torch, wl, rounding
         self.lib = rn.library()
         M, N = wl.M, wl.N
-        x0 = to_device(inp["x"], wl.dtype, device)
-        dy0 = to_device(inp["dy"], wl.dtype, device)
-        self.w = to_device(inp["w"], wl.dtype, device)
+
+        def dev(a):  # host arrays of T values, or tensors already on the device
+            return a.contiguous() if isinstance(a, torch.Tensor) else to_device(a, wl.dtype,
+                                                                                  device)
+        x0, dy0, self.w = dev(inp["x"]), dev(inp["dy"]), dev(inp["w"])
         self.sets = []
         for _ in range(nsets):
             s = {"x": x0.clone(), "dy": dy0.clone(),
@@ -427,6 +437,57 @@ def groupnorm_row(torch, rn, launches, rotate_mib):
             "passes": "fwd reads x twice (statistics, then normalize); bwd reads x and dy twice"}
 
 
+# Every RMSNorm configuration the library is specified for, timed like the headline: the
+# correctness case (fp32 64 x 1024, launch-bound), the headline shape in the other rounding mode,
+# the fp16 8192 x 8192 overflow case, the Gemma round-once shape, and the hidden-size sweep at
+# M = 4096 (N = 32768 takes the LDS-staged backward).
+CONFIG_SWEEP = [("fp32_64x1024", None), ("bf16_4096x4096", "once"), ("fp16_8192x8192", None),
+                ("bf16_16384x3072_gemma", None)] + [
+    (f"bf16_sweep_4096x{n}", None) for n in (1024, 2048, 4096, 8192, 16384, 32768)]
+MAX_SETS = 64
+
+
+def config_sweep(torch, rn, launches, rotate_mib):
+    """Per configuration and rounding mode: step time (graph of `launches` steps), each kernel's
+    average duration, algorithmic GB/s and fraction of the HBM peak per phase. Inputs are drawn on
+    the device with each workload's distributions (make_device_inputs). Small configurations
+    rotate over at most MAX_SETS buffer sets, so they run from the caches (their numbers are
+    launch-bound, not bandwidth figures)."""
+    from workloads import WORKLOADS, make_device_inputs
+    out = []
+    for name, rounding in CONFIG_SWEEP:
+        wl = WORKLOADS[name]
+        rounding = rounding or wl.rounding
+        inp = make_device_inputs(wl, "cuda:0")
+        nsets = min(MAX_SETS, max(4, -(-rotate_mib * 2**20 // (wl.M * wl.N * wl.itemsize))))
+        sets = Sets(rn, torch, wl, rounding, inp, nsets, "cuda:0")
+        del inp
+        for i in range(nsets):
+            sets.fwd(i)
+        torch.cuda.synchronize()
+        step = graph_time(torch, sets.step, launches)
+        dur = kernel_durations(torch, sets, launches)
+        bwd = dur["bwd_rows"] + dur["dw_reduce"]
+        fb, bb = wl.fwd_bytes(), wl.bwd_bytes()
+        cached = nsets * wl.M * wl.N * wl.itemsize < 2**30
+        out.append({
+            "workload": name, "dtype": wl.dtype, "M": wl.M, "N": wl.N, "rounding": rounding,
+            "offset": wl.offset, "buffer_sets": nsets, "cache_resident": cached,
+            "step_us": round(step * 1e6, 3), "fwd_us": round(dur["fwd"] * 1e6, 3),
+            "bwd_us": round(bwd * 1e6, 3), "bwd_rows_us": round(dur["bwd_rows"] * 1e6, 3),
+            "dw_reduce_us": round(dur["dw_reduce"] * 1e6, 3),
+            "step_GBps": round((fb + bb) / step / 1e9, 1),
+            "fwd_GBps": round(fb / dur["fwd"] / 1e9, 1), "bwd_GBps": round(bb / bwd / 1e9, 1),
+            "step_frac_of_peak": round((fb + bb) / step / 1e9 / PEAK_HBM_GBPS, 4),
+            "fwd_frac_of_peak": round(fb / dur["fwd"] / 1e9 / PEAK_HBM_GBPS, 4),
+            "bwd_frac_of_peak": round(bb / bwd / 1e9 / PEAK_HBM_GBPS, 4)})
+        print(json.dumps({"config_done": name, "rounding": rounding}), file=sys.stderr,
+              flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
 def row_cpu_baselines(budget_s):
     """The oracle of each widened row, one NumPy thread, on a bounded sample of the same workload
     (whole rows; GroupNorm on batch 0), forward + backward: algorithmic GB/s of the sample."""
@@ -614,7 +675,7 @@ def main(argv=None) -> int:
         launches = max(min(args.steps, 100), 20)
         line["rows"] = {"layernorm": layernorm_row(torch, rn, sets, launches),
                         "softmax": softmax_row(torch, rn, sets, launches)}
-        del sets
+        sets = None
         torch.cuda.empty_cache()
         line["rows"]["groupnorm"] = groupnorm_row(torch, rn, launches, args.rotate_mib)
         torch.cuda.empty_cache()
@@ -623,6 +684,10 @@ def main(argv=None) -> int:
         for r in line["rows"].values():
             r["fwd_frac_of_peak"] = round(r["fwd_GBps"] / PEAK_HBM_GBPS, 4)
             r["bwd_frac_of_peak"] = round(r["bwd_GBps"] / PEAK_HBM_GBPS, 4)
+    if not args.no_configs and name == HEADLINE:
+        sets = None
+        torch.cuda.empty_cache()
+        line["configs"] = config_sweep(torch, rn, max(min(args.steps, 100), 20), args.rotate_mib)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(wl, rounding, inp, args.cpu_seconds)
         if "rows" in line:

@@ -13,7 +13,10 @@ namespace {
 
 constexpr int kBwdBlockThreads = 1024;  // backward: 16 wavefronts per persistent block
 constexpr int kBwdRegMaxIters = 2;      // backward register kernel (rows + prefetch in registers)
-constexpr int kBwdLdsMaxIters = 4;      // backward LDS-staged kernel
+// LDS-staged backward: rows past the register kernel's reach (2048 to 4096 vectors) take one row
+// per 1024-thread block, 3 or 4 vectors per thread; the stage holds the row's x and dy
+// (2 * 4096 * 16 bytes = 128 KiB at most) while registers carry the next row's loads.
+constexpr int kBwdLdsMaxIters = 4;
 // Register backward pipeline per vectors-per-thread: rows per barrier (batch) and batches in flight
 // ahead of the current one. Ring registers: (DEPTH + 1) * RB * ITERS * 2 sixteen-byte vectors.
 template <int ITERS> struct BwdPipe;
@@ -113,16 +116,22 @@ rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
     return p.wide ? launch(bwd_stream_kernel<D, true, AG>, p.grid, block, p.lds, s, a)
                   : launch(bwd_stream_kernel<D, false, AG>, p.grid, block, p.lds, s, a);
   }
+  const bool full = tiles_row(p, a.N, Elem<D>::VEC);
   if (p.variant == RMSNORM_VARIANT_LDS) {
+    // Rows of 3 or 4 vectors per thread have 1024 threads (one row group) per block: the kernel
+    // takes that as a compile-time constant.
+#define RMSN_BWD_LDS(IT, TPRC)                                                              \
+  (full ? launch(bwd_lds_kernel<D, IT, AG, true, TPRC>, p.grid, block, p.lds, s, a)         \
+        : launch(bwd_lds_kernel<D, IT, AG, false, TPRC>, p.grid, block, p.lds, s, a))
     switch (p.iters) {
-      case 1: return launch(bwd_lds_kernel<D, 1, AG>, p.grid, block, p.lds, s, a);
-      case 2: return launch(bwd_lds_kernel<D, 2, AG>, p.grid, block, p.lds, s, a);
-      case 3: return launch(bwd_lds_kernel<D, 3, AG>, p.grid, block, p.lds, s, a);
-      case 4: return launch(bwd_lds_kernel<D, 4, AG>, p.grid, block, p.lds, s, a);
+      case 1: return RMSN_BWD_LDS(1, 0);
+      case 2: return RMSN_BWD_LDS(2, 0);
+      case 3: return RMSN_BWD_LDS(3, kBwdBlockThreads);
+      case 4: return RMSN_BWD_LDS(4, kBwdBlockThreads);
       default: return RMSNORM_ERR_UNSUPPORTED;
     }
+#undef RMSN_BWD_LDS
   }
-  const bool full = tiles_row(p, a.N, Elem<D>::VEC);
 #define RMSN_BWD_ROWS(IT, F)                                                                     \
   launch(bwd_rows_kernel<D, IT, BwdPipe<IT>::DEPTH, BwdPipe<IT>::RB, AG, BwdPipe<IT>::KEEP, F>, \
          p.grid, block, p.lds, s, a)

@@ -145,7 +145,10 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 
   const int TPR = a.tpr, wpr = TPR >> 6, G = a.groups, N = a.N;
   const int tid = threadIdx.x;
-  const int grp = tid / TPR;
+  // Scalar row addressing (wave_group) relieves the 2-vector kernel's register pressure (it was
+  // spilling) and measured faster there; the 1-vector kernel measured slower with it on partly
+  // idle row groups (N = 3072: 384 of 512 threads), so it keeps per-lane row indices.
+  const int grp = ITERS >= 2 ? wave_group(tid, TPR) : tid / TPR;
   const int tl = tid - grp * TPR;
   const int b = blockIdx.x, P = a.P;
   const int64_t nloc = block_rows(a.M, P, b);
@@ -164,8 +167,8 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
       Raw r = IO::zero();
-      if (col + V <= N) r = IO::load(wr + col);
-      else if (col < N) r = IO::load_part(wr + col, N - col);
+      if (col + V <= N) r = IO::load(at(wr, col));
+      else if (col < N) r = IO::load_part(at(wr, col), N - col);
       float wf[V];
       IO::unpack(r, wf);
 #pragma unroll
@@ -194,11 +197,11 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
         rd[slot][k][it] = IO::zero();
         if (li < nloc) {
           if (FULL || col + V <= N) {
-            rx[slot][k][it] = IO::load(xr + col);
-            rd[slot][k][it] = IO::load(dr + col);
+            rx[slot][k][it] = IO::load(at(xr, col));
+            rd[slot][k][it] = IO::load(at(dr, col));
           } else if (col < N) {
-            rx[slot][k][it] = IO::load_part(xr + col, N - col);
-            rd[slot][k][it] = IO::load_part(dr + col, N - col);
+            rx[slot][k][it] = IO::load_part(at(xr, col), N - col);
+            rd[slot][k][it] = IO::load_part(at(dr, col), N - col);
           }
         }
       }
@@ -273,8 +276,8 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
               }
             }
             const Raw out = IO::pack(o);
-            if (FULL || col + V <= N) IO::store(dxr + col, out);
-            else IO::store_part(dxr + col, out, N - col);
+            if (FULL || col + V <= N) IO::store(at(dxr, col), out);
+            else IO::store_part(at(dxr, col), out, N - col);
           }
         }
       }
@@ -286,11 +289,12 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 }
 
 // LDS-staged kernel for rows too wide to keep in registers (e.g. N = 32768 in 16-bit types): the
-// raw x and dy of the current row are written to LDS as they arrive and read back for the
-// elementwise pass, so registers hold only the column accumulators and one row's loads in flight.
-// The gain is re-read from w (cache-resident) in each pass. Same thread-to-element mapping and
-// summation order as the register kernel, so dx is bit-identical to it for the same shape.
-template <DT D, int ITERS, bool AG>
+// raw x and dy of the current row sit in LDS for both passes while the registers hold the next
+// row's loads in flight (a two-row pipeline), so registers carry the column accumulators and one
+// row of raw data. The gain is re-read from w (cache-resident) in each pass. Same thread-to-element
+// mapping and summation order as the register kernel, so dx is bit-identical to it for the same
+// shape. FULL: as in the register kernel.
+template <DT D, int ITERS, bool AG, bool FULL, int TPRC = 0>
 __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -298,9 +302,12 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
   constexpr int V = IO::V;
   extern __shared__ uint4 smem[];
 
-  const int TPR = a.tpr, wpr = TPR >> 6, G = a.groups, N = a.N;
+  // TPRC > 0: one row group of TPRC threads (the whole block), known at compile time, so the
+  // stage slots of a thread sit at constant offsets from two base addresses.
+  const int TPR = TPRC > 0 ? TPRC : a.tpr, G = TPRC > 0 ? 1 : a.groups;
+  const int wpr = TPR >> 6, N = a.N;
   const int tid = threadIdx.x;
-  const int grp = tid / TPR;
+  const int grp = wave_group(tid, TPR);
   const int tl = tid - grp * TPR;
   const int b = blockIdx.x, P = a.P;
   const int64_t nloc = block_rows(a.M, P, b);
@@ -309,45 +316,74 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
   Raw* stage = smem + ((2 * G * wpr + 3) >> 2) + (size_t)grp * 2 * ITERS * TPR;  // [G][2][ITERS*TPR]
 
   const S* wr = static_cast<const S*>(a.w);
+  const BufRsrc wbuf = buf_rsrc(wr);
+  // Whole vectors go through buffer accesses: lane offset tl * 16 bytes, vector it at the
+  // wave-uniform offset it * TPR * 16.
+  const uint32_t voff = (uint32_t)tl * 16u;
   float acc[ITERS * V];
 #pragma unroll
   for (int k = 0; k < ITERS * V; ++k) acc[k] = 0.f;
+
+  // Registers carry the next row's raw x and dy (and rstd) while the current one is processed
+  // from the stage; rows past the block's share load as zeros and rstd 0 (they add nothing).
+  Raw rx[ITERS], rd[ITERS];
+  float rs_next = 0.f;
+  auto load_row = [&](int s) {
+    const int64_t li = (int64_t)s * G + grp;
+    const bool ok = s < nsteps && li < nloc;
+    const int64_t row = b + (ok ? li : 0) * P;
+    const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
+    const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
+    const BufRsrc xb = buf_rsrc(xr), db = buf_rsrc(dr);
+    rs_next = ok ? a.rstd[row] : 0.f;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      const uint32_t soff = (uint32_t)(it * TPR) * 16u;
+      rx[it] = rd[it] = IO::zero();
+      if (ok) {
+        if (FULL || col + V <= N) {
+          rx[it] = IO::load_b(xb, voff, soff);
+          rd[it] = IO::load_b(db, voff, soff);
+        } else if (col < N) {
+          rx[it] = IO::load_part(at(xr, col), N - col);
+          rd[it] = IO::load_part(at(dr, col), N - col);
+        }
+      }
+    }
+  };
+  load_row(0);
 
   for (int s = 0; s < nsteps; ++s) {
     const int64_t li = (int64_t)s * G + grp;
     const bool valid = li < nloc;
     const int64_t row = b + (valid ? li : 0) * P;
-    const int64_t lrow = row;
-    const S* xr = static_cast<const S*>(a.x) + lrow * a.ldx;
-    const S* dr = static_cast<const S*>(a.dy) + lrow * a.lddy;
-    const float rs = valid ? a.rstd[row] : 0.f;  // issued with the row's loads
-    Raw rx[ITERS], rd[ITERS];
+    // Each thread reads back only the stage slots it wrote, so no barrier guards the stage.
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      const int col = (it * TPR + tl) * V;
-      rx[it] = rd[it] = IO::zero();
-      if (valid) {
-        if (col + V <= N) {
-          rx[it] = IO::load(xr + col);
-          rd[it] = IO::load(dr + col);
-        } else if (col < N) {
-          rx[it] = IO::load_part(xr + col, N - col);
-          rd[it] = IO::load_part(dr + col, N - col);
-        }
-      }
+      stage[it * TPR + tl] = rx[it];
+      stage[(ITERS + it) * TPR + tl] = rd[it];
     }
+    const float rs = rs_next;
+    load_row(s + 1);
+    // Opaque copies of the lane's stage index and w offset. Without them the compiler would
+    // forward the values just stored to the stage instead of reading them back (keeping this
+    // row's raw data live next to the next row's loads), and would hoist the w loads (the same for
+    // every row) out of the row loop, holding the whole gain in registers.
+    int tl1 = tl;
+    uint32_t wvoff = voff;
+    asm volatile("" : "+v"(tl1), "+v"(wvoff));
     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
-      stage[it * TPR + tl] = rx[it];
-      stage[(ITERS + it) * TPR + tl] = rd[it];
+      const uint32_t soff = (uint32_t)(it * TPR) * 16u;
       Raw rw = IO::zero();
-      if (col + V <= N) rw = IO::load(wr + col);
-      else if (col < N) rw = IO::load_part(wr + col, N - col);
+      if (FULL || col + V <= N) rw = IO::load_b(wbuf, wvoff, soff);
+      else if (col < N) rw = IO::load_part(at(wr, col), N - col);
       float xf[V], df[V], wf[V];
-      IO::unpack(rx[it], xf);
-      IO::unpack(rd[it], df);
+      IO::unpack(stage[it * TPR + tl1], xf);
+      IO::unpack(stage[(ITERS + it) * TPR + tl1], df);
       IO::unpack(rw, wf);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
@@ -357,19 +393,33 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
         if (e & 1) d1 = __builtin_fmaf(gd, xh, d1);
         else d0 = __builtin_fmaf(gd, xh, d0);
       }
+      // One vector at a time, with its dw updates done here: left to itself the compiler sinks
+      // them past the reduction and keeps every vector's xhat and dy live until then, which the
+      // accumulators and the next row's loads leave no registers for.
+#pragma unroll
+      for (int e = 0; e < V; ++e) asm volatile("" : "+v"(acc[it * V + e]));
+      __builtin_amdgcn_sched_barrier(0);
     }
     const float dot = group_sum(d0 + d1, red + (s & 1) * G * wpr + grp * wpr, wpr, tl);
     const float c = dot / (float)N;
+    // Fresh opaque copies for the second pass, which reads the same addresses as the first:
+    // otherwise the first pass's values stay live across the reduction.
+    int tl2 = tl;
+    uint32_t wvoff2 = voff;
+    asm volatile("" : "+v"(tl2), "+v"(wvoff2));
     if (valid) {
       S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
+      const BufRsrc dxb = buf_rsrc(dxr);
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
         const int col = (it * TPR + tl) * V;
-        if (col >= N) continue;
-        Raw rw = (col + V <= N) ? IO::load(wr + col) : IO::load_part(wr + col, N - col);
+        const uint32_t soff = (uint32_t)(it * TPR) * 16u;
+        if (!FULL && col >= N) continue;
+        const bool whole = FULL || col + V <= N;
+        Raw rw = whole ? IO::load_b(wbuf, wvoff2, soff) : IO::load_part(at(wr, col), N - col);
         float xf[V], df[V], wf[V], o[V];
-        IO::unpack(stage[it * TPR + tl], xf);
-        IO::unpack(stage[(ITERS + it) * TPR + tl], df);
+        IO::unpack(stage[it * TPR + tl2], xf);
+        IO::unpack(stage[(ITERS + it) * TPR + tl2], df);
         IO::unpack(rw, wf);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
@@ -378,8 +428,9 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
           o[e] = rs * (gd - xh * c);
         }
         const Raw out = IO::pack(o);
-        if (col + V <= N) IO::store(dxr + col, out);
-        else IO::store_part(dxr + col, out, N - col);
+        if (whole) IO::store_b(dxb, voff, soff, out);
+        else IO::store_part(at(dxr, col), out, N - col);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }

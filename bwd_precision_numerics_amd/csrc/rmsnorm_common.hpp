@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace rmsn {
 
@@ -78,11 +79,34 @@ template <> __device__ __forceinline__ uint32_t pack2<DT::F16>(float lo, float h
 // VecIO<D, false>: single elements.
 template <DT D, bool WIDE> struct VecIO;
 
+// Raw (untyped) buffer access: a 128-bit descriptor in scalar registers holds a row's base address,
+// and each access names a 32-bit lane offset (one vector register shared by all of a thread's
+// accesses) plus a wave-uniform 32-bit offset in a scalar register. Dword 3 sets the descriptor's
+// data format field (bits 15-18) to 4 (32 bits), without which untyped accesses return zero on
+// gfx9-family GPUs; no swizzle, no index. The record count is left at 2^31 - 1: callers address
+// only bytes of the row they own (partial vectors take the element-wise path).
+using BufRsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kBufDword3 = 0x00020000;
+constexpr int kBufNonTemporal = 2;  // cache-policy operand: non-temporal (nt) stores
+template <typename T>
+__device__ __forceinline__ BufRsrc buf_rsrc(const T* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, 0x7fffffff, kBufDword3);
+}
+
 template <DT D> struct VecIO<D, true> {
   using S = typename Elem<D>::S;
   static constexpr int V = Elem<D>::VEC;
   using Raw = uint4;
   static __device__ __forceinline__ Raw zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  // 16 bytes at byte offset voff + soff of the buffer (soff wave-uniform).
+  static __device__ __forceinline__ Raw load_b(BufRsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  }
+  static __device__ __forceinline__ void store_b(BufRsrc r, uint32_t voff, uint32_t soff, Raw v) {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, soff,
+                                           kBufNonTemporal);
+  }
   static __device__ __forceinline__ Raw load(const S* p) {
     return *reinterpret_cast<const uint4*>(p);
   }
@@ -175,6 +199,23 @@ template <DT D> __device__ __forceinline__ float round_trip(float f) {
   } else {
     return to_f32<D>(from_f32<D>(f));
   }
+}
+
+// Row group of a thread in a block of row groups of tpr threads. tpr is a multiple of 64, so all
+// lanes of a wavefront share the group; reading it from the first lane makes it, and every row
+// index and row pointer derived from it, wave-uniform (scalar registers), so row addresses need no
+// per-lane 64-bit registers.
+__device__ __forceinline__ int wave_group(int tid, int tpr) {
+  return __builtin_amdgcn_readfirstlane(tid / tpr);
+}
+
+// Element col of a row: the byte offset is formed in 32 bits (unsigned; rows are far below 4 GiB),
+// so with a wave-uniform row pointer the compiler addresses the element as scalar base + one 32-bit
+// lane offset instead of a 64-bit per-lane address. Precondition: col >= 0.
+template <typename T>
+__device__ __forceinline__ T* at(T* row, int col) {
+  using B = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+  return reinterpret_cast<T*>(reinterpret_cast<B*>(row) + (uint32_t)col * (uint32_t)sizeof(T));
 }
 
 // ---- reductions ----------------------------------------------------------------------------------

@@ -159,6 +159,27 @@ def test_kernel_families_agree_bit_for_bit(dtype, N):
         assert same_bits(results["registers"][3], results["lds"][3]).all()
 
 
+@pytest.mark.parametrize("dtype,N", [("bf16", 32768), ("bf16", 30000), ("f32", 16384),
+                                     ("f16", 20000)])
+def test_wide_rows_prefetch_pipeline(dtype, N):
+    """Rows past the register kernel's reach (2048 vectors) take the LDS-staged backward, which
+    loads a block's next row while it works on the current one. 300 rows over 256 blocks give 44
+    blocks two rows, so the prefetched rows are used; exactly tiled (32768, f32 16384) and ragged
+    widths. Checked against the oracle, and bit for bit against the streaming kernel (same shape,
+    same summation order)."""
+    _, lds = run_case(dtype, 300, N, variant="lds", seed=21)
+    wl = WL[dtype]
+    inp = make_inputs(wl, M=300, N=N, seed=21)
+    xt, wt, dyt = (to_device(inp[k], dtype, DEV) for k in ("x", "w", "dy"))
+    print(f"case streaming dtype={dtype} M=300 N={N}", flush=True)
+    y, r = rn.fwd(xt, wt, variant="streaming")
+    dx, dw = rn.bwd(dyt, xt, wt, r, variant="streaming")
+    torch.cuda.synchronize()
+    for k, t in enumerate((y, r, dx)):
+        assert same_bits(lds[k], to_np(t)).all(), k
+    assert np.allclose(lds[3], to_np(dw), rtol=1e-5, atol=1e-6)
+
+
 def test_forward_register_and_lds_staging_at_wide_rows():
     for variant in ("registers", "lds", "streaming"):
         wl = WL["bf16"]

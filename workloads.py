@@ -124,6 +124,34 @@ def make_inputs(wl: Workload, M: int | None = None, N: int | None = None,
     }
 
 
+def make_device_inputs(wl: Workload, device: str, seed: int | None = None) -> dict:
+    """Timing inputs drawn on the device: ``x`` [M, N], ``w`` [N], ``dy`` [M, N] as tensors of
+    dtype T, with the workload's distributions (float32 draws from torch's device generator, seeded,
+    x then w then dy, then cast to T). The values differ from make_inputs' (another generator);
+    they serve benchmarks of large shapes, where drawing on the host takes minutes."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed if seed is None else seed)
+
+    def draw(dist, shape):
+        kind = dist[0]
+        if kind == "normal":
+            t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+            return t.mul_(dist[2]).add_(dist[1])
+        if kind == "uniform":
+            t = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+            return t.mul_(dist[2] - dist[1]).add_(dist[1])
+        if kind == "ones":
+            return torch.ones(shape, device=device, dtype=torch.float32)
+        raise ValueError(f"unknown distribution {dist!r}")
+
+    td = torch_dtype(wl.dtype)
+    x = draw(wl.x_dist, (wl.M, wl.N)).to(td)
+    w = draw(wl.w_dist, (wl.N,)).to(td)
+    dy = draw(wl.dy_dist, (wl.M, wl.N)).to(td)
+    return {"x": x, "w": w, "dy": dy}
+
+
 def torch_dtype(dtype: str):
     import torch
     return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
