@@ -360,6 +360,13 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
             d2a = __builtin_fmaf(gd0, xh0, d2a);
             d2b = __builtin_fmaf(gd1, xh1, d2b);
           }
+          // Done here, not after the row's reduction where the compiler would otherwise sink
+          // them (measured 30.8 -> 30.4 us at 4096 x 4096 bf16).
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            asm volatile("" : "+v"(accw[it * V + e]));
+            if constexpr (HAS_DB) asm volatile("" : "+v"(accb[it * V + e]));
+          }
         }
         float dots[2] = {d1a + d1b, d2a + d2b};
         group_sum_batch<2>(dots, red + ((s & 1) * G + grp) * wpr * 2, wpr, tl);

@@ -208,9 +208,8 @@ rmsnorm_status reduce_partials(const float* part, int64_t P, int64_t N, float* o
       hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s,
                          out2, (int)N);
   } else {
-    hipLaunchKernelGGL(dw_reduce_kernel<float>, dim3((unsigned)ceil_div(N, 16), out2 ? 2u : 1u),
-                       dim3(256), 0, s, part, partial_ld(N), (int)P, (int)N, out, out2,
-                       P * partial_ld(N));
+    launch_dw_reduce(part, partial_ld(N), (int)P, (int)N, out, out2, P * partial_ld(N),
+                     out2 ? 2u : 1u, s);
   }
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
 }

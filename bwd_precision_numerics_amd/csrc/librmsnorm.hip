@@ -276,9 +276,8 @@ rmsnorm_status dw_reduce_impl(const void* workspace, size_t workspace_bytes_give
                        (int)N);
     return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
   }
-  hipLaunchKernelGGL(dw_reduce_kernel<float>, dim3((unsigned)ceil_div(N, 16)), dim3(256), 0, s,
-                     static_cast<const float*>(workspace), partial_ld(N), (int)num_partials(M),
-                     (int)N, dw, nullptr, (int64_t)0);
+  launch_dw_reduce(static_cast<const float*>(workspace), partial_ld(N), (int)num_partials(M),
+                   (int)N, dw, nullptr, (int64_t)0, 1u, s);
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
 }
 
