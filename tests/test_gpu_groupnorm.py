@@ -58,8 +58,10 @@ def test_gn_page_shapes(name):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("B,C,S,G", [
-    (2, 8, 4096, 2),      # one full chunk per segment (16-bit)
-    (3, 6, 9000, 3),      # several chunks, ragged last chunk
+    (2, 8, 8192, 2),      # one full chunk per segment (16-bit; two for float32)
+    (2, 8, 4096, 2),      # half a chunk per segment (16-bit)
+    (3, 6, 9000, 3),      # two chunks, ragged last chunk
+    (2, 4, 20000, 2),     # three chunks (16-bit), ragged last chunk
     (2, 4, 1000, 4),      # one channel per group; S * 2 bytes not a multiple of 16 for 16-bit
     (2, 6, 333, 1),       # one group, odd S: element-wise kernels
     (5, 12, 1, 3),        # one element per channel
