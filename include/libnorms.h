@@ -90,8 +90,8 @@ rmsnorm_status layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_
  *     dW_c = sum over batch and space of dy * xhat,      dB_c = sum over batch and space of dy
  *
  * sums over the n = Cg * S elements of a row, in float32 (Liger-Kernel pull request 1608). The
- * work is split into chunks of one (batch, channel) segment (at most 4096 elements for 16-bit types,
- * 2048 for float32); per-chunk statistics and sums go to a caller-provided float32 workspace and are
+ * work is split into chunks of one (batch, channel) segment (at most 8192 elements for 16-bit types,
+ * 4096 for float32); per-chunk statistics and sums go to a caller-provided float32 workspace and are
  * combined in a fixed order, so results are bit-reproducible and no atomics are used. Group sizes
  * up to RMSNORM_MAX_N elements are supported. S * sizeof(T) a multiple of 16 with 16-byte-aligned
  * tensors gives 16-byte accesses; anything else takes element-wise kernels. mean and rstd are

@@ -247,8 +247,9 @@ def test_groupnorm_bwd_rejects(lib, kw, status):
 def test_groupnorm_workspace_bytes(lib):
     f = lib.groupnorm_workspace_bytes
     assert f(2, 4, 8, 2, BF16) == 2 * 4 * 1 * 8
-    assert f(1, 16, 65536, 4, BF16) == 16 * 16 * 8          # 4096-element chunks
-    assert f(1, 16, 65536, 4, F32) == 16 * 32 * 8           # 2048-element chunks
+    assert f(1, 16, 65536, 4, BF16) == 16 * 8 * 8           # 8192-element chunks
+    assert f(1, 16, 65536, 4, F32) == 16 * 16 * 8           # 4096-element chunks
+    assert f(1, 16, 65537, 4, BF16) == 16 * 9 * 8           # a ragged last chunk
     assert f(0, 4, 8, 2, BF16) == 0
     assert f(2, 4, 8, 3, BF16) == 0 and f(2, 0, 8, 1, BF16) == 0 and f(2, 4, 8, 2, 9) == 0
 
