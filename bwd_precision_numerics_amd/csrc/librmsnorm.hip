@@ -17,6 +17,9 @@ constexpr int kBwdRegMaxIters = 2;      // backward register kernel (rows + pref
 // per 1024-thread block, 3 or 4 vectors per thread; the stage holds the row's x and dy
 // (2 * 4096 * 16 bytes = 128 KiB at most) while registers carry the next row's loads.
 constexpr int kBwdLdsMaxIters = 4;
+// Streaming backward with its dw sums in registers: up to 8 vectors per thread (8192 vectors a row
+// at 1024 threads, e.g. N = 65536 in 16-bit types).
+constexpr int kStreamRegVectors = 8;
 // Register backward pipeline per vectors-per-thread: rows per barrier (batch) and batches in flight
 // ahead of the current one. Ring registers: (DEPTH + 1) * RB * ITERS * 2 sixteen-byte vectors.
 template <int ITERS> struct BwdPipe;
@@ -113,6 +116,10 @@ template <DT D, bool AG>
 rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    // 16-byte rows of at most kStreamRegVectors vectors per thread keep their dw sums in registers.
+    const int64_t per_thread = ceil_div(ceil_div(a.N, Elem<D>::VEC), p.tpr);
+    if (p.wide && per_thread <= kStreamRegVectors)
+      return launch(bwd_stream_kernel<D, true, AG, kStreamRegVectors>, p.grid, block, p.lds, s, a);
     return p.wide ? launch(bwd_stream_kernel<D, true, AG>, p.grid, block, p.lds, s, a)
                   : launch(bwd_stream_kernel<D, false, AG>, p.grid, block, p.lds, s, a);
   }

@@ -440,13 +440,18 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
 }
 
 // Any N and any alignment. One row at a time per block (groups = 1); the elementwise pass reads
-// x and dy again, and the block's dw partial row accumulates in the workspace itself (each column
-// is owned by one thread, rows are added in order).
-template <DT D, bool WIDE, bool AG>
+// x and dy again (from the caches). KREG = 0: the block's dw partial row accumulates in the
+// workspace itself (each column is owned by one thread, rows are added in order). KREG > 0 (16-byte
+// vectors, at most KREG per thread: rows past the LDS-staged kernel's reach, up to 8192 vectors):
+// the same sums in registers, written once at the end — per row the workspace round trip would move
+// twice the row's float32 width (the kernel ran at 1.3 TB/s that way). Same operations in the same
+// order either way, so dx and dw are bit-identical between the two.
+template <DT D, bool WIDE, bool AG, int KREG = 0>
 __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
   using IO = VecIO<D, WIDE>;
   using S = typename IO::S;
   constexpr int V = IO::V;
+  static_assert(KREG == 0 || WIDE, "register sums take 16-byte vectors");
   extern __shared__ uint4 smem[];
 
   const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
@@ -456,12 +461,18 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
   float* red = reinterpret_cast<float*>(smem);  // [2][wpr]
   const S* wr = static_cast<const S*>(a.w);
   float* pr = a.part + (int64_t)b * a.ldp;
-
-  for (int v = tl; v < nv; v += TPR) {
-    const int col = v * V;
+  constexpr int K = KREG > 0 ? KREG * V : 1;
+  float acc[K];
 #pragma unroll
-    for (int e = 0; e < V; ++e)
-      if (col + e < N) pr[col + e] = 0.f;
+  for (int k = 0; k < K; ++k) acc[k] = 0.f;
+
+  if constexpr (KREG == 0) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (col + e < N) pr[col + e] = 0.f;
+    }
   }
 
   int s = 0;
@@ -487,7 +498,7 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
     const float dot = group_sum(d.total(), red + (s & 1) * wpr, wpr, tl);
     const float c = dot / (float)N;
     S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
-    for (int v = tl; v < nv; v += TPR) {
+    auto elementwise = [&](int v, float* accv) {
       const int col = v * V;
       const bool full = col + V <= N;
       float xf[V], df[V], wf[V], o[V];
@@ -499,11 +510,39 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
         const float xh = xf[e] * rs;
         const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
         o[e] = rs * (gd - xh * c);
-        if (col + e < N) pr[col + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), pr[col + e]);
+        if constexpr (KREG > 0) {
+          accv[e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), accv[e]);
+        } else {
+          if (col + e < N) pr[col + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), pr[col + e]);
+        }
       }
       const auto out = IO::pack(o);
       if (full) IO::store(dxr + col, out);
       else IO::store_part(dxr + col, out, N - col);
+    };
+    if constexpr (KREG > 0) {
+#pragma unroll
+      for (int k = 0; k < KREG; ++k) {
+        const int v = tl + k * TPR;
+        if (v < nv) elementwise(v, acc + k * V);
+        // One vector at a time, its dw sums done here (the compiler would otherwise keep every
+        // vector's loads and operands live at once next to the accumulators).
+#pragma unroll
+        for (int e = 0; e < V; ++e) asm volatile("" : "+v"(acc[k * V + e]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for (int v = tl; v < nv; v += TPR) elementwise(v, nullptr);
+    }
+  }
+
+  if constexpr (KREG > 0) {
+#pragma unroll
+    for (int k = 0; k < KREG; ++k) {
+      const int col = (tl + k * TPR) * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (col + e < N) pr[col + e] = acc[k * V + e];
     }
   }
 }
