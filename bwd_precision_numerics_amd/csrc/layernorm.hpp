@@ -413,14 +413,16 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   }
 }
 
-// Any N and any alignment. One row at a time per block; the elementwise pass reads x and dy again,
-// and the block's dw (and db) partial rows accumulate in the workspace itself (each column owned by
-// one thread, rows added in order).
-template <DT D, bool WIDE, bool HAS_DB>
+// Any N and any alignment. One row at a time per block; the elementwise pass reads x and dy again.
+// KREG = 0: the block's dw (and db) partial rows accumulate in the workspace itself (each column
+// owned by one thread, rows added in order). KREG > 0 (16-byte vectors, at most KREG per thread):
+// the same sums in registers, written once at the end; bit-identical to KREG = 0.
+template <DT D, bool WIDE, bool HAS_DB, int KREG = 0>
 __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
   using IO = VecIO<D, WIDE>;
   using S = typename IO::S;
   constexpr int V = IO::V;
+  static_assert(KREG == 0 || WIDE, "register sums take 16-byte vectors");
   extern __shared__ uint4 smem[];
 
   const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
@@ -431,14 +433,23 @@ __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
   const S* wr = static_cast<const S*>(a.w);
   float* pw = a.part + (int64_t)b * a.ldp;
   float* pb = a.part + (int64_t)(P + b) * a.ldp;
-
-  for (int v = tl; v < nv; v += TPR) {
-    const int col = v * V;
+  constexpr int K = KREG > 0 ? KREG * V : 1;
+  float accw[K], accb[HAS_DB ? K : 1];
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      if (col + e < N) {
-        pw[col + e] = 0.f;
-        if constexpr (HAS_DB) pb[col + e] = 0.f;
+  for (int k = 0; k < K; ++k) {
+    accw[k] = 0.f;
+    if constexpr (HAS_DB) accb[k] = 0.f;
+  }
+
+  if constexpr (KREG == 0) {
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (col + e < N) {
+          pw[col + e] = 0.f;
+          if constexpr (HAS_DB) pb[col + e] = 0.f;
+        }
       }
     }
   }
@@ -469,7 +480,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
     group_sum_batch<2>(dots, red + (s & 1) * wpr * 2, wpr, tl);
     const float c1 = dots[0] / (float)N, c2 = dots[1] / (float)N;
     S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
-    for (int v = tl; v < nv; v += TPR) {
+    auto elementwise = [&](int v, float* aw, float* ab) {
       const int col = v * V;
       const bool full = col + V <= N;
       float xf[V], df[V], wf[V], o[V];
@@ -481,7 +492,10 @@ __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
         const float xh = (xf[e] - mu) * rs;
         const float gd = wf[e] * df[e];
         o[e] = rs * ((gd - c1) - xh * c2);
-        if (col + e < N) {
+        if constexpr (KREG > 0) {
+          aw[e] = __builtin_fmaf(df[e], xh, aw[e]);
+          if constexpr (HAS_DB) ab[e] += df[e];
+        } else if (col + e < N) {
           pw[col + e] = __builtin_fmaf(df[e], xh, pw[col + e]);
           if constexpr (HAS_DB) pb[col + e] += df[e];
         }
@@ -489,6 +503,36 @@ __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
       const auto out = IO::pack(o);
       if (full) IO::store(dxr + col, out);
       else IO::store_part(dxr + col, out, N - col);
+    };
+    if constexpr (KREG > 0) {
+#pragma unroll
+      for (int k = 0; k < KREG; ++k) {
+        const int v = tl + k * TPR;
+        if (v < nv) elementwise(v, accw + k * V, HAS_DB ? accb + k * V : nullptr);
+        // One vector at a time, its sums done here (see the RMSNorm streaming kernel).
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          asm volatile("" : "+v"(accw[k * V + e]));
+          if constexpr (HAS_DB) asm volatile("" : "+v"(accb[k * V + e]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for (int v = tl; v < nv; v += TPR) elementwise(v, nullptr, nullptr);
+    }
+  }
+
+  if constexpr (KREG > 0) {
+#pragma unroll
+    for (int k = 0; k < KREG; ++k) {
+      const int col = (tl + k * TPR) * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (col + e < N) {
+          pw[col + e] = accw[k * V + e];
+          if constexpr (HAS_DB) pb[col + e] = accb[k * V + e];
+        }
+      }
     }
   }
 }

@@ -18,6 +18,9 @@ constexpr int kLnBwdBlockThreads = 1024;
 constexpr int kLnBwdRegMaxIters = 2;
 // Rows in flight ahead of the current one, and whether xhat and w * dy are kept between the
 // passes, per vectors-per-thread of the register backward.
+// Streaming backward with dw and db sums in registers: up to 4 vectors per thread (4096 vectors a
+// row at 1024 threads, e.g. N = 32768 in 16-bit types).
+constexpr int kLnStreamRegVectors = 4;
 template <int ITERS> struct LnBwdPipe;
 template <> struct LnBwdPipe<1> {
   static constexpr int DEPTH = 1;
@@ -171,6 +174,10 @@ template <DT D, bool HAS_DB>
 rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    // 16-byte rows of at most kLnStreamRegVectors vectors per thread keep dw, db in registers.
+    if (p.wide && ceil_div(ceil_div(a.N, Elem<D>::VEC), p.tpr) <= kLnStreamRegVectors)
+      return launch(ln_bwd_stream_kernel<D, true, HAS_DB, kLnStreamRegVectors>, p.grid, block,
+                    p.lds, s, a);
     return p.wide ? launch(ln_bwd_stream_kernel<D, true, HAS_DB>, p.grid, block, p.lds, s, a)
                   : launch(ln_bwd_stream_kernel<D, false, HAS_DB>, p.grid, block, p.lds, s, a);
   }

@@ -97,6 +97,13 @@ def test_ln_families_agree(dtype, N):
         assert np.allclose(reg[k], stream[k], rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("dtype,N", [("bf16", 20000), ("f16", 32768)])
+def test_ln_wide_rows_register_sums(dtype, N):
+    """Rows past the register kernel take the streaming kernel with dw and db summed in registers
+    over each block's rows: 300 rows over 256 blocks give 44 blocks two rows."""
+    run_ln(dtype, 300, N, seed=22)
+
+
 def test_ln_repeatable():
     _, a = run_ln("bf16", 1000, 4096, seed=9)
     _, b = run_ln("bf16", 1000, 4096, seed=9)

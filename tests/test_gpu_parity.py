@@ -180,6 +180,14 @@ def test_wide_rows_prefetch_pipeline(dtype, N):
     assert np.allclose(lds[3], to_np(dw), rtol=1e-5, atol=1e-6)
 
 
+@pytest.mark.parametrize("dtype,N", [("bf16", 40000), ("f16", 65536)])
+def test_wide_rows_streaming_register_sums(dtype, N):
+    """Rows past the LDS-staged kernel (more than 4096 vectors) take the streaming kernel with the
+    dw sums in registers (up to 8 vectors per thread) over each block's rows: 300 rows give 44
+    blocks two rows."""
+    run_case(dtype, 300, N, seed=23)
+
+
 def test_forward_register_and_lds_staging_at_wide_rows():
     for variant in ("registers", "lds", "streaming"):
         wl = WL["bf16"]
