@@ -15,6 +15,8 @@ namespace {
 // that the threads' vectors tile exactly (N = iters * tpr * 16 / element size: a 4096-wide 16-bit
 // row is then one wavefront with no LDS round).
 constexpr int kSmMaxIters = 4;
+// Float64 streaming backward with its dw sums in registers: up to 8 vectors (16 values) per thread.
+constexpr int kF64StreamRegVectors = 8;
 constexpr int kSmFwdFullMaxIters = 8;
 // Threads per block: the forward's row groups share a block's barriers, so it stays small; the
 // backward was measured faster with 1024.
@@ -208,6 +210,8 @@ rmsnorm_status f64_bwd_impl(const double* dy, int64_t lddy, const double* x, int
   const size_t lds = round16(sizeof(double) * 2 * (a.tpr / 64));
   if (wide && iters == 1) st = launch(rms_f64_bwd_rows_kernel<1>, a.P, a.tpr, lds, s, a);
   else if (wide && iters == 2) st = launch(rms_f64_bwd_rows_kernel<2>, a.P, a.tpr, lds, s, a);
+  else if (wide && iters <= kF64StreamRegVectors)  // dw sums in registers
+    st = launch(rms_f64_bwd_kernel<true, kF64StreamRegVectors>, a.P, a.tpr, lds, s, a);
   else
     st = wide ? launch(rms_f64_bwd_kernel<true>, a.P, a.tpr, lds, s, a)
               : launch(rms_f64_bwd_kernel<false>, a.P, a.tpr, lds, s, a);

@@ -482,10 +482,14 @@ __global__ void __launch_bounds__(1024) rms_f64_fwd_kernel(F64Args a) {
   }
 }
 
-template <bool WIDE>
+// KREG > 0 (16-byte vectors, at most KREG per thread): the dw sums stay in registers and are
+// written once, instead of a float64 round trip through the workspace per row; same operations in
+// the same order, bit-identical.
+template <bool WIDE, int KREG = 0>
 __global__ void __launch_bounds__(1024) rms_f64_bwd_kernel(F64Args a) {
   using IO = NumIO<DT::F64, WIDE>;
   constexpr int V = IO::V;
+  static_assert(KREG == 0 || WIDE, "register sums take 16-byte vectors");
   extern __shared__ uint4 smem[];
   const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
   const int nv = (N + V - 1) / V;
@@ -493,11 +497,17 @@ __global__ void __launch_bounds__(1024) rms_f64_bwd_kernel(F64Args a) {
   const int b = blockIdx.x, P = a.P;
   double* red = reinterpret_cast<double*>(smem);  // [2][wpr]
   double* pr = a.part + (int64_t)b * N;
-  // zeroed by the thread that owns each column below (same mapping, program order)
-  for (int v = tl; v < nv; v += TPR) {
+  constexpr int K = KREG > 0 ? KREG * V : 1;
+  double acc[K];
 #pragma unroll
-    for (int e = 0; e < V; ++e)
-      if (v * V + e < N) pr[v * V + e] = 0.0;
+  for (int k = 0; k < K; ++k) acc[k] = 0.0;
+  if constexpr (KREG == 0) {
+    // zeroed by the thread that owns each column below (same mapping, program order)
+    for (int v = tl; v < nv; v += TPR) {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (v * V + e < N) pr[v * V + e] = 0.0;
+    }
   }
   int s = 0;
   for (int64_t row = b; row < a.M; row += P, ++s) {
@@ -520,7 +530,7 @@ __global__ void __launch_bounds__(1024) rms_f64_bwd_kernel(F64Args a) {
     }
     const double c = group_reduce<false>(d0 + d1, red + (s & 1) * wpr, wpr, tl) / (double)N;
     double* xo = a.out + row * a.ldo;
-    for (int v = tl; v < nv; v += TPR) {
+    auto elementwise = [&](int v, double* accv) {
       const int col = v * V;
       double f[V], df[V], wf[V], o[V];
       IO::unpack(IO::load(xr + col, N - col), f);
@@ -530,9 +540,28 @@ __global__ void __launch_bounds__(1024) rms_f64_bwd_kernel(F64Args a) {
       for (int e = 0; e < V; ++e) {
         const double xh = f[e] * rs, gd = (a.offset + wf[e]) * df[e];
         o[e] = rs * (gd - xh * c);
-        if (col + e < N) pr[col + e] = fma(df[e], xh, pr[col + e]);
+        if constexpr (KREG > 0) accv[e] = fma(df[e], xh, accv[e]);
+        else if (col + e < N) pr[col + e] = fma(df[e], xh, pr[col + e]);
       }
       IO::store(xo + col, o, N - col);
+    };
+    if constexpr (KREG > 0) {
+#pragma unroll
+      for (int k = 0; k < KREG; ++k) {
+        const int v = tl + k * TPR;
+        if (v < nv) elementwise(v, acc + k * V);
+      }
+    } else {
+      for (int v = tl; v < nv; v += TPR) elementwise(v, nullptr);
+    }
+  }
+  if constexpr (KREG > 0) {
+#pragma unroll
+    for (int k = 0; k < KREG; ++k) {
+      const int col = (tl + k * TPR) * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (col + e < N) pr[col + e] = acc[k * V + e];
     }
   }
 }
