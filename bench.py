@@ -26,6 +26,8 @@ Measurement:
   null when the kernel sources have changed since that summary was taken.
 * copy_ceiling: a device-to-device copy with the forward's traffic, timed the same way; value is
   also reported as a fraction of it.
+* bwd_ceiling: an elementwise add with the backward's traffic pattern (read x and dy, write dx),
+  timed the same way; the backward rows kernel's bandwidth is also reported as a fraction of it.
 * cpu_baseline: the CPU oracle (NumPy, one thread) on a bounded sample of the same rows.
 * rows: LayerNorm, softmax, GroupNorm and the float64 RMSNorm, forward and backward, timed the same
   way (graph of back-to-back launches over rotating buffers), each with its own CPU oracle sample.
@@ -250,6 +252,22 @@ def copy_ceiling(torch, sets, launches):
     nbytes = 2 * sets.sets[0]["x"].numel() * sets.sets[0]["x"].element_size()
     return {"GBps": round(nbytes / sec / 1e9, 1), "us": round(sec * 1e6, 3),
             "bytes_per_launch": nbytes, "what": "hipMemcpy device-to-device, read x write y"}
+
+
+def add_ceiling(torch, sets, launches):
+    """An elementwise add dx = x + dy over the rotating sets (torch's vectorized kernel): the
+    backward's traffic pattern, two streams read and one written, without its row reductions, dw
+    sums or persistent grid, timed like the kernels."""
+    n = len(sets.sets)
+
+    def add(k):
+        s = sets.sets[k % n]
+        torch.add(s["x"], s["dy"], out=s["dx"])
+
+    sec = graph_time(torch, add, launches)
+    nbytes = 3 * sets.sets[0]["x"].numel() * sets.sets[0]["x"].element_size()
+    return {"GBps": round(nbytes / sec / 1e9, 1), "us": round(sec * 1e6, 3),
+            "bytes_per_launch": nbytes, "what": "torch.add(x, dy, out=dx): read x and dy, write dx"}
 
 
 def graph_time(torch, fn, launches):
@@ -573,7 +591,7 @@ def main(argv=None) -> int:
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: librmsnorm has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
@@ -632,6 +650,7 @@ def main(argv=None) -> int:
 
     dur = kernel_durations(torch, sets, max(args.steps, 20))
     copy = copy_ceiling(torch, sets, max(args.steps, 20))
+    addc = add_ceiling(torch, sets, max(args.steps, 20))
     del graph
     s = wl.itemsize
     rows_bytes = 3 * wl.M * wl.N * s + wl.N * s + 4 * wl.M
@@ -670,6 +689,8 @@ def main(argv=None) -> int:
                                     1)},
         "copy_ceiling": copy,
         "frac_of_copy_ceiling": round(value / copy["GBps"], 4),
+        "bwd_ceiling": addc,
+        "bwd_rows_frac_of_bwd_ceiling": round(achieved / addc["GBps"], 4),
     }
     if not args.no_rows and name == HEADLINE:
         launches = max(min(args.steps, 100), 20)
