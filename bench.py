@@ -94,7 +94,8 @@ def parse_args(argv=None):
     ap.add_argument("--rotate-mib", type=int, default=1024,
                     help="rotate over enough buffer sets that the x matrices span this many MiB")
     ap.add_argument("--no-graph", action="store_true",
-                    help="launch the timed steps eagerly instead of replaying a graph")
+                    help="launch everything eagerly (steps, per-kernel timings, rows) instead "
+                         "of replaying graphs, so per-dispatch profiler counters see each launch")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--kernel-only", choices=["fwd", "bwd_rows", "dw_reduce", "fwd_fp8"],
@@ -198,8 +199,28 @@ def copy_probe(torch, mib, steps):
                       "GBps": 2 * n * 4 * steps / dt / 1e9}), flush=True)
 
 
+class Eager:
+    """Stands in for a captured graph under --no-graph: replay() makes the calls directly on the
+    current stream, so a profiler that counts per dispatch sees every launch."""
+
+    def __init__(self, fn, count):
+        self.fn, self.count = fn, count
+
+    def replay(self):
+        for k in range(self.count):
+            self.fn(k)
+
+
+EAGER = False  # set by --no-graph
+
+
 def capture(torch, fn, count):
-    """A graph of `count` back-to-back calls fn(0), fn(1), ... on the capture stream."""
+    """A graph of `count` back-to-back calls fn(0), fn(1), ... on the capture stream (direct calls
+    under --no-graph)."""
+    if EAGER:
+        fn(0)
+        torch.cuda.synchronize()
+        return Eager(fn, count)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -589,6 +610,8 @@ def cpu_baseline(wl, rounding, inp, budget_s):
 
 def main(argv=None) -> int:
     args = parse_args(argv)
+    global EAGER
+    EAGER = args.no_graph
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: librmsnorm has no multi-GPU path "

@@ -553,7 +553,8 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
 // adds them in order of i; the four lanes of a column (l / 16 = 0..3) are then added in order, and
 // finally the four waves in order. blockIdx.y selects one of gridDim.y sets of partial rows,
 // set_stride floats apart, and its output (dw, or dw2 for the second set).
-// T is float, or double for the float64 RMSNorm.
+// The float64 RMSNorm reduces its double partials with it; float32 partials take
+// dw_reduce32_kernel or dw_reduce4_kernel below.
 static_assert(kMaxPartials % 16 == 0, "dw_reduce_kernel reads partial rows in groups of 16");
 template <typename T>
 __global__ void __launch_bounds__(256) dw_reduce_kernel(const T* part, int64_t ldp, int P, int N,
@@ -588,7 +589,7 @@ __global__ void __launch_bounds__(256) dw_reduce_kernel(const T* part, int64_t l
 // additions per column, but each lane reads 4 consecutive columns (16 lanes cover 64 columns, 256
 // contiguous bytes of a partial row, instead of 64), so a block owns 64 columns. Partial rows are
 // padded to a multiple of 4 floats (partial_ld), so a vector that starts below N stays inside its
-// row. Bit-identical to dw_reduce_kernel<float>.
+// row. It adds in the order dw_reduce_kernel would for float partials.
 inline __global__ void __launch_bounds__(256) dw_reduce4_kernel(const float* part, int64_t ldp,
                                                                 int P, int N, float* dw,
                                                                 float* dw2, int64_t set_stride) {
@@ -639,19 +640,75 @@ inline __global__ void __launch_bounds__(256) dw_reduce4_kernel(const float* par
   }
 }
 
+// The float32 reduction for rows below kReduce4MinN: a block owns 32 columns, one whole 128-byte
+// line of every partial row (16 columns of 4 bytes left each line half used, and the neighbouring
+// block, on another XCD, fetched the same line again: the counters read twice the partial bytes).
+// Lane l of wave k reads columns 4 * (l % 8) .. + 3 of partial rows p = 32 * i + 8 * k + l / 8
+// (i = 0 .. kMaxPartials / 32 - 1, all loads in flight together) and adds them in order of i; the
+// eight row phases of a wave (l / 8) are added by a butterfly over lane bits 3, 4, 5 (IEEE addition
+// commutes, so every lane ends with the same bits), then the four waves in order.
+static_assert(kMaxPartials % 32 == 0, "dw_reduce32_kernel reads partial rows in groups of 32");
+inline __global__ void __launch_bounds__(256) dw_reduce32_kernel(const float* part, int64_t ldp,
+                                                                 int P, int N, float* dw,
+                                                                 float* dw2, int64_t set_stride) {
+  if (blockIdx.y) {
+    part += set_stride;
+    dw = dw2;
+  }
+  constexpr int L = kMaxPartials / 32;
+  __shared__ float4 buf[4][8];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c4 = lane & 7, ph = lane >> 3;
+  const int col = blockIdx.x * 32 + c4 * 4;
+  float4 v[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int p = 32 * i + 8 * wv + ph;
+    v[i] = (col < N && p < P) ? *reinterpret_cast<const float4*>(part + (int64_t)p * ldp + col)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float4 t = v[0];
+#pragma unroll
+  for (int i = 1; i < L; ++i) {
+    t.x += v[i].x;
+    t.y += v[i].y;
+    t.z += v[i].z;
+    t.w += v[i].w;
+  }
+#pragma unroll
+  for (int m = 8; m < 64; m <<= 1) {
+    t.x += __shfl_xor(t.x, m, 64);
+    t.y += __shfl_xor(t.y, m, 64);
+    t.z += __shfl_xor(t.z, m, 64);
+    t.w += __shfl_xor(t.w, m, 64);
+  }
+  if (ph == 0) buf[wv][c4] = t;
+  __syncthreads();
+  if (wv == 0 && ph == 0 && col < N) {
+    const float4 a = buf[0][c4], b = buf[1][c4], d = buf[2][c4], e = buf[3][c4];
+    const float r[4] = {((a.x + b.x) + d.x) + e.x, ((a.y + b.y) + d.y) + e.y,
+                        ((a.z + b.z) + d.z) + e.z, ((a.w + b.w) + d.w) + e.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (col + k < N) dw[col + k] = r[k];
+  }
+}
+
 // Host side: the fixed-order float32 reduction of P partial rows into dw (and of the next P rows,
-// set_stride floats on, into dw2 when sets = 2). The 16-byte kernel owns 64 columns per block and
-// measured faster from N = 8192 on (N = 32768: 11.6 -> 3.6 us); below that it leaves compute units
-// idle (64 blocks at N = 4096), so the 4-byte kernel serves. Both add in the same order.
-constexpr int kReduce4MinN = 8192;
+// set_stride floats on, into dw2 when sets = 2). Rows below kReduce4MinN take the 32-column kernel
+// (N = 4096: 3.18 -> 2.82 us against 16 columns of 4-byte loads; N = 8192: 3.21 us against 3.32 for
+// the 64-column kernel); from kReduce4MinN on the 64-column kernel is as fast or faster (N = 32768:
+// 7.6 us against 8.2). The two add in different orders, each fixed, and the choice depends on N
+// alone, so dw stays a function of the inputs.
+constexpr int kReduce4MinN = 16384;
 inline void launch_dw_reduce(const float* part, int64_t ldp, int P, int N, float* dw, float* dw2,
                              int64_t set_stride, unsigned sets, hipStream_t s) {
   if (N >= kReduce4MinN)
     hipLaunchKernelGGL(dw_reduce4_kernel, dim3((unsigned)((N + 63) / 64), sets), dim3(256), 0, s,
                        part, ldp, P, N, dw, dw2, set_stride);
   else
-    hipLaunchKernelGGL(dw_reduce_kernel<float>, dim3((unsigned)((N + 15) / 16), sets), dim3(256),
-                       0, s, part, ldp, P, N, dw, dw2, set_stride);
+    hipLaunchKernelGGL(dw_reduce32_kernel, dim3((unsigned)((N + 31) / 32), sets), dim3(256), 0, s,
+                       part, ldp, P, N, dw, dw2, set_stride);
 }
 
 inline __global__ void fill_zero_kernel(float* p, int n) {
