@@ -313,8 +313,8 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
       rd[slot][it] = IO::zero();
       if (ok) {
         if (FULL || col + V <= N) {
-          rx[slot][it] = IO::load(xr + col);
-          rd[slot][it] = IO::load(dr + col);
+          rx[slot][it] = IO::load_nt(xr + col);
+          rd[slot][it] = IO::load_nt(dr + col);
         } else if (col < N) {
           rx[slot][it] = IO::load_part(xr + col, N - col);
           rd[slot][it] = IO::load_part(dr + col, N - col);

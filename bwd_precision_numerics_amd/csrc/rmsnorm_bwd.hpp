@@ -197,8 +197,8 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
         rd[slot][k][it] = IO::zero();
         if (li < nloc) {
           if (FULL || col + V <= N) {
-            rx[slot][k][it] = IO::load(at(xr, col));
-            rd[slot][k][it] = IO::load(at(dr, col));
+            rx[slot][k][it] = IO::load_nt(at(xr, col));
+            rd[slot][k][it] = IO::load_nt(at(dr, col));
           } else if (col < N) {
             rx[slot][k][it] = IO::load_part(at(xr, col), N - col);
             rd[slot][k][it] = IO::load_part(at(dr, col), N - col);
@@ -343,8 +343,8 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
       rx[it] = rd[it] = IO::zero();
       if (ok) {
         if (FULL || col + V <= N) {
-          rx[it] = IO::load_b(xb, voff, soff);
-          rd[it] = IO::load_b(db, voff, soff);
+          rx[it] = IO::load_b_nt(xb, voff, soff);
+          rd[it] = IO::load_b_nt(db, voff, soff);
         } else if (col < N) {
           rx[it] = IO::load_part(at(xr, col), N - col);
           rd[it] = IO::load_part(at(dr, col), N - col);

@@ -87,7 +87,7 @@ template <DT D, bool WIDE> struct VecIO;
 // only bytes of the row they own (partial vectors take the element-wise path).
 using BufRsrc = __amdgpu_buffer_rsrc_t;
 constexpr int kBufDword3 = 0x00020000;
-constexpr int kBufNonTemporal = 2;  // cache-policy operand: non-temporal (nt) stores
+constexpr int kBufNonTemporal = 2;  // cache-policy operand: non-temporal (nt) accesses
 template <typename T>
 __device__ __forceinline__ BufRsrc buf_rsrc(const T* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, 0x7fffffff, kBufDword3);
@@ -109,6 +109,16 @@ template <DT D> struct VecIO<D, true> {
   }
   static __device__ __forceinline__ Raw load(const S* p) {
     return *reinterpret_cast<const uint4*>(p);
+  }
+  // Non-temporal (nt) load, for streams read exactly once whose lines need not stay in the caches.
+  static __device__ __forceinline__ Raw load_nt(const S* p) {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(uint4,
+                              __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+  }
+  static __device__ __forceinline__ Raw load_b_nt(BufRsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff,
+                                                                           kBufNonTemporal));
   }
   static __device__ __forceinline__ Raw load_part(const S* p, int n) {
     S tmp[V];
@@ -159,6 +169,7 @@ template <DT D> struct VecIO<D, false> {
   using Raw = S;
   static __device__ __forceinline__ Raw zero() { return S(0); }
   static __device__ __forceinline__ Raw load(const S* p) { return *p; }
+  static __device__ __forceinline__ Raw load_nt(const S* p) { return *p; }
   static __device__ __forceinline__ Raw load_part(const S* p, int) { return *p; }
   static __device__ __forceinline__ void store(S* p, Raw r) { *p = r; }
   static __device__ __forceinline__ void store_part(S* p, Raw r, int) { *p = r; }

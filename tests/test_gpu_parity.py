@@ -71,6 +71,7 @@ SHAPES = [
     (257, 3072, None),
     (64, 4096, None),
     (40, 8192, None),
+    (20, 16383, None),     # widest row of the 32-column dw reduction, partial last vector
     (24, 16384, None),
     (12, 32768, None),     # LDS-staged backward
     (6, 40000, None),      # streaming backward (beyond the LDS kernel's width)
