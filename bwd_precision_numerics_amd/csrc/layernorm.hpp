@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
     Raw r = IO::zero(), rw = IO::zero(), rb = IO::zero();
     if (valid) {
       if (FULL || col + V <= N) {
-        r = IO::load(xr + col);
+        r = IO::load_nt(xr + col);
         if constexpr (!LATE_WB) {
           rw = IO::load(wr + col);
           if constexpr (HAS_B) rb = IO::load(br + col);

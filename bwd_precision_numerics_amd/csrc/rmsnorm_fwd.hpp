@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
     Raw r = IO::zero(), rw = IO::zero();
     if (valid) {
       if (FULL || col + V <= N) {
-        r = IO::load(xr + col);
+        r = IO::load_nt(xr + col);
         rw = IO::load(wr + col);
       } else if (col < N) {
         r = IO::load_part(xr + col, N - col);

@@ -34,6 +34,10 @@ template <DT D, bool WIDE> struct NumIO {
   static __device__ __forceinline__ Raw load(const S* p, int n) {
     return n >= V ? IO::load(p) : IO::load_part(p, n);
   }
+  // Non-temporal for full vectors: streams read exactly once.
+  static __device__ __forceinline__ Raw load_nt(const S* p, int n) {
+    return n >= V ? IO::load_nt(p) : IO::load_part(p, n);
+  }
   static __device__ __forceinline__ void unpack(const Raw& r, float (&f)[V]) { IO::unpack(r, f); }
   static __device__ __forceinline__ void store(S* p, const float (&f)[V], int n) {
     const Raw r = IO::pack(f);
@@ -49,6 +53,13 @@ template <> struct NumIO<DT::F64, true> {
     if (n >= 2) return *reinterpret_cast<const uint4*>(p);
     const uint2 u = __builtin_bit_cast(uint2, n > 0 ? p[0] : 0.0);
     return make_uint4(u.x, u.y, 0u, 0u);
+  }
+  static __device__ __forceinline__ Raw load_nt(const S* p, int n) {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    if (n >= 2)
+      return __builtin_bit_cast(uint4,
+                                __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+    return load(p, n);
   }
   static __device__ __forceinline__ void unpack(const Raw& r, double (&f)[2]) {
     f[0] = __builtin_bit_cast(double, make_uint2(r.x, r.y));
@@ -70,6 +81,7 @@ template <> struct NumIO<DT::F64, false> {
   using Raw = double;
   static constexpr int V = 1;
   static __device__ __forceinline__ Raw load(const S* p, int) { return *p; }
+  static __device__ __forceinline__ Raw load_nt(const S* p, int) { return *p; }
   static __device__ __forceinline__ void unpack(const Raw& r, double (&f)[1]) { f[0] = r; }
   static __device__ __forceinline__ void store(S* p, const double (&f)[1], int) { *p = f[0]; }
 };
@@ -360,8 +372,8 @@ __global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
       if (valid && col < N) {
-        ry[it] = IO::load(yr + col, N - col);
-        rd[it] = IO::load(dr + col, N - col);
+        ry[it] = IO::load_nt(yr + col, N - col);
+        rd[it] = IO::load_nt(dr + col, N - col);
       } else {
         ry[it] = IO::load(yr, 0);
         rd[it] = IO::load(dr, 0);
@@ -591,7 +603,7 @@ __global__ void __launch_bounds__(1024) rms_f64_fwd_rows_kernel(F64Args a) {
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
     const bool ok = valid && col < N;
-    rx[it] = IO::load(xr + (ok ? col : 0), ok ? N - col : 0);
+    rx[it] = IO::load_nt(xr + (ok ? col : 0), ok ? N - col : 0);
     rw[it] = IO::load(a.w + (ok ? col : 0), ok ? N - col : 0);
   }
   double q0 = 0, q1 = 0;
@@ -652,8 +664,8 @@ __global__ void __launch_bounds__(1024) rms_f64_bwd_rows_kernel(F64Args a) {
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
       const bool ok = col < N;
-      rx[slot][it] = IO::load(a.x + row * a.ldx + (ok ? col : 0), ok ? N - col : 0);
-      rd[slot][it] = IO::load(a.dy + row * a.lddy + (ok ? col : 0), ok ? N - col : 0);
+      rx[slot][it] = IO::load_nt(a.x + row * a.ldx + (ok ? col : 0), ok ? N - col : 0);
+      rd[slot][it] = IO::load_nt(a.dy + row * a.lddy + (ok ? col : 0), ok ? N - col : 0);
     }
   };
   const int64_t nloc = block_rows(a.M, P, b);
