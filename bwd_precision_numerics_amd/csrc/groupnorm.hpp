@@ -93,7 +93,9 @@ __device__ __forceinline__ Chunk chunk_of(const GnArgs& a, int64_t u) {
   return ch;
 }
 
-// Loads of one chunk: thread t holds vectors t and t + 256 (WIDE) or elements t + 256 i.
+// Loads of one chunk: thread t holds vectors t and t + 256 (WIDE) or elements t + 256 i. LAST:
+// the kernel's read is the last one of these bytes (the second pass), so whole vectors take
+// non-temporal loads; the first pass reads normally and leaves the lines to the caches.
 template <DT D, bool WIDE>
 struct ChunkIO {
   using IO = VecIO<D, WIDE>;
@@ -101,12 +103,13 @@ struct ChunkIO {
   using Raw = typename IO::Raw;
   static constexpr int V = IO::V;
   static constexpr int IT = gn_chunk<D>() / (kGnThreads * V);
+  template <bool LAST = false>
   static __device__ __forceinline__ void load(const S* p, int cnt, Raw (&r)[IT]) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int col = (it * kGnThreads + (int)threadIdx.x) * V;
       r[it] = IO::zero();
-      if (col + V <= cnt) r[it] = IO::load(p + col);
+      if (col + V <= cnt) r[it] = LAST ? IO::load_nt(p + col) : IO::load(p + col);
       else if (col < cnt) r[it] = IO::load_part(p + col, cnt - col);
     }
   }
@@ -184,7 +187,8 @@ __global__ void __launch_bounds__(kGnThreads) gn_fwd_kernel(GnArgs a) {
   const Chunk ch = chunk_of<D>(a, blockIdx.x);
   const int g = (int)(ch.c / a.Cg);
   typename CI::Raw r[IT];
-  CI::load(static_cast<const S*>(a.x) + ch.base, ch.cnt, r);  // in flight during the merge
+  // in flight during the merge
+  CI::template load<true>(static_cast<const S*>(a.x) + ch.base, ch.cnt, r);
   if (threadIdx.x < 64) {
     const Moments mo = row_moments<D>(a, ch.bidx, g);
     if (threadIdx.x == 0) {
@@ -297,8 +301,8 @@ __global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
   const float mean = a.mean[row], rs = a.rstd[row];
   const S* wp = static_cast<const S*>(a.w);
   typename CI::Raw rx[IT], rd[IT];
-  CI::load(static_cast<const S*>(a.x) + ch.base, ch.cnt, rx);
-  CI::load(static_cast<const S*>(a.dy) + ch.base, ch.cnt, rd);
+  CI::template load<true>(static_cast<const S*>(a.x) + ch.base, ch.cnt, rx);
+  CI::template load<true>(static_cast<const S*>(a.dy) + ch.base, ch.cnt, rd);
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int nent = a.Cg * a.K;

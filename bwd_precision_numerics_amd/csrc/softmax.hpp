@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
         const int col = (it * TPR + tl) * V;
-        IO::unpack(IO::load(xr + col, V), ev[it]);
+        IO::unpack(IO::load_nt(xr + col, V), ev[it]);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           mx = fmax(mx, ev[it][e]);
