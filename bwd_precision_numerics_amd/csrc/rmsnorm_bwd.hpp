@@ -502,8 +502,9 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
       const int col = v * V;
       const bool full = col + V <= N;
       float xf[V], df[V], wf[V], o[V];
-      IO::unpack(full ? IO::load(xr + col) : IO::load_part(xr + col, N - col), xf);
-      IO::unpack(full ? IO::load(dr + col) : IO::load_part(dr + col, N - col), df);
+      // the row's last read of x and dy: non-temporal
+      IO::unpack(full ? IO::load_nt(xr + col) : IO::load_part(xr + col, N - col), xf);
+      IO::unpack(full ? IO::load_nt(dr + col) : IO::load_part(dr + col, N - col), df);
       IO::unpack(full ? IO::load(wr + col) : IO::load_part(wr + col, N - col), wf);
 #pragma unroll
       for (int e = 0; e < V; ++e) {

@@ -213,7 +213,8 @@ __global__ void __launch_bounds__(1024) fwd_stream_kernel(FwdArgs a) {
   for (int v = tl; v < nv; v += TPR) {
     const int col = v * V;
     const bool full = col + V <= N;
-    const auto r = full ? IO::load(xr + col) : IO::load_part(xr + col, N - col);
+    // the row's last read of x: non-temporal
+    const auto r = full ? IO::load_nt(xr + col) : IO::load_part(xr + col, N - col);
     const auto wv = full ? IO::load(wr + col) : IO::load_part(wr + col, N - col);
     float xf[V], wf[V], yf[V];
     IO::unpack(r, xf);
