@@ -34,17 +34,27 @@ template <> struct BwdPipe<2> {
 
 int bwd_batch(int iters) { return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB; }
 
-rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
+// Automatic selection prefers the register kernel, then the LDS-staged one, except for two
+// instantiations that spill registers and measured slower than the streaming kernel (bf16, M = 4096):
+// the 2-vector register kernel with the autograd casts (N = 16384: 144 us against 127) and the
+// 4-vector LDS-staged kernel on rows its vectors do not tile (N = 30000: 256 us against 212;
+// N = 32760: 271 against 233). The families give bit-identical results, so this changes only speed.
+rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, bool ag,
                         rmsnorm_variant req, Plan* p) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
   int tpr, iters;
   bwd_shape(nv_wide, &tpr, &iters);
   const bool reg_ok = wide_ok && iters <= kBwdRegMaxIters;
   const bool lds_ok = wide_ok && iters <= kBwdLdsMaxIters;
+  const bool tiled = (int64_t)iters * tpr * vec_elems(dtype) == N;
   rmsnorm_variant v = req;
   if (v == RMSNORM_VARIANT_AUTO) {
-    v = reg_ok ? RMSNORM_VARIANT_REGISTERS
-               : (lds_ok ? RMSNORM_VARIANT_LDS : RMSNORM_VARIANT_STREAMING);
+    if (reg_ok)
+      v = ag && iters == 2 ? RMSNORM_VARIANT_STREAMING : RMSNORM_VARIANT_REGISTERS;
+    else if (lds_ok)
+      v = iters == 4 && !tiled ? RMSNORM_VARIANT_STREAMING : RMSNORM_VARIANT_LDS;
+    else
+      v = RMSNORM_VARIANT_STREAMING;
   }
   if (v == RMSNORM_VARIANT_REGISTERS && !reg_ok) return RMSNORM_ERR_UNSUPPORTED;
   if (v == RMSNORM_VARIANT_LDS && !lds_ok) return RMSNORM_ERR_UNSUPPORTED;
@@ -245,8 +255,9 @@ rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_
   const int eb = elem_bytes(dtype);
   const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) && wide_fits(dx, lddx, eb) &&
                     aligned(w, 16);
+  const bool ag = autograd_casts(rounding, dtype);
   Plan p;
-  if ((st = plan_bwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  if ((st = plan_bwd(M, N, dtype, wide, ag, variant, &p)) != RMSNORM_OK) return st;
   if (M == 0) return RMSNORM_OK;
 
   BwdArgs a;
@@ -257,7 +268,6 @@ rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_
   a.tpr = p.tpr; a.groups = p.groups; a.offset = offset;
   a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool ag = autograd_casts(rounding, dtype);
   switch (dtype) {
     case RMSNORM_DTYPE_F32:
       return bwd_dispatch<DT::F32, false>(p, a, s);
@@ -306,7 +316,9 @@ rmsnorm_status bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx
     const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) &&
                       wide_fits(dx, lddx, eb) && aligned(w, 16);
     Plan p;
-    if ((st = plan_bwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+    if ((st = plan_bwd(M, N, dtype, wide, autograd_casts(rounding, dtype), variant, &p)) !=
+        RMSNORM_OK)
+      return st;
   }
   st = bwd_rows_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace, workspace_bytes_given, M, N,
                      dtype, offset, rounding, variant, stream);
