@@ -105,6 +105,9 @@ def parse_args(argv=None):
                     help="skip the LayerNorm / GroupNorm measurements")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration RMSNorm sweep")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure torch's fill, copy and add kernels at several sizes "
+                         "and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, copy a buffer of this many MiB --steps times "
                          "(calibrates the HBM byte counters)")
@@ -289,6 +292,36 @@ def add_ceiling(torch, sets, launches):
     nbytes = 3 * sets.sets[0]["x"].numel() * sets.sets[0]["x"].element_size()
     return {"GBps": round(nbytes / sec / 1e9, 1), "us": round(sec * 1e6, 3),
             "bytes_per_launch": nbytes, "what": "torch.add(x, dy, out=dx): read x and dy, write dx"}
+
+
+def ceilings(torch, launches):
+    """HBM ceilings of plain torch elementwise kernels on this device: write-only (a fill), copy
+    (read + write) and add (two reads + one write), over buffers of several sizes rotating through
+    at least 2 GiB, timed like the kernels (graph of back-to-back launches). torch's reductions do
+    not reach the read bandwidth, so there is no read-only probe."""
+    out = []
+    for mib in (32, 64, 256, 1024):
+        n = mib * 2**20 // 2  # bf16 elements per buffer
+        nsets = max(2, -(-2048 // mib))
+        a = [torch.ones(n, dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
+        b = [torch.ones(n, dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
+        c = [torch.empty(n, dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
+        nb = n * 2
+        probes = {
+            "write": (lambda k: c[k % nsets].fill_(1.0), nb),
+            "copy": (lambda k: c[k % nsets].copy_(a[k % nsets]), 2 * nb),
+            "add": (lambda k: torch.add(a[k % nsets], b[k % nsets], out=c[k % nsets]), 3 * nb),
+        }
+        row = {"buffer_MiB": mib, "buffer_sets": nsets}
+        for name, (fn, nbytes) in probes.items():
+            sec = graph_time(torch, fn, launches)
+            row[name + "_GBps"] = round(nbytes / sec / 1e9, 1)
+            row[name + "_us"] = round(sec * 1e6, 3)
+        out.append(row)
+        print(json.dumps(row), flush=True)
+        del a, b, c
+        torch.cuda.empty_cache()
+    return out
 
 
 def graph_time(torch, fn, launches):
@@ -630,6 +663,9 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib, args.steps)
+        return 0
+    if args.ceilings:
+        ceilings(torch, max(min(args.steps, 100), 20))
         return 0
 
     name = args.workload or HEADLINE
