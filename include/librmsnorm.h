@@ -93,8 +93,9 @@ typedef enum rmsnorm_fp8_format {
   RMSNORM_FP8_E5M2 = 1   /* bias 15, largest finite 57344, IEEE-style: overflow gives +-inf */
 } rmsnorm_fp8_format;
 
-/* Kernel family. AUTO picks by dtype and N. The others force one family, for consistency tests
- * and measurements; a forced family that cannot serve the arguments returns
+/* Kernel family. AUTO picks by dtype and N (and, in the backward, the autograd-casts flag), for
+ * speed; rstd, y and dx do not depend on the family. The others force one family, for consistency
+ * tests and measurements; a forced family that cannot serve the arguments returns
  * RMSNORM_ERR_UNSUPPORTED with nothing launched.
  *   REGISTERS  a row lives in registers between the reduction and the elementwise pass
  *   LDS        a row is staged in LDS between the two passes (same thread-to-element mapping and
