@@ -150,15 +150,20 @@ def dtype_name(t) -> str:
 
 
 def _rows(t, name: str):
-    """Check a 2-D device tensor with unit column stride; return (ptr, row stride)."""
+    """Check a 2-D device tensor with unit column stride and rows that do not overlap; return
+    (ptr, row stride). A broadcast view (row stride 0) or any row stride below N is refused: the
+    kernels address M rows of N elements at the row stride."""
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D [M, N], got shape {tuple(t.shape)}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit stride along the last dimension")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} has overlapping rows (row stride {t.stride(0)} < {t.shape[1]}); "
+                         "pass a contiguous copy")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
     ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
-    return t.data_ptr(), max(ld, t.shape[1])
+    return t.data_ptr(), ld
 
 
 def _vec(t, name: str, n: int):
@@ -591,6 +596,15 @@ def bwd_f64(dy, x, w, rstd, offset: float = 0.0, dx=None, dw=None, workspace=Non
     return dx, dw
 
 
+def _as_rows(t, n: int):
+    """``t`` as a 2-D [rows, n] view the kernels can address (unit column stride, rows that do not
+    overlap), copying only when it is not: gradients often arrive as broadcast views."""
+    t2 = t.reshape(-1, n)
+    if (n > 1 and t2.stride(-1) != 1) or (t2.shape[0] > 1 and t2.stride(0) < n):
+        t2 = t2.contiguous()
+    return t2
+
+
 def _make_autograd():
     torch = _torch()
 
@@ -600,7 +614,7 @@ def _make_autograd():
         @staticmethod
         def forward(ctx, x, w, eps, offset, rounding, casts):
             shape = x.shape
-            x2 = x.reshape(-1, shape[-1])
+            x2 = _as_rows(x, shape[-1])
             y, rstd = fwd(x2, w, eps=eps, offset=offset, rounding=rounding)
             ctx.save_for_backward(x2, w, rstd)
             ctx.cfg = (eps, offset, rounding, shape, casts)
@@ -610,9 +624,7 @@ def _make_autograd():
         def backward(ctx, gy):
             x2, w, rstd = ctx.saved_tensors
             eps, offset, rounding, shape, casts = ctx.cfg
-            gy2 = gy.reshape(-1, shape[-1])
-            if gy2.stride(-1) != 1:
-                gy2 = gy2.contiguous()
+            gy2 = _as_rows(gy, shape[-1])
             dx, dw = bwd(gy2, x2, w, rstd, eps=eps, offset=offset, rounding=rounding, casts=casts)
             return dx.reshape(shape), dw.to(w.dtype), None, None, None, None
 
@@ -634,15 +646,11 @@ def rms_norm(x, w, eps: float = 1e-6, offset: float = 0.0, rounding: str = "twic
 def _make_autograd_widened():
     torch = _torch()
 
-    def rows(t, n):
-        t2 = t.reshape(-1, n)
-        return t2 if t2.stride(-1) == 1 else t2.contiguous()
-
     class LayerNormFunction(torch.autograd.Function):
         @staticmethod
         def forward(ctx, x, w, b, eps):
             shape = x.shape
-            x2 = rows(x, shape[-1])
+            x2 = _as_rows(x, shape[-1])
             y, mean, rstd = layernorm_fwd(x2, w, b, eps=eps)
             ctx.save_for_backward(x2, w, mean, rstd)
             ctx.cfg = (shape, b is not None)
@@ -652,7 +660,7 @@ def _make_autograd_widened():
         def backward(ctx, gy):
             x2, w, mean, rstd = ctx.saved_tensors
             shape, has_b = ctx.cfg
-            dx, dw, db = layernorm_bwd(rows(gy, shape[-1]), x2, w, mean, rstd, bias=has_b)
+            dx, dw, db = layernorm_bwd(_as_rows(gy, shape[-1]), x2, w, mean, rstd, bias=has_b)
             return (dx.reshape(shape), dw.to(w.dtype), db.to(w.dtype) if has_b else None,
                     None)
 
@@ -676,7 +684,7 @@ def _make_autograd_widened():
         @staticmethod
         def forward(ctx, x):
             shape = x.shape
-            y = softmax_fwd(rows(x, shape[-1]))
+            y = softmax_fwd(_as_rows(x, shape[-1]))
             ctx.save_for_backward(y)
             ctx.shape = shape
             return y.reshape(shape)
@@ -684,7 +692,7 @@ def _make_autograd_widened():
         @staticmethod
         def backward(ctx, gy):
             (y,) = ctx.saved_tensors
-            return softmax_bwd(rows(gy, ctx.shape[-1]), y).reshape(ctx.shape)
+            return softmax_bwd(_as_rows(gy, ctx.shape[-1]), y).reshape(ctx.shape)
 
     return LayerNormFunction, GroupNormFunction, SoftmaxFunction
 

@@ -157,6 +157,21 @@ def test_binding_rejects_host_tensors_before_calling():
         rn.fwd(x.double(), w.double())
 
 
+def test_binding_refuses_overlapping_rows_and_autograd_copies_them():
+    """A broadcast view (row stride 0) or any row stride below N would make the kernels address
+    M rows of N elements past the end of the allocation: the binding refuses it before any call,
+    and the autograd wrappers, whose upstream gradients are often broadcast views, copy it."""
+    import torch
+    row = torch.arange(8, dtype=torch.bfloat16).reshape(1, 8)
+    for bad in (row.expand(4, 8), torch.zeros(40, dtype=torch.bfloat16).as_strided((4, 8), (4, 1))):
+        with pytest.raises(ValueError, match="overlapping rows"):
+            rn.fwd(bad, torch.ones(8, dtype=torch.bfloat16))
+    g = rn._as_rows(row.expand(2, 3, 8), 8)
+    assert g.shape == (6, 8) and g.stride() == (8, 1) and torch.equal(g, row.expand(6, 8))
+    ok = torch.zeros(4, 16, dtype=torch.bfloat16)[:, :8]  # padded rows: kept as a view
+    assert rn._as_rows(ok, 8).data_ptr() == ok.data_ptr()
+
+
 def test_binding_signatures_match_the_header():
     """Each ctypes signature has as many arguments as the header's prototype."""
     import re

@@ -332,6 +332,29 @@ def test_autograd_function_matches_direct_calls():
     assert same_bits(to_np(w.grad), to_np(dw2.to(torch.bfloat16))).all()
 
 
+def test_autograd_with_a_broadcast_upstream_gradient():
+    """The gradient of (y.sum over the leading dims * c).sum() reaches the backward as c broadcast
+    over the rows (row stride 0); the wrapper passes a copy with whole rows, so the result equals
+    the direct call with the materialized gradient."""
+    wl = WL["bf16"]
+    inp = make_inputs(wl, M=64, N=1024, seed=13)
+    x = to_device(inp["x"], "bf16", DEV).reshape(4, 16, 1024).requires_grad_(True)
+    w = to_device(inp["w"], "bf16", DEV).requires_grad_(True)
+    c = to_device(inp["dy"][0], "bf16", DEV)
+    print("case autograd broadcast upstream bf16 64x1024", flush=True)
+    y = rn.rms_norm(x, w)
+    strides = []
+    y.register_hook(lambda g: strides.append(g.reshape(-1, 1024).stride()))
+    (y.sum(dim=(0, 1)) * c).sum().backward()
+    assert strides == [(0, 1)]  # the case under test: a row-broadcast upstream gradient
+    x2 = x.detach().reshape(64, 1024)
+    _, r = rn.fwd(x2, w.detach())
+    dx2, dw2 = rn.bwd(c.expand(64, 1024).contiguous(), x2, w.detach(), r)
+    torch.cuda.synchronize()
+    assert same_bits(to_np(x.grad.reshape(64, 1024)), to_np(dx2)).all()
+    assert same_bits(to_np(w.grad), to_np(dw2.to(torch.bfloat16))).all()
+
+
 def test_graph_replays_match_eager():
     """The benchmark replays the step from a captured graph: every replay (with eager work and
     synchronizations in between) must reproduce the eager results bit for bit."""
