@@ -497,6 +497,11 @@ def groupnorm_bwd(dy, x, G: int, w, mean, rstd, bias: bool = True, dx=None, dw=N
     B, C, S = _gn_shape(x)
     if dx is None:
         dx = torch.empty_like(x)
+    if dx.dtype != x.dtype or dx.shape != x.shape:
+        raise ValueError("dx must match x in shape and dtype")
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        if t.dtype != torch.float32 or t.numel() != B * G:
+            raise ValueError(f"{n} must be float32 with B * G elements")
     if dw is None:
         dw = torch.empty((C,), dtype=torch.float32, device=x.device)
     if bias and db is None:
@@ -548,6 +553,8 @@ def softmax_bwd(dy, y, variant: str = "auto", dx=None):
     M, N = y.shape
     if dx is None:
         dx = torch.empty((M, N), dtype=y.dtype, device=y.device)
+    if dx.dtype != y.dtype or tuple(dx.shape) != (M, N):
+        raise ValueError("dx must match y in shape and dtype")
     pdy, lddy = _rows(dy, "dy")
     py, ldy = _rows(y, "y")
     pdx, lddx = _rows(dx, "dx")
@@ -564,9 +571,13 @@ def fwd_f64(x, w, eps: float = 1e-6, offset: float = 0.0, y=None, rstd=None):
     if x.dtype != torch.float64 or w.dtype != torch.float64:
         raise TypeError("x and w must be float64")
     M, N = x.shape
-    px, ldx = _rows(x, "x")
     y = torch.empty_like(x) if y is None else y
+    if y.dtype != x.dtype or tuple(y.shape) != (M, N):
+        raise ValueError("y must match x in shape and dtype")
     rstd = torch.empty((M,), dtype=torch.float64, device=x.device) if rstd is None else rstd
+    if rstd.dtype != torch.float64:
+        raise TypeError("rstd must be float64")
+    px, ldx = _rows(x, "x")
     py, ldy = _rows(y, "y")
     _same_device(x, w, y, rstd)
     st = library().rmsnorm_fwd_f64(px, ldx, _vec(w, "w", N), py, ldy, _vec(rstd, "rstd", M), M,
@@ -578,8 +589,16 @@ def fwd_f64(x, w, eps: float = 1e-6, offset: float = 0.0, y=None, rstd=None):
 def bwd_f64(dy, x, w, rstd, offset: float = 0.0, dx=None, dw=None, workspace=None):
     """Backward of ``fwd_f64``. Returns ``(dx, dw)``, both float64."""
     torch = _torch()
+    if x.dtype != torch.float64 or dy.dtype != torch.float64 or w.dtype != torch.float64:
+        raise TypeError("dy, x and w must be float64")
+    if tuple(dy.shape) != tuple(x.shape):
+        raise ValueError("dy must have the shape of x")
     M, N = x.shape
     dx = torch.empty_like(x) if dx is None else dx
+    if dx.dtype != x.dtype or tuple(dx.shape) != (M, N):
+        raise ValueError("dx must match x in shape and dtype")
+    if rstd.dtype != torch.float64 or dw is not None and dw.dtype != torch.float64:
+        raise TypeError("rstd and dw must be float64")
     dw = torch.empty((N,), dtype=torch.float64, device=x.device) if dw is None else dw
     need = int(library().rmsnorm_bwd_f64_workspace_bytes(M, N))
     if workspace is None:

@@ -172,6 +172,33 @@ def test_binding_refuses_overlapping_rows_and_autograd_copies_them():
     assert rn._as_rows(ok, 8).data_ptr() == ok.data_ptr()
 
 
+def test_binding_checks_caller_outputs_against_the_inputs():
+    """Outputs and statistics the caller passes must have the inputs' shape and dtype: a smaller
+    buffer would be written or read past its end. Checked on host tensors, before any call."""
+    import torch
+    bf, f32, f64 = torch.bfloat16, torch.float32, torch.float64
+    x = torch.zeros(4, 8, dtype=bf)
+    with pytest.raises(ValueError, match="dx must match"):
+        rn.softmax_bwd(x, x, dx=torch.zeros(2, 8, dtype=bf))
+    xd = torch.zeros(4, 8, dtype=f64)
+    wd = torch.ones(8, dtype=f64)
+    with pytest.raises(ValueError, match="y must match"):
+        rn.fwd_f64(xd, wd, y=torch.zeros(2, 8, dtype=f64))
+    with pytest.raises(ValueError, match="dy must have the shape"):
+        rn.bwd_f64(torch.zeros(2, 8, dtype=f64), xd, wd, torch.ones(4, dtype=f64))
+    with pytest.raises(ValueError, match="dx must match"):
+        rn.bwd_f64(xd, xd, wd, torch.ones(4, dtype=f64), dx=torch.zeros(4, 4, dtype=f64))
+    xg = torch.zeros(2, 4, 16, dtype=bf)
+    wg = torch.ones(4, dtype=bf)
+    stats = torch.zeros(2, 2, dtype=f32)
+    with pytest.raises(ValueError, match="dx must match"):
+        rn.groupnorm_bwd(xg, xg, 2, wg, stats, stats, dx=torch.zeros(2, 4, 8, dtype=bf))
+    with pytest.raises(ValueError, match="mean must be float32"):
+        rn.groupnorm_bwd(xg, xg, 2, wg, torch.zeros(2, dtype=f32), stats)
+    with pytest.raises(ValueError, match="rstd must be float32"):
+        rn.groupnorm_bwd(xg, xg, 2, wg, stats, torch.zeros(3, 2, dtype=f32))
+
+
 def test_binding_signatures_match_the_header():
     """Each ctypes signature has as many arguments as the header's prototype."""
     import re
