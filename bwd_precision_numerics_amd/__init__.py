@@ -340,6 +340,11 @@ def bwd_rows(dy, x, w, rstd, workspace, offset: float = 0.0, variant: str = "aut
 
 def dw_reduce(workspace, dw, M: int, N: int, dtype: str):
     """Second backward stage: dw = fixed-order sum of the partials in ``workspace``."""
+    if dw.dtype != _torch().float32:
+        raise TypeError("dw must be float32")
+    if dtype not in DTYPE_CODES:
+        raise ValueError(f"dtype must be one of {sorted(DTYPE_CODES)}")
+    _same_device(workspace, dw)
     wsb = workspace.numel() * workspace.element_size()
     st = library().rmsnorm_bwd_dw_reduce(workspace.data_ptr(), wsb, _vec(dw, "dw", N), M, N,
                                          DTYPE_CODES[dtype], _stream(dw.device))

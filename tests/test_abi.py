@@ -197,6 +197,8 @@ def test_binding_checks_caller_outputs_against_the_inputs():
         rn.groupnorm_bwd(xg, xg, 2, wg, torch.zeros(2, dtype=f32), stats)
     with pytest.raises(ValueError, match="rstd must be float32"):
         rn.groupnorm_bwd(xg, xg, 2, wg, stats, torch.zeros(3, 2, dtype=f32))
+    with pytest.raises(TypeError, match="dw must be float32"):
+        rn.dw_reduce(torch.zeros(64, dtype=f32), torch.zeros(8, dtype=bf), 4, 8, "bf16")
 
 
 def test_binding_signatures_match_the_header():
