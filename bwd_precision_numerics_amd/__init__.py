@@ -282,12 +282,28 @@ def _bwd_common(dy, x, w, rstd, dx):
     return dt, M, N, dx
 
 
+def _ws_buffer(t, device, name: str = "workspace"):
+    """Pointer and byte size of a caller-provided workspace. It must be a contiguous GPU tensor on
+    the inputs' device; the size reported to the library is the tensor's extent, bounded by what
+    its storage holds from the tensor's first byte (so a view cannot claim memory it does not own).
+    The library checks that size against what the call needs."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    nbytes = t.numel() * t.element_size()
+    avail = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    return t.data_ptr(), max(0, min(nbytes, avail))
+
+
 def _workspace(M, N, dt, device, workspace):
     torch = _torch()
     need = workspace_bytes(M, N, dt)
     if workspace is None:
         workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+    return _ws_buffer(workspace, device)
 
 
 def bwd_rounding_code(rounding: str, casts: str) -> int:
@@ -312,9 +328,10 @@ def bwd(dy, x, w, rstd, eps: float = 1e-6, offset: float = 0.0, rounding: str = 
     pdy, lddy = _rows(dy, "dy")
     px, ldx = _rows(x, "x")
     pdx, lddx = _rows(dx, "dx")
-    workspace, wsb = _workspace(M, N, dt, x.device, workspace)
+    pws, wsb = _workspace(M, N, dt, x.device, workspace)
+    _same_device(x, dw)
     st = library().rmsnorm_bwd_variant(pdy, lddy, px, ldx, _vec(w, "w", N), _vec(rstd, "rstd", M),
-                                       pdx, lddx, _vec(dw, "dw", N), workspace.data_ptr(), wsb, M,
+                                       pdx, lddx, _vec(dw, "dw", N), pws, wsb, M,
                                        N, DTYPE_CODES[dt], eps, offset,
                                        bwd_rounding_code(rounding, casts),
                                        VARIANT_CODES[variant], _stream(x.device))
@@ -329,9 +346,9 @@ def bwd_rows(dy, x, w, rstd, workspace, offset: float = 0.0, variant: str = "aut
     pdy, lddy = _rows(dy, "dy")
     px, ldx = _rows(x, "x")
     pdx, lddx = _rows(dx, "dx")
-    wsb = workspace.numel() * workspace.element_size()
+    pws, wsb = _ws_buffer(workspace, x.device)
     st = library().rmsnorm_bwd_rows(pdy, lddy, px, ldx, _vec(w, "w", N), _vec(rstd, "rstd", M),
-                                    pdx, lddx, workspace.data_ptr(), wsb, M, N, DTYPE_CODES[dt],
+                                    pdx, lddx, pws, wsb, M, N, DTYPE_CODES[dt],
                                     offset, bwd_rounding_code(rounding, casts),
                                     VARIANT_CODES[variant], _stream(x.device))
     _check("rmsnorm_bwd_rows", st)
@@ -344,9 +361,9 @@ def dw_reduce(workspace, dw, M: int, N: int, dtype: str):
         raise TypeError("dw must be float32")
     if dtype not in DTYPE_CODES:
         raise ValueError(f"dtype must be one of {sorted(DTYPE_CODES)}")
-    _same_device(workspace, dw)
-    wsb = workspace.numel() * workspace.element_size()
-    st = library().rmsnorm_bwd_dw_reduce(workspace.data_ptr(), wsb, _vec(dw, "dw", N), M, N,
+    pdw = _vec(dw, "dw", N)
+    pws, wsb = _ws_buffer(workspace, dw.device)
+    st = library().rmsnorm_bwd_dw_reduce(pws, wsb, pdw, M, N,
                                          DTYPE_CODES[dtype], _stream(dw.device))
     _check("rmsnorm_bwd_dw_reduce", st)
     return dw
@@ -417,14 +434,14 @@ def layernorm_bwd(dy, x, w, mean, rstd, bias: bool = True, variant: str = "auto"
     need = layernorm_workspace_bytes(M, N, dt)
     if workspace is None:
         workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=x.device)
-    wsb = workspace.numel() * workspace.element_size()
+    pws, wsb = _ws_buffer(workspace, x.device)
     _same_device(*[t for t in (dy, x, w, mean, rstd, dx, dw, db, workspace) if t is not None])
     st = library().layernorm_bwd(pdy, lddy, px, ldx, _vec(w, "w", N),
                                  _opt_vec(mean, "mean", M, torch.float32),
                                  _opt_vec(rstd, "rstd", M, torch.float32), pdx, lddx,
                                  _opt_vec(dw, "dw", N, torch.float32),
                                  _opt_vec(db, "db", N, torch.float32) if bias else None,
-                                 workspace.data_ptr(), wsb, M, N, DTYPE_CODES[dt],
+                                 pws, wsb, M, N, DTYPE_CODES[dt],
                                  VARIANT_CODES[variant], _stream(x.device))
     _check("layernorm_bwd", st)
     return dx, dw, (db if bias else None)
@@ -459,7 +476,8 @@ def _gn_workspace(B, C, S, G, dt, device, workspace):
     need = groupnorm_workspace_bytes(B, C, S, G, dt)
     if workspace is None:
         workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+    pws, wsb = _ws_buffer(workspace, device)
+    return workspace, pws, wsb
 
 
 def groupnorm_fwd(x, G: int, w, b=None, eps: float = 1e-5, y=None, mean=None, rstd=None,
@@ -481,10 +499,10 @@ def groupnorm_fwd(x, G: int, w, b=None, eps: float = 1e-5, y=None, mean=None, rs
     for t, n in ((mean, "mean"), (rstd, "rstd")):
         if t.dtype != torch.float32 or t.numel() != B * G:
             raise ValueError(f"{n} must be float32 with B * G elements")
-    workspace, wsb = _gn_workspace(B, C, S, G, dt, x.device, workspace)
+    workspace, pws, wsb = _gn_workspace(B, C, S, G, dt, x.device, workspace)
     _same_device(*[t for t in (x, w, b, y, mean, rstd, workspace) if t is not None])
     st = library().groupnorm_fwd(px, pw, pb, _contig(y, "y"), _contig(mean, "mean"),
-                                 _contig(rstd, "rstd"), workspace.data_ptr(), wsb, B, C, S, G,
+                                 _contig(rstd, "rstd"), pws, wsb, B, C, S, G,
                                  DTYPE_CODES[dt], eps, _stream(x.device))
     _check("groupnorm_fwd", st)
     return y, mean, rstd
@@ -511,13 +529,13 @@ def groupnorm_bwd(dy, x, G: int, w, mean, rstd, bias: bool = True, dx=None, dw=N
         dw = torch.empty((C,), dtype=torch.float32, device=x.device)
     if bias and db is None:
         db = torch.empty((C,), dtype=torch.float32, device=x.device)
-    workspace, wsb = _gn_workspace(B, C, S, G, dt, x.device, workspace)
+    workspace, pws, wsb = _gn_workspace(B, C, S, G, dt, x.device, workspace)
     _same_device(*[t for t in (dy, x, w, mean, rstd, dx, dw, db, workspace) if t is not None])
     st = library().groupnorm_bwd(_contig(dy, "dy"), _contig(x, "x"), _vec(w, "w", C),
                                  _contig(mean, "mean"), _contig(rstd, "rstd"), _contig(dx, "dx"),
                                  _opt_vec(dw, "dw", C, torch.float32),
                                  _opt_vec(db, "db", C, torch.float32) if bias else None,
-                                 workspace.data_ptr(), wsb, B, C, S, G, DTYPE_CODES[dt],
+                                 pws, wsb, B, C, S, G, DTYPE_CODES[dt],
                                  _stream(x.device))
     _check("groupnorm_bwd", st)
     return dx, dw, (db if bias else None)
@@ -608,13 +626,13 @@ def bwd_f64(dy, x, w, rstd, offset: float = 0.0, dx=None, dw=None, workspace=Non
     need = int(library().rmsnorm_bwd_f64_workspace_bytes(M, N))
     if workspace is None:
         workspace = torch.empty((max(need, 16) + 7) // 8, dtype=torch.float64, device=x.device)
-    wsb = workspace.numel() * workspace.element_size()
+    pws, wsb = _ws_buffer(workspace, x.device)
     pdy, lddy = _rows(dy, "dy")
     px, ldx = _rows(x, "x")
     pdx, lddx = _rows(dx, "dx")
     _same_device(dy, x, w, rstd, dx, dw, workspace)
     st = library().rmsnorm_bwd_f64(pdy, lddy, px, ldx, _vec(w, "w", N), _vec(rstd, "rstd", M), pdx,
-                                   lddx, _vec(dw, "dw", N), workspace.data_ptr(), wsb, M, N, offset,
+                                   lddx, _vec(dw, "dw", N), pws, wsb, M, N, offset,
                                    _stream(x.device))
     _check("rmsnorm_bwd_f64", st)
     return dx, dw

@@ -20,32 +20,22 @@ constexpr int kBwdLdsMaxIters = 4;
 // Streaming backward with its dw sums in registers: up to 8 vectors per thread (8192 vectors a row
 // at 1024 threads, e.g. N = 65536 in 16-bit types).
 constexpr int kStreamRegVectors = 8;
-// Register backward pipeline per vectors-per-thread: rows per barrier (batch) and batches in flight
-// ahead of the current one. Ring registers: (DEPTH + 1) * RB * ITERS * 2 sixteen-byte vectors.
+// Register backward pipeline: rows per barrier (batch) and batches in flight ahead of the current
+// one, and whether pass 2 reuses xhat and g*dy from pass 1. With the ring's loads issued as
+// straight-line code, one batch ahead measured fastest at every depth tried (bf16 4096 x 4096 rows
+// kernel: depth 1 19.5 us, 2 20.3, 3 20.8, 5 23.0; no prefetch 21.7): more rows in flight per compute
+// unit lower the DRAM efficiency more than they hide latency. Two rows per barrier measured slower
+// (24.2 against 22.6 us with the dw reduction).
 template <int ITERS> struct BwdPipe;
 template <> struct BwdPipe<1> {
-  static constexpr int RB = 1, DEPTH = 5;
+  static constexpr int RB = 1, DEPTH = 1;
   static constexpr bool KEEP = true;
 };
 template <> struct BwdPipe<2> {
   static constexpr int RB = 1, DEPTH = 1;
   static constexpr bool KEEP = false;
 };
-// Narrow rows (row groups of at most kBwdNarrowTpr threads, e.g. N <= 2048 in 16-bit types): two
-// rows per barrier and one batch in flight ahead (bf16, M = 4096: N = 1024 8.3 -> 8.0 us, N = 2048
-// 12.1-12.5 -> 11.8 us). A group still takes its rows in the same order, so the results are the same.
-// Not with the autograd casts, whose two-row batch spills registers.
-constexpr int kBwdNarrowTpr = 256;
-struct BwdPipeNarrow {
-  static constexpr int RB = 2, DEPTH = 1;
-  static constexpr bool KEEP = true;
-};
-bool bwd_narrow(int iters, int tpr, bool ag) { return iters == 1 && tpr <= kBwdNarrowTpr && !ag; }
-
-int bwd_batch(int iters, int tpr, bool ag) {
-  if (bwd_narrow(iters, tpr, ag)) return BwdPipeNarrow::RB;
-  return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB;
-}
+int bwd_batch(int iters) { return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB; }
 
 // Automatic selection prefers the register kernel, then the LDS-staged one, except for two
 // instantiations that spill registers and measured slower than the streaming kernel (bf16, M = 4096):
@@ -94,7 +84,7 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
     main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr) +
                  (size_t)p->groups * 2 * iters * tpr * 16;
   } else {
-    main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr * bwd_batch(iters, tpr, ag));
+    main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr * bwd_batch(iters));
   }
   const size_t combine_bytes = sizeof(float) * (size_t)(p->groups / 2) * tpr * iters * V;
   p->lds = main_bytes > combine_bytes ? main_bytes : combine_bytes;
@@ -162,24 +152,34 @@ rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
     }
 #undef RMSN_BWD_LDS
   }
-#define RMSN_BWD_ROWS(IT, F)                                                                     \
-  launch(bwd_rows_kernel<D, IT, BwdPipe<IT>::DEPTH, BwdPipe<IT>::RB, AG, BwdPipe<IT>::KEEP, F>, \
+  // Whole 16-byte vectors on every lane (FULL), on the leading lanes (WHOLE), or a partial last
+  // vector (RAGGED, rows with a padded stride). FULL and WHOLE rows fix the row group's wave count
+  // at compile time (one of 1, 2, 4, 8, 16); RAGGED rows take it from the arguments.
+  const Tail tail = full ? Tail::FULL : (a.N % Elem<D>::VEC == 0 ? Tail::WHOLE : Tail::RAGGED);
+  const int wpr = p.tpr / 64;
+#define RMSN_BWD_ROWS(IT, T, W)                                                            \
+  launch(bwd_rows_kernel<D, IT, BwdPipe<IT>::DEPTH, BwdPipe<IT>::RB, AG, BwdPipe<IT>::KEEP, T, \
+                         W>,                                                                \
          p.grid, block, p.lds, s, a)
-#define RMSN_BWD_NARROW(F)                                                                  \
-  launch(bwd_rows_kernel<D, 1, BwdPipeNarrow::DEPTH, BwdPipeNarrow::RB, AG, BwdPipeNarrow::KEEP, \
-                         F>,                                                                 \
-         p.grid, block, p.lds, s, a)
+#define RMSN_BWD_WPR(IT, T)                                            \
+  (wpr == 1   ? RMSN_BWD_ROWS(IT, T, 1)                                 \
+   : wpr == 2 ? RMSN_BWD_ROWS(IT, T, 2)                                 \
+   : wpr == 4 ? RMSN_BWD_ROWS(IT, T, 4)                                 \
+   : wpr == 8 ? RMSN_BWD_ROWS(IT, T, 8)                                 \
+              : RMSN_BWD_ROWS(IT, T, 16))
+  if (p.groups * p.tpr != kBwdBlockThreads) return RMSNORM_ERR_UNSUPPORTED;
   switch (p.iters) {
     case 1:
-      if constexpr (!AG) {
-        if (bwd_narrow(1, p.tpr, false))
-          return full ? RMSN_BWD_NARROW(true) : RMSN_BWD_NARROW(false);
-      }
-      return full ? RMSN_BWD_ROWS(1, true) : RMSN_BWD_ROWS(1, false);
-    case 2: return full ? RMSN_BWD_ROWS(2, true) : RMSN_BWD_ROWS(2, false);
+      return tail == Tail::FULL    ? RMSN_BWD_WPR(1, Tail::FULL)
+             : tail == Tail::WHOLE ? RMSN_BWD_WPR(1, Tail::WHOLE)
+                                   : RMSN_BWD_ROWS(1, Tail::RAGGED, 0);
+    case 2:  // two vectors per thread: row groups of 1024 threads
+      return tail == Tail::FULL    ? RMSN_BWD_ROWS(2, Tail::FULL, 16)
+             : tail == Tail::WHOLE ? RMSN_BWD_ROWS(2, Tail::WHOLE, 16)
+                                   : RMSN_BWD_ROWS(2, Tail::RAGGED, 0);
     default: return RMSNORM_ERR_UNSUPPORTED;
   }
-#undef RMSN_BWD_NARROW
+#undef RMSN_BWD_WPR
 #undef RMSN_BWD_ROWS
 }
 

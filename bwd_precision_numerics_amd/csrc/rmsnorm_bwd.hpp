@@ -97,22 +97,20 @@ __device__ __forceinline__ void store_partial(const float (&acc)[ITERS * V], flo
 
 // Sums of RB values over the TPR threads of one row group, with the order of group_sum for each:
 // one LDS round trip and one barrier serve the whole batch. Every thread of the block must call it.
-template <int RB>
+// W > 0: the row group's wave count is known at compile time (wpr == W).
+template <int RB, int W = 0>
 __device__ __forceinline__ void group_sum_batch(float (&v)[RB], float* red, int wpr, int tl) {
 #pragma unroll
   for (int k = 0; k < RB; ++k) v[k] = wave_sum(v[k]);
-  if (wpr > 1) {
+  if (W > 1 || (W == 0 && wpr > 1)) {
     if ((tl & 63) == 0) {
 #pragma unroll
       for (int k = 0; k < RB; ++k) red[(tl >> 6) * RB + k] = v[k];
     }
     lds_barrier();
 #pragma unroll
-    for (int k = 0; k < RB; ++k) {
-      float t = red[k];
-      for (int w = 1; w < wpr; ++w) t += red[w * RB + k];
-      v[k] = t;
-    }
+    for (int k = 0; k < RB; ++k)
+      v[k] = W > 1 ? ordered_sum<(W > 1 ? W : 2), RB>(red + k) : waves_sum<RB>(red + k, wpr);
   }
 }
 
@@ -126,15 +124,35 @@ __device__ __forceinline__ float dw_factor(float xh) {
   return AG ? round_trip<D>(xh) : xh;
 }
 
+// How a row's 16-byte vectors fall on a row group's lanes.
+enum class Tail : int {
+  FULL = 0,    // N = ITERS * TPR * V: every lane has ITERS whole vectors
+  WHOLE = 1,   // N % V == 0: whole vectors, the last lanes may have none (idle)
+  RAGGED = 2,  // N % V != 0 (a padded row stride): one lane's last vector is partial
+};
+
 // Register kernel. A row group takes its block's rows in batches of RB rows (local index
 // (s * RB + k) * groups + grp for step s and batch index k; row = b + local * P) and keeps a ring of
-// DEPTH + 1 batches of raw (x, dy) in registers: while batch s is reduced and written, batches
-// s + 1 .. s + DEPTH are in flight, and one barrier serves all RB rows of a batch. Pass 1 upcasts
-// a raw row to form its dot product and its dw contributions; pass 2 either reuses xhat and g*dy
-// kept from pass 1 (KEEP: fewer VALU operations, more registers) or upcasts the raw row again.
-// The gain g = offset + w stays in registers. FULL: the host has checked N = ITERS * TPR * V (the
-// threads' vectors tile the row exactly), and the kernel carries no partial-vector code.
-template <DT D, int ITERS, int DEPTH, int RB, bool AG, bool KEEP, bool FULL = false>
+// DEPTH + 1 batches of raw (x, dy) and their rstd in registers: while batch s is reduced and
+// written, batches s + 1 .. s + DEPTH are in flight, and one barrier serves all RB rows of a batch.
+// Pass 1 upcasts a raw row to form its dot product and its dw contributions; pass 2 either reuses
+// xhat and g*dy kept from pass 1 (KEEP) or upcasts the raw row again. The gain g = offset + w stays
+// in registers.
+//
+// Loads are straight-line code: every step issues its batch's loads unconditionally; rows past the
+// block's share (and the empty steps that pad the last round of the ring) read w instead, which is
+// cache-resident, and lanes without a whole vector read the row's first one. Only the arithmetic and
+// the stores are guarded. Were the loads guarded too, the compiler would have to assume that any
+// later step might have skipped its loads, and it would wait for every outstanding load at each
+// step, leaving one row in flight whatever the ring depth. x, dy and dx move through buffer
+// instructions: the row's descriptor sits in scalar registers and each lane keeps one 32-bit byte
+// offset per vector, so no per-lane 64-bit addresses compete with the ring for registers (a
+// 64-bit address built in a ring slot's registers also forces the same full wait).
+//
+// WPR > 0 fixes the row group at WPR wavefronts (TPR = 64 * WPR, 1024 / TPR groups per block) at
+// compile time, so the row indices fold and the wave sums are read in one batch; WPR = 0 takes the
+// shape from the arguments.
+template <DT D, int ITERS, int DEPTH, int RB, bool AG, bool KEEP, Tail TAIL, int WPR>
 __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -143,12 +161,10 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   constexpr int RING = DEPTH + 1;
   extern __shared__ uint4 smem[];
 
-  const int TPR = a.tpr, wpr = TPR >> 6, G = a.groups, N = a.N;
+  const int TPR = WPR ? 64 * WPR : a.tpr, wpr = WPR ? WPR : TPR >> 6;
+  const int G = WPR ? 1024 / (64 * WPR) : a.groups, N = a.N;
   const int tid = threadIdx.x;
-  // Scalar row addressing (wave_group) relieves the 2-vector kernel's register pressure (it was
-  // spilling) and measured faster there; the 1-vector kernel measured slower with it on partly
-  // idle row groups (N = 3072: 384 of 512 threads), so it keeps per-lane row indices.
-  const int grp = ITERS >= 2 ? wave_group(tid, TPR) : tid / TPR;
+  const int grp = wave_group(tid, TPR);  // wave-uniform: row indices and row pointers are scalar
   const int tl = tid - grp * TPR;
   const int b = blockIdx.x, P = a.P;
   const int64_t nloc = block_rows(a.M, P, b);
@@ -156,19 +172,28 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   const int nsteps = (int)((nloc + span - 1) / span);
   float* red = reinterpret_cast<float*>(smem);  // [2][G][wpr][RB]
 
-  const S* dyb = static_cast<const S*>(a.dy);
-  const S* xb = static_cast<const S*>(a.x);
-  S* dxb = static_cast<S*>(a.dx);
+  const S* wr = static_cast<const S*>(a.w);
+  // Lane's vector `it`: byte offset in the row (0 for a lane without a whole vector, whose loads
+  // are never used), whether it is whole, and whether the lane has any element of it.
+  bool whole[ITERS], live[ITERS];
+  uint32_t voff[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    live[it] = TAIL == Tail::FULL || col < N;
+    // With N % V == 0 a lane's vector is whole or absent; said so, the element paths compile away.
+    whole[it] = TAIL == Tail::RAGGED ? col + V <= N : live[it];
+    voff[it] = whole[it] ? (uint32_t)col * (uint32_t)sizeof(S) : 0u;
+  }
 
   float g[ITERS][V];
   {
-    const S* wr = static_cast<const S*>(a.w);
+    const BufRsrc wb = buf_rsrc(wr);
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
-      Raw r = IO::zero();
-      if (col + V <= N) r = IO::load(at(wr, col));
-      else if (col < N) r = IO::load_part(at(wr, col), N - col);
+      Raw r = IO::load_b(wb, voff[it], 0);
+      if (!whole[it]) r = live[it] ? IO::load_part(at(wr, col), N - col) : IO::zero();
       float wf[V];
       IO::unpack(r, wf);
 #pragma unroll
@@ -181,25 +206,25 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 
   Raw rx[RING][RB][ITERS], rd[RING][RB][ITERS];
   float rr[RING][RB];  // the rows' rstd travels with their data: no dependent load per step
-  // Rows past the block's share load as zeros: they add nothing to the dot products or to dw.
   auto load_batch = [&](int slot, int s) {
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
       const int64_t li = ((int64_t)s * RB + k) * G + grp;
-      const int64_t row = b + (li < nloc ? li : 0) * P;
-      const S* xr = xb + row * a.ldx;
-      const S* dr = dyb + row * a.lddy;
-      rr[slot][k] = li < nloc ? a.rstd[row] : 0.f;
+      const bool ok = s < nsteps && li < nloc;
+      const int64_t row = b + (ok ? li : 0) * P;
+      const S* xr = ok ? static_cast<const S*>(a.x) + row * a.ldx : wr;
+      const S* dr = ok ? static_cast<const S*>(a.dy) + row * a.lddy : wr;
+      const BufRsrc xb = buf_rsrc(xr), db = buf_rsrc(dr);
+      rr[slot][k] = a.rstd[row];
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
-        const int col = (it * TPR + tl) * V;
-        rx[slot][k][it] = IO::zero();
-        rd[slot][k][it] = IO::zero();
-        if (li < nloc) {
-          if (FULL || col + V <= N) {
-            rx[slot][k][it] = IO::load_nt(at(xr, col));
-            rd[slot][k][it] = IO::load_nt(at(dr, col));
-          } else if (col < N) {
+        rx[slot][k][it] = IO::load_b_nt(xb, voff[it], 0);
+        rd[slot][k][it] = IO::load_b_nt(db, voff[it], 0);
+        if constexpr (TAIL == Tail::RAGGED) {
+          // The lane holding the row's partial vector reads it element by element (zeros past
+          // N); these lane-dependent loads cost this instantiation some of its rows in flight.
+          const int col = (it * TPR + tl) * V;
+          if (!whole[it] && live[it]) {
             rx[slot][k][it] = IO::load_part(at(xr, col), N - col);
             rd[slot][k][it] = IO::load_part(at(dr, col), N - col);
           }
@@ -210,55 +235,63 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load_batch(j, j);
 
+  // c = dot / N. Exactly tiled rows are a power of two wide (ITERS, TPR and V are), so 1/N is
+  // exact and the product has the quotient's bits; other widths divide.
+  const float inv_n = 1.0f / (float)N;
+
   for (int s0 = 0; s0 < nsteps; s0 += RING) {
 #pragma unroll
     for (int j = 0; j < RING; ++j) {
       const int s = s0 + j;
+      load_batch((j + DEPTH) % RING, s + DEPTH);
       if (s < nsteps) {  // block-uniform
-        if (s + DEPTH < nsteps) load_batch((j + DEPTH) % RING, s + DEPTH);
         float rs[RB], dot[RB];
         float kx[KEEP ? RB : 1][KEEP ? ITERS * V : 1], kg[KEEP ? RB : 1][KEEP ? ITERS * V : 1];
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
+          const int64_t li = ((int64_t)s * RB + k) * G + grp;
           rs[k] = rr[j][k];
           float d0 = 0.f, d1 = 0.f;
+          if (li < nloc) {  // wave-uniform
 #pragma unroll
-          for (int it = 0; it < ITERS; ++it) {
-            float xf[V], df[V];
-            IO::unpack(rx[j][k][it], xf);
-            IO::unpack(rd[j][k][it], df);
+            for (int it = 0; it < ITERS; ++it) {
+              if (!live[it]) continue;
+              float xf[V], df[V];
+              IO::unpack(rx[j][k][it], xf);
+              IO::unpack(rd[j][k][it], df);
 #pragma unroll
-            for (int e = 0; e < V; e += 2) {
-              const float xh0 = xf[e] * rs[k], xh1 = xf[e + 1] * rs[k];
-              const float gd0 = gain_dy<D, AG>(g[it][e], df[e]);
-              const float gd1 = gain_dy<D, AG>(g[it][e + 1], df[e + 1]);
-              acc[it * V + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh0), acc[it * V + e]);
-              acc[it * V + e + 1] =
-                  __builtin_fmaf(df[e + 1], dw_factor<D, AG>(xh1), acc[it * V + e + 1]);
-              if constexpr (KEEP) {
-                kx[k][it * V + e] = xh0;
-                kx[k][it * V + e + 1] = xh1;
-                kg[k][it * V + e] = gd0;
-                kg[k][it * V + e + 1] = gd1;
+              for (int e = 0; e < V; e += 2) {
+                const float xh0 = xf[e] * rs[k], xh1 = xf[e + 1] * rs[k];
+                const float gd0 = gain_dy<D, AG>(g[it][e], df[e]);
+                const float gd1 = gain_dy<D, AG>(g[it][e + 1], df[e + 1]);
+                acc[it * V + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh0), acc[it * V + e]);
+                acc[it * V + e + 1] =
+                    __builtin_fmaf(df[e + 1], dw_factor<D, AG>(xh1), acc[it * V + e + 1]);
+                if constexpr (KEEP) {
+                  kx[k][it * V + e] = xh0;
+                  kx[k][it * V + e + 1] = xh1;
+                  kg[k][it * V + e] = gd0;
+                  kg[k][it * V + e + 1] = gd1;
+                }
+                d0 = __builtin_fmaf(gd0, xh0, d0);
+                d1 = __builtin_fmaf(gd1, xh1, d1);
               }
-              d0 = __builtin_fmaf(gd0, xh0, d0);
-              d1 = __builtin_fmaf(gd1, xh1, d1);
             }
           }
           dot[k] = d0 + d1;
         }
-        group_sum_batch<RB>(dot, red + ((s & 1) * G + grp) * wpr * RB, wpr, tl);
+        group_sum_batch<RB, WPR>(dot, red + ((s & 1) * G + grp) * wpr * RB, wpr, tl);
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
           const int64_t li = ((int64_t)s * RB + k) * G + grp;
           if (li >= nloc) continue;
           const int64_t row = b + li * P;
-          const float c = dot[k] / (float)N;
-          S* dxr = dxb + row * a.lddx;
+          const float c = TAIL == Tail::FULL ? dot[k] * inv_n : dot[k] / (float)N;
+          S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
+          const BufRsrc ob = buf_rsrc(dxr);
 #pragma unroll
           for (int it = 0; it < ITERS; ++it) {
-            const int col = (it * TPR + tl) * V;
-            if (!FULL && col >= N) continue;
+            if (!live[it]) continue;
             float o[V];
             if constexpr (KEEP) {
 #pragma unroll
@@ -276,8 +309,8 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
               }
             }
             const Raw out = IO::pack(o);
-            if (FULL || col + V <= N) IO::store(at(dxr, col), out);
-            else IO::store_part(at(dxr, col), out, N - col);
+            if (whole[it]) IO::store_b(ob, voff[it], 0, out);
+            else IO::store_part(at(dxr, (it * TPR + tl) * V), out, N - (it * TPR + tl) * V);
           }
         }
       }

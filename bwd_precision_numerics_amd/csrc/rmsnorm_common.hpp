@@ -305,6 +305,35 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// red[0], red[STRIDE], ..., red[(W - 1) * STRIDE] added in that order. All W reads are issued
+// before the first addition (one LDS wait instead of one per value).
+template <int W, int STRIDE>
+__device__ __forceinline__ float ordered_sum(const float* red) {
+  float v[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) v[w] = red[w * STRIDE];
+  float t = v[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) t += v[w];
+  return t;
+}
+// The same for a wave count known only at run time: wpr is a power of two up to 16 (row groups
+// of 64 to 1024 threads).
+template <int STRIDE>
+__device__ __forceinline__ float waves_sum(const float* red, int wpr) {
+  switch (wpr) {
+    case 2: return ordered_sum<2, STRIDE>(red);
+    case 4: return ordered_sum<4, STRIDE>(red);
+    case 8: return ordered_sum<8, STRIDE>(red);
+    case 16: return ordered_sum<16, STRIDE>(red);
+    default: {
+      float t = red[0];
+      for (int w = 1; w < wpr; ++w) t += red[w * STRIDE];
+      return t;
+    }
+  }
+}
+
 // Sum of a value over the TPR threads of one row group (TPR = 64 * wpr). Waves publish their wave
 // sums in red[slot * wpr + wave] and every thread adds them in wave order, so all threads of the
 // group end with the same bits. Must be reached by every thread of the block when wpr > 1.
@@ -313,8 +342,7 @@ __device__ __forceinline__ float group_sum(float v, float* red, int wpr, int tl)
   if (wpr > 1) {
     if ((tl & 63) == 0) red[tl >> 6] = v;
     lds_barrier();
-    v = red[0];
-    for (int k = 1; k < wpr; ++k) v += red[k];
+    v = waves_sum<1>(red, wpr);
   }
   return v;
 }

@@ -201,6 +201,39 @@ def test_binding_checks_caller_outputs_against_the_inputs():
         rn.dw_reduce(torch.zeros(64, dtype=f32), torch.zeros(8, dtype=bf), 4, 8, "bf16")
 
 
+class _OnDevice:
+    """A host tensor presented as a GPU tensor on `device`: the binding's workspace check looks
+    only at these attributes, so its refusals can be exercised without a GPU."""
+
+    def __init__(self, t, device="cuda:0"):
+        import torch
+        self._t, self.is_cuda, self.device = t, True, torch.device(device)
+
+    def __getattr__(self, name):
+        return getattr(self._t, name)
+
+
+def test_binding_checks_caller_workspaces():
+    """A workspace the caller passes must be a contiguous GPU tensor on the inputs' device, and the
+    size reported to the library is what its storage holds from its first byte: an expanded view
+    of 4 bytes must not be reported as 256 KiB (the kernels would write the partial rows past it)."""
+    import torch
+    dev = torch.device("cuda:0")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rn._ws_buffer(torch.zeros(64), dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        rn._ws_buffer(_OnDevice(torch.zeros(1).expand(65536)), dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        rn._ws_buffer(_OnDevice(torch.zeros(8, 8).t()), dev)
+    with pytest.raises(ValueError, match="is on cuda:1"):
+        rn._ws_buffer(_OnDevice(torch.zeros(64), "cuda:1"), dev)
+    base = torch.zeros(64)
+    ptr, n = rn._ws_buffer(_OnDevice(base), dev)
+    assert (ptr, n) == (base.data_ptr(), 256)
+    ptr, n = rn._ws_buffer(_OnDevice(base[48:]), dev)  # a view: its own 16 floats, not the rest
+    assert (ptr, n) == (base[48:].data_ptr(), 64)
+
+
 def test_binding_signatures_match_the_header():
     """Each ctypes signature has as many arguments as the header's prototype."""
     import re
