@@ -73,6 +73,8 @@ SIGNATURES = {
                          _f, _i, _p]),
     "rmsnorm_bwd_variant": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p, _sz, _i64, _i64,
                                  _i, _f, _f, _i, _i, _p]),
+    "rmsnorm_bwd_noalloc": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _i64, _i64, _i, _f,
+                                 _f, _i, _p]),
     "rmsnorm_bwd_rows": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _sz, _i64, _i64, _i, _f,
                               _i, _i, _p]),
     "rmsnorm_bwd_dw_reduce": (_i, [_p, _sz, _p, _i64, _i64, _i, _p]),

@@ -3,11 +3,19 @@
 // Every argument check runs before the first HIP call, so a rejected call launches nothing and
 // touches no device state. The library keeps no state apart from a per-device cache of the LDS
 // limit, filled on first use (a relaxed atomic per device: racing threads store the same value).
+#include <mutex>
+
 #include "host_common.hpp"
 #include "rmsnorm_bwd.hpp"
 #include "rmsnorm_fwd.hpp"
 
 using namespace rmsn;
+
+// Scratch of rmsnorm_bwd_noalloc: the dw partial rows in a file-scope device array, one copy per
+// device, held until the process ends. Host code never passes `scratch` itself to a kernel (on the
+// host the name stands for a host-side shadow, not a device address): each device's address comes
+// from hipGetSymbolAddress on that device's first call, and only that address is used.
+static __device__ __align__(256) float scratch[RMSNORM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -349,6 +357,52 @@ rmsnorm_status bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx
   return dw_reduce_impl(workspace, workspace_bytes_given, dw, M, N, dtype, stream);
 }
 
+// The device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+rmsnorm_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RMSNORM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RMSNORM_ERR_UNSUPPORTED;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+  });
+  if (slot.err != hipSuccess || slot.ptr == nullptr) return RMSNORM_ERR_HIP;
+  *out = slot.ptr;
+  return RMSNORM_OK;
+}
+
+rmsnorm_status bwd_noalloc_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                                const void* w, const float* rstd, void* dx, int64_t lddx,
+                                float* dw, int64_t M, int64_t N, rmsnorm_dtype dtype, float eps,
+                                float offset, int rounding, void* stream) {
+  // Every check before any HIP call: the shape must fit the scratch array, and the arguments
+  // pass rmsnorm_bwd's checks with a stand-in workspace of the array's size (any aligned
+  // non-null address: nothing is launched on this pass).
+  rmsnorm_status st = check_common(M, N, dtype, eps, offset);
+  if (st != RMSNORM_OK) return st;
+  if (workspace_bytes(M, N) > RMSNORM_NOALLOC_SCRATCH_BYTES) return RMSNORM_ERR_WORKSPACE;
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t(256));
+  if ((st = check_bwd_rows(dy, lddy, x, ldx, w, rstd, dx, lddx, stand_in,
+                           RMSNORM_NOALLOC_SCRATCH_BYTES, M, N, dtype, offset, rounding,
+                           RMSNORM_VARIANT_AUTO)) != RMSNORM_OK)
+    return st;
+  if (dw == nullptr) return RMSNORM_ERR_INVALID_ARG;
+  if (!aligned(dw, 4)) return RMSNORM_ERR_MISALIGNED;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != RMSNORM_OK) return st;
+  return bwd_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, ws, RMSNORM_NOALLOC_SCRATCH_BYTES, M,
+                  N, dtype, eps, offset, rounding, RMSNORM_VARIANT_AUTO, stream);
+}
+
 }  // namespace
 
 // ---- exported C interface -------------------------------------------------------------------------
@@ -399,6 +453,14 @@ __attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_variant(
     void* stream) {
   return bwd_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, workspace, workspace_bytes_given, M, N,
                   dtype, eps, offset, rounding, variant, stream);
+}
+
+__attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_noalloc(
+    const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, const float* rstd,
+    void* dx, int64_t lddx, float* dw, int64_t M, int64_t N, rmsnorm_dtype dtype, float eps,
+    float offset, int rounding, void* stream) {
+  return bwd_noalloc_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, dw, M, N, dtype, eps, offset,
+                          rounding, stream);
 }
 
 __attribute__((visibility("default"))) rmsnorm_status rmsnorm_bwd_rows(

@@ -206,6 +206,24 @@ rmsnorm_status rmsnorm_bwd_rows(const void* dy, int64_t lddy, const void* x, int
 rmsnorm_status rmsnorm_bwd_dw_reduce(const void* workspace, size_t workspace_bytes, float* dw,
                                      int64_t M, int64_t N, rmsnorm_dtype dtype, void* stream);
 
+/* rmsnorm_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels and the same results
+ * as rmsnorm_bwd (automatic kernel selection), with the dw partial rows in a scratch array the
+ * library holds in each device's memory (RMSNORM_NOALLOC_SCRATCH_BYTES, kept until the process
+ * ends) instead of a caller workspace. The call itself allocates nothing; its first call on a
+ * device looks up that device's copy of the array.
+ *   arguments    as for rmsnorm_bwd, without the workspace
+ * Errors: RMSNORM_ERR_WORKSPACE (nothing launched) when rmsnorm_bwd_workspace_bytes(M, N, dtype)
+ * exceeds RMSNORM_NOALLOC_SCRATCH_BYTES (N up to 8192 for M >= 256 rows); otherwise as for
+ * rmsnorm_bwd. Every call on one device shares that device's array: calls that may overlap on one
+ * device (different streams, or different host threads without ordering) race and give wrong dw;
+ * calls ordered on one stream are safe. */
+#define RMSNORM_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+rmsnorm_status rmsnorm_bwd_noalloc(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                                   const void* w, const float* rstd, void* dx, int64_t lddx,
+                                   float* dw, int64_t M, int64_t N, rmsnorm_dtype dtype,
+                                   float eps, float offset, int rounding, void* stream);
+
 /* ---- float64 -------------------------------------------------------------------------------------
  * RMSNorm with float64 I/O and float64 arithmetic throughout, statistics included (candle pull
  * request 4059: float64 norm kernels take a float64 accumulator, so the forward's statistics equal

@@ -147,6 +147,29 @@ def test_bwd_stages_reject(lib):
     assert lib.rmsnorm_bwd_dw_reduce(FAKE, 4, FAKE, 4, 8, BF16, None) == WORKSPACE
 
 
+def test_bwd_noalloc_refuses_before_any_hip_call(lib):
+    """The no-allocation backward checks the shape against its scratch array and every argument
+    before its first HIP call (the scratch lookup), so these refusals need no GPU."""
+    f = lib.rmsnorm_bwd_noalloc
+    ok = dict(dy=FAKE, lddy=4096, x=FAKE, ldx=4096, w=FAKE, rstd=FAKE, dx=FAKE, lddx=4096, dw=FAKE,
+              M=4096, N=4096, dtype=BF16, eps=1e-6, offset=0.0, rounding=TWICE, stream=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["dy"], a["lddy"], a["x"], a["ldx"], a["w"], a["rstd"], a["dx"], a["lddx"],
+                 a["dw"], a["M"], a["N"], a["dtype"], a["eps"], a["offset"], a["rounding"],
+                 a["stream"])
+    # 256 partial rows of 16384 floats = 16 MiB > the 8 MiB scratch array
+    assert call(N=16384, lddy=16384, ldx=16384, lddx=16384) == WORKSPACE
+    assert call(M=300, N=8200, lddy=8200, ldx=8200, lddx=8200) == WORKSPACE
+    assert call(dw=None) == INVALID
+    assert call(rstd=None) == INVALID
+    assert call(ldx=100) == INVALID
+    assert call(dtype=7) == INVALID
+    assert call(N=1 << 25, lddy=1 << 25, ldx=1 << 25, lddx=1 << 25) == UNSUPPORTED
+    assert call(dw=FAKE + 2) == MISALIGNED
+
+
 def test_binding_rejects_host_tensors_before_calling():
     import torch
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
