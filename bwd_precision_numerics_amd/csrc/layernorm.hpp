@@ -253,8 +253,10 @@ struct LnBwdArgs {
 // A ring of DEPTH + 1 rows of raw (x, dy) and their (mean, rstd) per row group keeps DEPTH rows in
 // flight while one is reduced and written. HAS_DB adds the bias-gradient accumulators. KEEP holds
 // xhat and w * dy from the first pass for the second (fewer vector ALU operations, more registers)
-// instead of recomputing them from the raw row. FULL: as in the forward.
-template <DT D, int ITERS, int DEPTH, bool HAS_DB, bool KEEP, bool FULL = false>
+// instead of recomputing them from the raw row. TAIL and WPR as for the RMSNorm bwd_rows_kernel,
+// whose load discipline this kernel follows: every step issues its row's loads as straight-line
+// buffer loads (rows past the block's share read w), only the arithmetic and stores are guarded.
+template <DT D, int ITERS, int DEPTH, bool HAS_DB, bool KEEP, Tail TAIL, int WPR>
 __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -264,28 +266,35 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   constexpr int K = ITERS * V;
   extern __shared__ uint4 smem[];
 
-  const int TPR = a.tpr, wpr = TPR >> 6, G = a.groups, N = a.N;
+  const int TPR = WPR ? 64 * WPR : a.tpr, wpr = WPR ? WPR : TPR >> 6;
+  const int G = WPR ? 1024 / (64 * WPR) : a.groups, N = a.N;
   const int tid = threadIdx.x;
-  const int grp = tid / TPR;
+  const int grp = wave_group(tid, TPR);
   const int tl = tid - grp * TPR;
   const int b = blockIdx.x, P = a.P;
   const int64_t nloc = block_rows(a.M, P, b);
   const int nsteps = (int)((nloc + G - 1) / G);
   float* red = reinterpret_cast<float*>(smem);  // [2][G][wpr][2]
 
-  const S* dyb = static_cast<const S*>(a.dy);
-  const S* xb = static_cast<const S*>(a.x);
-  S* dxb = static_cast<S*>(a.dx);
+  const S* wr = static_cast<const S*>(a.w);
+  bool whole[ITERS], live[ITERS];
+  uint32_t voff[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    live[it] = TAIL == Tail::FULL || col < N;
+    whole[it] = TAIL == Tail::RAGGED ? col + V <= N : live[it];
+    voff[it] = whole[it] ? (uint32_t)col * (uint32_t)sizeof(S) : 0u;
+  }
 
   float g[ITERS][V];
   {
-    const S* wr = static_cast<const S*>(a.w);
+    const BufRsrc wb = buf_rsrc(wr);
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
-      Raw r = IO::zero();
-      if (col + V <= N) r = IO::load(wr + col);
-      else if (col < N) r = IO::load_part(wr + col, N - col);
+      Raw r = IO::load_b(wb, voff[it], 0);
+      if (!whole[it]) r = live[it] ? IO::load_part(at(wr, col), N - col) : IO::zero();
       IO::unpack(r, g[it]);
     }
   }
@@ -298,27 +307,24 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
 
   Raw rx[RING][ITERS], rd[RING][ITERS];
   float rm[RING], rr[RING];
-  // Rows past the block's share load as zeros (mean 0, rstd 0: xhat = 0): they add nothing.
   auto load_row = [&](int slot, int s) {
     const int64_t li = (int64_t)s * G + grp;
-    const bool ok = li < nloc;
+    const bool ok = s < nsteps && li < nloc;
     const int64_t row = b + (ok ? li : 0) * P;
-    const S* xr = xb + row * a.ldx;
-    const S* dr = dyb + row * a.lddy;
-    rm[slot] = ok ? a.mean[row] : 0.f;
-    rr[slot] = ok ? a.rstd[row] : 0.f;
+    const S* xr = ok ? static_cast<const S*>(a.x) + row * a.ldx : wr;
+    const S* dr = ok ? static_cast<const S*>(a.dy) + row * a.lddy : wr;
+    const BufRsrc xb = buf_rsrc(xr), db = buf_rsrc(dr);
+    rm[slot] = a.mean[row];
+    rr[slot] = a.rstd[row];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      const int col = (it * TPR + tl) * V;
-      rx[slot][it] = IO::zero();
-      rd[slot][it] = IO::zero();
-      if (ok) {
-        if (FULL || col + V <= N) {
-          rx[slot][it] = IO::load_nt(xr + col);
-          rd[slot][it] = IO::load_nt(dr + col);
-        } else if (col < N) {
-          rx[slot][it] = IO::load_part(xr + col, N - col);
-          rd[slot][it] = IO::load_part(dr + col, N - col);
+      rx[slot][it] = IO::load_b_nt(xb, voff[it], 0);
+      rd[slot][it] = IO::load_b_nt(db, voff[it], 0);
+      if constexpr (TAIL == Tail::RAGGED) {
+        const int col = (it * TPR + tl) * V;
+        if (!whole[it] && live[it]) {
+          rx[slot][it] = IO::load_part(at(xr, col), N - col);
+          rd[slot][it] = IO::load_part(at(dr, col), N - col);
         }
       }
     }
@@ -326,60 +332,68 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load_row(j, j);
 
+  // c1, c2 = sums / N: a multiply for exactly tiled rows (a power of two wide), else a division.
+  const float inv_n = 1.0f / (float)N;
+
   for (int s0 = 0; s0 < nsteps; s0 += RING) {
 #pragma unroll
     for (int j = 0; j < RING; ++j) {
       const int s = s0 + j;
+      load_row((j + DEPTH) % RING, s + DEPTH);
       if (s < nsteps) {  // block-uniform
-        if (s + DEPTH < nsteps) load_row((j + DEPTH) % RING, s + DEPTH);
+        const int64_t li = (int64_t)s * G + grp;
+        const bool valid = li < nloc;  // wave-uniform
         const float mu = rm[j], rs = rr[j];
         float d1a = 0.f, d1b = 0.f, d2a = 0.f, d2b = 0.f;
         float kx[KEEP ? K : 1], kg[KEEP ? K : 1];
+        if (valid) {
 #pragma unroll
-        for (int it = 0; it < ITERS; ++it) {
-          float xf[V], df[V];
-          IO::unpack(rx[j][it], xf);
-          IO::unpack(rd[j][it], df);
+          for (int it = 0; it < ITERS; ++it) {
+            if (!live[it]) continue;
+            float xf[V], df[V];
+            IO::unpack(rx[j][it], xf);
+            IO::unpack(rd[j][it], df);
 #pragma unroll
-          for (int e = 0; e < V; e += 2) {
-            const float xh0 = (xf[e] - mu) * rs, xh1 = (xf[e + 1] - mu) * rs;
-            const float gd0 = g[it][e] * df[e], gd1 = g[it][e + 1] * df[e + 1];
-            if constexpr (KEEP) {
-              kx[it * V + e] = xh0;
-              kx[it * V + e + 1] = xh1;
-              kg[it * V + e] = gd0;
-              kg[it * V + e + 1] = gd1;
+            for (int e = 0; e < V; e += 2) {
+              const float xh0 = (xf[e] - mu) * rs, xh1 = (xf[e + 1] - mu) * rs;
+              const float gd0 = g[it][e] * df[e], gd1 = g[it][e + 1] * df[e + 1];
+              if constexpr (KEEP) {
+                kx[it * V + e] = xh0;
+                kx[it * V + e + 1] = xh1;
+                kg[it * V + e] = gd0;
+                kg[it * V + e + 1] = gd1;
+              }
+              accw[it * V + e] = __builtin_fmaf(df[e], xh0, accw[it * V + e]);
+              accw[it * V + e + 1] = __builtin_fmaf(df[e + 1], xh1, accw[it * V + e + 1]);
+              if constexpr (HAS_DB) {
+                accb[it * V + e] += df[e];
+                accb[it * V + e + 1] += df[e + 1];
+              }
+              d1a += gd0;
+              d1b += gd1;
+              d2a = __builtin_fmaf(gd0, xh0, d2a);
+              d2b = __builtin_fmaf(gd1, xh1, d2b);
             }
-            accw[it * V + e] = __builtin_fmaf(df[e], xh0, accw[it * V + e]);
-            accw[it * V + e + 1] = __builtin_fmaf(df[e + 1], xh1, accw[it * V + e + 1]);
-            if constexpr (HAS_DB) {
-              accb[it * V + e] += df[e];
-              accb[it * V + e + 1] += df[e + 1];
-            }
-            d1a += gd0;
-            d1b += gd1;
-            d2a = __builtin_fmaf(gd0, xh0, d2a);
-            d2b = __builtin_fmaf(gd1, xh1, d2b);
-          }
-          // Done here, not after the row's reduction where the compiler would otherwise sink
-          // them (measured 30.8 -> 30.4 us at 4096 x 4096 bf16).
+            // Done here, not after the row's reduction where the compiler would otherwise sink
+            // them (which keeps every vector's operands live across the reduction).
 #pragma unroll
-          for (int e = 0; e < V; ++e) {
-            asm volatile("" : "+v"(accw[it * V + e]));
-            if constexpr (HAS_DB) asm volatile("" : "+v"(accb[it * V + e]));
+            for (int e = 0; e < V; ++e) {
+              asm volatile("" : "+v"(accw[it * V + e]));
+              if constexpr (HAS_DB) asm volatile("" : "+v"(accb[it * V + e]));
+            }
           }
         }
         float dots[2] = {d1a + d1b, d2a + d2b};
-        group_sum_batch<2>(dots, red + ((s & 1) * G + grp) * wpr * 2, wpr, tl);
-        const int64_t li = (int64_t)s * G + grp;
-        if (li < nloc) {
+        group_sum_batch<2, WPR>(dots, red + ((s & 1) * G + grp) * wpr * 2, wpr, tl);
+        if (valid) {
           const int64_t row = b + li * P;
-          const float c1 = dots[0] / (float)N, c2 = dots[1] / (float)N;
-          S* dxr = dxb + row * a.lddx;
+          const float c1 = TAIL == Tail::FULL ? dots[0] * inv_n : dots[0] / (float)N;
+          const float c2 = TAIL == Tail::FULL ? dots[1] * inv_n : dots[1] / (float)N;
+          S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
+          const BufRsrc ob = buf_rsrc(dxr);
 #pragma unroll
           for (int it = 0; it < ITERS; ++it) {
-            const int col = (it * TPR + tl) * V;
-            if (!FULL && col >= N) continue;
+            if (!live[it]) continue;
             float o[V];
             if constexpr (KEEP) {
 #pragma unroll
@@ -397,8 +411,8 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
               }
             }
             const Raw out = IO::pack(o);
-            if (FULL || col + V <= N) IO::store(dxr + col, out);
-            else IO::store_part(dxr + col, out, N - col);
+            if (whole[it]) IO::store_b(ob, voff[it], 0, out);
+            else IO::store_part(at(dxr, (it * TPR + tl) * V), out, N - (it * TPR + tl) * V);
           }
         }
       }

@@ -182,14 +182,31 @@ rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s)
                   : launch(ln_bwd_stream_kernel<D, false, HAS_DB>, p.grid, block, p.lds, s, a);
   }
   const bool full = (int64_t)p.iters * p.tpr * Elem<D>::VEC == a.N;
-#define RMSN_LNB(IT, F)                                                                          \
-  launch(ln_bwd_rows_kernel<D, IT, LnBwdPipe<IT>::DEPTH, HAS_DB, LnBwdPipe<IT>::KEEP, F>, p.grid, \
-         block, p.lds, s, a)
+  // The tail layouts and compile-time row-group widths of the RMSNorm register backward.
+  const Tail tail = full ? Tail::FULL : (a.N % Elem<D>::VEC == 0 ? Tail::WHOLE : Tail::RAGGED);
+  const int wpr = p.tpr / 64;
+  if (block != kLnBwdBlockThreads) return RMSNORM_ERR_UNSUPPORTED;
+#define RMSN_LNB(IT, T, W)                                                                      \
+  launch(ln_bwd_rows_kernel<D, IT, LnBwdPipe<IT>::DEPTH, HAS_DB, LnBwdPipe<IT>::KEEP, T, W>, \
+         p.grid, block, p.lds, s, a)
+#define RMSN_LNB_WPR(IT, T)                         \
+  (wpr == 1   ? RMSN_LNB(IT, T, 1)                  \
+   : wpr == 2 ? RMSN_LNB(IT, T, 2)                  \
+   : wpr == 4 ? RMSN_LNB(IT, T, 4)                  \
+   : wpr == 8 ? RMSN_LNB(IT, T, 8)                  \
+              : RMSN_LNB(IT, T, 16))
   switch (p.iters) {
-    case 1: return full ? RMSN_LNB(1, true) : RMSN_LNB(1, false);
-    case 2: return full ? RMSN_LNB(2, true) : RMSN_LNB(2, false);
+    case 1:
+      return tail == Tail::FULL    ? RMSN_LNB_WPR(1, Tail::FULL)
+             : tail == Tail::WHOLE ? RMSN_LNB_WPR(1, Tail::WHOLE)
+                                   : RMSN_LNB(1, Tail::RAGGED, 0);
+    case 2:
+      return tail == Tail::FULL    ? RMSN_LNB(2, Tail::FULL, 16)
+             : tail == Tail::WHOLE ? RMSN_LNB(2, Tail::WHOLE, 16)
+                                   : RMSN_LNB(2, Tail::RAGGED, 0);
     default: return RMSNORM_ERR_UNSUPPORTED;
   }
+#undef RMSN_LNB_WPR
 #undef RMSN_LNB
 }
 
