@@ -17,17 +17,18 @@ Measurement:
 * Algorithmic bytes: forward 2*M*N*s + N*s + 4*M (read x, write y, read w, write rstd); backward
   3*M*N*s + N*s + 4*M + 4*N (read dy and x, write dx, read w and rstd, write dw). The dw partials are
   implementation traffic and are not credited.
-* roofline: the dominant kernel is the backward rows kernel. Its average duration comes from HIP
-  events recorded on the launch stream around the replay of a graph of K back-to-back launches of
-  that kernel alone (over the same rotating sets), divided by K; achieved = its algorithmic bytes
-  per launch (3*M*N*s + N*s + 4*M) / that duration. traffic is the HBM bytes per
-  launch measured with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by the same counters'
-  reading for a plain copy of known size), read from the committed summary under profiles/, and
-  null when the kernel sources have changed since that summary was taken.
-* copy_ceiling: a device-to-device copy with the forward's traffic, timed the same way; value is
-  also reported as a fraction of it.
-* bwd_ceiling: an elementwise add with the backward's traffic pattern (read x and dy, write dx),
-  timed the same way; the backward rows kernel's bandwidth is also reported as a fraction of it.
+* roofline: the dominant kernel is the backward rows kernel. Its per-launch duration comes from HIP
+  events recorded on the launch stream around the replays of a graph of K back-to-back launches of
+  that kernel alone (over the same rotating sets): the mean over the replays, with median and min
+  in kernel_stats_us; achieved = its algorithmic bytes per launch (3*M*N*s + N*s + 4*M) / that
+  duration. traffic is the HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
+  WRITE_SIZE, scaled by the same counters' reading for the library's copy kernel of known size),
+  read from the committed summary under profiles/, and null when the kernel sources have changed
+  since that summary was taken.
+* ceilings: the library's own HBM reference kernels (rmsnorm_bandwidth_probe: read only, write
+  only, copy, two reads + one write; 16-byte non-temporal accesses) over the same rotating
+  buffers, timed the same way; the forward is reported as a fraction of the copy (its traffic)
+  and the backward rows kernel as a fraction of the two-read-one-write kernel (its traffic).
 * cpu_baseline: the CPU oracle (NumPy, one thread) on a bounded sample of the same rows.
 * rows: LayerNorm, softmax, GroupNorm and the float64 RMSNorm, forward and backward, timed the same
   way (graph of back-to-back launches over rotating buffers), each with its own CPU oracle sample.
@@ -106,8 +107,11 @@ def parse_args(argv=None):
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration RMSNorm sweep")
     ap.add_argument("--ceilings", action="store_true",
-                    help="measure torch's fill, copy and add kernels at several sizes "
-                         "and exit")
+                    help="time the library's HBM reference kernels (read, write, copy, two "
+                         "reads + one write) at 32 MiB to 1 GiB per stream and exit")
+    ap.add_argument("--summarize-trace", metavar="CSV", default=None,
+                    help="print per-kernel dispatch statistics (count, mean, median, min, max "
+                         "in ns) of a rocprofv3 kernel-trace CSV and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, copy a buffer of this many MiB --steps times "
                          "(calibrates the HBM byte counters)")
@@ -188,18 +192,42 @@ class Sets:
         self.dw_reduce(b)
 
 
-def copy_probe(torch, mib, steps):
-    n = mib * 2**20 // 4
-    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+def copy_probe(torch, rn, mib, steps):
+    """The library's copy kernel over one buffer of `mib` MiB, `steps` times (the known-size
+    reference that calibrates the HBM byte counters)."""
+    nbytes = mib * 2**20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
     t = time.perf_counter()
     for _ in range(steps):
-        dst.copy_(src)
+        probe_call(rn, "copy", src.data_ptr(), None, dst.data_ptr(), nbytes, stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t
-    print(json.dumps({"copy_probe_bytes_per_launch": 2 * n * 4, "launches": steps,
-                      "GBps": 2 * n * 4 * steps / dt / 1e9}), flush=True)
+    print(json.dumps({"copy_probe_bytes_per_launch": 2 * nbytes, "launches": steps,
+                      "GBps": 2 * nbytes * steps / dt / 1e9}), flush=True)
+
+
+def summarize_trace(path):
+    """Per-kernel dispatch statistics of a rocprofv3 kernel-trace CSV (durations in ns)."""
+    import csv
+    by = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("Kernel-Name")
+            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            by.setdefault(name, []).append(d)
+    rows = []
+    for name, v in by.items():
+        v.sort()
+        n = len(v)
+        med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+        rows.append({"kernel": name, "count": n, "mean_ns": round(sum(v) / n, 1),
+                     "median_ns": med, "min_ns": v[0], "max_ns": v[-1]})
+    rows.sort(key=lambda r: -r["mean_ns"] * r["count"])
+    for r in rows:
+        print(json.dumps(r))
 
 
 class Eager:
@@ -240,101 +268,118 @@ def capture(torch, fn, count):
 
 
 def kernel_durations(torch, sets, launches):
-    """Average duration (s) of each kernel: events on the launch stream around one replay of a
-    graph of `launches` back-to-back launches of that kernel over the rotating sets."""
-    out = {}
+    """Per-launch duration of each kernel: events on the launch stream around the replays of a
+    graph of `launches` back-to-back launches of that kernel alone over the rotating sets.
+    Returns ({kernel: mean seconds per launch over all replays}, {kernel: mean/median/min in
+    us over the replays})."""
+    mean, stats = {}, {}
     n = len(sets.sets)
     for name, fn in (("fwd", sets.fwd), ("bwd_rows", sets.bwd_rows),
                      ("dw_reduce", sets.dw_reduce), ("fwd_fp8", sets.fwd_fp8)):
-        g = capture(torch, lambda k: fn(k % n), launches)
+        t = graph_stats(torch, lambda k: fn(k % n), launches)
+        stats[name] = summary(t)
+        mean[name] = sum(t) / len(t)
+    return mean, stats
+
+
+PROBE_BYTES = {"read": 1, "write": 1, "copy": 2, "sum2": 3}  # streams moved per probe launch
+
+
+def probe_call(rn, kind, a, b, c, nbytes, stream, cached=False):
+    code = rn.PROBE_CODES[kind] | (rn.PROBE_CACHED_STORES if cached else 0)
+    st = rn.library().rmsnorm_bandwidth_probe(code, a, b, c, nbytes, stream)
+    if st:
+        raise RuntimeError(f"rmsnorm_bandwidth_probe status {st}")
+
+
+def probe_ceilings(torch, rn, streams, nbytes, launches, cached_too=False):
+    """The library's HBM reference kernels (read, write, copy, two reads + one write; with
+    `cached_too` also with plain stores) over the rotating buffers `streams` = [(a, b, c), ...] of
+    `nbytes` each, timed like the RMSNorm kernels (graph of back-to-back launches rotating through
+    the buffers), and an empty launch. GB/s counts every stream."""
+    n = len(streams)
+    out_words = torch.empty(max(rn.library().rmsnorm_bandwidth_probe_out_bytes(nbytes), 16) // 4,
+                            dtype=torch.int32, device="cuda:0")
+    res = {}
+    kinds = [("read", False), ("write", False), ("copy", False), ("sum2", False)]
+    if cached_too:
+        kinds += [("write", True), ("copy", True), ("sum2", True)]
+    for kind, cached in kinds:
+        def fn(k, kind=kind, cached=cached):
+            a, b, c = streams[k % n]
+            stream = torch.cuda.current_stream().cuda_stream
+            if kind == "read":
+                probe_call(rn, kind, a.data_ptr(), None, out_words.data_ptr(), nbytes, stream)
+            else:
+                probe_call(rn, kind, a.data_ptr(), b.data_ptr(), c.data_ptr(), nbytes, stream,
+                           cached)
+        t = graph_stats(torch, fn, launches)
+        med = sorted(t)[len(t) // 2]
+        moved = PROBE_BYTES[kind] * nbytes
+        res[kind + ("_cached_stores" if cached else "")] = {
+            "GBps": round(moved / med / 1e9, 1), **summary(t), "bytes_per_launch": moved}
+
+    def empty(k):
+        probe_call(rn, "launch", None, None, None, 0, torch.cuda.current_stream().cuda_stream)
+    res["empty_launch"] = summary(graph_stats(torch, empty, launches))
+    return res
+
+
+def large_ceilings(torch, rn, mib, launches, total_mib=2048):
+    """probe_ceilings over fresh buffers of `mib` MiB per stream, rotating through at least
+    `total_mib` MiB per stream role (past the 256 MiB Infinity Cache)."""
+    nbytes = mib * 2**20
+    nsets = max(2, -(-total_mib // mib))
+    streams = [tuple(torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda:0")
+                     for _ in range(3)) for _ in range(nsets)]
+    res = probe_ceilings(torch, rn, streams, nbytes, launches, cached_too=True)
+    del streams
+    torch.cuda.empty_cache()
+    return {"stream_MiB": mib, "buffer_sets": nsets, **res}
+
+
+def ceilings(torch, rn, launches):
+    """The reference kernels at several buffer sizes (--ceilings)."""
+    out = []
+    for mib in (32, 64, 256, 1024):
+        row = large_ceilings(torch, rn, mib, launches if mib < 1024 else max(8, launches // 8))
+        out.append(row)
+        print(json.dumps(row), flush=True)
+    return out
+
+
+REPLAYS = 5  # replays of each timing graph: per-launch mean, min and median over them
+
+
+def graph_stats(torch, fn, launches, replays=REPLAYS):
+    """Seconds per call of fn(k): a graph of `launches` back-to-back calls fn(0), fn(1), ...,
+    replayed `replays` times with events on the launch stream around each replay. Returns the
+    per-launch time of every replay (seconds)."""
+    g = capture(torch, fn, launches)
+    out = []
+    for _ in range(replays):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         g.replay()
         e1.record()
         torch.cuda.synchronize()
-        out[name] = e0.elapsed_time(e1) / 1e3 / launches
-        del g
+        out.append(e0.elapsed_time(e1) / 1e3 / launches)
+    del g
     return out
 
 
-def copy_ceiling(torch, sets, launches):
-    """Device-to-device copies with the forward's traffic (read x, write y of the same rotating
-    sets), timed like the kernels: the bandwidth a plain copy reaches under the same protocol."""
-    n = len(sets.sets)
-
-    def cp(k):
-        s = sets.sets[k % n]
-        s["y"].copy_(s["x"])
-
-    g = capture(torch, cp, launches)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / launches
-    nbytes = 2 * sets.sets[0]["x"].numel() * sets.sets[0]["x"].element_size()
-    return {"GBps": round(nbytes / sec / 1e9, 1), "us": round(sec * 1e6, 3),
-            "bytes_per_launch": nbytes, "what": "hipMemcpy device-to-device, read x write y"}
-
-
-def add_ceiling(torch, sets, launches):
-    """An elementwise add dx = x + dy over the rotating sets (torch's vectorized kernel): the
-    backward's traffic pattern, two streams read and one written, without its row reductions, dw
-    sums or persistent grid, timed like the kernels."""
-    n = len(sets.sets)
-
-    def add(k):
-        s = sets.sets[k % n]
-        torch.add(s["x"], s["dy"], out=s["dx"])
-
-    sec = graph_time(torch, add, launches)
-    nbytes = 3 * sets.sets[0]["x"].numel() * sets.sets[0]["x"].element_size()
-    return {"GBps": round(nbytes / sec / 1e9, 1), "us": round(sec * 1e6, 3),
-            "bytes_per_launch": nbytes, "what": "torch.add(x, dy, out=dx): read x and dy, write dx"}
-
-
-def ceilings(torch, launches):
-    """HBM ceilings of plain torch elementwise kernels on this device: write-only (a fill), copy
-    (read + write) and add (two reads + one write), over buffers of several sizes rotating through
-    at least 2 GiB, timed like the kernels (graph of back-to-back launches). torch's reductions do
-    not reach the read bandwidth, so there is no read-only probe."""
-    out = []
-    for mib in (32, 64, 256, 1024):
-        n = mib * 2**20 // 2  # bf16 elements per buffer
-        nsets = max(2, -(-2048 // mib))
-        a = [torch.ones(n, dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
-        b = [torch.ones(n, dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
-        c = [torch.empty(n, dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
-        nb = n * 2
-        probes = {
-            "write": (lambda k: c[k % nsets].fill_(1.0), nb),
-            "copy": (lambda k: c[k % nsets].copy_(a[k % nsets]), 2 * nb),
-            "add": (lambda k: torch.add(a[k % nsets], b[k % nsets], out=c[k % nsets]), 3 * nb),
-        }
-        row = {"buffer_MiB": mib, "buffer_sets": nsets}
-        for name, (fn, nbytes) in probes.items():
-            sec = graph_time(torch, fn, launches)
-            row[name + "_GBps"] = round(nbytes / sec / 1e9, 1)
-            row[name + "_us"] = round(sec * 1e6, 3)
-        out.append(row)
-        print(json.dumps(row), flush=True)
-        del a, b, c
-        torch.cuda.empty_cache()
-    return out
+def summary(times):
+    """mean / median / min of per-launch times (seconds) in microseconds."""
+    v = sorted(times)
+    mid = v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+    return {"mean_us": round(sum(v) / len(v) * 1e6, 3), "median_us": round(mid * 1e6, 3),
+            "min_us": round(v[0] * 1e6, 3)}
 
 
 def graph_time(torch, fn, launches):
-    """Average seconds per call of fn(k): events around one replay of a graph of `launches` calls."""
-    g = capture(torch, fn, launches)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / launches
-    del g
-    return sec
+    """Median seconds per call of fn(k) over the replays of graph_stats."""
+    v = sorted(graph_stats(torch, fn, launches))
+    return v[len(v) // 2]
 
 
 def layernorm_row(torch, rn, sets, launches):
@@ -516,15 +561,16 @@ def groupnorm_row(torch, rn, launches, rotate_mib):
 CONFIG_SWEEP = [("fp32_64x1024", None), ("bf16_4096x4096", "once"), ("fp16_8192x8192", None),
                 ("bf16_16384x3072_gemma", None)] + [
     (f"bf16_sweep_4096x{n}", None) for n in (1024, 2048, 4096, 8192, 16384, 32768)]
-MAX_SETS = 64
+MAX_SETS = 1024  # only the launch-bound float32 64 x 1024 correctness case reaches it
 
 
 def config_sweep(torch, rn, launches, rotate_mib):
     """Per configuration and rounding mode: step time (graph of `launches` steps), each kernel's
-    average duration, algorithmic GB/s and fraction of the HBM peak per phase. Inputs are drawn on
-    the device with each workload's distributions (make_device_inputs). Small configurations
-    rotate over at most MAX_SETS buffer sets, so they run from the caches (their numbers are
-    launch-bound, not bandwidth figures)."""
+    per-launch time (median, with mean and min, over the replays of its timing graph), algorithmic
+    GB/s and fraction of the HBM peak per phase. Inputs are drawn on the device with each
+    workload's distributions (make_device_inputs). Every configuration rotates over enough buffer
+    sets that its x matrices span `rotate_mib` MiB, except the float32 64 x 1024 case (capped at
+    MAX_SETS sets: cache-resident and launch-bound, not a bandwidth figure)."""
     from workloads import WORKLOADS, make_device_inputs
     out = []
     for name, rounding in CONFIG_SWEEP:
@@ -537,8 +583,10 @@ def config_sweep(torch, rn, launches, rotate_mib):
         for i in range(nsets):
             sets.fwd(i)
         torch.cuda.synchronize()
-        step = graph_time(torch, sets.step, launches)
-        dur = kernel_durations(torch, sets, launches)
+        step_t = graph_stats(torch, sets.step, launches)
+        step = sorted(step_t)[len(step_t) // 2]
+        dur, stats = kernel_durations(torch, sets, launches)
+        stats["step"] = summary(step_t)
         bwd = dur["bwd_rows"] + dur["dw_reduce"]
         fb, bb = wl.fwd_bytes(), wl.bwd_bytes()
         cached = nsets * wl.M * wl.N * wl.itemsize < 2**30
@@ -552,7 +600,8 @@ def config_sweep(torch, rn, launches, rotate_mib):
             "fwd_GBps": round(fb / dur["fwd"] / 1e9, 1), "bwd_GBps": round(bb / bwd / 1e9, 1),
             "step_frac_of_peak": round((fb + bb) / step / 1e9 / PEAK_HBM_GBPS, 4),
             "fwd_frac_of_peak": round(fb / dur["fwd"] / 1e9 / PEAK_HBM_GBPS, 4),
-            "bwd_frac_of_peak": round(bb / bwd / 1e9 / PEAK_HBM_GBPS, 4)})
+            "bwd_frac_of_peak": round(bb / bwd / 1e9 / PEAK_HBM_GBPS, 4),
+            "stats": {k: v for k, v in stats.items() if k != "fwd_fp8"}})
         print(json.dumps({"config_done": name, "rounding": rounding}), file=sys.stderr,
               flush=True)
         del sets
@@ -651,6 +700,10 @@ def main(argv=None) -> int:
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return 0
+
     import torch
 
     import bwd_precision_numerics_amd as rn
@@ -662,10 +715,10 @@ def main(argv=None) -> int:
     rn.library()  # fails loudly if the HIP library is missing
     torch.cuda.set_device(0)
     if args.copy_probe_mib:
-        copy_probe(torch, args.copy_probe_mib, args.steps)
+        copy_probe(torch, rn, args.copy_probe_mib, args.steps)
         return 0
     if args.ceilings:
-        ceilings(torch, max(min(args.steps, 100), 20))
+        ceilings(torch, rn, max(min(args.steps, 100), 20))
         return 0
 
     name = args.workload or HEADLINE
@@ -707,9 +760,11 @@ def main(argv=None) -> int:
     step_bytes = wl.fwd_bytes() + wl.bwd_bytes()
     value = step_bytes * args.steps / elapsed / 1e9
 
-    dur = kernel_durations(torch, sets, max(args.steps, 20))
-    copy = copy_ceiling(torch, sets, max(args.steps, 20))
-    addc = add_ceiling(torch, sets, max(args.steps, 20))
+    dur, kstats = kernel_durations(torch, sets, max(args.steps, 20))
+    # The library's reference kernels over the same rotating buffers (x, dy read; y, dx written),
+    # and at 1 GiB per stream (steady state).
+    streams = [(st["x"], st["dy"], st["dx"]) for st in sets.sets]
+    ceil32 = probe_ceilings(torch, rn, streams, wl.M * wl.N * wl.itemsize, max(args.steps, 20))
     del graph
     s = wl.itemsize
     rows_bytes = 3 * wl.M * wl.N * s + wl.N * s + 4 * wl.M
@@ -746,10 +801,14 @@ def main(argv=None) -> int:
                        "fwd_fp8": round(fp8_bytes / dur["fwd_fp8"] / 1e9, 1),
                        "bwd": round(wl.bwd_bytes() / (dur["bwd_rows"] + dur["dw_reduce"]) / 1e9,
                                     1)},
-        "copy_ceiling": copy,
-        "frac_of_copy_ceiling": round(value / copy["GBps"], 4),
-        "bwd_ceiling": addc,
-        "bwd_rows_frac_of_bwd_ceiling": round(achieved / addc["GBps"], 4),
+        "kernel_stats_us": kstats,
+        "ceilings": {"stream_bytes": wl.M * wl.N * s, "rotating_sets": len(sets.sets),
+                     "what": "rmsnorm_bandwidth_probe: read / write / copy (1 read + 1 write) / "
+                             "sum2 (2 reads + 1 write), 16-byte non-temporal accesses, same "
+                             "rotation and graph timing", **ceil32},
+        "fwd_frac_of_copy_ceiling": round(wl.fwd_bytes() / dur["fwd"] / 1e9
+                                          / ceil32["copy"]["GBps"], 4),
+        "bwd_rows_frac_of_sum2_ceiling": round(achieved / ceil32["sum2"]["GBps"], 4),
     }
     if not args.no_rows and name == HEADLINE:
         launches = max(min(args.steps, 100), 20)
@@ -768,6 +827,10 @@ def main(argv=None) -> int:
         sets = None
         torch.cuda.empty_cache()
         line["configs"] = config_sweep(torch, rn, max(min(args.steps, 100), 20), args.rotate_mib)
+    if not args.no_rows and name == HEADLINE:
+        sets = None
+        torch.cuda.empty_cache()
+        line["ceilings_1GiB"] = large_ceilings(torch, rn, 1024, 8)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(wl, rounding, inp, args.cpu_seconds)
         if "rows" in line:

@@ -39,6 +39,8 @@ BWD_AUTOGRAD_CASTS = 0x10  # flag OR-ed into the backward's rounding argument
 CASTS = ("float32", "autograd")
 VARIANT_CODES = {"auto": 0, "registers": 1, "lds": 2, "streaming": 3}
 FP8_CODES = {"e4m3": 0, "e5m2": 1}
+PROBE_CODES = {"read": 0, "write": 1, "copy": 2, "sum2": 3, "launch": 4}
+PROBE_CACHED_STORES = 0x100  # OR-ed into a probe kind: plain stores instead of non-temporal
 STATUS_NAMES = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_MISALIGNED",
                 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
@@ -92,6 +94,8 @@ SIGNATURES = {
     "rmsnorm_bwd_f64_workspace_bytes": (_sz, [_i64, _i64]),
     "rmsnorm_bwd_f64": (_i, [_p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p, _sz, _i64, _i64, _d,
                              _p]),
+    "rmsnorm_bandwidth_probe_out_bytes": (_sz, [_sz]),
+    "rmsnorm_bandwidth_probe": (_i, [_i, _p, _p, _p, _sz, _p]),
     "rmsnorm_status_string": (ctypes.c_char_p, [_i]),
     "rmsnorm_abi_version": (_i, []),
 }

@@ -1,8 +1,10 @@
 """Compile the HIP library ``librmsnorm.so`` for gfx950, in place next to this file.
 
-The library is built from three translation units: ``librmsnorm.hip`` (the RMSNorm entry points of
-``include/librmsnorm.h``), ``libnorms.hip`` (LayerNorm and GroupNorm, ``include/libnorms.h``) and
-``libsoftmax.hip`` (softmax, ``include/libsoftmax.h``, and the float64 RMSNorm).
+The library is built from four translation units: ``librmsnorm.hip`` (the RMSNorm entry points of
+``include/librmsnorm.h``), ``libnorms.hip`` (LayerNorm and GroupNorm, ``include/libnorms.h``),
+``libsoftmax.hip`` (softmax, ``include/libsoftmax.h``, and the float64 RMSNorm) and
+``libceiling.hip`` (the HBM bandwidth reference kernels of the measurement section of
+``include/librmsnorm.h``).
 
 Usage: ``python -m bwd_precision_numerics_amd.build [--resource-usage FILE]``.
 
@@ -25,7 +27,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", f) for f in ("librmsnorm.hip", "libnorms.hip", "libsoftmax.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("librmsnorm.hip", "libnorms.hip", "libsoftmax.hip",
+                                                 "libceiling.hip")]
 OUT = os.path.join(HERE, "librmsnorm.so")
 HEADERS = [os.path.join(HERE, "csrc", f) for f in
            ("host_common.hpp", "rmsnorm_common.hpp", "rmsnorm_fwd.hpp", "rmsnorm_bwd.hpp",

@@ -93,8 +93,8 @@ typedef enum rmsnorm_fp8_format {
   RMSNORM_FP8_E5M2 = 1   /* bias 15, largest finite 57344, IEEE-style: overflow gives +-inf */
 } rmsnorm_fp8_format;
 
-/* Kernel family. AUTO picks by dtype and N (and, in the backward, the autograd-casts flag), for
- * speed; rstd, y and dx do not depend on the family. The others force one family, for consistency
+/* Kernel family. AUTO picks by dtype, N and the row layout, for speed; rstd, y and dx do not
+ * depend on the family. The others force one family, for consistency
  * tests and measurements; a forced family that cannot serve the arguments returns
  * RMSNORM_ERR_UNSUPPORTED with nothing launched.
  *   REGISTERS  a row lives in registers between the reduction and the elementwise pass
@@ -250,6 +250,36 @@ rmsnorm_status rmsnorm_bwd_f64(const double* dy, int64_t lddy, const double* x, 
                                const double* w, const double* rstd, double* dx, int64_t lddx,
                                double* dw, void* workspace, size_t workspace_bytes, int64_t M,
                                int64_t N, double offset, void* stream);
+
+/* ---- measurement --------------------------------------------------------------------------------
+ * HBM bandwidth reference kernels: plain 16-byte streaming patterns with the RMSNorm kernels'
+ * non-temporal cache policy, the ceilings the benchmark reports the RMSNorm kernels against (the
+ * algorithmic bytes of a pass are those of one of these patterns: the forward moves a copy's, the
+ * backward rows a two-read-one-write's). `bytes` is the size of each stream, a multiple of 16;
+ * all pointers are 16-byte aligned device memory owned by the caller; one kernel is enqueued on
+ * `stream`, nothing is allocated.
+ *   RMSNORM_PROBE_READ    reads a; writes rmsnorm_bandwidth_probe_out_bytes(bytes) bytes to c
+ *                         (one word per block, so the loads are kept)
+ *   RMSNORM_PROBE_WRITE   writes c
+ *   RMSNORM_PROBE_COPY    c = a
+ *   RMSNORM_PROBE_SUM2    c = a + b (32-bit integer lanes)
+ *   RMSNORM_PROBE_LAUNCH  one empty 64-thread block (pointers and bytes ignored): the cost of a
+ *                         launch
+ * `kind` may be OR-ed with RMSNORM_PROBE_CACHED_STORES: plain stores instead of non-temporal ones.
+ * Errors: RMSNORM_ERR_INVALID_ARG (unknown kind, a needed pointer NULL, bytes not a multiple of
+ * 16), RMSNORM_ERR_MISALIGNED; all before any HIP call. */
+enum {
+  RMSNORM_PROBE_READ = 0,
+  RMSNORM_PROBE_WRITE = 1,
+  RMSNORM_PROBE_COPY = 2,
+  RMSNORM_PROBE_SUM2 = 3,
+  RMSNORM_PROBE_LAUNCH = 4,
+  RMSNORM_PROBE_CACHED_STORES = 0x100
+};
+
+size_t rmsnorm_bandwidth_probe_out_bytes(size_t bytes);
+rmsnorm_status rmsnorm_bandwidth_probe(int kind, const void* a, const void* b, void* c,
+                                       size_t bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* rmsnorm_status_string(rmsnorm_status status);

@@ -170,6 +170,22 @@ def test_bwd_noalloc_refuses_before_any_hip_call(lib):
     assert call(dw=FAKE + 2) == MISALIGNED
 
 
+def test_bandwidth_probe_refuses_before_any_hip_call(lib):
+    """The HBM reference kernels' entry point checks kind, pointers, size and alignment first."""
+    f = lib.rmsnorm_bandwidth_probe
+    assert f(0, FAKE, None, FAKE, 0, None) == OK  # nothing to move: nothing launched
+    assert f(9, FAKE, FAKE, FAKE, 4096, None) == INVALID
+    assert f(9 | 0x100, FAKE, FAKE, FAKE, 4096, None) == INVALID
+    assert f(0, FAKE, None, FAKE, 4100, None) == INVALID
+    assert f(0, None, None, FAKE, 4096, None) == INVALID
+    assert f(1, FAKE, None, None, 4096, None) == INVALID
+    assert f(3, FAKE, None, FAKE, 4096, None) == INVALID
+    assert f(2, FAKE + 4, None, FAKE, 4096, None) == MISALIGNED
+    assert f(2 | 0x100, FAKE, None, FAKE + 8, 4096, None) == MISALIGNED
+    # one word per 512-thread block of two 16-byte vectors per thread
+    assert lib.rmsnorm_bandwidth_probe_out_bytes(32 << 20) == ((32 << 20) // 16384) * 4
+
+
 def test_binding_rejects_host_tensors_before_calling():
     import torch
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
