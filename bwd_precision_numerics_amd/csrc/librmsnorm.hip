@@ -45,11 +45,12 @@ template <> struct BwdPipe<2> {
 };
 int bwd_batch(int iters) { return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB; }
 
-// Automatic selection prefers the register kernel, then the LDS-staged one, except for two
-// instantiations that spill registers and measured slower than the streaming kernel (bf16, M = 4096):
-// the 2-vector register kernel with the autograd casts (N = 16384: 144 us against 127) and the
-// 4-vector LDS-staged kernel on rows its vectors do not tile (N = 30000: 256 us against 212;
-// N = 32760: 271 against 233). The families give bit-identical results, so this changes only speed.
+// Automatic selection prefers the register kernel, then the LDS-staged one. The one exception is
+// the 4-vector LDS-staged kernel on rows with a partial 16-byte vector (padded row strides), which
+// spills registers; it takes the streaming kernel. Measured (bf16, M = 4096, rows + dw reduction):
+// autograd casts at N = 16384, registers 79 us against 123 streaming; N = 30000 and 32760 (whole
+// vectors, idle lanes), LDS-staged 161 and 179 us against 209 and 228. The families give
+// bit-identical results, so the choice changes only speed.
 rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, bool ag,
                         rmsnorm_variant req, Plan* p) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
@@ -57,13 +58,13 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   bwd_shape(nv_wide, &tpr, &iters);
   const bool reg_ok = wide_ok && iters <= kBwdRegMaxIters;
   const bool lds_ok = wide_ok && iters <= kBwdLdsMaxIters;
-  const bool tiled = (int64_t)iters * tpr * vec_elems(dtype) == N;
   rmsnorm_variant v = req;
   if (v == RMSNORM_VARIANT_AUTO) {
     if (reg_ok)
-      v = ag && iters == 2 ? RMSNORM_VARIANT_STREAMING : RMSNORM_VARIANT_REGISTERS;
+      v = RMSNORM_VARIANT_REGISTERS;
     else if (lds_ok)
-      v = iters == 4 && !tiled ? RMSNORM_VARIANT_STREAMING : RMSNORM_VARIANT_LDS;
+      v = iters == 4 && N % vec_elems(dtype) != 0 ? RMSNORM_VARIANT_STREAMING
+                                                  : RMSNORM_VARIANT_LDS;
     else
       v = RMSNORM_VARIANT_STREAMING;
   }
@@ -148,9 +149,13 @@ rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
   if (p.variant == RMSNORM_VARIANT_LDS) {
     // Rows of 3 or 4 vectors per thread have 1024 threads (one row group) per block: the kernel
     // takes that as a compile-time constant.
-#define RMSN_BWD_LDS(IT, TPRC)                                                              \
-  (full ? launch(bwd_lds_kernel<D, IT, AG, true, TPRC>, p.grid, block, p.lds, s, a)         \
-        : launch(bwd_lds_kernel<D, IT, AG, false, TPRC>, p.grid, block, p.lds, s, a))
+    const Tail ltail = full ? Tail::FULL : (a.N % Elem<D>::VEC == 0 ? Tail::WHOLE : Tail::RAGGED);
+#define RMSN_BWD_LDS(IT, TPRC)                                                                     \
+  (ltail == Tail::FULL ? launch(bwd_lds_kernel<D, IT, AG, Tail::FULL, TPRC>, p.grid, block, p.lds, \
+                                s, a)                                                               \
+   : ltail == Tail::WHOLE                                                                           \
+       ? launch(bwd_lds_kernel<D, IT, AG, Tail::WHOLE, TPRC>, p.grid, block, p.lds, s, a)         \
+       : launch(bwd_lds_kernel<D, IT, AG, Tail::RAGGED, TPRC>, p.grid, block, p.lds, s, a))
     switch (p.iters) {
       case 1: return RMSN_BWD_LDS(1, 0);
       case 2: return RMSN_BWD_LDS(2, 0);

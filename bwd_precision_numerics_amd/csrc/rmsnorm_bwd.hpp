@@ -326,8 +326,10 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 // row's loads in flight (a two-row pipeline), so registers carry the column accumulators and one
 // row of raw data. The gain is re-read from w (cache-resident) in each pass. Same thread-to-element
 // mapping and summation order as the register kernel, so dx is bit-identical to it for the same
-// shape. FULL: as in the register kernel.
-template <DT D, int ITERS, bool AG, bool FULL, int TPRC = 0>
+// shape. TAIL as for the register kernel: whole vectors on every lane, whole vectors or none
+// (idle lanes), or a partial last vector. The next row's loads are straight-line code (a block's
+// last step reads w instead), so the compiler waits only for them, not for the stores in flight.
+template <DT D, int ITERS, bool AG, Tail TAIL, int TPRC = 0>
 __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -350,35 +352,40 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
 
   const S* wr = static_cast<const S*>(a.w);
   const BufRsrc wbuf = buf_rsrc(wr);
-  // Whole vectors go through buffer accesses: lane offset tl * 16 bytes, vector it at the
-  // wave-uniform offset it * TPR * 16.
-  const uint32_t voff = (uint32_t)tl * 16u;
+  // Lane's vector it: byte offset in the row (vector it * TPR + tl; 0 for a lane without a whole
+  // vector, whose loads are never used), whole / any elements, as in the register kernel.
+  bool whole[ITERS], live[ITERS];
+  uint32_t voff[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    live[it] = TAIL == Tail::FULL || col < N;
+    whole[it] = TAIL == Tail::RAGGED ? col + V <= N : live[it];
+    voff[it] = whole[it] ? (uint32_t)col * (uint32_t)sizeof(S) : 0u;
+  }
   float acc[ITERS * V];
 #pragma unroll
   for (int k = 0; k < ITERS * V; ++k) acc[k] = 0.f;
 
   // Registers carry the next row's raw x and dy (and rstd) while the current one is processed
-  // from the stage; rows past the block's share load as zeros and rstd 0 (they add nothing).
+  // from the stage.
   Raw rx[ITERS], rd[ITERS];
   float rs_next = 0.f;
   auto load_row = [&](int s) {
     const int64_t li = (int64_t)s * G + grp;
     const bool ok = s < nsteps && li < nloc;
     const int64_t row = b + (ok ? li : 0) * P;
-    const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
-    const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
+    const S* xr = ok ? static_cast<const S*>(a.x) + row * a.ldx : wr;
+    const S* dr = ok ? static_cast<const S*>(a.dy) + row * a.lddy : wr;
     const BufRsrc xb = buf_rsrc(xr), db = buf_rsrc(dr);
-    rs_next = ok ? a.rstd[row] : 0.f;
+    rs_next = a.rstd[row];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      const int col = (it * TPR + tl) * V;
-      const uint32_t soff = (uint32_t)(it * TPR) * 16u;
-      rx[it] = rd[it] = IO::zero();
-      if (ok) {
-        if (FULL || col + V <= N) {
-          rx[it] = IO::load_b_nt(xb, voff, soff);
-          rd[it] = IO::load_b_nt(db, voff, soff);
-        } else if (col < N) {
+      rx[it] = IO::load_b_nt(xb, voff[it], 0);
+      rd[it] = IO::load_b_nt(db, voff[it], 0);
+      if constexpr (TAIL == Tail::RAGGED) {
+        const int col = (it * TPR + tl) * V;
+        if (!whole[it] && live[it]) {
           rx[it] = IO::load_part(at(xr, col), N - col);
           rd[it] = IO::load_part(at(dr, col), N - col);
         }
@@ -387,9 +394,12 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
   };
   load_row(0);
 
+  // c = dot / N: a multiply for exactly tiled rows (a power of two wide), else a division.
+  const float inv_n = 1.0f / (float)N;
+
   for (int s = 0; s < nsteps; ++s) {
     const int64_t li = (int64_t)s * G + grp;
-    const bool valid = li < nloc;
+    const bool valid = li < nloc;  // wave-uniform
     const int64_t row = b + (valid ? li : 0) * P;
     // Each thread reads back only the stage slots it wrote, so no barrier guards the stage.
 #pragma unroll
@@ -399,57 +409,65 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
     }
     const float rs = rs_next;
     load_row(s + 1);
-    // Opaque copies of the lane's stage index and w offset. Without them the compiler would
+    // Opaque copies of the lane's stage index and w offsets. Without them the compiler would
     // forward the values just stored to the stage instead of reading them back (keeping this
     // row's raw data live next to the next row's loads), and would hoist the w loads (the same for
     // every row) out of the row loop, holding the whole gain in registers.
     int tl1 = tl;
-    uint32_t wvoff = voff;
-    asm volatile("" : "+v"(tl1), "+v"(wvoff));
+    uint32_t wv1[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) wv1[it] = voff[it];
+    asm volatile("" : "+v"(tl1));
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) asm volatile("" : "+v"(wv1[it]));
     float d0 = 0.f, d1 = 0.f;
+    if (valid) {
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int col = (it * TPR + tl) * V;
-      const uint32_t soff = (uint32_t)(it * TPR) * 16u;
-      Raw rw = IO::zero();
-      if (FULL || col + V <= N) rw = IO::load_b(wbuf, wvoff, soff);
-      else if (col < N) rw = IO::load_part(at(wr, col), N - col);
-      float xf[V], df[V], wf[V];
-      IO::unpack(stage[it * TPR + tl1], xf);
-      IO::unpack(stage[(ITERS + it) * TPR + tl1], df);
-      IO::unpack(rw, wf);
+      for (int it = 0; it < ITERS; ++it) {
+        if (!live[it]) continue;
+        const int col = (it * TPR + tl) * V;
+        Raw rw = IO::load_b(wbuf, wv1[it], 0);
+        if (TAIL == Tail::RAGGED && !whole[it]) rw = IO::load_part(at(wr, col), N - col);
+        float xf[V], df[V], wf[V];
+        IO::unpack(stage[it * TPR + tl1], xf);
+        IO::unpack(stage[(ITERS + it) * TPR + tl1], df);
+        IO::unpack(rw, wf);
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const float xh = xf[e] * rs;
-        const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
-        acc[it * V + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), acc[it * V + e]);
-        if (e & 1) d1 = __builtin_fmaf(gd, xh, d1);
-        else d0 = __builtin_fmaf(gd, xh, d0);
+        for (int e = 0; e < V; ++e) {
+          const float xh = xf[e] * rs;
+          const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
+          acc[it * V + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), acc[it * V + e]);
+          if (e & 1) d1 = __builtin_fmaf(gd, xh, d1);
+          else d0 = __builtin_fmaf(gd, xh, d0);
+        }
+        // One vector at a time, with its dw updates done here: left to itself the compiler sinks
+        // them past the reduction and keeps every vector's xhat and dy live until then, which the
+        // accumulators and the next row's loads leave no registers for.
+#pragma unroll
+        for (int e = 0; e < V; ++e) asm volatile("" : "+v"(acc[it * V + e]));
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // One vector at a time, with its dw updates done here: left to itself the compiler sinks
-      // them past the reduction and keeps every vector's xhat and dy live until then, which the
-      // accumulators and the next row's loads leave no registers for.
-#pragma unroll
-      for (int e = 0; e < V; ++e) asm volatile("" : "+v"(acc[it * V + e]));
-      __builtin_amdgcn_sched_barrier(0);
     }
     const float dot = group_sum(d0 + d1, red + (s & 1) * G * wpr + grp * wpr, wpr, tl);
-    const float c = dot / (float)N;
+    const float c = TAIL == Tail::FULL ? dot * inv_n : dot / (float)N;
     // Fresh opaque copies for the second pass, which reads the same addresses as the first:
     // otherwise the first pass's values stay live across the reduction.
     int tl2 = tl;
-    uint32_t wvoff2 = voff;
-    asm volatile("" : "+v"(tl2), "+v"(wvoff2));
+    uint32_t wv2[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) wv2[it] = voff[it];
+    asm volatile("" : "+v"(tl2));
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) asm volatile("" : "+v"(wv2[it]));
     if (valid) {
       S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
       const BufRsrc dxb = buf_rsrc(dxr);
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
+        if (!live[it]) continue;
         const int col = (it * TPR + tl) * V;
-        const uint32_t soff = (uint32_t)(it * TPR) * 16u;
-        if (!FULL && col >= N) continue;
-        const bool whole = FULL || col + V <= N;
-        Raw rw = whole ? IO::load_b(wbuf, wvoff2, soff) : IO::load_part(at(wr, col), N - col);
+        Raw rw = IO::load_b(wbuf, wv2[it], 0);
+        if (TAIL == Tail::RAGGED && !whole[it]) rw = IO::load_part(at(wr, col), N - col);
         float xf[V], df[V], wf[V], o[V];
         IO::unpack(stage[it * TPR + tl2], xf);
         IO::unpack(stage[(ITERS + it) * TPR + tl2], df);
@@ -461,7 +479,7 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
           o[e] = rs * (gd - xh * c);
         }
         const Raw out = IO::pack(o);
-        if (whole) IO::store_b(dxb, voff, soff, out);
+        if (whole[it]) IO::store_b(dxb, voff[it], 0, out);
         else IO::store_part(at(dxr, col), out, N - col);
         __builtin_amdgcn_sched_barrier(0);
       }
