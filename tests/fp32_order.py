@@ -1,0 +1,167 @@
+"""Models of the float32 summation order of the LayerNorm and GroupNorm backward kernels.
+
+The oracle sums a row's c1 = sum(w * dy) / N and c2 = sum(w * dy * xhat) / N in float64 and rounds
+once; the GPU sums in float32, in the order its thread-to-element mapping fixes. Where w * dy is
+nearly constant along a row (an upstream gradient of ones), dx = rstd * ((w * dy - c1) - xhat * c2)
+cancels, and the last bits of c1 reach the rounding to T for more elements than elsewhere. These
+models reproduce the kernels' float32 order on the CPU, so a test can measure how many dx
+elements that order alone moves off the oracle on its own inputs, and bound the bit-exact rate
+from that instead of from the GPU's output.
+
+LayerNorm (one row group per row, the mapping of the register and streaming kernels): a row of
+nv 16-byte vectors of V elements goes to TPR = clamp(next power of two >= nv, 64, 1024) threads,
+thread t owning vectors t, t + TPR, ...; each thread keeps two accumulators (even and odd elements
+of its vectors, in order; compensated (Kahan) sums once a thread holds more than 8 vectors, plain
+sums with fused multiply-adds for c2 otherwise), adds them, and the 64 lanes of a wavefront are
+summed by a pairwise tree in lane order (the DPP reduction), then the wavefronts in order.
+
+GroupNorm (a row is a (batch, group) slice of Cg channels of S elements): each channel's elements
+are cut into chunks of at most 8192 (16-bit types) elements; a chunk's 256 threads own 4 vectors of
+8 elements each (vector it * 256 + t), keep even/odd accumulators, and the block sums them (the
+pairwise lane tree, then 4 wavefronts in order). The row constants then add w_c * chunk sum over
+the row's chunks, lane-strided over 64 lanes (chunk e to lane e % 64, in order) and a halving
+shuffle tree (lane i adds lane i + 32, then + 16, ...).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle.layernorm import normalize
+from oracle.rounding import rne_to
+
+import oracle
+
+
+def _fma(a, b, c):
+    """float32 fused multiply-add (the float64 product of two float32 values is exact)."""
+    return (a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)).astype(np.float32)
+
+
+def _kahan(s, c, v):
+    y = (v - c).astype(np.float32)
+    t = (s + y).astype(np.float32)
+    c = ((t - s).astype(np.float32) - y).astype(np.float32)
+    return t, c
+
+
+def _lane_tree(t):
+    """Pairwise sum over the last axis (64 lanes) in lane order."""
+    while t.shape[-1] > 1:
+        t = (t[..., 0::2] + t[..., 1::2]).astype(np.float32)
+    return t[..., 0]
+
+
+def ln_row_sums(gd, xh, V: int = 8):
+    """float32 sums(gd) and sums(gd * xhat) of each row [M, N], in the LayerNorm backward's order."""
+    M, N = gd.shape
+    nv = -(-N // V)
+    tpr = int(min(max(1 << max(nv - 1, 0).bit_length(), 64), 1024))
+    iters = -(-nv // tpr)
+    pad = iters * tpr * V - N
+    G = np.pad(gd, ((0, 0), (0, pad))).reshape(M, iters, tpr, V)
+    X = np.pad(xh, ((0, 0), (0, pad))).reshape(M, iters, tpr, V)
+    comp = iters > 8
+    acc = {k: np.zeros((M, tpr), np.float32) for k in ("a1", "b1", "a2", "b2",
+                                                     "ca1", "cb1", "ca2", "cb2")}
+    for it in range(iters):
+        for e in range(V):
+            g, x = G[:, it, :, e], X[:, it, :, e]
+            p = "a" if e % 2 == 0 else "b"
+            if comp:
+                acc[p + "1"], acc["c" + p + "1"] = _kahan(acc[p + "1"], acc["c" + p + "1"], g)
+                acc[p + "2"], acc["c" + p + "2"] = _kahan(acc[p + "2"], acc["c" + p + "2"],
+                                                          (g * x).astype(np.float32))
+            else:
+                acc[p + "1"] = (acc[p + "1"] + g).astype(np.float32)
+                acc[p + "2"] = _fma(g, x, acc[p + "2"])
+    out = []
+    for k in ("1", "2"):
+        t = ((acc["a" + k] + acc["b" + k]).astype(np.float32)
+             - (acc["ca" + k] + acc["cb" + k]).astype(np.float32)).astype(np.float32)
+        waves = _lane_tree(t.reshape(M, tpr // 64, 64))
+        s = waves[:, 0]
+        for w in range(1, waves.shape[1]):
+            s = (s + waves[:, w]).astype(np.float32)
+        out.append(s)
+    return out[0], out[1]
+
+
+def ln_dx_model_bitexact(dy, x, w, mean, rstd, *, dtype: str) -> float:
+    """Fraction of dx elements that the LayerNorm kernels' float32 order of c1, c2 leaves
+    bit-identical to the oracle's dx (same mean and rstd, same elementwise steps)."""
+    x = np.asarray(x, np.float32)
+    xh = normalize(x, mean, rstd, False).astype(np.float32)
+    gd = (np.asarray(w, np.float32) * np.asarray(dy, np.float32)).astype(np.float32)
+    s1, s2 = ln_row_sums(gd, xh, 4 if dtype == "f32" else 8)
+    n = np.float32(x.shape[-1])
+    c1 = (s1 / n).astype(np.float32)[:, None]
+    c2 = (s2 / n).astype(np.float32)[:, None]
+    r = np.asarray(rstd, np.float32)[:, None]
+    with np.errstate(invalid="ignore", over="ignore"):
+        dx = rne_to((r * ((gd - c1).astype(np.float32) - (xh * c2).astype(np.float32))
+                     ).astype(np.float32), dtype)
+    dx_o, _, _ = oracle.layernorm_bwd(dy, x, w, mean, rstd, dtype=dtype)
+    return _same_frac(dx, dx_o)
+
+
+def gn_dx_model_bitexact(dy, x, w, mean, rstd, *, G: int, dtype: str) -> float:
+    """As ln_dx_model_bitexact for GroupNorm ([B, C, S] inputs, mean and rstd [B, G])."""
+    x = np.asarray(x, np.float32)
+    dy = np.asarray(dy, np.float32)
+    B, C, S = x.shape
+    Cg = C // G
+    ch = 8192 if dtype != "f32" else 4096
+    V = 8 if dtype != "f32" else 4
+    K = -(-S // ch)
+    m = np.asarray(mean, np.float32).reshape(B, G)
+    r = np.asarray(rstd, np.float32).reshape(B, G)
+    mc = np.repeat(m, Cg, axis=1)[..., None]
+    rc = np.repeat(r, Cg, axis=1)[..., None]
+    xh = ((x - mc).astype(np.float32) * rc).astype(np.float32)  # [B, C, S]
+    # per-chunk sums: 256 threads x 4 vectors of V, even / odd accumulators, lane tree, 4 waves
+    pad = K * ch - S
+    D = np.pad(dy, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, 256, V)
+    X = np.pad(xh, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, 256, V)
+    a1 = b1 = a2 = b2 = np.zeros((B, C, K, 256), np.float32)
+    for it in range(4):
+        for e in range(V):
+            d, xx = D[..., it, :, e], X[..., it, :, e]
+            if e % 2:
+                b1, b2 = (b1 + d).astype(np.float32), _fma(d, xx, b2)
+            else:
+                a1, a2 = (a1 + d).astype(np.float32), _fma(d, xx, a2)
+    sums = []
+    for p, q in ((a1, b1), (a2, b2)):
+        waves = _lane_tree((p + q).astype(np.float32).reshape(B, C, K, 4, 64))
+        s = waves[..., 0]
+        for k in range(1, 4):
+            s = (s + waves[..., k]).astype(np.float32)
+        sums.append(s)  # [B, C, K]
+    wv = np.asarray(w, np.float32)
+    consts = []
+    for s in sums:
+        ent = (wv[None, :, None] * s).astype(np.float32).reshape(B, G, Cg * K)  # row entries
+        nent = Cg * K
+        lanes = np.zeros((B, G, 64), np.float32)
+        for e in range(nent):
+            lanes[..., e % 64] = (lanes[..., e % 64] + ent[..., e]).astype(np.float32)
+        off = 32
+        while off >= 1:
+            lanes[..., :off] = (lanes[..., :off] + lanes[..., off:2 * off]).astype(np.float32)
+            off //= 2
+        consts.append((lanes[..., 0] / np.float32(Cg * S)).astype(np.float32))
+    c1 = np.repeat(consts[0], Cg, axis=1)[..., None]
+    c2 = np.repeat(consts[1], Cg, axis=1)[..., None]
+    gd = (wv[None, :, None] * dy).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        dx = rne_to((rc * ((gd - c1).astype(np.float32) - (xh * c2).astype(np.float32))
+                     ).astype(np.float32), dtype)
+    dx_o, _, _ = oracle.groupnorm_bwd(dy, x, w, m, r, G=G, dtype=dtype)
+    return _same_frac(dx, dx_o)
+
+
+def _same_frac(a, b) -> float:
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    eq = (np.isnan(a) & np.isnan(b)) | (a.view(np.uint32) == b.view(np.uint32))
+    return float(eq.mean()) if eq.size else 1.0

@@ -196,11 +196,19 @@ def check_stats(mean_gpu, rstd_gpu, mean_o, rstd_o, x_rows) -> dict:
     return stats
 
 
-# LayerNorm's dx subtracts c1 = mean(w * dy) from w * dy; when dy is nearly constant along a row
-# (the upstream of ones of the fp16 workload) that difference cancels, and the float32 order in
-# which the GPU sums c1 (and c2) moves a larger share of the roundings to T than in RMSNorm's dx:
-# observed 98.97 % bit-identical on three 70000-wide float16 rows, every element within 1 ulp.
-LN_DX_BITEXACT_FRAC = 0.98
+# LayerNorm's and GroupNorm's dx subtract c1 = mean(w * dy) from w * dy. Where dy is nearly
+# constant along a row (an upstream gradient of ones) that difference cancels, and the float32
+# order in which the GPU sums c1 and c2 moves more of the roundings to T than in RMSNorm's dx. The
+# bit-exact bar for their dx is therefore the usual 99.9 %, lowered only where a CPU model of the
+# kernels' float32 summation order (tests/fp32_order.py) shows that order alone, on the case's own
+# inputs, leaves fewer elements bit-identical to the oracle: the bar is the model's rate minus
+# MODEL_MARGIN. On the test cases the model gives >= 99.95 % everywhere except the float16 rows of
+# 70000 elements with dy = 1 (98.97 %, the rate the GPU shows there).
+MODEL_MARGIN = 0.002
+
+
+def modeled_dx_floor(model_rate: float) -> float:
+    return min(DX_BITEXACT_FRAC, model_rate - MODEL_MARGIN)
 
 
 def check_floored(a_gpu, a_oracle, dtype: str, name: str, rows_axis=-1,
@@ -256,7 +264,10 @@ def check_ln_bwd(dx_gpu, dw_gpu, db_gpu, dy, x, w, mean_gpu, rstd_gpu, *, dtype)
         stats = {"dx_normwise": float(num / den) if den > 0 else float(num)}
         assert stats["dx_normwise"] <= F32_DX_NORMWISE, stats
     else:
-        stats = check_floored(dx_gpu, dx_o, dtype, "dx", frac=LN_DX_BITEXACT_FRAC)
+        from fp32_order import ln_dx_model_bitexact
+        model = ln_dx_model_bitexact(dy, x, w, mean_gpu, rstd_gpu, dtype=dtype)
+        stats = check_floored(dx_gpu, dx_o, dtype, "dx", frac=modeled_dx_floor(model))
+        stats["dx_model_bitexact"] = model
     stats.update(check_dw(dw_gpu, dw_o))
     if db_gpu is not None:
         s = check_dw(db_gpu, db_o)
@@ -292,8 +303,11 @@ def check_gn(y_gpu, mean_gpu, rstd_gpu, dx_gpu, dw_gpu, db_gpu, x, w, b, dy, *, 
         stats["dx_normwise"] = float(num / den) if den > 0 else float(num)
         assert stats["dx_normwise"] <= F32_DX_NORMWISE, stats
     else:
+        from fp32_order import gn_dx_model_bitexact
+        model = gn_dx_model_bitexact(dy, x, w, mg, rg, G=G, dtype=dtype)
         stats.update(check_floored(np.asarray(dx_gpu).reshape(B * G, -1), dx_o.reshape(B * G, -1),
-                                   dtype, "dx", frac=LN_DX_BITEXACT_FRAC))
+                                   dtype, "dx", frac=modeled_dx_floor(model)))
+        stats["dx_model_bitexact"] = model
     if dw_gpu is not None:
         stats.update(check_dw(dw_gpu, dw_o))
     if db_gpu is not None:

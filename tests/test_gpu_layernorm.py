@@ -69,6 +69,14 @@ def test_ln_parity(dtype, M, N, ld):
     run_ln(dtype, M, N, ld=ld)
 
 
+@pytest.mark.parametrize("dtype,M,N", [("bf16", 3333, 4096), ("bf16", 6200, 2048),
+                                     ("f16", 2049, 8192), ("bf16", 16500, 1024)])
+def test_ln_many_rows_per_block(dtype, M, N):
+    """Blocks of 7 to 9 steps of their row loop, the next step's rows loaded during the current
+    one, with a ragged last step."""
+    run_ln(dtype, M, N, seed=33)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("N", [1000, 4096, 16384])
 def test_ln_large_mean_rows(dtype, N):

@@ -101,6 +101,27 @@ def test_parity_autograd_casts(dtype, M, N, ld):
     run_case(dtype, M, N, rounding="twice", ld=ld, casts="autograd")
 
 
+# Many rows per backward block: each of the 256 blocks walks its rows in steps of one row group
+# (1024 threads: 8, 4, 2 or 1 rows of 1024, 2048, 4096 or 8192 columns), loading the next step's
+# rows while it computes the current one. These shapes give every block 7 to 9 steps, the last one
+# ragged (M is not a multiple of 256 row groups).
+MANY_STEPS = [(3333, 4096), (6200, 2048), (16500, 1024), (2049, 8192)]
+
+
+@pytest.mark.parametrize("M,N", MANY_STEPS)
+@pytest.mark.parametrize("mode", ["twice", "once", "autograd"])
+def test_parity_many_rows_per_block(M, N, mode):
+    if mode == "autograd":
+        run_case("bf16", M, N, rounding="twice", casts="autograd", seed=31)
+    else:
+        run_case("bf16", M, N, rounding=mode, offset=1.0 if mode == "once" else 0.0, seed=31)
+
+
+@pytest.mark.parametrize("M,N", [(3333, 4096), (2049, 8192)])
+def test_parity_many_rows_per_block_f16(M, N):
+    run_case("f16", M, N, rounding="twice", seed=32)
+
+
 @pytest.mark.parametrize("dtype,N", [("bf16", 1000), ("f16", 4096), ("bf16", 16384)])
 def test_autograd_casts_kernel_families_agree(dtype, N):
     results = {}
