@@ -75,18 +75,26 @@ __device__ __forceinline__ void combine_groups(float (&acc)[K], float* buf, int 
 }
 
 // Write a block's combined column accumulators as partial row b of the workspace (group 0 only).
+// Non-temporal (streaming cache policy) 16-byte stores: every block writes its row in the kernel's
+// last moments, with no input stream left to overlap, and the reduction launch that follows reads
+// them back sooner than rows written with the default policy (bf16 4096 x 4096, rows kernel then
+// reduction: LayerNorm's two partial rows 25.85 -> 25.24 us, RMSNorm's one 22.52 -> 22.38 us).
 template <int ITERS, int V>
 __device__ __forceinline__ void store_partial(const float (&acc)[ITERS * V], float* pr, int TPR,
                                               int tl, int N) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const BufRsrc r = buf_rsrc(pr);
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
     if (col + V <= N) {
 #pragma unroll
-      for (int q = 0; q < V; q += 4)
-        *reinterpret_cast<float4*>(pr + col + q) =
-            make_float4(acc[it * V + q], acc[it * V + q + 1], acc[it * V + q + 2],
-                        acc[it * V + q + 3]);
+      for (int q = 0; q < V; q += 4) {
+        const float4 v = make_float4(acc[it * V + q], acc[it * V + q + 1], acc[it * V + q + 2],
+                                     acc[it * V + q + 3]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r,
+                                               (uint32_t)(col + q) * 4u, 0, kBufNonTemporal);
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e)
