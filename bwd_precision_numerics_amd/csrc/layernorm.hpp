@@ -432,7 +432,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
 // KREG = 0: the block's dw (and db) partial rows accumulate in the workspace itself (each column
 // owned by one thread, rows added in order). KREG > 0 (16-byte vectors, at most KREG per thread):
 // the same sums in registers, written once at the end; bit-identical to KREG = 0.
-template <DT D, bool WIDE, bool HAS_DB, int KREG = 0>
+template <DT D, bool WIDE, bool HAS_DB, int KREG = 0, bool LACC = false>
 __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
   using IO = VecIO<D, WIDE>;
   using S = typename IO::S;
@@ -446,8 +446,13 @@ __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
   const int b = blockIdx.x, P = a.P;
   float* red = reinterpret_cast<float*>(smem);  // [2][wpr][2]
   const S* wr = static_cast<const S*>(a.w);
-  float* pw = a.part + (int64_t)b * a.ldp;
-  float* pb = a.part + (int64_t)(P + b) * a.ldp;
+  float* const gw = a.part + (int64_t)b * a.ldp;
+  float* const gb = a.part + (int64_t)(P + b) * a.ldp;
+  static_assert(!LACC || KREG == 0, "LDS sums replace the workspace sums");
+  // The row's dw and db sums: LDS (after the 64-float reduction area, ldp floats each) or the
+  // workspace rows themselves.
+  float* const pw = LACC ? reinterpret_cast<float*>(smem) + 64 : gw;
+  float* const pb = LACC ? reinterpret_cast<float*>(smem) + 64 + a.ldp : gb;
   constexpr int K = KREG > 0 ? KREG * V : 1;
   float accw[K], accb[HAS_DB ? K : 1];
 #pragma unroll
@@ -545,8 +550,20 @@ __global__ void __launch_bounds__(1024) ln_bwd_stream_kernel(LnBwdArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         if (col + e < N) {
-          pw[col + e] = accw[k * V + e];
-          if constexpr (HAS_DB) pb[col + e] = accb[k * V + e];
+          gw[col + e] = accw[k * V + e];
+          if constexpr (HAS_DB) gb[col + e] = accb[k * V + e];
+        }
+      }
+    }
+  } else if constexpr (LACC) {
+    // each thread copies the columns it summed: no barrier needed
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (col + e < N) {
+          gw[col + e] = pw[col + e];
+          if constexpr (HAS_DB) gb[col + e] = pb[col + e];
         }
       }
     }

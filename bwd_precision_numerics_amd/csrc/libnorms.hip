@@ -178,6 +178,13 @@ rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s)
     if (p.wide && ceil_div(ceil_div(a.N, Elem<D>::VEC), p.tpr) <= kLnStreamRegVectors)
       return launch(ln_bwd_stream_kernel<D, true, HAS_DB, kLnStreamRegVectors>, p.grid, block,
                     p.lds, s, a);
+    // Other rows keep the dw and db sums in LDS when both fit there (as the RMSNorm kernel).
+    if (2 * (int64_t)a.ldp <= kStreamLdsAccFloats) {
+      const size_t lds = 256 + 2 * sizeof(float) * (size_t)a.ldp;
+      return p.wide
+                 ? launch(ln_bwd_stream_kernel<D, true, HAS_DB, 0, true>, p.grid, block, lds, s, a)
+                 : launch(ln_bwd_stream_kernel<D, false, HAS_DB, 0, true>, p.grid, block, lds, s, a);
+    }
     return p.wide ? launch(ln_bwd_stream_kernel<D, true, HAS_DB>, p.grid, block, p.lds, s, a)
                   : launch(ln_bwd_stream_kernel<D, false, HAS_DB>, p.grid, block, p.lds, s, a);
   }
@@ -201,9 +208,9 @@ rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s)
              : tail == Tail::WHOLE ? RMSN_LNB_WPR(1, Tail::WHOLE)
                                    : RMSN_LNB(1, Tail::RAGGED, 0);
     case 2:
-      return tail == Tail::FULL    ? RMSN_LNB(2, Tail::FULL, 16)
-             : tail == Tail::WHOLE ? RMSN_LNB(2, Tail::WHOLE, 16)
-                                   : RMSN_LNB(2, Tail::RAGGED, 0);
+      // Exactly tiled rows take the WHOLE instantiation here: the FULL one spilled registers at two
+      // vectors a thread, and for these power-of-two widths dot / N and dot * (1 / N) agree.
+      return tail != Tail::RAGGED ? RMSN_LNB(2, Tail::WHOLE, 16) : RMSN_LNB(2, Tail::RAGGED, 0);
     default: return RMSNORM_ERR_UNSUPPORTED;
   }
 #undef RMSN_LNB_WPR

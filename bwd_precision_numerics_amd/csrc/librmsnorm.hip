@@ -27,7 +27,6 @@ constexpr int kBwdRegMaxIters = 2;      // backward register kernel (rows + pref
 constexpr int kBwdLdsMaxIters = 4;
 // Streaming backward with its dw sums in registers: up to 8 vectors per thread (8192 vectors a row
 // at 1024 threads, e.g. N = 65536 in 16-bit types).
-constexpr int kStreamRegVectors = 8;
 // Register backward pipeline: rows per barrier (batch) and batches in flight ahead of the current
 // one, and whether pass 2 reuses xhat and g*dy from pass 1. With the ring's loads issued as
 // straight-line code, one batch ahead measured fastest at every depth tried (bf16 4096 x 4096 rows
@@ -138,10 +137,22 @@ template <DT D, bool AG>
 rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if (p.variant == RMSNORM_VARIANT_STREAMING) {
-    // 16-byte rows of at most kStreamRegVectors vectors per thread keep their dw sums in registers.
+    // 16-byte rows of at most 8 vectors per thread keep their dw sums in registers. Up to 7 take
+    // the 7-vector instantiation (no spill); 8 take the 8-vector one, which spills 5 or 6 registers
+    // yet runs 2.5 times faster than sums kept in the workspace (bf16 4096 x 65536: 442 against
+    // 1116 us; at 7 vectors, 4096 x 57344, the 7-vector kernel takes 370 us, the 8-vector 389).
     const int64_t per_thread = ceil_div(ceil_div(a.N, Elem<D>::VEC), p.tpr);
-    if (p.wide && per_thread <= kStreamRegVectors)
-      return launch(bwd_stream_kernel<D, true, AG, kStreamRegVectors>, p.grid, block, p.lds, s, a);
+    if (p.wide && per_thread <= 7)
+      return launch(bwd_stream_kernel<D, true, AG, 7>, p.grid, block, p.lds, s, a);
+    if (p.wide && per_thread == 8)
+      return launch(bwd_stream_kernel<D, true, AG, 8>, p.grid, block, p.lds, s, a);
+    // Other rows (unaligned, or wider) keep the sums in LDS when the row fits there (bf16 4096 x
+    // 30001, rows not 16-byte aligned: 564 us with the sums in the workspace).
+    if (partial_ld(a.N) <= kStreamLdsAccFloats) {
+      const size_t lds = 128 + sizeof(float) * (size_t)partial_ld(a.N);
+      return p.wide ? launch(bwd_stream_kernel<D, true, AG, 0, true>, p.grid, block, lds, s, a)
+                    : launch(bwd_stream_kernel<D, false, AG, 0, true>, p.grid, block, lds, s, a);
+    }
     return p.wide ? launch(bwd_stream_kernel<D, true, AG>, p.grid, block, p.lds, s, a)
                   : launch(bwd_stream_kernel<D, false, AG>, p.grid, block, p.lds, s, a);
   }

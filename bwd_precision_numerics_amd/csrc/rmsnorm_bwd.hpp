@@ -188,9 +188,11 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
-    live[it] = TAIL == Tail::FULL || col < N;
+    // Only the last vector of a row can be absent or partial (ITERS = ceil(vectors / TPR)).
+    const bool last = it == ITERS - 1;
+    live[it] = TAIL == Tail::FULL || !last || col < N;
     // With N % V == 0 a lane's vector is whole or absent; said so, the element paths compile away.
-    whole[it] = TAIL == Tail::RAGGED ? col + V <= N : live[it];
+    whole[it] = TAIL == Tail::RAGGED && last ? col + V <= N : live[it];
     voff[it] = whole[it] ? (uint32_t)col * (uint32_t)sizeof(S) : 0u;
   }
 
@@ -367,8 +369,10 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
-    live[it] = TAIL == Tail::FULL || col < N;
-    whole[it] = TAIL == Tail::RAGGED ? col + V <= N : live[it];
+    // Only the last vector of a row can be absent or partial (ITERS = ceil(vectors / TPR)).
+    const bool last = it == ITERS - 1;
+    live[it] = TAIL == Tail::FULL || !last || col < N;
+    whole[it] = TAIL == Tail::RAGGED && last ? col + V <= N : live[it];
     voff[it] = whole[it] ? (uint32_t)col * (uint32_t)sizeof(S) : 0u;
   }
   float acc[ITERS * V];
@@ -499,13 +503,15 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
 }
 
 // Any N and any alignment. One row at a time per block (groups = 1); the elementwise pass reads
-// x and dy again (from the caches). KREG = 0: the block's dw partial row accumulates in the
-// workspace itself (each column is owned by one thread, rows are added in order). KREG > 0 (16-byte
-// vectors, at most KREG per thread: rows past the LDS-staged kernel's reach, up to 8192 vectors):
-// the same sums in registers, written once at the end — per row the workspace round trip would move
-// twice the row's float32 width (the kernel ran at 1.3 TB/s that way). Same operations in the same
-// order either way, so dx and dw are bit-identical between the two.
-template <DT D, bool WIDE, bool AG, int KREG = 0>
+// x and dy again (from the caches). KREG = 0: the block's dw partial row accumulates in LDS when
+// LACC (rows up to kStreamLdsAccFloats wide; each column is owned by one thread, rows are added in
+// order) and is written once at the end, else in the workspace itself. KREG > 0 (16-byte vectors,
+// at most KREG per thread: rows past the LDS-staged kernel's reach, up to 8192 vectors): the same
+// sums in registers — per row the workspace round trip would move twice the row's float32 width
+// (the kernel ran at 1.3 TB/s that way). Same operations in the same order every way, so dx and
+// dw are bit-identical between them.
+constexpr int kStreamLdsAccFloats = 36 * 1024;  // 144 KiB of LDS, after the 128-byte reduction area
+template <DT D, bool WIDE, bool AG, int KREG = 0, bool LACC = false>
 __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
   using IO = VecIO<D, WIDE>;
   using S = typename IO::S;
@@ -519,7 +525,10 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
   const int b = blockIdx.x, P = a.P;
   float* red = reinterpret_cast<float*>(smem);  // [2][wpr]
   const S* wr = static_cast<const S*>(a.w);
-  float* pr = a.part + (int64_t)b * a.ldp;
+  float* const pg = a.part + (int64_t)b * a.ldp;
+  static_assert(!LACC || KREG == 0, "LDS sums replace the workspace sums");
+  // The row's dw sums: LDS (after the 32-float reduction area) or the workspace row itself.
+  float* const pr = LACC ? reinterpret_cast<float*>(smem) + 32 : pg;
   constexpr int K = KREG > 0 ? KREG * V : 1;
   float acc[K];
 #pragma unroll
@@ -602,7 +611,15 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
       const int col = (tl + k * TPR) * V;
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        if (col + e < N) pr[col + e] = acc[k * V + e];
+        if (col + e < N) pg[col + e] = acc[k * V + e];
+    }
+  } else if constexpr (LACC) {
+    // each thread copies the columns it summed: no barrier needed
+    for (int v = tl; v < nv; v += TPR) {
+      const int col = v * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (col + e < N) pg[col + e] = pr[col + e];
     }
   }
 }

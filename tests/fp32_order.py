@@ -86,13 +86,15 @@ def ln_row_sums(gd, xh, V: int = 8):
     return out[0], out[1]
 
 
-def ln_dx_model_bitexact(dy, x, w, mean, rstd, *, dtype: str) -> float:
+def ln_dx_model_bitexact(dy, x, w, mean, rstd, *, dtype: str, wide: bool = True) -> float:
     """Fraction of dx elements that the LayerNorm kernels' float32 order of c1, c2 leaves
-    bit-identical to the oracle's dx (same mean and rstd, same elementwise steps)."""
+    bit-identical to the oracle's dx (same mean and rstd, same elementwise steps). ``wide``: rows
+    16-byte aligned (vectors of 16 bytes); else the element-wise kernel, whose threads hold single
+    elements (vectors of one, all in the even accumulator)."""
     x = np.asarray(x, np.float32)
     xh = normalize(x, mean, rstd, False).astype(np.float32)
     gd = (np.asarray(w, np.float32) * np.asarray(dy, np.float32)).astype(np.float32)
-    s1, s2 = ln_row_sums(gd, xh, 4 if dtype == "f32" else 8)
+    s1, s2 = ln_row_sums(gd, xh, (4 if dtype == "f32" else 8) if wide else 1)
     n = np.float32(x.shape[-1])
     c1 = (s1 / n).astype(np.float32)[:, None]
     c2 = (s2 / n).astype(np.float32)[:, None]

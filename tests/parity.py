@@ -256,7 +256,11 @@ def check_ln_fwd(y_gpu, mean_gpu, rstd_gpu, x, w, b, *, eps, dtype) -> dict:
     return stats
 
 
-def check_ln_bwd(dx_gpu, dw_gpu, db_gpu, dy, x, w, mean_gpu, rstd_gpu, *, dtype) -> dict:
+def check_ln_bwd(dx_gpu, dw_gpu, db_gpu, dy, x, w, mean_gpu, rstd_gpu, *, dtype,
+                 ld=None) -> dict:
+    """``ld``: the row stride of x, dy and dx on the device (default: contiguous rows). Rows that
+    are not 16-byte aligned take the element-wise kernels, whose summation order the dx model
+    then follows."""
     dx_o, dw_o, db_o = oracle.layernorm_bwd(dy, x, w, mean_gpu, rstd_gpu, dtype=dtype)
     if dtype == "f32":
         num = np.linalg.norm(dx_gpu.astype(np.float64) - dx_o)
@@ -265,7 +269,9 @@ def check_ln_bwd(dx_gpu, dw_gpu, db_gpu, dy, x, w, mean_gpu, rstd_gpu, *, dtype)
         assert stats["dx_normwise"] <= F32_DX_NORMWISE, stats
     else:
         from fp32_order import ln_dx_model_bitexact
-        model = ln_dx_model_bitexact(dy, x, w, mean_gpu, rstd_gpu, dtype=dtype)
+        itemsize = 4 if dtype == "f32" else 2
+        wide = ((ld or np.shape(x)[-1]) * itemsize) % 16 == 0
+        model = ln_dx_model_bitexact(dy, x, w, mean_gpu, rstd_gpu, dtype=dtype, wide=wide)
         stats = check_floored(dx_gpu, dx_o, dtype, "dx", frac=modeled_dx_floor(model))
         stats["dx_model_bitexact"] = model
     stats.update(check_dw(dw_gpu, dw_o))

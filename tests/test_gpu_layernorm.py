@@ -52,7 +52,7 @@ def run_ln(dtype, M, N, *, ld=None, variant="auto", seed=1, bias=True, x_dist=No
     yg, mg, rg, dxg, dwg = (to_np(t) for t in (y, mean, rstd, dx, dw))
     dbg = to_np(db) if bias else None
     st = check_ln_fwd(yg, mg, rg, x, w, b, eps=eps, dtype=dtype)
-    st.update(check_ln_bwd(dxg, dwg, dbg, dy, x, w, mg, rg, dtype=dtype))
+    st.update(check_ln_bwd(dxg, dwg, dbg, dy, x, w, mg, rg, dtype=dtype, ld=ld))
     return st, (yg, mg, rg, dxg, dwg, dbg)
 
 
@@ -60,6 +60,8 @@ SHAPES = [
     (1, 8, None), (5, 1, None), (7, 3, None), (33, 64, None), (300, 1000, None),
     (300, 1027, 1032), (129, 1027, None), (257, 3072, None), (64, 4096, None), (40, 8192, None),
     (24, 16384, None), (12, 32768, None), (3, 70000, None),
+    (40, 9001, None),   # rows not 16-byte aligned: element-wise, dw and db sums in LDS
+    (12, 30001, None),  # the same past the LDS sums' reach: sums in the workspace
 ]
 
 

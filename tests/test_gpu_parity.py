@@ -76,6 +76,8 @@ SHAPES = [
     (12, 32768, None),     # LDS-staged backward
     (6, 40000, None),      # streaming backward (beyond the LDS kernel's width)
     (3, 70000, None),      # streaming forward and backward
+    (40, 30001, None),     # wide rows not 16-byte aligned: element-wise, dw sums in LDS
+    (10, 40001, None),     # the same past the LDS sums' reach: dw sums in the workspace
 ]
 
 
@@ -202,11 +204,11 @@ def test_wide_rows_prefetch_pipeline(dtype, N):
     assert np.allclose(lds[3], to_np(dw), rtol=1e-5, atol=1e-6)
 
 
-@pytest.mark.parametrize("dtype,N", [("bf16", 40000), ("f16", 65536)])
+@pytest.mark.parametrize("dtype,N", [("bf16", 40000), ("bf16", 57344), ("f16", 65536)])
 def test_wide_rows_streaming_register_sums(dtype, N):
     """Rows past the LDS-staged kernel (more than 4096 vectors) take the streaming kernel with the
-    dw sums in registers (up to 8 vectors per thread) over each block's rows: 300 rows give 44
-    blocks two rows."""
+    dw sums in registers over each block's rows (7-vector instantiation up to 7 vectors a thread,
+    8-vector one at 8): 300 rows give 44 blocks two rows."""
     run_case(dtype, 300, N, seed=23)
 
 
