@@ -113,8 +113,14 @@ def parse_args(argv=None):
                     help="print per-kernel dispatch statistics (count, mean, median, min, max "
                          "in ns) of a rocprofv3 kernel-trace CSV and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="instead of the benchmark, copy a buffer of this many MiB --steps times "
-                         "(calibrates the HBM byte counters)")
+                    help="instead of the benchmark, run a reference kernel (--probe-kind, default "
+                         "copy) over streams of this many MiB --steps times (the copy calibrates "
+                         "the HBM byte counters)")
+    ap.add_argument("--probe-kind", choices=["read", "write", "copy", "sum2"], default="copy")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="print per-run, per-kernel means of the rocprofv3 --pmc CSVs under DIR "
+                         "(and HBM traffic scaled by the run named copy, whose buffer size "
+                         "--copy-probe-mib gives) and exit")
     return ap.parse_args(argv)
 
 
@@ -192,21 +198,70 @@ class Sets:
         self.dw_reduce(b)
 
 
-def copy_probe(torch, rn, mib, steps):
-    """The library's copy kernel over one buffer of `mib` MiB, `steps` times (the known-size
-    reference that calibrates the HBM byte counters)."""
+def copy_probe(torch, rn, mib, steps, kind="copy"):
+    """One of the library's reference kernels (default: copy) over streams of `mib` MiB, `steps`
+    times: the known-size reference that calibrates the HBM byte counters, and the ceiling kernels
+    for issue and occupancy counters."""
     nbytes = mib * 2**20
-    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
-    dst = torch.empty_like(src)
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.ones_like(a) if kind == "sum2" else None
+    c = torch.empty_like(a) if kind != "read" else torch.empty(
+        rn.library().rmsnorm_bandwidth_probe_out_bytes(nbytes) // 4 + 1, dtype=torch.float32,
+        device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
+    moved = {"read": 1, "write": 1, "copy": 2, "sum2": 3}[kind] * nbytes
     torch.cuda.synchronize()
     t = time.perf_counter()
     for _ in range(steps):
-        probe_call(rn, "copy", src.data_ptr(), None, dst.data_ptr(), nbytes, stream)
+        probe_call(rn, kind, None if kind == "write" else a.data_ptr(),
+                   None if b is None else b.data_ptr(), c.data_ptr(), nbytes, stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t
-    print(json.dumps({"copy_probe_bytes_per_launch": 2 * nbytes, "launches": steps,
-                      "GBps": 2 * nbytes * steps / dt / 1e9}), flush=True)
+    print(json.dumps({"probe": kind, "bytes_per_launch": moved, "launches": steps,
+                      "GBps": moved * steps / dt / 1e9}), flush=True)
+
+
+def summarize_counters(folder, copy_mib):
+    """Per (run, kernel, grid size) means of every counter in the rocprofv3 --pmc CSVs under
+    `folder` (one run per `<run>_counter_collection.csv`). With FETCH_SIZE and WRITE_SIZE present and a run
+    named `copy` (the library's copy kernel over one buffer of `copy_mib` MiB, --copy-probe-mib),
+    also the traffic in bytes: each counter scaled by the factor that maps its copy reading to the
+    copy's true bytes (one buffer read, one written)."""
+    import csv
+    import glob
+    vals = {}
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*_counter_collection.csv"),
+                                 recursive=True)):
+        run = os.path.basename(path)[:-len("_counter_collection.csv")]
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                # one kernel launched at several sizes is told apart by its grid size
+                kern = f'{r["Kernel_Name"]} [grid {r.get("Grid_Size", "?")}]'
+                key = (run, kern, r["Counter_Name"])
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    means = {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+    for (run, kern, ctr), (m, n) in sorted(means.items()):
+        print(json.dumps({"run": run, "kernel": kern, "counter": ctr, "dispatches": n,
+                          "mean": round(m, 3)}))
+    copies = {ctr: m for (run, kern, ctr), (m, n) in means.items()
+              if run == "copy" and "copy_kernel" in kern}
+    if "FETCH_SIZE" in copies and "WRITE_SIZE" in copies and copy_mib:
+        true = copy_mib * 2.0**20
+        fs = true / (copies["FETCH_SIZE"] * 1024.0)
+        ws = true / (copies["WRITE_SIZE"] * 1024.0)
+        print(json.dumps({"calibration": {"FETCH_SIZE_KiB": round(copies["FETCH_SIZE"], 1),
+                                          "WRITE_SIZE_KiB": round(copies["WRITE_SIZE"], 1),
+                                          "true_bytes": int(true), "fetch_scale": round(fs, 4),
+                                          "write_scale": round(ws, 4)}}))
+        for (run, kern, ctr), (m, n) in sorted(means.items()):
+            if ctr != "FETCH_SIZE" or run == "copy":
+                continue
+            w = means.get((run, kern, "WRITE_SIZE"))
+            if w is None:
+                continue
+            rb, wb = m * 1024.0 * fs, w[0] * 1024.0 * ws
+            print(json.dumps({"run": run, "kernel": kern, "read_bytes": round(rb),
+                              "write_bytes": round(wb), "traffic_bytes": round(rb + wb)}))
 
 
 def summarize_trace(path):
@@ -703,6 +758,9 @@ def main(argv=None) -> int:
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.copy_probe_mib)
+        return 0
 
     import torch
 
@@ -715,7 +773,7 @@ def main(argv=None) -> int:
     rn.library()  # fails loudly if the HIP library is missing
     torch.cuda.set_device(0)
     if args.copy_probe_mib:
-        copy_probe(torch, rn, args.copy_probe_mib, args.steps)
+        copy_probe(torch, rn, args.copy_probe_mib, args.steps, args.probe_kind)
         return 0
     if args.ceilings:
         ceilings(torch, rn, max(min(args.steps, 100), 20))

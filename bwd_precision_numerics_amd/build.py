@@ -6,7 +6,10 @@ The library is built from four translation units: ``librmsnorm.hip`` (the RMSNor
 ``libceiling.hip`` (the HBM bandwidth reference kernels of the measurement section of
 ``include/librmsnorm.h``).
 
-Usage: ``python -m bwd_precision_numerics_amd.build [--resource-usage FILE]``.
+Usage: ``python -m bwd_precision_numerics_amd.build [--resource-usage FILE [--summary]]``: with
+``--resource-usage`` the compiler's per-kernel resource remarks go to FILE, and ``--summary`` prints
+them as a table (one row per kernel instantiation: VGPRs, AGPRs, spilled VGPRs, scratch bytes per
+lane, occupancy in waves per SIMD, static LDS bytes).
 
 Flags:
 * ``--offload-arch=gfx950``: MI355X only.
@@ -88,12 +91,51 @@ def build(resource_usage: str | None = None, verbose: bool = False) -> str:
     return OUT
 
 
+def resource_table(diag: str) -> str:
+    """Markdown table of the kernel-resource-usage remarks in `diag` (names demangled with c++filt
+    when it is installed)."""
+    import re
+    rows, order = {}, []
+    cur = None
+    for line in diag.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            if cur not in rows:
+                order.append(cur)
+            rows[cur] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\w+)", line)
+        if m and cur:
+            rows[cur][m.group(1).strip()] = m.group(2)
+    names = order
+    if shutil.which("c++filt"):
+        out = subprocess.run(["c++filt"], input="\n".join(order), capture_output=True, text=True)
+        if out.returncode == 0:
+            names = out.stdout.splitlines()
+    lines = ["| kernel | VGPRs | AGPRs | VGPRs spilled | scratch B/lane | waves/SIMD | LDS B |",
+             "|---|---|---|---|---|---|---|"]
+    for mangled, name in sorted(zip(order, names), key=lambda p: p[1]):
+        r = rows[mangled]
+        lines.append(f"| `{name}` | {r.get('VGPRs', '?')} | {r.get('AGPRs', '?')} | "
+                     f"{r.get('VGPRs Spill', '?')} | {r.get('ScratchSize', '?')} | "
+                     f"{r.get('Occupancy', '?')} | {r.get('LDS Size', '?')} |")
+    return "\n".join(lines)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--resource-usage", help="write the compiler's per-kernel resource report here")
+    ap.add_argument("--summary", action="store_true",
+                    help="with --resource-usage: print the remarks as a table")
     ap.add_argument("-v", "--verbose", action="store_true")
     args = ap.parse_args()
-    print(build(args.resource_usage, args.verbose))
+    out = build(args.resource_usage, args.verbose)
+    if args.summary and args.resource_usage:
+        with open(args.resource_usage) as f:
+            print(resource_table(f.read()))
+    else:
+        print(out)
     return 0
 
 

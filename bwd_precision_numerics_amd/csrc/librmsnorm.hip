@@ -44,12 +44,11 @@ template <> struct BwdPipe<2> {
 };
 int bwd_batch(int iters) { return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB; }
 
-// Automatic selection prefers the register kernel, then the LDS-staged one. The one exception is
-// the 4-vector LDS-staged kernel on rows with a partial 16-byte vector (padded row strides), which
-// spills registers; it takes the streaming kernel. Measured (bf16, M = 4096, rows + dw reduction):
-// autograd casts at N = 16384, registers 79 us against 123 streaming; N = 30000 and 32760 (whole
-// vectors, idle lanes), LDS-staged 161 and 179 us against 209 and 228. The families give
-// bit-identical results, so the choice changes only speed.
+// Automatic selection prefers the register kernel, then the LDS-staged one, then the streaming
+// one. Measured (bf16, M = 4096, rows kernel): autograd casts at N = 16384, registers 79 us against
+// 123 streaming; whole-vector rows N = 30000, LDS-staged 159 us against 190; rows with a partial
+// last vector through a padded stride (N = 24577, 30001, 32767), LDS-staged 137, 171, 193 us
+// against 176, 235, 282. The families give bit-identical results, so the choice changes only speed.
 rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, bool ag,
                         rmsnorm_variant req, Plan* p) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
@@ -62,8 +61,7 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
     if (reg_ok)
       v = RMSNORM_VARIANT_REGISTERS;
     else if (lds_ok)
-      v = iters == 4 && N % vec_elems(dtype) != 0 ? RMSNORM_VARIANT_STREAMING
-                                                  : RMSNORM_VARIANT_LDS;
+      v = RMSNORM_VARIANT_LDS;
     else
       v = RMSNORM_VARIANT_STREAMING;
   }
