@@ -46,8 +46,11 @@ def run_ln(dtype, M, N, *, ld=None, variant="auto", seed=1, bias=True, x_dist=No
     bt = to_device(b, dtype, DEV) if bias else None
     print(f"ln case dtype={dtype} M={M} N={N} ld={ld} variant={variant} seed={seed} bias={bias} "
           f"x_dist={x_dist}", flush=True)
-    y, mean, rstd = rn.layernorm_fwd(xt, wt, bt, eps=eps, variant=variant)
-    dx, dw, db = rn.layernorm_bwd(dyt, xt, wt, mean, rstd, bias=bias, variant=variant)
+    # with a padded stride the outputs are padded too, so every operand keeps 16-byte rows
+    out = {} if ld is None else {"y": padded(np.zeros((M, N), np.float32), dtype, ld)}
+    y, mean, rstd = rn.layernorm_fwd(xt, wt, bt, eps=eps, variant=variant, **out)
+    out = {} if ld is None else {"dx": padded(np.zeros((M, N), np.float32), dtype, ld)}
+    dx, dw, db = rn.layernorm_bwd(dyt, xt, wt, mean, rstd, bias=bias, variant=variant, **out)
     torch.cuda.synchronize()
     yg, mg, rg, dxg, dwg = (to_np(t) for t in (y, mean, rstd, dx, dw))
     dbg = to_np(db) if bias else None

@@ -46,9 +46,12 @@ def run_case(dtype, M, N, rounding="twice", offset=0.0, eps=1e-6, ld=None, varia
     wt = to_device(w, dtype, DEV)
     print(f"case dtype={dtype} M={M} N={N} ld={ld} rounding={rounding} offset={offset} "
           f"variant={variant} seed={seed} casts={casts}", flush=True)
-    y, rstd = rn.fwd(xt, wt, eps=eps, offset=offset, rounding=rounding, variant=variant)
+    # with a padded stride the outputs are padded too, so every operand keeps 16-byte rows
+    out = {} if ld is None else {"y": padded(np.zeros((M, N), np.float32), dtype, ld)}
+    y, rstd = rn.fwd(xt, wt, eps=eps, offset=offset, rounding=rounding, variant=variant, **out)
+    out = {} if ld is None else {"dx": padded(np.zeros((M, N), np.float32), dtype, ld)}
     dx, dw = rn.bwd(dyt, xt, wt, rstd, eps=eps, offset=offset, rounding=rounding,
-                    variant=variant, casts=casts)
+                    variant=variant, casts=casts, **out)
     torch.cuda.synchronize()
     yg, rg, dxg, dwg = to_np(y), to_np(rstd), to_np(dx), to_np(dw)
     st = check_fwd(yg, rg, x, w, eps=eps, offset=offset, rounding=rounding, dtype=dtype)
@@ -76,6 +79,7 @@ SHAPES = [
     (12, 32768, None),     # LDS-staged backward
     (6, 40000, None),      # streaming backward (beyond the LDS kernel's width)
     (3, 70000, None),      # streaming forward and backward
+    (30, 30001, 30008),    # partial last vector through a padded stride, 4 vectors a thread: LDS-staged
     (40, 30001, None),     # wide rows not 16-byte aligned: element-wise, dw sums in LDS
     (10, 40001, None),     # the same past the LDS sums' reach: dw sums in the workspace
 ]
@@ -202,6 +206,22 @@ def test_wide_rows_prefetch_pipeline(dtype, N):
     for k, t in enumerate((y, r, dx)):
         assert same_bits(lds[k], to_np(t)).all(), k
     assert np.allclose(lds[3], to_np(dw), rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype,N,ld", [("bf16", 30001, 30008), ("f16", 24577, 24584),
+                                       ("bf16", 32767, 32768)])
+def test_ragged_wide_rows_lds_matches_streaming(dtype, N, ld):
+    """Rows with a partial last vector through a padded stride at 3-4 vectors a thread: AUTO takes
+    the LDS-staged backward (RAGGED layout); its dx and dw are bit-identical to the streaming
+    kernel's and match the oracle. 70 rows over 70 blocks."""
+    _, auto = run_case(dtype, 70, N, ld=ld, seed=24)
+    _, lds = run_case(dtype, 70, N, ld=ld, seed=24, variant="lds")
+    _, stream = run_case(dtype, 70, N, ld=ld, seed=24, variant="streaming")
+    for k in range(3):
+        assert same_bits(auto[k], lds[k]).all(), k
+        assert same_bits(lds[k], stream[k]).all(), k
+    assert same_bits(auto[3], lds[3]).all()
+    assert np.allclose(lds[3], stream[3], rtol=1e-5, atol=1e-6)
 
 
 @pytest.mark.parametrize("dtype,N", [("bf16", 40000), ("bf16", 57344), ("f16", 65536)])
