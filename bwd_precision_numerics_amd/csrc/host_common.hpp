@@ -70,6 +70,8 @@ rmsnorm_status lds_limit(int* out) {
 struct Plan {
   rmsnorm_variant variant;  // resolved (never AUTO)
   bool wide;                // 16-byte vectors
+  bool peel = false;        // streaming: rows not 16-byte aligned, whole vectors between an
+                            // element-wise head and tail
   int tpr, iters, groups;
   size_t lds;               // dynamic LDS bytes
   int64_t grid;
@@ -103,7 +105,7 @@ void bwd_shape(int64_t nv, int* tpr, int* iters) {
 }
 
 rmsnorm_status plan_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
-                        rmsnorm_variant req, Plan* p) {
+                        rmsnorm_variant req, Plan* p, bool peel_ok = false) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
   int tpr, iters;
   fwd_shape(nv_wide, &tpr, &iters);
@@ -115,7 +117,8 @@ rmsnorm_status plan_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   p->variant = v;
   if (v == RMSNORM_VARIANT_STREAMING) {
     p->wide = wide_ok;
-    const int64_t nv = wide_ok ? nv_wide : N;
+    p->peel = !wide_ok && peel_ok;
+    const int64_t nv = wide_ok || p->peel ? nv_wide : N;
     fwd_shape(nv, &tpr, &iters);
     iters = 0;
   } else {
@@ -169,6 +172,13 @@ rmsnorm_status check_matrix(const void* p, int64_t ld, int64_t M, int64_t N, int
 
 bool wide_fits(const void* p, int64_t ld, int eb) {
   return aligned(p, 16) && ((ld * eb) % 16 == 0);
+}
+
+// Row r of a matrix starts (base + r * ld * eb) bytes in; two matrices have every row at the same
+// offset from a 16-byte boundary when their bases and their row strides agree modulo 16 bytes.
+bool same_row_phase(const void* a, int64_t lda, const void* b, int64_t ldb, int eb) {
+  return ((uintptr_t)a & 15u) == ((uintptr_t)b & 15u) &&
+         (((uint64_t)lda * (uint64_t)eb) & 15u) == (((uint64_t)ldb * (uint64_t)eb) & 15u);
 }
 
 }  // namespace

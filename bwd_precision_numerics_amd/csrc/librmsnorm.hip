@@ -50,7 +50,7 @@ int bwd_batch(int iters) { return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB; 
 // last vector through a padded stride (N = 24577, 30001, 32767), LDS-staged 137, 171, 193 us
 // against 176, 235, 282. The families give bit-identical results, so the choice changes only speed.
 rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, bool ag,
-                        rmsnorm_variant req, Plan* p) {
+                        rmsnorm_variant req, Plan* p, bool peel_ok = false) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
   int tpr, iters;
   bwd_shape(nv_wide, &tpr, &iters);
@@ -71,12 +71,14 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   p->grid = num_partials(M);
   if (v == RMSNORM_VARIANT_STREAMING) {
     p->wide = wide_ok;
-    const int64_t nv = wide_ok ? nv_wide : N;
+    p->peel = !wide_ok && peel_ok;
+    const int64_t nv = wide_ok || p->peel ? nv_wide : N;
     bwd_shape(nv, &tpr, &iters);
     p->tpr = tpr;
     p->iters = 0;
     p->groups = 1;
     p->lds = round16(sizeof(float) * 2 * (tpr / 64));
+    if (p->peel) p->lds = 128 + sizeof(float) * (size_t)partial_ld(N);  // + the dw sums in LDS
     return RMSNORM_OK;
   }
   p->wide = true;
@@ -106,6 +108,7 @@ template <DT D, Out O>
 rmsnorm_status fwd_dispatch(const Plan& p, const FwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    if (p.peel) return launch(fwd_peel_kernel<D, O>, p.grid, block, p.lds, s, a);
     return p.wide ? launch(fwd_stream_kernel<D, true, O>, p.grid, block, p.lds, s, a)
                   : launch(fwd_stream_kernel<D, false, O>, p.grid, block, p.lds, s, a);
   }
@@ -135,6 +138,7 @@ template <DT D, bool AG>
 rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    if (p.peel) return launch(bwd_peel_kernel<D, AG>, p.grid, block, p.lds, s, a);
     // 16-byte rows of at most 8 vectors per thread keep their dw sums in registers. Up to 7 take
     // the 7-vector instantiation (no spill); 8 take the 8-vector one, which spills 5 or 6 registers
     // yet runs 2.5 times faster than sums kept in the workspace (bf16 4096 x 65536: 442 against
@@ -238,16 +242,21 @@ rmsnorm_status fwd_impl(const void* x, int64_t ldx, const void* w, void* y, int6
   if (!aligned(w, (uintptr_t)eb) || !aligned(rstd, 4)) return RMSNORM_ERR_MISALIGNED;
   const int yvec = vec_elems(dtype) * yb;  // output bytes per 16-byte input vector
   const bool wide = wide_fits(x, ldx, eb) && aligned(w, 16);
+  // Rows that are not 16-byte aligned (or a w that is not) move whole vectors between an
+  // element-wise head and tail when a row holds at least two vectors.
+  const bool peel_ok = N >= 2 * vec_elems(dtype);
   Plan p;
-  if ((st = plan_fwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  if ((st = plan_fwd(M, N, dtype, wide, variant, &p, peel_ok)) != RMSNORM_OK) return st;
   if (M == 0) return RMSNORM_OK;
 
   FwdArgs a;
   a.x = x; a.w = w; a.y = y; a.rstd = rstd;
   a.ldx = ldx; a.ldy = ldy; a.M = M; a.N = (int)N;
   a.tpr = p.tpr; a.groups = p.groups; a.eps = eps; a.offset = offset; a.scale = scale;
-  a.yvec = aligned(y, (uintptr_t)yvec) && (ldy * yb) % yvec == 0;
-  a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
+  a.yvec = p.peel ? !is_f8(out) && same_row_phase(x, ldx, y, ldy, eb)
+                  : aligned(y, (uintptr_t)yvec) && (ldy * yb) % yvec == 0;
+  a.comp = p.variant == RMSNORM_VARIANT_STREAMING &&
+           long_chain(N, dtype, p.wide || p.peel, p.tpr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (out) {
     case Out::ONCE: return fwd_by_dtype<Out::ONCE>(dtype, p, a, s);
@@ -300,9 +309,13 @@ rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_
   const int eb = elem_bytes(dtype);
   const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) && wide_fits(dx, lddx, eb) &&
                     aligned(w, 16);
+  // Otherwise x and dy rows at equal offsets from a 16-byte boundary move whole vectors between an
+  // element-wise head and tail, with the dw sums in LDS (rows up to kStreamLdsAccFloats wide).
+  const bool peel_ok = same_row_phase(x, ldx, dy, lddy, eb) && N >= 2 * vec_elems(dtype) &&
+                       partial_ld(N) <= kStreamLdsAccFloats;
   const bool ag = autograd_casts(rounding, dtype);
   Plan p;
-  if ((st = plan_bwd(M, N, dtype, wide, ag, variant, &p)) != RMSNORM_OK) return st;
+  if ((st = plan_bwd(M, N, dtype, wide, ag, variant, &p, peel_ok)) != RMSNORM_OK) return st;
   if (M == 0) return RMSNORM_OK;
 
   BwdArgs a;
@@ -311,7 +324,9 @@ rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_
   a.lddy = lddy; a.ldx = ldx; a.lddx = lddx; a.M = M;
   a.N = (int)N; a.ldp = (int)partial_ld(N); a.P = (int)num_partials(M);
   a.tpr = p.tpr; a.groups = p.groups; a.offset = offset;
-  a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
+  a.comp = p.variant == RMSNORM_VARIANT_STREAMING &&
+           long_chain(N, dtype, p.wide || p.peel, p.tpr);
+  a.dxvec = p.peel && same_row_phase(x, ldx, dx, lddx, eb);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case RMSNORM_DTYPE_F32:

@@ -48,6 +48,7 @@ struct BwdArgs {
   int groups;  // rows processed concurrently per block
   int comp;    // streaming kernel: compensated row sums (long per-thread chains)
   float offset;
+  int dxvec = 0;  // unaligned-row kernel: dx rows sit at x's offsets from a 16-byte boundary
 };
 
 // Fixed-order tree combine of per-group column accumulators into group 0. `buf` holds
@@ -622,6 +623,98 @@ __global__ void __launch_bounds__(1024) bwd_stream_kernel(BwdArgs a) {
         if (col + e < N) pg[col + e] = pr[col + e];
     }
   }
+}
+
+// Rows that are not 16-byte aligned whose x and dy rows sit at the same offset from a 16-byte
+// boundary (equal base offsets, equal row strides modulo 16 bytes: contiguous rows of an odd width,
+// say), as the forward's unaligned-row kernel: per row, h < V head and t < V tail elements one per
+// lane, whole 16-byte vectors between them, vector j after the boundary to thread j % TPR, h from
+// the row's address. One row per block at a time, two passes as the streaming kernel (the second
+// re-reads x and dy non-temporally; w as in the forward, peel_w). The thread that holds a column changes
+// from row to row, so the dw sums sit in LDS (N floats after the reduction area): each column gets
+// one addition per row, rows in the block's order, ordered by the barrier of the next row's
+// reduction; the block's partial row is written once at the end. dx takes vector stores when its
+// rows sit at x's offsets (dxvec), else element stores.
+template <DT D, bool AG>
+__global__ void __launch_bounds__(1024) bwd_peel_kernel(BwdArgs a) {
+  using IO = VecIO<D, true>;
+  using S = typename IO::S;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int tl = threadIdx.x;
+  const int b = blockIdx.x, P = a.P;
+  float* red = reinterpret_cast<float*>(smem);            // [2][wpr], at most 32 floats
+  float* const sums = reinterpret_cast<float*>(smem) + 32;  // dw sums [N]
+  const S* wr = static_cast<const S*>(a.w);
+  const bool walign = ((uintptr_t)wr & 15u) == 0;
+  const bool comp = a.comp != 0;
+  for (int c = tl; c < N; c += TPR) sums[c] = 0.f;
+
+  int s = 0;
+  for (int64_t row = b; row < a.M; row += P, ++s) {
+    const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
+    const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
+    S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
+    const float rs = a.rstd[row];
+    const int h = peel_head(xr, N);
+    const int nb = (N - h) / V;
+    const int t0 = h + nb * V;
+    RowAcc d;
+    auto first = [&](int col) {
+      const float xh = to_f32<D>(xr[col]) * rs;
+      const float gd = gain_dy<D, AG>(a.offset + to_f32<D>(wr[col]), to_f32<D>(dr[col]));
+      d.fma(0, gd, xh, comp);
+    };
+    if (tl < h) first(tl);
+    for (int j = tl; j < nb; j += TPR) {
+      const int col = h + j * V;
+      float xf[V], df[V], wf[V];
+      IO::unpack(IO::load(at(xr, col)), xf);
+      IO::unpack(IO::load(at(dr, col)), df);
+      peel_w<D, V>(wr, walign, N, h, col, wf);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float xh = xf[e] * rs;
+        const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
+        d.fma(e, gd, xh, comp);
+      }
+    }
+    if (tl < N - t0) first(t0 + tl);
+    const float dot = group_sum(d.total(), red + (s & 1) * wpr, wpr, tl);
+    const float c = dot / (float)N;
+    auto second = [&](int col) {
+      const float dyv = to_f32<D>(dr[col]);
+      const float xh = to_f32<D>(xr[col]) * rs;
+      const float gd = gain_dy<D, AG>(a.offset + to_f32<D>(wr[col]), dyv);
+      dxr[col] = from_f32<D>(rs * (gd - xh * c));
+      sums[col] = __builtin_fmaf(dyv, dw_factor<D, AG>(xh), sums[col]);
+    };
+    if (tl < h) second(tl);
+    for (int j = tl; j < nb; j += TPR) {
+      const int col = h + j * V;
+      float xf[V], df[V], wf[V], o[V];
+      // the row's last read of x and dy: non-temporal
+      IO::unpack(IO::load_nt(at(xr, col)), xf);
+      IO::unpack(IO::load_nt(at(dr, col)), df);
+      peel_w<D, V>(wr, walign, N, h, col, wf);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float xh = xf[e] * rs;
+        const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
+        o[e] = rs * (gd - xh * c);
+        sums[col + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), sums[col + e]);
+      }
+      const auto out = IO::pack(o);
+      if (a.dxvec) IO::store(at(dxr, col), out);
+      else IO::store_part(at(dxr, col), out, V);
+    }
+    if (tl < N - t0) second(t0 + tl);
+  }
+  lds_barrier();  // the last row's sums were added by other threads
+  float* const pg = a.part + (int64_t)b * a.ldp;
+  for (int c = tl; c < N; c += TPR) pg[c] = sums[c];
 }
 
 // dw_j = sum over p of part[p, j] in a fixed order, spread over many compute units: a block of

@@ -229,6 +229,73 @@ __device__ __forceinline__ T* at(T* row, int col) {
   return reinterpret_cast<T*>(reinterpret_cast<B*>(row) + (uint32_t)col * (uint32_t)sizeof(T));
 }
 
+// Elements of a row before its first 16-byte boundary (at most V - 1, at most N): the head a
+// kernel for rows that are not 16-byte aligned moves element by element before whole vectors.
+template <typename S>
+__device__ __forceinline__ int peel_head(const S* row, int N) {
+  const int h = (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / (uint32_t)sizeof(S));
+  return h < N ? h : N;
+}
+
+// The 16-byte vector of a row's elements [c, c + V) for c = 16-byte column + h (0 < h < V), from
+// the aligned vectors A = [c - h, c - h + V) and B = [c - h + V, c - h + 2V): a funnel shift by h
+// elements (H a compile-time constant; peel_vec dispatches on the block-uniform h).
+template <DT D, int H>
+__device__ __forceinline__ uint4 funnel_vec(uint4 A, uint4 B) {
+  const uint32_t c[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+  if constexpr (D == DT::F32) {
+    return make_uint4(c[H], c[H + 1], c[H + 2], c[H + 3]);
+  } else {
+    constexpr int m = H / 2;
+    if constexpr (H % 2 == 0) {
+      return make_uint4(c[m], c[m + 1], c[m + 2], c[m + 3]);
+    } else {  // odd element shift: the high half of dword k and the low half of dword k + 1
+      return make_uint4(__builtin_amdgcn_alignbyte(c[m + 1], c[m], 2),
+                        __builtin_amdgcn_alignbyte(c[m + 2], c[m + 1], 2),
+                        __builtin_amdgcn_alignbyte(c[m + 3], c[m + 2], 2),
+                        __builtin_amdgcn_alignbyte(c[m + 4], c[m + 3], 2));
+    }
+  }
+}
+template <DT D>
+__device__ __forceinline__ uint4 peel_vec(int h, uint4 A, uint4 B) {
+  switch (h) {
+    case 1: return funnel_vec<D, 1>(A, B);
+    case 2: return funnel_vec<D, 2>(A, B);
+    case 3: return funnel_vec<D, 3>(A, B);
+    default: break;
+  }
+  if constexpr (D != DT::F32) {
+    switch (h) {
+      case 4: return funnel_vec<D, 4>(A, B);
+      case 5: return funnel_vec<D, 5>(A, B);
+      case 6: return funnel_vec<D, 6>(A, B);
+      case 7: return funnel_vec<D, 7>(A, B);
+      default: break;
+    }
+  }
+  return A;  // h = 0
+}
+
+// The gain elements [col, col + V) of a peeled row's vector (col = h + j * V, h the row's head):
+// one aligned vector when h = 0; two and a funnel shift when w is 16-byte aligned and the second
+// vector lies inside w; else element by element (w misaligned, or the row's last vectors).
+template <DT D, int V>
+__device__ __forceinline__ void peel_w(const typename Elem<D>::S* wr, bool walign, int N, int h,
+                                       int col, float (&wf)[V]) {
+  using IO = VecIO<D, true>;
+  static_assert(V == IO::V, "16-byte vectors");
+  const int base = col - h;  // a multiple of V: w + base is 16-byte aligned when w is
+  if (walign && (h == 0 || base + 2 * V <= N)) {
+    const uint4 A = IO::load(at(wr, base));
+    const uint4 B = h ? IO::load(at(wr, base + V)) : A;
+    IO::unpack(peel_vec<D>(h, A, B), wf);
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) wf[e] = to_f32<D>(wr[col + e]);
+  }
+}
+
 // ---- reductions ----------------------------------------------------------------------------------
 // Sum over the 64 lanes of a wave with DPP lane moves (register-to-register, no LDS round trip):
 // pairs and quads (quad_perm), then rows of 16 (row_shr 4 and 8), then rows 0+1 and 2+3

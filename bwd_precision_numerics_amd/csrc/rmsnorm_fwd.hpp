@@ -224,4 +224,77 @@ __global__ void __launch_bounds__(1024) fwd_stream_kernel(FwdArgs a) {
   }
 }
 
+// Rows that are not 16-byte aligned (contiguous rows of an odd width, say). A row's first h < V
+// elements, up to its first 16-byte boundary, and its last t < V elements go one per lane (lanes
+// 0 .. h-1 and 0 .. t-1); the rest moves as whole 16-byte vectors, vector j after the boundary to
+// thread j % TPR. h comes from each row's own address, so the thread that holds a column changes
+// from row to row. Each thread adds its head element, its vectors in order (even / odd
+// accumulators) and its tail element, then the wave and row reductions; compensated sums on long
+// chains as the streaming kernel. y takes vector stores when its rows sit at x's offsets from a
+// 16-byte boundary (yvec), else element stores. w's columns for a vector are, in most rows, not
+// 16-byte aligned: two aligned vectors and a funnel shift by h elements (peel_w).
+template <DT D, Out O>
+__global__ void __launch_bounds__(1024) fwd_peel_kernel(FwdArgs a) {
+  using IO = VecIO<D, true>;
+  using S = typename IO::S;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPR;
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.groups + grp;
+  const bool valid = row < a.M;
+  float* red = reinterpret_cast<float*>(smem) + grp * wpr;
+
+  const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+  const S* wr = static_cast<const S*>(a.w);
+  const bool walign = ((uintptr_t)wr & 15u) == 0;
+  const int h = peel_head(xr, N);
+  const int nb = (N - h) / V;
+  const int t0 = h + nb * V;  // first element of the tail
+  const bool comp = a.comp != 0;
+  RowAcc acc;
+  if (valid) {
+    if (tl < h) {
+      const float f = to_f32<D>(xr[tl]);
+      acc.fma(0, f, f, comp);
+    }
+    for (int j = tl; j < nb; j += TPR) {
+      float f[V];
+      IO::unpack(IO::load(at(xr, h + j * V)), f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc.fma(e, f[e], f[e], comp);
+    }
+    if (tl < N - t0) {
+      const float f = to_f32<D>(xr[t0 + tl]);
+      acc.fma(0, f, f, comp);
+    }
+  }
+  const float ss = group_sum(acc.total(), red, wpr, tl);
+  const float rs = 1.0f / __builtin_sqrtf(ss / (float)N + a.eps);
+  if (!valid) return;
+  if (tl == 0 && a.rstd) a.rstd[row] = rs;
+
+  void* yr = out_row<D, O>(a.y, row, a.ldy);
+  auto one = [&](int col) {
+    const float xf[1] = {to_f32<D>(xr[col])}, wf[1] = {to_f32<D>(wr[col])};
+    float yf[1];
+    apply_gain<D, O, 1>(xf, wf, rs, a.offset, a.scale, yf);
+    store_out<D, O, false, 1>(yr, col, 1, false, yf);
+  };
+  if (tl < h) one(tl);
+  for (int j = tl; j < nb; j += TPR) {
+    const int col = h + j * V;
+    float xf[V], wf[V], yf[V];
+    // the row's last read of x: non-temporal
+    IO::unpack(IO::load_nt(at(xr, col)), xf);
+    peel_w<D, V>(wr, walign, N, h, col, wf);
+    apply_gain<D, O, V>(xf, wf, rs, a.offset, a.scale, yf);
+    store_out<D, O, true, V>(yr, col, V, a.yvec != 0, yf);
+  }
+  if (tl < N - t0) one(t0 + tl);
+}
+
 }  // namespace rmsn

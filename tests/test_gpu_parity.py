@@ -70,7 +70,7 @@ SHAPES = [
     (33, 64, None),
     (300, 1000, None),     # 125 vectors per row; 300 rows over 256 backward blocks
     (300, 1027, 1032),     # partial last vector through a padded row stride
-    (129, 1027, None),     # rows not 16-byte aligned: element-wise path
+    (129, 1027, None),     # rows not 16-byte aligned: vectors between an element-wise head and tail
     (257, 3072, None),
     (64, 4096, None),
     (40, 8192, None),
@@ -80,8 +80,8 @@ SHAPES = [
     (6, 40000, None),      # streaming backward (beyond the LDS kernel's width)
     (3, 70000, None),      # streaming forward and backward
     (30, 30001, 30008),    # partial last vector through a padded stride, 4 vectors a thread: LDS-staged
-    (40, 30001, None),     # wide rows not 16-byte aligned: element-wise, dw sums in LDS
-    (10, 40001, None),     # the same past the LDS sums' reach: dw sums in the workspace
+    (40, 30001, None),     # wide rows not 16-byte aligned: head/tail peeled, dw sums in LDS
+    (10, 40001, None),     # past the LDS sums' reach: element-wise, dw sums in the workspace
 ]
 
 
@@ -230,6 +230,61 @@ def test_wide_rows_streaming_register_sums(dtype, N):
     dw sums in registers over each block's rows (7-vector instantiation up to 7 vectors a thread,
     8-vector one at 8): 300 rows give 44 blocks two rows."""
     run_case(dtype, 300, N, seed=23)
+
+
+def strided(a: np.ndarray, dtype: str, ld: int, off: int):
+    """Device [M, N] view at column offset `off` of a [M, ld] buffer (its base `off` elements past
+    the buffer's, so its rows start off a 16-byte boundary unless off is a multiple of one)."""
+    M, N = a.shape
+    buf = np.zeros((M, ld), np.float32)
+    buf[:, off:off + N] = a
+    return to_device(buf, dtype, DEV)[:, off:off + N]
+
+
+# Layouts of x, dy and dx (and y) for rows that are not 16-byte aligned: (ld, column offset) per
+# operand, None for contiguous. Same phase everywhere: every row's head and tail peeled, vectors
+# between; an offset base with an aligned stride: the same head in every row; dx (y) at another
+# phase: element stores; dy at another phase than x: the element-wise kernels.
+UNALIGNED_LAYOUTS = {
+    "contiguous": (None, None, None),
+    "w_offset": (None, None, None),  # and w one element past a 16-byte boundary
+    "offset_base": ((1040, 3), (1040, 3), (1040, 3)),
+    "dx_other_phase": (None, None, (1032, 0)),
+    "dy_other_phase": (None, (1032, 0), None),
+}
+
+
+@pytest.mark.parametrize("layout", list(UNALIGNED_LAYOUTS))
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_unaligned_row_layouts(dtype, layout):
+    M, N = 257, 1027
+    lx, ldy, ldx_ = UNALIGNED_LAYOUTS[layout]
+    wl = WL[dtype].with_(rounding="twice")
+    inp = make_inputs(wl, M=M, N=N, seed=41)
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    place = lambda a, l: to_device(a, dtype, DEV) if l is None else strided(a, dtype, *l)
+    xt, dyt = place(x, lx), place(dy, ldy)
+    yt = place(np.zeros((M, N), np.float32), ldx_)
+    dxt = place(np.zeros((M, N), np.float32), ldx_)
+    if layout == "w_offset":
+        wbuf = to_device(np.concatenate([np.zeros(1, np.float32), w]), dtype, DEV)
+        wt = wbuf[1:]
+    else:
+        wt = to_device(w, dtype, DEV)
+    print(f"case unaligned dtype={dtype} layout={layout}", flush=True)
+    y, rstd = rn.fwd(xt, wt, y=yt)
+    dx, dw = rn.bwd(dyt, xt, wt, rstd, dx=dxt)
+    torch.cuda.synchronize()
+    rg = to_np(rstd)
+    check_fwd(to_np(y), rg, x, w, eps=1e-6, offset=0.0, rounding="twice", dtype=dtype)
+    check_dx(to_np(dx), dy, x, w, rg, offset=0.0, dtype=dtype)
+    check_dw(to_np(dw), oracle.rmsnorm_dw(dy, x, rg, dtype=dtype))
+    # nothing outside the rows was written
+    if ldx_ is not None:
+        full = dxt.as_strided((M, ldx_[0]), (ldx_[0], 1), dxt.storage_offset() - ldx_[1])
+        rest = to_np(full).copy()
+        rest[:, ldx_[1]:ldx_[1] + N] = 0
+        assert not rest.any()
 
 
 def test_forward_register_and_lds_staging_at_wide_rows():
