@@ -243,9 +243,20 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
         }
       }
     } else {
+      // Only a row's last vector can be partial or absent (ITERS = ceil(vectors / TPR)): the
+      // other iterations take the whole-vector code.
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
         const int col = (it * TPR + tl) * V;
+        if (it < ITERS - 1) {
+          IO::unpack(IO::load(xr + col, V), ev[it]);
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            mx = fmax(mx, ev[it][e]);
+            if constexpr (F32) nmn = fmax(nmn, -ev[it][e]);
+          }
+          continue;
+        }
         A f[V];
         if (col < N) IO::unpack(IO::load(xr + col, N - col), f);
 #pragma unroll
@@ -291,7 +302,7 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         A t = ex(Flag<true>{}, ev[it][e] - mx);
-        if constexpr (!FULL) t = col + e < N ? t : (A)0;
+        if (!FULL && it == R - 1) t = col + e < N ? t : (A)0;
         ev[it][e] = t;
         if (e & 1) s1 += t;
         else s0 += t;
@@ -321,11 +332,12 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
 #pragma unroll
     for (int it = 0; it < R; ++it) {
       const int col = (it * TPR + tl) * V;
-      if (!FULL && col >= N) continue;
+      const bool last = !FULL && it == R - 1;
+      if (last && col >= N) continue;
       A o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = ev[it][e] * r;
-      IO::store(yr + col, o, FULL ? V : N - col);
+      IO::store(yr + col, o, last ? N - col : V);
     }
   } else {
     auto store_pass = [&](auto fast_tag) {

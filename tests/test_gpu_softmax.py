@@ -53,13 +53,28 @@ def run_sm(dtype, M, N, variant="auto", seed=1, x=None, ld=None):
 
 
 SHAPES = [(1, 1), (3, 7), (33, 64), (300, 1000), (129, 1027), (257, 3072), (64, 4096),
-          (40, 8192), (12, 16384), (5, 32768), (3, 70000)]
+          (40, 8192), (12, 16384), (5, 32768), (6, 40000), (4, 50264), (3, 70000)]
 
 
 @pytest.mark.parametrize("M,N", SHAPES)
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32", "f64"])
 def test_softmax_parity(dtype, M, N):
     run_sm(dtype, M, N)
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 40000), ("f16", 50264), ("bf16", 65000)])
+def test_softmax_forward_families_agree_on_wide_rows(dtype, N):
+    """Forward rows of 5 to 8 vectors a thread that the vectors do not tile: the register kernel
+    (partial vector in the last iteration only) and the streaming kernel give the same bits."""
+    wl = WL[dtype]
+    x = make_inputs(wl, M=9, N=N, seed=8)["x"]
+    xt = to_device(x, dtype, DEV)
+    print(f"softmax fwd families dtype={dtype} N={N}", flush=True)
+    a = rn.softmax_fwd(xt, variant="registers")
+    b = rn.softmax_fwd(xt, variant="streaming")
+    torch.cuda.synchronize()
+    check_softmax_fwd(arr(a), x, dtype=dtype)
+    assert same_bits(arr(a), arr(b)).all()
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
