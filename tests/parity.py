@@ -15,7 +15,7 @@ Tolerances (the comparison contract):
 * y, float32 I/O: conditioned bit-exact; unconditioned elementwise relative error <= 2^-20.
 * dx, 16-bit I/O (oracle run from the GPU's rstd): >= 99.9 % bit-identical and every element within
   1 ulp of T, the ulp taken at max(|dx_oracle|, 2^-12 * rms of the oracle's dx row) so that
-  elements produced by cancellation are judged at the scale of their row.
+  elements produced by cancellation are measured at the scale of their row.
 * dx, float32 I/O: normwise relative error <= 1e-5.
 * dw (float32): normwise relative error <= 1e-4.
 """
@@ -215,7 +215,7 @@ def check_floored(a_gpu, a_oracle, dtype: str, name: str, rows_axis=-1,
                   frac: float = DX_BITEXACT_FRAC, cond=None) -> dict:
     """>= ``frac`` bit-identical and every element within 1 ulp of T, the ulp taken at
     max(|oracle|, 2^-12 * rms of the oracle's row) so that values produced by cancellation are
-    judged at the scale of their row; float32: within 2^-20 of max(|oracle|, rms of the row),
+    measured at the scale of their row; float32: within 2^-20 of max(|oracle|, rms of the row),
     times the row's condition number ``cond`` where given."""
     a_gpu = np.asarray(a_gpu, np.float32)
     a_oracle = np.asarray(a_oracle, np.float32)
@@ -224,7 +224,7 @@ def check_floored(a_gpu, a_oracle, dtype: str, name: str, rows_axis=-1,
     rms = np.sqrt(np.mean(a_oracle.astype(np.float64) ** 2, axis=rows_axis, keepdims=True))
     floor = DX_FLOOR * rms
     if dtype == "f32":
-        # float32 output: errors inherited from the statistics scale with the row, so judge them
+        # float32 output: errors inherited from the statistics scale with the row, so measure them
         # at max(|oracle|, rms of the row)
         ref = np.maximum(np.abs(a_oracle.astype(np.float64)), rms)
         if cond is not None:
