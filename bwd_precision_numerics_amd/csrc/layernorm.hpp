@@ -249,6 +249,33 @@ struct LnBwdArgs {
   int comp;    // streaming kernel: compensated row sums (long per-thread chains)
 };
 
+// combine_groups' first level split in two around a barrier the caller already has (the one of
+// the last row's sums), so that the block's column sums leave before the last row's dx is
+// written: combine_give (before that barrier) has the upper floor(groups / 2) groups hand their
+// sums over, combine_take (after it) adds them into the groups below, and combine_groups with
+// groups - floor(groups / 2) completes the same tree. `buf` as for combine_groups, apart from the
+// values of the barrier's own round.
+template <int K>
+__device__ __forceinline__ void combine_give(const float (&acc)[K], float* buf, int groups,
+                                             int grp, int tl, int slice_threads) {
+  const int h = groups >> 1;
+  if (grp >= groups - h) {
+    float* dst = buf + ((size_t)(grp - (groups - h)) * slice_threads + tl) * K;
+#pragma unroll
+    for (int k = 0; k < K; ++k) dst[k] = acc[k];
+  }
+}
+template <int K>
+__device__ __forceinline__ void combine_take(float (&acc)[K], const float* buf, int groups,
+                                             int grp, int tl, int slice_threads) {
+  const int h = groups >> 1;
+  if (grp >= groups - 2 * h && grp < groups - h) {
+    const float* src = buf + ((size_t)(grp - (groups - 2 * h)) * slice_threads + tl) * K;
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc[k] += src[k];
+  }
+}
+
 // Register kernel on the persistent grid of the RMSNorm backward (block b owns rows b, b + P, ...).
 // A ring of DEPTH + 1 rows of raw (x, dy) and their (mean, rstd) per row group keeps DEPTH rows in
 // flight while one is reduced and written. HAS_DB adds the bias-gradient accumulators. KEEP holds
@@ -264,6 +291,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   constexpr int V = IO::V;
   constexpr int RING = DEPTH + 1;
   constexpr int K = ITERS * V;
+  constexpr bool EARLY = ITERS == 1;  // partial rows written in the last step
   extern __shared__ uint4 smem[];
 
   const int TPR = WPR ? 64 * WPR : a.tpr, wpr = WPR ? WPR : TPR >> 6;
@@ -275,6 +303,10 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   const int64_t nloc = block_rows(a.M, P, b);
   const int nsteps = (int)((nloc + G - 1) / G);
   float* red = reinterpret_cast<float*>(smem);  // [2][G][wpr][2]
+  // The cross-group combine's slices past the row sums (dw sums, then db sums): the last step
+  // hands its column sums over in the barrier of its own row sums.
+  float* cbw = red + ((4 * G * wpr + 3) & ~3);
+  float* cbb = cbw + (size_t)(G >> 1) * TPR * K;
 
   const S* wr = static_cast<const S*>(a.w);
   bool whole[ITERS], live[ITERS];
@@ -384,7 +416,51 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
           }
         }
         float dots[2] = {d1a + d1b, d2a + d2b};
+        // After the last step's first pass the column sums are final: the first level of the
+        // cross-group combine rides on this step's barrier and, with two groups or fewer, the
+        // partial rows are written before the last row's dx. With two groups and a bias, group 1
+        // hands over its dw sums and group 0 its db sums, so each group adds one pair (in either
+        // order the same float32 sum) and writes one partial row.
+        // (One vector a thread only: at two the extra live sums would spill registers.)
+        const bool last = EARLY && s == nsteps - 1;  // block-uniform
+        const bool swap = HAS_DB && G == 2;
+        if (last) {
+          if (swap) {
+            if (grp == 1) {
+#pragma unroll
+              for (int k = 0; k < K; ++k) cbw[tl * K + k] = accw[k];
+            } else if constexpr (HAS_DB) {
+#pragma unroll
+              for (int k = 0; k < K; ++k) cbb[tl * K + k] = accb[k];
+            }
+          } else {
+            combine_give<K>(accw, cbw, G, grp, tl, TPR);
+            if constexpr (HAS_DB) combine_give<K>(accb, cbb, G, grp, tl, TPR);
+          }
+        }
         group_sum_batch<2, WPR>(dots, red + ((s & 1) * G + grp) * wpr * 2, wpr, tl);
+        if (last) {
+          if (!(WPR > 1 || (WPR == 0 && wpr > 1))) lds_barrier();  // one-wave rows: no barrier yet
+          if (swap) {
+            if (grp == 0) {
+#pragma unroll
+              for (int k = 0; k < K; ++k) accw[k] += cbw[tl * K + k];
+              store_partial<ITERS, V>(accw, a.part + (int64_t)b * a.ldp, TPR, tl, N);
+            } else if constexpr (HAS_DB) {
+#pragma unroll
+              for (int k = 0; k < K; ++k) accb[k] += cbb[tl * K + k];
+              store_partial<ITERS, V>(accb, a.part + (int64_t)(P + b) * a.ldp, TPR, tl, N);
+            }
+          } else {
+            combine_take<K>(accw, cbw, G, grp, tl, TPR);
+            if constexpr (HAS_DB) combine_take<K>(accb, cbb, G, grp, tl, TPR);
+            if (G - (G >> 1) == 1 && grp == 0) {
+              store_partial<ITERS, V>(accw, a.part + (int64_t)b * a.ldp, TPR, tl, N);
+              if constexpr (HAS_DB)
+                store_partial<ITERS, V>(accb, a.part + (int64_t)(P + b) * a.ldp, TPR, tl, N);
+            }
+          }
+        }
         if (valid) {
           const int64_t row = b + li * P;
           const float c1 = TAIL == Tail::FULL ? dots[0] * inv_n : dots[0] / (float)N;
@@ -419,12 +495,17 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
     }
   }
 
-  float* cbuf = reinterpret_cast<float*>(smem);
-  combine_groups<K>(accw, cbuf, G, grp, tl, TPR);
-  if (grp == 0) store_partial<ITERS, V>(accw, a.part + (int64_t)b * a.ldp, TPR, tl, N);
-  if constexpr (HAS_DB) {
-    combine_groups<K>(accb, cbuf, G, grp, tl, TPR);
-    if (grp == 0) store_partial<ITERS, V>(accb, a.part + (int64_t)(P + b) * a.ldp, TPR, tl, N);
+  // Without the early first level (no rows, or two vectors a thread) the whole tree runs here;
+  // with it and more than two groups, the tree's other levels.
+  const bool early = EARLY && nsteps > 0;
+  const int rest = early ? G - (G >> 1) : G;
+  if (rest > 1 || !early) {
+    combine_groups<K>(accw, cbw, rest, grp, tl, TPR);
+    if (grp == 0) store_partial<ITERS, V>(accw, a.part + (int64_t)b * a.ldp, TPR, tl, N);
+    if constexpr (HAS_DB) {
+      combine_groups<K>(accb, cbb, rest, grp, tl, TPR);
+      if (grp == 0) store_partial<ITERS, V>(accb, a.part + (int64_t)(P + b) * a.ldp, TPR, tl, N);
+    }
   }
 }
 

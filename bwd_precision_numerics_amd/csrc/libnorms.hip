@@ -164,9 +164,11 @@ rmsnorm_status plan_ln_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_
   p->iters = iters;
   p->groups = kLnBwdBlockThreads / tpr;
   const size_t red_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * (tpr / 64) * 2);
+  // The combine's slices for the dw and the db sums sit past the row sums (the last step fills
+  // them while its row sums are in use).
   const size_t combine_bytes =
       sizeof(float) * (size_t)(p->groups / 2) * tpr * iters * vec_elems(dtype);
-  p->lds = red_bytes > combine_bytes ? red_bytes : combine_bytes;
+  p->lds = red_bytes + 2 * combine_bytes;
   return RMSNORM_OK;
 }
 
