@@ -34,9 +34,14 @@ void sm_shape(int64_t nv, int max_iters, int* tpr, int* iters) {
 
 // Shape of a forward or backward row. Both kernel families of one direction take the same shape
 // for the same N and dtype, so with 16-byte vectors they map elements to threads identically.
-rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
+// peel: rows not 16-byte aligned, every matrix's rows at one offset from a 16-byte boundary; the
+// kernels take 16-byte vectors between a head and a tail of single elements, and the mapping is
+// sized for floor(N / V) vectors (the most a row holds).
+rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, bool peel,
                        rmsnorm_variant req, size_t acc_bytes, int slots, bool fwd, Plan* p) {
-  const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
+  const int64_t nv_wide = peel ? N / vec_elems(dtype) : ceil_div(N, vec_elems(dtype));
+  wide_ok = wide_ok || peel;
+  p->peel = peel;
   int tpr, iters, max_iters = kSmMaxIters;
   if (fwd) max_iters = kSmFwdFullMaxIters;
   sm_shape(nv_wide, max_iters, &tpr, &iters);
@@ -61,12 +66,43 @@ rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   return RMSNORM_OK;
 }
 
+// 16-byte-vector kernels: streaming (iters 0) or registers, whole rows or peeled (PEEL).
+template <DT D, bool FWD, bool PEEL>
+rmsnorm_status sm_dispatch_iters(const Plan& p, const SmArgs& a, hipStream_t s) {
+  const int block = p.groups * p.tpr;
+#define RMSN_SM(IT)                                                                                \
+  (FWD ? launch(softmax_fwd_kernel<D, true, IT, false, PEEL>, p.grid, block, p.lds, s, a)          \
+       : launch(softmax_bwd_kernel<D, true, IT, PEEL>, p.grid, block, p.lds, s, a))
+  const int iters = p.variant == RMSNORM_VARIANT_STREAMING ? 0 : p.iters;
+  switch (iters) {
+    case 0: return RMSN_SM(0);
+    case 1: return RMSN_SM(1);
+    case 2: return RMSN_SM(2);
+    case 3: return RMSN_SM(3);
+    case 4: return RMSN_SM(4);
+    default: break;
+  }
+#undef RMSN_SM
+  if constexpr (FWD) {
+#define RMSN_SMF(IT) launch(softmax_fwd_kernel<D, true, IT, false, PEEL>, p.grid, block, p.lds, s, a)
+    switch (iters) {
+      case 5: return RMSN_SMF(5);
+      case 6: return RMSN_SMF(6);
+      case 7: return RMSN_SMF(7);
+      case 8: return RMSN_SMF(8);
+      default: break;
+    }
+#undef RMSN_SMF
+  }
+  return RMSNORM_ERR_UNSUPPORTED;
+}
+
 template <DT D, bool FWD>
 rmsnorm_status sm_dispatch(const Plan& p, const SmArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if constexpr (FWD) {
     constexpr int V = 16 / (int)sizeof(typename Elem<D>::S);
-    if (p.variant != RMSNORM_VARIANT_STREAMING && (int64_t)p.iters * p.tpr * V == a.N) {
+    if (p.variant != RMSNORM_VARIANT_STREAMING && !p.peel && (int64_t)p.iters * p.tpr * V == a.N) {
 #define RMSN_SMF(IT) launch(softmax_fwd_kernel<D, true, IT, true>, p.grid, block, p.lds, s, a)
       switch (p.iters) {
         case 1: return RMSN_SMF(1);
@@ -82,28 +118,11 @@ rmsnorm_status sm_dispatch(const Plan& p, const SmArgs& a, hipStream_t s) {
 #undef RMSN_SMF
     }
   }
-#define RMSN_SM(W, IT)                                                                          \
-  (FWD ? launch(softmax_fwd_kernel<D, W, IT>, p.grid, block, p.lds, s, a)                       \
-       : launch(softmax_bwd_kernel<D, W, IT>, p.grid, block, p.lds, s, a))
-  if (p.variant == RMSNORM_VARIANT_STREAMING) return p.wide ? RMSN_SM(true, 0) : RMSN_SM(false, 0);
-  switch (p.iters) {
-    case 1: return RMSN_SM(true, 1);
-    case 2: return RMSN_SM(true, 2);
-    case 3: return RMSN_SM(true, 3);
-    case 4: return RMSN_SM(true, 4);
-    default: break;
-  }
-  if constexpr (FWD) {
-    switch (p.iters) {
-      case 5: return launch(softmax_fwd_kernel<D, true, 5>, p.grid, block, p.lds, s, a);
-      case 6: return launch(softmax_fwd_kernel<D, true, 6>, p.grid, block, p.lds, s, a);
-      case 7: return launch(softmax_fwd_kernel<D, true, 7>, p.grid, block, p.lds, s, a);
-      case 8: return launch(softmax_fwd_kernel<D, true, 8>, p.grid, block, p.lds, s, a);
-      default: break;
-    }
-  }
-  return RMSNORM_ERR_UNSUPPORTED;
-#undef RMSN_SM
+  if (p.peel) return sm_dispatch_iters<D, FWD, true>(p, a, s);
+  if (p.variant == RMSNORM_VARIANT_STREAMING && !p.wide)
+    return FWD ? launch(softmax_fwd_kernel<D, false, 0>, p.grid, block, p.lds, s, a)
+               : launch(softmax_bwd_kernel<D, false, 0>, p.grid, block, p.lds, s, a);
+  return sm_dispatch_iters<D, FWD, false>(p, a, s);
 }
 
 template <bool FWD>
@@ -120,9 +139,13 @@ rmsnorm_status sm_impl(const void* a_in, int64_t lda, const void* dy, int64_t ld
   if ((st = check_matrix(out, ldo, M, N, eb)) != RMSNORM_OK) return st;
   const bool wide = wide_fits(a_in, lda, eb) && wide_fits(out, ldo, eb) &&
                     (FWD || wide_fits(dy, lddy, eb));
+  // Rows not 16-byte aligned but all at one offset from a boundary (contiguous rows of an odd
+  // width, say): whole vectors between a head and a tail of single elements.
+  const bool peel = !wide && N >= 2 * vec_elems(dtype) && same_row_phase(a_in, lda, out, ldo, eb) &&
+                    (FWD || same_row_phase(a_in, lda, dy, lddy, eb));
   const size_t acc = dtype == RMSNORM_DTYPE_F64 ? 8 : 4;
   Plan p;
-  if ((st = plan_sm(M, N, dtype, wide, variant, acc, FWD ? 3 : 1, FWD, &p)) != RMSNORM_OK)
+  if ((st = plan_sm(M, N, dtype, wide, peel, variant, acc, FWD ? 3 : 1, FWD, &p)) != RMSNORM_OK)
     return st;
   if (M == 0) return RMSNORM_OK;
   SmArgs a;

@@ -197,17 +197,36 @@ template <typename A> struct SmAcc {
 };
 template <> struct SmAcc<float> : RowAcc {};
 
+// One element of a row in the compute type, and its store.
+template <DT D>
+__device__ __forceinline__ typename Acc<D>::A elem_in(const typename Elem<D>::S* p) {
+  if constexpr (D == DT::F64) return *p;
+  else return to_f32<D>(*p);
+}
+template <DT D>
+__device__ __forceinline__ void elem_out(typename Elem<D>::S* p, typename Acc<D>::A v) {
+  if constexpr (D == DT::F64) *p = v;
+  else *p = from_f32<D>(v);
+}
+
 // Forward. Register kernel (ITERS > 0: the row's exp values stay in registers between the
 // reductions and the store) or streaming (ITERS = 0: each pass reads x again from the caches).
 // FULL (register kernel): the host has checked that N = ITERS * TPR * V, so every vector of every
 // thread lies inside the row and the kernel carries no code for partial vectors or padding (that
 // code alone would push the 8-vector kernel past its register budget).
+// PEEL (16-byte vectors, rows not 16-byte aligned, y rows at x's offsets from a 16-byte boundary):
+// the row's whole vectors start h < V elements in (h from the row's address); the vector mapping
+// covers them, lanes 0 .. h-1 hold the h head elements and lanes 0 .. t-1 the t < V tail elements
+// after the last whole vector. A lane's head element opens its even sum and its tail element
+// closes its odd sum, in both kernel families, so they keep giving the same bits. The host sizes
+// the mapping for floor(N / V) vectors: a row with one vector fewer leaves the last iteration's
+// lanes idle, never an earlier one.
 // The max pass also finds the row's minimum: when max - min < kSmNormalSpan (false for rows with
 // infinities or only NaN), every e_j is a normal float32 and the float32 kernels use
 // exp_row_normal, else the library exp. The choice is made per row from exact values, so the two
 // kernel families take the same one. LDS: three reduction slots of wpr compute-type values per
 // row group (max and -min, then the sum).
-template <DT D, bool WIDE, int ITERS, bool FULL = false>
+template <DT D, bool WIDE, int ITERS, bool FULL = false, bool PEEL = false>
 __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   using A = typename Acc<D>::A;
   using IO = NumIO<D, WIDE>;
@@ -215,9 +234,9 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   constexpr int V = IO::V;
   constexpr bool F32 = sizeof(A) == 4;
   static_assert(!FULL || (ITERS > 0 && WIDE), "FULL applies to the register kernel");
+  static_assert(!PEEL || (WIDE && !FULL), "PEEL takes 16-byte vectors and partial rows");
   extern __shared__ uint4 smem[];
   const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
-  const int nv = (N + V - 1) / V;
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
@@ -226,16 +245,32 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   A* red = reinterpret_cast<A*>(smem) + grp * 3 * wpr;
   // Rows past M read row 0 (in bounds) and store nothing.
   const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+  // The vector part of the row: NV elements from xv (the whole row unless PEEL).
+  int h = 0, t = 0;
+  if constexpr (PEEL) {
+    h = peel_head(xr, N);
+    t = (N - h) % V;
+  }
+  const S* xv = xr + h;
+  const int NV = N - h - t;
+  const int nv = (NV + V - 1) / V;
   constexpr int R = ITERS > 0 ? ITERS : 1;
   A ev[R][V];
 
   A mx = -INFINITY, nmn = -INFINITY;  // max and -min over the row
+  A hx = -INFINITY, tx = -INFINITY;   // PEEL: the lane's head and tail elements
+  if constexpr (PEEL) {
+    if (tl < h) hx = elem_in<D>(xr + tl);
+    if (tl < t) tx = elem_in<D>(xv + NV + tl);
+    mx = fmax(hx, tx);
+    if constexpr (F32) nmn = fmax(tl < h ? -hx : (A)-INFINITY, tl < t ? -tx : (A)-INFINITY);
+  }
   if constexpr (ITERS > 0) {
     if constexpr (FULL) {
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
         const int col = (it * TPR + tl) * V;
-        IO::unpack(IO::load_nt(xr + col, V), ev[it]);
+        IO::unpack(IO::load_nt(xv + col, V), ev[it]);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           mx = fmax(mx, ev[it][e]);
@@ -249,7 +284,7 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
       for (int it = 0; it < ITERS; ++it) {
         const int col = (it * TPR + tl) * V;
         if (it < ITERS - 1) {
-          IO::unpack(IO::load(xr + col, V), ev[it]);
+          IO::unpack(IO::load(xv + col, V), ev[it]);
 #pragma unroll
           for (int e = 0; e < V; ++e) {
             mx = fmax(mx, ev[it][e]);
@@ -258,10 +293,10 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
           continue;
         }
         A f[V];
-        if (col < N) IO::unpack(IO::load(xr + col, N - col), f);
+        if (col < NV) IO::unpack(IO::load(xv + col, NV - col), f);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          const bool in = col + e < N;
+          const bool in = col + e < NV;
           ev[it][e] = in ? f[e] : (A)-INFINITY;
           mx = fmax(mx, ev[it][e]);
           if constexpr (F32) nmn = fmax(nmn, in ? -f[e] : (A)-INFINITY);
@@ -272,10 +307,10 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       A f[V];
-      IO::unpack(IO::load(xr + col, N - col), f);
+      IO::unpack(IO::load(xv + col, NV - col), f);
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        if (col + e < N) {
+        if (col + e < NV) {
           mx = fmax(mx, f[e]);
           if constexpr (F32) nmn = fmax(nmn, -f[e]);
         }
@@ -294,30 +329,43 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   // element-to-thread mapping and order, so register values are not held across the library exp.
   const bool in_regs = ITERS > 0 && fast;
   A s0 = 0, s1 = 0;
+  A he = 0, te = 0;  // PEEL: exp of the lane's head and tail elements
   if (in_regs) {
+    if constexpr (PEEL) {
+      if (tl < h) he = ex(Flag<true>{}, hx - mx);
+      if (tl < t) te = ex(Flag<true>{}, tx - mx);
+      s0 = he;
+    }
     // Padding lanes (partial rows) hold -inf, which the short exp does not take: select 0.
 #pragma unroll
     for (int it = 0; it < R; ++it) {
       const int col = (it * TPR + tl) * V;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        A t = ex(Flag<true>{}, ev[it][e] - mx);
-        if (!FULL && it == R - 1) t = col + e < N ? t : (A)0;
-        ev[it][e] = t;
-        if (e & 1) s1 += t;
-        else s0 += t;
+        A q = ex(Flag<true>{}, ev[it][e] - mx);
+        if (!FULL && it == R - 1) q = col + e < NV ? q : (A)0;
+        ev[it][e] = q;
+        if (e & 1) s1 += q;
+        else s0 += q;
       }
     }
+    if constexpr (PEEL) s1 += te;
   } else if (valid) {
     SmAcc<A> acc;
     auto sum_pass = [&](auto fast_tag) {
+      if constexpr (PEEL) {
+        if (tl < h) acc.add(0, ex(fast_tag, hx - mx), a.comp != 0);
+      }
       for (int v = tl; v < nv; v += TPR) {
         const int col = v * V;
         A f[V];
-        IO::unpack(IO::load(xr + col, N - col), f);
+        IO::unpack(IO::load(xv + col, NV - col), f);
 #pragma unroll
         for (int e = 0; e < V; ++e)
-          if (col + e < N) acc.add(e, ex(fast_tag, f[e] - mx), a.comp != 0);
+          if (col + e < NV) acc.add(e, ex(fast_tag, f[e] - mx), a.comp != 0);
+      }
+      if constexpr (PEEL) {
+        if (tl < t) acc.add(1, ex(fast_tag, tx - mx), a.comp != 0);
       }
     };
     if (fast) sum_pass(Flag<true>{});
@@ -328,26 +376,35 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   if (!valid) return;
   const A r = (A)1 / sum;
   S* yr = static_cast<S*>(a.out) + row * a.ldo;
+  S* yv = yr + h;
   if (in_regs) {
+    if constexpr (PEEL) {
+      if (tl < h) elem_out<D>(yr + tl, he * r);
+      if (tl < t) elem_out<D>(yv + NV + tl, te * r);
+    }
 #pragma unroll
     for (int it = 0; it < R; ++it) {
       const int col = (it * TPR + tl) * V;
       const bool last = !FULL && it == R - 1;
-      if (last && col >= N) continue;
+      if (last && col >= NV) continue;
       A o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = ev[it][e] * r;
-      IO::store(yr + col, o, last ? N - col : V);
+      IO::store(yv + col, o, last ? NV - col : V);
     }
   } else {
     auto store_pass = [&](auto fast_tag) {
+      if constexpr (PEEL) {
+        if (tl < h) elem_out<D>(yr + tl, ex(fast_tag, hx - mx) * r);
+        if (tl < t) elem_out<D>(yv + NV + tl, ex(fast_tag, tx - mx) * r);
+      }
       for (int v = tl; v < nv; v += TPR) {
         const int col = v * V;
         A f[V], o[V];
-        IO::unpack(IO::load(xr + col, N - col), f);
+        IO::unpack(IO::load(xv + col, NV - col), f);
 #pragma unroll
         for (int e = 0; e < V; ++e) o[e] = ex(fast_tag, f[e] - mx) * r;
-        IO::store(yr + col, o, N - col);
+        IO::store(yv + col, o, NV - col);
       }
     };
     if (fast) store_pass(Flag<true>{});
@@ -356,17 +413,19 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
 }
 
 // Backward: s = sum(dy * y) over the row, dx = T(y * (dy - s)). Register kernel (ITERS > 0: y and
-// dy stay in registers) or streaming (ITERS = 0: read again for the elementwise pass).
-template <DT D, bool WIDE, int ITERS>
+// dy stay in registers) or streaming (ITERS = 0: read again for the elementwise pass). PEEL as
+// for the forward (y, dy and dx rows at one offset from a 16-byte boundary): the lane's head
+// product opens its even sum, its tail product closes its odd sum.
+template <DT D, bool WIDE, int ITERS, bool PEEL = false>
 __global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
   using A = typename Acc<D>::A;
   using IO = NumIO<D, WIDE>;
   using S = typename IO::S;
   using Raw = typename IO::Raw;
   constexpr int V = IO::V;
+  static_assert(!PEEL || WIDE, "PEEL takes 16-byte vectors");
   extern __shared__ uint4 smem[];
   const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
-  const int nv = (N + V - 1) / V;
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
@@ -375,26 +434,49 @@ __global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
   A* red = reinterpret_cast<A*>(smem) + grp * wpr;
   const S* yr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
   const S* dr = static_cast<const S*>(a.dy) + (valid ? row : 0) * a.lddy;
+  int h = 0, t = 0;
+  if constexpr (PEEL) {
+    h = peel_head(yr, N);
+    t = (N - h) % V;
+  }
+  const S* yv = yr + h;
+  const S* dv = dr + h;
+  const int NV = N - h - t;
+  const int nv = (NV + V - 1) / V;
   constexpr int R = ITERS > 0 ? ITERS : 1;
   Raw ry[R], rd[R];
 
   A s0 = 0, s1 = 0;
+  A hy = 0, hd = 0, ty = 0, td = 0;  // PEEL: the lane's head and tail elements of y and dy
+  if constexpr (PEEL) {
+    if (valid && tl < h) {
+      hy = elem_in<D>(yr + tl);
+      hd = elem_in<D>(dr + tl);
+    }
+    if (valid && tl < t) {
+      ty = elem_in<D>(yv + NV + tl);
+      td = elem_in<D>(dv + NV + tl);
+    }
+  }
   if constexpr (ITERS > 0) {
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
-      if (valid && col < N) {
-        ry[it] = IO::load_nt(yr + col, N - col);
-        rd[it] = IO::load_nt(dr + col, N - col);
+      if (valid && col < NV) {
+        ry[it] = IO::load_nt(yv + col, NV - col);
+        rd[it] = IO::load_nt(dv + col, NV - col);
       } else {
         ry[it] = IO::load(yr, 0);
         rd[it] = IO::load(dr, 0);
       }
     }
+    if constexpr (PEEL) {
+      if (tl < h) s0 = fma(hd, hy, s0);
+    }
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
-      if (!(valid && col < N)) continue;
+      if (!(valid && col < NV)) continue;
       A yf[V], df[V];
       IO::unpack(ry[it], yf);
       IO::unpack(rd[it], df);
@@ -404,42 +486,56 @@ __global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
         else s0 = fma(df[e], yf[e], s0);
       }
     }
+    if constexpr (PEEL) {
+      if (tl < t) s1 = fma(td, ty, s1);
+    }
   } else if (valid) {
     SmAcc<A> acc;
+    if constexpr (PEEL) {
+      if (tl < h) acc.fma(0, hd, hy, a.comp != 0);
+    }
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       A yf[V], df[V];
-      IO::unpack(IO::load(yr + col, N - col), yf);
-      IO::unpack(IO::load(dr + col, N - col), df);
+      IO::unpack(IO::load(yv + col, NV - col), yf);
+      IO::unpack(IO::load(dv + col, NV - col), df);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc.fma(e, df[e], yf[e], a.comp != 0);
+    }
+    if constexpr (PEEL) {
+      if (tl < t) acc.fma(1, td, ty, a.comp != 0);
     }
     s0 = acc.total();
   }
   const A s = group_reduce<false>(s0 + s1, red, wpr, tl);
   if (!valid) return;
   S* xr = static_cast<S*>(a.out) + row * a.ldo;
+  S* xv = xr + h;
+  if constexpr (PEEL) {
+    if (tl < h) elem_out<D>(xr + tl, hy * (hd - s));
+    if (tl < t) elem_out<D>(xv + NV + tl, ty * (td - s));
+  }
   if constexpr (ITERS > 0) {
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int col = (it * TPR + tl) * V;
-      if (col >= N) continue;
+      if (col >= NV) continue;
       A yf[V], df[V], o[V];
       IO::unpack(ry[it], yf);
       IO::unpack(rd[it], df);
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = yf[e] * (df[e] - s);
-      IO::store(xr + col, o, N - col);
+      IO::store(xv + col, o, NV - col);
     }
   } else {
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       A yf[V], df[V], o[V];
-      IO::unpack(IO::load(yr + col, N - col), yf);
-      IO::unpack(IO::load(dr + col, N - col), df);
+      IO::unpack(IO::load(yv + col, NV - col), yf);
+      IO::unpack(IO::load(dv + col, NV - col), df);
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = yf[e] * (df[e] - s);
-      IO::store(xr + col, o, N - col);
+      IO::store(xv + col, o, NV - col);
     }
   }
 }

@@ -2,8 +2,9 @@
 interface) against the CPU oracle.
 
 Softmax: float32 / float16 / bfloat16 / float64, register and streaming kernels (bit-identical),
-ragged and misaligned widths, peaked rows (large logits), rows of -inf but one element, and the
-backward from the GPU's own forward output. Float64 RMSNorm: forward and backward to the candle
+ragged and misaligned widths (rows not 16-byte aligned: the peeled kernels when every matrix's rows
+sit at one offset from a 16-byte boundary, else the element-wise ones), peaked rows (large logits),
+rows of -inf but one element, and the backward from the GPU's own forward output. Float64 RMSNorm: forward and backward to the candle
 page's 1e-10 bound against the composed float64 formula.
 """
 import numpy as np
@@ -131,6 +132,68 @@ def test_softmax_exp_paths(dtype, N):
     for variant in ("registers", "streaming"):
         y = arr(rn.softmax_fwd(xt, variant=variant)).astype(np.float64)
         assert np.isnan(y[1]).all() and np.isfinite(y[0]).all() and np.isfinite(y[2]).all()
+
+
+# Contiguous rows of an odd width are not 16-byte aligned: whole vectors between a head and a tail
+# of single elements (register kernels up to 8 vectors a thread forward, 4 backward; streaming
+# beyond: 70001 forward, 50257 and 70001 backward).
+UNALIGNED = [("bf16", 129, 1027), ("bf16", 6, 50257), ("f16", 40, 4099), ("f32", 33, 1001),
+             ("f64", 17, 1001), ("bf16", 5, 70001), ("f16", 64, 17)]
+
+
+@pytest.mark.parametrize("dtype,M,N", UNALIGNED)
+def test_softmax_unaligned_rows(dtype, M, N):
+    run_sm(dtype, M, N, seed=M)
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 1027), ("f16", 30001), ("f32", 1001),
+                                     ("f64", 1001)])
+def test_softmax_unaligned_families_agree(dtype, N):
+    """Peeled rows: the register and streaming kernels give the same bits (head element first in
+    a lane's even sum, tail element last in its odd sum, in both)."""
+    _, a = run_sm(dtype, 37, N, variant="registers", seed=4)
+    _, b = run_sm(dtype, 37, N, variant="streaming", seed=4)
+    assert same_bits(a[0], b[0]).all() and same_bits(a[1], b[1]).all()
+
+
+def test_softmax_unaligned_forward_families_agree_wide():
+    """Forward rows of 7 vectors a thread between a head and a tail (50257, the GPT-2 vocabulary)."""
+    x = make_inputs(WL["bf16"], M=9, N=50257, seed=8)["x"]
+    xt = to_device(x, "bf16", DEV)
+    print("softmax fwd families bf16 N=50257 unaligned", flush=True)
+    a = rn.softmax_fwd(xt, variant="registers")
+    b = rn.softmax_fwd(xt, variant="streaming")
+    torch.cuda.synchronize()
+    check_softmax_fwd(arr(a), x, dtype="bf16")
+    assert same_bits(arr(a), arr(b)).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_softmax_unaligned_outputs(dtype):
+    """Outputs in padded rows at x's offsets (16 bytes of padding: peeled kernels) must leave the
+    padding untouched; outputs one element off x's offsets take the element-wise kernels."""
+    M, N = 20, 1027
+    inp = make_inputs(WL[dtype], M=M, N=N, seed=6)
+    xt, dyt = to_device(inp["x"], dtype, DEV), to_device(inp["dy"], dtype, DEV)
+    pad = 16 // xt.element_size()
+    for layout in ("padded", "shifted"):
+        print(f"softmax unaligned outputs dtype={dtype} layout={layout}", flush=True)
+        if layout == "padded":
+            ybuf = torch.full((M, N + pad), float("nan"), dtype=xt.dtype, device=DEV)
+            dbuf = torch.full((M, N + pad), float("nan"), dtype=xt.dtype, device=DEV)
+            y_out, dx_out = ybuf[:, :N], dbuf[:, :N]
+        else:
+            ybuf = torch.empty(M * N + 1, dtype=xt.dtype, device=DEV)
+            dbuf = torch.empty(M * N + 1, dtype=xt.dtype, device=DEV)
+            y_out, dx_out = ybuf[1:].view(M, N), dbuf[1:].view(M, N)
+        y = rn.softmax_fwd(xt, y=y_out)
+        dx = rn.softmax_bwd(dyt, y, dx=dx_out)
+        torch.cuda.synchronize()
+        yg = arr(y)
+        check_softmax_fwd(yg, inp["x"], dtype=dtype)
+        check_softmax_bwd(arr(dx), inp["dy"], yg, dtype=dtype)
+        if layout == "padded":
+            assert torch.isnan(ybuf[:, N:]).all() and torch.isnan(dbuf[:, N:]).all()
 
 
 def test_softmax_zero_rows():
