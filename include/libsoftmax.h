@@ -18,8 +18,12 @@
  *
  * Layout: row-major [M, N], unit column stride, row strides in elements (>= N); dtype is one of
  * RMSNORM_DTYPE_F32, _F16, _BF16, _F64 for all tensors of a call. variant: AUTO, REGISTERS (the
- * row stays in registers; rows up to 4 sixteen-byte vectors per thread of a 1024-thread group,
- * 16-byte aligned) or STREAMING (any N and alignment); LDS returns RMSNORM_ERR_UNSUPPORTED.
+ * row stays in registers; rows up to 8 (forward) or 4 (backward) sixteen-byte vectors per thread
+ * of a 1024-thread group) or STREAMING (any N and alignment); LDS returns RMSNORM_ERR_UNSUPPORTED.
+ * Rows take 16-byte accesses when every tensor is 16-byte aligned with row strides a multiple of
+ * 16 bytes, or when N >= 2 * (16 / sizeof(T)) and every tensor's rows sit at one offset from a
+ * 16-byte boundary (contiguous rows of an odd width, say: whole vectors between a head and a tail
+ * of single elements); REGISTERS needs one of the two. Other layouts take element-wise kernels.
  */
 #ifndef LIBSOFTMAX_H
 #define LIBSOFTMAX_H
