@@ -49,12 +49,18 @@ int bwd_batch(int iters) { return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB; 
 // 123 streaming; whole-vector rows N = 30000, LDS-staged 159 us against 190; rows with a partial
 // last vector through a padded stride (N = 24577, 30001, 32767), LDS-staged 137, 171, 193 us
 // against 176, 235, 282. The families give bit-identical results, so the choice changes only speed.
+// peel_ok: rows not 16-byte aligned whose x and dy rows sit at one offset from a 16-byte boundary
+// (streaming kernel, dw sums in LDS); peel_regs_ok: the same with w 16-byte aligned, where at most
+// one whole vector per lane (floor(N / V) <= 1024) takes the register kernel for such rows.
 rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, bool ag,
-                        rmsnorm_variant req, Plan* p, bool peel_ok = false) {
+                        rmsnorm_variant req, Plan* p, bool peel_ok = false,
+                        bool peel_regs_ok = false) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
   int tpr, iters;
   bwd_shape(nv_wide, &tpr, &iters);
-  const bool reg_ok = wide_ok && iters <= kBwdRegMaxIters;
+  const int64_t nv_peel = N / vec_elems(dtype);
+  const bool peel_regs = !wide_ok && peel_ok && peel_regs_ok && nv_peel <= kBwdBlockThreads;
+  const bool reg_ok = (wide_ok && iters <= kBwdRegMaxIters) || peel_regs;
   const bool lds_ok = wide_ok && iters <= kBwdLdsMaxIters;
   rmsnorm_variant v = req;
   if (v == RMSNORM_VARIANT_AUTO) {
@@ -78,7 +84,17 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
     p->iters = 0;
     p->groups = 1;
     p->lds = round16(sizeof(float) * 2 * (tpr / 64));
-    if (p->peel) p->lds = 128 + sizeof(float) * (size_t)partial_ld(N);  // + the dw sums in LDS
+    if (p->peel) p->lds = 128 + sizeof(float) * (size_t)peel_sum_floats(partial_ld(N));
+    return RMSNORM_OK;
+  }
+  if (!wide_ok) {  // registers on peeled rows: one vector per lane, dw sums of each group in LDS
+    p->peel = true;
+    p->wide = true;
+    p->tpr = (int)clamp64(pow2_ceil(nv_peel), 64, kBwdBlockThreads);
+    p->iters = 1;
+    p->groups = kBwdBlockThreads / p->tpr;
+    p->lds = round16(sizeof(float) * 2 * (size_t)p->groups * (p->tpr / 64)) +
+             sizeof(float) * (size_t)p->groups * (size_t)peel_sum_floats(partial_ld(N));
     return RMSNORM_OK;
   }
   p->wide = true;
@@ -158,6 +174,7 @@ rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
     return p.wide ? launch(bwd_stream_kernel<D, true, AG>, p.grid, block, p.lds, s, a)
                   : launch(bwd_stream_kernel<D, false, AG>, p.grid, block, p.lds, s, a);
   }
+  if (p.peel) return launch(bwd_peel_rows_kernel<D, AG>, p.grid, block, p.lds, s, a);
   const bool full = tiles_row(p, a.N, Elem<D>::VEC);
   if (p.variant == RMSNORM_VARIANT_LDS) {
     // Rows of 3 or 4 vectors per thread have 1024 threads (one row group) per block: the kernel
@@ -312,10 +329,11 @@ rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_
   // Otherwise x and dy rows at equal offsets from a 16-byte boundary move whole vectors between an
   // element-wise head and tail, with the dw sums in LDS (rows up to kStreamLdsAccFloats wide).
   const bool peel_ok = same_row_phase(x, ldx, dy, lddy, eb) && N >= 2 * vec_elems(dtype) &&
-                       partial_ld(N) <= kStreamLdsAccFloats;
+                       peel_sum_floats(partial_ld(N)) <= kStreamLdsAccFloats;
   const bool ag = autograd_casts(rounding, dtype);
   Plan p;
-  if ((st = plan_bwd(M, N, dtype, wide, ag, variant, &p, peel_ok)) != RMSNORM_OK) return st;
+  if ((st = plan_bwd(M, N, dtype, wide, ag, variant, &p, peel_ok, aligned(w, 16))) != RMSNORM_OK)
+    return st;
   if (M == 0) return RMSNORM_OK;
 
   BwdArgs a;
@@ -371,15 +389,7 @@ rmsnorm_status bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx
     return st;
   if (dw == nullptr) return RMSNORM_ERR_INVALID_ARG;
   if (!aligned(dw, 4)) return RMSNORM_ERR_MISALIGNED;
-  {
-    const int eb = elem_bytes(dtype);
-    const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) &&
-                      wide_fits(dx, lddx, eb) && aligned(w, 16);
-    Plan p;
-    if ((st = plan_bwd(M, N, dtype, wide, autograd_casts(rounding, dtype), variant, &p)) !=
-        RMSNORM_OK)
-      return st;
-  }
+
   st = bwd_rows_impl(dy, lddy, x, ldx, w, rstd, dx, lddx, workspace, workspace_bytes_given, M, N,
                      dtype, offset, rounding, variant, stream);
   if (st != RMSNORM_OK) return st;

@@ -34,6 +34,12 @@ inline int64_t num_partials(int64_t M) { return M < kMaxPartials ? M : kMaxParti
 __device__ __forceinline__ int64_t block_rows(int64_t M, int P, int b) { return (M - b + P - 1) / P; }
 // Row stride of the workspace in floats (16-byte aligned rows).
 inline int64_t partial_ld(int64_t N) { return (N + 3) & ~int64_t(3); }
+// Column sums in LDS indexed by a lane's 16-byte vector at an element offset h (rows not 16-byte
+// aligned): one pad float after every 8, so the lanes' stride of 8 floats becomes 9 and a 32-bit
+// LDS access of 64 lanes meets every bank at most once per pass instead of 8 or 16 lanes on one.
+__host__ __device__ __forceinline__ int peel_col(int c) { return c + (c >> 3); }
+// Floats of such a sums array for ldp columns.
+__host__ __device__ inline int64_t peel_sum_floats(int64_t ldp) { return ldp + (ldp >> 3) + 1; }
 
 struct BwdArgs {
   const void* dy;
@@ -646,11 +652,11 @@ __global__ void __launch_bounds__(1024) bwd_peel_kernel(BwdArgs a) {
   const int tl = threadIdx.x;
   const int b = blockIdx.x, P = a.P;
   float* red = reinterpret_cast<float*>(smem);            // [2][wpr], at most 32 floats
-  float* const sums = reinterpret_cast<float*>(smem) + 32;  // dw sums [N]
+  float* const sums = reinterpret_cast<float*>(smem) + 32;  // dw sums, columns at peel_col
   const S* wr = static_cast<const S*>(a.w);
   const bool walign = ((uintptr_t)wr & 15u) == 0;
   const bool comp = a.comp != 0;
-  for (int c = tl; c < N; c += TPR) sums[c] = 0.f;
+  for (int c = tl; c < N; c += TPR) sums[peel_col(c)] = 0.f;
 
   int s = 0;
   for (int64_t row = b; row < a.M; row += P, ++s) {
@@ -689,7 +695,8 @@ __global__ void __launch_bounds__(1024) bwd_peel_kernel(BwdArgs a) {
       const float xh = to_f32<D>(xr[col]) * rs;
       const float gd = gain_dy<D, AG>(a.offset + to_f32<D>(wr[col]), dyv);
       dxr[col] = from_f32<D>(rs * (gd - xh * c));
-      sums[col] = __builtin_fmaf(dyv, dw_factor<D, AG>(xh), sums[col]);
+      const int k = peel_col(col);
+      sums[k] = __builtin_fmaf(dyv, dw_factor<D, AG>(xh), sums[k]);
     };
     if (tl < h) second(tl);
     for (int j = tl; j < nb; j += TPR) {
@@ -704,7 +711,8 @@ __global__ void __launch_bounds__(1024) bwd_peel_kernel(BwdArgs a) {
         const float xh = xf[e] * rs;
         const float gd = gain_dy<D, AG>(a.offset + wf[e], df[e]);
         o[e] = rs * (gd - xh * c);
-        sums[col + e] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), sums[col + e]);
+        const int k = peel_col(col + e);
+        sums[k] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh), sums[k]);
       }
       const auto out = IO::pack(o);
       if (a.dxvec) IO::store(at(dxr, col), out);
@@ -714,7 +722,162 @@ __global__ void __launch_bounds__(1024) bwd_peel_kernel(BwdArgs a) {
   }
   lds_barrier();  // the last row's sums were added by other threads
   float* const pg = a.part + (int64_t)b * a.ldp;
-  for (int c = tl; c < N; c += TPR) pg[c] = sums[c];
+  for (int c = tl; c < N; c += TPR) pg[c] = sums[peel_col(c)];
+}
+
+// Rows that are not 16-byte aligned, as bwd_peel_kernel, of at most one whole 16-byte vector per
+// lane, on the register kernel's persistent grid and row order: G row groups of TPR threads, step s
+// of block b giving its group row b + (s * G + grp) * P. A lane holds the row's whole vector tl
+// (the vectors start h elements into the row, h from the row's address), lanes below h and below t
+// the head and tail elements, in registers for both passes. One step ahead the next row's x, dy,
+// rstd and gain are loaded, all unconditionally (a lane without a whole vector reads the row's first
+// one, head and tail indices are clamped into the row; the two aligned gain vectors that the funnel
+// shift by h takes come through a descriptor bounded at w's last 16-byte granule, so the one past
+// w's end reads zeros), so the compiler waits only for the row in use. The thread that holds a
+// column changes with h, so each row group keeps its dw sums in LDS (past the reduction slots,
+// columns at peel_col): per row one fma per column from one lane, in the group's row order, which the
+// barrier of the next row's reduction keeps. The block's partial row is the groups' sums added in
+// group order. w must be 16-byte aligned.
+template <DT D, bool AG>
+__global__ void __launch_bounds__(1024) bwd_peel_rows_kernel(BwdArgs a) {
+  using IO = VecIO<D, true>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, G = a.groups, N = a.N;
+  const int tid = threadIdx.x;
+  const int grp = wave_group(tid, TPR);
+  const int tl = tid - grp * TPR;
+  const int b = blockIdx.x, P = a.P;
+  const int64_t nloc = block_rows(a.M, P, b);
+  const int nsteps = (int)((nloc + G - 1) / G);
+  float* red = reinterpret_cast<float*>(smem);                  // [2][G][wpr]
+  const int stride = (int)peel_sum_floats(a.ldp);
+  float* const sums0 = red + ((2 * G * wpr + 3) & ~3);  // [G][stride], columns at peel_col
+  float* const sums = sums0 + (size_t)grp * stride;
+  for (int c = tl; c < N; c += TPR) sums[peel_col(c)] = 0.f;
+
+  const S* wr = static_cast<const S*>(a.w);
+  const BufRsrc wb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<S*>(wr), 0, (N * (int)sizeof(S) + 15) & ~15, kBufDword3);
+
+  Raw rx[2], rd[2], wa[2], wv[2];
+  S hx[2], hd[2], hw[2], tx[2], td[2], tw[2];
+  float rr[2];
+  int hh[2];
+  auto load_row = [&](int slot, int s) {
+    const int64_t li = (int64_t)s * G + grp;
+    const bool ok = s < nsteps && li < nloc;
+    const int64_t row = b + (ok ? li : 0) * P;
+    const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
+    const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
+    const int h = peel_head(xr, N);
+    const int nb = (N - h) / V;
+    const int t = N - h - nb * V;
+    hh[slot] = h;
+    const uint32_t vo = (uint32_t)((tl < nb ? tl : 0) * V) * (uint32_t)sizeof(S);
+    rx[slot] = IO::load_b_nt(buf_rsrc(xr), vo + (uint32_t)h * (uint32_t)sizeof(S), 0);
+    rd[slot] = IO::load_b_nt(buf_rsrc(dr), vo + (uint32_t)h * (uint32_t)sizeof(S), 0);
+    wa[slot] = IO::load_b(wb, vo, 0);
+    wv[slot] = IO::load_b(wb, vo + 16u, 0);
+    const int hi = tl < h ? tl : 0;
+    const int ti = t > 0 ? h + nb * V + (tl < t ? tl : 0) : 0;
+    hx[slot] = xr[hi];
+    hd[slot] = dr[hi];
+    hw[slot] = wr[hi];
+    tx[slot] = xr[ti];
+    td[slot] = dr[ti];
+    tw[slot] = wr[ti];
+    rr[slot] = a.rstd[row];
+  };
+  load_row(0, 0);
+
+  for (int s0 = 0; s0 < nsteps; s0 += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int s = s0 + j;
+      load_row(j ^ 1, s + 1);
+      if (s >= nsteps) continue;  // block-uniform
+      const int64_t li = (int64_t)s * G + grp;
+      const bool valid = li < nloc;  // wave-uniform
+      const int h = hh[j];
+      const int nb = (N - h) / V;
+      const int t = N - h - nb * V;
+      const int t0 = h + nb * V;
+      const float rs = rr[j];
+      float xh[V], gd[V], df[V];
+      float hxh = 0.f, hgd = 0.f, txh = 0.f, tgd = 0.f;
+      float d0 = 0.f, d1 = 0.f;
+      {
+        float xf[V], wf[V];
+        IO::unpack(rx[j], xf);
+        IO::unpack(rd[j], df);
+        IO::unpack(peel_vec<D>(h, wa[j], wv[j]), wf);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          xh[e] = xf[e] * rs;
+          gd[e] = gain_dy<D, AG>(a.offset + wf[e], df[e]);
+        }
+      }
+      if (valid) {
+        if (tl < h) {
+          hxh = to_f32<D>(hx[j]) * rs;
+          hgd = gain_dy<D, AG>(a.offset + to_f32<D>(hw[j]), to_f32<D>(hd[j]));
+          d0 = __builtin_fmaf(hgd, hxh, d0);
+        }
+        if (tl < nb) {
+#pragma unroll
+          for (int e = 0; e < V; e += 2) {
+            d0 = __builtin_fmaf(gd[e], xh[e], d0);
+            d1 = __builtin_fmaf(gd[e + 1], xh[e + 1], d1);
+          }
+        }
+        if (tl < t) {
+          txh = to_f32<D>(tx[j]) * rs;
+          tgd = gain_dy<D, AG>(a.offset + to_f32<D>(tw[j]), to_f32<D>(td[j]));
+          d1 = __builtin_fmaf(tgd, txh, d1);
+        }
+      }
+      float dot[1] = {d0 + d1};
+      group_sum_batch<1>(dot, red + ((s & 1) * G + grp) * wpr, wpr, tl);
+      if (wpr == 1) lds_barrier();  // orders the LDS sums of consecutive rows (no barrier above)
+      if (!valid) continue;
+      const float c = dot[0] / (float)N;
+      S* dxr = static_cast<S*>(a.dx) + (b + li * P) * a.lddx;
+      if (tl < h) {
+        dxr[tl] = from_f32<D>(rs * (hgd - hxh * c));
+        sums[peel_col(tl)] =
+            __builtin_fmaf(to_f32<D>(hd[j]), dw_factor<D, AG>(hxh), sums[peel_col(tl)]);
+      }
+      if (tl < nb) {
+        const int col = h + tl * V;
+        float o[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          o[e] = rs * (gd[e] - xh[e] * c);
+          const int k = peel_col(col + e);
+          sums[k] = __builtin_fmaf(df[e], dw_factor<D, AG>(xh[e]), sums[k]);
+        }
+        const Raw out = IO::pack(o);
+        if (a.dxvec) IO::store(at(dxr, col), out);
+        else IO::store_part(at(dxr, col), out, V);
+      }
+      if (tl < t) {
+        dxr[t0 + tl] = from_f32<D>(rs * (tgd - txh * c));
+        const int k = peel_col(t0 + tl);
+        sums[k] = __builtin_fmaf(to_f32<D>(td[j]), dw_factor<D, AG>(txh), sums[k]);
+      }
+    }
+  }
+  lds_barrier();  // every group's last sums are in LDS
+  float* const pg = a.part + (int64_t)b * a.ldp;
+  for (int c = tid; c < N; c += G * TPR) {
+    float v = sums0[peel_col(c)];
+    for (int g = 1; g < G; ++g) v += sums0[(size_t)g * stride + peel_col(c)];
+    pg[c] = v;
+  }
 }
 
 // dw_j = sum over p of part[p, j] in a fixed order, spread over many compute units: a block of

@@ -287,6 +287,33 @@ def test_unaligned_row_layouts(dtype, layout):
         assert not rest.any()
 
 
+# Contiguous rows of an odd width, many per block: the peeled register backward (one whole vector
+# per lane, 1 to 16 row groups, its ring wrapping over up to 16 steps), against the oracle, both
+# rounding modes and the autograd casts; the streaming peeled kernel on the same inputs.
+@pytest.mark.parametrize("dtype,M,N,mode", [
+    ("bf16", 4096, 4097, "twice"), ("bf16", 4096, 4097, "autograd"), ("f16", 3000, 1027, "once"),
+    ("bf16", 2100, 8199, "twice"), ("f32", 2000, 4097, "twice"), ("bf16", 700, 31, "once")])
+def test_unaligned_rows_many_per_block(dtype, M, N, mode):
+    rounding = "twice" if mode == "autograd" else mode
+    casts = "autograd" if mode == "autograd" else "float32"
+    wl = WL[dtype].with_(rounding=rounding)
+    inp = make_inputs(wl, M=M, N=N, seed=43)
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    xt, wt, dyt = (to_device(a, dtype, DEV) for a in (x, w, dy))
+    for variant in ("registers", "streaming"):
+        print(f"case unaligned many rows dtype={dtype} M={M} N={N} mode={mode} variant={variant}",
+              flush=True)
+        y, rstd = rn.fwd(xt, wt, rounding=rounding)
+        dx, dw = rn.bwd(dyt, xt, wt, rstd, rounding=rounding, casts=casts, variant=variant)
+        torch.cuda.synchronize()
+        rg = to_np(rstd)
+        st = check_dx(to_np(dx), dy, x, w, rg, offset=0.0, dtype=dtype, rounding=rounding,
+                      casts=casts)
+        st.update(check_dw(to_np(dw), oracle.rmsnorm_dw(dy, x, rg, dtype=dtype, rounding=rounding,
+                                                        casts=casts)))
+        print(st, flush=True)
+
+
 def test_forward_register_and_lds_staging_at_wide_rows():
     for variant in ("registers", "lds", "streaming"):
         wl = WL["bf16"]
