@@ -52,8 +52,10 @@
  * elements, ld* >= N; non-contiguous gradients are handled through the row stride). w is [N].
  * x, w, y, dy and dx share one dtype (the comparison in the blog post's footnote 6 assumes weights
  * stored in the input dtype). rstd is float32 [M]; dw is float32 [N]. Outputs must not overlap
- * inputs. The fast paths use 16-byte accesses; when a base pointer or a row stride does not allow
- * them the call still succeeds through an element-wise path.
+ * inputs. The fast paths use 16-byte accesses on 16-byte aligned bases and row strides. Rows that
+ * are not 16-byte aligned but sit at one offset from a 16-byte boundary in x and dy (contiguous rows
+ * of an odd width, say; N >= 2 * (16 / sizeof(T))) move whole 16-byte vectors between a head and a
+ * tail of single elements; any other layout still succeeds through an element-wise path.
  */
 #ifndef LIBRMSNORM_H
 #define LIBRMSNORM_H
