@@ -10,12 +10,16 @@ using namespace rmsn;
 
 namespace {
 
-// 16-byte vectors per thread in the register kernels: at most 4 in the backward (it keeps y and
-// dy), 8 in the forward (one float per element; a 4096-wide 16-bit row is one wavefront with no LDS
-// round). The forward's partial vector is handled in the last iteration only, which keeps its
-// 8-vector instantiation at 112 registers (bf16 1024 x 50264: 70 -> 55 us against the streaming
-// kernel).
+// 16-byte vectors per thread in the register kernels' row shapes: at most 4 in the backward (it
+// keeps y and dy) while 1024 threads can share a row, 8 in the forward (one float per element; a
+// 4096-wide 16-bit row is one wavefront with no LDS round). The forward's partial vector is handled
+// in the last iteration only, which keeps its 8-vector instantiation at 112 registers (bf16 1024 x
+// 50264: 70 -> 55 us against the streaming kernel).
 constexpr int kSmMaxIters = 4;
+// The backward's rows wider than 4 vectors a thread at 1024 threads keep y and dy in registers up
+// to 8 vectors a thread (64 registers of raw data) rather than reading them twice; float16 up to 6
+// (its 7- and 8-vector instantiations spill 14 to 64 registers).
+int sm_bwd_reg_max_iters(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F16 ? 6 : 8; }
 // Float64 streaming backward with its dw sums in registers: up to 8 vectors (16 values) per thread.
 constexpr int kF64StreamRegVectors = 8;
 constexpr int kSmFwdFullMaxIters = 8;
@@ -45,7 +49,7 @@ rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, 
   int tpr, iters, max_iters = kSmMaxIters;
   if (fwd) max_iters = kSmFwdFullMaxIters;
   sm_shape(nv_wide, max_iters, &tpr, &iters);
-  const bool reg_ok = wide_ok && iters <= max_iters;
+  const bool reg_ok = wide_ok && iters <= (fwd ? max_iters : sm_bwd_reg_max_iters(dtype));
   rmsnorm_variant v = req;
   if (v == RMSNORM_VARIANT_AUTO) v = reg_ok ? RMSNORM_VARIANT_REGISTERS : RMSNORM_VARIANT_STREAMING;
   if (v == RMSNORM_VARIANT_LDS || (v == RMSNORM_VARIANT_REGISTERS && !reg_ok))
@@ -66,13 +70,20 @@ rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, 
   return RMSNORM_OK;
 }
 
+// The backward's instantiations the plan can select (float16 stops at 6 vectors a thread).
+template <DT D, int IT, bool PEEL>
+rmsnorm_status sm_bwd_launch(const Plan& p, const SmArgs& a, hipStream_t s, int block) {
+  if constexpr (D == DT::F16 && IT > 6) return RMSNORM_ERR_UNSUPPORTED;
+  else return launch(softmax_bwd_kernel<D, true, IT, PEEL>, p.grid, block, p.lds, s, a);
+}
+
 // 16-byte-vector kernels: streaming (iters 0) or registers, whole rows or peeled (PEEL).
 template <DT D, bool FWD, bool PEEL>
 rmsnorm_status sm_dispatch_iters(const Plan& p, const SmArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
-#define RMSN_SM(IT)                                                                                \
-  (FWD ? launch(softmax_fwd_kernel<D, true, IT, false, PEEL>, p.grid, block, p.lds, s, a)          \
-       : launch(softmax_bwd_kernel<D, true, IT, PEEL>, p.grid, block, p.lds, s, a))
+#define RMSN_SM(IT)                                                                       \
+  (FWD ? launch(softmax_fwd_kernel<D, true, IT, false, PEEL>, p.grid, block, p.lds, s, a) \
+       : sm_bwd_launch<D, IT, PEEL>(p, a, s, block))
   const int iters = p.variant == RMSNORM_VARIANT_STREAMING ? 0 : p.iters;
   switch (iters) {
     case 0: return RMSN_SM(0);
@@ -80,20 +91,13 @@ rmsnorm_status sm_dispatch_iters(const Plan& p, const SmArgs& a, hipStream_t s) 
     case 2: return RMSN_SM(2);
     case 3: return RMSN_SM(3);
     case 4: return RMSN_SM(4);
+    case 5: return RMSN_SM(5);
+    case 6: return RMSN_SM(6);
+    case 7: return RMSN_SM(7);
+    case 8: return RMSN_SM(8);
     default: break;
   }
 #undef RMSN_SM
-  if constexpr (FWD) {
-#define RMSN_SMF(IT) launch(softmax_fwd_kernel<D, true, IT, false, PEEL>, p.grid, block, p.lds, s, a)
-    switch (iters) {
-      case 5: return RMSN_SMF(5);
-      case 6: return RMSN_SMF(6);
-      case 7: return RMSN_SMF(7);
-      case 8: return RMSN_SMF(8);
-      default: break;
-    }
-#undef RMSN_SMF
-  }
   return RMSNORM_ERR_UNSUPPORTED;
 }
 

@@ -18,7 +18,7 @@
  *
  * Layout: row-major [M, N], unit column stride, row strides in elements (>= N); dtype is one of
  * RMSNORM_DTYPE_F32, _F16, _BF16, _F64 for all tensors of a call. variant: AUTO, REGISTERS (the
- * row stays in registers; rows up to 8 (forward) or 4 (backward) sixteen-byte vectors per thread
+ * row stays in registers; rows up to 8 sixteen-byte vectors per thread (float16 backward: 6)
  * of a 1024-thread group) or STREAMING (any N and alignment); LDS returns RMSNORM_ERR_UNSUPPORTED.
  * Rows take 16-byte accesses when every tensor is 16-byte aligned with row strides a multiple of
  * 16 bytes, or when N >= 2 * (16 / sizeof(T)) and every tensor's rows sit at one offset from a

@@ -78,6 +78,16 @@ def test_softmax_forward_families_agree_on_wide_rows(dtype, N):
     assert same_bits(arr(a), arr(b)).all()
 
 
+@pytest.mark.parametrize("dtype,N", [("bf16", 40000), ("bf16", 65000), ("f16", 45000),
+                                     ("f64", 12000), ("bf16", 50257)])
+def test_softmax_backward_families_agree_on_wide_rows(dtype, N):
+    """Backward rows of 5 to 8 vectors a thread (float16: 6) in registers at 1024 threads, against
+    the streaming kernel (same bits) and the oracle; 50257 also peeled."""
+    _, a = run_sm(dtype, 5, N, variant="registers", seed=9)
+    _, b = run_sm(dtype, 5, N, variant="streaming", seed=9)
+    assert same_bits(a[0], b[0]).all() and same_bits(a[1], b[1]).all()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_softmax_padded_rows(dtype):
     run_sm(dtype, 100, 1000, ld=1032)
