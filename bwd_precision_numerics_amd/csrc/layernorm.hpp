@@ -172,15 +172,20 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
 
 // Any N and any alignment: three passes over the row (sum, centred squares, store), reading x again
 // from the caches. Same thread-to-element mapping and summation order as the register kernel.
-template <DT D, bool WIDE, bool HAS_B>
+// PEEL (16-byte vectors on rows that are not 16-byte aligned, as the RMSNorm forward's peeled
+// kernel): per row the whole vectors start h < V elements in (h from the row's address), lanes
+// 0 .. h-1 hold the head elements (first in their even sums) and lanes 0 .. t-1 the tail elements
+// (last in their odd sums); w and b for a vector come aligned and funnel-shifted by h (peel_w), and
+// y takes vector stores when its rows sit at x's offsets (yvec).
+template <DT D, bool WIDE, bool HAS_B, bool PEEL = false>
 __global__ void __launch_bounds__(1024) ln_fwd_stream_kernel(LnFwdArgs a) {
   using IO = VecIO<D, WIDE>;
   using S = typename IO::S;
   constexpr int V = IO::V;
+  static_assert(!PEEL || WIDE, "PEEL takes 16-byte vectors");
   extern __shared__ uint4 smem[];
 
   const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
-  const int nv = (N + V - 1) / V;
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
@@ -188,26 +193,53 @@ __global__ void __launch_bounds__(1024) ln_fwd_stream_kernel(LnFwdArgs a) {
   const bool valid = row < a.M;
   float* red = reinterpret_cast<float*>(smem) + grp * 2 * wpr;
   const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * a.ldx;
+  // The vector part of the row: NV elements from xv (the whole row unless PEEL).
+  int h = 0, t = 0;
+  if constexpr (PEEL) {
+    h = peel_head(xr, N);
+    t = (N - h) % V;
+  }
+  const S* xv = xr + h;
+  const int NV = N - h - t;
+  const int nv = (NV + V - 1) / V;
 
   const bool comp = a.comp != 0;
   RowAcc sx;
   if (valid) {
+    if constexpr (PEEL) {
+      if (tl < h) sx.add(0, to_f32<D>(xr[tl]), comp);
+    }
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       float f[V];
-      IO::unpack(col + V <= N ? IO::load(xr + col) : IO::load_part(xr + col, N - col), f);
+      IO::unpack(col + V <= NV ? IO::load(xv + col) : IO::load_part(xv + col, NV - col), f);
 #pragma unroll
       for (int e = 0; e < V; ++e) sx.add(e, f[e], comp);
+    }
+    if constexpr (PEEL) {
+      if (tl < t) sx.add(1, to_f32<D>(xv[NV + tl]), comp);
     }
   }
   const float mean = group_sum(sx.total(), red, wpr, tl) / (float)N;
   RowAcc q;
   if (valid) {
+    if constexpr (PEEL) {
+      if (tl < h) {
+        const float d = to_f32<D>(xr[tl]) - mean;
+        q.fma(0, d, d, comp);
+      }
+    }
     for (int v = tl; v < nv; v += TPR) {
       const int col = v * V;
       float f[V];
-      IO::unpack(col + V <= N ? IO::load(xr + col) : IO::load_part(xr + col, N - col), f);
-      add_centred_squares<V>(f, mean, N - col, q, comp);
+      IO::unpack(col + V <= NV ? IO::load(xv + col) : IO::load_part(xv + col, NV - col), f);
+      add_centred_squares<V>(f, mean, NV - col, q, comp);
+    }
+    if constexpr (PEEL) {
+      if (tl < t) {
+        const float d = to_f32<D>(xv[NV + tl]) - mean;
+        q.fma(1, d, d, comp);
+      }
     }
   }
   const float var = group_sum(q.total(), red + wpr, wpr, tl) / (float)N;
@@ -220,17 +252,34 @@ __global__ void __launch_bounds__(1024) ln_fwd_stream_kernel(LnFwdArgs a) {
   const S* wr = static_cast<const S*>(a.w);
   const S* br = static_cast<const S*>(a.b);
   void* yr = out_row<D, Out::ONCE>(a.y, row, a.ldy);
+  if constexpr (PEEL) {
+    auto one = [&](int col) {
+      const float xf[1] = {to_f32<D>(xr[col])}, wf[1] = {to_f32<D>(wr[col])};
+      const float bf[1] = {HAS_B ? to_f32<D>(br[col]) : 0.f};
+      float yf[1];
+      ln_affine<1, HAS_B>(xf, wf, bf, mean, rs, yf);
+      store_out<D, Out::ONCE, false, 1>(yr, col, 1, false, yf);
+    };
+    if (tl < h) one(tl);
+    if (tl < t) one(h + NV + tl);
+  }
+  const bool walign = ((uintptr_t)wr & 15u) == 0, balign = ((uintptr_t)br & 15u) == 0;
   for (int v = tl; v < nv; v += TPR) {
     const int col = v * V;
-    const bool full = col + V <= N;
+    const bool full = col + V <= NV;
     float xf[V], wf[V], bf[V], yf[V];
     // the row's last read of x: non-temporal
-    IO::unpack(full ? IO::load_nt(xr + col) : IO::load_part(xr + col, N - col), xf);
-    IO::unpack(full ? IO::load(wr + col) : IO::load_part(wr + col, N - col), wf);
-    if constexpr (HAS_B)
-      IO::unpack(full ? IO::load(br + col) : IO::load_part(br + col, N - col), bf);
+    IO::unpack(full ? IO::load_nt(xv + col) : IO::load_part(xv + col, NV - col), xf);
+    if constexpr (PEEL) {
+      peel_w<D, V>(wr, walign, N, h, h + col, wf);
+      if constexpr (HAS_B) peel_w<D, V>(br, balign, N, h, h + col, bf);
+    } else {
+      IO::unpack(full ? IO::load(wr + col) : IO::load_part(wr + col, N - col), wf);
+      if constexpr (HAS_B)
+        IO::unpack(full ? IO::load(br + col) : IO::load_part(br + col, N - col), bf);
+    }
     ln_affine<V, HAS_B>(xf, wf, bf, mean, rs, yf);
-    store_out<D, Out::ONCE, WIDE, V>(yr, col, N - col, a.yvec != 0, yf);
+    store_out<D, Out::ONCE, WIDE, V>(yr, h + col, NV - col, a.yvec != 0, yf);
   }
 }
 

@@ -44,8 +44,10 @@ void ln_fwd_shape(int64_t nv, int* tpr, int* iters) {
   *iters = (int)ceil_div(nv, *tpr);
 }
 
+// peel_ok: rows not 16-byte aligned (N >= 2 * V) take the streaming kernel with 16-byte vectors
+// between an element-wise head and tail.
 rmsnorm_status plan_ln_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
-                           rmsnorm_variant req, Plan* p) {
+                           rmsnorm_variant req, Plan* p, bool peel_ok = false) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
   int tpr, iters;
   ln_fwd_shape(nv_wide, &tpr, &iters);
@@ -57,7 +59,8 @@ rmsnorm_status plan_ln_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_
   p->variant = v;
   p->wide = v == RMSNORM_VARIANT_REGISTERS || wide_ok;
   if (v == RMSNORM_VARIANT_STREAMING) {
-    ln_fwd_shape(wide_ok ? nv_wide : N, &tpr, &iters);
+    p->peel = !wide_ok && peel_ok;
+    ln_fwd_shape(wide_ok || p->peel ? nv_wide : N, &tpr, &iters);
     iters = 0;
   }
   p->tpr = tpr;
@@ -73,6 +76,7 @@ template <DT D, bool HAS_B>
 rmsnorm_status ln_fwd_dispatch(const Plan& p, const LnFwdArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
   if (p.variant == RMSNORM_VARIANT_STREAMING) {
+    if (p.peel) return launch(ln_fwd_stream_kernel<D, true, HAS_B, true>, p.grid, block, p.lds, s, a);
     return p.wide ? launch(ln_fwd_stream_kernel<D, true, HAS_B>, p.grid, block, p.lds, s, a)
                   : launch(ln_fwd_stream_kernel<D, false, HAS_B>, p.grid, block, p.lds, s, a);
   }
@@ -123,16 +127,19 @@ rmsnorm_status ln_fwd_impl(const void* x, int64_t ldx, const void* w, const void
       !aligned(rstd, 4))
     return RMSNORM_ERR_MISALIGNED;
   const bool wide = wide_fits(x, ldx, eb) && aligned(w, 16) && aligned(b, 16);
+  // Otherwise whole 16-byte vectors of x between an element-wise head and tail (w and b funnel-
+  // shifted, or element by element when they are not 16-byte aligned).
+  const bool peel_ok = N >= 2 * vec_elems(dtype);
   Plan p;
-  if ((st = plan_ln_fwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  if ((st = plan_ln_fwd(M, N, dtype, wide, variant, &p, peel_ok)) != RMSNORM_OK) return st;
   if (M == 0) return RMSNORM_OK;
 
   LnFwdArgs a;
   a.x = x; a.w = w; a.b = b; a.y = y; a.mean = mean; a.rstd = rstd;
   a.ldx = ldx; a.ldy = ldy; a.M = M; a.N = (int)N;
   a.tpr = p.tpr; a.groups = p.groups; a.eps = eps;
-  a.yvec = wide_fits(y, ldy, eb);
-  a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
+  a.yvec = p.peel ? same_row_phase(x, ldx, y, ldy, eb) : wide_fits(y, ldy, eb);
+  a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide || p.peel, p.tpr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return b ? ln_fwd_by_dtype<true>(dtype, p, a, s) : ln_fwd_by_dtype<false>(dtype, p, a, s);
 }

@@ -117,6 +117,38 @@ def test_ln_wide_rows_register_sums(dtype, N):
     run_ln(dtype, 300, N, seed=22)
 
 
+# Contiguous rows of an odd width are not 16-byte aligned: the forward moves whole vectors between
+# an element-wise head and tail (w and b funnel-shifted, or element by element when w and b are not
+# 16-byte aligned; y stored as vectors when its rows sit at x's offsets).
+@pytest.mark.parametrize("layout", ["contiguous", "w_offset", "y_shifted", "no_bias"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_ln_unaligned_rows(dtype, layout):
+    M, N = 257, 1027
+    wl = WL[dtype]
+    inp = make_norm_inputs(wl, M=M, N=N, seed=12)
+    bias = layout != "no_bias"
+    x, w, b, dy = inp["x"], inp["w"], (inp["b"] if bias else None), inp["dy"]
+    xt, dyt = to_device(x, dtype, DEV), to_device(dy, dtype, DEV)
+    if layout == "w_offset":
+        wt = to_device(np.concatenate([np.zeros(1, np.float32), w]), dtype, DEV)[1:]
+        bt = to_device(np.concatenate([np.zeros(1, np.float32), b]), dtype, DEV)[1:]
+    else:
+        wt = to_device(w, dtype, DEV)
+        bt = to_device(b, dtype, DEV) if bias else None
+    out = {}
+    if layout == "y_shifted":
+        out["y"] = torch.empty(M * N + 1, dtype=xt.dtype, device=DEV)[1:].view(M, N)
+    print(f"ln unaligned dtype={dtype} layout={layout}", flush=True)
+    y, mean, rstd = rn.layernorm_fwd(xt, wt, bt, eps=wl.eps, **out)
+    dx, dw, db = rn.layernorm_bwd(dyt, xt, wt, mean, rstd, bias=bias)
+    torch.cuda.synchronize()
+    mg, rg = to_np(mean), to_np(rstd)
+    st = check_ln_fwd(to_np(y), mg, rg, x, w, b, eps=wl.eps, dtype=dtype)
+    st.update(check_ln_bwd(to_np(dx), to_np(dw), to_np(db) if bias else None, dy, x, w, mg, rg,
+                           dtype=dtype))
+    print(st, flush=True)
+
+
 def test_ln_repeatable():
     _, a = run_ln("bf16", 1000, 4096, seed=9)
     _, b = run_ln("bf16", 1000, 4096, seed=9)
