@@ -296,6 +296,7 @@ struct LnBwdArgs {
   int tpr;     // threads per row, multiple of 64
   int groups;  // rows processed concurrently per block
   int comp;    // streaming kernel: compensated row sums (long per-thread chains)
+  int dxvec = 0;  // peeled rows: dx rows sit at x's offsets from a 16-byte boundary
 };
 
 // combine_groups' first level split in two around a barrier the caller already has (the one of
@@ -554,6 +555,175 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
     if constexpr (HAS_DB) {
       combine_groups<K>(accb, cbb, rest, grp, tl, TPR);
       if (grp == 0) store_partial<ITERS, V>(accb, a.part + (int64_t)(P + b) * a.ldp, TPR, tl, N);
+    }
+  }
+}
+
+// Rows that are not 16-byte aligned, x and dy rows at one offset from a 16-byte boundary, at most one
+// whole vector per lane: the RMSNorm backward's peeled register kernel (bwd_peel_rows_kernel) with
+// the two row sums c1, c2 and the mean: G row groups on the persistent grid, the next row's x, dy,
+// mean, rstd and gain loaded one step ahead (all unconditionally), a lane's head element first in
+// its even sums and its tail element last in its odd sums, dw and db sums of each group in LDS
+// (columns at peel_col; the dw arrays of the G groups, then the db arrays), added in group order
+// into the block's two partial rows at the end. w must be 16-byte aligned.
+template <DT D, bool HAS_DB>
+__global__ void __launch_bounds__(1024) ln_bwd_peel_rows_kernel(LnBwdArgs a) {
+  using IO = VecIO<D, true>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  constexpr int V = IO::V;
+  extern __shared__ uint4 smem[];
+
+  const int TPR = a.tpr, wpr = TPR >> 6, G = a.groups, N = a.N;
+  const int tid = threadIdx.x;
+  const int grp = wave_group(tid, TPR);
+  const int tl = tid - grp * TPR;
+  const int b = blockIdx.x, P = a.P;
+  const int64_t nloc = block_rows(a.M, P, b);
+  const int nsteps = (int)((nloc + G - 1) / G);
+  const int stride = (int)peel_sum_floats(a.ldp);
+  float* red = reinterpret_cast<float*>(smem);            // [2][G][wpr][2]
+  float* const sw0 = red + ((4 * G * wpr + 3) & ~3);      // [G][stride] dw sums
+  float* const sb0 = sw0 + (size_t)G * stride;            // [G][stride] db sums
+  float* const sw = sw0 + (size_t)grp * stride;
+  float* const sb = sb0 + (size_t)grp * stride;
+  for (int c = tl; c < N; c += TPR) {
+    sw[peel_col(c)] = 0.f;
+    if constexpr (HAS_DB) sb[peel_col(c)] = 0.f;
+  }
+
+  const S* wr = static_cast<const S*>(a.w);
+  const BufRsrc wb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<S*>(wr), 0, (N * (int)sizeof(S) + 15) & ~15, kBufDword3);
+
+  Raw rx[2], rd[2], wa[2], wv[2];
+  S hx[2], hd[2], hw[2], tx[2], td[2], tw[2];
+  float rm[2], rr[2];
+  int hh[2];
+  auto load_row = [&](int slot, int s) {
+    const int64_t li = (int64_t)s * G + grp;
+    const bool ok = s < nsteps && li < nloc;
+    const int64_t row = b + (ok ? li : 0) * P;
+    const S* xr = static_cast<const S*>(a.x) + row * a.ldx;
+    const S* dr = static_cast<const S*>(a.dy) + row * a.lddy;
+    const int h = peel_head(xr, N);
+    const int nb = (N - h) / V;
+    const int t = N - h - nb * V;
+    hh[slot] = h;
+    const uint32_t vo = (uint32_t)((tl < nb ? tl : 0) * V) * (uint32_t)sizeof(S);
+    rx[slot] = IO::load_b_nt(buf_rsrc(xr), vo + (uint32_t)h * (uint32_t)sizeof(S), 0);
+    rd[slot] = IO::load_b_nt(buf_rsrc(dr), vo + (uint32_t)h * (uint32_t)sizeof(S), 0);
+    wa[slot] = IO::load_b(wb, vo, 0);
+    wv[slot] = IO::load_b(wb, vo + 16u, 0);
+    const int hi = tl < h ? tl : 0;
+    const int ti = t > 0 ? h + nb * V + (tl < t ? tl : 0) : 0;
+    hx[slot] = xr[hi];
+    hd[slot] = dr[hi];
+    hw[slot] = wr[hi];
+    tx[slot] = xr[ti];
+    td[slot] = dr[ti];
+    tw[slot] = wr[ti];
+    rm[slot] = a.mean[row];
+    rr[slot] = a.rstd[row];
+  };
+  load_row(0, 0);
+
+  for (int s0 = 0; s0 < nsteps; s0 += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int s = s0 + j;
+      load_row(j ^ 1, s + 1);
+      if (s >= nsteps) continue;  // block-uniform
+      const int64_t li = (int64_t)s * G + grp;
+      const bool valid = li < nloc;  // wave-uniform
+      const int h = hh[j];
+      const int nb = (N - h) / V;
+      const int t = N - h - nb * V;
+      const int t0 = h + nb * V;
+      const float mu = rm[j], rs = rr[j];
+      float xh[V], gd[V], df[V];
+      float hxh = 0.f, hgd = 0.f, hdy = 0.f, txh = 0.f, tgd = 0.f, tdy = 0.f;
+      float d1a = 0.f, d1b = 0.f, d2a = 0.f, d2b = 0.f;
+      {
+        float xf[V], wf[V];
+        IO::unpack(rx[j], xf);
+        IO::unpack(rd[j], df);
+        IO::unpack(peel_vec<D>(h, wa[j], wv[j]), wf);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          xh[e] = (xf[e] - mu) * rs;
+          gd[e] = wf[e] * df[e];
+        }
+      }
+      if (valid) {
+        if (tl < h) {
+          hxh = (to_f32<D>(hx[j]) - mu) * rs;
+          hdy = to_f32<D>(hd[j]);
+          hgd = to_f32<D>(hw[j]) * hdy;
+          d1a += hgd;
+          d2a = __builtin_fmaf(hgd, hxh, d2a);
+        }
+        if (tl < nb) {
+#pragma unroll
+          for (int e = 0; e < V; e += 2) {
+            d1a += gd[e];
+            d1b += gd[e + 1];
+            d2a = __builtin_fmaf(gd[e], xh[e], d2a);
+            d2b = __builtin_fmaf(gd[e + 1], xh[e + 1], d2b);
+          }
+        }
+        if (tl < t) {
+          txh = (to_f32<D>(tx[j]) - mu) * rs;
+          tdy = to_f32<D>(td[j]);
+          tgd = to_f32<D>(tw[j]) * tdy;
+          d1b += tgd;
+          d2b = __builtin_fmaf(tgd, txh, d2b);
+        }
+      }
+      float dots[2] = {d1a + d1b, d2a + d2b};
+      group_sum_batch<2>(dots, red + ((s & 1) * G + grp) * wpr * 2, wpr, tl);
+      if (wpr == 1) lds_barrier();  // orders the LDS sums of consecutive rows (no barrier above)
+      if (!valid) continue;
+      const float c1 = dots[0] / (float)N, c2 = dots[1] / (float)N;
+      S* dxr = static_cast<S*>(a.dx) + (b + li * P) * a.lddx;
+      auto sums = [&](int c, float dyv, float xhv) {
+        const int k = peel_col(c);
+        sw[k] = __builtin_fmaf(dyv, xhv, sw[k]);
+        if constexpr (HAS_DB) sb[k] += dyv;
+      };
+      if (tl < h) {
+        dxr[tl] = from_f32<D>(rs * ((hgd - c1) - hxh * c2));
+        sums(tl, hdy, hxh);
+      }
+      if (tl < nb) {
+        const int col = h + tl * V;
+        float o[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          o[e] = rs * ((gd[e] - c1) - xh[e] * c2);
+          sums(col + e, df[e], xh[e]);
+        }
+        const Raw out = IO::pack(o);
+        if (a.dxvec) IO::store(at(dxr, col), out);
+        else IO::store_part(at(dxr, col), out, V);
+      }
+      if (tl < t) {
+        dxr[t0 + tl] = from_f32<D>(rs * ((tgd - c1) - txh * c2));
+        sums(t0 + tl, tdy, txh);
+      }
+    }
+  }
+  lds_barrier();  // every group's last sums are in LDS
+  float* const pw = a.part + (int64_t)b * a.ldp;
+  float* const pb = a.part + (int64_t)(P + b) * a.ldp;
+  for (int c = tid; c < N; c += G * TPR) {
+    float v = sw0[peel_col(c)];
+    for (int g = 1; g < G; ++g) v += sw0[(size_t)g * stride + peel_col(c)];
+    pw[c] = v;
+    if constexpr (HAS_DB) {
+      float u = sb0[peel_col(c)];
+      for (int g = 1; g < G; ++g) u += sb0[(size_t)g * stride + peel_col(c)];
+      pb[c] = u;
     }
   }
 }

@@ -145,12 +145,17 @@ rmsnorm_status ln_fwd_impl(const void* x, int64_t ldx, const void* w, const void
 }
 
 // ---- LayerNorm backward ---------------------------------------------------------------------------
+// peel_regs_ok: rows not 16-byte aligned with x and dy rows at one offset from a 16-byte boundary
+// and w 16-byte aligned; at most one whole vector per lane (floor(N / V) <= 1024) takes the
+// peeled register kernel.
 rmsnorm_status plan_ln_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
-                           rmsnorm_variant req, Plan* p) {
+                           rmsnorm_variant req, Plan* p, bool peel_regs_ok = false) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
   int tpr, iters;
   bwd_shape(nv_wide, &tpr, &iters);
-  const bool reg_ok = wide_ok && iters <= kLnBwdRegMaxIters;
+  const int64_t nv_peel = N / vec_elems(dtype);
+  const bool peel_regs = !wide_ok && peel_regs_ok && nv_peel <= kLnBwdBlockThreads;
+  const bool reg_ok = (wide_ok && iters <= kLnBwdRegMaxIters) || peel_regs;
   rmsnorm_variant v = req;
   if (v == RMSNORM_VARIANT_AUTO) v = reg_ok ? RMSNORM_VARIANT_REGISTERS : RMSNORM_VARIANT_STREAMING;
   if (v == RMSNORM_VARIANT_LDS) return RMSNORM_ERR_UNSUPPORTED;
@@ -164,6 +169,16 @@ rmsnorm_status plan_ln_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_
     p->iters = 0;
     p->groups = 1;
     p->lds = round16(sizeof(float) * 2 * 2 * (tpr / 64));
+    return RMSNORM_OK;
+  }
+  if (!wide_ok) {  // registers on peeled rows: one vector per lane, dw and db sums in LDS
+    p->peel = true;
+    p->wide = true;
+    p->tpr = (int)clamp64(pow2_ceil(nv_peel), 64, kLnBwdBlockThreads);
+    p->iters = 1;
+    p->groups = kLnBwdBlockThreads / p->tpr;
+    p->lds = round16(sizeof(float) * 2 * (size_t)p->groups * (p->tpr / 64) * 2) +
+             2 * sizeof(float) * (size_t)p->groups * (size_t)peel_sum_floats(partial_ld(N));
     return RMSNORM_OK;
   }
   p->wide = true;
@@ -197,6 +212,7 @@ rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s)
     return p.wide ? launch(ln_bwd_stream_kernel<D, true, HAS_DB>, p.grid, block, p.lds, s, a)
                   : launch(ln_bwd_stream_kernel<D, false, HAS_DB>, p.grid, block, p.lds, s, a);
   }
+  if (p.peel) return launch(ln_bwd_peel_rows_kernel<D, HAS_DB>, p.grid, block, p.lds, s, a);
   const bool full = (int64_t)p.iters * p.tpr * Elem<D>::VEC == a.N;
   // The tail layouts and compile-time row-group widths of the RMSNorm register backward.
   const Tail tail = full ? Tail::FULL : (a.N % Elem<D>::VEC == 0 ? Tail::WHOLE : Tail::RAGGED);
@@ -275,8 +291,12 @@ rmsnorm_status ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t 
   if (workspace_bytes_given < ln_workspace_bytes(M, N)) return RMSNORM_ERR_WORKSPACE;
   const bool wide = wide_fits(dy, lddy, eb) && wide_fits(x, ldx, eb) && wide_fits(dx, lddx, eb) &&
                     aligned(w, 16);
+  // Otherwise x and dy rows at one offset from a 16-byte boundary (and w 16-byte aligned) move
+  // whole vectors between an element-wise head and tail.
+  const bool peel_regs_ok = same_row_phase(x, ldx, dy, lddy, eb) && N >= 2 * vec_elems(dtype) &&
+                            aligned(w, 16);
   Plan p;
-  if ((st = plan_ln_bwd(M, N, dtype, wide, variant, &p)) != RMSNORM_OK) return st;
+  if ((st = plan_ln_bwd(M, N, dtype, wide, variant, &p, peel_regs_ok)) != RMSNORM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t P = num_partials(M);
   float* part = static_cast<float*>(workspace);
@@ -287,6 +307,7 @@ rmsnorm_status ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t 
     a.N = (int)N; a.ldp = (int)partial_ld(N); a.P = (int)P;
     a.tpr = p.tpr; a.groups = p.groups;
     a.comp = p.variant == RMSNORM_VARIANT_STREAMING && long_chain(N, dtype, p.wide, p.tpr);
+    a.dxvec = p.peel && same_row_phase(x, ldx, dx, lddx, eb);
     st = db ? ln_bwd_by_dtype<true>(dtype, p, a, s) : ln_bwd_by_dtype<false>(dtype, p, a, s);
     if (st != RMSNORM_OK) return st;
   }

@@ -51,7 +51,9 @@ extern "C" {
  *   eps         >= 0 and finite; added to the variance under the root
  *   variant     AUTO, REGISTERS or STREAMING (LDS returns RMSNORM_ERR_UNSUPPORTED)
  * M = 0 is a no-op. 16-byte accesses need x, w and b 16-byte aligned and ldx * sizeof(T) a
- * multiple of 16; otherwise an element-wise kernel serves the call. */
+ * multiple of 16; otherwise, for N >= 2 * (16 / sizeof(T)), whole 16-byte vectors of x between a
+ * head and a tail of single elements (y as vectors when its rows sit at x's offsets from a 16-byte
+ * boundary), else an element-wise kernel. */
 rmsnorm_status layernorm_fwd(const void* x, int64_t ldx, const void* w, const void* b, void* y,
                              int64_t ldy, float* mean, float* rstd, int64_t M, int64_t N,
                              rmsnorm_dtype dtype, float eps, rmsnorm_variant variant,
@@ -72,7 +74,11 @@ size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype dtype);
  *   db           float32 [N] bias gradient, or NULL to skip it
  *   workspace    at least layernorm_bwd_workspace_bytes(M, N, dtype) bytes, 16-byte aligned;
  *                contents on entry do not matter and are clobbered
- *   variant      AUTO, REGISTERS or STREAMING (LDS returns RMSNORM_ERR_UNSUPPORTED) */
+ *   variant      AUTO, REGISTERS or STREAMING (LDS returns RMSNORM_ERR_UNSUPPORTED)
+ * 16-byte accesses need dy, x and dx 16-byte aligned with row strides a multiple of 16 bytes and w
+ * 16-byte aligned; rows that are not but whose x and dy rows sit at one offset from a 16-byte
+ * boundary, with w 16-byte aligned and N / (16 / sizeof(T)) <= 1024, take whole vectors between a
+ * head and a tail of single elements (REGISTERS); anything else the element-wise kernel. */
 rmsnorm_status layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                              const void* w, const float* mean, const float* rstd, void* dx,
                              int64_t lddx, float* dw, float* db, void* workspace,

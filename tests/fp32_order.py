@@ -15,6 +15,13 @@ of its vectors, in order; compensated (Kahan) sums once a thread holds more than
 sums with fused multiply-adds for c2 otherwise), adds them, and the 64 lanes of a wavefront are
 summed by a pairwise tree in lane order (the DPP reduction), then the wavefronts in order.
 
+Rows that are not 16-byte aligned (x and dy rows at one offset from a 16-byte boundary, at most
+1024 whole vectors a row): the peeled register kernel. Row r's whole vectors start h_r < V elements
+in (h_r from the row's address); TPR = clamp(next power of two >= N // V, 64, 1024) lanes, lane l
+holding whole vector l, lanes below h_r the head elements (first in the even accumulators) and
+lanes below t_r the tail elements (last in the odd accumulators); plain sums, fused multiply-adds
+for c2; then as above.
+
 GroupNorm (a row is a (batch, group) slice of Cg channels of S elements): each channel's elements
 are cut into chunks of at most 8192 (16-bit types) elements; a chunk's 256 threads own 4 vectors of
 8 elements each (vector it * 256 + t), keep even/odd accumulators, and the block sums them (the
@@ -86,15 +93,68 @@ def ln_row_sums(gd, xh, V: int = 8):
     return out[0], out[1]
 
 
-def ln_dx_model_bitexact(dy, x, w, mean, rstd, *, dtype: str, wide: bool = True) -> float:
+def row_heads(M: int, N: int, itemsize: int, ld: int | None = None, base: int = 0):
+    """Elements before the first 16-byte boundary of each row (at most N) for rows starting at byte
+    base + r * ld * itemsize (the kernels' peel_head)."""
+    ld = N if ld is None else ld
+    addr = base + np.arange(M, dtype=np.int64) * ld * itemsize
+    return np.minimum(((16 - addr % 16) % 16) // itemsize, N)
+
+
+def ln_row_sums_peel(gd, xh, V: int, heads):
+    """float32 sums(gd) and sums(gd * xhat) of each row in the peeled register kernel's order."""
+    M, N = gd.shape
+    tpr = int(min(max(1 << max(N // V - 1, 0).bit_length(), 64), 1024))
+    out1 = np.zeros(M, np.float32)
+    out2 = np.zeros(M, np.float32)
+    heads = np.asarray(heads)
+    for h in np.unique(heads):
+        rows = np.nonzero(heads == h)[0]
+        g, x = gd[rows], xh[rows]
+        R = len(rows)
+        nb = (N - h) // V
+        t0 = h + nb * V
+        t = N - t0
+        a1, b1, a2, b2 = (np.zeros((R, tpr), np.float32) for _ in range(4))
+        a1[:, :h] = g[:, :h]
+        a2[:, :h] = _fma(g[:, :h], x[:, :h], a2[:, :h])
+        G = g[:, h:t0].reshape(R, nb, V)
+        X = x[:, h:t0].reshape(R, nb, V)
+        for e in range(0, V, 2):
+            a1[:, :nb] = (a1[:, :nb] + G[:, :, e]).astype(np.float32)
+            b1[:, :nb] = (b1[:, :nb] + G[:, :, e + 1]).astype(np.float32)
+            a2[:, :nb] = _fma(G[:, :, e], X[:, :, e], a2[:, :nb])
+            b2[:, :nb] = _fma(G[:, :, e + 1], X[:, :, e + 1], b2[:, :nb])
+        b1[:, :t] = (b1[:, :t] + g[:, t0:]).astype(np.float32)
+        b2[:, :t] = _fma(g[:, t0:], x[:, t0:], b2[:, :t])
+        for out, (p, q) in ((out1, (a1, b1)), (out2, (a2, b2))):
+            waves = _lane_tree((p + q).astype(np.float32).reshape(R, tpr // 64, 64))
+            acc = waves[:, 0]
+            for k in range(1, waves.shape[1]):
+                acc = (acc + waves[:, k]).astype(np.float32)
+            out[rows] = acc
+    return out1, out2
+
+
+def ln_dx_model_bitexact(dy, x, w, mean, rstd, *, dtype: str, wide: bool = True,
+                         mapping: str | None = None, heads=None) -> float:
     """Fraction of dx elements that the LayerNorm kernels' float32 order of c1, c2 leaves
-    bit-identical to the oracle's dx (same mean and rstd, same elementwise steps). ``wide``: rows
-    16-byte aligned (vectors of 16 bytes); else the element-wise kernel, whose threads hold single
-    elements (vectors of one, all in the even accumulator)."""
+    bit-identical to the oracle's dx (same mean and rstd, same elementwise steps). ``mapping``:
+    "wide" (rows 16-byte aligned, vectors of 16 bytes), "elementwise" (threads hold single elements,
+    vectors of one, all in the even accumulator) or "peel" (rows not 16-byte aligned; ``heads`` the
+    rows' h, by default contiguous rows from a 16-byte aligned base); by default ``wide`` picks
+    between the first two."""
     x = np.asarray(x, np.float32)
     xh = normalize(x, mean, rstd, False).astype(np.float32)
     gd = (np.asarray(w, np.float32) * np.asarray(dy, np.float32)).astype(np.float32)
-    s1, s2 = ln_row_sums(gd, xh, (4 if dtype == "f32" else 8) if wide else 1)
+    V = 4 if dtype == "f32" else 8
+    mapping = mapping or ("wide" if wide else "elementwise")
+    if mapping == "peel":
+        if heads is None:
+            heads = row_heads(x.shape[0], x.shape[1], 4 if dtype == "f32" else 2)
+        s1, s2 = ln_row_sums_peel(gd, xh, V, heads)
+    else:
+        s1, s2 = ln_row_sums(gd, xh, V if mapping == "wide" else 1)
     n = np.float32(x.shape[-1])
     c1 = (s1 / n).astype(np.float32)[:, None]
     c2 = (s2 / n).astype(np.float32)[:, None]

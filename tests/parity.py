@@ -257,10 +257,11 @@ def check_ln_fwd(y_gpu, mean_gpu, rstd_gpu, x, w, b, *, eps, dtype) -> dict:
 
 
 def check_ln_bwd(dx_gpu, dw_gpu, db_gpu, dy, x, w, mean_gpu, rstd_gpu, *, dtype,
-                 ld=None) -> dict:
-    """``ld``: the row stride of x, dy and dx on the device (default: contiguous rows). Rows that
-    are not 16-byte aligned take the element-wise kernels, whose summation order the dx model
-    then follows."""
+                 ld=None, mapping=None) -> dict:
+    """``ld``: the row stride of x, dy and dx on the device (default: contiguous rows from a
+    16-byte aligned base). ``mapping``: the kernel family whose summation order the dx model
+    follows; by default 16-byte rows take the vector kernels, other rows of at most 1024 whole
+    vectors the peeled register kernel (w 16-byte aligned), the rest the element-wise kernels."""
     dx_o, dw_o, db_o = oracle.layernorm_bwd(dy, x, w, mean_gpu, rstd_gpu, dtype=dtype)
     if dtype == "f32":
         num = np.linalg.norm(dx_gpu.astype(np.float64) - dx_o)
@@ -268,10 +269,18 @@ def check_ln_bwd(dx_gpu, dw_gpu, db_gpu, dy, x, w, mean_gpu, rstd_gpu, *, dtype,
         stats = {"dx_normwise": float(num / den) if den > 0 else float(num)}
         assert stats["dx_normwise"] <= F32_DX_NORMWISE, stats
     else:
-        from fp32_order import ln_dx_model_bitexact
-        itemsize = 4 if dtype == "f32" else 2
-        wide = ((ld or np.shape(x)[-1]) * itemsize) % 16 == 0
-        model = ln_dx_model_bitexact(dy, x, w, mean_gpu, rstd_gpu, dtype=dtype, wide=wide)
+        from fp32_order import ln_dx_model_bitexact, row_heads
+        M, N = np.shape(x)
+        if mapping is None:
+            if ((ld or N) * 2) % 16 == 0:
+                mapping = "wide"
+            elif N >= 16 and N // 8 <= 1024:
+                mapping = "peel"
+            else:
+                mapping = "elementwise"
+        heads = row_heads(M, N, 2, ld) if mapping == "peel" else None
+        model = ln_dx_model_bitexact(dy, x, w, mean_gpu, rstd_gpu, dtype=dtype, mapping=mapping,
+                                     heads=heads)
         stats = check_floored(dx_gpu, dx_o, dtype, "dx", frac=modeled_dx_floor(model))
         stats["dx_model_bitexact"] = model
     stats.update(check_dw(dw_gpu, dw_o))

@@ -4,7 +4,9 @@ The models (tests/fp32_order.py) reproduce the kernels' float32 order of the row
 parity.py lowers the 99.9 % bit-exact bar for a case only by what its model shows. Pinned here:
 * integer inputs, whose float32 sums are exact in any order, give the exact sums;
 * the order itself: one value 2^24 among ones, where each order loses a different number of
-  them (sequential: all 63, the pairwise lane tree: one);
+  them (sequential: all 63, the pairwise lane tree: one); for rows that are not 16-byte aligned,
+  that the head element opens the even sum, and that without a head the peeled order is the
+  register kernel's;
 * the rates the bars rest on: >= 99.9 % on the LayerNorm and GroupNorm test inputs except the
   float16 rows of 70000 (and 9001 and 30001) elements with an upstream of ones (about 98.9 %, also
   the GPU's rates there).
@@ -13,7 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from fp32_order import gn_dx_model_bitexact, ln_dx_model_bitexact, ln_row_sums
+from fp32_order import (gn_dx_model_bitexact, ln_dx_model_bitexact, ln_row_sums,
+                        ln_row_sums_peel, row_heads)
 from workloads import GN_WORKLOADS, LN_WORKLOADS, make_gn_inputs, make_norm_inputs
 
 
@@ -37,6 +40,43 @@ def test_ln_row_sums_use_the_lane_tree():
     gd[0, 0] = 2.0**24
     s1, _ = ln_row_sums(gd, np.ones_like(gd))
     assert s1[0] == 2.0**24 + 62
+
+
+@pytest.mark.parametrize("N", [16, 17, 1027, 4097, 8199])
+def test_ln_row_sums_peel_are_exact_on_integer_inputs(N):
+    """Every element enters the peeled order once: integer sums are exact for rows of every
+    head offset."""
+    rng = np.random.default_rng(N)
+    gd = rng.integers(-8, 9, size=(9, N)).astype(np.float32)
+    xh = rng.integers(-8, 9, size=(9, N)).astype(np.float32)
+    heads = row_heads(9, N, 2)
+    assert len(set(heads.tolist())) > 1 or N % 8 == 0
+    s1, s2 = ln_row_sums_peel(gd, xh, 8, heads)
+    assert np.array_equal(s1, gd.astype(np.float64).sum(axis=1))
+    assert np.array_equal(s2, (gd.astype(np.float64) * xh).sum(axis=1))
+
+
+@pytest.mark.parametrize("N", [128, 1024, 4096, 8192])
+def test_ln_row_sums_peel_without_a_head_is_the_wide_order(N):
+    """Rows on a 16-byte boundary with whole vectors: one vector per lane in both mappings, so the
+    peeled order is the register kernel's."""
+    rng = np.random.default_rng(N + 1)
+    gd = rng.standard_normal((5, N)).astype(np.float32)
+    xh = rng.standard_normal((5, N)).astype(np.float32)
+    a = ln_row_sums(gd, xh, 8)
+    b = ln_row_sums_peel(gd, xh, 8, np.zeros(5, int))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_ln_row_sums_peel_head_opens_the_even_sum():
+    """N = 17, h = 3 (bf16): lane 0 holds head element 0, whole vector 0 (elements 3..10) and tail
+    element 11. With 2^24 at element 0 and ones at the vector's even positions, the head first in
+    the even sum absorbs the four ones (2^24 + 1 rounds to 2^24); in the odd sum it would not."""
+    gd = np.zeros((1, 17), np.float32)
+    gd[0, 0] = 2.0**24
+    gd[0, [3, 5, 7, 9]] = 1.0
+    s1, _ = ln_row_sums_peel(gd, np.ones_like(gd), 8, np.array([3]))
+    assert s1[0] == 2.0**24
 
 
 LN_WL = {"bf16": LN_WORKLOADS["ln_bf16_4096x4096"], "f16": LN_WORKLOADS["ln_fp16_8192x8192"]}
@@ -71,6 +111,20 @@ def test_ln_model_rates_element_wise(dtype, M, N, lo, hi):
     _, mean, rstd = oracle.layernorm_fwd(inp["x"], inp["w"], inp["b"], eps=wl.eps, dtype=dtype)
     rate = ln_dx_model_bitexact(inp["dy"], inp["x"], inp["w"], mean, rstd, dtype=dtype,
                                 wide=False)
+    assert lo <= rate <= hi, rate
+
+
+@pytest.mark.parametrize("dtype,M,N,lo,hi", [("f16", 129, 1027, 0.985, 1.0),
+                                             ("bf16", 129, 1027, 0.9995, 1.0),
+                                             ("f16", 257, 4097, 0.985, 1.0)])
+def test_ln_model_rates_peeled(dtype, M, N, lo, hi):
+    """Rows not 16-byte aligned in the peeled register kernel's order (contiguous rows: every head
+    offset occurs)."""
+    wl = LN_WL[dtype]
+    inp = make_norm_inputs(wl, M=M, N=N, seed=1)
+    _, mean, rstd = oracle.layernorm_fwd(inp["x"], inp["w"], inp["b"], eps=wl.eps, dtype=dtype)
+    rate = ln_dx_model_bitexact(inp["dy"], inp["x"], inp["w"], mean, rstd, dtype=dtype,
+                                mapping="peel")
     assert lo <= rate <= hi, rate
 
 
