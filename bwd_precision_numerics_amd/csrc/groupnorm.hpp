@@ -50,6 +50,7 @@ struct GnArgs {
   int64_t B, C, S;
   int G, Cg, K;     // groups, channels per group, chunks per (batch, channel) segment
   float eps;
+  int tpr = 0, rows = 0;  // row kernels: threads per (batch, group) row, rows per block
 };
 
 // (count, mean, M2) of a set of values; merge() is Chan et al.'s pairwise update (float32).
@@ -351,6 +352,222 @@ __global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
     if (col + V <= ch.cnt) IO::store(dxp + col, out);
     else IO::store_part(dxp + col, out, ch.cnt - col);
   }
+}
+
+// ---- (batch, group) rows that fit one row group's registers ------------------------------------
+// Many channels of a small spatial size (7 x 7 to 32 x 32, say) make rows of a few thousand
+// elements and (batch, channel) segments of a few dozen: one block per segment chunk would leave
+// each block almost no work. Rows of n = Cg * S elements up to ITERS values per lane (16-byte
+// vectors when n * sizeof(T) is a multiple of 16 and the tensors are 16-byte aligned, else single
+// elements) are instead held whole by TPR threads, a.rows rows per block (row r = b * G + g starts
+// at element r * n; element j of it belongs to channel g * Cg + j / S).
+//   forward   mean = sum(x) / n, var = sum((x - mean)^2) / n over the registers (plain float32
+//             sums: even and odd values of a lane, the lanes, then the waves in order), y from the
+//             same registers: x read once.
+//   backward  p1 = dy and p2 = fl(dy * xhat) go to LDS; each (batch, channel) segment is summed by
+//             one wavefront (lane l the segment's elements l, l + 64, ... in order, then the wave
+//             sum) into the same per-chunk pairs as the chunked kernels (one chunk per segment);
+//             c1 = sum_c w_c * (sum dy) / n and c2 likewise over the row's Cg entries in the
+//             chunked kernel's order (lane-strided, then the shuffle tree); dx from the registers.
+//             dW and dB then come from the pairs as before (gn_params_kernel).
+template <DT D, bool WIDE, int ITERS>
+struct GnRowIO {
+  using IO = VecIO<D, WIDE>;
+  using S = typename IO::S;
+  using Raw = typename IO::Raw;
+  static constexpr int V = IO::V;
+  // The lane's values of row r (zeros past n).
+  static __device__ __forceinline__ void load(const S* p, int n, int TPR, int tl, Raw (&r)[ITERS]) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int col = (it * TPR + tl) * V;
+      r[it] = IO::zero();
+      if (col + V <= n) r[it] = IO::load(p + col);
+      else if (col < n) r[it] = IO::load_part(p + col, n - col);
+    }
+  }
+};
+
+template <DT D, bool WIDE, int ITERS, bool HAS_B>
+__global__ void __launch_bounds__(1024) gn_rows_fwd_kernel(GnArgs a) {
+  using RI = GnRowIO<D, WIDE, ITERS>;
+  using IO = typename RI::IO;
+  using S = typename RI::S;
+  constexpr int V = RI::V;
+  extern __shared__ uint4 smem[];
+  const int TPR = a.tpr, wpr = TPR >> 6;
+  const int tid = threadIdx.x;
+  const int grp = wave_group(tid, TPR);
+  const int tl = tid - grp * TPR;
+  const int64_t row = (int64_t)blockIdx.x * a.rows + grp;
+  const bool valid = row < a.B * a.G;
+  const int n = a.Cg * (int)a.S;
+  float* red = reinterpret_cast<float*>(smem) + grp * 2 * wpr;
+  const S* xr = static_cast<const S*>(a.x) + (valid ? row : 0) * n;
+  typename RI::Raw r[ITERS];
+  RI::load(xr, n, TPR, tl, r);
+  float f[ITERS][V];
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    IO::unpack(r[it], f[it]);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {  // values past n are zeros
+      if (e & 1) s1 += f[it][e];
+      else s0 += f[it][e];
+    }
+  }
+  const float mean = group_sum(s0 + s1, red, wpr, tl) / (float)n;
+  float q0 = 0.f, q1 = 0.f;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float d = col + e < n ? f[it][e] - mean : 0.f;
+      if (e & 1) q1 = __builtin_fmaf(d, d, q1);
+      else q0 = __builtin_fmaf(d, d, q0);
+    }
+  }
+  const float var = group_sum(q0 + q1, red + wpr, wpr, tl) / (float)n;
+  const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
+  if (!valid) return;
+  if (tl == 0) {
+    if (a.mean) a.mean[row] = mean;
+    if (a.rstd) a.rstd[row] = rs;
+  }
+  const int g = (int)(row % a.G);
+  const S* wp = static_cast<const S*>(a.w) + (int64_t)g * a.Cg;
+  const S* bp = HAS_B ? static_cast<const S*>(a.b) + (int64_t)g * a.Cg : nullptr;
+  const int Sl = (int)a.S;
+  S* yr = static_cast<S*>(a.out) + row * n;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    if (col >= n) continue;
+    float o[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int c = (col + e < n ? col + e : col) / Sl;
+      const float xh = (f[it][e] - mean) * rs;
+      o[e] = HAS_B ? xh * to_f32<D>(wp[c]) + to_f32<D>(bp[c]) : xh * to_f32<D>(wp[c]);
+    }
+    const auto out = IO::pack(o);
+    if (col + V <= n) IO::store(yr + col, out);
+    else IO::store_part(yr + col, out, n - col);
+  }
+}
+
+// LDS of the backward row kernel, per row group: two reduction slots and the row constants
+// (4 * wpr + 2 floats, rounded to 4), the segment pairs (2 * Cg), then p1 and p2 (n each).
+__host__ __device__ inline int gn_rows_bwd_lds_floats(int wpr, int Cg, int n) {
+  return ((4 * wpr + 2 + 3) & ~3) + ((2 * Cg + 3) & ~3) + 2 * ((n + 3) & ~3);
+}
+
+template <DT D, bool WIDE, int ITERS>
+__global__ void __launch_bounds__(1024) gn_rows_bwd_kernel(GnArgs a) {
+  using RI = GnRowIO<D, WIDE, ITERS>;
+  using IO = typename RI::IO;
+  using S = typename RI::S;
+  constexpr int V = RI::V;
+  extern __shared__ uint4 smem[];
+  const int TPR = a.tpr, wpr = TPR >> 6;
+  const int tid = threadIdx.x;
+  const int grp = wave_group(tid, TPR);
+  const int tl = tid - grp * TPR;
+  const int lane = tl & 63, wave = tl >> 6;
+  const int64_t row = (int64_t)blockIdx.x * a.rows + grp;
+  const bool valid = row < a.B * a.G;
+  const int Cg = a.Cg, Sl = (int)a.S, n = Cg * Sl;
+  float* base = reinterpret_cast<float*>(smem) + (size_t)grp * gn_rows_bwd_lds_floats(wpr, Cg, n);
+  float* cst = base + 4 * wpr;                 // c1, c2
+  float* seg = base + ((4 * wpr + 2 + 3) & ~3);  // [Cg][2]
+  float* p1 = seg + ((2 * Cg + 3) & ~3);       // [n]
+  float* p2 = p1 + ((n + 3) & ~3);             // [n]
+  const int64_t r = valid ? row : 0;
+  const float mean = a.mean[r], rs = a.rstd[r];
+  typename RI::Raw rx[ITERS], rd[ITERS];
+  RI::load(static_cast<const S*>(a.x) + r * n, n, TPR, tl, rx);
+  RI::load(static_cast<const S*>(a.dy) + r * n, n, TPR, tl, rd);
+  float xh[ITERS][V], df[ITERS][V];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    float xf[V];
+    IO::unpack(rx[it], xf);
+    IO::unpack(rd[it], df[it]);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      xh[it][e] = (xf[e] - mean) * rs;
+      if (col + e < n) {
+        p1[col + e] = df[it][e];
+        p2[col + e] = df[it][e] * xh[it][e];
+      }
+    }
+  }
+  lds_barrier();
+  // one wavefront per (batch, channel) segment of the row
+  for (int k = wave; k < Cg; k += wpr) {
+    float u1 = 0.f, u2 = 0.f;
+    for (int j = lane; j < Sl; j += 64) {
+      u1 += p1[k * Sl + j];
+      u2 += p2[k * Sl + j];
+    }
+    u1 = wave_sum(u1);
+    u2 = wave_sum(u2);
+    if (lane == 0) {
+      seg[2 * k] = u1;
+      seg[2 * k + 1] = u2;
+      if (valid) a.ws[r * Cg + k] = make_float2(u1, u2);
+    }
+  }
+  lds_barrier();
+  const int g = (int)(r % a.G);
+  const S* wp = static_cast<const S*>(a.w) + (int64_t)g * Cg;
+  if (wave == 0) {
+    float u1 = 0.f, u2 = 0.f;
+    for (int e = lane; e < Cg; e += 64) {
+      const float wc = to_f32<D>(wp[e]);
+      u1 += wc * seg[2 * e];
+      u2 += wc * seg[2 * e + 1];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float o1 = __shfl_down(u1, off, 64), o2 = __shfl_down(u2, off, 64);
+      if (lane < off) {
+        u1 += o1;
+        u2 += o2;
+      }
+    }
+    if (lane == 0) {
+      cst[0] = u1 / (float)n;
+      cst[1] = u2 / (float)n;
+    }
+  }
+  lds_barrier();
+  if (!valid) return;
+  const float c1 = cst[0], c2 = cst[1];
+  S* dxr = static_cast<S*>(a.out) + row * n;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int col = (it * TPR + tl) * V;
+    if (col >= n) continue;
+    float o[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float wc = to_f32<D>(wp[(col + e < n ? col + e : col) / Sl]);
+      o[e] = rs * ((wc * df[it][e] - c1) - xh[it][e] * c2);
+    }
+    const auto out = IO::pack(o);
+    if (col + V <= n) IO::store(dxr + col, out);
+    else IO::store_part(dxr + col, out, n - col);
+  }
+}
+
+// dW and dB from the per-chunk pairs: one wavefront per channel.
+__global__ void __launch_bounds__(256) gn_params_kernel(GnArgs a) {
+  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c < a.C) gn_param_sums(a, c);
 }
 
 }  // namespace rmsn

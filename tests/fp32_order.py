@@ -22,12 +22,16 @@ holding whole vector l, lanes below h_r the head elements (first in the even acc
 lanes below t_r the tail elements (last in the odd accumulators); plain sums, fused multiply-adds
 for c2; then as above.
 
-GroupNorm (a row is a (batch, group) slice of Cg channels of S elements): each channel's elements
-are cut into chunks of at most 8192 (16-bit types) elements; a chunk's 256 threads own 4 vectors of
-8 elements each (vector it * 256 + t), keep even/odd accumulators, and the block sums them (the
-pairwise lane tree, then 4 wavefronts in order). The row constants then add w_c * chunk sum over
+GroupNorm (a row is a (batch, group) slice of Cg channels of S elements), rows of more than 8192
+elements (float32: 4096): each channel's elements are cut into chunks of at most 8192 (16-bit
+types) elements; a chunk's 256 threads own 4 vectors of 8 elements each (vector it * 256 + t), keep
+even/odd accumulators, and the block sums them (the pairwise lane tree, then 4 wavefronts in
+order). The row constants then add w_c * chunk sum over
 the row's chunks, lane-strided over 64 lanes (chunk e to lane e % 64, in order) and a halving
-shuffle tree (lane i adds lane i + 32, then + 16, ...).
+shuffle tree (lane i adds lane i + 32, then + 16, ...). Shorter rows (the row kernels): each
+(batch, channel) segment is one chunk whose sums are taken by one wavefront, lane l adding the
+segment's p1 = dy and p2 = fl(dy * xhat) at l, l + 64, ... in order (plain float32 additions), then
+the lane tree; the row constants as above.
 """
 from __future__ import annotations
 
@@ -166,39 +170,64 @@ def ln_dx_model_bitexact(dy, x, w, mean, rstd, *, dtype: str, wide: bool = True,
     return _same_frac(dx, dx_o)
 
 
-def gn_dx_model_bitexact(dy, x, w, mean, rstd, *, G: int, dtype: str) -> float:
-    """As ln_dx_model_bitexact for GroupNorm ([B, C, S] inputs, mean and rstd [B, G])."""
+def gn_uses_row_kernels(C: int, S: int, G: int, dtype: str) -> bool:
+    """(batch, group) rows of at most 8192 elements (float32: 4096) take the row kernels."""
+    return (C // G) * S <= (4096 if dtype == "f32" else 8192)
+
+
+def gn_segment_sums(p):
+    """float32 sums over the last axis of p [B, C, S] in the row kernels' segment order: lane l
+    adds elements l, l + 64, ... in order, then the 64-lane tree."""
+    B, C, S = p.shape
+    L = -(-S // 64)
+    P = np.pad(np.asarray(p, np.float32), ((0, 0), (0, 0), (0, L * 64 - S))).reshape(B, C, L, 64)
+    lanes = np.zeros((B, C, 64), np.float32)
+    for i in range(L):
+        lanes = (lanes + P[:, :, i, :]).astype(np.float32)
+    return _lane_tree(lanes)
+
+
+def gn_dx_model_bitexact(dy, x, w, mean, rstd, *, G: int, dtype: str,
+                         rows: bool | None = None) -> float:
+    """As ln_dx_model_bitexact for GroupNorm ([B, C, S] inputs, mean and rstd [B, G]). ``rows``:
+    the row kernels' segment sums (by default where the row kernels serve the shape) instead of
+    the chunked kernels'."""
     x = np.asarray(x, np.float32)
     dy = np.asarray(dy, np.float32)
     B, C, S = x.shape
     Cg = C // G
     ch = 8192 if dtype != "f32" else 4096
     V = 8 if dtype != "f32" else 4
-    K = -(-S // ch)
+    if rows is None:
+        rows = gn_uses_row_kernels(C, S, G, dtype)
+    K = 1 if rows else -(-S // ch)
     m = np.asarray(mean, np.float32).reshape(B, G)
     r = np.asarray(rstd, np.float32).reshape(B, G)
     mc = np.repeat(m, Cg, axis=1)[..., None]
     rc = np.repeat(r, Cg, axis=1)[..., None]
     xh = ((x - mc).astype(np.float32) * rc).astype(np.float32)  # [B, C, S]
-    # per-chunk sums: 256 threads x 4 vectors of V, even / odd accumulators, lane tree, 4 waves
-    pad = K * ch - S
-    D = np.pad(dy, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, 256, V)
-    X = np.pad(xh, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, 256, V)
-    a1 = b1 = a2 = b2 = np.zeros((B, C, K, 256), np.float32)
-    for it in range(4):
-        for e in range(V):
-            d, xx = D[..., it, :, e], X[..., it, :, e]
-            if e % 2:
-                b1, b2 = (b1 + d).astype(np.float32), _fma(d, xx, b2)
-            else:
-                a1, a2 = (a1 + d).astype(np.float32), _fma(d, xx, a2)
-    sums = []
-    for p, q in ((a1, b1), (a2, b2)):
-        waves = _lane_tree((p + q).astype(np.float32).reshape(B, C, K, 4, 64))
-        s = waves[..., 0]
-        for k in range(1, 4):
-            s = (s + waves[..., k]).astype(np.float32)
-        sums.append(s)  # [B, C, K]
+    if rows:
+        sums = [gn_segment_sums(p)[..., None] for p in (dy, (dy * xh).astype(np.float32))]
+    else:
+        # per-chunk sums: 256 threads x 4 vectors of V, even / odd accumulators, lane tree, 4 waves
+        pad = K * ch - S
+        D = np.pad(dy, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, 256, V)
+        X = np.pad(xh, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, 256, V)
+        a1 = b1 = a2 = b2 = np.zeros((B, C, K, 256), np.float32)
+        for it in range(4):
+            for e in range(V):
+                d, xx = D[..., it, :, e], X[..., it, :, e]
+                if e % 2:
+                    b1, b2 = (b1 + d).astype(np.float32), _fma(d, xx, b2)
+                else:
+                    a1, a2 = (a1 + d).astype(np.float32), _fma(d, xx, a2)
+        sums = []
+        for p, q in ((a1, b1), (a2, b2)):
+            waves = _lane_tree((p + q).astype(np.float32).reshape(B, C, K, 4, 64))
+            s = waves[..., 0]
+            for k in range(1, 4):
+                s = (s + waves[..., k]).astype(np.float32)
+            sums.append(s)  # [B, C, K]
     wv = np.asarray(w, np.float32)
     consts = []
     for s in sums:

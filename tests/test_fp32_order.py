@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from fp32_order import (gn_dx_model_bitexact, ln_dx_model_bitexact, ln_row_sums,
-                        ln_row_sums_peel, row_heads)
+from fp32_order import (gn_dx_model_bitexact, gn_segment_sums, ln_dx_model_bitexact,
+                        ln_row_sums, ln_row_sums_peel, row_heads)
 from workloads import GN_WORKLOADS, LN_WORKLOADS, make_gn_inputs, make_norm_inputs
 
 
@@ -155,3 +155,45 @@ def test_gn_model_on_integer_chunks_is_exact():
     mean = np.zeros((B, G), np.float32)
     rstd = np.ones((B, G), np.float32)
     assert gn_dx_model_bitexact(dy, x, w, mean, rstd, G=G, dtype="bf16") == 1.0
+
+
+def test_gn_segment_sums_order():
+    """65 elements: lane 0 adds elements 0 and 64, lanes 1..63 one each, then the pairwise lane tree.
+    With 2^24 at element 0 and ones elsewhere, lane 0 loses element 64's one and the tree's first
+    pair (2^24 + 1) loses lane 1's: 2^24 + 62 (a sequential sum would keep none of the 64 ones)."""
+    p = np.ones((1, 1, 65), np.float32)
+    p[0, 0, 0] = 2.0**24
+    assert gn_segment_sums(p)[0, 0] == 2.0**24 + 62
+
+
+@pytest.mark.parametrize("S", [1, 7, 49, 64, 65, 196, 1000])
+def test_gn_segment_sums_are_exact_on_integers(S):
+    rng = np.random.default_rng(S)
+    p = rng.integers(-8, 9, size=(3, 5, S)).astype(np.float32)
+    assert np.array_equal(gn_segment_sums(p), p.astype(np.float64).sum(axis=2))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,C,S,G", [(4, 64, 49, 8), (2, 32, 196, 8), (2, 16, 1000, 2)])
+def test_gn_model_rates_row_kernels(dtype, B, C, S, G):
+    """Rows of at most 8192 elements (the row kernels' segment sums)."""
+    wl = GN_BASE[dtype]
+    inp = make_gn_inputs(wl, B=B, C=C, S=S, seed=B * 1000 + C + S)
+    _, mean, rstd = oracle.groupnorm_fwd(inp["x"], inp["w"], inp["b"], G=G, eps=wl.eps,
+                                         dtype=dtype)
+    rate = gn_dx_model_bitexact(inp["dy"], inp["x"], inp["w"], mean, rstd, G=G, dtype=dtype,
+                                rows=True)
+    assert rate >= 0.999, rate
+
+
+def test_gn_row_model_on_integer_inputs_is_exact():
+    """Integer x, dy, w with mean 0 and rstd 1: every float32 sum in the row kernels' order is
+    exact, so the model's dx equals the oracle's everywhere."""
+    rng = np.random.default_rng(4)
+    B, C, S, G = 2, 8, 49, 2
+    x = rng.integers(-4, 5, size=(B, C, S)).astype(np.float32)
+    dy = rng.integers(-4, 5, size=(B, C, S)).astype(np.float32)
+    w = rng.integers(1, 4, size=C).astype(np.float32)
+    mean = np.zeros((B, G), np.float32)
+    rstd = np.ones((B, G), np.float32)
+    assert gn_dx_model_bitexact(dy, x, w, mean, rstd, G=G, dtype="bf16", rows=True) == 1.0

@@ -67,6 +67,13 @@ def test_gn_page_shapes(name):
     (5, 12, 1, 3),        # one element per channel
     (1, 3, 7, 3),         # one channel per group, tiny S
     (4, 64, 64, 16),
+    # rows of at most 8192 elements (float32: 4096): the row kernels
+    (32, 256, 49, 32),    # 7 x 7, 8 channels a group: rows not 16-byte aligned (element-wise)
+    (16, 128, 196, 32),   # 14 x 14
+    (8, 64, 256, 32),     # 16 x 16: 16-byte rows
+    (3, 8, 1024, 1),      # rows of 8192 elements: the largest for 16-bit types
+    (3, 8, 1025, 1),      # one element more: the chunked kernels
+    (5, 6, 500, 3),       # 1000-element rows, 1000 * 2 bytes a multiple of 16
 ])
 def test_gn_shapes(dtype, B, C, S, G):
     run_gn(BASE[dtype], B=B, C=C, S=S, G=G, seed=B * 1000 + C + S)
@@ -78,11 +85,18 @@ def test_gn_without_bias():
     assert same_bits(a[3], b[3]).all() and same_bits(a[4], b[4]).all()
 
 
-def test_gn_repeatable():
-    _, a = run_gn(BASE["bf16"], B=4, C=32, S=4096, G=8, seed=7)
-    _, b = run_gn(BASE["bf16"], B=4, C=32, S=4096, G=8, seed=7)
+@pytest.mark.parametrize("S", [4096, 49])
+def test_gn_repeatable(S):
+    _, a = run_gn(BASE["bf16"], B=4, C=32, S=S, G=8, seed=7)
+    _, b = run_gn(BASE["bf16"], B=4, C=32, S=S, G=8, seed=7)
     for u, v in zip(a, b):
         assert same_bits(u, v).all()
+
+
+def test_gn_row_kernels_without_bias():
+    _, a = run_gn(BASE["bf16"], B=8, C=64, S=49, G=16, seed=6, bias=False)
+    _, b = run_gn(BASE["bf16"], B=8, C=64, S=49, G=16, seed=6, bias=True)
+    assert same_bits(a[3], b[3]).all() and same_bits(a[4], b[4]).all()
 
 
 def test_gn_four_dim_input():
