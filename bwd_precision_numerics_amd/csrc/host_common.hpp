@@ -73,6 +73,7 @@ struct Plan {
   bool peel = false;        // streaming: rows not 16-byte aligned, whole vectors between an
                             // element-wise head and tail
   int tpr, iters, groups;
+  int sub = 0;              // register kernels on narrow rows: row groups of `sub` lanes (4 to 32)
   size_t lds;               // dynamic LDS bytes
   int64_t grid;
 };
@@ -104,6 +105,14 @@ void bwd_shape(int64_t nv, int* tpr, int* iters) {
   *iters = (int)ceil_div(nv, *tpr);
 }
 
+// Register kernels on rows of at most 32 vectors: row groups of the next power of two (at least
+// 4) lanes instead of a whole wavefront, so a wavefront holds 64 / sub rows (bf16 65536 x 128
+// forward: one row per wavefront leaves 48 of its 64 lanes idle). 0: a wavefront or more per row.
+constexpr int kMaxSubLanes = 32;
+int narrow_lanes(int64_t nv) {
+  return nv <= kMaxSubLanes ? (int)clamp64(pow2_ceil(nv), 4, kMaxSubLanes) : 0;
+}
+
 rmsnorm_status plan_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
                         rmsnorm_variant req, Plan* p, bool peel_ok = false) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
@@ -123,6 +132,7 @@ rmsnorm_status plan_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
     iters = 0;
   } else {
     p->wide = true;
+    if (v == RMSNORM_VARIANT_REGISTERS && (p->sub = narrow_lanes(nv_wide)) > 0) tpr = p->sub;
   }
   p->tpr = tpr;
   p->iters = iters;

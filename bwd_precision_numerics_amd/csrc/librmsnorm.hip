@@ -54,7 +54,7 @@ int bwd_batch(int iters) { return iters == 1 ? BwdPipe<1>::RB : BwdPipe<2>::RB; 
 // one whole vector per lane (floor(N / V) <= 1024) takes the register kernel for such rows.
 rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, bool ag,
                         rmsnorm_variant req, Plan* p, bool peel_ok = false,
-                        bool peel_regs_ok = false) {
+                        bool peel_regs_ok = false, bool narrow_ok = false) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
   int tpr, iters;
   bwd_shape(nv_wide, &tpr, &iters);
@@ -98,11 +98,21 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
     return RMSNORM_OK;
   }
   p->wide = true;
+  const int V = vec_elems(dtype);
+  if (v == RMSNORM_VARIANT_REGISTERS && narrow_ok && N % V == 0 &&
+      (p->sub = narrow_lanes(nv_wide)) > 0) {
+    // Narrow rows of whole vectors: 1024 / sub row groups of sub lanes; LDS only for the
+    // combine of the groups' dw sums.
+    p->tpr = p->sub;
+    p->iters = 1;
+    p->groups = kBwdBlockThreads / p->sub;
+    p->lds = sizeof(float) * (size_t)(p->groups / 2) * p->sub * V;
+    return RMSNORM_OK;
+  }
   p->tpr = tpr;
   p->iters = iters;
   p->groups = kBwdBlockThreads / tpr;
   const int wpr = tpr / 64;
-  const int V = vec_elems(dtype);
   size_t main_bytes;
   if (v == RMSNORM_VARIANT_LDS) {
     main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr) +
@@ -130,6 +140,19 @@ rmsnorm_status fwd_dispatch(const Plan& p, const FwdArgs& a, hipStream_t s) {
   }
   const bool lds = p.variant == RMSNORM_VARIANT_LDS;
   const bool full = tiles_row(p, a.N, Elem<D>::VEC);
+  if (p.sub > 0) {  // narrow rows: one vector per lane, row groups of p.sub lanes
+#define RMSN_FWD_SUB(SB)                                                                        \
+  (full ? launch(fwd_rows_kernel<D, 1, O, false, true, SB>, p.grid, block, p.lds, s, a)         \
+        : launch(fwd_rows_kernel<D, 1, O, false, false, SB>, p.grid, block, p.lds, s, a))
+    switch (p.sub) {
+      case 4: return RMSN_FWD_SUB(4);
+      case 8: return RMSN_FWD_SUB(8);
+      case 16: return RMSN_FWD_SUB(16);
+      case 32: return RMSN_FWD_SUB(32);
+      default: return RMSNORM_ERR_UNSUPPORTED;
+    }
+#undef RMSN_FWD_SUB
+  }
 #define RMSN_FWD_CASE(IT)                                                                   \
   case IT:                                                                                  \
     return lds    ? launch(fwd_rows_kernel<D, IT, O, true>, p.grid, block, p.lds, s, a)     \
@@ -211,6 +234,24 @@ rmsnorm_status bwd_dispatch(const Plan& p, const BwdArgs& a, hipStream_t s) {
    : wpr == 8 ? RMSN_BWD_ROWS(IT, T, 8)                                 \
               : RMSN_BWD_ROWS(IT, T, 16))
   if (p.groups * p.tpr != kBwdBlockThreads) return RMSNORM_ERR_UNSUPPORTED;
+  if (p.sub > 0) {  // narrow rows of whole vectors, one per lane
+#define RMSN_BWD_SUB(T, SB)                                                                  \
+  launch(bwd_rows_kernel<D, 1, BwdPipe<1>::DEPTH, BwdPipe<1>::RB, AG, BwdPipe<1>::KEEP, T, 0, \
+                         SB>,                                                                 \
+         p.grid, block, p.lds, s, a)
+#define RMSN_BWD_SUBT(SB) \
+  (tail == Tail::FULL ? RMSN_BWD_SUB(Tail::FULL, SB) : RMSN_BWD_SUB(Tail::WHOLE, SB))
+    if (tail == Tail::RAGGED) return RMSNORM_ERR_UNSUPPORTED;
+    switch (p.sub) {
+      case 4: return RMSN_BWD_SUBT(4);
+      case 8: return RMSN_BWD_SUBT(8);
+      case 16: return RMSN_BWD_SUBT(16);
+      case 32: return RMSN_BWD_SUBT(32);
+      default: return RMSNORM_ERR_UNSUPPORTED;
+    }
+#undef RMSN_BWD_SUBT
+#undef RMSN_BWD_SUB
+  }
   switch (p.iters) {
     case 1:
       return tail == Tail::FULL    ? RMSN_BWD_WPR(1, Tail::FULL)
@@ -331,8 +372,14 @@ rmsnorm_status bwd_rows_impl(const void* dy, int64_t lddy, const void* x, int64_
   const bool peel_ok = same_row_phase(x, ldx, dy, lddy, eb) && N >= 2 * vec_elems(dtype) &&
                        peel_sum_floats(partial_ld(N)) <= kStreamLdsAccFloats;
   const bool ag = autograd_casts(rounding, dtype);
+  // Narrow rows: the register kernel addresses a wavefront's rows, up to 15 workspace-row counts
+  // (num_partials) of strides apart, as 32-bit byte offsets from the first.
+  const int64_t ld_max = ldx > lddy ? (ldx > lddx ? ldx : lddx) : (lddy > lddx ? lddy : lddx);
+  const bool narrow_ok =
+      ((int64_t)(64 / 4 - 1) * num_partials(M) * ld_max + N) * eb <= (int64_t)INT32_MAX;
   Plan p;
-  if ((st = plan_bwd(M, N, dtype, wide, ag, variant, &p, peel_ok, aligned(w, 16))) != RMSNORM_OK)
+  if ((st = plan_bwd(M, N, dtype, wide, ag, variant, &p, peel_ok, aligned(w, 16), narrow_ok)) !=
+      RMSNORM_OK)
     return st;
   if (M == 0) return RMSNORM_OK;
 

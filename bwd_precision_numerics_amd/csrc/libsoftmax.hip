@@ -59,6 +59,8 @@ rmsnorm_status plan_sm(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok, 
   if (v == RMSNORM_VARIANT_STREAMING) {
     sm_shape(wide_ok ? nv_wide : N, max_iters, &tpr, &iters);
     iters = 0;
+  } else if (!peel && dtype != RMSNORM_DTYPE_F64 && (p->sub = narrow_lanes(nv_wide)) > 0) {
+    tpr = p->sub;  // narrow rows: segments of lanes, 64 / sub rows per wavefront
   }
   p->tpr = tpr;
   p->iters = iters;
@@ -101,9 +103,32 @@ rmsnorm_status sm_dispatch_iters(const Plan& p, const SmArgs& a, hipStream_t s) 
   return RMSNORM_ERR_UNSUPPORTED;
 }
 
+// Narrow rows on segments of p.sub lanes (float32 compute), one 16-byte vector a lane.
+template <DT D, bool FWD, int SB>
+rmsnorm_status sm_sub_launch(const Plan& p, const SmArgs& a, hipStream_t s, int block, bool full) {
+  if constexpr (!FWD)
+    return launch(softmax_bwd_kernel<D, true, 1, false, SB>, p.grid, block, p.lds, s, a);
+  else if (full)
+    return launch(softmax_fwd_kernel<D, true, 1, true, false, SB>, p.grid, block, p.lds, s, a);
+  else
+    return launch(softmax_fwd_kernel<D, true, 1, false, false, SB>, p.grid, block, p.lds, s, a);
+}
+
 template <DT D, bool FWD>
 rmsnorm_status sm_dispatch(const Plan& p, const SmArgs& a, hipStream_t s) {
   const int block = p.groups * p.tpr;
+  if constexpr (D != DT::F64) {
+    if (p.sub > 0) {
+      const bool full = (int64_t)p.sub * Elem<D>::VEC == a.N;
+      switch (p.sub) {
+        case 4: return sm_sub_launch<D, FWD, 4>(p, a, s, block, full);
+        case 8: return sm_sub_launch<D, FWD, 8>(p, a, s, block, full);
+        case 16: return sm_sub_launch<D, FWD, 16>(p, a, s, block, full);
+        case 32: return sm_sub_launch<D, FWD, 32>(p, a, s, block, full);
+        default: return RMSNORM_ERR_UNSUPPORTED;
+      }
+    }
+  }
   if constexpr (FWD) {
     constexpr int V = 16 / (int)sizeof(typename Elem<D>::S);
     if (p.variant != RMSNORM_VARIANT_STREAMING && !p.peel && (int64_t)p.iters * p.tpr * V == a.N) {

@@ -167,20 +167,36 @@ enum class Tail : int {
 // WPR > 0 fixes the row group at WPR wavefronts (TPR = 64 * WPR, 1024 / TPR groups per block) at
 // compile time, so the row indices fold and the wave sums are read in one batch; WPR = 0 takes the
 // shape from the arguments.
-template <DT D, int ITERS, int DEPTH, int RB, bool AG, bool KEEP, Tail TAIL, int WPR>
+//
+// SUB > 0: rows of at most SUB whole vectors (SUB = 4 to 32) take row groups of SUB lanes, 64 / SUB
+// rows per wavefront and 1024 / SUB per block, summed with segment_sum (bit for bit the TPR = 64
+// sums, so dx does not change). A wavefront's rows are then local indices g0 .. g0 + 64 / SUB - 1,
+// P rows apart: the buffer descriptor holds the wavefront's first row and each lane adds its own
+// row's distance, dg * P row strides (the host checks that these offsets fit in 31 bits).
+template <DT D, int ITERS, int DEPTH, int RB, bool AG, bool KEEP, Tail TAIL, int WPR, int SUB = 0>
 __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
   using Raw = typename IO::Raw;
   constexpr int V = IO::V;
   constexpr int RING = DEPTH + 1;
+  static_assert(SUB == 0 || (ITERS == 1 && TAIL != Tail::RAGGED),
+                "narrow rows: at most one whole vector per lane");
   extern __shared__ uint4 smem[];
 
-  const int TPR = WPR ? 64 * WPR : a.tpr, wpr = WPR ? WPR : TPR >> 6;
-  const int G = WPR ? 1024 / (64 * WPR) : a.groups, N = a.N;
+  const int TPR = SUB ? SUB : WPR ? 64 * WPR : a.tpr, wpr = SUB ? 1 : WPR ? WPR : TPR >> 6;
+  const int G = SUB ? 1024 / SUB : WPR ? 1024 / (64 * WPR) : a.groups, N = a.N;
   const int tid = threadIdx.x;
-  const int grp = wave_group(tid, TPR);  // wave-uniform: row indices and row pointers are scalar
+  // Row group: wave-uniform (row indices and row pointers are scalar) unless SUB; g0 is the group
+  // of the wavefront's first lane and dg = grp - g0 the lane's row within the wavefront.
+  const int grp = SUB ? tid / TPR : wave_group(tid, TPR);
+  const int g0 = SUB ? wave_group(tid & ~63, TPR) : grp;
+  const int dg = grp - g0;
   const int tl = tid - grp * TPR;
+  // Byte distance between a wavefront's consecutive rows in x, dy and dx.
+  const uint32_t dx_step = SUB ? (uint32_t)((int64_t)a.P * a.ldx * (int64_t)sizeof(S)) : 0u;
+  const uint32_t dd_step = SUB ? (uint32_t)((int64_t)a.P * a.lddy * (int64_t)sizeof(S)) : 0u;
+  const uint32_t do_step = SUB ? (uint32_t)((int64_t)a.P * a.lddx * (int64_t)sizeof(S)) : 0u;
   const int b = blockIdx.x, P = a.P;
   const int64_t nloc = block_rows(a.M, P, b);
   const int64_t span = (int64_t)G * RB;
@@ -226,17 +242,20 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
   auto load_batch = [&](int slot, int s) {
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
-      const int64_t li = ((int64_t)s * RB + k) * G + grp;
-      const bool ok = s < nsteps && li < nloc;
-      const int64_t row = b + (ok ? li : 0) * P;
-      const S* xr = ok ? static_cast<const S*>(a.x) + row * a.ldx : wr;
-      const S* dr = ok ? static_cast<const S*>(a.dy) + row * a.lddy : wr;
+      const int64_t l0 = ((int64_t)s * RB + k) * G + g0, li = l0 + dg;
+      const bool ok0 = s < nsteps && l0 < nloc, ok = s < nsteps && li < nloc;
+      const int64_t row0 = b + (ok0 ? l0 : 0) * P;
+      const S* xr = ok0 ? static_cast<const S*>(a.x) + row0 * a.ldx : wr;
+      const S* dr = ok0 ? static_cast<const S*>(a.dy) + row0 * a.lddy : wr;
       const BufRsrc xb = buf_rsrc(xr), db = buf_rsrc(dr);
-      rr[slot][k] = a.rstd[row];
+      // A lane whose own row lies past the block's share reads the wavefront's first row (or w).
+      const uint32_t ex = SUB && ok ? (uint32_t)dg * dx_step : 0u;
+      const uint32_t ed = SUB && ok ? (uint32_t)dg * dd_step : 0u;
+      rr[slot][k] = a.rstd[SUB ? b + (ok ? li : 0) * P : row0];
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
-        rx[slot][k][it] = IO::load_b_nt(xb, voff[it], 0);
-        rd[slot][k][it] = IO::load_b_nt(db, voff[it], 0);
+        rx[slot][k][it] = IO::load_b_nt(xb, voff[it] + ex, 0);
+        rd[slot][k][it] = IO::load_b_nt(db, voff[it] + ed, 0);
         if constexpr (TAIL == Tail::RAGGED) {
           // The lane holding the row's partial vector reads it element by element (zeros past
           // N); these lane-dependent loads cost this instantiation some of its rows in flight.
@@ -269,7 +288,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
           const int64_t li = ((int64_t)s * RB + k) * G + grp;
           rs[k] = rr[j][k];
           float d0 = 0.f, d1 = 0.f;
-          if (li < nloc) {  // wave-uniform
+          if (li < nloc) {  // wave-uniform unless SUB
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
               if (!live[it]) continue;
@@ -297,15 +316,21 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
           }
           dot[k] = d0 + d1;
         }
-        group_sum_batch<RB, WPR>(dot, red + ((s & 1) * G + grp) * wpr * RB, wpr, tl);
+        if constexpr (SUB > 0) {
+#pragma unroll
+          for (int k = 0; k < RB; ++k) dot[k] = segment_sum<SUB>(dot[k]);
+        } else {
+          group_sum_batch<RB, WPR>(dot, red + ((s & 1) * G + grp) * wpr * RB, wpr, tl);
+        }
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
-          const int64_t li = ((int64_t)s * RB + k) * G + grp;
+          const int64_t l0 = ((int64_t)s * RB + k) * G + g0, li = l0 + dg;
           if (li >= nloc) continue;
-          const int64_t row = b + li * P;
+          const int64_t row0 = b + l0 * P;  // l0 <= li: the wavefront's first row is valid too
           const float c = TAIL == Tail::FULL ? dot[k] * inv_n : dot[k] / (float)N;
-          S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
+          S* dxr = static_cast<S*>(a.dx) + row0 * a.lddx;
           const BufRsrc ob = buf_rsrc(dxr);
+          const uint32_t eo = SUB ? (uint32_t)dg * do_step : 0u;
 #pragma unroll
           for (int it = 0; it < ITERS; ++it) {
             if (!live[it]) continue;
@@ -326,7 +351,7 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
               }
             }
             const Raw out = IO::pack(o);
-            if (whole[it]) IO::store_b(ob, voff[it], 0, out);
+            if (whole[it]) IO::store_b(ob, voff[it] + eo, 0, out);
             else IO::store_part(at(dxr, (it * TPR + tl) * V), out, N - (it * TPR + tl) * V);
           }
         }

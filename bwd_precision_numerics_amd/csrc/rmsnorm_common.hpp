@@ -316,6 +316,28 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Sum over each aligned segment of SUB lanes (SUB = 4, 8, 16 or 32; a row group narrower than a
+// wave), every lane getting its segment's sum. The moves are wave_sum's first steps: after the
+// quad moves lane 3 of each quad holds its quad's sum, after row_shr:4 lane 7 of each 8 lanes,
+// after row_shr:8 lane 15 of each row, after row_bcast:15 into rows 1 and 3 lanes 31 and 63 their
+// halves'. A segment's last lane then holds exactly what wave_sum makes of the same lanes with
+// every other lane of the wave zero, which only goes on to add +0 to it: adding one +0 here (turns
+// a -0 sum into +0, changes nothing else) gives bit for bit wave_sum's result for a row whose
+// vectors fill only the wave's first SUB lanes. The sum is spread over the segment with a
+// cross-lane read (ds_bpermute, no LDS memory).
+template <int SUB>
+__device__ __forceinline__ float segment_sum(float v) {
+  static_assert(SUB == 4 || SUB == 8 || SUB == 16 || SUB == 32, "segment of 4 to 32 lanes");
+  v += dpp_move<0xb1, 0xf, true>(v);
+  v += dpp_move<0x4e, 0xf, true>(v);
+  if constexpr (SUB >= 8) v += dpp_move<0x114, 0xf, true>(v);
+  if constexpr (SUB >= 16) v += dpp_move<0x118, 0xf, true>(v);
+  if constexpr (SUB == 32) v += dpp_move<0x142, 0xa, false>(v);
+  const int lane = (int)__lane_id();
+  v = __shfl(v, (lane & ~(SUB - 1)) + SUB - 1, 64);
+  return v + 0.0f;
+}
+
 // Maximum over the 64 lanes with the same moves; here a lane without a source keeps its own value
 // (max(v, v) = v) instead of reading 0. Every lane gets lane 63's result.
 template <int CTRL, int ROW_MASK>
@@ -331,6 +353,20 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
   v = fmaxf(v, dpp_keep<0x143, 0xc>(v));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Maximum over each aligned segment of SUB lanes with segment_sum's moves (lanes without a source
+// keep their value), spread over the segment. Every order gives the same maximum.
+template <int SUB>
+__device__ __forceinline__ float segment_max(float v) {
+  static_assert(SUB == 4 || SUB == 8 || SUB == 16 || SUB == 32, "segment of 4 to 32 lanes");
+  v = fmaxf(v, dpp_keep<0xb1, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x4e, 0xf>(v));
+  if constexpr (SUB >= 8) v = fmaxf(v, dpp_keep<0x114, 0xf>(v));
+  if constexpr (SUB >= 16) v = fmaxf(v, dpp_keep<0x118, 0xf>(v));
+  if constexpr (SUB == 32) v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+  const int lane = (int)__lane_id();
+  return __shfl(v, (lane & ~(SUB - 1)) + SUB - 1, 64);
 }
 
 // A thread's share of a row sum in two interleaved float32 accumulators (even / odd elements of a

@@ -104,15 +104,19 @@ __device__ __forceinline__ void* out_row(void* y, int64_t row, int64_t ldy) {
 // Row held in registers (STAGE_LDS = false) or staged in LDS (true) between the two passes.
 // FULL: the host has checked N = ITERS * TPR * V (the threads' vectors tile the row exactly), and
 // the kernel carries no partial-vector code.
-template <DT D, int ITERS, Out O, bool STAGE_LDS, bool FULL = false>
+// SUB > 0: rows of at most SUB vectors (SUB = 4 to 32) take row groups of SUB lanes, 64 / SUB rows
+// per wavefront, summed with segment_sum; the lanes hold the vectors they hold at TPR = 64 and the
+// sum comes out bit for bit as wave_sum's, so rstd and y do not change, only how many lanes idle.
+template <DT D, int ITERS, Out O, bool STAGE_LDS, bool FULL = false, int SUB = 0>
 __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
   using Raw = typename IO::Raw;
   constexpr int V = IO::V;
+  static_assert(SUB == 0 || (ITERS == 1 && !STAGE_LDS), "narrow rows: one vector per lane");
   extern __shared__ uint4 smem[];
 
-  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int TPR = SUB ? SUB : a.tpr, wpr = TPR >> 6, N = a.N;
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
@@ -153,7 +157,9 @@ __global__ void __launch_bounds__(1024) fwd_rows_kernel(FwdArgs a) {
     }
     if constexpr (STAGE_LDS) stage[it * TPR + tl] = raw[it];
   }
-  const float ss = group_sum(acc0 + acc1, red, wpr, tl);
+  float ss;
+  if constexpr (SUB > 0) ss = segment_sum<SUB>(acc0 + acc1);
+  else ss = group_sum(acc0 + acc1, red, wpr, tl);
   const float rs = 1.0f / __builtin_sqrtf(ss / (float)N + a.eps);
   if (!valid) return;
   if (tl == 0 && a.rstd) a.rstd[row] = rs;

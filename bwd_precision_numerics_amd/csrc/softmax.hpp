@@ -226,7 +226,10 @@ __device__ __forceinline__ void elem_out(typename Elem<D>::S* p, typename Acc<D>
 // exp_row_normal, else the library exp. The choice is made per row from exact values, so the two
 // kernel families take the same one. LDS: three reduction slots of wpr compute-type values per
 // row group (max and -min, then the sum).
-template <DT D, bool WIDE, int ITERS, bool FULL = false, bool PEEL = false>
+// SUB > 0 (float32 compute, rows of at most SUB vectors, one per lane): row groups of SUB lanes,
+// 64 / SUB rows per wavefront, reduced with segment_max and segment_sum; each lane holds what it
+// holds at one wavefront per row and the sums keep their bits, so y does not change. No LDS.
+template <DT D, bool WIDE, int ITERS, bool FULL = false, bool PEEL = false, int SUB = 0>
 __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   using A = typename Acc<D>::A;
   using IO = NumIO<D, WIDE>;
@@ -235,8 +238,9 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
   constexpr bool F32 = sizeof(A) == 4;
   static_assert(!FULL || (ITERS > 0 && WIDE), "FULL applies to the register kernel");
   static_assert(!PEEL || (WIDE && !FULL), "PEEL takes 16-byte vectors and partial rows");
+  static_assert(SUB == 0 || (F32 && WIDE && ITERS == 1 && !PEEL), "narrow rows: one vector a lane");
   extern __shared__ uint4 smem[];
-  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int TPR = SUB ? SUB : a.tpr, wpr = TPR >> 6, N = a.N;
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
@@ -316,8 +320,14 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
         }
     }
   }
-  if constexpr (F32) group_max2(mx, nmn, red, wpr, tl);
-  else mx = group_reduce<true>(mx, red, wpr, tl);
+  if constexpr (SUB > 0) {
+    mx = segment_max<SUB>(mx);
+    nmn = segment_max<SUB>(nmn);
+  } else if constexpr (F32) {
+    group_max2(mx, nmn, red, wpr, tl);
+  } else {
+    mx = group_reduce<true>(mx, red, wpr, tl);
+  }
   const bool fast = F32 && mx + nmn < (A)kSmNormalSpan;
   auto ex = [&](auto fast_tag, A v) -> A {
     if constexpr (F32 && decltype(fast_tag)::value) return exp_row_normal(v);
@@ -372,7 +382,9 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
     else sum_pass(Flag<false>{});
     s0 = acc.total();
   }
-  const A sum = group_reduce<false>(s0 + s1, red + 2 * wpr, wpr, tl);
+  A sum;
+  if constexpr (SUB > 0) sum = segment_sum<SUB>(s0 + s1);
+  else sum = group_reduce<false>(s0 + s1, red + 2 * wpr, wpr, tl);
   if (!valid) return;
   const A r = (A)1 / sum;
   S* yr = static_cast<S*>(a.out) + row * a.ldo;
@@ -416,7 +428,8 @@ __global__ void __launch_bounds__(1024) softmax_fwd_kernel(SmArgs a) {
 // dy stay in registers) or streaming (ITERS = 0: read again for the elementwise pass). PEEL as
 // for the forward (y, dy and dx rows at one offset from a 16-byte boundary): the lane's head
 // product opens its even sum, its tail product closes its odd sum.
-template <DT D, bool WIDE, int ITERS, bool PEEL = false>
+// SUB > 0: row groups of SUB lanes on narrow rows, as in the forward.
+template <DT D, bool WIDE, int ITERS, bool PEEL = false, int SUB = 0>
 __global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
   using A = typename Acc<D>::A;
   using IO = NumIO<D, WIDE>;
@@ -424,8 +437,10 @@ __global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
   using Raw = typename IO::Raw;
   constexpr int V = IO::V;
   static_assert(!PEEL || WIDE, "PEEL takes 16-byte vectors");
+  static_assert(SUB == 0 || (sizeof(A) == 4 && WIDE && ITERS == 1 && !PEEL),
+                "narrow rows: one vector a lane");
   extern __shared__ uint4 smem[];
-  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int TPR = SUB ? SUB : a.tpr, wpr = TPR >> 6, N = a.N;
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
@@ -507,7 +522,9 @@ __global__ void __launch_bounds__(1024) softmax_bwd_kernel(SmArgs a) {
     }
     s0 = acc.total();
   }
-  const A s = group_reduce<false>(s0 + s1, red, wpr, tl);
+  A s;
+  if constexpr (SUB > 0) s = segment_sum<SUB>(s0 + s1);
+  else s = group_reduce<false>(s0 + s1, red, wpr, tl);
   if (!valid) return;
   S* xr = static_cast<S*>(a.out) + row * a.ldo;
   S* xv = xr + h;

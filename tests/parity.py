@@ -332,7 +332,13 @@ def check_gn(y_gpu, mean_gpu, rstd_gpu, dx_gpu, dw_gpu, db_gpu, x, w, b, dy, *, 
 
 
 # ---- softmax and float64 ------------------------------------------------------------------------
-SM_F32_REL = 2.0**-18   # float32 softmax: expf, the x - max rounding, sums and the division
+# float32 softmax y, relative to the exact value: the float32 difference x - max alone is off by up
+# to half an ulp of 64 <= |x - max| < 128, 2^-18, which exp turns into a relative error of 2^-18
+# (below that range less; beyond it the results are subnormal or zero, where the 1e-38 floor of the
+# comparison's denominator keeps the check absolute). On top of it: exp itself (2^-22), the
+# float32 row sum (2^-21 for trees and chains up to 32 additions deep), the reciprocal and the
+# product (2^-24 each): 2^-20 covers them.
+SM_F32_REL = 2.0**-18 + 2.0**-20
 F64_NORMWISE = 1e-10    # the candle page's bound for float64 fused kernels vs the composed formula
 
 

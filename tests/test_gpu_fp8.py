@@ -55,8 +55,8 @@ def run_fp8(dtype, M, N, *, fmt="e4m3", scale=1.0, offset=0.0, eps=1e-6, variant
     return st, yg, rg
 
 
-SHAPES = [(1, 8), (5, 1), (7, 3), (33, 64), (300, 1000), (129, 1027), (257, 3072), (64, 4096),
-          (24, 16384), (3, 70000)]
+SHAPES = [(1, 8), (5, 1), (7, 3), (33, 64), (5000, 128), (3001, 96), (300, 1000), (129, 1027),
+          (257, 3072), (64, 4096), (24, 16384), (3, 70000)]
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])

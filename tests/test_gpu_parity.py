@@ -128,6 +128,44 @@ def test_parity_many_rows_per_block_f16(M, N):
     run_case("f16", M, N, rounding="twice", seed=32)
 
 
+# Narrow rows (at most 32 vectors): the register kernels give each row a segment of 4 to 32 lanes
+# (the next power of two of its vector count), 64 / that rows per wavefront. The row counts give
+# every backward block several steps of 1024 / lanes rows with a ragged last step, so a
+# wavefront's lanes hold rows of the block's share and rows past it.
+NARROW = [("bf16", 50152, 128, None),   # 16 lanes, vectors tile the row exactly
+          ("bf16", 65869, 64, None),    # 8 lanes
+          ("bf16", 131077, 32, None),   # 4 lanes
+          ("bf16", 40000, 96, None),    # 12 vectors on 16 lanes
+          ("bf16", 20000, 200, None),   # 25 vectors on 32 lanes
+          ("f16", 20000, 256, None),    # 32 lanes
+          ("f32", 50000, 64, None),     # 16 lanes of 4 floats
+          ("f32", 30000, 128, None),    # 32 lanes
+          ("bf16", 30000, 128, 136),    # padded row stride
+          ("bf16", 30000, 100, 104)]    # partial last vector: whole-wavefront rows
+
+
+@pytest.mark.parametrize("dtype,M,N,ld", NARROW)
+@pytest.mark.parametrize("mode", ["twice", "once", "autograd"])
+def test_parity_narrow_rows(dtype, M, N, ld, mode):
+    if mode == "autograd":
+        run_case(dtype, M, N, rounding="twice", casts="autograd", ld=ld, seed=41)
+    else:
+        run_case(dtype, M, N, rounding=mode, offset=1.0 if mode == "once" else 0.0, ld=ld, seed=41)
+
+
+@pytest.mark.parametrize("dtype,M,N", [("bf16", 20000, 128), ("bf16", 33000, 64), ("f32", 9000, 64),
+                                       ("f16", 7000, 256), ("bf16", 5000, 40)])
+def test_narrow_row_segments_match_wavefront_rows(dtype, M, N):
+    """A row on a segment of lanes gets, bit for bit, the rstd, y and dx of the same row on a whole
+    wavefront (the streaming kernels keep one wavefront per row); dw within float32 rounding (its
+    per-block groups are finer)."""
+    _, reg = run_case(dtype, M, N, variant="registers", seed=42)
+    _, strm = run_case(dtype, M, N, variant="streaming", seed=42)
+    for k in range(3):
+        assert same_bits(reg[k], strm[k]).all(), k
+    assert np.linalg.norm(reg[3] - strm[3]) <= 1e-5 * np.linalg.norm(strm[3])
+
+
 @pytest.mark.parametrize("dtype,N", [("bf16", 1000), ("f16", 4096), ("bf16", 16384)])
 def test_autograd_casts_kernel_families_agree(dtype, N):
     results = {}

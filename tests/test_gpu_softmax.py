@@ -111,7 +111,8 @@ def test_softmax_peaked_and_infinite_logits():
     assert yg[3, 17] == 1.0 and np.count_nonzero(yg[3]) == 1
 
 
-@pytest.mark.parametrize("dtype,N", [("bf16", 4096), ("f32", 2048), ("bf16", 1000)])
+@pytest.mark.parametrize("dtype,N", [("bf16", 4096), ("f32", 2048), ("bf16", 1000), ("bf16", 128),
+                                     ("f32", 64), ("bf16", 96)])
 def test_softmax_exp_paths(dtype, N):
     """Rows whose span max - min straddles 87 (the bound below which every exp is a normal float32
     and the forward takes its short exp) and rows with -inf: both exp paths against the oracle, on
@@ -142,6 +143,29 @@ def test_softmax_exp_paths(dtype, N):
     for variant in ("registers", "streaming"):
         y = arr(rn.softmax_fwd(xt, variant=variant)).astype(np.float64)
         assert np.isnan(y[1]).all() and np.isfinite(y[0]).all() and np.isfinite(y[2]).all()
+
+
+# Narrow rows (at most 32 vectors, float32 compute): the register kernels give each row a segment of
+# 4 to 32 lanes, 64 / that rows per wavefront; row counts leave the last block partly empty.
+NARROW = [("bf16", 50000, 128, None), ("bf16", 70001, 64, None), ("bf16", 100003, 32, None),
+          ("bf16", 30000, 96, None), ("bf16", 20000, 200, None), ("f16", 20000, 256, None),
+          ("f32", 40000, 64, None), ("f32", 30000, 128, None), ("bf16", 30000, 128, 136),
+          ("f64", 3000, 64, None)]
+
+
+@pytest.mark.parametrize("dtype,M,N,ld", NARROW)
+def test_softmax_narrow_rows(dtype, M, N, ld):
+    run_sm(dtype, M, N, ld=ld, seed=12)
+
+
+@pytest.mark.parametrize("dtype,M,N", [("bf16", 20000, 128), ("bf16", 33000, 64),
+                                       ("f32", 9000, 64), ("f16", 7000, 256), ("bf16", 5000, 40)])
+def test_softmax_narrow_segments_match_wavefront_rows(dtype, M, N):
+    """A row on a segment of lanes (register kernels) gets the bits of the same row on a whole
+    wavefront (streaming kernels), forward and backward."""
+    _, a = run_sm(dtype, M, N, variant="registers", seed=13)
+    _, b = run_sm(dtype, M, N, variant="streaming", seed=13)
+    assert same_bits(a[0], b[0]).all() and same_bits(a[1], b[1]).all()
 
 
 # Contiguous rows of an odd width are not 16-byte aligned: whole vectors between a head and a tail

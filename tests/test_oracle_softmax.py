@@ -145,6 +145,27 @@ def test_float32_output_is_correctly_rounded():
                           oracle.rne_f32(oracle.softmax_fwd(x, dtype="f32", exact=True)))
 
 
+def test_float32_bar_covers_the_rounded_difference():
+    """The float32 softmax bar of the GPU tests, 2^-18 + 2^-20 relative: rounding x - max to float32
+    and nothing else (exact exp, sum and division, then y rounded to float32) already goes past
+    2^-18 on 64-wide rows spread up to 88 below their maximum, and stays inside the bar."""
+    from parity import SM_F32_REL
+    rng = np.random.default_rng(11)
+    rows = []
+    for sp in (50.0, 86.5, 86.99, 87.0, 87.01, 88.0, 100.0):
+        for _ in range(3):
+            r = rng.uniform(-sp, 0.0, 64).astype(np.float32)
+            rows.append(r + np.float32(rng.uniform(-5, 5)))
+    x = np.stack(rows)
+    d = (x - x.max(axis=1, keepdims=True)).astype(np.float32)  # the only float32 step
+    e = np.exp(d.astype(np.float64))
+    y = oracle.rne_f32(e / e.sum(axis=1, keepdims=True))
+    y_o = oracle.softmax_fwd(x, dtype="f32", exact=True)
+    rel = np.abs(y - y_o) / np.maximum(np.abs(y_o), 1e-38)
+    assert rel.max() > 2.0**-18
+    assert rel.max() <= SM_F32_REL
+
+
 def test_rmsnorm_f64_matches_exact_mode_for_float32_eps():
     x = _rand((5, 64), 15).astype(np.float64)
     w = _rand((64,), 16).astype(np.float64)
