@@ -76,15 +76,18 @@ __device__ __forceinline__ void add_centred_squares(const float (&f)[V], float m
 // with x, so wider rows fit one wavefront without holding three row slices in registers.
 // LDS: two reduction slots of wpr floats per row group. FULL: the host has checked
 // N = ITERS * TPR * V (the threads' vectors tile the row), and there is no partial-vector code.
-template <DT D, int ITERS, bool HAS_B, bool LATE_WB = false, bool FULL = false>
+// SUB > 0: rows of at most SUB vectors on row groups of SUB lanes (segment_sum, bit for bit the
+// one-wavefront sums), as the RMSNorm forward; no LDS.
+template <DT D, int ITERS, bool HAS_B, bool LATE_WB = false, bool FULL = false, int SUB = 0>
 __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
   using Raw = typename IO::Raw;
   constexpr int V = IO::V;
+  static_assert(SUB == 0 || (ITERS == 1 && !LATE_WB), "narrow rows: one vector per lane");
   extern __shared__ uint4 smem[];
 
-  const int TPR = a.tpr, wpr = TPR >> 6, N = a.N;
+  const int TPR = SUB ? SUB : a.tpr, wpr = TPR >> 6, N = a.N;
   const int tid = threadIdx.x;
   const int grp = tid / TPR;
   const int tl = tid - grp * TPR;
@@ -133,7 +136,10 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
       s1 += f[e + 1];
     }
   }
-  const float mean = group_sum(s0 + s1, red, wpr, tl) / (float)N;
+  float sum_x;
+  if constexpr (SUB > 0) sum_x = segment_sum<SUB>(s0 + s1);
+  else sum_x = group_sum(s0 + s1, red, wpr, tl);
+  const float mean = sum_x / (float)N;
   RowAcc q;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
@@ -142,7 +148,10 @@ __global__ void __launch_bounds__(1024) ln_fwd_rows_kernel(LnFwdArgs a) {
     IO::unpack(raw[it], f);
     add_centred_squares<V>(f, mean, FULL ? V : N - col, q, false);
   }
-  const float var = group_sum(q.total(), red + wpr, wpr, tl) / (float)N;
+  float sum_q;
+  if constexpr (SUB > 0) sum_q = segment_sum<SUB>(q.total());
+  else sum_q = group_sum(q.total(), red + wpr, wpr, tl);
+  const float var = sum_q / (float)N;
   const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
   if (!valid) return;
   if (tl == 0) {
@@ -333,7 +342,10 @@ __device__ __forceinline__ void combine_take(float (&acc)[K], const float* buf, 
 // instead of recomputing them from the raw row. TAIL and WPR as for the RMSNorm bwd_rows_kernel,
 // whose load discipline this kernel follows: every step issues its row's loads as straight-line
 // buffer loads (rows past the block's share read w), only the arithmetic and stores are guarded.
-template <DT D, int ITERS, int DEPTH, bool HAS_DB, bool KEEP, Tail TAIL, int WPR>
+// SUB > 0: narrow rows of whole vectors on row groups of SUB lanes, as the RMSNorm bwd_rows_kernel
+// (a wavefront's rows addressed from its first row's descriptor, segment_sum for the row sums);
+// the row-sum slots in LDS are laid out as for one-wavefront groups and left unused.
+template <DT D, int ITERS, int DEPTH, bool HAS_DB, bool KEEP, Tail TAIL, int WPR, int SUB = 0>
 __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   using IO = VecIO<D, true>;
   using S = typename IO::S;
@@ -342,13 +354,21 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   constexpr int RING = DEPTH + 1;
   constexpr int K = ITERS * V;
   constexpr bool EARLY = ITERS == 1;  // partial rows written in the last step
+  static_assert(SUB == 0 || (ITERS == 1 && TAIL != Tail::RAGGED && WPR == 0),
+                "narrow rows: at most one whole vector per lane");
   extern __shared__ uint4 smem[];
 
-  const int TPR = WPR ? 64 * WPR : a.tpr, wpr = WPR ? WPR : TPR >> 6;
-  const int G = WPR ? 1024 / (64 * WPR) : a.groups, N = a.N;
+  const int TPR = SUB ? SUB : WPR ? 64 * WPR : a.tpr, wpr = SUB ? 1 : WPR ? WPR : TPR >> 6;
+  const int G = SUB ? 1024 / SUB : WPR ? 1024 / (64 * WPR) : a.groups, N = a.N;
   const int tid = threadIdx.x;
-  const int grp = wave_group(tid, TPR);
+  const int grp = SUB ? tid / TPR : wave_group(tid, TPR);
+  const int g0 = SUB ? wave_group(tid & ~63, TPR) : grp;  // group of the wavefront's first lane
+  const int dg = grp - g0;
   const int tl = tid - grp * TPR;
+  // Byte distance between a wavefront's consecutive rows in x, dy and dx.
+  const uint32_t dx_step = SUB ? (uint32_t)((int64_t)a.P * a.ldx * (int64_t)sizeof(S)) : 0u;
+  const uint32_t dd_step = SUB ? (uint32_t)((int64_t)a.P * a.lddy * (int64_t)sizeof(S)) : 0u;
+  const uint32_t do_step = SUB ? (uint32_t)((int64_t)a.P * a.lddx * (int64_t)sizeof(S)) : 0u;
   const int b = blockIdx.x, P = a.P;
   const int64_t nloc = block_rows(a.M, P, b);
   const int nsteps = (int)((nloc + G - 1) / G);
@@ -390,18 +410,22 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   Raw rx[RING][ITERS], rd[RING][ITERS];
   float rm[RING], rr[RING];
   auto load_row = [&](int slot, int s) {
-    const int64_t li = (int64_t)s * G + grp;
-    const bool ok = s < nsteps && li < nloc;
-    const int64_t row = b + (ok ? li : 0) * P;
-    const S* xr = ok ? static_cast<const S*>(a.x) + row * a.ldx : wr;
-    const S* dr = ok ? static_cast<const S*>(a.dy) + row * a.lddy : wr;
+    const int64_t l0 = (int64_t)s * G + g0, li = l0 + dg;
+    const bool ok0 = s < nsteps && l0 < nloc, ok = s < nsteps && li < nloc;
+    const int64_t row0 = b + (ok0 ? l0 : 0) * P;
+    const S* xr = ok0 ? static_cast<const S*>(a.x) + row0 * a.ldx : wr;
+    const S* dr = ok0 ? static_cast<const S*>(a.dy) + row0 * a.lddy : wr;
     const BufRsrc xb = buf_rsrc(xr), db = buf_rsrc(dr);
+    // A lane whose own row lies past the block's share reads the wavefront's first row (or w).
+    const uint32_t ex = SUB && ok ? (uint32_t)dg * dx_step : 0u;
+    const uint32_t ed = SUB && ok ? (uint32_t)dg * dd_step : 0u;
+    const int64_t row = SUB ? b + (ok ? li : 0) * P : row0;
     rm[slot] = a.mean[row];
     rr[slot] = a.rstd[row];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      rx[slot][it] = IO::load_b_nt(xb, voff[it], 0);
-      rd[slot][it] = IO::load_b_nt(db, voff[it], 0);
+      rx[slot][it] = IO::load_b_nt(xb, voff[it] + ex, 0);
+      rd[slot][it] = IO::load_b_nt(db, voff[it] + ed, 0);
       if constexpr (TAIL == Tail::RAGGED) {
         const int col = (it * TPR + tl) * V;
         if (!whole[it] && live[it]) {
@@ -423,8 +447,8 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
       const int s = s0 + j;
       load_row((j + DEPTH) % RING, s + DEPTH);
       if (s < nsteps) {  // block-uniform
-        const int64_t li = (int64_t)s * G + grp;
-        const bool valid = li < nloc;  // wave-uniform
+        const int64_t l0 = (int64_t)s * G + g0, li = l0 + dg;
+        const bool valid = li < nloc;  // wave-uniform unless SUB
         const float mu = rm[j], rs = rr[j];
         float d1a = 0.f, d1b = 0.f, d2a = 0.f, d2b = 0.f;
         float kx[KEEP ? K : 1], kg[KEEP ? K : 1];
@@ -488,7 +512,12 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
             if constexpr (HAS_DB) combine_give<K>(accb, cbb, G, grp, tl, TPR);
           }
         }
-        group_sum_batch<2, WPR>(dots, red + ((s & 1) * G + grp) * wpr * 2, wpr, tl);
+        if constexpr (SUB > 0) {
+          dots[0] = segment_sum<SUB>(dots[0]);
+          dots[1] = segment_sum<SUB>(dots[1]);
+        } else {
+          group_sum_batch<2, WPR>(dots, red + ((s & 1) * G + grp) * wpr * 2, wpr, tl);
+        }
         if (last) {
           if (!(WPR > 1 || (WPR == 0 && wpr > 1))) lds_barrier();  // one-wave rows: no barrier yet
           if (swap) {
@@ -512,11 +541,12 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
           }
         }
         if (valid) {
-          const int64_t row = b + li * P;
+          const int64_t row0 = b + l0 * P;  // l0 <= li: the wavefront's first row is valid too
           const float c1 = TAIL == Tail::FULL ? dots[0] * inv_n : dots[0] / (float)N;
           const float c2 = TAIL == Tail::FULL ? dots[1] * inv_n : dots[1] / (float)N;
-          S* dxr = static_cast<S*>(a.dx) + row * a.lddx;
+          S* dxr = static_cast<S*>(a.dx) + row0 * a.lddx;
           const BufRsrc ob = buf_rsrc(dxr);
+          const uint32_t eo = SUB ? (uint32_t)dg * do_step : 0u;
 #pragma unroll
           for (int it = 0; it < ITERS; ++it) {
             if (!live[it]) continue;
@@ -537,7 +567,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
               }
             }
             const Raw out = IO::pack(o);
-            if (whole[it]) IO::store_b(ob, voff[it], 0, out);
+            if (whole[it]) IO::store_b(ob, voff[it] + eo, 0, out);
             else IO::store_part(at(dxr, (it * TPR + tl) * V), out, N - (it * TPR + tl) * V);
           }
         }

@@ -62,6 +62,8 @@ rmsnorm_status plan_ln_fwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_
     p->peel = !wide_ok && peel_ok;
     ln_fwd_shape(wide_ok || p->peel ? nv_wide : N, &tpr, &iters);
     iters = 0;
+  } else if ((p->sub = narrow_lanes(nv_wide)) > 0) {
+    tpr = p->sub;  // narrow rows: segments of lanes, 64 / sub rows per wavefront
   }
   p->tpr = tpr;
   p->iters = iters;
@@ -84,6 +86,19 @@ rmsnorm_status ln_fwd_dispatch(const Plan& p, const LnFwdArgs& a, hipStream_t s)
   // Rows that the threads' vectors tile exactly take the FULL instantiation (no partial-vector
   // code; the same arithmetic).
   const bool full = (int64_t)p.iters * p.tpr * Elem<D>::VEC == a.N;
+  if (p.sub > 0) {
+#define RMSN_LNF_SUB(SB)                                                                         \
+  (full ? launch(ln_fwd_rows_kernel<D, 1, HAS_B, false, true, SB>, p.grid, block, p.lds, s, a)   \
+        : launch(ln_fwd_rows_kernel<D, 1, HAS_B, false, false, SB>, p.grid, block, p.lds, s, a))
+    switch (p.sub) {
+      case 4: return RMSN_LNF_SUB(4);
+      case 8: return RMSN_LNF_SUB(8);
+      case 16: return RMSN_LNF_SUB(16);
+      case 32: return RMSN_LNF_SUB(32);
+      default: return RMSNORM_ERR_UNSUPPORTED;
+    }
+#undef RMSN_LNF_SUB
+  }
 #define RMSN_LNF(IT, LATE)                                                                    \
   (full ? launch(ln_fwd_rows_kernel<D, IT, HAS_B, LATE, true>, p.grid, block, p.lds, s, a)  \
         : launch(ln_fwd_rows_kernel<D, IT, HAS_B, LATE>, p.grid, block, p.lds, s, a))
@@ -148,8 +163,11 @@ rmsnorm_status ln_fwd_impl(const void* x, int64_t ldx, const void* w, const void
 // peel_regs_ok: rows not 16-byte aligned with x and dy rows at one offset from a 16-byte boundary
 // and w 16-byte aligned; at most one whole vector per lane (floor(N / V) <= 1024) takes the
 // peeled register kernel.
+// narrow_ok: a wavefront's rows on narrow rows (up to 15 workspace-row counts of strides apart)
+// are addressable as 32-bit byte offsets from its first row.
 rmsnorm_status plan_ln_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
-                           rmsnorm_variant req, Plan* p, bool peel_regs_ok = false) {
+                           rmsnorm_variant req, Plan* p, bool peel_regs_ok = false,
+                           bool narrow_ok = false) {
   const int64_t nv_wide = ceil_div(N, vec_elems(dtype));
   int tpr, iters;
   bwd_shape(nv_wide, &tpr, &iters);
@@ -182,6 +200,18 @@ rmsnorm_status plan_ln_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_
     return RMSNORM_OK;
   }
   p->wide = true;
+  const int V = vec_elems(dtype);
+  if (v == RMSNORM_VARIANT_REGISTERS && narrow_ok && N % V == 0 &&
+      (p->sub = narrow_lanes(nv_wide)) > 0) {
+    // Narrow rows of whole vectors: 1024 / sub row groups of sub lanes. LDS as for one-wavefront
+    // groups: row-sum slots (unused), then the dw and db slices of the combine.
+    p->tpr = p->sub;
+    p->iters = 1;
+    p->groups = kLnBwdBlockThreads / p->sub;
+    p->lds = round16(sizeof(float) * 4 * (size_t)p->groups) +
+             2 * sizeof(float) * (size_t)(p->groups / 2) * p->sub * V;
+    return RMSNORM_OK;
+  }
   p->tpr = tpr;
   p->iters = iters;
   p->groups = kLnBwdBlockThreads / tpr;
@@ -218,6 +248,23 @@ rmsnorm_status ln_bwd_dispatch(const Plan& p, const LnBwdArgs& a, hipStream_t s)
   const Tail tail = full ? Tail::FULL : (a.N % Elem<D>::VEC == 0 ? Tail::WHOLE : Tail::RAGGED);
   const int wpr = p.tpr / 64;
   if (block != kLnBwdBlockThreads) return RMSNORM_ERR_UNSUPPORTED;
+  if (p.sub > 0) {  // narrow rows of whole vectors, one per lane
+#define RMSN_LNB_SUB(T, SB)                                                                    \
+  launch(ln_bwd_rows_kernel<D, 1, LnBwdPipe<1>::DEPTH, HAS_DB, LnBwdPipe<1>::KEEP, T, 0, SB>, \
+         p.grid, block, p.lds, s, a)
+#define RMSN_LNB_SUBT(SB) \
+  (tail == Tail::FULL ? RMSN_LNB_SUB(Tail::FULL, SB) : RMSN_LNB_SUB(Tail::WHOLE, SB))
+    if (tail == Tail::RAGGED) return RMSNORM_ERR_UNSUPPORTED;
+    switch (p.sub) {
+      case 4: return RMSN_LNB_SUBT(4);
+      case 8: return RMSN_LNB_SUBT(8);
+      case 16: return RMSN_LNB_SUBT(16);
+      case 32: return RMSN_LNB_SUBT(32);
+      default: return RMSNORM_ERR_UNSUPPORTED;
+    }
+#undef RMSN_LNB_SUBT
+#undef RMSN_LNB_SUB
+  }
 #define RMSN_LNB(IT, T, W)                                                                      \
   launch(ln_bwd_rows_kernel<D, IT, LnBwdPipe<IT>::DEPTH, HAS_DB, LnBwdPipe<IT>::KEEP, T, W>, \
          p.grid, block, p.lds, s, a)
@@ -295,8 +342,12 @@ rmsnorm_status ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t 
   // whole vectors between an element-wise head and tail.
   const bool peel_regs_ok = same_row_phase(x, ldx, dy, lddy, eb) && N >= 2 * vec_elems(dtype) &&
                             aligned(w, 16);
+  const int64_t ld_max = ldx > lddy ? (ldx > lddx ? ldx : lddx) : (lddy > lddx ? lddy : lddx);
+  const bool narrow_ok =
+      ((int64_t)(64 / 4 - 1) * num_partials(M) * ld_max + N) * eb <= (int64_t)INT32_MAX;
   Plan p;
-  if ((st = plan_ln_bwd(M, N, dtype, wide, variant, &p, peel_regs_ok)) != RMSNORM_OK) return st;
+  if ((st = plan_ln_bwd(M, N, dtype, wide, variant, &p, peel_regs_ok, narrow_ok)) != RMSNORM_OK)
+    return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t P = num_partials(M);
   float* part = static_cast<float*>(workspace);

@@ -84,6 +84,33 @@ def test_ln_many_rows_per_block(dtype, M, N):
     run_ln(dtype, M, N, seed=33)
 
 
+# Narrow rows (at most 32 vectors): row groups of 4 to 32 lanes, 64 / that rows per wavefront,
+# several backward steps per block with a ragged last one.
+NARROW = [("bf16", 50152, 128, None), ("bf16", 65869, 64, None), ("bf16", 131077, 32, None),
+          ("bf16", 40000, 96, None), ("bf16", 20000, 200, None), ("f16", 20000, 256, None),
+          ("f32", 50000, 64, None), ("f32", 30000, 128, None), ("bf16", 30000, 128, 136),
+          ("bf16", 30000, 100, 104)]
+
+
+@pytest.mark.parametrize("dtype,M,N,ld", NARROW)
+def test_ln_narrow_rows(dtype, M, N, ld):
+    run_ln(dtype, M, N, ld=ld, seed=34)
+
+
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("dtype,M,N", [("bf16", 20000, 128), ("bf16", 33000, 64),
+                                       ("f32", 9000, 64), ("f16", 7000, 256), ("bf16", 5000, 40)])
+def test_ln_narrow_segments_match_wavefront_rows(dtype, M, N, bias):
+    """Rows on segments of lanes (register kernels) against rows on whole wavefronts (streaming):
+    y, mean, rstd and dx bit for bit; dw and db within float32 rounding (finer per-block groups)."""
+    _, reg = run_ln(dtype, M, N, variant="registers", seed=35, bias=bias)
+    _, stream = run_ln(dtype, M, N, variant="streaming", seed=35, bias=bias)
+    for k in range(4):
+        assert same_bits(reg[k], stream[k]).all(), k
+    for k in ((4, 5) if bias else (4,)):
+        assert np.linalg.norm(reg[k] - stream[k]) <= 1e-5 * np.linalg.norm(stream[k]), k
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("N", [1000, 4096, 16384])
 def test_ln_large_mean_rows(dtype, N):
