@@ -31,7 +31,8 @@ Measurement:
   and the backward rows kernel as a fraction of the two-read-one-write kernel (its traffic).
 * cpu_baseline: the CPU oracle (NumPy, one thread) on a bounded sample of the same rows.
 * rows: LayerNorm, softmax, GroupNorm and the float64 RMSNorm, forward and backward, timed the same
-  way (graph of back-to-back launches over rotating buffers), each with its own CPU oracle sample.
+  way (graph of back-to-back launches over rotating buffers), each with its own CPU oracle sample;
+  and RMSNorm, LayerNorm and softmax on many narrow rows (bf16 65536 x 128).
 * configs: every RMSNorm configuration (fp32 64 x 1024; bf16 4096 x 4096 in the other rounding
   mode; fp16 8192 x 8192; bf16 16384 x 3072 Gemma round once; bf16 M = 4096 hidden-size sweep up to
   N = 32768): step, forward and backward times, GB/s and fraction of peak per phase, on inputs
@@ -513,6 +514,92 @@ def softmax_row(torch, rn, sets, launches):
             "bwd_GBps": round(bb / tb / 1e9, 1), "fwd_bytes": fb, "bwd_bytes": bb}
 
 
+NARROW_SHAPE = (65536, 128)  # many narrow rows (per-head widths): 16 vectors of 16 bits a row
+
+
+def narrow_rows(torch, rn, launches, rotate_mib):
+    """RMSNorm (round twice), LayerNorm and softmax, forward and backward, on bf16 65536 x 128: rows
+    of 16 vectors, which the register kernels give 16 lanes each (4 rows a wavefront). Inputs drawn
+    on the device (x, dy ~ N(0, 1), w ~ U(0.9, 1.1), LayerNorm bias ~ U(-0.1, 0.1)), timed like the
+    other rows over rotating buffer sets."""
+    from workloads import WORKLOADS, make_device_inputs
+    M, N = NARROW_SHAPE
+    dev = "cuda:0"
+    wl = WORKLOADS["bf16_4096x4096"].with_(name=f"bf16_{M}x{N}", M=M, N=N)
+    inp = make_device_inputs(wl, dev)
+    n = max(4, -(-rotate_mib * 2**20 // (M * N * wl.itemsize)))
+    sets = Sets(rn, torch, wl, "twice", inp, n, dev)
+    del inp
+    lib, dt, s, ss = sets.lib, sets.dt, wl.itemsize, sets.sets
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    b = (torch.rand(N, generator=g, device=dev) * 0.2 - 0.1).to(torch.bfloat16)
+    mean = [torch.empty(M, dtype=torch.float32, device=dev) for _ in range(n)]
+    db = torch.empty(N, dtype=torch.float32, device=dev)
+    lwsb = rn.layernorm_workspace_bytes(M, N, wl.dtype)
+    lws = torch.empty(lwsb // 4, dtype=torch.float32, device=dev)
+
+    def half(k):
+        return (k + n // 2) % n
+
+    def check(st, what):
+        if st:
+            raise RuntimeError(f"{what} status {st}")
+
+    def rms_fwd(k):
+        sets.fwd(k % n)
+
+    def rms_bwd(k):
+        sets.bwd_rows(half(k))
+        sets.dw_reduce(half(k))
+
+    def ln_fwd(k):
+        t = ss[k % n]
+        check(lib.layernorm_fwd(t["x"].data_ptr(), N, sets.w.data_ptr(), b.data_ptr(),
+                                t["y"].data_ptr(), N, mean[k % n].data_ptr(),
+                                t["rstd"].data_ptr(), M, N, dt, 1e-5, 0, sets.stream()),
+              "layernorm_fwd")
+
+    def ln_bwd(k):
+        t = ss[half(k)]
+        check(lib.layernorm_bwd(t["dy"].data_ptr(), N, t["x"].data_ptr(), N, sets.w.data_ptr(),
+                                mean[half(k)].data_ptr(), t["rstd"].data_ptr(),
+                                t["dx"].data_ptr(), N, t["dw"].data_ptr(), db.data_ptr(),
+                                lws.data_ptr(), lwsb, M, N, dt, 0, sets.stream()),
+              "layernorm_bwd")
+
+    def sm_fwd(k):
+        t = ss[k % n]
+        check(lib.softmax_fwd(t["x"].data_ptr(), N, t["y"].data_ptr(), N, M, N, dt, 0,
+                              sets.stream()), "softmax_fwd")
+
+    def sm_bwd(k):
+        t = ss[half(k)]
+        check(lib.softmax_bwd(t["dy"].data_ptr(), N, t["y"].data_ptr(), N, t["dx"].data_ptr(), N,
+                              M, N, dt, 0, sets.stream()), "softmax_bwd")
+
+    mn = M * N * s
+    families = (
+        ("rmsnorm_narrow", rms_fwd, rms_bwd, wl.fwd_bytes(), wl.bwd_bytes(),
+         "rows kernel + dw reduction"),
+        ("layernorm_narrow", ln_fwd, ln_bwd, 2 * mn + 2 * N * s + 8 * M,
+         3 * mn + N * s + 8 * M + 8 * N, "rows kernel + dw and db reductions"),
+        ("softmax_narrow", sm_fwd, sm_bwd, 2 * mn, 3 * mn, None))
+    out = {}
+    for name, fwd, bwd, fb, bb, inc in families:
+        for k in range(n):
+            fwd(k)
+        torch.cuda.synchronize()
+        tf, tb = graph_time(torch, fwd, launches), graph_time(torch, bwd, launches)
+        out[name] = {"workload": wl.name, "fwd_us": round(tf * 1e6, 3),
+                     "bwd_us": round(tb * 1e6, 3), "fwd_GBps": round(fb / tf / 1e9, 1),
+                     "bwd_GBps": round(bb / tb / 1e9, 1), "fwd_bytes": fb, "bwd_bytes": bb,
+                     "buffer_sets": n}
+        if inc:
+            out[name]["bwd_includes"] = inc
+    return out
+
+
 def f64_row(torch, rn, launches, rotate_mib):
     """The float64 RMSNorm, forward and backward, at 4096 x 4096."""
     from workloads import F64_WORKLOADS, make_inputs, to_device
@@ -877,6 +964,8 @@ def main(argv=None) -> int:
         line["rows"]["groupnorm"] = groupnorm_row(torch, rn, launches, args.rotate_mib)
         torch.cuda.empty_cache()
         line["rows"]["rmsnorm_f64"] = f64_row(torch, rn, launches, args.rotate_mib)
+        torch.cuda.empty_cache()
+        line["rows"].update(narrow_rows(torch, rn, launches, args.rotate_mib))
     if "rows" in line:
         for r in line["rows"].values():
             r["fwd_frac_of_peak"] = round(r["fwd_GBps"] / PEAK_HBM_GBPS, 4)
