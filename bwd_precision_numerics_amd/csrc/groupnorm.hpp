@@ -370,6 +370,38 @@ __global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
 //             c1 = sum_c w_c * (sum dy) / n and c2 likewise over the row's Cg entries in the
 //             chunked kernel's order (lane-strided, then the shuffle tree); dx from the registers.
 //             dW and dB then come from the pairs as before (gn_params_kernel).
+// w_c (and b_c) of the elements col .. col + V - 1 of a (batch, group) row (channel = element / Sl
+// within the row): with Sl >= V a vector crosses at most one channel boundary, so one division
+// and two loads per parameter serve the vector (elements from nb on take the next channel's);
+// smaller spatial sizes divide per element. Elements past n take some channel's value, unused.
+template <DT D, int V, bool HAS_B>
+__device__ __forceinline__ void row_params(const typename Elem<D>::S* wp,
+                                           const typename Elem<D>::S* bp, int col, int n, int Sl,
+                                           int Cg, float (&wv)[V], float (&bv)[V]) {
+  if (Sl >= V) {
+    const int c0 = col / Sl, nb = (c0 + 1) * Sl - col;
+    const int c1 = c0 + 1 < Cg ? c0 + 1 : c0;
+    const float w0 = to_f32<D>(wp[c0]), w1 = to_f32<D>(wp[c1]);
+    float b0 = 0.f, b1 = 0.f;
+    if constexpr (HAS_B) {
+      b0 = to_f32<D>(bp[c0]);
+      b1 = to_f32<D>(bp[c1]);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      wv[e] = e < nb ? w0 : w1;
+      bv[e] = e < nb ? b0 : b1;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int c = (col + e < n ? col + e : col) / Sl;
+      wv[e] = to_f32<D>(wp[c]);
+      bv[e] = HAS_B ? to_f32<D>(bp[c]) : 0.f;
+    }
+  }
+}
+
 template <DT D, bool WIDE, int ITERS>
 struct GnRowIO {
   using IO = VecIO<D, WIDE>;
@@ -445,12 +477,12 @@ __global__ void __launch_bounds__(1024) gn_rows_fwd_kernel(GnArgs a) {
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
     if (col >= n) continue;
-    float o[V];
+    float o[V], wv[V], bv[V];
+    row_params<D, V, HAS_B>(wp, bp, col, n, Sl, a.Cg, wv, bv);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const int c = (col + e < n ? col + e : col) / Sl;
       const float xh = (f[it][e] - mean) * rs;
-      o[e] = HAS_B ? xh * to_f32<D>(wp[c]) + to_f32<D>(bp[c]) : xh * to_f32<D>(wp[c]);
+      o[e] = HAS_B ? xh * wv[e] + bv[e] : xh * wv[e];
     }
     const auto out = IO::pack(o);
     if (col + V <= n) IO::store(yr + col, out);
@@ -459,13 +491,20 @@ __global__ void __launch_bounds__(1024) gn_rows_fwd_kernel(GnArgs a) {
 }
 
 // LDS of the backward row kernel, per row group: two reduction slots and the row constants
-// (4 * wpr + 2 floats, rounded to 4), the segment pairs (2 * Cg), then p1 and p2 (n each).
-__host__ __device__ inline int gn_rows_bwd_lds_floats(int wpr, int Cg, int n) {
-  return ((4 * wpr + 2 + 3) & ~3) + ((2 * Cg + 3) & ~3) + 2 * ((n + 3) & ~3);
+// (4 * wpr + 2 floats, rounded to 4), the segment pairs (2 * Cg), then p1 and p2 (m each: n
+// elements, or n / V vector sums with VSEG).
+__host__ __device__ inline int gn_rows_bwd_lds_floats(int wpr, int Cg, int m) {
+  return ((4 * wpr + 2 + 3) & ~3) + ((2 * Cg + 3) & ~3) + 2 * ((m + 3) & ~3);
 }
 
-template <DT D, bool WIDE, int ITERS>
+// VSEG (16-byte vectors, S a multiple of V, so no vector straddles two channels): each lane first
+// adds the V values of each of its vectors in element order, and p1, p2 hold these vector sums
+// (n / V each): a segment's wavefront then adds S / V of them (lane l the vector sums l, l + 64,
+// ... in order, then the wave sum) instead of S single values, and the row's LDS shrinks V-fold,
+// which lets rows of up to 4 vectors a lane (bf16 32768 elements) keep their pairs in LDS.
+template <DT D, bool WIDE, int ITERS, bool VSEG = false>
 __global__ void __launch_bounds__(1024) gn_rows_bwd_kernel(GnArgs a) {
+  static_assert(!VSEG || WIDE, "vector sums need 16-byte vectors");
   using RI = GnRowIO<D, WIDE, ITERS>;
   using IO = typename RI::IO;
   using S = typename RI::S;
@@ -479,11 +518,12 @@ __global__ void __launch_bounds__(1024) gn_rows_bwd_kernel(GnArgs a) {
   const int64_t row = (int64_t)blockIdx.x * a.rows + grp;
   const bool valid = row < a.B * a.G;
   const int Cg = a.Cg, Sl = (int)a.S, n = Cg * Sl;
-  float* base = reinterpret_cast<float*>(smem) + (size_t)grp * gn_rows_bwd_lds_floats(wpr, Cg, n);
+  const int m = VSEG ? n / V : n;  // staged values per row
+  float* base = reinterpret_cast<float*>(smem) + (size_t)grp * gn_rows_bwd_lds_floats(wpr, Cg, m);
   float* cst = base + 4 * wpr;                 // c1, c2
   float* seg = base + ((4 * wpr + 2 + 3) & ~3);  // [Cg][2]
-  float* p1 = seg + ((2 * Cg + 3) & ~3);       // [n]
-  float* p2 = p1 + ((n + 3) & ~3);             // [n]
+  float* p1 = seg + ((2 * Cg + 3) & ~3);       // [m]
+  float* p2 = p1 + ((m + 3) & ~3);             // [m]
   const int64_t r = valid ? row : 0;
   const float mean = a.mean[r], rs = a.rstd[r];
   typename RI::Raw rx[ITERS], rd[ITERS];
@@ -496,22 +536,56 @@ __global__ void __launch_bounds__(1024) gn_rows_bwd_kernel(GnArgs a) {
     float xf[V];
     IO::unpack(rx[it], xf);
     IO::unpack(rd[it], df[it]);
+    float q[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       xh[it][e] = (xf[e] - mean) * rs;
-      if (col + e < n) {
-        p1[col + e] = df[it][e];
-        p2[col + e] = df[it][e] * xh[it][e];
+      q[e] = df[it][e] * xh[it][e];
+    }
+    if constexpr (VSEG) {  // n is a multiple of V: a lane's vector is whole or absent
+      if (col < n) {
+        float u1 = df[it][0], u2 = q[0];
+#pragma unroll
+        for (int e = 1; e < V; ++e) {
+          u1 += df[it][e];
+          u2 += q[e];
+        }
+        p1[col / V] = u1;
+        p2[col / V] = u2;
+      }
+      continue;
+    }
+    bool staged = false;
+    if constexpr (WIDE) {  // whole vectors: 16-byte LDS stores (p1, p2, col multiples of 4 floats)
+      if (col + V <= n) {
+#pragma unroll
+        for (int e = 0; e < V; e += 4) {
+          *reinterpret_cast<float4*>(p1 + col + e) =
+              make_float4(df[it][e], df[it][e + 1], df[it][e + 2], df[it][e + 3]);
+          *reinterpret_cast<float4*>(p2 + col + e) =
+              make_float4(q[e], q[e + 1], q[e + 2], q[e + 3]);
+        }
+        staged = true;
+      }
+    }
+    if (!staged) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (col + e < n) {
+          p1[col + e] = df[it][e];
+          p2[col + e] = q[e];
+        }
       }
     }
   }
   lds_barrier();
   // one wavefront per (batch, channel) segment of the row
+  const int ms = VSEG ? Sl / V : Sl;  // staged values per segment
   for (int k = wave; k < Cg; k += wpr) {
     float u1 = 0.f, u2 = 0.f;
-    for (int j = lane; j < Sl; j += 64) {
-      u1 += p1[k * Sl + j];
-      u2 += p2[k * Sl + j];
+    for (int j = lane; j < ms; j += 64) {
+      u1 += p1[k * ms + j];
+      u2 += p2[k * ms + j];
     }
     u1 = wave_sum(u1);
     u2 = wave_sum(u2);
@@ -552,12 +626,10 @@ __global__ void __launch_bounds__(1024) gn_rows_bwd_kernel(GnArgs a) {
   for (int it = 0; it < ITERS; ++it) {
     const int col = (it * TPR + tl) * V;
     if (col >= n) continue;
-    float o[V];
+    float o[V], wv[V], bv[V];
+    row_params<D, V, false>(wp, nullptr, col, n, Sl, Cg, wv, bv);
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const float wc = to_f32<D>(wp[(col + e < n ? col + e : col) / Sl]);
-      o[e] = rs * ((wc * df[it][e] - c1) - xh[it][e] * c2);
-    }
+    for (int e = 0; e < V; ++e) o[e] = rs * ((wv[e] * df[it][e] - c1) - xh[it][e] * c2);
     const auto out = IO::pack(o);
     if (col + V <= n) IO::store(dxr + col, out);
     else IO::store_part(dxr + col, out, n - col);

@@ -446,25 +446,52 @@ rmsnorm_status gn_by_dtype(rmsnorm_dtype dtype, const GnArgs& a, int64_t chunks,
 // multiple of 16 (chunks are whole numbers of vectors).
 bool gn_wide(const void* p, int64_t S, int eb) { return aligned(p, 16) && (S * eb) % 16 == 0; }
 
-// (batch, group) rows of at most this many elements take the row kernels (one row group holds a
-// row; one launch per forward, x read once).
-int64_t gn_rows_max(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F32 ? 4096 : 8192; }
+// (batch, group) rows held whole by one row group (one launch per forward, x read once) instead of
+// chunks, when the spatial size fits one chunk (the per-chunk pairs then hold one chunk per segment,
+// the layout the parameter sums read) and the backward's LDS for one row (p1, p2 and the segment
+// pairs, and its reduction slots, 2 * (m + Cg) + 128 floats) stays within kGnRowsLdsFloats:
+//   GN_ROWS_VEC   16-byte vectors and S a multiple of V: p1, p2 hold per-vector sums (m = n / V),
+//                 rows of up to 4 vectors a lane at 1024 lanes (n <= 32768 16-bit, 16384 float32)
+//   GN_ROWS_ELEM  otherwise p1, p2 hold single values (m = n), up to 16384 (float32 8192)
+// Several rows a block occur only for rows of at most 2048 elements, whose LDS stays below it too.
+enum GnRowsMode { GN_CHUNKS = 0, GN_ROWS_ELEM = 1, GN_ROWS_VEC = 2 };
+int64_t gn_rows_max(rmsnorm_dtype d) { return d == RMSNORM_DTYPE_F32 ? 8192 : 16384; }
+constexpr int64_t kGnRowsLdsFloats = 36864;  // 144 KiB of a compute unit's 160 KiB
+GnRowsMode gn_rows_mode(int64_t n, int64_t S, int64_t Cg, rmsnorm_dtype d, bool wide) {
+  if (S > gn_chunk_elems(d)) return GN_CHUNKS;
+  const int V = vec_elems(d);
+  if (wide && S % V == 0 && n <= 2 * gn_rows_max(d) && 2 * (n / V + Cg) + 128 <= kGnRowsLdsFloats)
+    return GN_ROWS_VEC;
+  if (n <= gn_rows_max(d) && 2 * (n + Cg) + 128 <= kGnRowsLdsFloats) return GN_ROWS_ELEM;
+  return GN_CHUNKS;
+}
 
-// Row-kernel shape: one value a lane while 1024 threads can cover the row (always for 16-byte
-// vectors: at most 1024 of them), else a power of two up to 8 single elements a lane (many threads
-// per row hide more latency than few threads with more values: bf16 (32, 256, 14 x 14), 32
-// groups, forward 7.1 -> 5.4 us and backward 11.0 -> 10.0 us against up to 4 vectors a lane);
-// threads per row and rows per block (blocks of at least 256 threads).
+// Row-kernel shape: one value a lane while 1024 threads can cover the row, else a power of two up
+// to 4 16-byte vectors or 16 single elements a lane (many threads per row hide more latency than
+// few threads with more values: bf16 (32, 256, 14 x 14), 32 groups, forward 7.1 -> 5.4 us and
+// backward 11.0 -> 10.0 us against up to 4 vectors a lane); threads per row and rows per block
+// (blocks of at least 256 threads). With 16-byte vectors, when all rows' threads would exceed one
+// full round of the device (256 compute units x 2048 threads), a row takes half the threads and
+// twice the vectors a lane (up to 4), so the whole grid is resident at once: bf16
+// (32, 256, 32 x 32), 32 groups, forward 12.6 -> 9.9 us and backward 17.1 -> 14.3 us; rows that
+// already fit keep one vector a lane ((16, 512, 16 x 16): four a lane measured 4.9 -> 5.9 us and
+// 9.2 -> 11.0 us).
+constexpr int64_t kGnRoundThreads = 256 * 2048;
 struct GnRowShape {
   int iters, tpr, rows;
-  bool wide;
+  bool wide, vseg;
 };
-GnRowShape gn_row_shape(int64_t n, bool wide, rmsnorm_dtype d) {
+GnRowShape gn_row_shape(int64_t n, GnRowsMode mode, bool wide, rmsnorm_dtype d, int64_t nrows) {
   const int64_t nv = wide ? ceil_div(n, vec_elems(d)) : n;
   GnRowShape sh;
   sh.wide = wide;
+  sh.vseg = mode == GN_ROWS_VEC;
   sh.tpr = (int)clamp64(pow2_ceil(nv), 64, 1024);
   sh.iters = (int)pow2_ceil(ceil_div(nv, sh.tpr));
+  while (wide && sh.tpr > 64 && sh.iters < 4 && nrows * sh.tpr > kGnRoundThreads) {
+    sh.tpr /= 2;
+    sh.iters = (int)pow2_ceil(ceil_div(nv, sh.tpr));
+  }
   sh.rows = sh.tpr >= 256 ? 1 : 256 / sh.tpr;
   return sh;
 }
@@ -476,15 +503,21 @@ rmsnorm_status gn_rows_fwd_launch(const GnRowShape& sh, GnArgs a, hipStream_t s)
   const int64_t grid = ceil_div(a.B * a.G, sh.rows);
   const size_t lds = sizeof(float) * 2 * (size_t)sh.rows * (sh.tpr / 64);
   const int block = sh.rows * sh.tpr;
-  if (sh.iters == 1) return launch(gn_rows_fwd_kernel<D, WIDE, 1, HAS_B>, grid, block, lds, s, a);
-  if constexpr (!WIDE) {  // single elements: up to 8 a lane
+#define RMSN_GNRF(IT) launch(gn_rows_fwd_kernel<D, WIDE, IT, HAS_B>, grid, block, lds, s, a)
+  switch (sh.iters) {
+    case 1: return RMSN_GNRF(1);
+    case 2: return RMSN_GNRF(2);
+    case 4: return RMSN_GNRF(4);
+    default: break;
+  }
+  if constexpr (!WIDE) {  // single elements: up to 16 a lane
     switch (sh.iters) {
-      case 2: return launch(gn_rows_fwd_kernel<D, false, 2, HAS_B>, grid, block, lds, s, a);
-      case 4: return launch(gn_rows_fwd_kernel<D, false, 4, HAS_B>, grid, block, lds, s, a);
-      case 8: return launch(gn_rows_fwd_kernel<D, false, 8, HAS_B>, grid, block, lds, s, a);
+      case 8: return RMSN_GNRF(8);
+      case 16: return RMSN_GNRF(16);
       default: break;
     }
   }
+#undef RMSN_GNRF
   return RMSNORM_ERR_UNSUPPORTED;
 }
 
@@ -494,19 +527,30 @@ rmsnorm_status gn_rows_bwd_launch(const GnRowShape& sh, GnArgs a, hipStream_t s)
   a.rows = sh.rows;
   const int64_t grid = ceil_div(a.B * a.G, sh.rows);
   const int n = a.Cg * (int)a.S;
+  const int m = sh.vseg ? n / Elem<D>::VEC : n;
   const size_t lds =
-      sizeof(float) * (size_t)sh.rows * gn_rows_bwd_lds_floats(sh.tpr / 64, a.Cg, n);
+      sizeof(float) * (size_t)sh.rows * gn_rows_bwd_lds_floats(sh.tpr / 64, a.Cg, m);
+  if (lds > sizeof(float) * (size_t)kGnRowsLdsFloats) return RMSNORM_ERR_UNSUPPORTED;
   const int block = sh.rows * sh.tpr;
-  rmsnorm_status st;
-  if (sh.iters == 1) st = launch(gn_rows_bwd_kernel<D, WIDE, 1>, grid, block, lds, s, a);
-  else if constexpr (!WIDE) {  // single elements: up to 8 a lane
-    if (sh.iters == 2) st = launch(gn_rows_bwd_kernel<D, false, 2>, grid, block, lds, s, a);
-    else if (sh.iters == 4) st = launch(gn_rows_bwd_kernel<D, false, 4>, grid, block, lds, s, a);
-    else if (sh.iters == 8) st = launch(gn_rows_bwd_kernel<D, false, 8>, grid, block, lds, s, a);
-    else return RMSNORM_ERR_UNSUPPORTED;
-  } else {
-    return RMSNORM_ERR_UNSUPPORTED;
+  rmsnorm_status st = RMSNORM_ERR_UNSUPPORTED;
+#define RMSN_GNRB(IT, VS) launch(gn_rows_bwd_kernel<D, WIDE, IT, VS>, grid, block, lds, s, a)
+  if constexpr (WIDE) {  // 16-byte vectors: up to 4 a lane, vector or single-value pairs
+    if (sh.vseg) {
+      if (sh.iters == 1) st = RMSN_GNRB(1, true);
+      else if (sh.iters == 2) st = RMSN_GNRB(2, true);
+      else if (sh.iters == 4) st = RMSN_GNRB(4, true);
+    } else {
+      if (sh.iters == 1) st = RMSN_GNRB(1, false);
+      else if (sh.iters == 2) st = RMSN_GNRB(2, false);
+    }
+  } else {  // single elements: up to 16 a lane
+    if (sh.iters == 1) st = RMSN_GNRB(1, false);
+    else if (sh.iters == 2) st = RMSN_GNRB(2, false);
+    else if (sh.iters == 4) st = RMSN_GNRB(4, false);
+    else if (sh.iters == 8) st = RMSN_GNRB(8, false);
+    else if (sh.iters == 16) st = RMSN_GNRB(16, false);
   }
+#undef RMSN_GNRB
   if (st != RMSNORM_OK) return st;
   return launch(gn_params_kernel, ceil_div(a.C, 4), 256, 0, s, a);
 }
@@ -543,10 +587,10 @@ rmsnorm_status gn_fwd_impl(const void* x, const void* w, const void* b, void* y,
   a.x = x; a.w = w; a.b = b; a.out = y; a.mean = mean; a.rstd = rstd; a.eps = eps;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t n = (C / G) * S;
-  if (n <= gn_rows_max(dtype)) {
-    const bool rwide = aligned(x, 16) && aligned(y, 16) && (n * eb) % 16 == 0;
-    return gn_rows_by_dtype<true>(dtype, gn_row_shape(n, rwide, dtype), a, s);
-  }
+  const bool rwide = aligned(x, 16) && aligned(y, 16) && (n * eb) % 16 == 0;
+  const GnRowsMode mode = gn_rows_mode(n, S, C / G, dtype, rwide);
+  if (mode != GN_CHUNKS)
+    return gn_rows_by_dtype<true>(dtype, gn_row_shape(n, mode, rwide, dtype, B * G), a, s);
   const bool wide = gn_wide(x, S, eb) && gn_wide(y, S, eb);
   return wide ? gn_by_dtype<true, true>(dtype, a, chunks, s)
               : gn_by_dtype<true, false>(dtype, a, chunks, s);
@@ -578,10 +622,10 @@ rmsnorm_status gn_bwd_impl(const void* dy, const void* x, const void* w, const f
   a.x = x; a.dy = dy; a.w = w; a.out = dx; a.dw = dw; a.db = db;
   a.mean = const_cast<float*>(mean); a.rstd = const_cast<float*>(rstd);
   const int64_t n = (C / G) * S;
-  if (n <= gn_rows_max(dtype)) {  // one chunk per segment (K = 1): the pairs' layout is shared
-    const bool rwide = aligned(x, 16) && aligned(dy, 16) && aligned(dx, 16) && (n * eb) % 16 == 0;
-    return gn_rows_by_dtype<false>(dtype, gn_row_shape(n, rwide, dtype), a, s);
-  }
+  const bool rwide = aligned(x, 16) && aligned(dy, 16) && aligned(dx, 16) && (n * eb) % 16 == 0;
+  const GnRowsMode mode = gn_rows_mode(n, S, C / G, dtype, rwide);
+  if (mode != GN_CHUNKS)  // one chunk per segment (K = 1): the pairs' layout is shared
+    return gn_rows_by_dtype<false>(dtype, gn_row_shape(n, mode, rwide, dtype, B * G), a, s);
   const bool wide = gn_wide(x, S, eb) && gn_wide(dy, S, eb) && gn_wide(dx, S, eb);
   return wide ? gn_by_dtype<false, true>(dtype, a, chunks, s)
               : gn_by_dtype<false, false>(dtype, a, chunks, s);

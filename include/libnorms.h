@@ -98,12 +98,15 @@ rmsnorm_status layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_
  * sums over the n = Cg * S elements of a row, in float32 (Liger-Kernel pull request 1608). The
  * work is split into chunks of one (batch, channel) segment (at most 8192 elements for 16-bit types,
  * 4096 for float32); per-chunk statistics and sums go to a caller-provided float32 workspace and are
- * combined in a fixed order, so results are bit-reproducible and no atomics are used. Rows of at
- * most 8192 elements (4096 for float32) are instead held whole by one group of threads (statistics
- * from one read of x; in the backward each segment's sums go to the same workspace pairs, one per
- * segment). Group sizes up to RMSNORM_MAX_N elements are supported. S * sizeof(T) (rows of at
- * most 8192 elements: Cg * S * sizeof(T)) a multiple of 16 with 16-byte-aligned tensors gives
- * 16-byte accesses; anything else takes element-wise kernels. mean and rstd are float32 [B, G]. */
+ * combined in a fixed order, so results are bit-reproducible and no atomics are used. Rows whose S
+ * fits one chunk are instead held whole by one group of threads (statistics from one read of x; in
+ * the backward each segment's sums go to the same workspace pairs, one per segment) when they have
+ * at most 32768 elements (16384 for float32) with 16-byte accesses and S a multiple of the
+ * 16-byte vector, else at most 16384 (8192), and the backward's 2 * (m + Cg) + 128 floats of LDS
+ * (m = n / vector or n staged values) fit 144 KiB. Group sizes up to RMSNORM_MAX_N elements are
+ * supported. S * sizeof(T) (rows held whole: Cg * S * sizeof(T)) a multiple of 16 with
+ * 16-byte-aligned tensors gives 16-byte accesses; anything else takes element-wise kernels. mean
+ * and rstd are float32 [B, G]. */
 
 /* Bytes of workspace groupnorm_fwd and groupnorm_bwd need (the same for both): 8 bytes per chunk.
  * A pure function of the shape and dtype; 0 for invalid shapes. */

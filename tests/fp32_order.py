@@ -170,17 +170,48 @@ def ln_dx_model_bitexact(dy, x, w, mean, rstd, *, dtype: str, wide: bool = True,
     return _same_frac(dx, dx_o)
 
 
+def gn_row_kernel_mode(C: int, S: int, G: int, dtype: str):
+    """Which kernels serve a GroupNorm shape (16-byte aligned contiguous tensors): "vector" (row
+    kernels whose segment sums add per-vector sums: 16-byte rows, S a multiple of the vector, rows
+    of up to 32768 elements, float32 16384), "element" (row kernels adding single values: rows of up
+    to 16384, float32 8192), or None (the chunked kernels). Both row modes need S within one chunk
+    (8192 elements, float32 4096) and the backward's LDS, 2 * (m + Cg) + 128 floats for m staged
+    values a row, within 36864."""
+    f32 = dtype == "f32"
+    V = 4 if f32 else 8
+    Cg = C // G
+    n = Cg * S
+    rmax = 8192 if f32 else 16384
+    if S > (4096 if f32 else 8192):
+        return None
+    wide = (n * (4 if f32 else 2)) % 16 == 0
+    if wide and S % V == 0 and n <= 2 * rmax and 2 * (n // V + Cg) + 128 <= 36864:
+        return "vector"
+    if n <= rmax and 2 * (n + Cg) + 128 <= 36864:
+        return "element"
+    return None
+
+
 def gn_uses_row_kernels(C: int, S: int, G: int, dtype: str) -> bool:
-    """(batch, group) rows of at most 8192 elements (float32: 4096) take the row kernels."""
-    return (C // G) * S <= (4096 if dtype == "f32" else 8192)
+    """Whether the row kernels serve the shape (gn_row_kernel_mode)."""
+    return gn_row_kernel_mode(C, S, G, dtype) is not None
 
 
-def gn_segment_sums(p):
+def gn_segment_sums(p, V: int = 1):
     """float32 sums over the last axis of p [B, C, S] in the row kernels' segment order: lane l
-    adds elements l, l + 64, ... in order, then the 64-lane tree."""
+    adds values l, l + 64, ... in order, then the 64-lane tree. V > 1 (the "vector" mode): the
+    values are first the per-vector sums, each vector's V elements added in element order."""
+    p = np.asarray(p, np.float32)
+    if V > 1:
+        B, C, S = p.shape
+        q = p.reshape(B, C, S // V, V)
+        acc = q[..., 0]
+        for e in range(1, V):
+            acc = (acc + q[..., e]).astype(np.float32)
+        p = acc
     B, C, S = p.shape
     L = -(-S // 64)
-    P = np.pad(np.asarray(p, np.float32), ((0, 0), (0, 0), (0, L * 64 - S))).reshape(B, C, L, 64)
+    P = np.pad(p, ((0, 0), (0, 0), (0, L * 64 - S))).reshape(B, C, L, 64)
     lanes = np.zeros((B, C, 64), np.float32)
     for i in range(L):
         lanes = (lanes + P[:, :, i, :]).astype(np.float32)
@@ -188,10 +219,11 @@ def gn_segment_sums(p):
 
 
 def gn_dx_model_bitexact(dy, x, w, mean, rstd, *, G: int, dtype: str,
-                         rows: bool | None = None) -> float:
+                         rows: bool | str | None = None) -> float:
     """As ln_dx_model_bitexact for GroupNorm ([B, C, S] inputs, mean and rstd [B, G]). ``rows``:
-    the row kernels' segment sums (by default where the row kernels serve the shape) instead of
-    the chunked kernels'."""
+    None takes the kernels that serve the shape (gn_row_kernel_mode); False the chunked kernels'
+    sums; True the row kernels' ("vector" when S is a multiple of the vector, else "element");
+    or the mode itself."""
     x = np.asarray(x, np.float32)
     dy = np.asarray(dy, np.float32)
     B, C, S = x.shape
@@ -199,7 +231,11 @@ def gn_dx_model_bitexact(dy, x, w, mean, rstd, *, G: int, dtype: str,
     ch = 8192 if dtype != "f32" else 4096
     V = 8 if dtype != "f32" else 4
     if rows is None:
-        rows = gn_uses_row_kernels(C, S, G, dtype)
+        rows = gn_row_kernel_mode(C, S, G, dtype)
+    elif rows is True:
+        rows = "vector" if S % V == 0 else "element"
+    elif rows is False:
+        rows = None
     K = 1 if rows else -(-S // ch)
     m = np.asarray(mean, np.float32).reshape(B, G)
     r = np.asarray(rstd, np.float32).reshape(B, G)
@@ -207,7 +243,8 @@ def gn_dx_model_bitexact(dy, x, w, mean, rstd, *, G: int, dtype: str,
     rc = np.repeat(r, Cg, axis=1)[..., None]
     xh = ((x - mc).astype(np.float32) * rc).astype(np.float32)  # [B, C, S]
     if rows:
-        sums = [gn_segment_sums(p)[..., None] for p in (dy, (dy * xh).astype(np.float32))]
+        vs = V if rows == "vector" else 1
+        sums = [gn_segment_sums(p, vs)[..., None] for p in (dy, (dy * xh).astype(np.float32))]
     else:
         # per-chunk sums: 256 threads x 4 vectors of V, even / odd accumulators, lane tree, 4 waves
         pad = K * ch - S

@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from fp32_order import (gn_dx_model_bitexact, gn_segment_sums, ln_dx_model_bitexact,
+from fp32_order import (gn_dx_model_bitexact, gn_row_kernel_mode, gn_segment_sums,
+                        ln_dx_model_bitexact,
                         ln_row_sums, ln_row_sums_peel, row_heads)
 from workloads import GN_WORKLOADS, LN_WORKLOADS, make_gn_inputs, make_norm_inputs
 
@@ -173,10 +174,47 @@ def test_gn_segment_sums_are_exact_on_integers(S):
     assert np.array_equal(gn_segment_sums(p), p.astype(np.float64).sum(axis=2))
 
 
+def test_gn_vector_segment_sums_order():
+    """The "vector" mode adds each vector's 8 values in element order before the lanes: with 2^24
+    at element 0 and ones at elements 1..7, every one is lost against 2^24 (2^24 + 1 rounds back
+    to 2^24); one value a lane instead keeps six of them (the tree adds lanes 0 and 1 first, which
+    loses one, then the other ones in pairs)."""
+    p = np.zeros((1, 1, 16), np.float32)
+    p[0, 0, 0] = 2.0**24
+    p[0, 0, 1:8] = 1.0
+    assert gn_segment_sums(p, 8)[0, 0] == 2.0**24
+    assert gn_segment_sums(p)[0, 0] == 2.0**24 + 6
+
+
+@pytest.mark.parametrize("S", [8, 64, 72, 200, 1000, 8192])
+def test_gn_vector_segment_sums_are_exact_on_integers(S):
+    rng = np.random.default_rng(S + 1)
+    p = rng.integers(-8, 9, size=(2, 3, S)).astype(np.float32)
+    assert np.array_equal(gn_segment_sums(p, 8), p.astype(np.float64).sum(axis=2))
+    assert np.array_equal(gn_segment_sums(p, 4), p.astype(np.float64).sum(axis=2))
+
+
+@pytest.mark.parametrize("B,C,S,G,dtype,mode", [
+    (2, 8, 8192, 2, "bf16", "vector"), (2, 8, 8192, 2, "f32", None),
+    (2, 16, 1024, 1, "bf16", "vector"), (2, 16, 1024, 1, "f32", "vector"),
+    (2, 16, 1025, 1, "bf16", None), (3, 8, 1025, 1, "bf16", "element"),
+    (2, 32, 1024, 1, "bf16", "vector"), (2, 32, 1024, 1, "f32", None),
+    (4, 64, 49, 8, "bf16", "element"), (4, 1280, 16, 32, "f32", "vector"),
+    (2, 12, 1111, 1, "f16", "element"), (1, 4096, 4, 1, "bf16", None),
+    (2, 64, 10, 4, "bf16", "element"), (2, 64, 10, 4, "f32", "element"),
+    (2, 64, 12, 4, "f32", "vector"), (1, 8, 4097, 1, "f32", None)])
+def test_gn_kernel_modes(B, C, S, G, dtype, mode):
+    """Which kernels serve a shape: rows of up to 32768 (float32 16384) 16-byte elements in channels
+    of whole vectors ("vector"), up to 16384 (8192) otherwise ("element"), within one chunk of
+    spatial size and 144 KiB of backward LDS; the chunked kernels beyond (None)."""
+    assert gn_row_kernel_mode(C, S, G, dtype) == mode
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("B,C,S,G", [(4, 64, 49, 8), (2, 32, 196, 8), (2, 16, 1000, 2)])
+@pytest.mark.parametrize("B,C,S,G", [(4, 64, 49, 8), (2, 32, 196, 8), (2, 16, 1000, 2),
+                                     (2, 16, 1024, 1), (4, 320, 16, 32)])
 def test_gn_model_rates_row_kernels(dtype, B, C, S, G):
-    """Rows of at most 8192 elements (the row kernels' segment sums)."""
+    """Rows held by one row group (the row kernels' segment sums, by value or by vector)."""
     wl = GN_BASE[dtype]
     inp = make_gn_inputs(wl, B=B, C=C, S=S, seed=B * 1000 + C + S)
     _, mean, rstd = oracle.groupnorm_fwd(inp["x"], inp["w"], inp["b"], G=G, eps=wl.eps,
@@ -197,3 +235,6 @@ def test_gn_row_model_on_integer_inputs_is_exact():
     mean = np.zeros((B, G), np.float32)
     rstd = np.ones((B, G), np.float32)
     assert gn_dx_model_bitexact(dy, x, w, mean, rstd, G=G, dtype="bf16", rows=True) == 1.0
+    x64 = rng.integers(-4, 5, size=(B, C, 64)).astype(np.float32)
+    dy64 = rng.integers(-4, 5, size=(B, C, 64)).astype(np.float32)
+    assert gn_dx_model_bitexact(dy64, x64, w, mean, rstd, G=G, dtype="bf16", rows="vector") == 1.0

@@ -59,7 +59,7 @@ def test_gn_page_shapes(name):
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("B,C,S,G", [
     (2, 8, 8192, 2),      # one full chunk per segment (16-bit; two for float32)
-    (2, 8, 4096, 2),      # half a chunk per segment (16-bit)
+    (2, 8, 4096, 2),      # 16384-element rows: row kernels (16-bit), chunks (float32)
     (3, 6, 9000, 3),      # two chunks, ragged last chunk
     (2, 4, 20000, 2),     # three chunks (16-bit), ragged last chunk
     (2, 4, 1000, 4),      # one channel per group; S * 2 bytes not a multiple of 16 for 16-bit
@@ -67,12 +67,24 @@ def test_gn_page_shapes(name):
     (5, 12, 1, 3),        # one element per channel
     (1, 3, 7, 3),         # one channel per group, tiny S
     (4, 64, 64, 16),
-    # rows of at most 8192 elements (float32: 4096): the row kernels
+    # rows held by one row group: up to 32768 elements (float32 16384) in channels of whole
+    # 16-byte vectors, up to 16384 (8192) otherwise
     (32, 256, 49, 32),    # 7 x 7, 8 channels a group: rows not 16-byte aligned (element-wise)
-    (16, 128, 196, 32),   # 14 x 14
-    (8, 64, 256, 32),     # 16 x 16: 16-byte rows
-    (3, 8, 1024, 1),      # rows of 8192 elements: the largest for 16-bit types
-    (3, 8, 1025, 1),      # one element more: the chunked kernels
+    (16, 128, 196, 32),   # 14 x 14: 16-byte rows, channels of 24.5 vectors (16-bit)
+    (8, 64, 256, 32),     # 16 x 16: per-vector segment sums
+    (3, 8, 1024, 1),      # rows of 8192 elements: one vector a lane at 1024 lanes
+    (3, 8, 1025, 1),      # one element more: two vectors a lane, a partial one
+    (2, 16, 1024, 1),     # 16384 elements: two vectors a lane (float32: four)
+    (2, 16, 1025, 1),     # channels of 1025 elements: past the by-value rows, chunked kernels
+    (2, 32, 1024, 1),     # 32768 elements: four vectors a lane (float32: chunks)
+    (2, 640, 1024, 32),   # 20 channels of 32 x 32 a group (20480-element rows)
+    (4, 1280, 16, 32),    # 40 channels of 16 elements a group (10240-element rows)
+    (17, 512, 512, 64),   # 1088 rows: half the threads a row, two vectors a lane (one round)
+    (3, 10, 1111, 2),     # 5555-element rows, not 16-byte aligned: 8 elements a lane
+    (2, 12, 1111, 1),     # 13332 elements a row: 16 elements a lane (16-bit)
+    (1, 4096, 4, 1),      # 16384 elements in 4096 channels: past the LDS cap, chunked kernels
+    (2, 64, 10, 4),       # 10-element channels: vectors straddle channel boundaries
+    (2, 64, 4, 2),        # channels narrower than a vector (16-bit)
     (5, 6, 500, 3),       # 1000-element rows, 1000 * 2 bytes a multiple of 16
 ])
 def test_gn_shapes(dtype, B, C, S, G):
