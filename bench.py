@@ -32,7 +32,8 @@ Measurement:
 * cpu_baseline: the CPU oracle (NumPy, one thread) on a bounded sample of the same rows.
 * rows: LayerNorm, softmax, GroupNorm and the float64 RMSNorm, forward and backward, timed the same
   way (graph of back-to-back launches over rotating buffers), each with its own CPU oracle sample;
-  and RMSNorm, LayerNorm and softmax on many narrow rows (bf16 65536 x 128).
+  RMSNorm, LayerNorm and softmax on many narrow rows (bf16 65536 x 128); GroupNorm with many
+  channels of a small spatial size (bf16 (8, 640, 32, 32), 32 groups: rows held whole).
 * configs: every RMSNorm configuration (fp32 64 x 1024; bf16 4096 x 4096 in the other rounding
   mode; fp16 8192 x 8192; bf16 16384 x 3072 Gemma round once; bf16 M = 4096 hidden-size sweep up to
   N = 32768): step, forward and backward times, GB/s and fraction of peak per phase, on inputs
@@ -646,10 +647,14 @@ def f64_row(torch, rn, launches, rotate_mib):
             "bwd_includes": "rows kernel + float64 dw reduction"}
 
 
-def groupnorm_row(torch, rn, launches, rotate_mib):
-    """GroupNorm forward and backward at the group_norm page's (16, 32, 256, 256), 8 groups."""
+GN_PASSES = "fwd reads x twice (statistics, then normalize); bwd reads x and dy twice"
+
+
+def groupnorm_row(torch, rn, launches, rotate_mib, name=None, passes=GN_PASSES):
+    """GroupNorm forward and backward at the group_norm page's (16, 32, 256, 256), 8 groups, or
+    the GroupNorm workload `name`."""
     from workloads import GN_HEADLINE, GN_WORKLOADS, make_gn_inputs, to_device
-    wl = GN_WORKLOADS[GN_HEADLINE]
+    wl = GN_WORKLOADS[name or GN_HEADLINE]
     lib, dev = rn.library(), "cuda:0"
     dt = rn.DTYPE_CODES[wl.dtype]
     inp = make_gn_inputs(wl)
@@ -693,7 +698,7 @@ def groupnorm_row(torch, rn, launches, rotate_mib):
             "fwd_GBps": round(wl.fwd_bytes() / tf / 1e9, 1),
             "bwd_GBps": round(wl.bwd_bytes() / tb / 1e9, 1),
             "fwd_bytes": wl.fwd_bytes(), "bwd_bytes": wl.bwd_bytes(), "buffer_sets": n,
-            "passes": "fwd reads x twice (statistics, then normalize); bwd reads x and dy twice"}
+            "passes": passes}
 
 
 # Every RMSNorm configuration the library is specified for, timed like the headline: the
@@ -962,6 +967,10 @@ def main(argv=None) -> int:
         sets = None
         torch.cuda.empty_cache()
         line["rows"]["groupnorm"] = groupnorm_row(torch, rn, launches, args.rotate_mib)
+        torch.cuda.empty_cache()
+        line["rows"]["groupnorm_rows"] = groupnorm_row(
+            torch, rn, launches, args.rotate_mib, "gn_bf16_8x640x32x32_g32",
+            "a (batch, group) row held by one row group: x (and dy) read once")
         torch.cuda.empty_cache()
         line["rows"]["rmsnorm_f64"] = f64_row(torch, rn, launches, args.rotate_mib)
         torch.cuda.empty_cache()

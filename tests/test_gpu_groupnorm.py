@@ -77,6 +77,7 @@ def test_gn_page_shapes(name):
     (2, 16, 1024, 1),     # 16384 elements: two vectors a lane (float32: four)
     (2, 16, 1025, 1),     # channels of 1025 elements: past the by-value rows, chunked kernels
     (2, 32, 1024, 1),     # 32768 elements: four vectors a lane (float32: chunks)
+    (2, 320, 4096, 32),   # 10 channels of 64 x 64 a group (40960-element rows): chunks
     (2, 640, 1024, 32),   # 20 channels of 32 x 32 a group (20480-element rows)
     (4, 1280, 16, 32),    # 40 channels of 16 elements a group (10240-element rows)
     (17, 512, 512, 64),   # 1088 rows: half the threads a row, two vectors a lane (one round)
@@ -131,6 +132,13 @@ def test_gn_zero_batch():
     dx, dw, db = rn.groupnorm_bwd(x, x, 4, w, m, r)
     torch.cuda.synchronize()
     assert y.shape == (0, 8, 16) and float(dw.abs().sum()) == 0.0 and float(db.abs().sum()) == 0.0
+
+
+def test_gn_rows_bench_shape():
+    """The benchmark's GroupNorm row of many small channels at its full size: bf16 (8, 640, 32, 32),
+    32 groups (20480-element rows held by one row group, per-vector segment sums), every element
+    against the oracle."""
+    run_gn(GN_WORKLOADS["gn_bf16_8x640x32x32_g32"])
 
 
 def test_gn_full_size_bench_shape():

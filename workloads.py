@@ -250,6 +250,10 @@ GN_WORKLOADS = {
         GnWorkload("gn_bf16_16x512x64x64_g32", "bf16", 16, 512, 64 * 64, 32, 1e-5, _STD, _GAIN,
                    _STD),
         GnWorkload("gn_bf16_64x64x8192_g8", "bf16", 64, 64, 8192, 8, 1e-5, _STD, _GAIN, _STD),
+        # many channels of a small spatial size (20 channels of 32 x 32 a group): 20480-element
+        # (batch, group) rows
+        GnWorkload("gn_bf16_8x640x32x32_g32", "bf16", 8, 640, 32 * 32, 32, 1e-5, _STD, _GAIN,
+                   _STD),
         GnWorkload("gn_f16_1x16x256x256_g4_ones", "f16", 1, 16, 256 * 256, 4, 1e-5, _STD,
                    ("ones",), ("ones",), ("normal", 0.0, 0.0)),
         GnWorkload("gn_bf16_2x64x32x32_g8_offset16", "bf16", 2, 64, 32 * 32, 8, 1e-5,
