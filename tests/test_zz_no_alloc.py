@@ -61,6 +61,7 @@ def test_noalloc_matches_rmsnorm_bwd_on_consecutive_calls():
     # the largest shape the scratch array holds (256 partial rows of 8192 floats = 8 MiB), then
     # smaller ones on the same array
     _compare(4096, 8192, "bf16", "twice", 0.0, "float32", 31)
+    _compare(40000, 128, "bf16", "twice", 0.0, "float32", 37)  # narrow rows: 16-lane row groups
     _compare(300, 1000, "bf16", "twice", 0.0, "float32", 32)
     _compare(257, 3072, "bf16", "once", 1.0, "float32", 33)
     _compare(64, 4096, "f16", "twice", 0.0, "autograd", 34)
