@@ -343,8 +343,8 @@ __device__ __forceinline__ void combine_take(float (&acc)[K], const float* buf, 
 // whose load discipline this kernel follows: every step issues its row's loads as straight-line
 // buffer loads (rows past the block's share read w), only the arithmetic and stores are guarded.
 // SUB > 0: narrow rows of whole vectors on row groups of SUB lanes, as the RMSNorm bwd_rows_kernel
-// (a wavefront's rows addressed from its first row's descriptor, segment_sum for the row sums);
-// the row-sum slots in LDS are laid out as for one-wavefront groups and left unused.
+// (a wavefront's rows addressed from its first row's descriptor, segment_sum for the row sums,
+// combine_columns for the dw and db sums: its LDS is the only LDS such an instantiation uses).
 template <DT D, int ITERS, int DEPTH, bool HAS_DB, bool KEEP, Tail TAIL, int WPR, int SUB = 0>
 __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   using IO = VecIO<D, true>;
@@ -353,7 +353,8 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
   constexpr int V = IO::V;
   constexpr int RING = DEPTH + 1;
   constexpr int K = ITERS * V;
-  constexpr bool EARLY = ITERS == 1;  // partial rows written in the last step
+  // partial rows written in the last step (row groups of whole wavefronts)
+  constexpr bool EARLY = ITERS == 1 && SUB == 0;
   static_assert(SUB == 0 || (ITERS == 1 && TAIL != Tail::RAGGED && WPR == 0),
                 "narrow rows: at most one whole vector per lane");
   extern __shared__ uint4 smem[];
@@ -575,6 +576,18 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
     }
   }
 
+  if constexpr (SUB > 0) {  // narrow rows: the two-round column combine, dw then db
+    float* buf = reinterpret_cast<float*>(smem);
+    const float tw = combine_columns<V>(accw, buf, grp, tl, SUB);
+    if (tid < SUB * V && tid < N)
+      __builtin_nontemporal_store(tw, a.part + (int64_t)b * a.ldp + tid);
+    if constexpr (HAS_DB) {
+      const float tb = combine_columns<V>(accb, buf, grp, tl, SUB);
+      if (tid < SUB * V && tid < N)
+        __builtin_nontemporal_store(tb, a.part + (int64_t)(P + b) * a.ldp + tid);
+    }
+    return;
+  }
   // Without the early first level (no rows, or two vectors a thread) the whole tree runs here;
   // with it and more than two groups, the tree's other levels.
   const bool early = EARLY && nsteps > 0;

@@ -203,13 +203,12 @@ rmsnorm_status plan_ln_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_
   const int V = vec_elems(dtype);
   if (v == RMSNORM_VARIANT_REGISTERS && narrow_ok && N % V == 0 &&
       (p->sub = narrow_lanes(nv_wide)) > 0) {
-    // Narrow rows of whole vectors: 1024 / sub row groups of sub lanes. LDS as for one-wavefront
-    // groups: row-sum slots (unused), then the dw and db slices of the combine.
+    // Narrow rows of whole vectors: 1024 / sub row groups of sub lanes; LDS only for the column
+    // combine of the groups' dw and db sums (one after the other).
     p->tpr = p->sub;
     p->iters = 1;
     p->groups = kLnBwdBlockThreads / p->sub;
-    p->lds = round16(sizeof(float) * 4 * (size_t)p->groups) +
-             2 * sizeof(float) * (size_t)(p->groups / 2) * p->sub * V;
+    p->lds = sizeof(float) * (size_t)combine_columns_floats(V);
     return RMSNORM_OK;
   }
   p->tpr = tpr;

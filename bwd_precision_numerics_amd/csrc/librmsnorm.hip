@@ -102,11 +102,11 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   if (v == RMSNORM_VARIANT_REGISTERS && narrow_ok && N % V == 0 &&
       (p->sub = narrow_lanes(nv_wide)) > 0) {
     // Narrow rows of whole vectors: 1024 / sub row groups of sub lanes; LDS only for the
-    // combine of the groups' dw sums.
+    // column combine of the groups' dw sums.
     p->tpr = p->sub;
     p->iters = 1;
     p->groups = kBwdBlockThreads / p->sub;
-    p->lds = sizeof(float) * (size_t)(p->groups / 2) * p->sub * V;
+    p->lds = sizeof(float) * (size_t)combine_columns_floats(V);
     return RMSNORM_OK;
   }
   p->tpr = tpr;

@@ -81,6 +81,40 @@ __device__ __forceinline__ void combine_groups(float (&acc)[K], float* buf, int 
   }
 }
 
+// Narrow rows (row groups of SUB lanes, 1024 / SUB of them, each lane V column sums): the groups'
+// column sums added through LDS in two rounds instead of the pairwise tree (whose 2 log2(groups)
+// barriers cost 0.7-0.9 us of a 12 us rows kernel at 64 groups). Every group writes its sums as row
+// grp of a [groups][C] array (C = SUB * V columns); thread t adds rows q V .. q V + V - 1 of column
+// t % C in order (q = t / C), and thread c < C adds the 1024 / C results of column c in order.
+// Returns column t's sum in threads t < C; LDS: combine_columns_floats(V) floats. Every thread of
+// the 1024-thread block must call it.
+constexpr int combine_columns_floats(int V) { return 1024 * V + 1024; }
+template <int V>
+__device__ __forceinline__ float combine_columns(const float (&acc)[V], float* buf, int grp, int tl,
+                                                 int sub) {
+  const int C = sub * V, t = threadIdx.x;
+  float* rows = buf;               // [1024 / sub][C] = 1024 * V floats
+  float* parts = buf + 1024 * V;   // [1024 / C][C]
+  lds_barrier();  // earlier users of the LDS are done
+  float* row = rows + grp * C + tl * V;
+#pragma unroll
+  for (int k = 0; k < V; k += 4)
+    *reinterpret_cast<float4*>(row + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+  lds_barrier();
+  const int c = t % C, q = t / C;
+  float s = rows[(q * V) * C + c];
+#pragma unroll
+  for (int i = 1; i < V; ++i) s += rows[(q * V + i) * C + c];
+  parts[q * C + c] = s;
+  lds_barrier();
+  float total = 0.f;
+  if (t < C) {
+    total = parts[t];
+    for (int j = 1; j < 1024 / C; ++j) total += parts[j * C + t];
+  }
+  return total;
+}
+
 // Write a block's combined column accumulators as partial row b of the workspace (group 0 only).
 // Non-temporal (streaming cache policy) 16-byte stores: every block writes its row in the kernel's
 // last moments, with no input stream left to overlap, and the reduction launch that follows reads
@@ -170,7 +204,7 @@ enum class Tail : int {
 //
 // SUB > 0: rows of at most SUB whole vectors (SUB = 4 to 32) take row groups of SUB lanes, 64 / SUB
 // rows per wavefront and 1024 / SUB per block, summed with segment_sum (bit for bit the TPR = 64
-// sums, so dx does not change). A wavefront's rows are then local indices g0 .. g0 + 64 / SUB - 1,
+// sums, so dx does not change); the groups' dw sums meet in combine_columns. A wavefront's rows are then local indices g0 .. g0 + 64 / SUB - 1,
 // P rows apart: the buffer descriptor holds the wavefront's first row and each lane adds its own
 // row's distance, dg * P row strides (the host checks that these offsets fit in 31 bits).
 template <DT D, int ITERS, int DEPTH, int RB, bool AG, bool KEEP, Tail TAIL, int WPR, int SUB = 0>
@@ -359,8 +393,14 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
     }
   }
 
-  combine_groups<ITERS * V>(acc, reinterpret_cast<float*>(smem), G, grp, tl, TPR);
-  if (grp == 0) store_partial<ITERS, V>(acc, a.part + (int64_t)b * a.ldp, TPR, tl, N);
+  if constexpr (SUB > 0) {
+    const float t = combine_columns<V>(acc, reinterpret_cast<float*>(smem), grp, tl, SUB);
+    if (tid < SUB * V && tid < N)
+      __builtin_nontemporal_store(t, a.part + (int64_t)b * a.ldp + tid);
+  } else {
+    combine_groups<ITERS * V>(acc, reinterpret_cast<float*>(smem), G, grp, tl, TPR);
+    if (grp == 0) store_partial<ITERS, V>(acc, a.part + (int64_t)b * a.ldp, TPR, tl, N);
+  }
 }
 
 // LDS-staged kernel for rows too wide to keep in registers (e.g. N = 32768 in 16-bit types): the
