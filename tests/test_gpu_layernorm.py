@@ -97,6 +97,11 @@ def test_ln_narrow_rows(dtype, M, N, ld):
     run_ln(dtype, M, N, ld=ld, seed=34)
 
 
+def test_ln_narrow_rows_bench_shape():
+    """The benchmark's narrow-row shape at its full size, bf16 65536 x 128 with a bias."""
+    run_ln("bf16", 65536, 128, seed=36)
+
+
 @pytest.mark.parametrize("bias", [True, False])
 @pytest.mark.parametrize("dtype,M,N", [("bf16", 20000, 128), ("bf16", 33000, 64),
                                        ("f32", 9000, 64), ("f16", 7000, 256), ("bf16", 5000, 40)])

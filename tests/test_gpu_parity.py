@@ -153,6 +153,12 @@ def test_parity_narrow_rows(dtype, M, N, ld, mode):
         run_case(dtype, M, N, rounding=mode, offset=1.0 if mode == "once" else 0.0, ld=ld, seed=41)
 
 
+def test_narrow_rows_bench_shape():
+    """The benchmark's narrow-row shape at its full size, bf16 65536 x 128, round twice: every
+    element against the oracle."""
+    run_case("bf16", 65536, 128, seed=43)
+
+
 @pytest.mark.parametrize("dtype,M,N", [("bf16", 20000, 128), ("bf16", 33000, 64), ("f32", 9000, 64),
                                        ("f16", 7000, 256), ("bf16", 5000, 40)])
 def test_narrow_row_segments_match_wavefront_rows(dtype, M, N):

@@ -158,6 +158,11 @@ def test_softmax_narrow_rows(dtype, M, N, ld):
     run_sm(dtype, M, N, ld=ld, seed=12)
 
 
+def test_softmax_narrow_rows_bench_shape():
+    """The benchmark's narrow-row shape at its full size, bf16 65536 x 128."""
+    run_sm("bf16", 65536, 128, seed=14)
+
+
 @pytest.mark.parametrize("dtype,M,N", [("bf16", 20000, 128), ("bf16", 33000, 64),
                                        ("f32", 9000, 64), ("f16", 7000, 256), ("bf16", 5000, 40)])
 def test_softmax_narrow_segments_match_wavefront_rows(dtype, M, N):
