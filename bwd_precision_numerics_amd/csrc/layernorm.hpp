@@ -578,14 +578,9 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
 
   if constexpr (SUB > 0) {  // narrow rows: the two-round column combine, dw then db
     float* buf = reinterpret_cast<float*>(smem);
-    const float tw = combine_columns<V>(accw, buf, grp, tl, SUB);
-    if (tid < SUB * V && tid < N)
-      __builtin_nontemporal_store(tw, a.part + (int64_t)b * a.ldp + tid);
-    if constexpr (HAS_DB) {
-      const float tb = combine_columns<V>(accb, buf, grp, tl, SUB);
-      if (tid < SUB * V && tid < N)
-        __builtin_nontemporal_store(tb, a.part + (int64_t)(P + b) * a.ldp + tid);
-    }
+    combine_columns<V>(accw, buf, grp, tl, SUB, a.part + (int64_t)b * a.ldp, N);
+    if constexpr (HAS_DB)
+      combine_columns<V>(accb, buf, grp, tl, SUB, a.part + (int64_t)(P + b) * a.ldp, N);
     return;
   }
   // Without the early first level (no rows, or two vectors a thread) the whole tree runs here;

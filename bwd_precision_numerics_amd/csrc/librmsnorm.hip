@@ -120,7 +120,12 @@ rmsnorm_status plan_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_ok,
   } else {
     main_bytes = round16(sizeof(float) * 2 * (size_t)p->groups * wpr * bwd_batch(iters));
   }
-  const size_t combine_bytes = sizeof(float) * (size_t)(p->groups / 2) * tpr * iters * V;
+  // The groups' dw sums: the pairwise tree's slices, or with one vector a lane and four or more
+  // groups the column combine's array (combine_block).
+  const size_t combine_bytes =
+      iters == 1 && p->groups >= 4
+          ? sizeof(float) * (size_t)combine_columns_floats(V)
+          : sizeof(float) * (size_t)(p->groups / 2) * tpr * iters * V;
   p->lds = main_bytes > combine_bytes ? main_bytes : combine_bytes;
   return RMSNORM_OK;
 }

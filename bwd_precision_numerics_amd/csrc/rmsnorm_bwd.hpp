@@ -81,38 +81,46 @@ __device__ __forceinline__ void combine_groups(float (&acc)[K], float* buf, int 
   }
 }
 
-// Narrow rows (row groups of SUB lanes, 1024 / SUB of them, each lane V column sums): the groups'
-// column sums added through LDS in two rounds instead of the pairwise tree (whose 2 log2(groups)
-// barriers cost 0.7-0.9 us of a 12 us rows kernel at 64 groups). Every group writes its sums as row
-// grp of a [groups][C] array (C = SUB * V columns); thread t adds rows q V .. q V + V - 1 of column
-// t % C in order (q = t / C), and thread c < C adds the 1024 / C results of column c in order.
-// Returns column t's sum in threads t < C; LDS: combine_columns_floats(V) floats. Every thread of
-// the 1024-thread block must call it.
+// Column sums of the 1024 / tpr row groups of a block (lane tl of a group holds the V columns
+// tl V .. tl V + V - 1, so C = tpr * V columns) through LDS in at most two rounds instead of the
+// pairwise tree, whose 2 log2(groups) barriers cost 0.55-0.9 us of a rows kernel with 4 to 64
+// groups. Every group writes its sums as row grp of a [groups][C] array. With C >= 1024 columns
+// thread t adds all groups' rows of columns t, t + 1024, ... in group order; with fewer, thread t
+// adds rows q V .. q V + V - 1 of column t % C in order (q = t / C), and thread c < C adds the
+// 1024 / C results of column c in order. Column c < N of the result goes to out[c] (non-temporal).
+// LDS: combine_columns_floats(V) floats. Every thread of the 1024-thread block must call it.
 constexpr int combine_columns_floats(int V) { return 1024 * V + 1024; }
 template <int V>
-__device__ __forceinline__ float combine_columns(const float (&acc)[V], float* buf, int grp, int tl,
-                                                 int sub) {
-  const int C = sub * V, t = threadIdx.x;
-  float* rows = buf;               // [1024 / sub][C] = 1024 * V floats
-  float* parts = buf + 1024 * V;   // [1024 / C][C]
+__device__ __forceinline__ void combine_columns(const float (&acc)[V], float* buf, int grp, int tl,
+                                                int tpr, float* out, int N) {
+  const int C = tpr * V, G = 1024 / tpr, t = threadIdx.x;
+  float* rows = buf;               // [G][C] = 1024 * V floats
+  float* parts = buf + 1024 * V;   // [1024 / C][C] when C < 1024
   lds_barrier();  // earlier users of the LDS are done
   float* row = rows + grp * C + tl * V;
 #pragma unroll
   for (int k = 0; k < V; k += 4)
     *reinterpret_cast<float4*>(row + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
   lds_barrier();
+  if (C >= 1024) {  // block-uniform
+    for (int c = t; c < C; c += 1024) {
+      float s = rows[c];
+      for (int g = 1; g < G; ++g) s += rows[g * C + c];
+      if (c < N) __builtin_nontemporal_store(s, out + c);
+    }
+    return;
+  }
   const int c = t % C, q = t / C;
   float s = rows[(q * V) * C + c];
 #pragma unroll
   for (int i = 1; i < V; ++i) s += rows[(q * V + i) * C + c];
   parts[q * C + c] = s;
   lds_barrier();
-  float total = 0.f;
   if (t < C) {
-    total = parts[t];
+    float total = parts[t];
     for (int j = 1; j < 1024 / C; ++j) total += parts[j * C + t];
+    if (t < N) __builtin_nontemporal_store(total, out + t);
   }
-  return total;
 }
 
 // Write a block's combined column accumulators as partial row b of the workspace (group 0 only).
@@ -142,6 +150,22 @@ __device__ __forceinline__ void store_partial(const float (&acc)[ITERS * V], flo
         if (col + e < N) pr[col + e] = acc[it * V + e];
     }
   }
+}
+
+// A block's G row groups' column sums (ITERS vectors of V a lane) into partial row `out`: the
+// column combine for one vector a lane and four or more groups, else the pairwise tree and group
+// 0's stores. G is block-uniform. Every thread of the block must call it.
+template <int ITERS, int V>
+__device__ __forceinline__ void combine_block(float (&acc)[ITERS * V], float* buf, int G, int grp,
+                                              int tl, int tpr, float* out, int N) {
+  if constexpr (ITERS == 1) {
+    if (G >= 4) {
+      combine_columns<V>(acc, buf, grp, tl, tpr, out, N);
+      return;
+    }
+  }
+  combine_groups<ITERS * V>(acc, buf, G, grp, tl, tpr);
+  if (grp == 0) store_partial<ITERS, V>(acc, out, tpr, tl, N);
 }
 
 // Sums of RB values over the TPR threads of one row group, with the order of group_sum for each:
@@ -393,14 +417,10 @@ __global__ void __launch_bounds__(1024) bwd_rows_kernel(BwdArgs a) {
     }
   }
 
-  if constexpr (SUB > 0) {
-    const float t = combine_columns<V>(acc, reinterpret_cast<float*>(smem), grp, tl, SUB);
-    if (tid < SUB * V && tid < N)
-      __builtin_nontemporal_store(t, a.part + (int64_t)b * a.ldp + tid);
-  } else {
-    combine_groups<ITERS * V>(acc, reinterpret_cast<float*>(smem), G, grp, tl, TPR);
-    if (grp == 0) store_partial<ITERS, V>(acc, a.part + (int64_t)b * a.ldp, TPR, tl, N);
-  }
+  // Four or more row groups (rows of at most 256 lanes) meet in the column combine; one or two in
+  // the pairwise tree (one level at two groups).
+  combine_block<ITERS, V>(acc, reinterpret_cast<float*>(smem), G, grp, tl, TPR,
+                          a.part + (int64_t)b * a.ldp, N);
 }
 
 // LDS-staged kernel for rows too wide to keep in registers (e.g. N = 32768 in 16-bit types): the
@@ -570,8 +590,9 @@ __global__ void __launch_bounds__(1024) bwd_lds_kernel(BwdArgs a) {
     }
   }
 
-  combine_groups<ITERS * V>(acc, reinterpret_cast<float*>(smem), G, grp, tl, TPR);
-  if (grp == 0) store_partial<ITERS, V>(acc, a.part + (int64_t)b * a.ldp, TPR, tl, N);
+  // The register kernel's combine for the same shape (so the two give the same dw bits).
+  combine_block<ITERS, V>(acc, reinterpret_cast<float*>(smem), G, grp, tl, TPR,
+                          a.part + (int64_t)b * a.ldp, N);
 }
 
 // Any N and any alignment. One row at a time per block (groups = 1); the elementwise pass reads
