@@ -497,7 +497,7 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
         // hands over its dw sums and group 0 its db sums, so each group adds one pair (in either
         // order the same float32 sum) and writes one partial row.
         // (One vector a thread only: at two the extra live sums would spill registers.)
-        const bool last = EARLY && s == nsteps - 1;  // block-uniform
+        const bool last = EARLY && G <= 2 && s == nsteps - 1;  // block-uniform
         const bool swap = HAS_DB && G == 2;
         if (last) {
           if (swap) {
@@ -576,16 +576,18 @@ __global__ void __launch_bounds__(1024) ln_bwd_rows_kernel(LnBwdArgs a) {
     }
   }
 
-  if constexpr (SUB > 0) {  // narrow rows: the two-round column combine, dw then db
-    float* buf = reinterpret_cast<float*>(smem);
-    combine_columns<V>(accw, buf, grp, tl, SUB, a.part + (int64_t)b * a.ldp, N);
-    if constexpr (HAS_DB)
-      combine_columns<V>(accb, buf, grp, tl, SUB, a.part + (int64_t)(P + b) * a.ldp, N);
-    return;
+  if constexpr (ITERS == 1) {
+    if (SUB > 0 || G >= 4) {  // four or more row groups: the column combine, dw then db
+      float* buf = reinterpret_cast<float*>(smem);
+      combine_columns<V>(accw, buf, grp, tl, TPR, a.part + (int64_t)b * a.ldp, N);
+      if constexpr (HAS_DB)
+        combine_columns<V>(accb, buf, grp, tl, TPR, a.part + (int64_t)(P + b) * a.ldp, N);
+      return;
+    }
   }
   // Without the early first level (no rows, or two vectors a thread) the whole tree runs here;
-  // with it and more than two groups, the tree's other levels.
-  const bool early = EARLY && nsteps > 0;
+  // with it and two groups, nothing is left.
+  const bool early = EARLY && G <= 2 && nsteps > 0;
   const int rest = early ? G - (G >> 1) : G;
   if (rest > 1 || !early) {
     combine_groups<K>(accw, cbw, rest, grp, tl, TPR);

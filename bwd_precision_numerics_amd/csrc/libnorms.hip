@@ -220,6 +220,10 @@ rmsnorm_status plan_ln_bwd(int64_t M, int64_t N, rmsnorm_dtype dtype, bool wide_
   const size_t combine_bytes =
       sizeof(float) * (size_t)(p->groups / 2) * tpr * iters * vec_elems(dtype);
   p->lds = red_bytes + 2 * combine_bytes;
+  // Four or more groups at one vector a lane combine through the column combine's array instead,
+  // from the start of the LDS, after the last row.
+  const size_t columns_bytes = sizeof(float) * (size_t)combine_columns_floats(V);
+  if (iters == 1 && p->groups >= 4 && p->lds < columns_bytes) p->lds = columns_bytes;
   return RMSNORM_OK;
 }
 
