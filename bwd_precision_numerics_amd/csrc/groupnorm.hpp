@@ -104,11 +104,13 @@ struct ChunkIO {
   using Raw = typename IO::Raw;
   static constexpr int V = IO::V;
   static constexpr int IT = gn_chunk<D>() / (kGnThreads * V);
+  // t: the thread's index among the chunk's `stride` threads (the block's 256, or a wavefront's 64
+  // for chunks of at most a quarter of CH).
   template <bool LAST = false>
-  static __device__ __forceinline__ void load(const S* p, int cnt, Raw (&r)[IT]) {
+  static __device__ __forceinline__ void load(const S* p, int cnt, Raw (&r)[IT], int t, int stride) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int col = (it * kGnThreads + (int)threadIdx.x) * V;
+      const int col = (it * stride + t) * V;
       r[it] = IO::zero();
       if (col + V <= cnt) r[it] = LAST ? IO::load_nt(p + col) : IO::load(p + col);
       else if (col < cnt) r[it] = IO::load_part(p + col, cnt - col);
@@ -116,16 +118,41 @@ struct ChunkIO {
   }
 };
 
+// The chunk a thread works on. WPC = false: one chunk a block (its 256 threads). WPC: four chunks a
+// block, one a wavefront, for segments of at most CH / 4 elements (a whole block would leave at
+// least three quarters of its threads idle; a wavefront's lanes hold the same 4 vectors each, and
+// its sums need no barrier). Waves past the last chunk have nothing to do (`idle`).
+template <bool WPC>
+struct ChunkSlot {
+  int64_t u;   // chunk index (into the per-chunk pairs)
+  int t;       // thread index among the chunk's threads
+  int stride;  // the chunk's threads
+  bool idle;
+  __device__ __forceinline__ explicit ChunkSlot(const GnArgs& a) {
+    u = WPC ? (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6) : (int64_t)blockIdx.x;
+    t = WPC ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
+    stride = WPC ? 64 : kGnThreads;
+    idle = WPC && u >= a.B * a.C * a.K;
+  }
+};
+// A chunk's sum: the block's (4 wavefronts in order, one barrier) or the wavefront's.
+template <bool WPC>
+__device__ __forceinline__ float chunk_sum(float v, float* red) {
+  return WPC ? wave_sum(v) : block_sum(v, red);
+}
+
 // Forward pass 1: per-chunk (mean, M2).
-template <DT D, bool WIDE>
+template <DT D, bool WIDE, bool WPC = false>
 __global__ void __launch_bounds__(kGnThreads) gn_stats_kernel(GnArgs a) {
   using CI = ChunkIO<D, WIDE>;
   using IO = typename CI::IO;
   constexpr int V = CI::V, IT = CI::IT;
   __shared__ float red[8];
-  const Chunk ch = chunk_of<D>(a, blockIdx.x);
+  const ChunkSlot<WPC> sl(a);
+  if (sl.idle) return;  // whole wavefronts, and no barrier follows with WPC
+  const Chunk ch = chunk_of<D>(a, sl.u);
   typename CI::Raw r[IT];
-  CI::load(static_cast<const typename CI::S*>(a.x) + ch.base, ch.cnt, r);
+  CI::load(static_cast<const typename CI::S*>(a.x) + ch.base, ch.cnt, r, sl.t, sl.stride);
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -137,11 +164,11 @@ __global__ void __launch_bounds__(kGnThreads) gn_stats_kernel(GnArgs a) {
       else s0 += f[e];
     }
   }
-  const float m = block_sum(s0 + s1, red) / (float)ch.cnt;
+  const float m = chunk_sum<WPC>(s0 + s1, red) / (float)ch.cnt;
   float q0 = 0.f, q1 = 0.f;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int col = (it * kGnThreads + (int)threadIdx.x) * V;
+    const int col = (it * sl.stride + sl.t) * V;
     float f[V];
     IO::unpack(r[it], f);
 #pragma unroll
@@ -151,8 +178,8 @@ __global__ void __launch_bounds__(kGnThreads) gn_stats_kernel(GnArgs a) {
       else q0 = __builtin_fmaf(d, d, q0);
     }
   }
-  const float m2 = block_sum(q0 + q1, red + 4);
-  if (threadIdx.x == 0) a.ws[blockIdx.x] = make_float2(m, m2);
+  const float m2 = chunk_sum<WPC>(q0 + q1, red + 4);
+  if (sl.t == 0) a.ws[sl.u] = make_float2(m, m2);
 }
 
 // Chunk statistics of the row (batch, group) merged in a fixed order by wave 0; lane 0 returns it.
@@ -178,39 +205,50 @@ __device__ __forceinline__ Moments row_moments(const GnArgs& a, int64_t bidx, in
 }
 
 // Forward pass 2: merge the row's statistics, write the caches (first chunk of the row), normalize.
-template <DT D, bool WIDE, bool HAS_B>
+// WPC: each wavefront merges its own chunk's row statistics.
+template <DT D, bool WIDE, bool HAS_B, bool WPC = false>
 __global__ void __launch_bounds__(kGnThreads) gn_fwd_kernel(GnArgs a) {
   using CI = ChunkIO<D, WIDE>;
   using IO = typename CI::IO;
   using S = typename CI::S;
   constexpr int V = CI::V, IT = CI::IT;
   __shared__ float stat[2];
-  const Chunk ch = chunk_of<D>(a, blockIdx.x);
+  const ChunkSlot<WPC> sl(a);
+  if (sl.idle) return;  // whole wavefronts, and no barrier follows with WPC
+  const Chunk ch = chunk_of<D>(a, sl.u);
   const int g = (int)(ch.c / a.Cg);
   typename CI::Raw r[IT];
   // in flight during the merge
-  CI::template load<true>(static_cast<const S*>(a.x) + ch.base, ch.cnt, r);
-  if (threadIdx.x < 64) {
-    const Moments mo = row_moments<D>(a, ch.bidx, g);
-    if (threadIdx.x == 0) {
-      const float rs = 1.0f / __builtin_sqrtf(mo.m2 / mo.n + a.eps);
-      stat[0] = mo.m;
-      stat[1] = rs;
+  CI::template load<true>(static_cast<const S*>(a.x) + ch.base, ch.cnt, r, sl.t, sl.stride);
+  float mean, rs;
+  if (WPC || threadIdx.x < 64) {
+    const Moments mo = row_moments<D>(a, ch.bidx, g);  // lane 0 holds the row's moments
+    const float m0 = __shfl(mo.m, 0, 64), m2 = __shfl(mo.m2, 0, 64), n0 = __shfl(mo.n, 0, 64);
+    mean = m0;
+    rs = 1.0f / __builtin_sqrtf(m2 / n0 + a.eps);
+    if ((threadIdx.x & 63) == 0) {
+      if (!WPC) {
+        stat[0] = mean;
+        stat[1] = rs;
+      }
       if (ch.k == 0 && ch.c == (int64_t)g * a.Cg) {
         const int64_t row = ch.bidx * a.G + g;
-        if (a.mean) a.mean[row] = mo.m;
+        if (a.mean) a.mean[row] = mean;
         if (a.rstd) a.rstd[row] = rs;
       }
     }
   }
-  __syncthreads();
-  const float mean = stat[0], rs = stat[1];
+  if constexpr (!WPC) {
+    __syncthreads();
+    mean = stat[0];
+    rs = stat[1];
+  }
   const float wc = to_f32<D>(static_cast<const S*>(a.w)[ch.c]);
   const float bc = HAS_B ? to_f32<D>(static_cast<const S*>(a.b)[ch.c]) : 0.f;
   S* yp = static_cast<S*>(a.out) + ch.base;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int col = (it * kGnThreads + (int)threadIdx.x) * V;
+    const int col = (it * sl.stride + sl.t) * V;
     if (col >= ch.cnt) continue;
     float f[V], o[V];
     IO::unpack(r[it], f);
@@ -226,19 +264,21 @@ __global__ void __launch_bounds__(kGnThreads) gn_fwd_kernel(GnArgs a) {
 }
 
 // Backward pass 1: per-chunk (sum dy, sum dy * xhat).
-template <DT D, bool WIDE>
+template <DT D, bool WIDE, bool WPC = false>
 __global__ void __launch_bounds__(kGnThreads) gn_bwd_sums_kernel(GnArgs a) {
   using CI = ChunkIO<D, WIDE>;
   using IO = typename CI::IO;
   using S = typename CI::S;
   constexpr int V = CI::V, IT = CI::IT;
   __shared__ float red[8];
-  const Chunk ch = chunk_of<D>(a, blockIdx.x);
+  const ChunkSlot<WPC> sl(a);
+  if (sl.idle) return;  // whole wavefronts, and no barrier follows with WPC
+  const Chunk ch = chunk_of<D>(a, sl.u);
   const int64_t row = ch.bidx * a.G + ch.c / a.Cg;
   const float mean = a.mean[row], rs = a.rstd[row];
   typename CI::Raw rx[IT], rd[IT];
-  CI::load(static_cast<const S*>(a.x) + ch.base, ch.cnt, rx);
-  CI::load(static_cast<const S*>(a.dy) + ch.base, ch.cnt, rd);
+  CI::load(static_cast<const S*>(a.x) + ch.base, ch.cnt, rx, sl.t, sl.stride);
+  CI::load(static_cast<const S*>(a.dy) + ch.base, ch.cnt, rd, sl.t, sl.stride);
   float s0 = 0.f, s1 = 0.f, t0 = 0.f, t1 = 0.f;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -257,9 +297,9 @@ __global__ void __launch_bounds__(kGnThreads) gn_bwd_sums_kernel(GnArgs a) {
       }
     }
   }
-  const float sdy = block_sum(s0 + s1, red);
-  const float sdx = block_sum(t0 + t1, red + 4);
-  if (threadIdx.x == 0) a.ws[blockIdx.x] = make_float2(sdy, sdx);
+  const float sdy = chunk_sum<WPC>(s0 + s1, red);
+  const float sdx = chunk_sum<WPC>(t0 + t1, red + 4);
+  if (sl.t == 0) a.ws[sl.u] = make_float2(sdy, sdx);
 }
 
 // dW_c = sum over (batch, chunk) of sum(dy * xhat), dB_c of sum(dy), by one wavefront: lane-strided
@@ -289,23 +329,28 @@ __device__ __forceinline__ void gn_param_sums(const GnArgs& a, int64_t c) {
 }
 
 // Backward pass 2: row constants from the chunk sums (fixed order), then dx for the chunk.
-template <DT D, bool WIDE>
+template <DT D, bool WIDE, bool WPC = false>
 __global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
   using CI = ChunkIO<D, WIDE>;
   using IO = typename CI::IO;
   using S = typename CI::S;
   constexpr int V = CI::V, IT = CI::IT;
   __shared__ float cst[2];
-  const Chunk ch = chunk_of<D>(a, blockIdx.x);
+  const ChunkSlot<WPC> sl(a);
+  if (sl.idle) return;  // whole wavefronts, and no barrier follows with WPC
+  const Chunk ch = chunk_of<D>(a, sl.u);
   const int g = (int)(ch.c / a.Cg);
   const int64_t row = ch.bidx * a.G + g;
   const float mean = a.mean[row], rs = a.rstd[row];
   const S* wp = static_cast<const S*>(a.w);
   typename CI::Raw rx[IT], rd[IT];
-  CI::template load<true>(static_cast<const S*>(a.x) + ch.base, ch.cnt, rx);
-  CI::template load<true>(static_cast<const S*>(a.dy) + ch.base, ch.cnt, rd);
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
+  CI::template load<true>(static_cast<const S*>(a.x) + ch.base, ch.cnt, rx, sl.t, sl.stride);
+  CI::template load<true>(static_cast<const S*>(a.dy) + ch.base, ch.cnt, rd, sl.t, sl.stride);
+  // The row constants from the chunk sums, by the block's first wavefront (WPC: every wavefront
+  // for its own chunk's row).
+  float c1 = 0.f, c2 = 0.f;
+  if (WPC || threadIdx.x < 64) {
+    const int lane = threadIdx.x & 63;
     const int nent = a.Cg * a.K;
     const int64_t first = (ch.bidx * a.C + (int64_t)g * a.Cg) * a.K;
     float u1 = 0.f, u2 = 0.f;
@@ -323,22 +368,31 @@ __global__ void __launch_bounds__(kGnThreads) gn_bwd_dx_kernel(GnArgs a) {
         u2 += o2;
       }
     }
-    if (lane == 0) {
-      const float n = (float)(a.Cg * a.S);
-      cst[0] = u1 / n;
-      cst[1] = u2 / n;
+    const float n = (float)(a.Cg * a.S);
+    c1 = __shfl(u1, 0, 64) / n;
+    c2 = __shfl(u2, 0, 64) / n;
+    if (!WPC && lane == 0) {
+      cst[0] = c1;
+      cst[1] = c2;
     }
   }
-  // The first chunk of batch 0 of each channel also sums that channel's dW and dB in its second
-  // wavefront (the per-chunk sums are complete since the previous kernel).
-  if (ch.bidx == 0 && ch.k == 0 && threadIdx.x >= 64 && threadIdx.x < 128) gn_param_sums(a, ch.c);
-  __syncthreads();
-  const float c1 = cst[0], c2 = cst[1];
+  // The first chunk of batch 0 of each channel also sums that channel's dW and dB (the per-chunk
+  // sums are complete since the previous kernel): in the block's second wavefront, or with WPC in
+  // the chunk's own wavefront.
+  if (ch.bidx == 0 && ch.k == 0) {
+    if (WPC) gn_param_sums(a, ch.c);
+    else if (threadIdx.x >= 64 && threadIdx.x < 128) gn_param_sums(a, ch.c);
+  }
+  if constexpr (!WPC) {
+    __syncthreads();
+    c1 = cst[0];
+    c2 = cst[1];
+  }
   const float wc = to_f32<D>(wp[ch.c]);
   S* dxp = static_cast<S*>(a.out) + ch.base;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int col = (it * kGnThreads + (int)threadIdx.x) * V;
+    const int col = (it * sl.stride + sl.t) * V;
     if (col >= ch.cnt) continue;
     float xf[V], df[V], o[V];
     IO::unpack(rx[it], xf);

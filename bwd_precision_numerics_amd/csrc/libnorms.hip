@@ -410,26 +410,37 @@ GnArgs gn_args(int64_t B, int64_t C, int64_t S, int64_t G, int64_t K, void* work
   return a;
 }
 
-template <DT D, bool WIDE>
-rmsnorm_status gn_fwd_launch(const GnArgs& a, int64_t chunks, hipStream_t s) {
-  hipLaunchKernelGGL((gn_stats_kernel<D, WIDE>), dim3((unsigned)chunks), dim3(kGnThreads), 0, s,
-                     a);
+// Segments of at most a quarter chunk (S <= CH / 4) take one chunk per wavefront, four a block
+// (WPC): bf16 (2, 1280, 32 x 32), 32 groups, 1024-element segments, had filled a quarter of each
+// 256-thread chunk block.
+template <DT D, bool WIDE, bool WPC>
+rmsnorm_status gn_fwd_launch_as(const GnArgs& a, int64_t chunks, hipStream_t s) {
+  const unsigned grid = (unsigned)(WPC ? ceil_div(chunks, 4) : chunks);
+  hipLaunchKernelGGL((gn_stats_kernel<D, WIDE, WPC>), dim3(grid), dim3(kGnThreads), 0, s, a);
   if (a.b)
-    hipLaunchKernelGGL((gn_fwd_kernel<D, WIDE, true>), dim3((unsigned)chunks), dim3(kGnThreads),
-                       0, s, a);
+    hipLaunchKernelGGL((gn_fwd_kernel<D, WIDE, true, WPC>), dim3(grid), dim3(kGnThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((gn_fwd_kernel<D, WIDE, false>), dim3((unsigned)chunks), dim3(kGnThreads),
-                       0, s, a);
+    hipLaunchKernelGGL((gn_fwd_kernel<D, WIDE, false, WPC>), dim3(grid), dim3(kGnThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
 }
-
 template <DT D, bool WIDE>
-rmsnorm_status gn_bwd_launch(const GnArgs& a, int64_t chunks, hipStream_t s) {
-  hipLaunchKernelGGL((gn_bwd_sums_kernel<D, WIDE>), dim3((unsigned)chunks), dim3(kGnThreads), 0,
-                     s, a);
-  hipLaunchKernelGGL((gn_bwd_dx_kernel<D, WIDE>), dim3((unsigned)chunks), dim3(kGnThreads), 0, s,
+rmsnorm_status gn_fwd_launch(const GnArgs& a, int64_t chunks, hipStream_t s) {
+  return a.S <= gn_chunk<D>() / 4 ? gn_fwd_launch_as<D, WIDE, true>(a, chunks, s)
+                                  : gn_fwd_launch_as<D, WIDE, false>(a, chunks, s);
+}
+
+template <DT D, bool WIDE, bool WPC>
+rmsnorm_status gn_bwd_launch_as(const GnArgs& a, int64_t chunks, hipStream_t s) {
+  const unsigned grid = (unsigned)(WPC ? ceil_div(chunks, 4) : chunks);
+  hipLaunchKernelGGL((gn_bwd_sums_kernel<D, WIDE, WPC>), dim3(grid), dim3(kGnThreads), 0, s, a);
+  hipLaunchKernelGGL((gn_bwd_dx_kernel<D, WIDE, WPC>), dim3(grid), dim3(kGnThreads), 0, s,
                      a);  // also writes dW, dB
   return hipGetLastError() == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_HIP;
+}
+template <DT D, bool WIDE>
+rmsnorm_status gn_bwd_launch(const GnArgs& a, int64_t chunks, hipStream_t s) {
+  return a.S <= gn_chunk<D>() / 4 ? gn_bwd_launch_as<D, WIDE, true>(a, chunks, s)
+                                  : gn_bwd_launch_as<D, WIDE, false>(a, chunks, s);
 }
 
 template <bool FWD, bool WIDE>

@@ -246,11 +246,14 @@ def gn_dx_model_bitexact(dy, x, w, mean, rstd, *, G: int, dtype: str,
         vs = V if rows == "vector" else 1
         sums = [gn_segment_sums(p, vs)[..., None] for p in (dy, (dy * xh).astype(np.float32))]
     else:
-        # per-chunk sums: 256 threads x 4 vectors of V, even / odd accumulators, lane tree, 4 waves
-        pad = K * ch - S
-        D = np.pad(dy, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, 256, V)
-        X = np.pad(xh, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, 256, V)
-        a1 = b1 = a2 = b2 = np.zeros((B, C, K, 256), np.float32)
+        # per-chunk sums: T threads x 4 vectors of V (thread t holds vectors t, t + T, ...), even /
+        # odd accumulators, lane tree, the 4 waves in order (T = 256); segments of at most a
+        # quarter chunk take one wavefront each (T = 64: the lane tree is the sum)
+        T = 64 if S <= ch // 4 else 256
+        pad = K * (4 * T * V) - S
+        D = np.pad(dy, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, T, V)
+        X = np.pad(xh, ((0, 0), (0, 0), (0, pad))).reshape(B, C, K, 4, T, V)
+        a1 = b1 = a2 = b2 = np.zeros((B, C, K, T), np.float32)
         for it in range(4):
             for e in range(V):
                 d, xx = D[..., it, :, e], X[..., it, :, e]
@@ -260,9 +263,9 @@ def gn_dx_model_bitexact(dy, x, w, mean, rstd, *, G: int, dtype: str,
                     a1, a2 = (a1 + d).astype(np.float32), _fma(d, xx, a2)
         sums = []
         for p, q in ((a1, b1), (a2, b2)):
-            waves = _lane_tree((p + q).astype(np.float32).reshape(B, C, K, 4, 64))
+            waves = _lane_tree((p + q).astype(np.float32).reshape(B, C, K, T // 64, 64))
             s = waves[..., 0]
-            for k in range(1, 4):
+            for k in range(1, T // 64):
                 s = (s + waves[..., k]).astype(np.float32)
             sums.append(s)  # [B, C, K]
     wv = np.asarray(w, np.float32)

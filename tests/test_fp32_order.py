@@ -156,6 +156,24 @@ def test_gn_model_on_integer_chunks_is_exact():
     mean = np.zeros((B, G), np.float32)
     rstd = np.ones((B, G), np.float32)
     assert gn_dx_model_bitexact(dy, x, w, mean, rstd, G=G, dtype="bf16") == 1.0
+    # segments of at most a quarter chunk: one wavefront a chunk
+    x1, dy1 = x[..., :1000], dy[..., :1000]
+    for dt in ("bf16", "f32"):
+        assert gn_dx_model_bitexact(dy1, x1, w, mean, rstd, G=G, dtype=dt, rows=False) == 1.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,C,S,G", [(2, 16, 1025, 1), (1, 4096, 4, 1), (2, 1280, 1024, 32)])
+def test_gn_model_rates_wavefront_chunks(dtype, B, C, S, G):
+    """Chunked shapes whose segments fill at most a quarter chunk (one wavefront a chunk); the
+    16-bit bar rests on these rates (float32 dx has a normwise bar)."""
+    base = GN_BASE[dtype]
+    inp = make_gn_inputs(base, B=B, C=C, S=S, seed=B * 1000 + C + S)
+    _, mean, rstd = oracle.groupnorm_fwd(inp["x"], inp["w"], inp["b"], G=G, eps=base.eps,
+                                         dtype=dtype)
+    rate = gn_dx_model_bitexact(inp["dy"], inp["x"], inp["w"], mean, rstd, G=G, dtype=dtype,
+                                rows=False)
+    assert rate >= 0.999, rate
 
 
 def test_gn_segment_sums_order():

@@ -84,6 +84,8 @@ def test_gn_page_shapes(name):
     (3, 10, 1111, 2),     # 5555-element rows, not 16-byte aligned: 8 elements a lane
     (2, 12, 1111, 1),     # 13332 elements a row: 16 elements a lane (16-bit)
     (1, 4096, 4, 1),      # 16384 elements in 4096 channels: past the LDS cap, chunked kernels
+    (1, 4095, 4, 1),      # the same with 4095 chunks: one wavefront a chunk, an idle last one
+    (2, 1280, 1024, 32),  # 40 channels of 32 x 32 a group: chunks of one wavefront each
     (2, 64, 10, 4),       # 10-element channels: vectors straddle channel boundaries
     (2, 64, 4, 2),        # channels narrower than a vector (16-bit)
     (5, 6, 500, 3),       # 1000-element rows, 1000 * 2 bytes a multiple of 16
