@@ -78,6 +78,8 @@ def test_gn_page_shapes(name):
     (2, 16, 1025, 1),     # channels of 1025 elements: past the by-value rows, chunked kernels
     (2, 32, 1024, 1),     # 32768 elements: four vectors a lane (float32: chunks)
     (2, 320, 4096, 32),   # 10 channels of 64 x 64 a group (40960-element rows): chunks
+    (2, 16, 3000, 1),     # chunks of 3000 elements: half a block's lanes hold a partial last vector
+    (2, 16, 2000, 1),     # 16-bit: rows held whole; float32: chunks of half a block
     (2, 640, 1024, 32),   # 20 channels of 32 x 32 a group (20480-element rows)
     (4, 1280, 16, 32),    # 40 channels of 16 elements a group (10240-element rows)
     (17, 512, 512, 64),   # 1088 rows: half the threads a row, two vectors a lane (one round)
