@@ -11,8 +11,9 @@
 //   dW_c = sum over batch and space of dy * xhat,      dB_c = sum over batch and space of dy
 //
 // Work is split into chunks of at most CH elements of one (batch, channel) segment, one 256-thread
-// block per chunk, so the affine weight and bias are one scalar per block and rows of any length
-// spread over the whole GPU. Every cross-chunk combination runs in a fixed order:
+// block per chunk (one wavefront per chunk for segments of at most CH / 4 elements), so the affine
+// weight and bias are one scalar per chunk and rows of any length spread over the whole GPU. Every
+// cross-chunk combination runs in a fixed order:
 //   forward   gn_stats_kernel writes each chunk's (mean, M2 = sum of squared deviations from the
 //             chunk mean, taken in a second pass over registers); gn_fwd_kernel merges the row's
 //             chunk statistics with Chan's pairwise update (lane-strided sequential merges, then a
