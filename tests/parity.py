@@ -363,8 +363,18 @@ def check_softmax_fwd(y_gpu, x, *, dtype) -> dict:
         return st
     d = ulps(y_gpu, y_o, dtype)
     st["y_max_ulp"] = float(d.max()) if d.size else 0.0
-    assert st["y_bitexact"] >= Y_BITEXACT_FRAC, st
     assert np.all(d <= 1), st
+    # A 16-bit y can differ from the correctly rounded value only where the float32 arithmetic's
+    # error (SM_F32_REL, absolute below 1e-38) carries the value across the rounding midpoint
+    # between the two candidates: each differing element must lie that close to it.
+    v = oracle.softmax_fwd(x, dtype=dtype, exact=True)
+    mid = (np.asarray(y_gpu, np.float64) + y_o) / 2.0
+    near = np.abs(v - mid) <= SM_F32_REL * np.maximum(np.abs(v), 1e-38)
+    st["y_off_midpoint"] = int((~eq & ~near).sum())
+    assert st["y_off_midpoint"] == 0, (st, np.argwhere(~eq & ~near)[:5])
+    # The rate as a count with one element's grace: below 1000 elements a single such midpoint
+    # case would otherwise break the 99.9 % rate by itself.
+    assert int((~eq).sum()) <= (1.0 - Y_BITEXACT_FRAC) * eq.size + 1, st
     return st
 
 

@@ -228,3 +228,29 @@ def test_pins_catch_planted_mistake(name):
         except (AssertionError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake: {name}"
+
+
+def test_half_type_check_accepts_only_midpoint_differences():
+    """The 16-bit softmax check lets a value differ from the correctly rounded one only where the
+    exact value lies within the float32 bound of the midpoint between the two candidates: moving
+    the element nearest a midpoint to its other candidate passes, moving the element farthest
+    from one fails."""
+    from parity import check_softmax_fwd
+    rng = np.random.default_rng(5)
+    x = np.asarray(rng.standard_normal((40, 50)), np.float16).astype(np.float32)
+    v = oracle.softmax_fwd(x, dtype="f16", exact=True)
+    y = oracle.softmax_fwd(x, dtype="f16").astype(np.float16)
+    other = np.where(v > y, np.nextafter(y, np.float16(np.inf)),
+                     np.nextafter(y, np.float16(-np.inf)))
+    gap = np.abs(v - (y.astype(np.float64) + other.astype(np.float64)) / 2) / np.abs(v)
+    near, far = np.unravel_index(np.argmin(gap), gap.shape), np.unravel_index(np.argmax(gap),
+                                                                               gap.shape)
+    assert gap[near] <= 2.0**-18 < gap[far]
+    check_softmax_fwd(y.astype(np.float32), x, dtype="f16")
+    ok = y.copy()
+    ok[near] = other[near]
+    assert check_softmax_fwd(ok.astype(np.float32), x, dtype="f16")["y_off_midpoint"] == 0
+    bad = y.copy()
+    bad[far] = other[far]
+    with pytest.raises(AssertionError):
+        check_softmax_fwd(bad.astype(np.float32), x, dtype="f16")
