@@ -219,3 +219,39 @@ def test_ln_full_size_bf16():
     wl = LN_WORKLOADS["ln_bf16_4096x4096"]
     st, _ = run_ln("bf16", wl.M, wl.N, seed=wl.seed)
     print(st)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ln_two_value_rows(dtype):
+    """Rows of two values: xhat = +-1 up to eps, so dx = rstd * ((gdy - c1) - xhat * c2) cancels to
+    rounding noise (it vanishes exactly at eps = 0) and no bit-exact rate applies. Each 16-bit dx
+    element must lie within the float32 evaluation error of that expression from the oracle's,
+    8 * 2^-24 * rstd * (|gdy| + |c1| + |xhat * c2|), plus one ulp of T; y, dw and db as elsewhere."""
+    import oracle
+    from parity import check_dw
+    M, N, ld = 31, 2, 14
+    wl = WL[dtype]
+    inp = make_norm_inputs(wl, M=M, N=N, seed=236)
+    x, w, b, dy = inp["x"], inp["w"], inp["b"], inp["dy"]
+    print(f"ln two-value rows dtype={dtype} M={M} ld={ld}", flush=True)
+    xt, dyt = padded(x, dtype, ld), padded(dy, dtype, ld)
+    wt, bt = to_device(w, dtype, DEV), to_device(b, dtype, DEV)
+    y, mean, rstd = rn.layernorm_fwd(xt, wt, bt, eps=wl.eps,
+                                     y=padded(np.zeros((M, N), np.float32), dtype, ld))
+    dx, dw, db = rn.layernorm_bwd(dyt, xt, wt, mean, rstd,
+                                  dx=padded(np.zeros((M, N), np.float32), dtype, ld))
+    torch.cuda.synchronize()
+    yg, mg, rg, dxg, dwg, dbg = (to_np(t) for t in (y, mean, rstd, dx, dw, db))
+    check_ln_fwd(yg, mg, rg, x, w, b, eps=wl.eps, dtype=dtype)
+    dx_o, dw_o, db_o = oracle.layernorm_bwd(dy, x, w, mg, rg, dtype=dtype)
+    r = rg.astype(np.float64)[:, None]
+    xh = (x.astype(np.float64) - mg.astype(np.float64)[:, None]) * r
+    gdy = w.astype(np.float64)[None, :] * dy.astype(np.float64)
+    c1 = gdy.mean(axis=1, keepdims=True)
+    c2 = (gdy * xh).mean(axis=1, keepdims=True)
+    bound = 8 * 2.0**-24 * r * (np.abs(gdy) + np.abs(c1) + np.abs(xh * c2))
+    err = np.abs(dxg.astype(np.float64) - dx_o)
+    ok = err <= bound + oracle.ulp_of(np.abs(dx_o.astype(np.float64)), dtype)
+    assert ok.all(), (np.argwhere(~ok)[:5], float((err / np.maximum(bound, 1e-30)).max()))
+    check_dw(dwg, dw_o)
+    check_dw(dbg, db_o)
