@@ -1,5 +1,6 @@
-"""GPU parity on seeded random shapes: every entry point (RMSNorm in all three backward modes,
-LayerNorm with and without bias, softmax, GroupNorm) against the CPU oracle on shapes drawn
+"""GPU parity on seeded random shapes: every entry point (RMSNorm in all three backward modes, its
+FP8-output forward and its float64 entry points, LayerNorm with and without bias, softmax,
+GroupNorm) against the CPU oracle on shapes drawn
 log-uniformly, so that widths land on every kernel family (lane segments, one or more wavefronts a
 row, register, LDS-staged and streaming rows, element-wise rows that are not 16-byte aligned) and
 row counts are ragged against the blocks. Each case is small enough for the oracle to finish in
@@ -18,7 +19,8 @@ if not torch.cuda.is_available():
 from test_gpu_groupnorm import BASE as GN_BASE, run_gn  # noqa: E402
 from test_gpu_layernorm import run_ln  # noqa: E402
 from test_gpu_parity import run_case  # noqa: E402
-from test_gpu_softmax import run_sm  # noqa: E402
+from test_gpu_fp8 import run_fp8  # noqa: E402
+from test_gpu_softmax import run_f64, run_sm  # noqa: E402
 
 MAX_ELEMS = 1_200_000
 CASES = 40
@@ -92,6 +94,26 @@ def _gn_cases():
     return out
 
 
+def _fp8_cases():
+    rng = np.random.default_rng(20260105)
+    out = []
+    for i in range(CASES // 2):
+        N = _width(rng)
+        out.append((i, ["bf16", "f16", "f32"][int(rng.integers(3))], _rows(rng, N), N,
+                    ["e4m3", "e5m2"][int(rng.integers(2))], float(2.0 ** rng.integers(-4, 5)),
+                    float(rng.integers(2))))
+    return out
+
+
+def _f64_cases():
+    rng = np.random.default_rng(20260106)
+    out = []
+    for i in range(CASES // 2):
+        N = _width(rng)
+        out.append((i, _rows(rng, N), N, _stride(rng, N), float(rng.integers(2))))
+    return out
+
+
 @pytest.mark.parametrize("i,dtype,M,N,ld,mode,offset", _rms_cases())
 def test_sweep_rmsnorm(i, dtype, M, N, ld, mode, offset):
     if mode == "autograd":
@@ -113,3 +135,13 @@ def test_sweep_softmax(i, dtype, M, N, ld):
 @pytest.mark.parametrize("i,dtype,B,C,S,G,bias", _gn_cases())
 def test_sweep_groupnorm(i, dtype, B, C, S, G, bias):
     run_gn(GN_BASE[dtype], B=B, C=C, S=S, G=G, seed=400 + i, bias=bias)
+
+
+@pytest.mark.parametrize("i,dtype,M,N,fmt,scale,offset", _fp8_cases())
+def test_sweep_fp8_forward(i, dtype, M, N, fmt, scale, offset):
+    run_fp8(dtype, M, N, fmt=fmt, scale=scale, offset=offset, seed=500 + i)
+
+
+@pytest.mark.parametrize("i,M,N,ld,offset", _f64_cases())
+def test_sweep_rmsnorm_f64(i, M, N, ld, offset):
+    run_f64(M, N, seed=600 + i, offset=offset, ld=ld)
