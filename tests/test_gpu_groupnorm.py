@@ -91,6 +91,7 @@ def test_gn_page_shapes(name):
     (2, 64, 10, 4),       # 10-element channels: vectors straddle channel boundaries
     (2, 64, 4, 2),        # channels narrower than a vector (16-bit)
     (5, 6, 500, 3),       # 1000-element rows, 1000 * 2 bytes a multiple of 16
+    (1, 2049, 2100, 3),   # 2049 block chunks of 2100 elements, more than the chip holds at once
 ])
 def test_gn_shapes(dtype, B, C, S, G):
     run_gn(BASE[dtype], B=B, C=C, S=S, G=G, seed=B * 1000 + C + S)
