@@ -1,4 +1,5 @@
-"""Graph capture of the widened entry points: LayerNorm, GroupNorm, softmax, the FP8-output
+"""Graph capture of the widened entry points: LayerNorm, GroupNorm (rows held whole, block and
+wavefront chunks), softmax, narrow rows of all three row operations, the FP8-output
 forward and the float64 RMSNorm, each forward + backward captured once in a HIP graph and replayed
 several times, with unrelated eager work and synchronizations between the replays; every replay
 must reproduce the eager results bit for bit (the entry points record kernels only: no memsets, no
@@ -69,22 +70,27 @@ def test_layernorm_graph():
     replay_matches_eager(step, [y, mean, rstd, dx, dw, db], "layernorm")
 
 
-def test_groupnorm_graph():
+@pytest.mark.parametrize("B,C,S,G", [
+    (2, 16, 5000, 4),     # rows held whole
+    (2, 4, 20000, 2),     # chunks of a block each, three a segment
+    (2, 1280, 1024, 32),  # chunks of a wavefront each
+])
+def test_groupnorm_graph(B, C, S, G):
     wl = GN_WORKLOADS["gn_bf16_1x16x256x256_g4"]
-    inp = make_gn_inputs(wl, B=2, C=16, S=5000, seed=32)
+    inp = make_gn_inputs(wl, B=B, C=C, S=S, seed=32)
     x, dy = to_device(inp["x"], "bf16", DEV), to_device(inp["dy"], "bf16", DEV)
     w, b = to_device(inp["w"], "bf16", DEV), to_device(inp["b"], "bf16", DEV)
     y, dx = torch.empty_like(x), torch.empty_like(x)
-    mean = torch.empty((2, 4), dtype=torch.float32, device=DEV)
+    mean = torch.empty((B, G), dtype=torch.float32, device=DEV)
     rstd = torch.empty_like(mean)
-    dw = torch.empty(16, dtype=torch.float32, device=DEV)
+    dw = torch.empty(C, dtype=torch.float32, device=DEV)
     db = torch.empty_like(dw)
-    ws = torch.empty(rn.groupnorm_workspace_bytes(2, 16, 5000, 4, "bf16") // 4,
+    ws = torch.empty(rn.groupnorm_workspace_bytes(B, C, S, G, "bf16") // 4,
                      dtype=torch.float32, device=DEV)
 
     def step():
-        rn.groupnorm_fwd(x, 4, w, b, y=y, mean=mean, rstd=rstd, workspace=ws)
-        rn.groupnorm_bwd(dy, x, 4, w, mean, rstd, dx=dx, dw=dw, db=db, workspace=ws)
+        rn.groupnorm_fwd(x, G, w, b, y=y, mean=mean, rstd=rstd, workspace=ws)
+        rn.groupnorm_bwd(dy, x, G, w, mean, rstd, dx=dx, dw=dw, db=db, workspace=ws)
 
     replay_matches_eager(step, [y, mean, rstd, dx, dw, db], "groupnorm")
 
@@ -170,3 +176,29 @@ def test_autograd_wrappers_equal_direct_calls():
     dx3 = rn.softmax_bwd(gy.reshape(-1, 768), y3)
     torch.cuda.synchronize()
     assert torch.equal(ysm.reshape(-1, 768), y3) and torch.equal(xsm.grad.reshape(-1, 768), dx3)
+
+
+def test_narrow_rows_graph():
+    """Rows of 128 bf16 values (16-lane segments): RMSNorm, LayerNorm and softmax forward and
+    backward in one graph."""
+    M, N = 3000, 128
+    inp = make_norm_inputs(LN_WORKLOADS["ln_bf16_4096x4096"], M=M, N=N, seed=34)
+    x, w, b, dy = (to_device(inp[k], "bf16", DEV) for k in ("x", "w", "b", "dy"))
+    outs = {k: torch.empty_like(x) for k in ("y", "dx", "ly", "ldx", "sy", "sdx")}
+    rstd = torch.empty(M, dtype=torch.float32, device=DEV)
+    mean, lrstd = torch.empty_like(rstd), torch.empty_like(rstd)
+    dw, lw, lb = (torch.empty(N, dtype=torch.float32, device=DEV) for _ in range(3))
+    ws = torch.empty(rn.workspace_bytes(M, N, "bf16") // 4, dtype=torch.float32, device=DEV)
+    lws = torch.empty(rn.layernorm_workspace_bytes(M, N, "bf16") // 4, dtype=torch.float32,
+                      device=DEV)
+
+    def step():
+        rn.fwd(x, w, y=outs["y"], rstd=rstd)
+        rn.bwd(dy, x, w, rstd, dx=outs["dx"], dw=dw, workspace=ws)
+        rn.layernorm_fwd(x, w, b, y=outs["ly"], mean=mean, rstd=lrstd)
+        rn.layernorm_bwd(dy, x, w, mean, lrstd, dx=outs["ldx"], dw=lw, db=lb, workspace=lws)
+        rn.softmax_fwd(x, y=outs["sy"])
+        rn.softmax_bwd(dy, outs["sy"], dx=outs["sdx"])
+
+    replay_matches_eager(step, list(outs.values()) + [rstd, mean, lrstd, dw, lw, lb],
+                         "narrow rows")
